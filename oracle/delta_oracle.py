@@ -1,0 +1,148 @@
+"""CPU oracle for the gated delta-rule recurrence (token by token, float64).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product
+path never calls it, and it shares no code with the HIP kernels.
+
+What it computes is the plain definition of the recurrence, one token at a
+time, on the exact (already rounded) input values the GPU receives:
+
+* the delta rule is one serial gradient step of a linear memory on the
+  regression loss 1/2 ||S k - v||^2: read ``S k``, subtract it from the
+  value, write the residual along ``k`` with step size beta (DeltaTTT
+  summary, paperlayer.ai, §2 Background and §4.1 "Layerwise memory
+  optimization"; Gated DeltaNet-2 abstract, thelatestinai.com/papers/2607.07953:
+  delta-rule models subtract the current read before writing a new value);
+* a decay multiplies the memory before the read: a scalar per head and token
+  for Gated DeltaNet, a vector over key channels for Kimi Delta Attention
+  ("Delta-Rule Linear Attention" topic page, FG^2-GDN card: KDA refines the
+  head-wise decay gate into channel-wise decay);
+* Gated DeltaNet-2 replaces the single step size by a channel-wise erase gate
+  b (key side) and a channel-wise write gate w (value side), and reduces to
+  KDA when both equal the same scalar (Gated DeltaNet-2 abstract).
+
+With S of shape [d_v, d_k] and a_t the decay (1, a scalar, or a d_k-vector),
+one token does, in this order:
+
+    S'  = S · Diag(a_t)                          decay the key columns
+    r   = S' k_t                                  read
+    S   = S' + beta_t (v_t - r) k_t^T             DeltaNet, GDN, KDA
+    S   = S' - r (b_t ⊙ k_t)^T + (w_t ⊙ v_t) k_t^T   Gated DeltaNet-2
+    o_t = S q_t                                   readout after the write
+
+The erase placement ``r (b ⊙ k)^T`` for Gated DeltaNet-2 is a reading: the
+abstract names the two gates but prints no formula.  That reading is parity
+unpinned beyond the reduction to KDA at b = w = beta.
+
+``run_recurrence`` works on any numpy dtype, including ``object`` arrays of
+``fractions.Fraction`` for exact-arithmetic tests; the public wrappers use
+float64.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+VARIANTS = ("deltanet", "gdn", "kda", "gdn2")
+
+
+def run_recurrence(S0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                   a: np.ndarray, beta: Optional[np.ndarray] = None,
+                   erase: Optional[np.ndarray] = None, write: Optional[np.ndarray] = None
+                   ) -> Tuple[np.ndarray, np.ndarray]:
+    """Sequential recurrence over a batch of independent sequences.
+
+    S0: [N, dv, dk]; q, k: [N, T, dk]; v: [N, T, dv]; a: [N, T, dk] decay
+    factors (already broadcast over key channels).  Either ``beta`` [N, T]
+    (single step size) or both ``erase`` [N, T, dk] and ``write`` [N, T, dv]
+    (split gates).  Returns o [N, T, dv] and the final state [N, dv, dk].
+    """
+    split = erase is not None
+    if split != (write is not None) or split == (beta is not None):
+        raise ValueError("pass either beta, or both erase and write")
+    S = np.array(S0, copy=True)
+    N, T, _ = q.shape
+    o = np.empty((N, T, v.shape[2]), dtype=S.dtype)
+    for t in range(T):
+        kt = k[:, t, :]
+        Sp = S * a[:, t, None, :]
+        r = (Sp @ kt[:, :, None])[:, :, 0]
+        if split:
+            S = (Sp - r[:, :, None] * (erase[:, t, :] * kt)[:, None, :]
+                 + (write[:, t, :] * v[:, t, :])[:, :, None] * kt[:, None, :])
+        else:
+            S = Sp + beta[:, t, None, None] * (v[:, t, :] - r)[:, :, None] * kt[:, None, :]
+        o[:, t, :] = (S @ q[:, t, :, None])[:, :, 0]
+    return o, S
+
+
+def _decay(variant: str, g: Optional[np.ndarray], lead: tuple, dk: int) -> np.ndarray:
+    """Per-channel decay factors a = exp(g), broadcast to lead + (dk,)."""
+    if variant == "deltanet":
+        if g is not None:
+            raise ValueError("the ungated form takes no decay")
+        return np.ones(lead + (dk,), dtype=np.float64)
+    if g is None:
+        raise ValueError(f"{variant} needs a log-decay")
+    g = np.asarray(g, dtype=np.float64)
+    if variant == "gdn":
+        if g.shape != lead:
+            raise ValueError(f"scalar decay must have shape {lead}, got {g.shape}")
+        return np.broadcast_to(np.exp(g)[..., None], lead + (dk,))
+    if g.shape != lead + (dk,):
+        raise ValueError(f"channel decay must have shape {lead + (dk,)}, got {g.shape}")
+    return np.exp(g)
+
+
+def _to_heads(x: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    """[B, T, H, ...] -> [B*H, T, ...] in float64."""
+    if x is None:
+        return None
+    x = np.asarray(x, dtype=np.float64)
+    B, T, H = x.shape[:3]
+    x = np.moveaxis(x, 2, 1)
+    return x.reshape((B * H, T) + x.shape[3:])
+
+
+def delta_fwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward pass over a whole sequence, argument layout of the C boundary.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (for gdn2 the erase
+    gate [B, T, H, dk]); wgate: gdn2 write gate [B, T, H, dv], else None;
+    g: log-decay, None / [B, T, H] / [B, T, H, dk]; S0: [B, H, dv, dk] or None
+    (zero state).  Returns o [B, T, H, dv] and S_T [B, H, dv, dk], float64.
+    """
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    q = np.asarray(q, dtype=np.float64)
+    B, T, H, dk = q.shape
+    dv = np.shape(v)[3]
+    a = _to_heads(_decay(variant, g, (B, T, H), dk))
+    if S0 is None:
+        S = np.zeros((B * H, dv, dk), dtype=np.float64)
+    else:
+        S = np.asarray(S0, dtype=np.float64).reshape(B * H, dv, dk)
+    if variant == "gdn2":
+        if wgate is None:
+            raise ValueError("gdn2 needs the write gate")
+        o, S = run_recurrence(S, _to_heads(q), _to_heads(k), _to_heads(v), a,
+                              erase=_to_heads(beta), write=_to_heads(wgate))
+    else:
+        if wgate is not None:
+            raise ValueError("only gdn2 takes a write gate")
+        o, S = run_recurrence(S, _to_heads(q), _to_heads(k), _to_heads(v), a,
+                              beta=_to_heads(beta))
+    o = np.moveaxis(o.reshape(B, H, T, dv), 1, 2)
+    return np.ascontiguousarray(o), S.reshape(B, H, dv, dk)
+
+
+def delta_decode(variant: str, q, k, v, beta=None, wgate=None, g=None, S=None
+                 ) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step: per-token tensors [B, H, d] (beta/g [B, H] or [B, H, dk]),
+    state S [B, H, dv, dk].  Returns o [B, H, dv] and the new state, float64."""
+    add_t = (lambda x: None if x is None else np.asarray(x)[:, None])
+    o, S_new = delta_fwd(variant, add_t(q), add_t(k), add_t(v), add_t(beta), add_t(wgate),
+                         add_t(g), S)
+    return o[:, 0], S_new
