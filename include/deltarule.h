@@ -1,0 +1,139 @@
+/*
+ * deltarule.h — C ABI of the MI355X (gfx950) gated delta-rule library.
+ *
+ * The library evaluates the delta-rule recurrence of a linear matrix memory
+ * S (d_v rows, d_k columns, fp32) over a sequence of tokens.  For token t with
+ * query q_t, key k_t (d_k), value v_t (d_v) and decay a_t = exp(g_t):
+ *
+ *   S' = S · Diag(a_t)                         decay the key columns
+ *   r  = S' k_t                                read the memory at the key
+ *   S  = S' + beta_t (v_t - r) k_t^T           DR_DELTANET, DR_GDN, DR_KDA
+ *   S  = S' - r (b_t ⊙ k_t)^T + (w_t ⊙ v_t) k_t^T      DR_GDN2
+ *   o_t = S q_t                                readout after the write
+ *
+ * Sources (web pages):
+ *  - delta rule = one serial gradient step of a linear memory on
+ *    1/2 ||S k - v||^2, read before write: "DeltaTTT: Layerwise Optimization
+ *    for Nonlinear Recurrent Memory" summary (paperlayer.ai), §2 Background,
+ *    §4.1; "Gated DeltaNet-2" abstract (thelatestinai.com/papers/2607.07953);
+ *  - scalar head-wise decay (Gated DeltaNet) and channel-wise decay (Kimi
+ *    Delta Attention): "Delta-Rule Linear Attention" topic page, FG^2-GDN card;
+ *  - split channel-wise erase gate b_t and write gate w_t, reducing to KDA when
+ *    both are the same scalar: Gated DeltaNet-2 abstract.  The placement of b on
+ *    the key side of the erase term is this library's reading of that abstract;
+ *  - the update is affine in the previous memory, so chunks of tokens can be
+ *    evaluated in parallel (DeltaTTT summary, §2), by a chunkwise WY algorithm
+ *    with channel-wise decay absorbed into the erase factors (Gated DeltaNet-2
+ *    abstract): that is how delta_fwd evaluates it;
+ *  - decode is one read and one write pass over each state matrix per token
+ *    ("Delta-Rule Linear Attention" topic page, GDN FPGA decode card).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers on the current HIP device, dense
+ *    and row-major with the shapes given below (no strides).  Every pointer
+ *    must be 16-byte aligned.  The caller owns every buffer; the library
+ *    allocates no device memory and keeps no per-call state.
+ *  - dtype (dr_desc.dtype) is the element type of q, k, v, beta, wgate, g and
+ *    o.  The state (S0, S_T, S) is always fp32.
+ *  - The stream argument is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous: they enqueue kernels and return without synchronising.
+ *  - Every argument is validated on the host before any HIP call.  Errors are
+ *    returned as a dr_status and never abort; C++ exceptions never cross the
+ *    ABI.  On an error nothing has been enqueued and no output was touched.
+ *  - Results are deterministic: no atomics, fixed reduction order.
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk = 64; any T >= 1 (the
+ *    last chunk is masked when T is not a multiple of 64).
+ */
+#ifndef DELTARULE_H
+#define DELTARULE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DR_ABI_VERSION 1
+
+typedef enum {
+    DR_DELTANET = 0, /* a = 1: no decay, g must be NULL                          */
+    DR_GDN = 1,      /* scalar decay per (token, head): g is [B,T,H]             */
+    DR_KDA = 2,      /* channel-wise decay: g is [B,T,H,d_k]                     */
+    DR_GDN2 = 3      /* channel-wise decay + erase gate b + write gate w         */
+} dr_variant;
+
+typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+typedef enum {
+    DR_OK = 0,
+    DR_E_NULLPTR = 1,     /* a required pointer (or the descriptor) is NULL       */
+    DR_E_SHAPE = 2,       /* a size is out of range (B, T, H < 1, decode T != 1)  */
+    DR_E_UNSUPPORTED = 3, /* unknown variant/dtype, unsupported d_k/d_v/chunk, or
+                             a pointer given that the variant does not take     */
+    DR_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
+    DR_E_DEVICE = 5,      /* no HIP device, or the current device is not gfx950   */
+    DR_E_LAUNCH = 6,      /* the kernel launch failed (hipGetLastError)           */
+    DR_E_ALIAS = 7        /* an output overlaps an input it may not alias         */
+} dr_status;
+
+typedef struct {
+    int32_t B;       /* batch                                                  */
+    int32_t T;       /* tokens per sequence (1 for delta_decode)               */
+    int32_t H;       /* heads                                                  */
+    int32_t d_k;     /* key/query width                                        */
+    int32_t d_v;     /* value width                                            */
+    int32_t chunk;   /* chunk length of the chunkwise evaluation; must be 64   */
+    int32_t variant; /* dr_variant                                             */
+    int32_t dtype;   /* dr_dtype                                               */
+} dr_desc;
+
+/*
+ * delta_fwd — chunkwise-parallel forward pass over whole sequences.
+ *
+ *   q, k   [B, T, H, d_k]   dtype
+ *   v      [B, T, H, d_v]   dtype
+ *   beta   DR_DELTANET/GDN/KDA: step size beta [B, T, H];
+ *          DR_GDN2: erase gate b [B, T, H, d_k]                         dtype
+ *   wgate  DR_GDN2: write gate w [B, T, H, d_v]; otherwise must be NULL  dtype
+ *   g      log-decay log(a) <= 0: DR_DELTANET must be NULL; DR_GDN
+ *          [B, T, H]; DR_KDA/DR_GDN2 [B, T, H, d_k]                       dtype
+ *   S0     initial state [B, H, d_v, d_k] fp32; NULL means zero
+ *   o      output [B, T, H, d_v] dtype (written); must not overlap any input
+ *   S_T    final state [B, H, d_v, d_k] fp32 (written); NULL if not wanted;
+ *          may be the same pointer as S0 (in-place update) but must not
+ *          otherwise overlap an input
+ *
+ * Channel-wise decays are evaluated with exponents taken relative to points
+ * inside each chunk; a single channel whose log-decay falls by more than
+ * about 80 within 8 consecutive tokens exceeds the fp32 exponent range.
+ */
+dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
+                    const void* beta, const void* wgate, const void* g, const float* S0,
+                    void* o, float* S_T, void* stream);
+
+/*
+ * delta_decode — one token per sequence, state updated in place.
+ *
+ *   desc->T must be 1; shapes as delta_fwd with the T axis removed:
+ *   q, k [B, H, d_k]; v [B, H, d_v]; beta [B, H] (DR_GDN2: b [B, H, d_k]);
+ *   wgate [B, H, d_v] (DR_GDN2 only); g NULL / [B, H] / [B, H, d_k];
+ *   S      state [B, H, d_v, d_k] fp32, read and overwritten in place
+ *   o      output [B, H, d_v] dtype; must not overlap any input or S
+ *
+ * Each state matrix is read once and written once.
+ */
+dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const void* v,
+                       const void* beta, const void* wgate, const void* g, float* S, void* o,
+                       void* stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* dr_status_str(int status);
+
+/* DR_ABI_VERSION of the loaded library. */
+int dr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTARULE_H */

@@ -1,0 +1,194 @@
+// C ABI of the gated delta-rule library: host-side validation, device check and
+// dispatch to the kernel launchers.  See include/deltarule.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/deltarule.h"
+#include "kernels.h"
+
+namespace {
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span_of(const void* p, int64_t elems, int64_t elem_bytes) {
+    Span s;
+    if (p != nullptr) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + static_cast<uintptr_t>(elems * elem_bytes);
+    }
+    return s;
+}
+
+bool overlap(const Span& a, const Span& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Elements of each operand for a descriptor (T tokens per sequence).
+struct Sizes {
+    int64_t qk, v, beta, wgate, g, state;
+};
+
+dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
+    if (d == nullptr) return DR_E_NULLPTR;
+    if (d->variant < DR_DELTANET || d->variant > DR_GDN2) return DR_E_UNSUPPORTED;
+    if (d->dtype != DR_F32 && d->dtype != DR_BF16) return DR_E_UNSUPPORTED;
+    if (d->B < 1 || d->H < 1 || d->T < 1) return DR_E_SHAPE;
+    if (decode && d->T != 1) return DR_E_SHAPE;
+    if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128)) return DR_E_UNSUPPORTED;
+    if (d->chunk != 64) return DR_E_UNSUPPORTED;
+    const int64_t tok = static_cast<int64_t>(d->B) * d->T * d->H;
+    // Keep every element index well inside int64 and every grid within limits.
+    if (tok > (int64_t(1) << 34) || static_cast<int64_t>(d->B) * d->H > (int64_t(1) << 30))
+        return DR_E_SHAPE;
+    sz->qk = tok * d->d_k;
+    sz->v = tok * d->d_v;
+    sz->beta = d->variant == DR_GDN2 ? tok * d->d_k : tok;
+    sz->wgate = d->variant == DR_GDN2 ? tok * d->d_v : 0;
+    sz->g = d->variant == DR_DELTANET ? 0 : (d->variant == DR_GDN ? tok : tok * d->d_k);
+    sz->state = static_cast<int64_t>(d->B) * d->H * d->d_v * d->d_k;
+    return DR_OK;
+}
+
+dr_status check_gate_ptrs(const dr_desc* d, const void* beta, const void* wgate, const void* g) {
+    if (beta == nullptr) return DR_E_NULLPTR;
+    if (d->variant == DR_GDN2) {
+        if (wgate == nullptr) return DR_E_NULLPTR;
+    } else if (wgate != nullptr) {
+        return DR_E_UNSUPPORTED;
+    }
+    if (d->variant == DR_DELTANET) {
+        if (g != nullptr) return DR_E_UNSUPPORTED;
+    } else if (g == nullptr) {
+        return DR_E_NULLPTR;
+    }
+    return DR_OK;
+}
+
+std::atomic<int> g_arch_state[64];  // per device: 0 unknown, 1 gfx950, 2 other
+
+dr_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return DR_E_DEVICE;
+    }
+    if (dev < 64) {
+        const int st = g_arch_state[dev].load(std::memory_order_acquire);
+        if (st == 1) return DR_OK;
+        if (st == 2) return DR_E_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return DR_E_DEVICE;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+    return ok ? DR_OK : DR_E_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
+                    const void* beta, const void* wgate, const void* g, const float* S0,
+                    void* o, float* S_T, void* stream) {
+    try {
+        Sizes sz;
+        dr_status st = check_desc(desc, false, &sz);
+        if (st != DR_OK) return st;
+        if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return DR_E_NULLPTR;
+        st = check_gate_ptrs(desc, beta, wgate, g);
+        if (st != DR_OK) return st;
+        const void* ptrs[] = {q, k, v, beta, wgate, g, S0, o, S_T};
+        for (const void* p : ptrs)
+            if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
+        const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
+        const Span in[] = {span_of(q, sz.qk, eb),       span_of(k, sz.qk, eb),
+                           span_of(v, sz.v, eb),        span_of(beta, sz.beta, eb),
+                           span_of(wgate, sz.wgate, eb), span_of(g, sz.g, eb),
+                           span_of(S0, sz.state, 4)};
+        const Span so = span_of(o, sz.v, eb);
+        const Span sst = span_of(S_T, sz.state, 4);
+        for (const Span& s : in) {
+            if (overlap(so, s)) return DR_E_ALIAS;
+        }
+        for (int i = 0; i < 6; ++i)
+            if (overlap(sst, in[i])) return DR_E_ALIAS;
+        if (overlap(sst, in[6]) && static_cast<const void*>(S_T) != static_cast<const void*>(S0))
+            return DR_E_ALIAS;
+        if (overlap(sst, so)) return DR_E_ALIAS;
+
+        st = check_device();
+        if (st != DR_OK) return st;
+        dr::FwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g,
+                      S0, o, S_T};
+        const hipError_t e = dr::launch_fwd(desc->variant, desc->dtype, a,
+                                            static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
+dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const void* v,
+                       const void* beta, const void* wgate, const void* g, float* S, void* o,
+                       void* stream) {
+    try {
+        Sizes sz;
+        dr_status st = check_desc(desc, true, &sz);
+        if (st != DR_OK) return st;
+        if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || S == nullptr)
+            return DR_E_NULLPTR;
+        st = check_gate_ptrs(desc, beta, wgate, g);
+        if (st != DR_OK) return st;
+        const void* ptrs[] = {q, k, v, beta, wgate, g, S, o};
+        for (const void* p : ptrs)
+            if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
+        const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
+        const Span in[] = {span_of(q, sz.qk, eb),       span_of(k, sz.qk, eb),
+                           span_of(v, sz.v, eb),        span_of(beta, sz.beta, eb),
+                           span_of(wgate, sz.wgate, eb), span_of(g, sz.g, eb),
+                           span_of(S, sz.state, 4)};
+        const Span so = span_of(o, sz.v, eb);
+        for (const Span& s : in)
+            if (overlap(so, s)) return DR_E_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(in[6], in[i])) return DR_E_ALIAS;
+
+        st = check_device();
+        if (st != DR_OK) return st;
+        dr::DecodeArgs a{desc->B, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g, S, o};
+        const hipError_t e = dr::launch_decode(desc->variant, desc->dtype, a,
+                                               static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
+const char* dr_status_str(int s) {
+    switch (s) {
+        case DR_OK: return "ok";
+        case DR_E_NULLPTR: return "null pointer";
+        case DR_E_SHAPE: return "bad shape";
+        case DR_E_UNSUPPORTED: return "unsupported variant, dtype, size or argument";
+        case DR_E_ALIGN: return "pointer not 16-byte aligned";
+        case DR_E_DEVICE: return "no gfx950 HIP device";
+        case DR_E_LAUNCH: return "kernel launch failed";
+        case DR_E_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int dr_abi_version(void) { return DR_ABI_VERSION; }
+
+}  // extern "C"

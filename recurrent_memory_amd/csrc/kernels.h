@@ -1,0 +1,41 @@
+// Internal launcher interface between the C ABI (abi.hip) and the kernels.
+// Arguments have been validated by the caller; launchers only pick a template
+// instance, size the grid and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+struct FwdArgs {
+    int B, T, H, dk, dv;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;   // beta [B,T,H], or the erase gate [B,T,H,dk] (split gates)
+    const void* wgate;  // write gate [B,T,H,dv] (split gates) or nullptr
+    const void* g;      // log-decay: nullptr, [B,T,H] or [B,T,H,dk]
+    const float* S0;    // [B,H,dv,dk] or nullptr (zero state)
+    void* o;            // [B,T,H,dv]
+    float* ST;          // [B,H,dv,dk] or nullptr
+};
+
+struct DecodeArgs {
+    int B, H, dk, dv;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const void* wgate;
+    const void* g;
+    float* S;  // [B,H,dv,dk], in place
+    void* o;   // [B,H,dv]
+};
+
+// variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
+// dtype: 0 fp32, 1 bf16.
+hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace dr

@@ -1,0 +1,496 @@
+// Chunkwise-parallel forward of the gated delta rule on gfx950.
+//
+// The recurrence is affine in the previous memory (DeltaTTT summary,
+// paperlayer.ai, §2 Background), so a chunk of C = 64 tokens acts on its
+// incoming state S in closed form; the decay is absorbed into the keys and
+// the chunk's erase steps are collected in a unit lower-triangular (WY/UT)
+// factor (Gated DeltaNet-2 abstract, thelatestinai.com/papers/2607.07953:
+// chunkwise WY algorithm with decay absorbed into the erase factors).
+//
+// Per chunk, with G_r the in-chunk cumulative log-decay, Q^ = Q ⊙ e^G,
+// K^ = K ⊙ e^G, K- = K ⊙ e^(G_C - G) and (rows r, columns j)
+//   A[r,j] = beta_r Σ_c k_rc k_jc e^(G_rc - G_jc)   (j < r)
+//   P[r,j] =        Σ_c q_rc k_jc e^(G_rc - G_jc)   (j <= r)
+//   T  = (I + A)^-1                                  unit lower triangular
+//   V~ = T (beta ⊙ (V - K^ S^T))                     row j = beta_j (v_j - S'_j k_j)
+//   O  = Q^ S^T + P V~                               readout after each write
+//   S^T <- Diag(e^G_C) S^T + K-^T V~
+//
+// Work decomposition.  One workgroup of four 64-lane waves owns one
+// (batch, head, 64-column value tile); each wave owns 16 value columns and
+// keeps its 128 x 16 slice of S^T in fp32 MFMA accumulators for the whole
+// sequence, so the state never leaves the chip between chunks.  The outputs
+// of one MFMA feed the next one directly from registers: an accumulator tile
+// holds rows 4*(lane/16)+i of column lane%16, which is exactly the operand
+// layout of a contraction over those rows, once the other operand is read
+// from LDS with the same row order.  The key-side work of a chunk (K K^T,
+// Q K^T, the triangular inverse) is shared by the four waves through LDS.
+// Value columns are independent (row i of S only ever mixes with v_i), so
+// the value tiles of one head need no communication.
+//
+// Numerics: MFMA operands are in the input dtype (bf16 x bf16 or fp32 x fp32
+// products, fp32 accumulation); the state, the cumulative gates and the
+// triangular inverse are fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace dr {
+namespace {
+
+constexpr int kC = 64;          // chunk length
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVT = 16 * kWaves;  // value columns per workgroup
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Operand handling per input dtype.  S = LDS storage element, R = a 16x16
+// register tile converted to operand form (4 values per lane).
+template <typename E>
+struct Ops;
+
+template <>
+struct Ops<BF16> {
+    typedef uint16_t S;
+    typedef bf16x4 R;
+    static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
+    __device__ static __forceinline__ S enc(float x) { return f32_to_bf16_bits(x); }
+    __device__ static __forceinline__ float dec(S s) { return bf16_bits_to_f32(s); }
+    __device__ static __forceinline__ R to_reg(f32x4 x) {
+        R r;
+        r[0] = static_cast<bf16_t>(x[0]);
+        r[1] = static_cast<bf16_t>(x[1]);
+        r[2] = static_cast<bf16_t>(x[2]);
+        r[3] = static_cast<bf16_t>(x[3]);
+        return r;
+    }
+    // acc += A[16 x K] · B[16 x K]^T; arow/brow point at this lane's row
+    // (tile row lane%16) of A and B in LDS.
+    template <int K>
+    __device__ static __forceinline__ f32x4 nat(f32x4 acc, const S* arow, const S* brow, int g) {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + k0 + 8 * g);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(brow + k0 + 8 * g);
+            acc = mfma32(a, b, acc);
+        }
+        return acc;
+    }
+    // acc += A[16 x 16*(T1-T0)] · [X[T0]; ...; X[T1-1]]: contraction over the
+    // rows of register tiles; arow points at this lane's row of A in LDS, A's
+    // column 16t + 4g + i pairs with row 4g + i of tile t.
+    template <int T0, int T1, int N>
+    __device__ static __forceinline__ f32x4 reg(f32x4 acc, const S* arow, const R (&X)[N], int g) {
+#pragma unroll
+        for (int t = T0; t + 1 < T1; t += 2) {
+            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(arow + 16 * t + 4 * g);
+            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(arow + 16 * (t + 1) + 4 * g);
+            const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 b = __builtin_shufflevector(X[t], X[t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = mfma32(a, b, acc);
+        }
+        if constexpr (((T1 - T0) & 1) != 0) {
+            // An odd tile count ends with a zero-padded 16x16x32 step.  Mixing in
+            // the 16x16x16 instruction is avoided on purpose: hipcc (ROCm 7.2)
+            // schedules a 16x16x16 bf16 MFMA that reads as its accumulator input
+            // the result of a 16x16x32 MFMA without the required wait states,
+            // which produced wrong accumulator elements on gfx950.
+            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(arow + 16 * (T1 - 1) + 4 * g);
+            const bf16x4 z = {0, 0, 0, 0};
+            const bf16x8 a = __builtin_shufflevector(a0, z, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 b = __builtin_shufflevector(X[T1 - 1], z, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = mfma32(a, b, acc);
+        }
+        return acc;
+    }
+};
+
+template <>
+struct Ops<F32> {
+    typedef float S;
+    typedef f32x4 R;
+    static constexpr int kPad = 4;
+    __device__ static __forceinline__ S enc(float x) { return x; }
+    __device__ static __forceinline__ float dec(S s) { return s; }
+    __device__ static __forceinline__ R to_reg(f32x4 x) { return x; }
+    template <int K>
+    __device__ static __forceinline__ f32x4 nat(f32x4 acc, const S* arow, const S* brow, int g) {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 4) acc = mfma4(arow[k0 + g], brow[k0 + g], acc);
+        return acc;
+    }
+    template <int T0, int T1, int N>
+    __device__ static __forceinline__ f32x4 reg(f32x4 acc, const S* arow, const R (&X)[N], int g) {
+#pragma unroll
+        for (int t = T0; t < T1; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma4(arow[16 * t + 4 * g + i], X[t][i], acc);
+        }
+        return acc;
+    }
+};
+
+// Lower-triangular 16x16 tiles (R, J), J <= R, of a 64x64 chunk matrix.
+__device__ __forceinline__ void tri_tile(int idx, int& R, int& J) {
+    // idx: 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
+    R = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
+    J = idx - (R * (R + 1)) / 2;
+}
+
+template <int VAR, typename E, int DK>
+struct Layout {
+    typedef typename Ops<E>::S S;
+    static constexpr int P = Ops<E>::kPad;
+    static constexpr int LDQ = DK + P;       // q, k rows (chunk row major)
+    static constexpr int LDKT = kC + P;      // k transposed (key channel major)
+    static constexpr int LDP = kC + P;       // P, T in operand dtype
+    static constexpr int LDF = kC + 4;       // fp32 A and T
+    static constexpr int LDO = kVT + P;      // output staging
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + kC * LDQ * sizeof(S);
+    static constexpr int oKT = oK + kC * LDQ * sizeof(S);
+    static constexpr int oP = oKT + DK * LDKT * sizeof(S);
+    static constexpr int oTe = oP + kC * LDP * sizeof(S);
+    static constexpr int oT = oTe + (sizeof(S) == 4 ? 0 : kC * LDP * sizeof(S));
+    static constexpr int oA = oT + kC * LDF * 4;  // also the output staging buffer
+    static constexpr int oVec = oA + kC * LDF * 4;
+    // fp32 per-row vectors: beta, G, e^G, e^(G_C - G), and gamma = e^G_C
+    static constexpr int bytes = oVec + (4 * kC + 4) * 4;
+    static_assert(kC * LDO * sizeof(S) <= kC * LDF * 4, "output staging fits in A");
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+template <int VAR, typename E, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
+    static_assert(VAR == 0 || VAR == 1, "channel-wise gates use their own kernel");
+    typedef Ops<E> O_;
+    typedef typename O_::S S;
+    typedef typename O_::R R;
+    typedef Layout<VAR, E, DK> L;
+    constexpr int NVT = DV / kVT;   // value tiles per head
+    constexpr int NKT = DK / 16;    // key-channel tiles
+    constexpr int EPC = 16 / sizeof(S);  // elements per 16-byte chunk
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
+    S* sQ = reinterpret_cast<S*>(smem + L::oQ);
+    S* sK = reinterpret_cast<S*>(smem + L::oK);
+    S* sKT = reinterpret_cast<S*>(smem + L::oKT);
+    S* sP = reinterpret_cast<S*>(smem + L::oP);
+    S* sTe = reinterpret_cast<S*>(smem + L::oTe);
+    float* sT = reinterpret_cast<float*>(smem + L::oT);
+    float* sA = reinterpret_cast<float*>(smem + L::oA);
+    S* sO = reinterpret_cast<S*>(smem + L::oA);
+    float* sBeta = reinterpret_cast<float*>(smem + L::oVec);
+    float* sG = sBeta + kC;
+    float* sEG = sG + kC;
+    float* sEGC = sEG + kC;
+    float* sGam = sEGC + kC;
+
+    // Workgroup -> (head, value tile).  Workgroups are dispatched round-robin
+    // over the 8 XCDs; the NVT tiles of one head get ids that are 8 apart, so
+    // they run on the same XCD and share its L2 for q and k.
+    const int x = blockIdx.x;
+    const int vt = (x / 8) % NVT;
+    const int bh = (x % 8) + 8 * (x / (8 * NVT));
+    if (bh >= p.B * p.H) return;
+    const int b = bh / p.H, h = bh % p.H;
+    const int T = p.T, H = p.H;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int vc0 = vt * kVT + 16 * w;   // first value column of this wave
+
+    // S^T slice: ST[t][i] = S[vc0 + c][16 t + 4 g + i].
+    f32x4 ST[NKT];
+    {
+        const float* s0 = p.S0 ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            if (s0) {
+                const float4 v4 = *reinterpret_cast<const float4*>(s0 + 16 * t + 4 * g);
+                ST[t] = f32x4{v4.x, v4.y, v4.z, v4.w};
+            } else {
+                ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+
+    const int nchunks = (T + kC - 1) / kC;
+    for (int n = 0; n < nchunks; ++n) {
+        const int t0 = n * kC;
+        const int Cn = min(kC, T - t0);
+        const int64_t tok0 = (static_cast<int64_t>(b) * T + t0) * H + h;  // token (b, t0, h)
+
+        // ---- stage the chunk: q, k (and k^T) into LDS, beta, cumulative gate
+        {
+            constexpr int CPR = DK / EPC;
+            for (int idx = tid; idx < kC * CPR; idx += kThreads) {
+                const int row = idx / CPR, cc = idx % CPR;
+                uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
+                if (row < Cn) {
+                    const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * DK + cc * EPC;
+                    qv = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
+                    kv = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
+                }
+                *reinterpret_cast<uint4*>(sQ + row * L::LDQ + cc * EPC) = qv;
+                *reinterpret_cast<uint4*>(sK + row * L::LDQ + cc * EPC) = kv;
+                const S* ke = reinterpret_cast<const S*>(&kv);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) sKT[(cc * EPC + e) * L::LDKT + row] = ke[e];
+            }
+            if (tid < kC) {
+                sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tok0 + static_cast<int64_t>(tid) * H) : 0.f;
+            }
+            if (w == 0) {
+                float G = 0.f;
+                if constexpr (VAR == 1) {
+                    G = lane < Cn ? load_elem<E>(p.g, tok0 + static_cast<int64_t>(lane) * H) : 0.f;
+#pragma unroll
+                    for (int s = 1; s < 64; s <<= 1) {
+                        const float y = __shfl_up(G, s, 64);
+                        if (lane >= s) G += y;
+                    }
+                }
+                const float GC = __shfl(G, 63, 64);
+                sG[lane] = G;
+                sEG[lane] = VAR == 0 ? 1.f : __expf(G);
+                sEGC[lane] = VAR == 0 ? 1.f : __expf(GC - G);
+                if (lane == 0) sGam[0] = VAR == 0 ? 1.f : __expf(GC);
+            }
+        }
+        // This wave's value tile, straight into the accumulator layout.
+        f32x4 Vr[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * m + 4 * g + i;
+                Vr[m][i] = row < Cn ? load_elem<E>(p.v, (tok0 + static_cast<int64_t>(row) * H) * DV + vc0 + c) : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- A = beta ⊙ (K K^T ⊙ Gamma), strictly lower, fp32
+        for (int idx = w; idx < 10; idx += kWaves) {
+            int R, J;
+            tri_tile(idx, R, J);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = O_::template nat<DK>(acc, sK + (16 * R + c) * L::LDQ, sK + (16 * J + c) * L::LDQ, g);
+            const int col = 16 * J + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * R + 4 * g + i;
+                float val = 0.f;
+                if (row > col) {
+                    val = acc[i] * sBeta[row];
+                    if constexpr (VAR == 1) val *= __expf(sG[row] - sG[col]);
+                }
+                sA[row * L::LDF + col] = val;
+            }
+        }
+        __syncthreads();
+
+        // ---- wave 0: diagonal 16x16 blocks of T by forward substitution;
+        //      waves 1..3: P = Q K^T ⊙ Gamma, lower incl. diagonal
+        if (w == 0) {
+            const int rb = 16 * (lane >> 4);
+            const int j = lane & 15;
+            float xcol[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == j) ? 1.f : 0.f;
+                const float* arow = sA + (rb + i) * L::LDF + rb;
+#pragma unroll
+                for (int m = 0; m < i; ++m) s -= arow[m] * xcol[m];
+                xcol[i] = s;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sT[(rb + i) * L::LDF + rb + j] = xcol[i];
+                if constexpr (sizeof(S) != 4) sTe[(rb + i) * L::LDP + rb + j] = O_::enc(xcol[i]);
+            }
+        } else {
+            for (int idx = w - 1; idx < 10; idx += kWaves - 1) {
+                int R, J;
+                tri_tile(idx, R, J);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = O_::template nat<DK>(acc, sQ + (16 * R + c) * L::LDQ, sK + (16 * J + c) * L::LDQ, g);
+                const int col = 16 * J + c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * R + 4 * g + i;
+                    float val = 0.f;
+                    if (row >= col) {
+                        val = acc[i];
+                        if constexpr (VAR == 1) val *= __expf(sG[row] - sG[col]);
+                    }
+                    sP[row * L::LDP + col] = O_::enc(val);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- off-diagonal blocks of T: T_RJ = -T_RR · Σ_{M=J}^{R-1} A_RM T_MJ,
+        //      by distance R - J = 1, 2, 3 (fp32 MFMA)
+#pragma unroll
+        for (int dist = 1; dist <= 3; ++dist) {
+            if (w < 4 - dist) {
+                const int J = w, R = w + dist;
+                f32x4 inner = {0.f, 0.f, 0.f, 0.f};
+                for (int M = J; M < R; ++M) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const float a = sA[(16 * R + c) * L::LDF + 16 * M + 4 * ks + g];
+                        const float bb = sT[(16 * M + 4 * ks + g) * L::LDF + 16 * J + c];
+                        inner = mfma4(a, bb, inner);
+                    }
+                }
+                f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out = mfma4(sT[(16 * R + c) * L::LDF + 16 * R + 4 * g + i], inner[i], out);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * R + 4 * g + i, col = 16 * J + c;
+                    sT[row * L::LDF + col] = -out[i];
+                    if constexpr (sizeof(S) != 4) sTe[row * L::LDP + col] = O_::enc(-out[i]);
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- the state-dependent chain, per wave (16 value columns)
+        {
+            const S* Te = sizeof(S) == 4 ? reinterpret_cast<const S*>(sT) : sTe;
+            constexpr int LDTe = sizeof(S) == 4 ? L::LDF : L::LDP;
+            R STr[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) STr[t] = O_::to_reg(ST[t]);
+            f32x4 X[4], Y[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Y[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                X[m] = O_::template reg<0, NKT>(X[m], sK + (16 * m + c) * L::LDQ, STr, g);
+                Y[m] = O_::template reg<0, NKT>(Y[m], sQ + (16 * m + c) * L::LDQ, STr, g);
+            }
+            // R = beta ⊙ (V - e^G ⊙ K S^T)
+            R Rr[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * m + 4 * g + i;
+                    r[i] = sBeta[row] * (Vr[m][i] - sEG[row] * X[m][i]);
+                }
+                Rr[m] = O_::to_reg(r);
+            }
+            // V~ = T R  (T lower triangular: tile m needs tiles 0..m)
+            f32x4 Vt[4];
+            Vt[0] = O_::template reg<0, 1>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (0 + c) * LDTe, Rr, g);
+            Vt[1] = O_::template reg<0, 2>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (16 + c) * LDTe, Rr, g);
+            Vt[2] = O_::template reg<0, 3>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (32 + c) * LDTe, Rr, g);
+            Vt[3] = O_::template reg<0, 4>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (48 + c) * LDTe, Rr, g);
+            R Vtr[4], Vgr[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                Vtr[m] = O_::to_reg(Vt[m]);
+                f32x4 vg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vg[i] = sEGC[16 * m + 4 * g + i] * Vt[m][i];
+                Vgr[m] = O_::to_reg(vg);
+            }
+            // O = e^G ⊙ Q S^T + P V~
+            f32x4 Ot[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ot[m][i] = sEG[16 * m + 4 * g + i] * Y[m][i];
+            }
+            Ot[0] = O_::template reg<0, 1>(Ot[0], sP + (0 + c) * L::LDP, Vtr, g);
+            Ot[1] = O_::template reg<0, 2>(Ot[1], sP + (16 + c) * L::LDP, Vtr, g);
+            Ot[2] = O_::template reg<0, 3>(Ot[2], sP + (32 + c) * L::LDP, Vtr, g);
+            Ot[3] = O_::template reg<0, 4>(Ot[3], sP + (48 + c) * L::LDP, Vtr, g);
+            // S^T <- e^G_C S^T + K^T (e^(G_C - G) ⊙ V~)
+            const float gam = sGam[0];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                f32x4 s = ST[t] * gam;
+                ST[t] = O_::template reg<0, 4>(s, sKT + (16 * t + c) * L::LDKT, Vgr, g);
+            }
+            // sO aliases sA: the last reads of sA were before the final level barrier.
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sO[(16 * m + 4 * g + i) * L::LDO + 16 * w + c] = O_::enc(Ot[m][i]);
+            }
+        }
+        __syncthreads();
+        // ---- coalesced store of the chunk's outputs (this tile's kVT columns)
+        {
+            constexpr int CPR = kVT / EPC;
+            for (int idx = tid; idx < kC * CPR; idx += kThreads) {
+                const int row = idx / CPR, cc = idx % CPR;
+                if (row < Cn) {
+                    const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * DV + vt * kVT + cc * EPC;
+                    *reinterpret_cast<uint4*>(static_cast<S*>(p.o) + off) =
+                        *reinterpret_cast<const uint4*>(sO + row * L::LDO + cc * EPC);
+                }
+            }
+        }
+        // No barrier needed here: the next chunk only writes the sA/sO region
+        // after its staging barrier, and everything else the chain read was
+        // consumed before the barrier above.
+    }
+
+    if (p.ST) {
+        float* st = p.ST + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+            *reinterpret_cast<float4*>(st + 16 * t + 4 * g) = make_float4(ST[t][0], ST[t][1], ST[t][2], ST[t][3]);
+    }
+}
+
+template <int VAR, typename E, int DK, int DV>
+hipError_t launch_one(const FwdArgs& a, hipStream_t s) {
+    constexpr int NVT = DV / kVT;
+    const int bh = a.B * a.H;
+    const int groups = (bh + 7) / 8;
+    const dim3 grid(static_cast<unsigned>(groups) * 8u * NVT);
+    hipLaunchKernelGGL((prefill_kernel<VAR, E, DK, DV>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int VAR, typename E>
+hipError_t launch_dims(const FwdArgs& a, hipStream_t s) {
+    if (a.dk == 128 && a.dv == 128) return launch_one<VAR, E, 128, 128>(a, s);
+    if (a.dk == 128 && a.dv == 64) return launch_one<VAR, E, 128, 64>(a, s);
+    if (a.dk == 64 && a.dv == 128) return launch_one<VAR, E, 64, 128>(a, s);
+    return launch_one<VAR, E, 64, 64>(a, s);
+}
+
+template <int VAR>
+hipError_t launch_dtype(int dtype, const FwdArgs& a, hipStream_t s) {
+    return dtype == 0 ? launch_dims<VAR, F32>(a, s) : launch_dims<VAR, BF16>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
+    switch (variant) {
+        case 0: return launch_dtype<0>(dtype, a, s);
+        case 1: return launch_dtype<1>(dtype, a, s);
+        default: return hipErrorInvalidValue;  // channel-wise gates: not built yet
+    }
+}
+
+}  // namespace dr

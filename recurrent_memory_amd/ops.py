@@ -1,0 +1,181 @@
+"""Thin ctypes binding of ``libdeltarule.so`` (see include/deltarule.h).
+
+Argument marshalling only: shapes and dtypes of torch device tensors are
+checked, outputs are allocated with torch when not supplied, and the call is
+enqueued on the current HIP stream.  Every step of the computation runs in the
+library's gfx950 kernels; there is no fallback.  If the library is missing the
+import-time loader raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdeltarule.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "deltarule.h")
+
+VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "DR_OK", 1: "DR_E_NULLPTR", 2: "DR_E_SHAPE", 3: "DR_E_UNSUPPORTED",
+          4: "DR_E_ALIGN", 5: "DR_E_DEVICE", 6: "DR_E_LAUNCH", 7: "DR_E_ALIAS"}
+
+
+class DrDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class DeltaRuleError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the library was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m recurrent_memory_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.delta_fwd.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.delta_fwd.restype = ctypes.c_int
+    lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.delta_decode.restype = ctypes.c_int
+    lib.dr_status_str.argtypes = [ctypes.c_int]
+    lib.dr_status_str.restype = ctypes.c_char_p
+    lib.dr_abi_version.argtypes = []
+    lib.dr_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions declared in the public header."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(status: int):
+    lib = load_library()
+    raise DeltaRuleError(status, lib.dr_status_str(status).decode())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+              beta: torch.Tensor, wgate: Optional[torch.Tensor] = None,
+              g: Optional[torch.Tensor] = None, S0: Optional[torch.Tensor] = None,
+              o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+              want_state: bool = True, chunk: int = 64, stream=None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise forward; tensors as in include/deltarule.h ([B, T, H, d] per token).
+
+    Returns (o, S_T).  ``S_T`` is allocated when ``want_state`` and not given;
+    passing ``S_T=S0`` updates the state in place.
+    """
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check("q", q, (B, T, H, dk), dt, dev)
+    _check("k", k, (B, T, H, dk), dt, dev)
+    _check("v", v, (B, T, H, dv), dt, dev)
+    _check("beta", beta, (B, T, H, dk) if variant == "gdn2" else (B, T, H), dt, dev)
+    if variant == "gdn2":
+        _check("wgate", wgate, (B, T, H, dv), dt, dev)
+    elif wgate is not None:
+        raise ValueError("only gdn2 takes a write gate")
+    if variant == "deltanet":
+        if g is not None:
+            raise ValueError("deltanet takes no decay")
+    else:
+        _check("g", g, (B, T, H) if variant == "gdn" else (B, T, H, dk), dt, dev)
+    if S0 is not None:
+        _check("S0", S0, (B, H, dv, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _check("S_T", S_T, (B, H, dv, dk), torch.float32, dev)
+    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt])
+    st = lib.delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
+                       _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return o, S_T
+
+
+def delta_decode(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 beta: torch.Tensor, S: torch.Tensor, wgate: Optional[torch.Tensor] = None,
+                 g: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """One decode step; q, k [B, H, dk], v [B, H, dv]; S [B, H, dv, dk] fp32 updated in place."""
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check("q", q, (B, H, dk), dt, dev)
+    _check("k", k, (B, H, dk), dt, dev)
+    _check("v", v, (B, H, dv), dt, dev)
+    _check("beta", beta, (B, H, dk) if variant == "gdn2" else (B, H), dt, dev)
+    if variant == "gdn2":
+        _check("wgate", wgate, (B, H, dv), dt, dev)
+    elif wgate is not None:
+        raise ValueError("only gdn2 takes a write gate")
+    if variant == "deltanet":
+        if g is not None:
+            raise ValueError("deltanet takes no decay")
+    else:
+        _check("g", g, (B, H) if variant == "gdn" else (B, H, dk), dt, dev)
+    _check("S", S, (B, H, dv, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, H, dv), dt, dev)
+    desc = DrDesc(B, 1, H, dk, dv, 64, var, DTYPES[dt])
+    st = lib.delta_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
+                          _ptr(g), _ptr(S), _ptr(o), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return o

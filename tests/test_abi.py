@@ -1,0 +1,104 @@
+"""C ABI contract on the CPU: the library loads, exports what the header declares,
+and rejects bad arguments with the documented status before any HIP call.
+
+Every call here fails validation, so no pointer is ever dereferenced (the
+pointers are fake, aligned, non-overlapping addresses) and nothing is launched.
+"""
+import ctypes
+
+import pytest
+
+from recurrent_memory_amd import ops
+
+lib = ops.load_library()
+
+DR_OK, DR_E_NULLPTR, DR_E_SHAPE, DR_E_UNSUPPORTED, DR_E_ALIGN, DR_E_DEVICE, DR_E_LAUNCH, DR_E_ALIAS = range(8)
+FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(12)]
+
+
+def test_exports_every_header_symbol():
+    names = ops.header_functions()
+    assert set(names) == {"delta_fwd", "delta_decode", "dr_status_str", "dr_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert lib.dr_abi_version() == 1
+    assert lib.dr_status_str(0) == b"ok"
+    assert lib.dr_status_str(99) == b"unknown status"
+    for s in range(8):
+        assert lib.dr_status_str(s) and lib.dr_status_str(s) != b"unknown status"
+
+
+def desc(**kw):
+    d = dict(B=2, T=100, H=3, d_k=128, d_v=128, chunk=64, variant=1, dtype=1)
+    d.update(kw)
+    return ops.DrDesc(**d)
+
+
+def fwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S0=None,
+        o=FAKE[7], ST=None):
+    return lib.delta_fwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g, S0,
+                         o, ST, None)
+
+
+def dec(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S=FAKE[6],
+        o=FAKE[7]):
+    return lib.delta_decode(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g,
+                            S, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(variant=4), DR_E_UNSUPPORTED), (dict(variant=-1), DR_E_UNSUPPORTED),
+    (dict(dtype=2), DR_E_UNSUPPORTED), (dict(d_k=96), DR_E_UNSUPPORTED),
+    (dict(d_v=256), DR_E_UNSUPPORTED), (dict(chunk=32), DR_E_UNSUPPORTED),
+    (dict(B=0), DR_E_SHAPE), (dict(T=0), DR_E_SHAPE), (dict(H=-1), DR_E_SHAPE),
+    (dict(T=1 << 30, B=1 << 10), DR_E_SHAPE),
+])
+def test_bad_descriptor(kw, status):
+    assert fwd(desc(**kw)) == status
+
+
+def test_null_descriptor_and_pointers():
+    assert fwd(None) == DR_E_NULLPTR
+    assert dec(None) == DR_E_NULLPTR
+    for name in ("q", "k", "v", "beta", "o"):
+        assert fwd(desc(), **{name: None}) == DR_E_NULLPTR, name
+    assert fwd(desc(variant=1), g=None) == DR_E_NULLPTR
+    assert fwd(desc(variant=3), wgate=None) == DR_E_NULLPTR
+    assert dec(desc(T=1), S=None) == DR_E_NULLPTR
+
+
+def test_arguments_the_variant_does_not_take():
+    assert fwd(desc(variant=0)) == DR_E_UNSUPPORTED            # decay given to the ungated form
+    assert fwd(desc(variant=1), wgate=FAKE[4]) == DR_E_UNSUPPORTED
+
+
+def test_alignment():
+    bad = ctypes.c_void_p(FAKE[0].value + 8)
+    assert fwd(desc(), q=bad) == DR_E_ALIGN
+    assert fwd(desc(), S0=ctypes.c_void_p(FAKE[8].value + 4)) == DR_E_ALIGN
+    assert dec(desc(T=1), S=ctypes.c_void_p(FAKE[6].value + 4)) == DR_E_ALIGN
+
+
+def test_aliasing():
+    assert fwd(desc(), o=FAKE[2]) == DR_E_ALIAS                 # o == v
+    assert fwd(desc(), ST=FAKE[0]) == DR_E_ALIAS                # S_T == q
+    inside = ctypes.c_void_p(FAKE[8].value + 256)
+    assert fwd(desc(), S0=FAKE[8], ST=inside) == DR_E_ALIAS     # partial overlap with S0
+    assert dec(desc(T=1), o=FAKE[6]) == DR_E_ALIAS              # o == S
+    assert dec(desc(T=1), S=FAKE[0]) == DR_E_ALIAS              # S == q
+
+
+def test_decode_requires_one_token():
+    assert dec(desc(T=2)) == DR_E_SHAPE
+
+
+def test_no_device_returns_device_error():
+    """With valid arguments and no usable GPU the call reports DR_E_DEVICE."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid arguments would launch on fake pointers")
+    assert fwd(desc(), S0=FAKE[8], ST=FAKE[8]) == DR_E_DEVICE
+    assert dec(desc(T=1)) == DR_E_DEVICE

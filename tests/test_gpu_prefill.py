@@ -1,0 +1,126 @@
+"""Chunkwise forward on the GPU against the token-by-token oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, announce, dev, errs, gpu_fwd, host, slice_rel_err
+from oracle import delta_fwd as oracle_fwd
+from recurrent_memory_amd import ops
+from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs
+
+pytestmark = pytest.mark.gpu
+
+BUILT_VARIANTS = ["deltanet", "gdn"]
+
+
+def _check(variant, dtype, x, tol=None, **kw):
+    o, S = gpu_fwd(variant, x, dtype, **kw)
+    o_ref, S_ref = oracle_fwd(variant, **x)
+    eo, es = errs(o, S, o_ref, S_ref)
+    tol = TOL[dtype] if tol is None else tol
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+@pytest.mark.parametrize("variant", BUILT_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_small_shapes(variant, dtype, dk, dv, T):
+    announce("prefill_small", variant, dtype, dk, dv, T)
+    w = Workload("t", variant, dtype, B=2, H=3, T=T, dk=dk, dv=dv, random_s0=True, seed=T + dk)
+    _check(variant, dtype, make_forward_inputs(w))
+
+
+@pytest.mark.parametrize("variant", BUILT_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_weak_decay_long_carry(variant, dtype):
+    """Weak decay (g/16) so the state carries across many chunks."""
+    announce("prefill_weak_decay", variant, dtype)
+    w = Workload("t", variant, dtype, B=1, H=4, T=700, dk=128, dv=128, random_s0=True, seed=5)
+    _check(variant, dtype, make_forward_inputs(w, gate_scale=1 / 16))
+
+
+def test_deltanet_fp32_workload_full():
+    w = WORKLOADS["deltanet_fp32_t256_d64"]
+    announce("prefill_full", w.name)
+    x = make_forward_inputs(w)
+    eo, es = _check("deltanet", "f32", x)
+    assert eo <= 1e-4
+
+
+def test_gdn_bf16_workload_full_sampled_heads():
+    """The headline workload at full size; every output is computed on the GPU,
+    the oracle checks 6 sampled (batch, head) sequences end to end."""
+    w = WORKLOADS["gdn_bf16_b4_h16_t4096_d128"]
+    announce("prefill_full", w.name)
+    x = make_forward_inputs(w)
+    o, S = gpu_fwd("gdn", x, "bf16")
+    rng = np.random.default_rng(1)
+    for b, h in zip(rng.integers(0, w.B, 6), rng.integers(0, w.H, 6)):
+        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
+               for n, a in x.items()}
+        o_ref, S_ref = oracle_fwd("gdn", **sub)
+        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
+        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (b, h, eo, es)
+
+
+def test_unit_write_full_size_no_oracle():
+    """beta = 1, q = k, unit keys: o_t = v_t exactly in exact arithmetic, at full size.
+    In bf16 the rounded key is not exactly unit-norm, which bounds the error."""
+    w = WORKLOADS["gdn_bf16_b4_h16_t4096_d128"]
+    announce("prefill_unit_write", w.name)
+    x = make_forward_inputs(w)
+    x["beta"] = np.ones_like(x["beta"])
+    x["q"] = x["k"]
+    o, _ = gpu_fwd("gdn", x, "bf16", want_state=False)
+    knorm2 = (x["k"].astype(np.float64) ** 2).sum(-1)
+    assert np.abs(knorm2 - 1).max() < 8e-3
+    assert slice_rel_err(o, x["v"], (0, 2)) <= 2e-2
+
+
+def test_in_place_state_and_split_sequence():
+    """S_T written over S0, and running [0, T1) then [T1, T) equals [0, T)."""
+    announce("prefill_in_place_split")
+    w = Workload("t", "gdn", "f32", B=2, H=2, T=300, dk=128, dv=128, random_s0=True, seed=9)
+    x = make_forward_inputs(w, gate_scale=1 / 8)
+    o_full, S_full = gpu_fwd("gdn", x, "f32")
+    per_tok = ("q", "k", "v", "beta", "g")
+    xa = {n: x[n][:, :130] for n in per_tok}
+    xa["S0"], xa["wgate"] = x["S0"], None
+    S0 = dev(x["S0"], "f32")
+    o_a, _ = ops.delta_fwd("gdn", *(dev(xa[n], "f32") for n in ("q", "k", "v", "beta")),
+                           g=dev(xa["g"], "f32"), S0=S0, S_T=S0)
+    o_b, _ = ops.delta_fwd("gdn", *(dev(x[n][:, 130:], "f32") for n in ("q", "k", "v", "beta")),
+                           g=dev(x["g"][:, 130:], "f32"), S0=S0, S_T=S0)
+    torch.cuda.synchronize()
+    o_split = np.concatenate([host(o_a), host(o_b)], axis=1)
+    assert slice_rel_err(o_split, o_full, (0, 2)) <= 1e-5
+    assert slice_rel_err(host(S0), S_full, (0, 1)) <= 1e-5
+
+
+def test_deterministic():
+    announce("prefill_deterministic")
+    w = Workload("t", "gdn", "bf16", B=2, H=4, T=333, dk=128, dv=128, random_s0=True, seed=3)
+    x = make_forward_inputs(w)
+    o1, S1 = gpu_fwd("gdn", x, "bf16")
+    o2, S2 = gpu_fwd("gdn", x, "bf16")
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_decode_continues_prefill():
+    """Decode of token T+1 from the prefill state equals prefill over T+1 tokens."""
+    announce("decode_after_prefill")
+    w = Workload("t", "gdn", "f32", B=2, H=3, T=129, dk=128, dv=128, random_s0=True, seed=4)
+    x = make_forward_inputs(w)
+    o_full, S_full = gpu_fwd("gdn", x, "f32")
+    xa = {n: (None if x[n] is None else x[n][:, :128]) for n in ("q", "k", "v", "beta", "wgate", "g")}
+    xa["S0"] = x["S0"]
+    _, S_a = gpu_fwd("gdn", xa, "f32")
+    S = dev(S_a.astype(np.float32), "f32")
+    step = {n: dev(x[n][:, 128], "f32") for n in ("q", "k", "v", "beta", "g")}
+    o = ops.delta_decode("gdn", step["q"], step["k"], step["v"], step["beta"], S, g=step["g"])
+    torch.cuda.synchronize()
+    assert slice_rel_err(host(o), o_full[:, 128], (0, 1)) <= 1e-5
+    assert slice_rel_err(host(S), S_full, (0, 1)) <= 1e-5
