@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated delta-rule forward (and the decode step) on one MI355X.
+
+One bench step = one ``delta_fwd`` over the Gated DeltaNet workload
+(bf16 inputs, fp32 state; B=4, H=16, T=4096, d_k=d_v=128, chunk 64, S0 = 0),
+i.e. one pass of the whole chunkwise path.  ``value`` is tokens/s over the
+timed region (a token carries all 16 heads), inputs already resident in HBM.
+Three copies of the inputs are cycled so that no step finds its operands in
+the 256 MB last-level cache left behind by the previous step.
+
+The JSON line also carries
+  roofline      the prefill kernel's algorithmic HBM bytes per launch over its
+                average HIP-event duration, against 8 TB/s;
+  mfma          algorithmic flops per launch over the same duration, against the
+                2.5 PFLOP/s dense bf16 MFMA peak;
+  decode        the single-token decode step (batch 256, 16 heads, d=128, fp32
+                state updated in place), 1000 steps: state bytes moved per step
+                over the per-step time, against 8 TB/s;
+  cpu_baseline  the float64 CPU oracle timed on this host on the same workload
+                (a process pool over (batch, head) sequences).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+PREFILL_KERNEL = "prefill_kernel"
+DECODE_KERNEL = "decode_kernel"
+
+
+def prefill_bytes(B, T, H, dk, dv, elem=2, with_state_out=True):
+    """Algorithmic HBM bytes of one forward: q, k, v, beta, g read once, o written
+    once, plus the fp32 final state written once."""
+    per_token_head = elem * (2 * dk + dv + 1 + 1) + elem * dv
+    state = 4 * dv * dk if with_state_out else 0
+    return B * T * H * per_token_head + B * H * state
+
+
+def prefill_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic flops of one forward (triangular blocks counted once):
+    6 dk dv + 3 C dk + 2 C dv + C^2/3 per token and head."""
+    return B * T * H * (6 * dk * dv + 3 * C * dk + 2 * C * dv + C * C / 3.0)
+
+
+def decode_bytes(B, H, dk, dv, elem=2):
+    """Per decode step: the fp32 state read and written once, plus q, k, v, beta, g
+    read and o written."""
+    return B * H * (2 * 4 * dv * dk + elem * (2 * dk + dv + 2) + elem * dv)
+
+
+def kernel_source_sha(name):
+    import hashlib
+    path = os.path.join(ROOT, "recurrent_memory_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(record, source):
+    """HBM bytes per launch from a committed rocprofv3 counter record
+    (profiles/*.json: FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a reference
+    copy), or None when the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", record)
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha(source):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _oracle_worker(args):
+    from threadpoolctl import threadpool_limits
+    from oracle import delta_fwd
+    variant, x = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        delta_fwd(variant, **x)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(variant, x, B, T, H, max_workers=16):
+    """Time the float64 oracle on this host: one worker per group of (batch, head)
+    sequences over the first ``T`` tokens, BLAS limited to one thread per worker."""
+    import multiprocessing as mp
+    ncpu = len(os.sched_getaffinity(0))
+    workers = max(1, min(max_workers, ncpu, B * H))
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    groups = [pairs[i::workers] for i in range(workers)]
+    jobs = []
+    for grp in groups:
+        bs = [p[0] for p in grp]
+        hs = [p[1] for p in grp]
+        sub = {}
+        for n, a in x.items():
+            if a is None:
+                sub[n] = None
+            elif n == "S0":
+                sub[n] = np.ascontiguousarray(a[bs, hs][:, None])
+            else:  # [B, T, H, ...] -> [len(grp), T, 1, ...]
+                sub[n] = np.ascontiguousarray(a[bs, :T, hs][:, :, None])
+        jobs.append((variant, sub))
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    head_tokens = B * H * T
+    return dict(value=head_tokens / H / wall, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"float64 token-by-token oracle over all {B}x{H} (batch, head) sequences, "
+                       f"first {T} tokens each, {workers} worker processes (1 BLAS thread each), "
+                       f"wall {wall:.2f} s including worker start-up",
+                wall_s=wall)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens per sequence in the oracle's timed sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB "
+                         "(reference kernel for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU: the path shards by "
+                                   "(batch, head) with no communication, but no multi-GPU run is "
+                                   "part of it; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from recurrent_memory_amd import ops
+    from recurrent_memory_amd.inputs import DECODE_HEADLINE, PREFILL_HEADLINE, WORKLOADS, \
+        make_decode_inputs, make_forward_inputs
+
+    ops.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[PREFILL_HEADLINE]
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    x = make_forward_inputs(w)
+    bf = torch.bfloat16
+
+    def up(a):
+        return None if a is None else torch.from_numpy(a).to(bf).to(dev)
+
+    n_sets = 3
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), beta=up(x["beta"]), g=up(x["g"]),
+                         o=torch.empty((B, T, H, dv), dtype=bf, device=dev),
+                         ST=torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        ops.delta_fwd("gdn", s["q"], s["k"], s["v"], s["beta"], g=s["g"], o=s["o"], S_T=s["ST"],
+                      stream=stream)
+
+    for i in range(args.warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(sets[i % n_sets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = B * T
+    value = tokens / (wall / args.steps)
+    nbytes = prefill_bytes(B, T, H, dk, dv)
+    nflops = prefill_flops(B, T, H, dk, dv)
+    gbs = nbytes / kern_avg_s / 1e9
+    tflops = nflops / kern_avg_s / 1e12
+
+    result = {
+        "metric": "tokens/s + % MFMA peak, GDN fwd bf16 H=16 d=128 T=4096; decode HBM GB/s",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N), "
+                "g=-softplus(N))",
+        "config": {"workload": "gated delta-rule chunkwise forward, scalar decay (GDN)",
+                   "B": B, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": 64,
+                   "inputs": "bf16", "state": "fp32", "S0": "zero", "S_T": "written",
+                   "input_sets_cycled": n_sets},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_gdn_bf16_b4_h16_t4096_d128.counters.json",
+                                                 "prefill.hip"),
+                     "kernel": PREFILL_KERNEL, "kernel_avg_us": kern_avg_s * 1e6,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "algorithmic_flops_per_launch": nflops},
+    }
+
+    if not args.no_decode:
+        wd = WORKLOADS[DECODE_HEADLINE]
+        n_distinct = 16
+        d = make_decode_inputs(wd, n_distinct)
+        S = torch.from_numpy(d["S"]).to(dev)
+        steps_in = [{n: up(a) for n, a in s.items()} for s in d["steps"]]
+        od = torch.empty((wd.B, wd.H, wd.dv), dtype=bf, device=dev)
+
+        def dstep(i):
+            s = steps_in[i % n_distinct]
+            ops.delta_decode("gdn", s["q"], s["k"], s["v"], s["beta"], S, g=s["g"], o=od,
+                             stream=stream)
+
+        for i in range(10):
+            dstep(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            dstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dstep_s = e0.elapsed_time(e1) / 1e3 / args.decode_steps
+        dbytes = decode_bytes(wd.B, wd.H, wd.dk, wd.dv)
+        result["decode"] = {
+            "workload": "gated delta-rule decode step, scalar decay, batch 256, H=16, d=128, "
+                        "fp32 state in place",
+            "steps": args.decode_steps, "us_per_step": dstep_s * 1e6,
+            "achieved": dbytes / dstep_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dbytes / dstep_s / 1e9 / HBM_PEAK_GBS, "bytes_per_step": dbytes,
+            "traffic": measured_traffic("decode_gdn_bf16_b256_h16_d128.counters.json", "decode.hip"),
+            "kernel": DECODE_KERNEL, "step_inputs_cycled": n_distinct}
+
+    if args.calib_copy_mib > 0:
+        # reference copy of known size; a 1 GiB fill in between evicts the
+        # source from the 256 MB last-level cache so its reads reach HBM
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev)
+        flush.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n * 4
+
+    if not args.no_cpu_baseline:
+        Tc = min(args.cpu_tokens, T)
+        result["cpu_baseline"] = cpu_baseline("gdn", x, B, Tc, H)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

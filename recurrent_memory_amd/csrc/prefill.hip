@@ -23,10 +23,16 @@
 // of one MFMA feed the next one directly from registers: an accumulator tile
 // holds rows 4*(lane/16)+i of column lane%16, which is exactly the operand
 // layout of a contraction over those rows, once the other operand is read
-// from LDS with the same row order.  The key-side work of a chunk (K K^T,
-// Q K^T, the triangular inverse) is shared by the four waves through LDS.
-// Value columns are independent (row i of S only ever mixes with v_i), so
-// the value tiles of one head need no communication.
+// from LDS with the same row order.  Where that other operand is needed
+// transposed (K^T for the state update, the value tile in accumulator
+// layout) it is read with the gfx950 LDS transpose load, so no transposed
+// copy is kept.  The key-side work of a chunk (K K^T, Q K^T, the triangular
+// inverse) is shared by the four waves through LDS.  Value columns are
+// independent (row i of S only ever mixes with v_i), so the value tiles of one
+// head need no communication.
+//
+// The next chunk's q, k, v, beta and g are loaded into registers while the
+// current chunk is computed; barriers wait for LDS traffic only.
 //
 // Numerics: MFMA operands are in the input dtype (bf16 x bf16 or fp32 x fp32
 // products, fp32 accumulation); the state, the cumulative gates and the
@@ -37,16 +43,40 @@
 namespace dr {
 namespace {
 
-constexpr int kC = 64;          // chunk length
-constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kC = 64;            // chunk length
+constexpr int kWaves = 4;         // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVT = 16 * kWaves;  // value columns per workgroup
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Workgroup barrier that waits only for this wave's LDS traffic.  A plain
+// __syncthreads() also drains outstanding global loads (vmcnt(0)), which would
+// pull the next chunk's prefetch onto the critical path at every barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS transpose load (16-bit elements).  Within each group of 16 lanes, lane
+// p supplies the address of 4 consecutive elements; lane i receives element
+// i % 4 of the piece addressed by lane 4 j + i / 4, for j = 0..3.  Lane p of
+// group g therefore points at row r0 + 4 g + p / 4, columns c0 + 4 (p % 4) of
+// a row-major tile, and lane c receives rows r0 + 4 g + j of column c0 + c.
+__device__ __forceinline__ bf16x4 tr_load(const uint16_t* base, int ld, int r0, int c0, int g, int c) {
+    const uint16_t* p = base + (r0 + 4 * g + (c >> 2)) * ld + c0 + 4 * (c & 3);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
 }
 
 // Operand handling per input dtype.  S = LDS storage element, R = a 16x16
@@ -60,7 +90,6 @@ struct Ops<BF16> {
     typedef bf16x4 R;
     static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
     __device__ static __forceinline__ S enc(float x) { return f32_to_bf16_bits(x); }
-    __device__ static __forceinline__ float dec(S s) { return bf16_bits_to_f32(s); }
     __device__ static __forceinline__ R to_reg(f32x4 x) {
         R r;
         r[0] = static_cast<bf16_t>(x[0]);
@@ -69,44 +98,67 @@ struct Ops<BF16> {
         r[3] = static_cast<bf16_t>(x[3]);
         return r;
     }
-    // acc += A[16 x K] · B[16 x K]^T; arow/brow point at this lane's row
-    // (tile row lane%16) of A and B in LDS.
+    // acc += A[16 x K] · B[16 x K]^T, both row-major in LDS; arow/brow point
+    // at this lane's row (tile row lane % 16).  Fragments are read first.
     template <int K>
     __device__ static __forceinline__ f32x4 nat(f32x4 acc, const S* arow, const S* brow, int g) {
+        bf16x8 a[K / 32], b[K / 32];
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 32) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + k0 + 8 * g);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(brow + k0 + 8 * g);
-            acc = mfma32(a, b, acc);
+        for (int k = 0; k < K / 32; ++k) {
+            a[k] = *reinterpret_cast<const bf16x8*>(arow + 32 * k + 8 * g);
+            b[k] = *reinterpret_cast<const bf16x8*>(brow + 32 * k + 8 * g);
+        }
+#pragma unroll
+        for (int k = 0; k < K / 32; ++k) acc = mfma32(a[k], b[k], acc);
+        return acc;
+    }
+    // acc += A[16 x 16 (T1 - T0)] · [X[T0]; ...; X[T1 - 1]]: contraction over
+    // the rows of register tiles.  arow points at this lane's row of A in LDS;
+    // A's column 16 t + 4 g + i pairs with row 4 g + i of tile t.  An odd tile
+    // count ends with a zero-padded 16x16x32 step: the 16x16x16 instruction is
+    // not mixed in, because hipcc (ROCm 7.2) can issue it without the wait
+    // states required after a 16x16x32 MFMA that produced its accumulator.
+    template <int T0, int T1, int N>
+    __device__ static __forceinline__ f32x4 reg(f32x4 acc, const S* arow, const R (&X)[N], int g) {
+        constexpr int NP = (T1 - T0 + 1) / 2;
+        bf16x8 a[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int t = T0 + 2 * q;
+            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(arow + 16 * t + 4 * g);
+            bf16x4 a1 = {0, 0, 0, 0};
+            if (t + 1 < T1) a1 = *reinterpret_cast<const bf16x4*>(arow + 16 * (t + 1) + 4 * g);
+            a[q] = cat(a0, a1);
+        }
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int t = T0 + 2 * q;
+            const bf16x4 z = {0, 0, 0, 0};
+            const bf16x8 b = cat(X[t], t + 1 < T1 ? X[t + 1] : z);
+            acc = mfma32(a[q], b, acc);
         }
         return acc;
     }
-    // acc += A[16 x 16*(T1-T0)] · [X[T0]; ...; X[T1-1]]: contraction over the
-    // rows of register tiles; arow points at this lane's row of A in LDS, A's
-    // column 16t + 4g + i pairs with row 4g + i of tile t.
-    template <int T0, int T1, int N>
-    __device__ static __forceinline__ f32x4 reg(f32x4 acc, const S* arow, const R (&X)[N], int g) {
+    // acc += M^T[rows c0 .. c0 + 15] · [X[0]; ...; X[NT - 1]] where M is a
+    // row-major (chunk row, column) tile in LDS with leading dimension ld:
+    // the A operand is M transposed, read with the transpose load.
+    template <int NT, int N>
+    __device__ static __forceinline__ f32x4 regT(f32x4 acc, const S* M, int ld, int c0, const R (&X)[N],
+                                               int g, int c) {
+        bf16x8 a[NT / 2];
 #pragma unroll
-        for (int t = T0; t + 1 < T1; t += 2) {
-            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(arow + 16 * t + 4 * g);
-            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(arow + 16 * (t + 1) + 4 * g);
-            const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 b = __builtin_shufflevector(X[t], X[t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc = mfma32(a, b, acc);
-        }
-        if constexpr (((T1 - T0) & 1) != 0) {
-            // An odd tile count ends with a zero-padded 16x16x32 step.  Mixing in
-            // the 16x16x16 instruction is avoided on purpose: hipcc (ROCm 7.2)
-            // schedules a 16x16x16 bf16 MFMA that reads as its accumulator input
-            // the result of a 16x16x32 MFMA without the required wait states,
-            // which produced wrong accumulator elements on gfx950.
-            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(arow + 16 * (T1 - 1) + 4 * g);
-            const bf16x4 z = {0, 0, 0, 0};
-            const bf16x8 a = __builtin_shufflevector(a0, z, 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 b = __builtin_shufflevector(X[T1 - 1], z, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc = mfma32(a, b, acc);
-        }
+        for (int q = 0; q < NT / 2; ++q)
+            a[q] = cat(tr_load(M, ld, 32 * q, c0, g, c), tr_load(M, ld, 32 * q + 16, c0, g, c));
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) acc = mfma32(a[q], cat(X[2 * q], X[2 * q + 1]), acc);
         return acc;
+    }
+    // A 16 x 16 tile of a row-major LDS matrix in accumulator layout:
+    // element i of lane (g, c) is M[r0 + 4 g + i][c0 + c].
+    __device__ static __forceinline__ f32x4 acc_tile(const S* M, int ld, int r0, int c0, int g, int c) {
+        const bf16x4 v = tr_load(M, ld, r0, c0, g, c);
+        return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                     static_cast<float>(v[3])};
     }
 };
 
@@ -116,7 +168,6 @@ struct Ops<F32> {
     typedef f32x4 R;
     static constexpr int kPad = 4;
     __device__ static __forceinline__ S enc(float x) { return x; }
-    __device__ static __forceinline__ float dec(S s) { return s; }
     __device__ static __forceinline__ R to_reg(f32x4 x) { return x; }
     template <int K>
     __device__ static __forceinline__ f32x4 nat(f32x4 acc, const S* arow, const S* brow, int g) {
@@ -133,6 +184,22 @@ struct Ops<F32> {
         }
         return acc;
     }
+    template <int NT, int N>
+    __device__ static __forceinline__ f32x4 regT(f32x4 acc, const S* M, int ld, int c0, const R (&X)[N],
+                                               int g, int c) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma4(M[(16 * t + 4 * g + i) * ld + c0 + c], X[t][i], acc);
+        }
+        return acc;
+    }
+    __device__ static __forceinline__ f32x4 acc_tile(const S* M, int ld, int r0, int c0, int g, int c) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = M[(r0 + 4 * g + i) * ld + c0 + c];
+        return v;
+    }
 };
 
 // Lower-triangular 16x16 tiles (R, J), J <= R, of a 64x64 chunk matrix.
@@ -142,26 +209,25 @@ __device__ __forceinline__ void tri_tile(int idx, int& R, int& J) {
     J = idx - (R * (R + 1)) / 2;
 }
 
-template <int VAR, typename E, int DK>
+template <typename E, int DK>
 struct Layout {
     typedef typename Ops<E>::S S;
     static constexpr int P = Ops<E>::kPad;
-    static constexpr int LDQ = DK + P;       // q, k rows (chunk row major)
-    static constexpr int LDKT = kC + P;      // k transposed (key channel major)
-    static constexpr int LDP = kC + P;       // P, T in operand dtype
-    static constexpr int LDF = kC + 4;       // fp32 A and T
-    static constexpr int LDO = kVT + P;      // output staging
+    static constexpr int LDQ = DK + P;   // q, k rows (chunk row major)
+    static constexpr int LDV = kVT + P;  // value tile, output staging
+    static constexpr int LDP = kC + P;   // P, T in operand dtype
+    static constexpr int LDF = kC + 4;   // fp32 A and T
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + kC * LDQ * sizeof(S);
-    static constexpr int oKT = oK + kC * LDQ * sizeof(S);
-    static constexpr int oP = oKT + DK * LDKT * sizeof(S);
+    static constexpr int oV = oK + kC * LDQ * sizeof(S);
+    static constexpr int oP = oV + kC * LDV * sizeof(S);
     static constexpr int oTe = oP + kC * LDP * sizeof(S);
     static constexpr int oT = oTe + (sizeof(S) == 4 ? 0 : kC * LDP * sizeof(S));
     static constexpr int oA = oT + kC * LDF * 4;  // also the output staging buffer
     static constexpr int oVec = oA + kC * LDF * 4;
     // fp32 per-row vectors: beta, G, e^G, e^(G_C - G), and gamma = e^G_C
     static constexpr int bytes = oVec + (4 * kC + 4) * 4;
-    static_assert(kC * LDO * sizeof(S) <= kC * LDF * 4, "output staging fits in A");
+    static_assert(kC * LDV * sizeof(S) <= kC * LDF * 4, "output staging fits in A");
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -171,15 +237,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
     typedef Ops<E> O_;
     typedef typename O_::S S;
     typedef typename O_::R R;
-    typedef Layout<VAR, E, DK> L;
-    constexpr int NVT = DV / kVT;   // value tiles per head
-    constexpr int NKT = DK / 16;    // key-channel tiles
-    constexpr int EPC = 16 / sizeof(S);  // elements per 16-byte chunk
+    typedef Layout<E, DK> L;
+    constexpr bool kBF = sizeof(S) == 2;
+    constexpr int NVT = DV / kVT;        // value tiles per head
+    constexpr int NKT = DK / 16;         // key-channel tiles
+    constexpr int EPC = 16 / sizeof(S);  // elements per 16-byte piece
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
     S* sQ = reinterpret_cast<S*>(smem + L::oQ);
     S* sK = reinterpret_cast<S*>(smem + L::oK);
-    S* sKT = reinterpret_cast<S*>(smem + L::oKT);
+    S* sV = reinterpret_cast<S*>(smem + L::oV);
     S* sP = reinterpret_cast<S*>(smem + L::oP);
     S* sTe = reinterpret_cast<S*>(smem + L::oTe);
     float* sT = reinterpret_cast<float*>(smem + L::oT);
@@ -222,36 +289,68 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
         }
     }
 
+    // Global -> register prefetch of one chunk: lane `lane` of wave w stages
+    // chunk row `lane`, 16-byte pieces w, w + 4, ... of q, k and the value
+    // tile.  Loads are unconditional (rows past the end of the sequence re-read
+    // its last row) so no branch forces an early wait; padding rows are zeroed
+    // when the registers are committed to LDS at the top of the next chunk.
+    constexpr int NPF = DK / EPC / kWaves;    // q/k pieces per thread
+    constexpr int NPV = kVT / EPC / kWaves;   // value pieces per thread
+    typedef typename E::T Raw;
+    uint4 pq[NPF], pk[NPF], pv[NPV];
+    Raw pbeta = Raw(0), pg = Raw(0);
     const int nchunks = (T + kC - 1) / kC;
+    auto prefetch = [&](int n) {
+        const int t0 = n * kC;
+        const int last = min(kC, T - t0) - 1;
+        const int64_t tok = (static_cast<int64_t>(b) * T + t0 + min(lane, last)) * H + h;
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int64_t off = tok * DK + (w + kWaves * j) * EPC;
+            pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
+            pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
+        }
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            const int64_t off = tok * DV + vt * kVT + (w + kWaves * j) * EPC;
+            pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + off);
+        }
+        if (w == 0) {
+            pbeta = static_cast<const Raw*>(p.beta)[tok];
+            if constexpr (VAR == 1) pg = static_cast<const Raw*>(p.g)[tok];
+        }
+    };
+    auto raw_to_f32 = [](Raw r) -> float {
+        if constexpr (sizeof(Raw) == 4) return __builtin_bit_cast(float, r);
+        else return bf16_bits_to_f32(r);
+    };
+
+    prefetch(0);
     for (int n = 0; n < nchunks; ++n) {
         const int t0 = n * kC;
         const int Cn = min(kC, T - t0);
         const int64_t tok0 = (static_cast<int64_t>(b) * T + t0) * H + h;  // token (b, t0, h)
 
-        // ---- stage the chunk: q, k (and k^T) into LDS, beta, cumulative gate
+        // ---- commit the prefetched chunk to LDS (rows past the end are zeroed)
         {
-            constexpr int CPR = DK / EPC;
-            for (int idx = tid; idx < kC * CPR; idx += kThreads) {
-                const int row = idx / CPR, cc = idx % CPR;
-                uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-                if (row < Cn) {
-                    const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * DK + cc * EPC;
-                    qv = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
-                    kv = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
-                }
-                *reinterpret_cast<uint4*>(sQ + row * L::LDQ + cc * EPC) = qv;
-                *reinterpret_cast<uint4*>(sK + row * L::LDQ + cc * EPC) = kv;
-                const S* ke = reinterpret_cast<const S*>(&kv);
+            const bool rowok = lane < Cn;
+            auto sel = [rowok](uint4 v) {
+                return make_uint4(rowok ? v.x : 0u, rowok ? v.y : 0u, rowok ? v.z : 0u, rowok ? v.w : 0u);
+            };
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) sKT[(cc * EPC + e) * L::LDKT + row] = ke[e];
+            for (int j = 0; j < NPF; ++j) {
+                const int cc = w + kWaves * j;
+                *reinterpret_cast<uint4*>(sQ + lane * L::LDQ + cc * EPC) = sel(pq[j]);
+                *reinterpret_cast<uint4*>(sK + lane * L::LDQ + cc * EPC) = sel(pk[j]);
             }
-            if (tid < kC) {
-                sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tok0 + static_cast<int64_t>(tid) * H) : 0.f;
-            }
+#pragma unroll
+            for (int j = 0; j < NPV; ++j)
+                *reinterpret_cast<uint4*>(sV + lane * L::LDV + (w + kWaves * j) * EPC) = sel(pv[j]);
             if (w == 0) {
+                sBeta[lane] = rowok ? raw_to_f32(pbeta) : 0.f;
                 float G = 0.f;
                 if constexpr (VAR == 1) {
-                    G = lane < Cn ? load_elem<E>(p.g, tok0 + static_cast<int64_t>(lane) * H) : 0.f;
+                    G = rowok ? raw_to_f32(pg) : 0.f;
 #pragma unroll
                     for (int s = 1; s < 64; s <<= 1) {
                         const float y = __shfl_up(G, s, 64);
@@ -265,77 +364,85 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
                 if (lane == 0) sGam[0] = VAR == 0 ? 1.f : __expf(GC);
             }
         }
-        // This wave's value tile, straight into the accumulator layout.
-        f32x4 Vr[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * m + 4 * g + i;
-                Vr[m][i] = row < Cn ? load_elem<E>(p.v, (tok0 + static_cast<int64_t>(row) * H) * DV + vc0 + c) : 0.f;
-            }
-        }
-        __syncthreads();
+        lds_barrier();
+        if (n + 1 < nchunks) prefetch(n + 1);
 
         // ---- A = beta ⊙ (K K^T ⊙ Gamma), strictly lower, fp32
         for (int idx = w; idx < 10; idx += kWaves) {
             int R, J;
             tri_tile(idx, R, J);
+            const int col = 16 * J + c;
+            float brow[4], grow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                brow[i] = sBeta[16 * R + 4 * g + i];
+                grow[i] = sG[16 * R + 4 * g + i];
+            }
+            const float gcol = sG[col];
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = O_::template nat<DK>(acc, sK + (16 * R + c) * L::LDQ, sK + (16 * J + c) * L::LDQ, g);
-            const int col = 16 * J + c;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * R + 4 * g + i;
-                float val = 0.f;
-                if (row > col) {
-                    val = acc[i] * sBeta[row];
-                    if constexpr (VAR == 1) val *= __expf(sG[row] - sG[col]);
-                }
-                sA[row * L::LDF + col] = val;
+                float val = acc[i] * brow[i];
+                if constexpr (VAR == 1) val *= __expf(grow[i] - gcol);
+                sA[row * L::LDF + col] = row > col ? val : 0.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- wave 0: diagonal 16x16 blocks of T by forward substitution;
-        //      waves 1..3: P = Q K^T ⊙ Gamma, lower incl. diagonal
+        // ---- wave 0: diagonal 16x16 blocks of T; waves 1..3: P = Q K^T ⊙ Gamma
         if (w == 0) {
+            // Lane (block rb, column j) solves (I + A_bb) x = e_j by columns:
+            // once x[m] is final, every later row i subtracts A[i][m] x[m].
             const int rb = 16 * (lane >> 4);
             const int j = lane & 15;
-            float xcol[16];
+            float a[16][16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == j) ? 1.f : 0.f;
-                const float* arow = sA + (rb + i) * L::LDF + rb;
+            for (int i = 1; i < 16; ++i) {
 #pragma unroll
-                for (int m = 0; m < i; ++m) s -= arow[m] * xcol[m];
-                xcol[i] = s;
+                for (int m4 = 0; m4 < i; m4 += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(sA + (rb + i) * L::LDF + rb + m4);
+                    a[i][m4] = v.x;
+                    a[i][m4 + 1] = v.y;
+                    a[i][m4 + 2] = v.z;
+                    a[i][m4 + 3] = v.w;
+                }
+            }
+            float xs[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xs[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) xs[i] -= a[i][m] * xs[m];
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                sT[(rb + i) * L::LDF + rb + j] = xcol[i];
-                if constexpr (sizeof(S) != 4) sTe[(rb + i) * L::LDP + rb + j] = O_::enc(xcol[i]);
+                sT[(rb + i) * L::LDF + rb + j] = xs[i];
+                if constexpr (kBF) sTe[(rb + i) * L::LDP + rb + j] = O_::enc(xs[i]);
             }
         } else {
             for (int idx = w - 1; idx < 10; idx += kWaves - 1) {
                 int R, J;
                 tri_tile(idx, R, J);
+                const int col = 16 * J + c;
+                float grow[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) grow[i] = sG[16 * R + 4 * g + i];
+                const float gcol = sG[col];
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = O_::template nat<DK>(acc, sQ + (16 * R + c) * L::LDQ, sK + (16 * J + c) * L::LDQ, g);
-                const int col = 16 * J + c;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * R + 4 * g + i;
-                    float val = 0.f;
-                    if (row >= col) {
-                        val = acc[i];
-                        if constexpr (VAR == 1) val *= __expf(sG[row] - sG[col]);
-                    }
-                    sP[row * L::LDP + col] = O_::enc(val);
+                    float val = acc[i];
+                    if constexpr (VAR == 1) val *= __expf(grow[i] - gcol);
+                    sP[row * L::LDP + col] = O_::enc(row >= col ? val : 0.f);
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- off-diagonal blocks of T: T_RJ = -T_RR · Σ_{M=J}^{R-1} A_RM T_MJ,
         //      by distance R - J = 1, 2, 3 (fp32 MFMA)
@@ -343,98 +450,112 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
         for (int dist = 1; dist <= 3; ++dist) {
             if (w < 4 - dist) {
                 const int J = w, R = w + dist;
-                f32x4 inner = {0.f, 0.f, 0.f, 0.f};
-                for (int M = J; M < R; ++M) {
+                float av[3][4], tv[3][4], dv[4];
+#pragma unroll
+                for (int mm = 0; mm < dist; ++mm) {
+                    const int M = J + mm;
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        const float a = sA[(16 * R + c) * L::LDF + 16 * M + 4 * ks + g];
-                        const float bb = sT[(16 * M + 4 * ks + g) * L::LDF + 16 * J + c];
-                        inner = mfma4(a, bb, inner);
+                        av[mm][ks] = sA[(16 * R + c) * L::LDF + 16 * M + 4 * ks + g];
+                        tv[mm][ks] = sT[(16 * M + 4 * ks + g) * L::LDF + 16 * J + c];
                     }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dv[i] = sT[(16 * R + c) * L::LDF + 16 * R + 4 * g + i];
+                f32x4 inner = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int mm = 0; mm < dist; ++mm) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) inner = mfma4(av[mm][ks], tv[mm][ks], inner);
                 }
                 f32x4 out = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    out = mfma4(sT[(16 * R + c) * L::LDF + 16 * R + 4 * g + i], inner[i], out);
+                for (int i = 0; i < 4; ++i) out = mfma4(dv[i], inner[i], out);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * R + 4 * g + i, col = 16 * J + c;
                     sT[row * L::LDF + col] = -out[i];
-                    if constexpr (sizeof(S) != 4) sTe[row * L::LDP + col] = O_::enc(-out[i]);
+                    if constexpr (kBF) sTe[row * L::LDP + col] = O_::enc(-out[i]);
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- the state-dependent chain, per wave (16 value columns)
         {
-            const S* Te = sizeof(S) == 4 ? reinterpret_cast<const S*>(sT) : sTe;
-            constexpr int LDTe = sizeof(S) == 4 ? L::LDF : L::LDP;
+            const S* Te = kBF ? sTe : reinterpret_cast<const S*>(sT);
+            constexpr int LDTe = kBF ? L::LDP : L::LDF;
+            float eg[4][4], egc[4][4], bt[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * m + 4 * g + i;
+                    eg[m][i] = sEG[row];
+                    egc[m][i] = sEGC[row];
+                    bt[m][i] = sBeta[row];
+                }
+            }
+            const float gam = sGam[0];
             R STr[NKT];
 #pragma unroll
             for (int t = 0; t < NKT; ++t) STr[t] = O_::to_reg(ST[t]);
             f32x4 X[4], Y[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Y[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                X[m] = O_::template reg<0, NKT>(X[m], sK + (16 * m + c) * L::LDQ, STr, g);
-                Y[m] = O_::template reg<0, NKT>(Y[m], sQ + (16 * m + c) * L::LDQ, STr, g);
+                X[m] = O_::template reg<0, NKT>(f32x4{0.f, 0.f, 0.f, 0.f}, sK + (16 * m + c) * L::LDQ, STr, g);
+                Y[m] = O_::template reg<0, NKT>(f32x4{0.f, 0.f, 0.f, 0.f}, sQ + (16 * m + c) * L::LDQ, STr, g);
             }
             // R = beta ⊙ (V - e^G ⊙ K S^T)
             R Rr[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                const f32x4 v = O_::acc_tile(sV, L::LDV, 16 * m, 16 * w, g, c);
                 f32x4 r;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * m + 4 * g + i;
-                    r[i] = sBeta[row] * (Vr[m][i] - sEG[row] * X[m][i]);
-                }
+                for (int i = 0; i < 4; ++i) r[i] = bt[m][i] * (v[i] - eg[m][i] * X[m][i]);
                 Rr[m] = O_::to_reg(r);
             }
             // V~ = T R  (T lower triangular: tile m needs tiles 0..m)
             f32x4 Vt[4];
-            Vt[0] = O_::template reg<0, 1>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (0 + c) * LDTe, Rr, g);
-            Vt[1] = O_::template reg<0, 2>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (16 + c) * LDTe, Rr, g);
-            Vt[2] = O_::template reg<0, 3>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (32 + c) * LDTe, Rr, g);
-            Vt[3] = O_::template reg<0, 4>(f32x4{0.f, 0.f, 0.f, 0.f}, Te + (48 + c) * LDTe, Rr, g);
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            Vt[0] = O_::template reg<0, 1>(zero, Te + (0 + c) * LDTe, Rr, g);
+            Vt[1] = O_::template reg<0, 2>(zero, Te + (16 + c) * LDTe, Rr, g);
+            Vt[2] = O_::template reg<0, 3>(zero, Te + (32 + c) * LDTe, Rr, g);
+            Vt[3] = O_::template reg<0, 4>(zero, Te + (48 + c) * LDTe, Rr, g);
             R Vtr[4], Vgr[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 Vtr[m] = O_::to_reg(Vt[m]);
                 f32x4 vg;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vg[i] = sEGC[16 * m + 4 * g + i] * Vt[m][i];
+                for (int i = 0; i < 4; ++i) vg[i] = egc[m][i] * Vt[m][i];
                 Vgr[m] = O_::to_reg(vg);
             }
+            // S^T <- e^G_C S^T + K^T (e^(G_C - G) ⊙ V~)
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+                ST[t] = O_::template regT<4>(ST[t] * gam, sK, L::LDQ, 16 * t, Vgr, g, c);
             // O = e^G ⊙ Q S^T + P V~
             f32x4 Ot[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Ot[m][i] = sEG[16 * m + 4 * g + i] * Y[m][i];
+                for (int i = 0; i < 4; ++i) Ot[m][i] = eg[m][i] * Y[m][i];
             }
             Ot[0] = O_::template reg<0, 1>(Ot[0], sP + (0 + c) * L::LDP, Vtr, g);
             Ot[1] = O_::template reg<0, 2>(Ot[1], sP + (16 + c) * L::LDP, Vtr, g);
             Ot[2] = O_::template reg<0, 3>(Ot[2], sP + (32 + c) * L::LDP, Vtr, g);
             Ot[3] = O_::template reg<0, 4>(Ot[3], sP + (48 + c) * L::LDP, Vtr, g);
-            // S^T <- e^G_C S^T + K^T (e^(G_C - G) ⊙ V~)
-            const float gam = sGam[0];
-#pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                f32x4 s = ST[t] * gam;
-                ST[t] = O_::template reg<0, 4>(s, sKT + (16 * t + c) * L::LDKT, Vgr, g);
-            }
             // sO aliases sA: the last reads of sA were before the final level barrier.
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sO[(16 * m + 4 * g + i) * L::LDO + 16 * w + c] = O_::enc(Ot[m][i]);
+                    sO[(16 * m + 4 * g + i) * L::LDV + 16 * w + c] = O_::enc(Ot[m][i]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- coalesced store of the chunk's outputs (this tile's kVT columns)
         {
             constexpr int CPR = kVT / EPC;
@@ -443,12 +564,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
                 if (row < Cn) {
                     const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * DV + vt * kVT + cc * EPC;
                     *reinterpret_cast<uint4*>(static_cast<S*>(p.o) + off) =
-                        *reinterpret_cast<const uint4*>(sO + row * L::LDO + cc * EPC);
+                        *reinterpret_cast<const uint4*>(sO + row * L::LDV + cc * EPC);
                 }
             }
         }
-        // No barrier needed here: the next chunk only writes the sA/sO region
-        // after its staging barrier, and everything else the chain read was
+        // No barrier needed here: the next chunk writes the sA/sO region only
+        // after its commit barrier, and everything else the chain read was
         // consumed before the barrier above.
     }
 
