@@ -58,10 +58,18 @@ def decode_bytes(B, H, dk, dv, elem=2):
     return B * H * (2 * 4 * dv * dk + elem * (2 * dk + dv + 2) + elem * dv)
 
 
+KERNEL_SOURCES = {"prefill.hip": ["prefill.hip", "chunk_ops.h", "common.h"],
+                  "prefill_cw.hip": ["prefill_cw.hip", "chunk_ops.h", "common.h"],
+                  "decode.hip": ["decode.hip", "common.h"]}
+
+
 def kernel_source_sha(name):
+    """Hash of a kernel's source files (the kernel file and the headers it uses)."""
     import hashlib
-    path = os.path.join(ROOT, "recurrent_memory_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        h.update(open(os.path.join(ROOT, "recurrent_memory_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(record, source):

@@ -103,9 +103,11 @@ typedef struct {
  *          may be the same pointer as S0 (in-place update) but must not
  *          otherwise overlap an input
  *
- * Channel-wise decays are evaluated with exponents taken relative to points
- * inside each chunk; a single channel whose log-decay falls by more than
- * about 80 within 8 consecutive tokens exceeds the fp32 exponent range.
+ * Channel-wise decays (DR_KDA, DR_GDN2) are evaluated with exponents taken
+ * relative to the boundaries of 16-token blocks: the log-decay of one channel
+ * summed over any 16 consecutive tokens must stay above about -85 (a decay
+ * factor of e^-85), otherwise a split factor leaves the fp32 range and the
+ * outputs become inf/NaN.  Per-token decays down to e^-5 always satisfy this.
  */
 dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,

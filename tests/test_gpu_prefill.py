@@ -6,11 +6,11 @@ import torch
 from gpu_util import TOL, announce, dev, errs, gpu_fwd, host, slice_rel_err
 from oracle import delta_fwd as oracle_fwd
 from recurrent_memory_amd import ops
-from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs
+from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
-BUILT_VARIANTS = ["deltanet", "gdn"]
+BUILT_VARIANTS = ["deltanet", "gdn", "kda", "gdn2"]
 
 
 def _check(variant, dtype, x, tol=None, **kw):
@@ -64,6 +64,55 @@ def test_gdn_bf16_workload_full_sampled_heads():
         eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
         es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
         assert eo <= TOL["bf16"] and es <= TOL["bf16"], (b, h, eo, es)
+
+
+@pytest.mark.parametrize("name,variant,n_sample", [("kda_bf16_b2_h16_t8192_d128", "kda", 4),
+                                                    ("gdn2_bf16_b1_h16_t32768_d128", "gdn2", 2)])
+def test_channel_decay_workloads_full_sampled_heads(name, variant, n_sample):
+    """KDA and Gated DeltaNet-2 workloads at full size: every output is computed on
+    the GPU; the oracle checks sampled (batch, head) sequences end to end."""
+    w = WORKLOADS[name]
+    announce("prefill_full", w.name)
+    x = make_forward_inputs(w)
+    o, S = gpu_fwd(variant, x, "bf16")
+    rng = np.random.default_rng(2)
+    for b, h in zip(rng.integers(0, w.B, n_sample), rng.integers(0, w.H, n_sample)):
+        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
+               for n, a in x.items()}
+        o_ref, S_ref = oracle_fwd(variant, **sub)
+        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
+        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (b, h, eo, es)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdn2_reduces_to_kda_on_gpu(dtype):
+    """Gated DeltaNet-2 with erase and write gates equal to beta reproduces KDA."""
+    announce("gdn2_reduction", dtype)
+    w = Workload("t", "kda", dtype, B=2, H=3, T=300, dk=128, dv=128, random_s0=True, seed=12)
+    x = make_forward_inputs(w, gate_scale=1 / 4)
+    o_kda, S_kda = gpu_fwd("kda", x, dtype)
+    b = np.repeat(x["beta"][..., None], 128, axis=-1)
+    x2 = {**x, "beta": b, "wgate": b.copy()}
+    o2, S2 = gpu_fwd("gdn2", x2, dtype)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert slice_rel_err(o2, o_kda, (0, 2)) <= tol
+    assert slice_rel_err(S2, S_kda, (0, 1)) <= tol
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+def test_channel_decay_strong_gates(variant):
+    """Per-channel log-decays down to -4 per token (decay e^-4, so up to -64 summed
+    over a 16-token block): the split exponentials stay inside the fp32 range
+    because each is taken relative to a block boundary."""
+    announce("strong_gates", variant)
+    for dtype in ("f32", "bf16"):
+        w = Workload("t", variant, dtype, B=1, H=2, T=150, dk=64, dv=64, random_s0=True, seed=13)
+        x = make_forward_inputs(w)
+        rng = np.random.default_rng(5)
+        g = (-rng.uniform(0, 4, x["g"].shape)).astype(np.float32)
+        x["g"] = g if dtype == "f32" else round_to_bf16(g)
+        _check(variant, dtype, x)
 
 
 def test_unit_write_full_size_no_oracle():
