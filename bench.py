@@ -38,18 +38,24 @@ PREFILL_KERNEL = "prefill_kernel"
 DECODE_KERNEL = "decode_kernel"
 
 
-def prefill_bytes(B, T, H, dk, dv, elem=2, with_state_out=True):
-    """Algorithmic HBM bytes of one forward: q, k, v, beta, g read once, o written
-    once, plus the fp32 final state written once."""
-    per_token_head = elem * (2 * dk + dv + 1 + 1) + elem * dv
-    state = 4 * dv * dk if with_state_out else 0
-    return B * T * H * per_token_head + B * H * state
+def prefill_bytes(variant, B, T, H, dk, dv, elem=2, with_state_in=False, with_state_out=True):
+    """Algorithmic HBM bytes of one forward: every per-token input read once, o
+    written once, the fp32 initial state read and the final state written once."""
+    per_tok = {"deltanet": 2 * dk + dv + 1, "gdn": 2 * dk + dv + 2,
+               "kda": 3 * dk + dv + 1, "gdn2": 4 * dk + 2 * dv}[variant] + dv
+    state = 4 * dv * dk * (int(with_state_in) + int(with_state_out))
+    return B * T * H * elem * per_tok + B * H * state
 
 
-def prefill_flops(B, T, H, dk, dv, C=64):
-    """Algorithmic flops of one forward (triangular blocks counted once):
-    6 dk dv + 3 C dk + 2 C dv + C^2/3 per token and head."""
-    return B * T * H * (6 * dk * dv + 3 * C * dk + 2 * C * dv + C * C / 3.0)
+def prefill_flops(variant, B, T, H, dk, dv, C=64):
+    """Algorithmic flops of one forward with chunk length C (triangular blocks
+    counted once): 6 dk dv + 3 C dk + 2 C dv + C^2/3 per token and head for one
+    step size, 8 dk dv + 5 C dk + 4 C dv + C^2/3 for split gates."""
+    if variant == "gdn2":
+        per = 8 * dk * dv + 5 * C * dk + 4 * C * dv + C * C / 3.0
+    else:
+        per = 6 * dk * dv + 3 * C * dk + 2 * C * dv + C * C / 3.0
+    return B * T * H * per
 
 
 def decode_bytes(B, H, dk, dv, elem=2):
@@ -130,6 +136,45 @@ def cpu_baseline(variant, x, B, T, H, max_workers=16):
                 wall_s=wall)
 
 
+def time_forward(w, steps, warmup, n_sets, stream):
+    """Time delta_fwd on workload ``w`` with ``n_sets`` input copies cycled; returns
+    (per-launch HIP-event seconds list, wall seconds for the timed steps)."""
+    import torch
+    from recurrent_memory_amd import ops
+    from recurrent_memory_amd.inputs import make_forward_inputs
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    dev = torch.device("cuda:0")
+    x = make_forward_inputs(w)
+
+    def up(a, d=dt):
+        return None if a is None else torch.from_numpy(a).to(d).to(dev)
+
+    sets = []
+    for _ in range(n_sets):
+        sets.append(dict(q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), beta=up(x["beta"]),
+                         wgate=up(x["wgate"]), g=up(x["g"]), S0=up(x["S0"], torch.float32),
+                         o=torch.empty((w.B, w.T, w.H, w.dv), dtype=dt, device=dev),
+                         ST=torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)))
+
+    def step(s):
+        ops.delta_fwd(w.variant, s["q"], s["k"], s["v"], s["beta"], wgate=s["wgate"], g=s["g"],
+                      S0=s["S0"], o=s["o"], S_T=s["ST"], stream=stream)
+
+    for i in range(warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(sets[i % n_sets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) / 1e3 for a, b in ev], wall, x
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +183,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the non-headline forward workloads")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens per sequence in the oracle's timed sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -162,44 +208,20 @@ def main():
     torch.cuda.set_device(dev)
     w = WORKLOADS[PREFILL_HEADLINE]
     B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
-    x = make_forward_inputs(w)
     bf = torch.bfloat16
+    stream = torch.cuda.current_stream()
 
     def up(a):
         return None if a is None else torch.from_numpy(a).to(bf).to(dev)
 
     n_sets = 3
-    sets = []
-    for _ in range(n_sets):
-        sets.append(dict(q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), beta=up(x["beta"]), g=up(x["g"]),
-                         o=torch.empty((B, T, H, dv), dtype=bf, device=dev),
-                         ST=torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)))
-    stream = torch.cuda.current_stream()
-
-    def step(s):
-        ops.delta_fwd("gdn", s["q"], s["k"], s["v"], s["beta"], g=s["g"], o=s["o"], S_T=s["ST"],
-                      stream=stream)
-
-    for i in range(args.warmup):
-        step(sets[i % n_sets])
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(sets[i % n_sets])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    kern_s, wall, x = time_forward(w, args.steps, args.warmup, n_sets, stream)
+    kern_avg_s = float(np.mean(kern_s))
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (wall / args.steps)
-    nbytes = prefill_bytes(B, T, H, dk, dv)
-    nflops = prefill_flops(B, T, H, dk, dv)
+    nbytes = prefill_bytes("gdn", B, T, H, dk, dv)
+    nflops = prefill_flops("gdn", B, T, H, dk, dv)
     gbs = nbytes / kern_avg_s / 1e9
     tflops = nflops / kern_avg_s / 1e12
 
@@ -224,6 +246,26 @@ def main():
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_launch": nflops},
     }
+
+    if not args.no_other:
+        # the other forward workloads: parity-test shapes, reported beside the headline
+        others = []
+        for name, sub_c in [("deltanet_fp32_t256_d64", 16), ("kda_bf16_b2_h16_t8192_d128", 32),
+                            ("gdn2_bf16_b1_h16_t32768_d128", 32)]:
+            wo = WORKLOADS[name]
+            ks, _, _ = time_forward(wo, 5, 2, 2, stream)
+            t_s = float(np.mean(ks))
+            elem = 4 if wo.dtype == "f32" else 2
+            nb = prefill_bytes(wo.variant, wo.B, wo.T, wo.H, wo.dk, wo.dv, elem=elem,
+                               with_state_in=wo.random_s0)
+            chunk = 64 if wo.variant in ("deltanet", "gdn") else sub_c
+            nf = prefill_flops(wo.variant, wo.B, wo.T, wo.H, wo.dk, wo.dv, C=chunk)
+            others.append({"workload": name, "variant": wo.variant, "dtype": wo.dtype,
+                           "kernel_avg_us": t_s * 1e6, "tokens_per_s": wo.B * wo.T / t_s,
+                           "hbm_GBs": nb / t_s / 1e9, "hbm_frac": nb / t_s / 1e9 / HBM_PEAK_GBS,
+                           "tflops": nf / t_s / 1e12, "flops_chunk_length": chunk,
+                           "algorithmic_bytes_per_launch": nb})
+        result["other_workloads"] = others
 
     if not args.no_decode:
         wd = WORKLOADS[DECODE_HEADLINE]
