@@ -36,6 +36,8 @@ struct DecodeArgs {
 // variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
 // dtype: 0 fp32, 1 bf16.
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
+// software-pipelined bf16 kernel for variants 0 and 1, called by launch_fwd
+hipError_t launch_fwd_pipelined(int variant, const FwdArgs& a, hipStream_t stream);
 // channel-wise decay forms (variant 2 or 3), called by launch_fwd
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);

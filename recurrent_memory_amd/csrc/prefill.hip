@@ -136,13 +136,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
         }
     }
 
-    // Global -> register prefetch of one chunk: lane `lane` of wave w stages
-    // chunk row `lane`, 16-byte pieces w, w + 4, ... of q, k and the value
-    // tile.  Loads are unconditional (rows past the end of the sequence re-read
-    // its last row) so no branch forces an early wait; padding rows are zeroed
-    // when the registers are committed to LDS at the top of the next chunk.
-    constexpr int NPF = DK / EPC / kWaves;    // q/k pieces per thread
-    constexpr int NPV = kVT / EPC / kWaves;   // value pieces per thread
+    // Global -> register prefetch of one chunk in coalesced 16-byte pieces
+    // (piece p = tid + 256 j: row p / pieces-per-row).  Loads are unconditional
+    // (rows past the end of the sequence re-read its last row) so no branch
+    // forces an early wait; padding rows are zeroed when the registers are
+    // committed to LDS at the top of the next chunk.
+    constexpr int CPR = DK / EPC;                 // q/k pieces per row
+    constexpr int VPR = kVT / EPC;                // value pieces per row
+    constexpr int NPF = kC * CPR / kThreads;      // q/k pieces per thread
+    constexpr int NPV = kC * VPR / kThreads;      // value pieces per thread
+    static_assert(NPF * kThreads == kC * CPR && NPV * kThreads == kC * VPR, "piece split");
     typedef typename E::T Raw;
     uint4 pq[NPF], pk[NPF], pv[NPV];
     Raw pbeta = Raw(0), pg = Raw(0);
@@ -150,19 +153,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
     auto prefetch = [&](int n) {
         const int t0 = n * kC;
         const int last = min(kC, T - t0) - 1;
-        const int64_t tok = (static_cast<int64_t>(b) * T + t0 + min(lane, last)) * H + h;
+        const int64_t tokb = static_cast<int64_t>(b) * T + t0;
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
-            const int64_t off = tok * DK + (w + kWaves * j) * EPC;
+            const int pidx = tid + kThreads * j;
+            const int64_t off = ((tokb + min(pidx / CPR, last)) * H + h) * DK + (pidx % CPR) * EPC;
             pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
             pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
         }
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
-            const int64_t off = tok * DV + vt * kVT + (w + kWaves * j) * EPC;
+            const int pidx = tid + kThreads * j;
+            const int64_t off = ((tokb + min(pidx / VPR, last)) * H + h) * DV + vt * kVT + (pidx % VPR) * EPC;
             pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + off);
         }
         if (w == 0) {
+            const int64_t tok = (tokb + min(lane, last)) * H + h;
             pbeta = static_cast<const Raw*>(p.beta)[tok];
             if constexpr (VAR == 1) pg = static_cast<const Raw*>(p.g)[tok];
         }
@@ -181,18 +187,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
         // ---- commit the prefetched chunk to LDS (rows past the end are zeroed)
         {
             const bool rowok = lane < Cn;
-            auto sel = [rowok](uint4 v) {
-                return make_uint4(rowok ? v.x : 0u, rowok ? v.y : 0u, rowok ? v.z : 0u, rowok ? v.w : 0u);
+            auto sel = [](bool ok, uint4 v) {
+                return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
             };
 #pragma unroll
             for (int j = 0; j < NPF; ++j) {
-                const int cc = w + kWaves * j;
-                *reinterpret_cast<uint4*>(sQ + lane * L::LDQ + cc * EPC) = sel(pq[j]);
-                *reinterpret_cast<uint4*>(sK + lane * L::LDQ + cc * EPC) = sel(pk[j]);
+                const int pidx = tid + kThreads * j;
+                const int row = pidx / CPR, cc = pidx % CPR;
+                *reinterpret_cast<uint4*>(sQ + row * L::LDQ + cc * EPC) = sel(row < Cn, pq[j]);
+                *reinterpret_cast<uint4*>(sK + row * L::LDQ + cc * EPC) = sel(row < Cn, pk[j]);
             }
 #pragma unroll
-            for (int j = 0; j < NPV; ++j)
-                *reinterpret_cast<uint4*>(sV + lane * L::LDV + (w + kWaves * j) * EPC) = sel(pv[j]);
+            for (int j = 0; j < NPV; ++j) {
+                const int pidx = tid + kThreads * j;
+                const int row = pidx / VPR, cc = pidx % VPR;
+                *reinterpret_cast<uint4*>(sV + row * L::LDV + cc * EPC) = sel(row < Cn, pv[j]);
+            }
             if (w == 0) {
                 sBeta[lane] = rowok ? raw_to_f32(pbeta) : 0.f;
                 float G = 0.f;
@@ -405,9 +415,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
         lds_barrier();
         // ---- coalesced store of the chunk's outputs (this tile's kVT columns)
         {
-            constexpr int CPR = kVT / EPC;
-            for (int idx = tid; idx < kC * CPR; idx += kThreads) {
-                const int row = idx / CPR, cc = idx % CPR;
+            for (int idx = tid; idx < kC * VPR; idx += kThreads) {
+                const int row = idx / VPR, cc = idx % VPR;
                 if (row < Cn) {
                     const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * DV + vt * kVT + cc * EPC;
                     *reinterpret_cast<uint4*>(static_cast<S*>(p.o) + off) =
@@ -454,10 +463,11 @@ hipError_t launch_dtype(int dtype, const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
+    if (variant >= 2) return launch_fwd_channel(variant, dtype, a, s);
+    if (dtype == 1) return launch_fwd_pipelined(variant, a, s);   // bf16: pipelined kernel
     switch (variant) {
         case 0: return launch_dtype<0>(dtype, a, s);
-        case 1: return launch_dtype<1>(dtype, a, s);
-        default: return launch_fwd_channel(variant, dtype, a, s);
+        default: return launch_dtype<1>(dtype, a, s);
     }
 }
 
