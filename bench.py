@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-PREFILL_KERNEL = "prefill_kernel"
+PREFILL_KERNEL = "prefill_pipe_kernel"
 DECODE_KERNEL = "decode_kernel"
 
 
@@ -65,6 +65,7 @@ def decode_bytes(B, H, dk, dv, elem=2):
 
 
 KERNEL_SOURCES = {"prefill.hip": ["prefill.hip", "chunk_ops.h", "common.h"],
+                  "prefill_pipe.hip": ["prefill_pipe.hip", "chunk_ops.h", "common.h"],
                   "prefill_cw.hip": ["prefill_cw.hip", "chunk_ops.h", "common.h"],
                   "decode.hip": ["decode.hip", "common.h"]}
 
@@ -239,7 +240,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("prefill_gdn_bf16_b4_h16_t4096_d128.counters.json",
-                                                 "prefill.hip"),
+                                                 "prefill_pipe.hip"),
                      "kernel": PREFILL_KERNEL, "kernel_avg_us": kern_avg_s * 1e6,
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -9,21 +9,19 @@
 //   V~ = T (beta ⊙ (V - e^G ⊙ K S^T))
 //   O  = e^G ⊙ Q S^T + P V~
 //   S^T <- e^G_C S^T + K^T (e^(G_C - G) ⊙ V~)
-// Only the last three lines depend on the state, so T and P of chunk n + 1 can
-// be built while chunk n runs through the state.  One workgroup of four waves
-// per (batch, head, 32 value columns):
+// Only the last three lines depend on the state, so A, T and P of chunk
+// n + 1 can be built while chunk n runs through the state.  One workgroup of
+// four waves per (batch, head, 32 value columns):
 //   waves 0, 1 ("chain")  chunk n: the state-dependent lines above, 16 value
 //                         columns each, S^T in fp32 accumulators throughout;
-//   wave 2 ("T builder")  chunk n + 1: A from register-resident K fragments,
-//                         diagonal 16x16 blocks of T by column substitution
-//                         (fp32), off-diagonal blocks chained in registers
-//                         with bf16 MFMA: T_RJ = -T_RR Σ_M A_RM T_MJ;
-//   wave 3 ("P builder")  chunk n + 1: P from register-resident Q and K
-//                         fragments, and the per-row decay vectors of n + 2.
-// Waves 2 and 3 also load q and k of chunk n + 2 into registers at the start
-// of a step and commit them to LDS at its end, so HBM latency is hidden behind
-// a whole step; each step ends in one barrier.  LDS holds q/k in three slots
-// (n, n + 1, n + 2), T and P in two.
+//   wave 2 ("T builder")  chunk n + 1: A from K K^T, diagonal 16x16 blocks of
+//                         T by substitution (fp32), off-diagonal blocks
+//                         chained with bf16 MFMA: T_RJ = -T_RR Σ_M A_RM T_MJ;
+//   wave 3                issues the HBM -> LDS loads of q and k of chunk
+//                         n + 2, builds P of chunk n + 1 and the per-row decay
+//                         vectors of chunk n + 2.
+// Each step ends in one barrier.  LDS holds q/k in three slots (n, n + 1,
+// n + 2), T and P in two.
 #include "chunk_ops.h"
 #include "common.h"
 #include "kernels.h"
@@ -34,23 +32,67 @@ namespace {
 constexpr int kCP = 64;          // chunk length
 constexpr int kVTP = 32;         // value columns per workgroup
 constexpr int kThreadsP = 256;   // 4 waves
+// One 16x16 fp32 diagonal block in LDS: rows of 20 floats (16-byte aligned);
+// blocks 16 bytes further apart than 16 rows so that the four blocks read at
+// once fall in different banks.
+constexpr int kDS = 16 * 20 + 4;
+
+// q/k tiles in LDS: unpadded rows of DK bf16; the 16-byte piece p of row r
+// sits in slot p ^ swz(r).  The swizzle keeps the three read patterns free of
+// bank conflicts: 16 lanes reading 16 B (or 8 B) from one piece column of 16
+// consecutive rows, and the transpose read (4 consecutive rows x 4 pieces of
+// 8 B).  For DK = 128 a row spans all 64 banks; for DK = 64 two rows do.
+template <int DK>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (DK == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+// element offset of (row r, column col) in a q/k tile; col % 8 + width <= 8
+template <int DK>
+__device__ __forceinline__ int qk_off(int r, int col) {
+    return r * DK + ((((col >> 3) ^ swz<DK>(r))) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 8-byte LDS transpose read at a per-lane address (see tr_load)
+__device__ __forceinline__ bf16x4 tr_read(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p)));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes bytes
+// 16 l .. 16 l + 15 after the wave-uniform address lds.  Completion is counted
+// by vmcnt, like any global load.
+__device__ __forceinline__ void load_to_lds16(const uint16_t* src, uint16_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds), 16, 0, 0);
+}
+
+// Barrier for waves that issued global-to-LDS loads: their data must have
+// landed (vmcnt) before other waves may read it.
+__device__ __forceinline__ void dma_lds_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Empty use that keeps four 8-byte register values (and their registers) live.
+__device__ __forceinline__ void keep_alive(const bf16x4 (&v)[4]) {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+}
 
 template <int DK>
 struct LayoutP {
-    static constexpr int LDQ = DK + 8;   // bf16 q/k rows
     static constexpr int LDP = kCP + 8;  // bf16 T, P rows
     static constexpr int LDV = 16 + 8;   // bf16 per-wave value / output staging
-    static constexpr int QK = kCP * LDQ * 2;
+    static constexpr int QK = kCP * DK * 2;
     static constexpr int MP = kCP * LDP * 2;
-    static constexpr int VEC = (4 * kCP + 4) * 4;    // beta, G, e^G, e^(G_C - G), gamma
+    static constexpr int VEC = (8 * kCP + 4) * 4;    // per-row vectors of one chunk
     static constexpr int oQ = 0;                     // [3] slots
     static constexpr int oK = oQ + 3 * QK;           // [3]
     static constexpr int oTe = oK + 3 * QK;          // [2]
     static constexpr int oP = oTe + 2 * MP;          // [2]
     static constexpr int oVec = oP + 2 * MP;         // [3]
-    static constexpr int oAd = oVec + 3 * VEC;       // T builder: diagonal A blocks, fp32 [4][16][20]
-    static constexpr int oTd = oAd + 4 * 16 * 20 * 4;  // T builder: diagonal T blocks, fp32
-    static constexpr int oVw = oTd + 4 * 16 * 20 * 4;  // chain waves: [2][64][LDV] bf16
+    static constexpr int oAd = oVec + 3 * VEC;       // T builder: diagonal A blocks, fp32 [4][kDS]
+    static constexpr int oTd = oAd + 4 * kDS * 4;      // T builder: diagonal T blocks, fp32 [4][kDS]
+    static constexpr int oVw = oTd + 4 * kDS * 4;      // chain waves: [2][64][LDV] bf16
     static constexpr int bytes = oVw + 2 * kCP * LDV * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -71,16 +113,12 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
 }
 
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
+__global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_pipe_kernel(FwdArgs p) {
     static_assert(VAR == 0 || VAR == 1, "scalar or no decay");
-    typedef Ops<BF16> O_;
     typedef LayoutP<DK> L;
-    typedef bf16x4 R;
     constexpr int NVT = DV / kVTP;
     constexpr int NKT = DK / 16;   // 16-wide key-channel tiles
     constexpr int NKK = DK / 32;   // 32-wide k steps
-    constexpr int CPR = DK / 8;    // 16-byte pieces per q/k row
-    constexpr int NPQ = kCP * CPR / 64;   // pieces per lane for one wave loading q (or k)
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
     uint16_t* sQs = reinterpret_cast<uint16_t*>(smem + L::oQ);
@@ -96,7 +134,11 @@ __global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
     auto teslot = [&](int n) { return sTes + (n & 1) * (L::MP / 2); };
     auto pslot = [&](int n) { return sPs + (n & 1) * (L::MP / 2); };
     auto vslot = [&](int n) { return sVecs + (n % 3) * (L::VEC / 4); };
-    // vector slot layout: [0,64) beta, [64,128) G, [128,192) e^G, [192,256) e^(G_C-G), [256] gamma
+    // vector slot layout: [0,64) beta, [64,128) G (cumulative log-decay),
+    // [128,192) e^G, [192,256) e^(G_C - G), [256] gamma = e^G_C,
+    // [260,324) u_r = e^(G_r - G_16floor(r/16)), [324 + 64 (R - 1) + j] =
+    // w_R[j] = e^(G_16R - G_j) for R = 1..3 (used for j < 16 R).  For r in
+    // block R > J, e^(G_r - G_j) = u_r w_R[j] with both factors in (0, 1].
 
     const int x = blockIdx.x;
     const int vt = (x / 8) % NVT;
@@ -140,6 +182,43 @@ __global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
             pv0 = *reinterpret_cast<const uint4*>(src);
             pv1 = *reinterpret_cast<const uint4*>(src + 8);
         };
+        // A-operand fragments of K and Q for X = K S^T and Y = Q S^T, read at
+        // the end of the previous step so that a step starts with its
+        // contractions: fragment (m, q) of lane (g, c) holds row 16 m + c,
+        // columns 32 q + 4 g + (0..3) and 32 q + 16 + 4 g + (0..3), matching the
+        // row order of the register tiles of S^T paired two by two.
+        constexpr int NKP = NKT / 2;
+        // lane parts of every LDS address the chain uses (loop invariant)
+        int xo0[NKP], xo1[NKP], kto[NKT];
+#pragma unroll
+        for (int q = 0; q < NKP; ++q) {
+            xo0[q] = qk_off<DK>(c, 32 * q + 4 * g);
+            xo1[q] = qk_off<DK>(c, 32 * q + 16 + 4 * g);
+        }
+        // transpose reads of K: lane (g, c) of a 16-lane group points at row
+        // r0 + 4 g + c / 4, columns 16 t + 4 (c % 4) .. + 3 and receives column
+        // 16 t + c of rows r0 + 4 g .. + 3 (r0 a multiple of 16 leaves the
+        // swizzle unchanged)
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) kto[t] = qk_off<DK>(4 * g + (c >> 2), 16 * t + 4 * (c & 3));
+        const int tpo = c * L::LDP + 4 * g;                       // T, P rows
+        const int vvo = (4 * g + (c >> 2)) * L::LDV + 4 * (c & 3);  // value tile, transposed
+        bf16x8 kx[4][NKP], qx[4][NKP];
+        auto load_xy = [&](int n) {
+            const uint16_t* sK = kslot(n);
+            const uint16_t* sQ = qslot(n);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int q = 0; q < NKP; ++q) {
+                    const int rb = 16 * m * DK;
+                    kx[m][q] = cat(*reinterpret_cast<const bf16x4*>(sK + rb + xo0[q]), *reinterpret_cast<const bf16x4*>(sK + rb + xo1[q]));
+                    qx[m][q] = cat(*reinterpret_cast<const bf16x4*>(sQ + rb + xo0[q]), *reinterpret_cast<const bf16x4*>(sQ + rb + xo1[q]));
+                }
+            }
+        };
+        const bf16x4 z4 = {0, 0, 0, 0};
+        bf16x4 od[4] = {z4, z4, z4, z4};   // output rows being stored
         for (int s = -2; s < N; ++s) {
             if (s == -1) vload(0);
             if (s >= 0) {
@@ -150,48 +229,85 @@ __global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
                     *reinterpret_cast<uint4*>(sV + lane * L::LDV + 8) = sel_rows(ok, pv1);
                 }
                 if (s + 1 < N) vload(s + 1);
-                const uint16_t* sQ = qslot(s);
                 const uint16_t* sK = kslot(s);
                 const uint16_t* Te = teslot(s);
                 const uint16_t* Pm = pslot(s);
                 const float* vec = vslot(s);
-                float eg[4][4], egc[4][4], bt[4][4];
+                // ---- every LDS operand of the step is requested up front
+                f32x4 bt[4], eg[4], egc[4];
+                float egr[4];   // e^G of row 16 m + c (outputs are kept transposed)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * m + 4 * g + i;
-                        bt[m][i] = vec[row];
-                        eg[m][i] = vec[128 + row];
-                        egc[m][i] = vec[192 + row];
-                    }
+                    bt[m] = *reinterpret_cast<const f32x4*>(vec + 16 * m + 4 * g);
+                    eg[m] = *reinterpret_cast<const f32x4*>(vec + 128 + 16 * m + 4 * g);
+                    egc[m] = *reinterpret_cast<const f32x4*>(vec + 192 + 16 * m + 4 * g);
+                    egr[m] = vec[128 + 16 * m + c];
                 }
                 const float gam = vec[256];
-                R STr[NKT];
+                bf16x4 vv[4];   // value tile in accumulator layout (rows 4 g + i, column c)
 #pragma unroll
-                for (int t = 0; t < NKT; ++t) STr[t] = to_bf16x4(ST[t]);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                f32x4 X[4], Y[4];
+                for (int m = 0; m < 4; ++m) vv[m] = tr_read(sV + 16 * m * L::LDV + vvo);
+                // lower-triangular T and P rows as A operands: row 16 m + c,
+                // column tiles paired (0, 1) and (2, 3); an unpaired tile is
+                // padded with zeros
+                bf16x8 tf[4][2], pf[4][2];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    X[m] = O_::template reg<0, NKT>(zero, sK + (16 * m + c) * L::LDQ, STr, g);
-                    Y[m] = O_::template reg<0, NKT>(zero, sQ + (16 * m + c) * L::LDQ, STr, g);
+#pragma unroll
+                    for (int q = 0; q <= m / 2; ++q) {
+                        const int off = 16 * m * L::LDP + 32 * q + tpo;
+                        const bool two = 2 * q + 1 <= m;
+                        const bf16x4 t0 = *reinterpret_cast<const bf16x4*>(Te + off);
+                        const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(Pm + off);
+                        tf[m][q] = cat(t0, two ? *reinterpret_cast<const bf16x4*>(Te + off + 16) : z4);
+                        pf[m][q] = cat(p0, two ? *reinterpret_cast<const bf16x4*>(Pm + off + 16) : z4);
+                    }
                 }
-                R Rr[4];
+                // K^T fragments for the state update
+                bf16x8 kt[NKT][2];
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        kt[t][q] = cat(tr_read(sK + 32 * q * DK + kto[t]), tr_read(sK + (32 * q + 16) * DK + kto[t]));
+                }
+                // ---- X = K S^T (accumulator layout), Y = Q S^T (transposed:
+                // swapping the operands makes lane (g, c) hold row 16 m + c,
+                // value columns 4 g .. + 3)
+                bf16x8 STp[NKP];
+#pragma unroll
+                for (int q = 0; q < NKP; ++q) STp[q] = cat(to_bf16x4(ST[2 * q]), to_bf16x4(ST[2 * q + 1]));
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                f32x4 X[4], Yt[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const f32x4 v = O_::acc_tile(sV, L::LDV, 16 * m, 0, g, c);
+                    X[m] = zero;
+                    Yt[m] = zero;
+                }
+#pragma unroll
+                for (int q = 0; q < NKP; ++q) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        X[m] = mfma32(kx[m][q], STp[q], X[m]);
+                        Yt[m] = mfma32(STp[q], qx[m][q], Yt[m]);
+                    }
+                }
+                // ---- R = beta (V - e^G X);  V~ = T R
+                bf16x4 Rr[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
                     f32x4 r;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) r[i] = bt[m][i] * (v[i] - eg[m][i] * X[m][i]);
+                    for (int i = 0; i < 4; ++i) r[i] = bt[m][i] * (static_cast<float>(vv[m][i]) - eg[m][i] * X[m][i]);
                     Rr[m] = to_bf16x4(r);
                 }
+                const bf16x8 R01 = cat(Rr[0], Rr[1]), R2z = cat(Rr[2], z4), R23 = cat(Rr[2], Rr[3]), R0z = cat(Rr[0], z4);
                 f32x4 Vt[4];
-                Vt[0] = O_::template reg<0, 1>(zero, Te + (0 + c) * L::LDP, Rr, g);
-                Vt[1] = O_::template reg<0, 2>(zero, Te + (16 + c) * L::LDP, Rr, g);
-                Vt[2] = O_::template reg<0, 3>(zero, Te + (32 + c) * L::LDP, Rr, g);
-                Vt[3] = O_::template reg<0, 4>(zero, Te + (48 + c) * L::LDP, Rr, g);
-                R Vtr[4], Vgr[4];
+                Vt[0] = mfma32(tf[0][0], R0z, zero);
+                Vt[1] = mfma32(tf[1][0], R01, zero);
+                Vt[2] = mfma32(tf[2][1], R2z, mfma32(tf[2][0], R01, zero));
+                Vt[3] = mfma32(tf[3][1], R23, mfma32(tf[3][0], R01, zero));
+                bf16x4 Vtr[4], Vgr[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     Vtr[m] = to_bf16x4(Vt[m]);
@@ -200,33 +316,32 @@ __global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
                     for (int i = 0; i < 4; ++i) vg[i] = egc[m][i] * Vt[m][i];
                     Vgr[m] = to_bf16x4(vg);
                 }
+                // ---- S^T <- gamma S^T + K^T (e^(G_C - G) V~)
+                const bf16x8 Vg01 = cat(Vgr[0], Vgr[1]), Vg23 = cat(Vgr[2], Vgr[3]);
 #pragma unroll
-                for (int t = 0; t < NKT; ++t)
-                    ST[t] = O_::template regT<4>(ST[t] * gam, sK, L::LDQ, 16 * t, Vgr, g, c);
+                for (int t = 0; t < NKT; ++t) ST[t] = mfma32(kt[t][1], Vg23, mfma32(kt[t][0], Vg01, ST[t] * gam));
+                // ---- O = e^G Y + P V~, transposed like Y
+                const bf16x8 V01 = cat(Vtr[0], Vtr[1]), V2z = cat(Vtr[2], z4), V23 = cat(Vtr[2], Vtr[3]), V0z = cat(Vtr[0], z4);
                 f32x4 Ot[4];
 #pragma unroll
+                for (int m = 0; m < 4; ++m) Ot[m] = Yt[m] * egr[m];
+                Ot[0] = mfma32(V0z, pf[0][0], Ot[0]);
+                Ot[1] = mfma32(V01, pf[1][0], Ot[1]);
+                Ot[2] = mfma32(V2z, pf[2][1], mfma32(V01, pf[2][0], Ot[2]));
+                Ot[3] = mfma32(V23, pf[3][1], mfma32(V01, pf[3][0], Ot[3]));
+                // The registers that feed the global stores stay reserved until
+                // the next step refills them (empty asm use), so no instruction
+                // of that step waits for these stores to drain.
+                keep_alive(od);
+                uint16_t* orow = static_cast<uint16_t*>(p.o) + token(s, c) * DV + vc0 + 4 * g;
+                const int64_t mstride = static_cast<int64_t>(16) * H * DV;
+#pragma unroll
                 for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Ot[m][i] = eg[m][i] * Y[m][i];
-                }
-                Ot[0] = O_::template reg<0, 1>(Ot[0], Pm + (0 + c) * L::LDP, Vtr, g);
-                Ot[1] = O_::template reg<0, 2>(Ot[1], Pm + (16 + c) * L::LDP, Vtr, g);
-                Ot[2] = O_::template reg<0, 3>(Ot[2], Pm + (32 + c) * L::LDP, Vtr, g);
-                Ot[3] = O_::template reg<0, 4>(Ot[3], Pm + (48 + c) * L::LDP, Vtr, g);
-                // outputs through the wave's staging area (same wave: LDS
-                // accesses stay in program order), then 16-byte stores
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sV[(16 * m + 4 * g + i) * L::LDV + c] = f32_to_bf16_bits(Ot[m][i]);
-                }
-                if (lane < Cn) {
-                    uint16_t* dst = static_cast<uint16_t*>(p.o) + token(s, lane) * DV + vc0;
-                    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(sV + lane * L::LDV);
-                    *reinterpret_cast<uint4*>(dst + 8) = *reinterpret_cast<const uint4*>(sV + lane * L::LDV + 8);
+                    od[m] = to_bf16x4(Ot[m]);
+                    if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = od[m];
                 }
             }
+            if (s + 1 >= 0 && s + 1 < N) load_xy(s + 1);
             lds_barrier();
         }
         if (p.ST) {
@@ -240,211 +355,264 @@ __global__ __launch_bounds__(kThreadsP) void prefill_pipe_kernel(FwdArgs p) {
     }
 
     // ------------------------------------------------- key side (waves 2, 3)
-    // Wave 2 stages k, wave 3 stages q, beta and g, two chunks ahead.
-    const bool tb = (w == 2);
-    const void* src_qk = tb ? p.k : p.q;
-    uint4 pf[NPQ];
+    // Wave 3 stages q, k, beta and g of chunk n + 2 at the start of a step (so
+    // the loads get the whole step to land) and builds P of chunk n + 1; wave
+    // 2 builds A and T of chunk n + 1.  q and k go straight from HBM into LDS
+    // (global_load_lds: lane l of instruction j fills bytes 1024 j + 16 l of
+    // the slot, so each lane fetches the piece that the swizzle puts there);
+    // no registers are held and no LDS write instructions are spent on them.
+    // Rows past the end of the sequence hold copies of its last token: their
+    // beta is zero, which removes them from every product that reaches an
+    // output or the state.
+    const bool lw = (w == 3);   // loader and P builder; wave 2 builds T
     uint16_t pbeta = 0, pg = 0;
-    auto load_qk = [&](int n) {
+    // Per-lane element offsets of the pieces this lane fetches, relative to
+    // the first token of a chunk (32-bit; computed once).
+    constexpr int RPI = 512 / DK;   // rows per 1 KB instruction
+    constexpr int PPR = DK / 8;     // 16-byte pieces per row
+    constexpr int NJ = kCP / RPI;   // instructions per tile
+    uint32_t qk_lane_off[NJ];
 #pragma unroll
-        for (int j = 0; j < NPQ; ++j) {
-            const int pidx = lane + 64 * j;
-            const int row = pidx / CPR, cc = pidx % CPR;
-            pf[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src_qk) +
-                                                   token(n, row) * DK + cc * 8);
-        }
-        if (!tb) {
-            pbeta = static_cast<const uint16_t*>(p.beta)[token(n, lane)];
-            if constexpr (VAR == 1) pg = static_cast<const uint16_t*>(p.g)[token(n, lane)];
-        }
-    };
-    auto commit_qk = [&](int n) {
-        const int Cn = rows_in(n);
-        uint16_t* dst = tb ? kslot(n) : qslot(n);
+    for (int j = 0; j < NJ; ++j) {
+        const int r = j * RPI + lane / PPR;
+        qk_lane_off[j] = static_cast<uint32_t>(r * H * DK + 8 * ((lane % PPR) ^ swz<DK>(r)));
+    }
+    auto load_tile = [&](const uint16_t* src, uint16_t* dst, int n) {
+        if (n * kCP + kCP <= T) {   // whole chunk: wave-uniform base + lane offset
+            const uint16_t* base = src + ((tokb + n * kCP) * H + h) * DK;
 #pragma unroll
-        for (int j = 0; j < NPQ; ++j) {
-            const int pidx = lane + 64 * j;
-            const int row = pidx / CPR, cc = pidx % CPR;
-            *reinterpret_cast<uint4*>(dst + row * L::LDQ + cc * 8) = sel_rows(row < Cn, pf[j]);
-        }
-        if (!tb) {   // per-row vectors of chunk n
-            float* vec = vslot(n);
-            const bool ok = lane < Cn;
-            const float beta = ok ? bf16_bits_to_f32(pbeta) : 0.f;
-            float G = 0.f;
-            if constexpr (VAR == 1) {
-                G = ok ? bf16_bits_to_f32(pg) : 0.f;
+            for (int j = 0; j < NJ; ++j) load_to_lds16(base + qk_lane_off[j], dst + 512 * j);
+        } else {                    // last, partial chunk: rows clamped to the sequence
 #pragma unroll
-                for (int sh = 1; sh < 64; sh <<= 1) {
-                    const float y = __shfl_up(G, sh, 64);
-                    if (lane >= sh) G += y;
-                }
+            for (int j = 0; j < NJ; ++j) {
+                const int r = j * RPI + lane / PPR;
+                const int piece = (lane % PPR) ^ swz<DK>(r);
+                load_to_lds16(src + token(n, r) * DK + 8 * piece, dst + 512 * j);
             }
-            const float GC = __shfl(G, 63, 64);
-            vec[lane] = beta;
-            vec[64 + lane] = G;
-            vec[128 + lane] = VAR == 0 ? 1.f : __expf(G);
-            vec[192 + lane] = VAR == 0 ? 1.f : __expf(GC - G);
-            if (lane == 0) vec[256] = VAR == 0 ? 1.f : __expf(GC);
         }
     };
+    auto load_vec = [&](int n) {
+        pbeta = static_cast<const uint16_t*>(p.beta)[token(n, lane)];
+        if constexpr (VAR == 1) pg = static_cast<const uint16_t*>(p.g)[token(n, lane)];
+    };
+    auto commit_vec = [&](int n) {   // per-row vectors of chunk n
+        const int Cn = rows_in(n);
+        float* vec = vslot(n);
+        const bool ok = lane < Cn;
+        const float beta = ok ? bf16_bits_to_f32(pbeta) : 0.f;
+        float G = 0.f;
+        if constexpr (VAR == 1) {
+            G = ok ? bf16_bits_to_f32(pg) : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const float y = __shfl_up(G, sh, 64);
+                if (lane >= sh) G += y;
+            }
+        }
+        const float GC = __shfl(G, 63, 64);
+        vec[lane] = beta;
+        vec[64 + lane] = G;
+        vec[128 + lane] = VAR == 0 ? 1.f : __expf(G);
+        vec[192 + lane] = VAR == 0 ? 1.f : __expf(GC - G);
+        if (lane == 0) vec[256] = VAR == 0 ? 1.f : __expf(GC);
+        vec[260 + lane] = VAR == 0 ? 1.f : __expf(G - __shfl(G, lane & ~15, 64));
+#pragma unroll
+        for (int Rt = 1; Rt < 4; ++Rt)
+            vec[324 + 64 * (Rt - 1) + lane] = VAR == 0 ? 1.f : __expf(__shfl(G, 16 * Rt, 64) - G);
+    };
+    // A-operand fragment: lane (g, c) holds row 16 R + c, columns 32 kk + 8 g .. + 7
+    auto frag = [&](const uint16_t* tile, int Rt, int kk) {
+        const int r = 16 * Rt + c;
+        return *reinterpret_cast<const bf16x8*>(tile + qk_off<DK>(r, 32 * kk + 8 * g));
+    };
+    const bf16x4 z4 = {0, 0, 0, 0};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     for (int s = -2; s < N; ++s) {
         const int nl = s + 2;   // chunk staged during this step
         const int nb = s + 1;   // chunk whose T (wave 2) or P (wave 3) is built now
-        if (nl < N) load_qk(nl);
+        if (lw && nl < N) {     // stage chunk nl: the loads get the whole step to land
+            load_vec(nl);
+            load_tile(static_cast<const uint16_t*>(p.k), kslot(nl), nl);
+            load_tile(static_cast<const uint16_t*>(p.q), qslot(nl), nl);
+        }
         if (nb >= 0 && nb < N) {
-            const uint16_t* sK = kslot(nb);
             const float* vec = vslot(nb);
-            // K fragments of all four row tiles: lane (g, c) holds row 16 R + c,
-            // columns 32 kk + 8 g .. + 7
             bf16x8 kf[4][NKK];
 #pragma unroll
             for (int Rt = 0; Rt < 4; ++Rt) {
 #pragma unroll
-                for (int kk = 0; kk < NKK; ++kk)
-                    kf[Rt][kk] = *reinterpret_cast<const bf16x8*>(sK + (16 * Rt + c) * L::LDQ + 32 * kk + 8 * g);
+                for (int kk = 0; kk < NKK; ++kk) kf[Rt][kk] = frag(kslot(nb), Rt, kk);
             }
-            if (tb) {
-                // ---- A tiles.  Off-diagonal tiles are produced transposed
-                // (At_RJ[j][r] = A[16 R + r][16 J + j] in accumulator layout),
-                // which is the MFMA A-operand layout of A_RJ for the level products.
-                float bta[4], gra[4], brc, grc;
-                f32x4 At[4][4];   // [R][J], J < R
+            // per-row vectors of chunk nb: rows 16 R + c and rows 16 R + 4 g .. + 3
+            float gc[4], uc[4], bc[4];
+            f32x4 gr[4], br[4], wv[4][3];   // wv[R][J] = w_R[16 J + 4 g .. + 3]
 #pragma unroll
-                for (int Rt = 1; Rt < 4; ++Rt) {
-                    brc = vec[16 * Rt + c];
-                    grc = vec[64 + 16 * Rt + c];
+            for (int Rt = 0; Rt < 4; ++Rt) {
+                bc[Rt] = vec[16 * Rt + c];
+                gc[Rt] = vec[64 + 16 * Rt + c];
+                uc[Rt] = vec[260 + 16 * Rt + c];
+                br[Rt] = *reinterpret_cast<const f32x4*>(vec + 16 * Rt + 4 * g);
+                gr[Rt] = *reinterpret_cast<const f32x4*>(vec + 64 + 16 * Rt + 4 * g);
 #pragma unroll
-                    for (int Jt = 0; Jt < Rt; ++Jt) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Jt][kk], kf[Rt][kk], acc);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float val = acc[i] * brc;   // row 16 Rt + c, column 16 Jt + 4 g + i
-                            if constexpr (VAR == 1) val *= __expf(grc - vec[64 + 16 * Jt + 4 * g + i]);
-                            acc[i] = val;
-                        }
-                        At[Rt][Jt] = acc;
-                    }
-                }
-                // diagonal tiles, natural orientation, into LDS for the substitution
+                for (int Jt = 0; Jt < Rt; ++Jt)
+                    wv[Rt][Jt] = *reinterpret_cast<const f32x4*>(vec + 324 + 64 * (Rt - 1) + 16 * Jt + 4 * g);
+            }
+            if (!lw) {
+                // ---- diagonal blocks of A first: K_R K_R^T in accumulator
+                // layout (rows 4 g + i, column c), scaled and masked to A_RR,
+                // stored column-major (sAd[R][col][row]: one 16-byte piece per lane)
 #pragma unroll
                 for (int Rt = 0; Rt < 4; ++Rt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 acc = zero;
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Rt][kk], kf[Rt][kk], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * g + i;
-                        bta[i] = vec[16 * Rt + r];
-                        gra[i] = vec[64 + 16 * Rt + r];
-                        float val = acc[i] * bta[i];
-                        if constexpr (VAR == 1) val *= __expf(gra[i] - vec[64 + 16 * Rt + c]);
-                        sAd[(Rt * 16 + r) * 20 + c] = r > c ? val : 0.f;
+                        float val = acc[i] * br[Rt][i];
+                        if constexpr (VAR == 1) val *= __expf(gr[Rt][i] - gc[Rt]);
+                        acc[i] = (4 * g + i > c) ? val : 0.f;
+                    }
+                    *reinterpret_cast<f32x4*>(sAd + Rt * kDS + c * 20 + 4 * g) = acc;
+                }
+                // ---- diagonal blocks of T by backward substitution on the
+                // transposed system: lane (block rb, j) solves (I + A_bb)^T y = e_j,
+                // which gives row j of T_bb = (I + A_bb)^-1:
+                //   y_i = [i == j] - Σ_{m > i} A[m][i] y_m,  i = 15 .. 0
+                // The columns of A_bb are requested here; the off-diagonal A
+                // tiles are computed while they are in flight.
+                const int rb = lane >> 4, j = lane & 15;
+                const float* Ab = sAd + rb * kDS;
+                f32x4 col[16][4];
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+#pragma unroll
+                    for (int q = (i + 1) / 4; q < 4; ++q) col[i][q] = *reinterpret_cast<const f32x4*>(Ab + i * 20 + 4 * q);
+                }
+                // ---- off-diagonal A tiles.  Swapping the two operands of a
+                // product yields its transpose in accumulator layout: lane
+                // (g, c) then holds A[16 R + c][16 J + 4 g + i], the A-operand
+                // layout of the level products.
+                bf16x4 At[4][3];
+#pragma unroll
+                for (int Rt = 1; Rt < 4; ++Rt) {
+#pragma unroll
+                    for (int Jt = 0; Jt < Rt; ++Jt) {
+                        f32x4 acc = zero;
+#pragma unroll
+                        for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Jt][kk], kf[Rt][kk], acc);
+                        // beta_r e^(G_r - G_j) = (beta_r u_r) w_R[j]
+                        const float fr = bc[Rt] * uc[Rt];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] *= fr * wv[Rt][Jt][i];
+                        At[Rt][Jt] = to_bf16x4(acc);
                     }
                 }
-                // ---- diagonal blocks of T: lane (block rb, column j) solves
-                // (I + A_bb) x = e_j by columns
-                {
-                    const int rb = lane >> 4, j = lane & 15;
-                    float xs[16];
+                float y[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) xs[i] = (i == j) ? 1.f : 0.f;
+                for (int i = 15; i >= 0; --i) {
+                    float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                    for (int m = 0; m < 15; ++m) {
-#pragma unroll
-                        for (int i = m + 1; i < 16; ++i) xs[i] -= sAd[(rb * 16 + i) * 20 + m] * xs[m];
-                    }
-                    uint16_t* Te = teslot(nb);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        sTd[(rb * 16 + i) * 20 + j] = xs[i];
-                        Te[(16 * rb + i) * L::LDP + 16 * rb + j] = f32_to_bf16_bits(xs[i]);
-                    }
+                    for (int m = i + 1; m < 16; ++m) acc -= col[i][m / 4][m % 4] * y[m];
+                    y[i] = acc;
                 }
-                // ---- off-diagonal blocks: T_RJ = -T_RR (Σ_{M=J}^{R-1} A_RM T_MJ)
-                // D_J as a B operand (k = row 4 g + i, column c) and D_R as an A
-                // operand (row c, k = 4 g + i), from the fp32 diagonal blocks
-                auto dB = [&](int J) {
-                    bf16x4 r;
+                // fp32 copy (row-major sTd[b][row][col]) for the level products
+                // and the bf16 diagonal block of T
+                float* Tr = sTd + rb * kDS + j * 20;
+                uint16_t* Te = teslot(nb) + (16 * rb + j) * L::LDP + 16 * rb;
+                uint32_t hw[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) r[i] = static_cast<bf16_t>(sTd[(J * 16 + 4 * g + i) * 20 + c]);
-                    return r;
-                };
-                auto dA = [&](int Rt) {
-                    bf16x4 r;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) r[i] = static_cast<bf16_t>(sTd[(Rt * 16 + c) * 20 + 4 * g + i]);
-                    return r;
-                };
-                const bf16x4 z4 = {0, 0, 0, 0};
-                auto finish = [&](int Rt, f32x4 inner) {   // -T_RR · inner
-                    f32x4 out = {0.f, 0.f, 0.f, 0.f};
-                    out = mfma32(cat(dA(Rt), z4), cat(to_bf16x4(inner), z4), out);
-                    return -out;
-                };
-                f32x4 T10, T21, T32, T20, T31, T30;
-                {
-                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                    T10 = finish(1, mfma32(cat(to_bf16x4(At[1][0]), z4), cat(dB(0), z4), zero));
-                    T21 = finish(2, mfma32(cat(to_bf16x4(At[2][1]), z4), cat(dB(1), z4), zero));
-                    T32 = finish(3, mfma32(cat(to_bf16x4(At[3][2]), z4), cat(dB(2), z4), zero));
-                    T20 = finish(2, mfma32(cat(to_bf16x4(At[2][0]), to_bf16x4(At[2][1])),
-                                           cat(dB(0), to_bf16x4(T10)), zero));
-                    T31 = finish(3, mfma32(cat(to_bf16x4(At[3][1]), to_bf16x4(At[3][2])),
-                                           cat(dB(1), to_bf16x4(T21)), zero));
-                    f32x4 in30 = mfma32(cat(to_bf16x4(At[3][0]), to_bf16x4(At[3][1])),
-                                        cat(dB(0), to_bf16x4(T10)), zero);
-                    in30 = mfma32(cat(to_bf16x4(At[3][2]), z4), cat(to_bf16x4(T20), z4), in30);
-                    T30 = finish(3, in30);
+                for (int q = 0; q < 4; ++q) {
+                    *reinterpret_cast<f32x4*>(Tr + 4 * q) = f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+                    hw[2 * q] = static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q])) |
+                                (static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q + 1])) << 16);
+                    hw[2 * q + 1] = static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q + 2])) |
+                                    (static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q + 3])) << 16);
                 }
-                uint16_t* Te = teslot(nb);
-                auto put = [&](int Rt, int Jt, f32x4 t) {
+                // written through a float vector type: type-based alias analysis
+                // then separates these stores from the global-to-LDS loads in
+                // flight (they target q/k slots), so no wait for them is inserted
+                *reinterpret_cast<f32x4*>(Te) = __builtin_bit_cast(f32x4, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                *reinterpret_cast<f32x4*>(Te + 8) = __builtin_bit_cast(f32x4, make_uint4(hw[4], hw[5], hw[6], hw[7]));
+                // ---- off-diagonal blocks: T_RJ = -T_RR (Σ_{M=J}^{R-1} A_RM T_MJ).
+                // T_RR as an A operand (lane (g, c): row c, columns 4 g + i) is
+                // one 16-byte read of the row-major copy; T_JJ as a B operand
+                // (rows 4 g + i, column c) is four scalar reads.
+                bf16x4 dA[4], dB[3];
+#pragma unroll
+                for (int Rt = 1; Rt < 4; ++Rt)
+                    dA[Rt] = to_bf16x4(*reinterpret_cast<const f32x4*>(sTd + Rt * kDS + c * 20 + 4 * g));
+#pragma unroll
+                for (int Jt = 0; Jt < 3; ++Jt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dB[Jt][i] = static_cast<bf16_t>(sTd[Jt * kDS + (4 * g + i) * 20 + c]);
+                }
+                // -T_RR · inner in accumulator layout (rows 4 g + i, column c) ...
+                auto finish = [&](int Rt, f32x4 inner) {
+                    return -mfma32(cat(dA[Rt], z4), cat(to_bf16x4(inner), z4), zero);
+                };
+                // ... or transposed (lane (g, c): row c, columns 4 g + i)
+                auto finishT = [&](int Rt, f32x4 inner) {
+                    return -mfma32(cat(to_bf16x4(inner), z4), cat(dA[Rt], z4), zero);
+                };
+                const f32x4 T10 = finish(1, mfma32(cat(At[1][0], z4), cat(dB[0], z4), zero));
+                const f32x4 T21 = finish(2, mfma32(cat(At[2][1], z4), cat(dB[1], z4), zero));
+                const f32x4 T32t = finishT(3, mfma32(cat(At[3][2], z4), cat(dB[2], z4), zero));
+                const f32x4 T20 = finish(2, mfma32(cat(At[2][0], At[2][1]), cat(dB[0], to_bf16x4(T10)), zero));
+                const f32x4 T31t = finishT(3, mfma32(cat(At[3][1], At[3][2]), cat(dB[1], to_bf16x4(T21)), zero));
+                f32x4 in30 = mfma32(cat(At[3][0], At[3][1]), cat(dB[0], to_bf16x4(T10)), zero);
+                in30 = mfma32(cat(At[3][2], z4), cat(to_bf16x4(T20), z4), in30);
+                const f32x4 T30t = finishT(3, in30);
+                uint16_t* Tm = teslot(nb);
+                auto put = [&](int Rt, int Jt, f32x4 t) {   // accumulator layout
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        Te[(16 * Rt + 4 * g + i) * L::LDP + 16 * Jt + c] = f32_to_bf16_bits(t[i]);
+                        Tm[(16 * Rt + 4 * g + i) * L::LDP + 16 * Jt + c] = f32_to_bf16_bits(t[i]);
+                };
+                auto putT = [&](int Rt, int Jt, f32x4 t) {  // transposed layout: one 8-byte write
+                    *reinterpret_cast<bf16x4*>(Tm + (16 * Rt + c) * L::LDP + 16 * Jt + 4 * g) = to_bf16x4(t);
                 };
                 put(1, 0, T10);
                 put(2, 1, T21);
-                put(3, 2, T32);
                 put(2, 0, T20);
-                put(3, 1, T31);
-                put(3, 0, T30);
+                putT(3, 2, T32t);
+                putT(3, 1, T31t);
+                putT(3, 0, T30t);
             } else {
-                // ---- P = Tril(Q K^T ⊙ Gamma) from register fragments
-                const uint16_t* sQ = qslot(nb);
+                // ---- P = Tril(Q K^T ⊙ Gamma), transposed products: lane (g, c)
+                // holds P[16 R + c][16 J + 4 g + i] and writes it as one 8-byte piece
                 bf16x8 qf[4][NKK];
 #pragma unroll
                 for (int Rt = 0; Rt < 4; ++Rt) {
 #pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk)
-                        qf[Rt][kk] = *reinterpret_cast<const bf16x8*>(sQ + (16 * Rt + c) * L::LDQ + 32 * kk + 8 * g);
+                    for (int kk = 0; kk < NKK; ++kk) qf[Rt][kk] = frag(qslot(nb), Rt, kk);
                 }
                 uint16_t* Pm = pslot(nb);
 #pragma unroll
                 for (int Rt = 0; Rt < 4; ++Rt) {
 #pragma unroll
                     for (int Jt = 0; Jt <= Rt; ++Jt) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        f32x4 acc = zero;
 #pragma unroll
-                        for (int kk = 0; kk < NKK; ++kk) acc = mfma32(qf[Rt][kk], kf[Jt][kk], acc);
-                        const int col = 16 * Jt + c;
-                        const float gcol = vec[64 + col];
+                        for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Jt][kk], qf[Rt][kk], acc);
+                        if (Jt < Rt) {   // e^(G_r - G_j) = u_r w_R[j]
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = 16 * Rt + 4 * g + i;
-                            float val = acc[i];
-                            if constexpr (VAR == 1) val *= __expf(vec[64 + row] - gcol);
-                            Pm[row * L::LDP + col] = f32_to_bf16_bits(row >= col ? val : 0.f);
+                            for (int i = 0; i < 4; ++i) acc[i] *= uc[Rt] * wv[Rt][Jt][i];
+                        } else {         // diagonal block: masked, exact exponent
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                float val = acc[i];
+                                if constexpr (VAR == 1) val *= __expf(gc[Rt] - gr[Jt][i]);
+                                acc[i] = (c >= 4 * g + i) ? val : 0.f;
+                            }
                         }
+                        *reinterpret_cast<bf16x4*>(Pm + (16 * Rt + c) * L::LDP + 16 * Jt + 4 * g) = to_bf16x4(acc);
                     }
                 }
             }
         }
-        if (nl < N) commit_qk(nl);
-        lds_barrier();
+        if (lw && nl < N) commit_vec(nl);
+        dma_lds_barrier();
     }
 }
 
