@@ -6,8 +6,10 @@
 // state: one workgroup per (batch, head) state matrix, 256 threads in eight
 // 32-lane groups, each group owning every eighth value row.  A lane holds
 // d_k/32 consecutive key columns of each of its rows, so every row is one
-// coalesced 512-byte (d_k = 128) read and write.  All row loads are issued
-// before any arithmetic.
+// coalesced 512-byte (d_k = 128) read and write.  The small per-token
+// operands are requested first, then every state row; the rows are finished
+// in two batches, so the first batch's writes overlap the second batch's
+// reads.
 //
 // Per row i (value channel) with a = exp(g) and S' = S·Diag(a):
 //   r_i  = S'_i · k          (read)        s_i = S'_i · q
@@ -28,8 +30,7 @@ template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     constexpr int CPL = DK / 32;       // key columns per lane
     constexpr int RPG = DV / 8;        // rows per 32-lane group
-    constexpr int NVAL = 2 * RPG;      // partial dot products to reduce per lane
-    static_assert(NVAL == 16 || NVAL == 32, "row layout");
+    static_assert(RPG == 8 || RPG == 16, "row layout");
     const int bh = blockIdx.x;         // b * H + h
     const int grp = threadIdx.x >> 5;  // 0..7
     const int li = threadIdx.x & 31;
@@ -38,7 +39,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
 
     float* S = p.S + static_cast<int64_t>(bh) * DV * DK;
 
-    // Issue the state loads first: they dominate the kernel's time.
+    // The small per-token operands first, then every state row: the rows
+    // arrive in issue order, so the first batch below waits only for its own.
+    float kk[CPL], qq[CPL], aa[CPL], bk[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        kk[c] = load_elem<E>(p.k, tok * DK + c0 + c);
+        qq[c] = load_elem<E>(p.q, tok * DK + c0 + c);
+        if constexpr (VAR == 0) {
+            aa[c] = 0.0f;
+        } else if constexpr (VAR == 1) {
+            aa[c] = load_elem<E>(p.g, tok);
+        } else {
+            aa[c] = load_elem<E>(p.g, tok * DK + c0 + c);
+        }
+        if constexpr (VAR == 3) bk[c] = load_elem<E>(p.beta, tok * DK + c0 + c);
+        else bk[c] = 0.0f;
+    }
+    float beta_s = 0.f;
+    if constexpr (VAR != 3) beta_s = load_elem<E>(p.beta, tok);
     float st[RPG][CPL];
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
@@ -51,21 +70,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
             st[j][0] = x.x; st[j][1] = x.y;
         }
     }
-
-    float kk[CPL], qq[CPL], aa[CPL], bk[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        kk[c] = load_elem<E>(p.k, tok * DK + c0 + c);
-        qq[c] = load_elem<E>(p.q, tok * DK + c0 + c);
-        if constexpr (VAR == 0) {
-            aa[c] = 1.0f;
-        } else if constexpr (VAR == 1) {
-            aa[c] = __expf(load_elem<E>(p.g, tok));
-        } else {
-            aa[c] = __expf(load_elem<E>(p.g, tok * DK + c0 + c));
-        }
-        if constexpr (VAR == 3) bk[c] = load_elem<E>(p.beta, tok * DK + c0 + c) * kk[c];
-        else bk[c] = 0.0f;
+        aa[c] = VAR == 0 ? 1.0f : __expf(aa[c]);
+        if constexpr (VAR == 3) bk[c] *= kk[c];
     }
     float kq = 0.f, bkq = 0.f;
 #pragma unroll
@@ -76,82 +84,87 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     kq = half_wave_sum(kq);
     if constexpr (VAR == 3) bkq = half_wave_sum(bkq);
 
-    // Decay and the two partial dot products of every row.
-    float val[NVAL];
+    // Rows in two batches: the first batch is reduced, updated and written
+    // back while the second batch's loads are still arriving.
+    constexpr int RB = RPG / 2;        // rows per batch
+    constexpr int NV = 2 * RB;         // partial dot products per lane and batch
 #pragma unroll
-    for (int j = 0; j < RPG; ++j) {
-        float r = 0.f, s = 0.f;
+    for (int bt = 0; bt < 2; ++bt) {
+        float val[NV];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            st[j][c] *= aa[c];
-            r += st[j][c] * kk[c];
-            s += st[j][c] * qq[c];
-        }
-        val[j] = r;
-        val[RPG + j] = s;
-    }
-    // Transpose-reduce across the 32 lanes: each step halves the number of
-    // values a lane carries; at the end lane li holds the full sum of value
-    // index (li >> (5 - log2 NVAL)).
-    int n = NVAL;
+        for (int jj = 0; jj < RB; ++jj) {
+            const int j = bt * RB + jj;
+            float r = 0.f, s = 0.f;
 #pragma unroll
-    for (int s = 16; s >= 1; s >>= 1) {
-        if (n > 1) {
-            const bool upper = (li & s) != 0;
-#pragma unroll
-            for (int i = 0; i < n / 2; ++i) {
-                float keep = upper ? val[n / 2 + i] : val[i];
-                float send = upper ? val[i] : val[n / 2 + i];
-                val[i] = keep + __shfl_xor(send, s, 32);
+            for (int c = 0; c < CPL; ++c) {
+                st[j][c] *= aa[c];
+                r += st[j][c] * kk[c];
+                s += st[j][c] * qq[c];
             }
-            n >>= 1;
-        } else {
-            val[0] += __shfl_xor(val[0], s, 32);
+            val[jj] = r;
+            val[RB + jj] = s;
         }
-    }
-    constexpr int kShift = (NVAL == 32) ? 0 : 1;
-    const int idx = li >> kShift;               // value index this lane holds
-    // r of row idx sits at value idx, s of row idx at value RPG + idx.
-    const float other = __shfl_xor(val[0], RPG << kShift, 32);
-    const bool owner = idx < RPG && (li & ((1 << kShift) - 1)) == 0;
-    const int orow = grp + 8 * idx;             // value row this lane finishes
-    float coef_u = 0.f, coef_x = 0.f;           // per-row update coefficients
-    if (idx < RPG) {
-        const float r = val[0], s = other;
-        const float vi = load_elem<E>(p.v, tok * DV + orow);
-        float o;
-        if constexpr (VAR == 3) {
-            const float x = load_elem<E>(p.wgate, tok * DV + orow) * vi;
-            coef_u = r;
-            coef_x = x;
-            o = s - r * bkq + x * kq;
-        } else {
-            const float beta = load_elem<E>(p.beta, tok);
-            const float u = beta * (vi - r);
-            coef_u = u;
-            o = s + u * kq;
-        }
-        if (owner) store_elem<E>(p.o, tok * DV + orow, o);
-    }
-
-    // Broadcast the per-row coefficients and write the new rows.
+        // Transpose-reduce across the 32 lanes: each step halves the number of
+        // values a lane carries; at the end lane li holds the full sum of value
+        // index (li >> (5 - log2 NV)).
+        int n = NV;
 #pragma unroll
-    for (int j = 0; j < RPG; ++j) {
-        const int src = j << kShift;
-        const float u = __shfl(coef_u, src, 32);
-        float x = 0.f;
-        if constexpr (VAR == 3) x = __shfl(coef_x, src, 32);
-        float* row = S + static_cast<int64_t>(grp + 8 * j) * DK + c0;
-        float out[CPL];
+        for (int sh = 16; sh >= 1; sh >>= 1) {
+            if (n > 1) {
+                const bool upper = (li & sh) != 0;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            if constexpr (VAR == 3) out[c] = st[j][c] - u * bk[c] + x * kk[c];
-            else out[c] = st[j][c] + u * kk[c];
+                for (int i = 0; i < n / 2; ++i) {
+                    float keep = upper ? val[n / 2 + i] : val[i];
+                    float send = upper ? val[i] : val[n / 2 + i];
+                    val[i] = keep + __shfl_xor(send, sh, 32);
+                }
+                n >>= 1;
+            } else {
+                val[0] += __shfl_xor(val[0], sh, 32);
+            }
         }
-        if constexpr (CPL == 4) {
-            *reinterpret_cast<float4*>(row) = make_float4(out[0], out[1], out[2], out[3]);
-        } else {
-            *reinterpret_cast<float2*>(row) = make_float2(out[0], out[1]);
+        constexpr int kShift = (NV == 16) ? 1 : 2;  // lanes per value index
+        const int idx = li >> kShift;               // value index this lane holds
+        // r of row idx sits at value idx, s of row idx at value RB + idx.
+        const float other = __shfl_xor(val[0], RB << kShift, 32);
+        const bool owner = idx < RB && (li & ((1 << kShift) - 1)) == 0;
+        const int orow = grp + 8 * (bt * RB + idx);  // value row this lane finishes
+        float coef_u = 0.f, coef_x = 0.f;
+        if (idx < RB) {
+            const float r = val[0], s = other;
+            const float vi = load_elem<E>(p.v, tok * DV + orow);
+            float o;
+            if constexpr (VAR == 3) {
+                const float x = load_elem<E>(p.wgate, tok * DV + orow) * vi;
+                coef_u = r;
+                coef_x = x;
+                o = s - r * bkq + x * kq;
+            } else {
+                const float u = beta_s * (vi - r);
+                coef_u = u;
+                o = s + u * kq;
+            }
+            if (owner) store_elem<E>(p.o, tok * DV + orow, o);
+        }
+#pragma unroll
+        for (int jj = 0; jj < RB; ++jj) {
+            const int j = bt * RB + jj;
+            const int src = jj << kShift;
+            const float u = __shfl(coef_u, src, 32);
+            float x = 0.f;
+            if constexpr (VAR == 3) x = __shfl(coef_x, src, 32);
+            float* row = S + static_cast<int64_t>(grp + 8 * j) * DK + c0;
+            float out[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                if constexpr (VAR == 3) out[c] = st[j][c] - u * bk[c] + x * kk[c];
+                else out[c] = st[j][c] + u * kk[c];
+            }
+            if constexpr (CPL == 4) {
+                *reinterpret_cast<float4*>(row) = make_float4(out[0], out[1], out[2], out[3]);
+            } else {
+                *reinterpret_cast<float2*>(row) = make_float2(out[0], out[1]);
+            }
         }
     }
 }
