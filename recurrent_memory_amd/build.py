@@ -19,8 +19,11 @@ LIB = os.path.join(PKG, "libdeltarule.so")
 SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "prefill_cw.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -amdgpu-mfma-vgpr-form: MFMA results go to VGPRs, where the epilogues read
+# them, instead of AGPRs plus a v_accvgpr_read per element.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-result"]
 
 

@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                     *reinterpret_cast<uint4*>(sV + lane * L::LDV + 8) = sel_rows(ok, pv1);
                 }
                 if (s + 1 < N) vload(s + 1);
+                load_xy(s);
                 const uint16_t* sK = kslot(s);
                 const uint16_t* Te = teslot(s);
                 const uint16_t* Pm = pslot(s);
@@ -341,7 +342,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                     if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = od[m];
                 }
             }
-            if (s + 1 >= 0 && s + 1 < N) load_xy(s + 1);
             lds_barrier();
         }
         if (p.ST) {
