@@ -60,6 +60,29 @@ __device__ __forceinline__ bf16x4 tr_read(const uint16_t* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p)));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves only (no
+// LDS-pipe instructions, so nothing here is ordered behind loads into LDS):
+// shifts within each 16-lane row, then the last lane of a row is broadcast to
+// the rows after it.  DPP controls: row_shr:n = 0x110 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143; lanes without a source read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_move<0x111, 0xf>(x);
+    x += dpp_move<0x112, 0xf>(x);
+    x += dpp_move<0x114, 0xf>(x);
+    x += dpp_move<0x118, 0xf>(x);
+    x += dpp_move<0x142, 0xa>(x);
+    x += dpp_move<0x143, 0xc>(x);
+    return x;
+}
+// value of x in lane l (wave-uniform result)
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l writes bytes
 // 16 l .. 16 l + 15 after the wave-uniform address lds.  Completion is counted
 // by vmcnt, like any global load.
@@ -71,6 +94,11 @@ __device__ __forceinline__ void load_to_lds16(const uint16_t* src, uint16_t* lds
 // landed (vmcnt) before other waves may read it.
 __device__ __forceinline__ void dma_lds_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Empty use of four loaded words (forces the loads to complete here).
+__device__ __forceinline__ void keep_alive_u32x4(const uint32_t (&v)[4]) {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
 }
 
 // Empty use that keeps four 8-byte register values (and their registers) live.
@@ -365,6 +393,20 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     // beta is zero, which removes them from every product that reaches an
     // output or the state.
     const bool lw = (w == 3);   // loader and P builder; wave 2 builds T
+    // Wave 3 also touches one 4-byte word per 128-byte line of q and k of
+    // chunk n + 3 (before its loads of chunk n + 2), so those lines are in L2
+    // when they are staged a step later.  The words are consumed by an empty
+    // asm after the end-of-step wait, so the loads are kept and cost no wait.
+    uint32_t touch[4] = {0u, 0u, 0u, 0u};
+    const uint32_t touch_off = static_cast<uint32_t>((lane >> 1) * H * DK + 64 * (lane & 1));
+    auto l2_touch = [&](int n) {   // whole chunks only
+        const int64_t base = ((tokb + n * kCP) * H + h) * DK;
+        const uint32_t half = 32u * H * DK;   // rows 32..63
+        touch[0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k) + base + touch_off);
+        touch[1] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k) + base + half + touch_off);
+        touch[2] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + base + touch_off);
+        touch[3] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + base + half + touch_off);
+    };
     uint16_t pbeta = 0, pg = 0;
     // Per-lane element offsets of the pieces this lane fetches, relative to
     // the first token of a chunk (32-bit; computed once).
@@ -401,24 +443,20 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         const bool ok = lane < Cn;
         const float beta = ok ? bf16_bits_to_f32(pbeta) : 0.f;
         float G = 0.f;
-        if constexpr (VAR == 1) {
-            G = ok ? bf16_bits_to_f32(pg) : 0.f;
-#pragma unroll
-            for (int sh = 1; sh < 64; sh <<= 1) {
-                const float y = __shfl_up(G, sh, 64);
-                if (lane >= sh) G += y;
-            }
-        }
-        const float GC = __shfl(G, 63, 64);
+        if constexpr (VAR == 1) G = wave_prefix_sum(ok ? bf16_bits_to_f32(pg) : 0.f);
+        // G at lanes 0, 16, 32, 48 (block starts) and 63 (chunk end)
+        const float G0 = lane_value(G, 0), G16 = lane_value(G, 16), G32 = lane_value(G, 32),
+                    G48 = lane_value(G, 48), GC = lane_value(G, 63);
+        const float Gb = lane < 16 ? G0 : lane < 32 ? G16 : lane < 48 ? G32 : G48;
         vec[lane] = beta;
         vec[64 + lane] = G;
         vec[128 + lane] = VAR == 0 ? 1.f : __expf(G);
         vec[192 + lane] = VAR == 0 ? 1.f : __expf(GC - G);
         if (lane == 0) vec[256] = VAR == 0 ? 1.f : __expf(GC);
-        vec[260 + lane] = VAR == 0 ? 1.f : __expf(G - __shfl(G, lane & ~15, 64));
-#pragma unroll
-        for (int Rt = 1; Rt < 4; ++Rt)
-            vec[324 + 64 * (Rt - 1) + lane] = VAR == 0 ? 1.f : __expf(__shfl(G, 16 * Rt, 64) - G);
+        vec[260 + lane] = VAR == 0 ? 1.f : __expf(G - Gb);
+        vec[324 + lane] = VAR == 0 ? 1.f : __expf(G16 - G);
+        vec[388 + lane] = VAR == 0 ? 1.f : __expf(G32 - G);
+        vec[452 + lane] = VAR == 0 ? 1.f : __expf(G48 - G);
     };
     // A-operand fragment: lane (g, c) holds row 16 R + c, columns 32 kk + 8 g .. + 7
     auto frag = [&](const uint16_t* tile, int Rt, int kk) {
@@ -431,6 +469,7 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     for (int s = -2; s < N; ++s) {
         const int nl = s + 2;   // chunk staged during this step
         const int nb = s + 1;   // chunk whose T (wave 2) or P (wave 3) is built now
+        if (lw && (s + 3) * kCP + kCP <= T) l2_touch(s + 3);
         if (lw && nl < N) {     // stage chunk nl: the loads get the whole step to land
             load_vec(nl);
             load_tile(static_cast<const uint16_t*>(p.k), kslot(nl), nl);
@@ -613,6 +652,7 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         }
         if (lw && nl < N) commit_vec(nl);
         dma_lds_barrier();
+        if (lw) keep_alive_u32x4(touch);
     }
 }
 
