@@ -42,9 +42,10 @@
 // The sub-chunk is 32 tokens for bf16 inputs (two 16-token blocks) and 16
 // for fp32 inputs; the result does not depend on the sub-chunk length in exact
 // arithmetic.  Work decomposition, operand layouts and the register-tile
-// contractions are those of the scalar-decay kernel: one workgroup of four
-// waves per (batch, head, 64 value columns), each wave owning 16 columns of
-// the fp32 state in MFMA accumulators for the whole sequence.
+// contractions are those of the scalar-decay kernels: one workgroup of four
+// waves per (batch, head, 16 value columns); the four waves share the
+// key-side work and wave 0 keeps the 128 x 16 slice of the fp32 state in MFMA
+// accumulators for the whole sequence.
 #include "chunk_ops.h"
 #include "common.h"
 #include "kernels.h"
@@ -54,7 +55,11 @@ namespace {
 
 constexpr int kWavesCW = 4;
 constexpr int kThreadsCW = 64 * kWavesCW;
-constexpr int kVTCW = 16 * kWavesCW;
+// Value columns per workgroup: one 16-column tile, whose state wave 0 carries.
+// The four waves share the key-side work of every sub-chunk; a narrow value
+// tile gives B * H * d_v / 16 workgroups, enough to fill the chip for the
+// head counts of the channel-wise workloads.
+constexpr int kVTCW = 16;
 
 template <typename E, int DK, int NB, bool SPLIT>
 struct LayoutCW {
@@ -142,11 +147,12 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int vc0 = vt * kVTCW + 16 * w;
+    const int vc0 = vt * kVTCW;
+    const bool chain = (w == 0);   // the wave that carries the state
 
     f32x4 ST[NKT];
     {
-        const float* s0 = p.S0 ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
+        const float* s0 = (p.S0 && chain) ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
             if (s0) {
@@ -259,81 +265,165 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
         lds_barrier();
         if (n + 1 < nchunks) prefetch(n + 1);
 
-        // ---- per channel: cumulative decay and the decay-carrying key copies
-        for (int ch = tid; ch < DK; ch += kThreadsCW) {
-            auto ld = [&](const S* m, int r) -> float {
-                if constexpr (kBF) return bf16_bits_to_f32(m[r * L::LDK + ch]);
-                else return m[r * L::LDK + ch];
+        // ---- per channel: cumulative decay and the decay-carrying key copies.
+        // Thread (channel pair cp, row group rq): channels 2 cp, 2 cp + 1 and
+        // RPT consecutive rows; the NRQ row groups of a channel pair are
+        // adjacent lanes, which exchange their partial decay sums by shuffles.
+        {
+            constexpr int NRQ = 2 * kThreadsCW / DK;   // row groups per channel pair
+            constexpr int RPT = C / NRQ;               // rows per thread
+            static_assert(RPT >= 1 && C % NRQ == 0 && 16 % RPT == 0, "row split");
+            const int rq = tid % NRQ, cp = tid / NRQ;
+            const int ch = 2 * cp, r0 = rq * RPT;
+            auto ld2 = [&](const S* m, int r) -> float2 {
+                const S* q = m + r * L::LDK + ch;
+                if constexpr (kBF) {
+                    const uint32_t u = *reinterpret_cast<const uint32_t*>(q);
+                    return make_float2(bf16_bits_to_f32(static_cast<uint16_t>(u & 0xffffu)),
+                                       bf16_bits_to_f32(static_cast<uint16_t>(u >> 16)));
+                } else {
+                    return *reinterpret_cast<const float2*>(q);
+                }
             };
-            float G[C];
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < C; ++r) {
-                acc += ld(sRawG, r);
-                G[r] = acc;
-            }
-            const float GC = G[C - 1];
-#pragma unroll
-            for (int r = 0; r < C; ++r) {
-                const int Rb = r / 16;
-                const float Gb = Rb == 0 ? 0.f : G[16 * Rb - 1];
-                const float kv = ld(sKh, r), qv = ld(sQh, r);
-                const float fh = __expf(G[r] - Gb);
-                const float fi = __expf(Gb - G[r]);
-                const float fc = __expf(GC - G[r]);
-                sKh[r * L::LDK + ch] = O_::enc(kv * fh);
-                const float qh = qv * fh;
-                sQh[r * L::LDK + ch] = O_::enc(qh);
-                if constexpr (kBF) sQl[r * L::LDK + ch] = O_::enc(qh - bf16_bits_to_f32(O_::enc(qh)));
-                sKi[r * L::LDK + ch] = O_::enc(kv * fi);
-                sKb[r * L::LDK + ch] = O_::enc(kv * fc);
-                float fe = 0.f;
-                if (Rb < NB - 1) {
-                    fe = __expf(G[16 * Rb + 15] - G[r]);
-                    sKe[r * L::LDK + ch] = O_::enc(kv * fe);
+            auto st2 = [&](S* m, int r, float x0, float x1) {
+                S* q = m + r * L::LDK + ch;
+                if constexpr (kBF) {
+                    *reinterpret_cast<uint32_t*>(q) = static_cast<uint32_t>(O_::enc(x0)) |
+                                                      (static_cast<uint32_t>(O_::enc(x1)) << 16);
+                } else {
+                    *reinterpret_cast<float2*>(q) = make_float2(x0, x1);
                 }
+            };
+            // raw log-decays of this thread's rows and their sum
+            float g0[RPT], g1[RPT];
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const float2 v = ld2(sRawG, r0 + j);
+                g0[j] = v.x;
+                g1[j] = v.y;
+                p0 += v.x;
+                p1 += v.y;
+            }
+            // exclusive prefix over the row groups, and the block-start and
+            // chunk-end values (G is the running sum of the raw log-decays)
+            float e0 = 0.f, e1 = 0.f, tot0 = 0.f, tot1 = 0.f, bs0 = 0.f, bs1 = 0.f;
+            const int my_block = r0 / 16;
+#pragma unroll
+            for (int q = 0; q < NRQ; ++q) {
+                const float s0 = __shfl(p0, (lane & ~(NRQ - 1)) + q, 64);
+                const float s1 = __shfl(p1, (lane & ~(NRQ - 1)) + q, 64);
+                if (q < rq) { e0 += s0; e1 += s1; }
+                if (q * RPT < 16 * my_block) { bs0 += s0; bs1 += s1; }
+                tot0 += s0;
+                tot1 += s1;
+            }
+            const float GC0 = tot0, GC1 = tot1;
+            // end of block 0 (the only block that has a next block when NB = 2)
+            float end0 = 0.f, end1 = 0.f;
+            if constexpr (NB > 1) {
+#pragma unroll
+                for (int q = 0; q < NRQ; ++q) {
+                    const float s0 = __shfl(p0, (lane & ~(NRQ - 1)) + q, 64);
+                    const float s1 = __shfl(p1, (lane & ~(NRQ - 1)) + q, 64);
+                    if (q * RPT < 16) { end0 += s0; end1 += s1; }
+                }
+            }
+            // e^(G_end(R) - G_b(R)) for this thread's block (rows of block 0 only)
+            const float eb0 = NB > 1 ? __expf(end0 - bs0) : 0.f, eb1 = NB > 1 ? __expf(end1 - bs1) : 0.f;
+            float G0 = e0, G1 = e1;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const int r = r0 + j;
+                G0 += g0[j];
+                G1 += g1[j];
+                const float2 kv = ld2(sKh, r), qv = ld2(sQh, r);
+                const float fh0 = __expf(G0 - bs0), fh1 = __expf(G1 - bs1);
+                const float fi0 = __expf(bs0 - G0), fi1 = __expf(bs1 - G1);
+                const float fc0 = __expf(GC0 - G0), fc1 = __expf(GC1 - G1);
+                st2(sKh, r, kv.x * fh0, kv.y * fh1);
+                const float qh0 = qv.x * fh0, qh1 = qv.y * fh1;
+                st2(sQh, r, qh0, qh1);
+                if constexpr (kBF)
+                    st2(sQl, r, qh0 - bf16_bits_to_f32(O_::enc(qh0)), qh1 - bf16_bits_to_f32(O_::enc(qh1)));
+                st2(sKi, r, kv.x * fi0, kv.y * fi1);
+                st2(sKb, r, kv.x * fc0, kv.y * fc1);
+                // e^(G_end - G_r) = e^(G_b - G_r) e^(G_end - G_b), both within one block
+                const float fe0 = fi0 * eb0, fe1 = fi1 * eb1;
+                if (my_block < NB - 1) st2(sKe, r, kv.x * fe0, kv.y * fe1);
                 if constexpr (SPLIT) {
-                    const float ev = ld(sRawB, r) * kv;
-                    sEi[r * L::LDK + ch] = O_::enc(ev * fi);
-                    sEb[r * L::LDK + ch] = O_::enc(ev * fc);
-                    if (Rb < NB - 1) sEe[r * L::LDK + ch] = O_::enc(ev * fe);
+                    const float2 bv = ld2(sRawB, r);
+                    const float ev0 = bv.x * kv.x, ev1 = bv.y * kv.y;
+                    st2(sEi, r, ev0 * fi0, ev1 * fi1);
+                    st2(sEb, r, ev0 * fc0, ev1 * fc1);
+                    if (my_block < NB - 1) st2(sEe, r, ev0 * fe0, ev1 * fe1);
                 }
             }
-#pragma unroll
-            for (int R = 0; R < NB; ++R) sEgb[R * DK + ch] = R == 0 ? 1.f : __expf(G[16 * R - 1]);
-            sGam[ch] = __expf(GC);
+            if (rq == 0) {
+                sEgb[ch] = 1.f;
+                sEgb[ch + 1] = 1.f;
+                if constexpr (NB > 1) {
+                    sEgb[DK + ch] = __expf(end0);
+                    sEgb[DK + ch + 1] = __expf(end1);
+                }
+                sGam[ch] = __expf(GC0);
+                sGam[ch + 1] = __expf(GC1);
+            }
         }
         lds_barrier();
 
-        // ---- C x C products over 16x16 tiles (R, J), J <= R
+        // ---- C x C products over 16x16 tiles (R, J), J <= R.  Tasks (matrix,
+        // tile) go round-robin over the waves; a wave requests the operand
+        // fragments of all its tasks before its first MFMA.
         {
             constexpr int NTILE = NB * (NB + 1) / 2;
             constexpr int NMAT = SPLIT ? 4 : 2;
-            for (int task = w; task < NTILE * NMAT; task += kWavesCW) {
-                const int mat = task / NTILE, tix = task % NTILE;
-                const int Rr = tix == 0 ? 0 : (tix == 1 ? 1 : 1);
-                const int Jr = tix == 0 ? 0 : (tix == 1 ? 0 : 1);
-                // mat 0: A (or A_e)   1: P (or M_k)   2: A_k   3: M_e
-                const bool useQ = mat == 1 || mat == 3;
-                const bool useE = SPLIT && (mat == 0 || mat == 3);
-                const S* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
-                const S* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
-                const S* brow = bsrc + (16 * Jr + c) * L::LDK;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = O_::template nat<DK>(acc, arow, brow, g);
-                if (kBF && useQ) acc = O_::template nat<DK>(acc, sQl + (16 * Rr + c) * L::LDK, brow, g);
-                const bool strict = mat == 0 || mat == 2;
-                const int col = 16 * Jr + c;
+            constexpr int NTASK = NTILE * NMAT;
+            constexpr int MAXT = (NTASK + kWavesCW - 1) / kWavesCW;
+            constexpr int NKF = DK / 32;
+            // mat 0: A (or A_e)   1: P (or M_k)   2: A_k   3: M_e
+            auto task_rj = [](int tix, int& Rr, int& Jr) {
+                Rr = tix == 0 ? 0 : 1;
+                Jr = tix == 2 ? 1 : 0;
+            };
+            f32x4 acc[MAXT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * Rr + 4 * g + i;
-                    float val = acc[i];
-                    if (!SPLIT && mat == 0) val *= sBeta[row];
-                    val = (strict ? row > col : row >= col) ? val : 0.f;
-                    if (mat == 0) sA[row * L::LDF + col] = val;
-                    else if (mat == 1) sP[row * L::LDM + col] = O_::enc(val);
-                    else if (mat == 2) sAk[row * L::LDM + col] = O_::enc(val);
-                    else sMe[row * L::LDM + col] = O_::enc(val);
+            for (int k = 0; k < MAXT; ++k) {
+                const int task = w + kWavesCW * k;
+                acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (task < NTASK) {
+                    const int mat = task / NTILE, tix = task % NTILE;
+                    int Rr, Jr;
+                    task_rj(tix, Rr, Jr);
+                    const bool useQ = mat == 1 || mat == 3;
+                    const bool useE = SPLIT && (mat == 0 || mat == 3);
+                    const S* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
+                    const S* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
+                    const S* brow = bsrc + (16 * Jr + c) * L::LDK;
+                    acc[k] = O_::template nat<DK>(acc[k], arow, brow, g);
+                    if (kBF && useQ) acc[k] = O_::template nat<DK>(acc[k], sQl + (16 * Rr + c) * L::LDK, brow, g);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < MAXT; ++k) {
+                const int task = w + kWavesCW * k;
+                if (task < NTASK) {
+                    const int mat = task / NTILE, tix = task % NTILE;
+                    int Rr, Jr;
+                    task_rj(tix, Rr, Jr);
+                    const bool strict = mat == 0 || mat == 2;
+                    const int col = 16 * Jr + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * Rr + 4 * g + i;
+                        float val = acc[k][i];
+                        if (!SPLIT && mat == 0) val *= sBeta[row];
+                        val = (strict ? row > col : row >= col) ? val : 0.f;
+                        if (mat == 0) sA[row * L::LDF + col] = val;
+                        else if (mat == 1) sP[row * L::LDM + col] = O_::enc(val);
+                        else if (mat == 2) sAk[row * L::LDM + col] = O_::enc(val);
+                        else sMe[row * L::LDM + col] = O_::enc(val);
+                    }
                 }
             }
         }
@@ -397,8 +487,8 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
             lds_barrier();
         }
 
-        // ---- state-dependent chain, per wave (16 value columns)
-        {
+        // ---- state-dependent chain (wave 0, 16 value columns)
+        if (chain) {
             const S* Te = kBF ? sTe : reinterpret_cast<const S*>(sT);
             constexpr int LDTe = kBF ? L::LDM : L::LDF;
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -422,7 +512,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
             }
             f32x4 Vr[NB];
 #pragma unroll
-            for (int m = 0; m < NB; ++m) Vr[m] = O_::acc_tile(sV, L::LDV, 16 * m, 16 * w, g, c);
+            for (int m = 0; m < NB; ++m) Vr[m] = O_::acc_tile(sV, L::LDV, 16 * m, 0, g, c);
             f32x4 Ot[NB];
             R Ur[NB];   // V~ (one step size) or W (split gates), operand form
             R Wn[NB];   // split gates: -Y~, operand form
@@ -476,7 +566,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
             for (int m = 0; m < NB; ++m) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sO[(16 * m + 4 * g + i) * L::LDV + 16 * w + c] = O_::enc(Ot[m][i]);
+                    sO[(16 * m + 4 * g + i) * L::LDV + c] = O_::enc(Ot[m][i]);
             }
         }
         lds_barrier();
@@ -496,7 +586,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
         lds_barrier();
     }
 
-    if (p.ST) {
+    if (p.ST && chain) {
         float* st = p.ST + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK;
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
