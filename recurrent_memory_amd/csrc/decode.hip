@@ -8,8 +8,8 @@
 // d_k/32 consecutive key columns of each of its rows, so every row is one
 // coalesced 512-byte (d_k = 128) read and write.  The small per-token
 // operands are requested first, then every state row; the rows are finished
-// in two batches, so the first batch's writes overlap the second batch's
-// reads.
+// in four batches, so the writes of a batch overlap the reads still arriving
+// for the next ones.
 //
 // Per row i (value channel) with a = exp(g) and S' = S·Diag(a):
 //   r_i  = S'_i · k          (read)        s_i = S'_i · q
@@ -84,12 +84,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     kq = half_wave_sum(kq);
     if constexpr (VAR == 3) bkq = half_wave_sum(bkq);
 
-    // Rows in two batches: the first batch is reduced, updated and written
-    // back while the second batch's loads are still arriving.
-    constexpr int RB = RPG / 2;        // rows per batch
+    // Rows in four batches: a batch is reduced, updated and written back while
+    // the loads of the later batches are still arriving.
+    constexpr int NBATCH = RPG >= 4 ? 4 : RPG;
+    constexpr int RB = RPG / NBATCH;   // rows per batch
     constexpr int NV = 2 * RB;         // partial dot products per lane and batch
 #pragma unroll
-    for (int bt = 0; bt < 2; ++bt) {
+    for (int bt = 0; bt < NBATCH; ++bt) {
         float val[NV];
 #pragma unroll
         for (int jj = 0; jj < RB; ++jj) {
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
                 val[0] += __shfl_xor(val[0], sh, 32);
             }
         }
-        constexpr int kShift = (NV == 16) ? 1 : 2;  // lanes per value index
+        constexpr int kShift = NV == 32 ? 0 : NV == 16 ? 1 : NV == 8 ? 2 : NV == 4 ? 3 : 4;  // log2(32 / NV)
         const int idx = li >> kShift;               // value index this lane holds
         // r of row idx sits at value idx, s of row idx at value RB + idx.
         const float other = __shfl_xor(val[0], RB << kShift, 32);
