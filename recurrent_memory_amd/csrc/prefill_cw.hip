@@ -174,27 +174,58 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
     uint4 pq[NPK], pk[NPK], pg[NPK], pb[NPK], pv[NPV], pw[NPV];
     Raw pbeta = Raw(0);
     const int nchunks = (T + C - 1) / C;
+    // per-thread element offsets relative to the first token of a sub-chunk
+    // (32-bit, computed once); only the last, partial sub-chunk clamps rows
+    uint32_t koff[NPK], voff[NPV];
+#pragma unroll
+    for (int j = 0; j < NPK; ++j) {
+        const int pidx = tid + kThreadsCW * j;
+        const int row = min(pidx / CPR, C - 1), cc = pidx % CPR;
+        koff[j] = static_cast<uint32_t>(row * H * DK + cc * EPC);
+    }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+        const int pidx = tid + kThreadsCW * j;
+        const int row = min(pidx / VPR, C - 1), cc = pidx % VPR;
+        voff[j] = static_cast<uint32_t>(row * H * DV + cc * EPC);
+    }
     auto prefetch = [&](int n) {
         const int t0 = n * C;
         const int last = min(C, T - t0) - 1;
         const int64_t tokb = static_cast<int64_t>(b) * T + t0;
+        if (last == C - 1) {   // whole sub-chunk: uniform base + thread offset
+            const int64_t kb = (tokb * H + h) * DK, vb = (tokb * H + h) * DV + vt * kVTCW;
 #pragma unroll
-        for (int j = 0; j < NPK; ++j) {
-            const int pidx = tid + kThreadsCW * j;
-            const int row = min(min(pidx / CPR, C - 1), last), cc = pidx % CPR;
-            const int64_t off = ((tokb + row) * H + h) * DK + cc * EPC;
-            pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
-            pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
-            pg[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.g) + off);
-            if constexpr (SPLIT) pb[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.beta) + off);
-        }
+            for (int j = 0; j < NPK; ++j) {
+                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + kb + koff[j]);
+                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + kb + koff[j]);
+                pg[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.g) + kb + koff[j]);
+                if constexpr (SPLIT) pb[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.beta) + kb + koff[j]);
+            }
 #pragma unroll
-        for (int j = 0; j < NPV; ++j) {
-            const int pidx = tid + kThreadsCW * j;
-            const int row = min(min(pidx / VPR, C - 1), last), cc = pidx % VPR;
-            const int64_t off = ((tokb + row) * H + h) * DV + vt * kVTCW + cc * EPC;
-            pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + off);
-            if constexpr (SPLIT) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + off);
+            for (int j = 0; j < NPV; ++j) {
+                pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + vb + voff[j]);
+                if constexpr (SPLIT) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + vb + voff[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPK; ++j) {
+                const int pidx = tid + kThreadsCW * j;
+                const int row = min(min(pidx / CPR, C - 1), last), cc = pidx % CPR;
+                const int64_t off = ((tokb + row) * H + h) * DK + cc * EPC;
+                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
+                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
+                pg[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.g) + off);
+                if constexpr (SPLIT) pb[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.beta) + off);
+            }
+#pragma unroll
+            for (int j = 0; j < NPV; ++j) {
+                const int pidx = tid + kThreadsCW * j;
+                const int row = min(min(pidx / VPR, C - 1), last), cc = pidx % VPR;
+                const int64_t off = ((tokb + row) * H + h) * DV + vt * kVTCW + cc * EPC;
+                pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + off);
+                if constexpr (SPLIT) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + off);
+            }
         }
         if constexpr (!SPLIT) {
             if (tid < C) pbeta = static_cast<const Raw*>(p.beta)[(tokb + min(tid, last)) * H + h];
