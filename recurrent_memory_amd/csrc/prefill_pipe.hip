@@ -9,19 +9,23 @@
 //   V~ = T (beta ⊙ (V - e^G ⊙ K S^T))
 //   O  = e^G ⊙ Q S^T + P V~
 //   S^T <- e^G_C S^T + K^T (e^(G_C - G) ⊙ V~)
-// Only the last three lines depend on the state, so A, T and P of chunk
-// n + 1 can be built while chunk n runs through the state.  One workgroup of
-// four waves per (batch, head, 32 value columns):
+// Only the last three lines depend on the state, so the blocks of A and T
+// and P of chunk n + 1 can be built while chunk n runs through the state.
+// T is applied by block forward substitution over the four 16-row blocks,
+//   V~_J = T_JJ (R_J - Σ_{M<J} A_JM V~_M),   R = beta ⊙ (V - e^G ⊙ K S^T),
+// which needs only the diagonal blocks T_JJ = (I + A_JJ)^-1 and the
+// off-diagonal blocks of A.  One workgroup of four waves per (batch, head,
+// 32 value columns):
 //   waves 0, 1 ("chain")  chunk n: the state-dependent lines above, 16 value
 //                         columns each, S^T in fp32 accumulators throughout;
-//   wave 2 ("T builder")  chunk n + 1: A from K K^T, diagonal 16x16 blocks of
-//                         T by substitution (fp32), off-diagonal blocks
-//                         chained with bf16 MFMA: T_RJ = -T_RR Σ_M A_RM T_MJ;
+//   wave 2 ("T builder")  chunk n + 1: the diagonal blocks of A from K K^T,
+//                         T_JJ by substitution (fp32), and the off-diagonal
+//                         blocks A_JM by MFMA;
 //   wave 3                issues the HBM -> LDS loads of q and k of chunk
 //                         n + 2, builds P of chunk n + 1 and the per-row decay
 //                         vectors of chunk n + 2.
 // Each step ends in one barrier.  LDS holds q/k in three slots (n, n + 1,
-// n + 2), T and P in two.
+// n + 2), the T/A blocks and P in two.
 #include "chunk_ops.h"
 #include "common.h"
 #include "kernels.h"
@@ -38,14 +42,17 @@ constexpr int kThreadsP = 256;   // 4 waves
 constexpr int kDS = 16 * 20 + 4;
 
 // q/k tiles in LDS: unpadded rows of DK bf16; the 16-byte piece p of row r
-// sits in slot p ^ swz(r).  The swizzle keeps the three read patterns free of
-// bank conflicts: 16 lanes reading 16 B (or 8 B) from one piece column of 16
-// consecutive rows, and the transpose read (4 consecutive rows x 4 pieces of
-// 8 B).  For DK = 128 a row spans all 64 banks; for DK = 64 two rows do.
+// sits in slot p ^ swz(r).  The swizzle keeps both read patterns free of bank
+// conflicts within 16 lanes: 16 B from one piece column of 16 consecutive
+// rows, and the transpose read (4 consecutive rows x 4 consecutive pieces, 8 B
+// from each).  The first needs swz to be one-to-one on r mod 16, the second
+// needs rows 4 a .. 4 a + 3 to differ in the bits of swz above the low two.
+// For DK = 128 a row spans all 64 banks; for DK = 64 two rows do, so there
+// only rows of equal parity can collide.
 template <int DK>
 __device__ __forceinline__ int swz(int r) {
-    if constexpr (DK == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    if constexpr (DK == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 // element offset of (row r, column col) in a q/k tile; col % 8 + width <= 8
 template <int DK>
@@ -96,10 +103,6 @@ __device__ __forceinline__ void dma_lds_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Empty use of four loaded words (forces the loads to complete here).
-__device__ __forceinline__ void keep_alive_u32x4(const uint32_t (&v)[4]) {
-    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
-}
 
 // Empty use that keeps four 8-byte register values (and their registers) live.
 __device__ __forceinline__ void keep_alive(const bf16x4 (&v)[4]) {
@@ -112,15 +115,14 @@ struct LayoutP {
     static constexpr int LDV = 16 + 8;   // bf16 per-wave value / output staging
     static constexpr int QK = kCP * DK * 2;
     static constexpr int MP = kCP * LDP * 2;
-    static constexpr int VEC = (8 * kCP + 4) * 4;    // per-row vectors of one chunk
+    static constexpr int VEC = (9 * kCP + 4) * 4;    // per-row vectors of one chunk
     static constexpr int oQ = 0;                     // [3] slots
     static constexpr int oK = oQ + 3 * QK;           // [3]
     static constexpr int oTe = oK + 3 * QK;          // [2]
     static constexpr int oP = oTe + 2 * MP;          // [2]
     static constexpr int oVec = oP + 2 * MP;         // [3]
     static constexpr int oAd = oVec + 3 * VEC;       // T builder: diagonal A blocks, fp32 [4][kDS]
-    static constexpr int oTd = oAd + 4 * kDS * 4;      // T builder: diagonal T blocks, fp32 [4][kDS]
-    static constexpr int oVw = oTd + 4 * kDS * 4;      // chain waves: [2][64][LDV] bf16
+    static constexpr int oVw = oAd + 4 * kDS * 4;      // chain waves: [2][64][LDV] bf16
     static constexpr int bytes = oVw + 2 * kCP * LDV * 2;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -155,7 +157,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     uint16_t* sPs = reinterpret_cast<uint16_t*>(smem + L::oP);
     float* sVecs = reinterpret_cast<float*>(smem + L::oVec);
     float* sAd = reinterpret_cast<float*>(smem + L::oAd);
-    float* sTd = reinterpret_cast<float*>(smem + L::oTd);
     uint16_t* sVw = reinterpret_cast<uint16_t*>(smem + L::oVw);
     auto qslot = [&](int n) { return sQs + (n % 3) * (L::QK / 2); };
     auto kslot = [&](int n) { return sKs + (n % 3) * (L::QK / 2); };
@@ -165,12 +166,21 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     // vector slot layout: [0,64) beta, [64,128) G (cumulative log-decay),
     // [128,192) e^G, [192,256) e^(G_C - G), [256] gamma = e^G_C,
     // [260,324) u_r = e^(G_r - G_16floor(r/16)), [324 + 64 (R - 1) + j] =
-    // w_R[j] = e^(G_16R - G_j) for R = 1..3 (used for j < 16 R).  For r in
-    // block R > J, e^(G_r - G_j) = u_r w_R[j] with both factors in (0, 1].
+    // w_R[j] = e^(G_16R - G_j) for R = 1..3 (used for j < 16 R), [516,580)
+    // beta_r u_r.  For r in block R > J, e^(G_r - G_j) = u_r w_R[j] with both
+    // factors in (0, 1].
 
+    // Workgroup -> (head, value tile).  Workgroups are dispatched round-robin
+    // over the 8 XCDs.  The NVT tiles of one head get ids 8 apart, so they run
+    // on the same XCD and share its L2 for q and k, and each XCD takes a run
+    // of consecutive heads: in the [B, T, H, d] layout a head is one fixed
+    // d-element column of every token row, and heads that are congruent
+    // modulo 8 on one XCD made all of its traffic use the same address bits
+    // (those workgroups ran 17% longer).
     const int x = blockIdx.x;
+    const int groups = (p.B * p.H + 7) / 8;
     const int vt = (x / 8) % NVT;
-    const int bh = (x % 8) + 8 * (x / (8 * NVT));
+    const int bh = (x % 8) * groups + x / (8 * NVT);
     if (bh >= p.B * p.H) return;
     const int b = bh / p.H, h = bh % p.H;
     const int T = p.T, H = p.H;
@@ -190,13 +200,19 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     if (w < 2) {
         const int vc0 = vt * kVTP + 16 * w;
         uint16_t* sV = sVw + w * kCP * L::LDV;
+        // S^T register tiles: tile t, lane (g, c), element i holds value
+        // column vc0 + c at key channel 32 (t / 2) + 8 g + 4 (t % 2) + i.  Two
+        // tiles paired as one B operand then hold channels 32 q + 8 g .. + 7 at
+        // lane (g, c): eight consecutive channels, one 16-byte piece of a key
+        // row, so the A operands of X and Y are single 16-byte LDS reads.
+        auto chan = [&](int t) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
         f32x4 ST[NKT];
         {
             const float* s0 = p.S0 ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 if (s0) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(s0 + 16 * t + 4 * g);
+                    const float4 v4 = *reinterpret_cast<const float4*>(s0 + chan(t));
                     ST[t] = f32x4{v4.x, v4.y, v4.z, v4.w};
                 } else {
                     ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -210,29 +226,37 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
             pv0 = *reinterpret_cast<const uint4*>(src);
             pv1 = *reinterpret_cast<const uint4*>(src + 8);
         };
-        // A-operand fragments of K and Q for X = K S^T and Y = Q S^T, read at
-        // the end of the previous step so that a step starts with its
-        // contractions: fragment (m, q) of lane (g, c) holds row 16 m + c,
-        // columns 32 q + 4 g + (0..3) and 32 q + 16 + 4 g + (0..3), matching the
-        // row order of the register tiles of S^T paired two by two.
+        // A-operand fragments of K and Q for X = K S^T and Y = Q S^T: fragment
+        // (m, q) of lane (g, c) holds row 16 m + c, columns 32 q + 8 g .. + 7,
+        // the channel order of the S^T tiles paired two by two.
         constexpr int NKP = NKT / 2;
         // lane parts of every LDS address the chain uses (loop invariant)
-        int xo0[NKP], xo1[NKP], kto[NKT];
+        int xo[NKP], kto[NKT];
 #pragma unroll
-        for (int q = 0; q < NKP; ++q) {
-            xo0[q] = qk_off<DK>(c, 32 * q + 4 * g);
-            xo1[q] = qk_off<DK>(c, 32 * q + 16 + 4 * g);
-        }
-        // transpose reads of K: lane (g, c) of a 16-lane group points at row
-        // r0 + 4 g + c / 4, columns 16 t + 4 (c % 4) .. + 3 and receives column
-        // 16 t + c of rows r0 + 4 g .. + 3 (r0 a multiple of 16 leaves the
-        // swizzle unchanged)
+        for (int q = 0; q < NKP; ++q) xo[q] = qk_off<DK>(c, 32 * q + 8 * g);
+        // transpose reads of K: within a 16-lane group, lane i receives element
+        // i % 4 of the 8-byte piece addressed by lane 4 j + i / 4, j = 0..3.
+        // Lane (g, c) points at row r0 + 4 g + c / 4, columns
+        // 32 (t / 2) + 8 (c % 4) + 4 (t % 2) .. + 3, so lane c receives rows
+        // r0 + 4 g .. + 3 of the channel that row c of S^T tile t holds (r0 a
+        // multiple of 16 leaves the swizzle unchanged).
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) kto[t] = qk_off<DK>(4 * g + (c >> 2), 16 * t + 4 * (c & 3));
+        for (int t = 0; t < NKT; ++t) kto[t] = qk_off<DK>(4 * g + (c >> 2), 32 * (t >> 1) + 8 * (c & 3) + 4 * (t & 1));
         const int tpo = c * L::LDP + 4 * g;                       // T, P rows
         const int vvo = (4 * g + (c >> 2)) * L::LDV + 4 * (c & 3);  // value tile, transposed
-        bf16x8 kx[4][NKP], qx[4][NKP];
-        auto load_xy = [&](int n) {
+        // Operands of chunk n that are complete one step before chunk n is
+        // processed (q, k, the per-row vectors and the wave's own value tile)
+        // are read during the step before it, each group right after the
+        // last use of the registers it refills, so the reads overlap that
+        // step's products.  T and P of chunk n are built during that step
+        // and are read at the start of step n.
+        bf16x8 kx[4][NKP], qx[4][NKP];   // A operands of X = K S^T, Y = Q S^T
+        bf16x8 kt[NKT][2];               // K^T fragments for the state update
+        f32x4 bt[4], eg[4], egc[4];
+        float egr[4];                    // e^G of row 16 m + c (outputs are kept transposed)
+        float gam = 1.f;
+        bf16x4 vv[4];                    // value tile in accumulator layout (rows 4 g + i, column c)
+        auto read_xy = [&](int n) {
             const uint16_t* sK = kslot(n);
             const uint16_t* sQ = qslot(n);
 #pragma unroll
@@ -240,65 +264,71 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
                 for (int q = 0; q < NKP; ++q) {
                     const int rb = 16 * m * DK;
-                    kx[m][q] = cat(*reinterpret_cast<const bf16x4*>(sK + rb + xo0[q]), *reinterpret_cast<const bf16x4*>(sK + rb + xo1[q]));
-                    qx[m][q] = cat(*reinterpret_cast<const bf16x4*>(sQ + rb + xo0[q]), *reinterpret_cast<const bf16x4*>(sQ + rb + xo1[q]));
+                    kx[m][q] = *reinterpret_cast<const bf16x8*>(sK + rb + xo[q]);
+                    qx[m][q] = *reinterpret_cast<const bf16x8*>(sQ + rb + xo[q]);
                 }
             }
+        };
+        // value tile and the vectors of the R epilogue
+        auto read_rv = [&](int n) {
+            const bool ok = lane < rows_in(n);
+            // commit the value tile of chunk n to the wave's staging area
+            *reinterpret_cast<uint4*>(sV + lane * L::LDV) = sel_rows(ok, pv0);
+            *reinterpret_cast<uint4*>(sV + lane * L::LDV + 8) = sel_rows(ok, pv1);
+            if (n + 1 < N) vload(n + 1);
+            const float* vec = vslot(n);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bt[m] = *reinterpret_cast<const f32x4*>(vec + 16 * m + 4 * g);
+                eg[m] = *reinterpret_cast<const f32x4*>(vec + 128 + 16 * m + 4 * g);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) vv[m] = tr_read(sV + 16 * m * L::LDV + vvo);
+        };
+        auto read_kt = [&](int n) {
+            const uint16_t* sK = kslot(n);
+            const float* vec = vslot(n);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) egc[m] = *reinterpret_cast<const f32x4*>(vec + 192 + 16 * m + 4 * g);
+            gam = vec[256];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    kt[t][q] = cat(tr_read(sK + 32 * q * DK + kto[t]), tr_read(sK + (32 * q + 16) * DK + kto[t]));
+            }
+        };
+        auto read_egr = [&](int n) {
+            const float* vec = vslot(n);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) egr[m] = vec[128 + 16 * m + c];
         };
         const bf16x4 z4 = {0, 0, 0, 0};
         bf16x4 od[4] = {z4, z4, z4, z4};   // output rows being stored
         for (int s = -2; s < N; ++s) {
-            if (s == -1) vload(0);
             if (s >= 0) {
                 const int Cn = rows_in(s);
-                {   // commit this chunk's value tile to the wave's staging area
-                    const bool ok = lane < Cn;
-                    *reinterpret_cast<uint4*>(sV + lane * L::LDV) = sel_rows(ok, pv0);
-                    *reinterpret_cast<uint4*>(sV + lane * L::LDV + 8) = sel_rows(ok, pv1);
-                }
-                if (s + 1 < N) vload(s + 1);
-                load_xy(s);
-                const uint16_t* sK = kslot(s);
                 const uint16_t* Te = teslot(s);
                 const uint16_t* Pm = pslot(s);
-                const float* vec = vslot(s);
-                // ---- every LDS operand of the step is requested up front
-                f32x4 bt[4], eg[4], egc[4];
-                float egr[4];   // e^G of row 16 m + c (outputs are kept transposed)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    bt[m] = *reinterpret_cast<const f32x4*>(vec + 16 * m + 4 * g);
-                    eg[m] = *reinterpret_cast<const f32x4*>(vec + 128 + 16 * m + 4 * g);
-                    egc[m] = *reinterpret_cast<const f32x4*>(vec + 192 + 16 * m + 4 * g);
-                    egr[m] = vec[128 + 16 * m + c];
-                }
-                const float gam = vec[256];
-                bf16x4 vv[4];   // value tile in accumulator layout (rows 4 g + i, column c)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) vv[m] = tr_read(sV + 16 * m * L::LDV + vvo);
-                // lower-triangular T and P rows as A operands: row 16 m + c,
+                // diagonal blocks T_mm and off-diagonal blocks A_mJ (lane
+                // (g, c): row 16 m + c, columns 16 J + 4 g .. + 3) and the
+                // lower-triangular rows of P, as A operands: row 16 m + c,
                 // column tiles paired (0, 1) and (2, 3); an unpaired tile is
                 // padded with zeros
-                bf16x8 tf[4][2], pf[4][2];
+                bf16x4 td[4], Ab[4][3];
+                bf16x8 pf[4][2];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
+                    td[m] = *reinterpret_cast<const bf16x4*>(Te + 16 * m * L::LDP + 16 * m + tpo);
+#pragma unroll
+                    for (int J = 0; J < m; ++J) Ab[m][J] = *reinterpret_cast<const bf16x4*>(Te + 16 * m * L::LDP + 16 * J + tpo);
 #pragma unroll
                     for (int q = 0; q <= m / 2; ++q) {
                         const int off = 16 * m * L::LDP + 32 * q + tpo;
                         const bool two = 2 * q + 1 <= m;
-                        const bf16x4 t0 = *reinterpret_cast<const bf16x4*>(Te + off);
                         const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(Pm + off);
-                        tf[m][q] = cat(t0, two ? *reinterpret_cast<const bf16x4*>(Te + off + 16) : z4);
                         pf[m][q] = cat(p0, two ? *reinterpret_cast<const bf16x4*>(Pm + off + 16) : z4);
                     }
-                }
-                // K^T fragments for the state update
-                bf16x8 kt[NKT][2];
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        kt[t][q] = cat(tr_read(sK + 32 * q * DK + kto[t]), tr_read(sK + (32 * q + 16) * DK + kto[t]));
                 }
                 // ---- X = K S^T (accumulator layout), Y = Q S^T (transposed:
                 // swapping the operands makes lane (g, c) hold row 16 m + c,
@@ -321,25 +351,34 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                         Yt[m] = mfma32(STp[q], qx[m][q], Yt[m]);
                     }
                 }
-                // ---- R = beta (V - e^G X);  V~ = T R
-                bf16x4 Rr[4];
+                // (at the last step these read slots that nothing writes any more)
+                read_xy(s + 1);
+                // ---- R = beta (V - e^G X);  V~ = (I + A)^-1 R by block forward
+                // substitution: V~_J = T_JJ (R_J - sum_{M<J} A_JM V~_M)
+                f32x4 Rf[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    f32x4 r;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) r[i] = bt[m][i] * (static_cast<float>(vv[m][i]) - eg[m][i] * X[m][i]);
-                    Rr[m] = to_bf16x4(r);
+                    for (int i = 0; i < 4; ++i) Rf[m][i] = bt[m][i] * (static_cast<float>(vv[m][i]) - eg[m][i] * X[m][i]);
                 }
-                const bf16x8 R01 = cat(Rr[0], Rr[1]), R2z = cat(Rr[2], z4), R23 = cat(Rr[2], Rr[3]), R0z = cat(Rr[0], z4);
+                read_rv(s + 1);
                 f32x4 Vt[4];
-                Vt[0] = mfma32(tf[0][0], R0z, zero);
-                Vt[1] = mfma32(tf[1][0], R01, zero);
-                Vt[2] = mfma32(tf[2][1], R2z, mfma32(tf[2][0], R01, zero));
-                Vt[3] = mfma32(tf[3][1], R23, mfma32(tf[3][0], R01, zero));
                 bf16x4 Vtr[4], Vgr[4];
+                Vt[0] = mfma32(cat(td[0], z4), cat(to_bf16x4(Rf[0]), z4), zero);
+                Vtr[0] = to_bf16x4(Vt[0]);
+                const f32x4 y1 = mfma32(cat(Ab[1][0], z4), cat(Vtr[0], z4), zero);
+                Vt[1] = mfma32(cat(td[1], z4), cat(to_bf16x4(Rf[1] - y1), z4), zero);
+                Vtr[1] = to_bf16x4(Vt[1]);
+                const bf16x8 V01 = cat(Vtr[0], Vtr[1]);
+                const f32x4 y2 = mfma32(cat(Ab[2][0], Ab[2][1]), V01, zero);
+                f32x4 y3 = mfma32(cat(Ab[3][0], Ab[3][1]), V01, zero);
+                Vt[2] = mfma32(cat(td[2], z4), cat(to_bf16x4(Rf[2] - y2), z4), zero);
+                Vtr[2] = to_bf16x4(Vt[2]);
+                y3 = mfma32(cat(Ab[3][2], z4), cat(Vtr[2], z4), y3);
+                Vt[3] = mfma32(cat(td[3], z4), cat(to_bf16x4(Rf[3] - y3), z4), zero);
+                Vtr[3] = to_bf16x4(Vt[3]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    Vtr[m] = to_bf16x4(Vt[m]);
                     f32x4 vg;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) vg[i] = egc[m][i] * Vt[m][i];
@@ -349,11 +388,13 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                 const bf16x8 Vg01 = cat(Vgr[0], Vgr[1]), Vg23 = cat(Vgr[2], Vgr[3]);
 #pragma unroll
                 for (int t = 0; t < NKT; ++t) ST[t] = mfma32(kt[t][1], Vg23, mfma32(kt[t][0], Vg01, ST[t] * gam));
+                read_kt(s + 1);
                 // ---- O = e^G Y + P V~, transposed like Y
-                const bf16x8 V01 = cat(Vtr[0], Vtr[1]), V2z = cat(Vtr[2], z4), V23 = cat(Vtr[2], Vtr[3]), V0z = cat(Vtr[0], z4);
+                const bf16x8 V2z = cat(Vtr[2], z4), V23 = cat(Vtr[2], Vtr[3]), V0z = cat(Vtr[0], z4);
                 f32x4 Ot[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) Ot[m] = Yt[m] * egr[m];
+                read_egr(s + 1);
                 Ot[0] = mfma32(V0z, pf[0][0], Ot[0]);
                 Ot[1] = mfma32(V01, pf[1][0], Ot[1]);
                 Ot[2] = mfma32(V2z, pf[2][1], mfma32(V01, pf[2][0], Ot[2]));
@@ -370,13 +411,20 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                     if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = od[m];
                 }
             }
+            if (s == -1) {
+                vload(0);
+                read_xy(0);
+                read_rv(0);
+                read_kt(0);
+                read_egr(0);
+            }
             lds_barrier();
         }
         if (p.ST) {
             float* st = p.ST + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK;
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
-                *reinterpret_cast<float4*>(st + 16 * t + 4 * g) =
+                *reinterpret_cast<float4*>(st + chan(t)) =
                     make_float4(ST[t][0], ST[t][1], ST[t][2], ST[t][3]);
         }
         return;
@@ -393,20 +441,9 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     // beta is zero, which removes them from every product that reaches an
     // output or the state.
     const bool lw = (w == 3);   // loader and P builder; wave 2 builds T
-    // Wave 3 also touches one 4-byte word per 128-byte line of q and k of
-    // chunk n + 3 (before its loads of chunk n + 2), so those lines are in L2
-    // when they are staged a step later.  The words are consumed by an empty
-    // asm after the end-of-step wait, so the loads are kept and cost no wait.
-    uint32_t touch[4] = {0u, 0u, 0u, 0u};
-    const uint32_t touch_off = static_cast<uint32_t>((lane >> 1) * H * DK + 64 * (lane & 1));
-    auto l2_touch = [&](int n) {   // whole chunks only
-        const int64_t base = ((tokb + n * kCP) * H + h) * DK;
-        const uint32_t half = 32u * H * DK;   // rows 32..63
-        touch[0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k) + base + touch_off);
-        touch[1] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k) + base + half + touch_off);
-        touch[2] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + base + touch_off);
-        touch[3] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + base + half + touch_off);
-    };
+    // (A prefetch of chunk n + 3 into L2 by 4-byte loads, one per 128-byte
+    // line, made every workgroup of heads h = 1 mod 4 about 18% slower with
+    // cold inputs, and the whole kernel with it; the loads are not issued.)
     uint16_t pbeta = 0, pg = 0;
     // Per-lane element offsets of the pieces this lane fetches, relative to
     // the first token of a chunk (32-bit; computed once).
@@ -457,6 +494,7 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         vec[324 + lane] = VAR == 0 ? 1.f : __expf(G16 - G);
         vec[388 + lane] = VAR == 0 ? 1.f : __expf(G32 - G);
         vec[452 + lane] = VAR == 0 ? 1.f : __expf(G48 - G);
+        vec[516 + lane] = VAR == 0 ? beta : beta * __expf(G - Gb);
     };
     // A-operand fragment: lane (g, c) holds row 16 R + c, columns 32 kk + 8 g .. + 7
     auto frag = [&](const uint16_t* tile, int Rt, int kk) {
@@ -469,7 +507,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     for (int s = -2; s < N; ++s) {
         const int nl = s + 2;   // chunk staged during this step
         const int nb = s + 1;   // chunk whose T (wave 2) or P (wave 3) is built now
-        if (lw && (s + 3) * kCP + kCP <= T) l2_touch(s + 3);
         if (lw && nl < N) {     // stage chunk nl: the loads get the whole step to land
             load_vec(nl);
             load_tile(static_cast<const uint16_t*>(p.k), kslot(nl), nl);
@@ -484,31 +521,29 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                 for (int kk = 0; kk < NKK; ++kk) kf[Rt][kk] = frag(kslot(nb), Rt, kk);
             }
             // per-row vectors of chunk nb: rows 16 R + c and rows 16 R + 4 g .. + 3
-            float gc[4], uc[4], bc[4];
-            f32x4 gr[4], br[4], wv[4][3];   // wv[R][J] = w_R[16 J + 4 g .. + 3]
+            float gc[4];
+            f32x4 gr[4], wv[4][3];   // wv[R][J] = w_R[16 J + 4 g .. + 3]
 #pragma unroll
             for (int Rt = 0; Rt < 4; ++Rt) {
-                bc[Rt] = vec[16 * Rt + c];
                 gc[Rt] = vec[64 + 16 * Rt + c];
-                uc[Rt] = vec[260 + 16 * Rt + c];
-                br[Rt] = *reinterpret_cast<const f32x4*>(vec + 16 * Rt + 4 * g);
                 gr[Rt] = *reinterpret_cast<const f32x4*>(vec + 64 + 16 * Rt + 4 * g);
 #pragma unroll
                 for (int Jt = 0; Jt < Rt; ++Jt)
                     wv[Rt][Jt] = *reinterpret_cast<const f32x4*>(vec + 324 + 64 * (Rt - 1) + 16 * Jt + 4 * g);
             }
             if (!lw) {
-                // ---- diagonal blocks of A first: K_R K_R^T in accumulator
-                // layout (rows 4 g + i, column c), scaled and masked to A_RR,
-                // stored column-major (sAd[R][col][row]: one 16-byte piece per lane)
+                // ---- diagonal blocks of A: K_R K_R^T in accumulator layout
+                // (rows 4 g + i, column c), scaled and masked to A_RR, stored
+                // column-major (sAd[R][col][row]: one 16-byte piece per lane)
 #pragma unroll
                 for (int Rt = 0; Rt < 4; ++Rt) {
+                    const f32x4 br = *reinterpret_cast<const f32x4*>(vec + 16 * Rt + 4 * g);
                     f32x4 acc = zero;
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Rt][kk], kf[Rt][kk], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float val = acc[i] * br[Rt][i];
+                        float val = acc[i] * br[i];
                         if constexpr (VAR == 1) val *= __expf(gr[Rt][i] - gc[Rt]);
                         acc[i] = (4 * g + i > c) ? val : 0.f;
                     }
@@ -518,8 +553,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                 // transposed system: lane (block rb, j) solves (I + A_bb)^T y = e_j,
                 // which gives row j of T_bb = (I + A_bb)^-1:
                 //   y_i = [i == j] - Σ_{m > i} A[m][i] y_m,  i = 15 .. 0
-                // The columns of A_bb are requested here; the off-diagonal A
-                // tiles are computed while they are in flight.
                 const int rb = lane >> 4, j = lane & 15;
                 const float* Ab = sAd + rb * kDS;
                 f32x4 col[16][4];
@@ -528,23 +561,24 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
                     for (int q = (i + 1) / 4; q < 4; ++q) col[i][q] = *reinterpret_cast<const f32x4*>(Ab + i * 20 + 4 * q);
                 }
-                // ---- off-diagonal A tiles.  Swapping the two operands of a
-                // product yields its transpose in accumulator layout: lane
-                // (g, c) then holds A[16 R + c][16 J + 4 g + i], the A-operand
-                // layout of the level products.
-                bf16x4 At[4][3];
+                // ---- off-diagonal blocks of A, computed while the columns are
+                // in flight.  Swapping the two operands of K_J K_R^T leaves lane
+                // (g, c) with A[16 R + c][16 J + 4 g + i], the A-operand layout
+                // of the chain's block substitution; they are stored below the
+                // diagonal blocks of T in the same slot (one 8-byte write each).
+                uint16_t* Tm = teslot(nb);
 #pragma unroll
                 for (int Rt = 1; Rt < 4; ++Rt) {
+                    const float fr = vec[516 + 16 * Rt + c];   // beta_r u_r
 #pragma unroll
                     for (int Jt = 0; Jt < Rt; ++Jt) {
                         f32x4 acc = zero;
 #pragma unroll
                         for (int kk = 0; kk < NKK; ++kk) acc = mfma32(kf[Jt][kk], kf[Rt][kk], acc);
                         // beta_r e^(G_r - G_j) = (beta_r u_r) w_R[j]
-                        const float fr = bc[Rt] * uc[Rt];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc[i] *= fr * wv[Rt][Jt][i];
-                        At[Rt][Jt] = to_bf16x4(acc);
+                        *reinterpret_cast<bf16x4*>(Tm + (16 * Rt + c) * L::LDP + 16 * Jt + 4 * g) = to_bf16x4(acc);
                     }
                 }
                 float y[16];
@@ -555,14 +589,11 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                     for (int m = i + 1; m < 16; ++m) acc -= col[i][m / 4][m % 4] * y[m];
                     y[i] = acc;
                 }
-                // fp32 copy (row-major sTd[b][row][col]) for the level products
-                // and the bf16 diagonal block of T
-                float* Tr = sTd + rb * kDS + j * 20;
+                // bf16 diagonal block of T: row j of block rb, 16 columns
                 uint16_t* Te = teslot(nb) + (16 * rb + j) * L::LDP + 16 * rb;
                 uint32_t hw[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    *reinterpret_cast<f32x4*>(Tr + 4 * q) = f32x4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
                     hw[2 * q] = static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q])) |
                                 (static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q + 1])) << 16);
                     hw[2 * q + 1] = static_cast<uint32_t>(f32_to_bf16_bits(y[4 * q + 2])) |
@@ -573,50 +604,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                 // flight (they target q/k slots), so no wait for them is inserted
                 *reinterpret_cast<f32x4*>(Te) = __builtin_bit_cast(f32x4, make_uint4(hw[0], hw[1], hw[2], hw[3]));
                 *reinterpret_cast<f32x4*>(Te + 8) = __builtin_bit_cast(f32x4, make_uint4(hw[4], hw[5], hw[6], hw[7]));
-                // ---- off-diagonal blocks: T_RJ = -T_RR (Σ_{M=J}^{R-1} A_RM T_MJ).
-                // T_RR as an A operand (lane (g, c): row c, columns 4 g + i) is
-                // one 16-byte read of the row-major copy; T_JJ as a B operand
-                // (rows 4 g + i, column c) is four scalar reads.
-                bf16x4 dA[4], dB[3];
-#pragma unroll
-                for (int Rt = 1; Rt < 4; ++Rt)
-                    dA[Rt] = to_bf16x4(*reinterpret_cast<const f32x4*>(sTd + Rt * kDS + c * 20 + 4 * g));
-#pragma unroll
-                for (int Jt = 0; Jt < 3; ++Jt) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dB[Jt][i] = static_cast<bf16_t>(sTd[Jt * kDS + (4 * g + i) * 20 + c]);
-                }
-                // -T_RR · inner in accumulator layout (rows 4 g + i, column c) ...
-                auto finish = [&](int Rt, f32x4 inner) {
-                    return -mfma32(cat(dA[Rt], z4), cat(to_bf16x4(inner), z4), zero);
-                };
-                // ... or transposed (lane (g, c): row c, columns 4 g + i)
-                auto finishT = [&](int Rt, f32x4 inner) {
-                    return -mfma32(cat(to_bf16x4(inner), z4), cat(dA[Rt], z4), zero);
-                };
-                const f32x4 T10 = finish(1, mfma32(cat(At[1][0], z4), cat(dB[0], z4), zero));
-                const f32x4 T21 = finish(2, mfma32(cat(At[2][1], z4), cat(dB[1], z4), zero));
-                const f32x4 T32t = finishT(3, mfma32(cat(At[3][2], z4), cat(dB[2], z4), zero));
-                const f32x4 T20 = finish(2, mfma32(cat(At[2][0], At[2][1]), cat(dB[0], to_bf16x4(T10)), zero));
-                const f32x4 T31t = finishT(3, mfma32(cat(At[3][1], At[3][2]), cat(dB[1], to_bf16x4(T21)), zero));
-                f32x4 in30 = mfma32(cat(At[3][0], At[3][1]), cat(dB[0], to_bf16x4(T10)), zero);
-                in30 = mfma32(cat(At[3][2], z4), cat(to_bf16x4(T20), z4), in30);
-                const f32x4 T30t = finishT(3, in30);
-                uint16_t* Tm = teslot(nb);
-                auto put = [&](int Rt, int Jt, f32x4 t) {   // accumulator layout
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Tm[(16 * Rt + 4 * g + i) * L::LDP + 16 * Jt + c] = f32_to_bf16_bits(t[i]);
-                };
-                auto putT = [&](int Rt, int Jt, f32x4 t) {  // transposed layout: one 8-byte write
-                    *reinterpret_cast<bf16x4*>(Tm + (16 * Rt + c) * L::LDP + 16 * Jt + 4 * g) = to_bf16x4(t);
-                };
-                put(1, 0, T10);
-                put(2, 1, T21);
-                put(2, 0, T20);
-                putT(3, 2, T32t);
-                putT(3, 1, T31t);
-                putT(3, 0, T30t);
             } else {
                 // ---- P = Tril(Q K^T ⊙ Gamma), transposed products: lane (g, c)
                 // holds P[16 R + c][16 J + 4 g + i] and writes it as one 8-byte piece
@@ -626,6 +613,9 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) qf[Rt][kk] = frag(qslot(nb), Rt, kk);
                 }
+                float uc[4];
+#pragma unroll
+                for (int Rt = 0; Rt < 4; ++Rt) uc[Rt] = vec[260 + 16 * Rt + c];
                 uint16_t* Pm = pslot(nb);
 #pragma unroll
                 for (int Rt = 0; Rt < 4; ++Rt) {
@@ -652,7 +642,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         }
         if (lw && nl < N) commit_vec(nl);
         dma_lds_barrier();
-        if (lw) keep_alive_u32x4(touch);
     }
 }
 
