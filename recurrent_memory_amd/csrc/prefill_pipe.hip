@@ -108,6 +108,9 @@ __device__ __forceinline__ void dma_lds_barrier() {
 __device__ __forceinline__ void keep_alive(const bf16x4 (&v)[4]) {
     asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
 }
+__device__ __forceinline__ void keep_alive(uint16_t* const (&v)[4]) {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+}
 
 template <int DK>
 struct LayoutP {
@@ -218,6 +221,10 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                     ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
+            // the initial state has landed before the loop starts: otherwise
+            // the wait for it is placed at the top of the loop body, where it
+            // also waits for every store and load of the previous step
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         }
         // value prefetch: lane = chunk row, two 16-byte pieces (16 columns)
         uint4 pv0 = make_uint4(0, 0, 0, 0), pv1 = make_uint4(0, 0, 0, 0);
@@ -305,6 +312,7 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         };
         const bf16x4 z4 = {0, 0, 0, 0};
         bf16x4 od[4] = {z4, z4, z4, z4};   // output rows being stored
+        uint16_t* oad[4] = {nullptr, nullptr, nullptr, nullptr};   // and their addresses
         for (int s = -2; s < N; ++s) {
             if (s >= 0) {
                 const int Cn = rows_in(s);
@@ -399,16 +407,19 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                 Ot[1] = mfma32(V01, pf[1][0], Ot[1]);
                 Ot[2] = mfma32(V2z, pf[2][1], mfma32(V01, pf[2][0], Ot[2]));
                 Ot[3] = mfma32(V23, pf[3][1], mfma32(V01, pf[3][0], Ot[3]));
-                // The registers that feed the global stores stay reserved until
-                // the next step refills them (empty asm use), so no instruction
-                // of that step waits for these stores to drain.
+                // The registers that feed the global stores (data and address)
+                // stay reserved until the next step refills them (empty asm
+                // use): overwriting a store's source register earlier makes the
+                // compiler wait for the store to complete.
                 keep_alive(od);
+                keep_alive(oad);
                 uint16_t* orow = static_cast<uint16_t*>(p.o) + token(s, c) * DV + vc0 + 4 * g;
                 const int64_t mstride = static_cast<int64_t>(16) * H * DV;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     od[m] = to_bf16x4(Ot[m]);
-                    if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = od[m];
+                    oad[m] = orow + m * mstride;
+                    if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(oad[m]) = od[m];
                 }
             }
             if (s == -1) {
