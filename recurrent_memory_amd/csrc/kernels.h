@@ -40,6 +40,10 @@ hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stre
 hipError_t launch_fwd_pipelined(int variant, const FwdArgs& a, hipStream_t stream);
 // channel-wise decay forms (variant 2 or 3), called by launch_fwd
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
+// channel-wise decay forms with bf16 operands, two passes (state-independent
+// operands of every sub-chunk first, then the recurrence), called by
+// launch_fwd_channel
+hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace dr

@@ -646,6 +646,7 @@ hipError_t launch_cw_dims(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
+    if (dtype == 1) return launch_fwd_channel_two_pass(variant, a, s);
     if (variant == 2)
         return dtype == 0 ? launch_cw_dims<2, F32>(a, s) : launch_cw_dims<2, BF16>(a, s);
     return dtype == 0 ? launch_cw_dims<3, F32>(a, s) : launch_cw_dims<3, BF16>(a, s);

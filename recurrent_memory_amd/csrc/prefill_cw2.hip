@@ -1,0 +1,671 @@
+// Two-pass chunkwise forward for the channel-wise decay forms with bf16
+// operands on gfx950: Kimi Delta Attention (one step size beta_t) and Gated
+// DeltaNet-2 (channel-wise erase gate b_t on the key side, write gate w_t on
+// the value side; Gated DeltaNet-2 abstract, thelatestinai.com/papers/
+// 2607.07953, whose chunkwise WY algorithm absorbs the channel-wise decay into
+// asymmetric erase factors).  The algebra per sub-chunk of C = 32 tokens (two
+// 16-token blocks) is that of the single-pass kernel in prefill_cw.hip:
+//   Kh_r = k_r ⊙ e^(G_r - G_b(R)), Qh likewise (kept as a bf16 hi + lo pair),
+//   Kb_j = k_j ⊙ e^(G_C - G_j), and for the C x C products the diagonal-block
+//   copies Ki_j = k_j ⊙ e^(G_b(R) - G_j) and the below-diagonal copies
+//   Ke_j = k_j ⊙ e^(G_end(J) - G_j);
+// one step size:
+//   A = StrictTril(diag(beta) Kh Kx^T), T = (I + A)^-1, P = Tril(Qh Kx^T)
+//   V~ = T (beta ⊙ (V - X)), X_R = Kh_R (S ⊙ e^G_b(R))^T
+//   O = Y + P V~, Y_R = Qh_R (S ⊙ e^G_b(R))^T, S^T <- Diag(e^G_C) S^T + Kb^T V~
+// split gates (E = b ⊙ K, W = w ⊙ V):
+//   A_e = StrictTril(Kh Ex^T), A_k = StrictTril(Kh Kx^T), T = (I + A_e)^-1
+//   Z = X + A_k W, Y~ = T Z, O = Y + M_k W - M_e Y~
+//   S^T <- Diag(e^G_C) S^T + Kb^T W - Eb^T Y~
+//
+// Everything above except X, Y and the state lines is the same for every
+// value tile of a head, and it is most of the work.  Pass 1 computes it once
+// per (batch, head, sub-chunk), all sub-chunks in parallel, and writes it to a
+// workspace as the exact LDS image that pass 2 reads (a "blob": MFMA operand
+// fragments of 16 bytes per lane, 1 KB per fragment, lane-linear, plus the
+// per-channel decay vectors).  Pass 2 runs the recurrence per (batch, head, 32
+// value columns): two waves, each carrying a 128 x 16 slice of S^T in fp32
+// accumulators, copy the blob of sub-chunk n + 2 into LDS with
+// global_load_lds while they run sub-chunk n, so the copy is one linear
+// stream and no address arithmetic.
+//
+// The state's key channels are held in a permuted order (tile t, lane (g, c),
+// element i <-> channel 32 (t / 2) + 8 g + 4 (t % 2) + i), so that two state
+// tiles paired as one B operand cover 8 consecutive channels and a key/query
+// fragment is one contiguous 16-byte piece of a row.
+#include <mutex>
+
+#include "chunk_ops.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace dr {
+namespace {
+
+constexpr int kC2 = 32;          // sub-chunk length (two 16-token blocks)
+constexpr int kPrepThreads = 256;
+constexpr int kChainWaves = 2;   // 16 value columns each
+constexpr int kVT2 = 16 * kChainWaves;
+
+// key channel held by element i of lane group g in state tile t
+__device__ __forceinline__ int perm_chan(int t, int g, int i) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i; }
+
+// Byte offsets of one sub-chunk's blob.  Fragments: 64 lanes x 16 bytes.
+template <int DK, bool SPLIT>
+struct Blob {
+    static constexpr int NKP = DK / 32;   // 32-channel k steps
+    static constexpr int NKT = DK / 16;   // 16-channel state tiles
+    static constexpr int F = 1024;
+    static constexpr int oKh = 0;                    // [block m][k step q]: Kh[16 m + c][32 q + 8 g ..]
+    static constexpr int oQh = oKh + 2 * NKP * F;    // Qh hi
+    static constexpr int oQl = oQh + 2 * NKP * F;    // Qh lo
+    static constexpr int oKb = oQl + 2 * NKP * F;    // [tile t]: Kb^T, row = channel of state row c
+    static constexpr int oEb = oKb + NKT * F;        // split gates: Eb^T
+    static constexpr int oT = oEb + (SPLIT ? NKT * F : 0);   // [block m]: row 16 m + c of T
+    static constexpr int oP = oT + 2 * F;            // P (or M_k)
+    static constexpr int oAk = oP + 2 * F;           // split gates: A_k
+    static constexpr int oMe = oAk + (SPLIT ? 2 * F : 0);    // split gates: M_e
+    static constexpr int oVec = oMe + (SPLIT ? 2 * F : 0);
+    // fp32 vectors: e^(G_end(0)) [DK] and e^(G_C) [DK], both in state order,
+    // then beta [C]
+    static constexpr int vE1 = 0, vGam = DK, vBeta = 2 * DK;
+    static constexpr int bytes = ((oVec + (2 * DK + kC2) * 4 + F - 1) / F) * F;
+};
+
+// ----------------------------------------------------------------- pass 1
+template <int DK, bool SPLIT>
+struct PrepLds {
+    static constexpr int C = kC2;
+    static constexpr int LDK = DK + 8;     // bf16 [C][DK] operand copies
+    static constexpr int LDM = C + 8;      // bf16 C x C
+    static constexpr int LDF = C + 4;      // fp32 C x C
+    static constexpr int KM = C * LDK * 2;
+    static constexpr int KE = 16 * LDK * 2;
+    static constexpr int MM = C * LDM * 2;
+    static constexpr int MF = C * LDF * 4;
+    static constexpr int oKh = 0;
+    static constexpr int oQh = oKh + KM;
+    static constexpr int oQl = oQh + KM;
+    static constexpr int oKi = oQl + KM;
+    static constexpr int oKb = oKi + KM;
+    static constexpr int oKe = oKb + KM;
+    static constexpr int oEi = oKe + KE;
+    static constexpr int oEb = oEi + (SPLIT ? KM : 0);
+    static constexpr int oEe = oEb + (SPLIT ? KM : 0);
+    static constexpr int oRawG = oEe + (SPLIT ? KE : 0);
+    static constexpr int oRawB = oRawG + KM;
+    static constexpr int oA = oRawB + (SPLIT ? KM : 0);   // A or A_e (fp32)
+    static constexpr int oT = oA + MF;                    // T (fp32)
+    static constexpr int oTe = oT + MF;                   // T (bf16)
+    static constexpr int oP = oTe + MM;                   // P or M_k
+    static constexpr int oAk = oP + MM;
+    static constexpr int oMe = oAk + (SPLIT ? MM : 0);
+    static constexpr int oVec = oMe + (SPLIT ? MM : 0);   // beta[C], e^G_b [2][DK], e^G_C [DK]
+    static constexpr int bytes = oVec + (C + 3 * DK) * 4;
+    static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, bool SPLIT>
+__global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsigned char* ws, int NC) {
+    typedef PrepLds<DK, SPLIT> L;
+    typedef Blob<DK, SPLIT> BL;
+    constexpr int C = kC2;
+    constexpr int NB = 2;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes];
+    uint16_t* sKh = reinterpret_cast<uint16_t*>(smem + L::oKh);
+    uint16_t* sQh = reinterpret_cast<uint16_t*>(smem + L::oQh);
+    uint16_t* sQl = reinterpret_cast<uint16_t*>(smem + L::oQl);
+    uint16_t* sKi = reinterpret_cast<uint16_t*>(smem + L::oKi);
+    uint16_t* sKb = reinterpret_cast<uint16_t*>(smem + L::oKb);
+    uint16_t* sKe = reinterpret_cast<uint16_t*>(smem + L::oKe);
+    uint16_t* sEi = reinterpret_cast<uint16_t*>(smem + L::oEi);
+    uint16_t* sEb = reinterpret_cast<uint16_t*>(smem + L::oEb);
+    uint16_t* sEe = reinterpret_cast<uint16_t*>(smem + L::oEe);
+    uint16_t* sRawG = reinterpret_cast<uint16_t*>(smem + L::oRawG);
+    uint16_t* sRawB = reinterpret_cast<uint16_t*>(smem + L::oRawB);
+    float* sA = reinterpret_cast<float*>(smem + L::oA);
+    float* sT = reinterpret_cast<float*>(smem + L::oT);
+    uint16_t* sTe = reinterpret_cast<uint16_t*>(smem + L::oTe);
+    uint16_t* sP = reinterpret_cast<uint16_t*>(smem + L::oP);
+    uint16_t* sAk = reinterpret_cast<uint16_t*>(smem + L::oAk);
+    uint16_t* sMe = reinterpret_cast<uint16_t*>(smem + L::oMe);
+    float* sBeta = reinterpret_cast<float*>(smem + L::oVec);
+    float* sEgb = sBeta + C;          // [NB][DK]
+    float* sGam = sEgb + NB * DK;     // [DK]
+
+    const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
+    const int b = bh / p.H, h = bh % p.H;
+    const int T = p.T, H = p.H;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int t0 = n * C;
+    const int Cn = min(C, T - t0);
+    const int64_t tokb = static_cast<int64_t>(b) * T + t0;
+
+    // ---- raw q, k, g (and the erase gate) of the sub-chunk; rows past the
+    // end are zero (zero decay, no key, no query)
+    {
+        constexpr int PPR = DK / 8;   // 16-byte pieces per row
+        for (int idx = tid; idx < C * PPR; idx += kPrepThreads) {
+            const int row = idx / PPR, cc = idx % PPR;
+            uint4 vq = make_uint4(0, 0, 0, 0), vk = vq, vg = vq, vb = vq;
+            if (row < Cn) {
+                const int64_t off = ((tokb + row) * H + h) * DK + 8 * cc;
+                vq = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
+                vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
+                vg = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.g) + off);
+                if constexpr (SPLIT) vb = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
+            }
+            *reinterpret_cast<uint4*>(sQh + row * L::LDK + 8 * cc) = vq;
+            *reinterpret_cast<uint4*>(sKh + row * L::LDK + 8 * cc) = vk;
+            *reinterpret_cast<uint4*>(sRawG + row * L::LDK + 8 * cc) = vg;
+            if constexpr (SPLIT) *reinterpret_cast<uint4*>(sRawB + row * L::LDK + 8 * cc) = vb;
+        }
+        if constexpr (!SPLIT) {
+            if (tid < C)
+                sBeta[tid] = tid < Cn ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.beta)[(tokb + tid) * H + h]) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- per channel: cumulative decay and the decay-carrying copies.
+    // Thread (channel pair cp, row group rq): channels 2 cp, 2 cp + 1 and RPT
+    // consecutive rows; the row groups of a channel pair are adjacent lanes,
+    // which exchange their partial decay sums by shuffles.
+    {
+        constexpr int NRQ = 2 * kPrepThreads / DK;
+        constexpr int RPT = C / NRQ;
+        static_assert(RPT >= 1 && C % NRQ == 0 && 16 % RPT == 0, "row split");
+        const int rq = tid % NRQ, cp = tid / NRQ;
+        const int ch = 2 * cp, r0 = rq * RPT;
+        auto ld2 = [&](const uint16_t* m, int r) -> float2 {
+            const uint32_t u = *reinterpret_cast<const uint32_t*>(m + r * L::LDK + ch);
+            return make_float2(bf16_bits_to_f32(static_cast<uint16_t>(u & 0xffffu)),
+                               bf16_bits_to_f32(static_cast<uint16_t>(u >> 16)));
+        };
+        auto st2 = [&](uint16_t* m, int r, float x0, float x1) {
+            *reinterpret_cast<uint32_t*>(m + r * L::LDK + ch) =
+                static_cast<uint32_t>(f32_to_bf16_bits(x0)) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
+        };
+        float g0[RPT], g1[RPT];
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const float2 v = ld2(sRawG, r0 + j);
+            g0[j] = v.x;
+            g1[j] = v.y;
+            p0 += v.x;
+            p1 += v.y;
+        }
+        float e0 = 0.f, e1 = 0.f, tot0 = 0.f, tot1 = 0.f, bs0 = 0.f, bs1 = 0.f, end0 = 0.f, end1 = 0.f;
+        const int my_block = r0 / 16;
+#pragma unroll
+        for (int q = 0; q < NRQ; ++q) {
+            const float s0 = __shfl(p0, (lane & ~(NRQ - 1)) + q, 64);
+            const float s1 = __shfl(p1, (lane & ~(NRQ - 1)) + q, 64);
+            if (q < rq) { e0 += s0; e1 += s1; }
+            if (q * RPT < 16 * my_block) { bs0 += s0; bs1 += s1; }
+            if (q * RPT < 16) { end0 += s0; end1 += s1; }
+            tot0 += s0;
+            tot1 += s1;
+        }
+        const float GC0 = tot0, GC1 = tot1;
+        // e^(G_end(0) - G_b(R)) for rows of block 0
+        const float eb0 = __expf(end0 - bs0), eb1 = __expf(end1 - bs1);
+        float G0 = e0, G1 = e1;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int r = r0 + j;
+            G0 += g0[j];
+            G1 += g1[j];
+            const float2 kv = ld2(sKh, r), qv = ld2(sQh, r);
+            const float fh0 = __expf(G0 - bs0), fh1 = __expf(G1 - bs1);
+            const float fi0 = __expf(bs0 - G0), fi1 = __expf(bs1 - G1);
+            const float fc0 = __expf(GC0 - G0), fc1 = __expf(GC1 - G1);
+            st2(sKh, r, kv.x * fh0, kv.y * fh1);
+            const float qh0 = qv.x * fh0, qh1 = qv.y * fh1;
+            st2(sQh, r, qh0, qh1);
+            st2(sQl, r, qh0 - bf16_bits_to_f32(f32_to_bf16_bits(qh0)), qh1 - bf16_bits_to_f32(f32_to_bf16_bits(qh1)));
+            st2(sKi, r, kv.x * fi0, kv.y * fi1);
+            st2(sKb, r, kv.x * fc0, kv.y * fc1);
+            // e^(G_end - G_r) = e^(G_b - G_r) e^(G_end - G_b), both within one block
+            const float fe0 = fi0 * eb0, fe1 = fi1 * eb1;
+            if (my_block == 0) st2(sKe, r, kv.x * fe0, kv.y * fe1);
+            if constexpr (SPLIT) {
+                const float2 bv = ld2(sRawB, r);
+                const float ev0 = bv.x * kv.x, ev1 = bv.y * kv.y;
+                st2(sEi, r, ev0 * fi0, ev1 * fi1);
+                st2(sEb, r, ev0 * fc0, ev1 * fc1);
+                if (my_block == 0) st2(sEe, r, ev0 * fe0, ev1 * fe1);
+            }
+        }
+        if (rq == 0) {
+            sEgb[ch] = 1.f;
+            sEgb[ch + 1] = 1.f;
+            sEgb[DK + ch] = __expf(end0);
+            sEgb[DK + ch + 1] = __expf(end1);
+            sGam[ch] = __expf(GC0);
+            sGam[ch + 1] = __expf(GC1);
+        }
+    }
+    __syncthreads();
+
+    // ---- C x C products over 16x16 tiles (R, J), J <= R; tasks (matrix,
+    // tile) go round-robin over the waves.
+    {
+        constexpr int NTILE = 3;
+        constexpr int NMAT = SPLIT ? 4 : 2;
+        constexpr int NTASK = NTILE * NMAT;
+        constexpr int NW = kPrepThreads / 64;
+        constexpr int MAXT = (NTASK + NW - 1) / NW;
+        // mat 0: A (or A_e)   1: P (or M_k)   2: A_k   3: M_e
+        auto task_rj = [](int tix, int& Rr, int& Jr) {
+            Rr = tix == 0 ? 0 : 1;
+            Jr = tix == 2 ? 1 : 0;
+        };
+        f32x4 acc[MAXT];
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) {
+            const int task = w + NW * k;
+            acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (task < NTASK) {
+                const int mat = task / NTILE, tix = task % NTILE;
+                int Rr, Jr;
+                task_rj(tix, Rr, Jr);
+                const bool useQ = mat == 1 || mat == 3;
+                const bool useE = SPLIT && (mat == 0 || mat == 3);
+                const uint16_t* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
+                const uint16_t* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
+                const uint16_t* brow = bsrc + (16 * Jr + c) * L::LDK;
+                acc[k] = Ops<BF16>::template nat<DK>(acc[k], arow, brow, g);
+                if (useQ) acc[k] = Ops<BF16>::template nat<DK>(acc[k], sQl + (16 * Rr + c) * L::LDK, brow, g);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) {
+            const int task = w + NW * k;
+            if (task < NTASK) {
+                const int mat = task / NTILE, tix = task % NTILE;
+                int Rr, Jr;
+                task_rj(tix, Rr, Jr);
+                const bool strict = mat == 0 || mat == 2;
+                const int col = 16 * Jr + c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * Rr + 4 * g + i;
+                    float val = acc[k][i];
+                    if (!SPLIT && mat == 0) val *= sBeta[row];
+                    val = (strict ? row > col : row >= col) ? val : 0.f;
+                    if (mat == 0) sA[row * L::LDF + col] = val;
+                    else if (mat == 1) sP[row * L::LDM + col] = f32_to_bf16_bits(val);
+                    else if (mat == 2) sAk[row * L::LDM + col] = f32_to_bf16_bits(val);
+                    else sMe[row * L::LDM + col] = f32_to_bf16_bits(val);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A)^-1: diagonal 16x16 blocks by column substitution (fp32),
+    // then T_10 = -T_11 A_10 T_00 (fp32 MFMA)
+    if (w == 0 && lane < 32) {
+        const int rb = 16 * (lane >> 4);
+        const int j = lane & 15;
+        float a[16][16];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(sA + (rb + i) * L::LDF + rb + m4);
+                a[i][m4] = v.x;
+                a[i][m4 + 1] = v.y;
+                a[i][m4 + 2] = v.z;
+                a[i][m4 + 3] = v.w;
+            }
+        }
+        float xs[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) xs[i] -= a[i][m] * xs[m];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sT[(rb + i) * L::LDF + rb + j] = xs[i];
+            sTe[(rb + i) * L::LDM + rb + j] = f32_to_bf16_bits(xs[i]);
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+        float av[4], tv[4], dv[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            av[ks] = sA[(16 + c) * L::LDF + 4 * ks + g];
+            tv[ks] = sT[(4 * ks + g) * L::LDF + c];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv[i] = sT[(16 + c) * L::LDF + 16 + 4 * g + i];
+        f32x4 inner = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) inner = mfma4(av[ks], tv[ks], inner);
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out = mfma4(dv[i], inner[i], out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sTe[(16 + 4 * g + i) * L::LDM + c] = f32_to_bf16_bits(-out[i]);
+    }
+    __syncthreads();
+
+    // ---- the blob: fragments in the chain's lane order
+    unsigned char* blob = ws + (static_cast<int64_t>(bh) * NC + n) * BL::bytes;
+    // row fragments of Kh, Qh, Ql: lane (g, c) of fragment (m, q) holds
+    // row 16 m + c, columns 32 q + 8 g .. + 7
+    for (int idx = tid; idx < 3 * 2 * BL::NKP * 64; idx += kPrepThreads) {
+        const int mat = idx / (2 * BL::NKP * 64), f = (idx / 64) % (2 * BL::NKP), l = idx % 64;
+        const int m = f / BL::NKP, q = f % BL::NKP;
+        const uint16_t* src = (mat == 0 ? sKh : mat == 1 ? sQh : sQl) + (16 * m + (l & 15)) * L::LDK + 32 * q + 8 * (l >> 4);
+        const int off = (mat == 0 ? BL::oKh : mat == 1 ? BL::oQh : BL::oQl) + f * 1024 + l * 16;
+        *reinterpret_cast<uint4*>(blob + off) = *reinterpret_cast<const uint4*>(src);
+    }
+    // transposed key copies for the state update: lane (g, c) of fragment t
+    // holds rows 4 g .. + 3 and 16 + 4 g .. + 3 of the channel that row c of
+    // state tile t holds
+    for (int idx = tid; idx < (SPLIT ? 2 : 1) * BL::NKT * 64; idx += kPrepThreads) {
+        const int mat = idx / (BL::NKT * 64), t = (idx / 64) % BL::NKT, l = idx % 64;
+        const int lg = l >> 4, lc = l & 15;
+        const int ch = perm_chan(t, lc >> 2, lc & 3);
+        const uint16_t* src = (mat == 0 ? sKb : sEb) + ch;
+        uint32_t wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            wv[i / 2] = static_cast<uint32_t>(src[(4 * lg + i) * L::LDK]) |
+                        (static_cast<uint32_t>(src[(4 * lg + i + 1) * L::LDK]) << 16);
+            wv[2 + i / 2] = static_cast<uint32_t>(src[(16 + 4 * lg + i) * L::LDK]) |
+                            (static_cast<uint32_t>(src[(16 + 4 * lg + i + 1) * L::LDK]) << 16);
+        }
+        *reinterpret_cast<uint4*>(blob + (mat == 0 ? BL::oKb : BL::oEb) + t * 1024 + l * 16) =
+            make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    // C x C row fragments: lane (g, c) of fragment m holds row 16 m + c,
+    // columns 4 g .. + 3 (block 0) and 16 + 4 g .. + 3 (block 1; zero for m = 0)
+    for (int idx = tid; idx < (SPLIT ? 4 : 2) * 2 * 64; idx += kPrepThreads) {
+        const int mat = idx / 128, m = (idx / 64) % 2, l = idx % 64;
+        const int lg = l >> 4, lc = l & 15;
+        const uint16_t* M = mat == 0 ? sTe : mat == 1 ? sP : mat == 2 ? sAk : sMe;
+        const uint16_t* row = M + (16 * m + lc) * L::LDM;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * lg);
+        const uint2 hi = m == 0 ? make_uint2(0, 0) : *reinterpret_cast<const uint2*>(row + 16 + 4 * lg);
+        const int base = mat == 0 ? BL::oT : mat == 1 ? BL::oP : mat == 2 ? BL::oAk : BL::oMe;
+        *reinterpret_cast<uint4*>(blob + base + m * 1024 + l * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    // per-channel vectors in state order, and beta
+    float* vec = reinterpret_cast<float*>(blob + BL::oVec);
+    for (int k = tid; k < DK; k += kPrepThreads) {
+        const int t = k / 16, lg = (k / 4) % 4, i = k % 4;
+        const int ch = perm_chan(t, lg, i);
+        vec[BL::vE1 + k] = sEgb[DK + ch];
+        vec[BL::vGam + k] = sGam[ch];
+    }
+    if (tid < C) vec[BL::vBeta + tid] = SPLIT ? 0.f : sBeta[tid];
+}
+
+// ----------------------------------------------------------------- pass 2
+typedef __attribute__((address_space(3))) void lds_void2;
+
+__device__ __forceinline__ void blob_to_lds(const unsigned char* src, unsigned char* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void2*)(lds), 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+    bf16x4 r;
+    r[0] = static_cast<bf16_t>(x[0]);
+    r[1] = static_cast<bf16_t>(x[1]);
+    r[2] = static_cast<bf16_t>(x[2]);
+    r[3] = static_cast<bf16_t>(x[3]);
+    return r;
+}
+
+template <int DK, int DV, bool SPLIT>
+__global__ __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
+    typedef Blob<DK, SPLIT> BL;
+    constexpr int NKP = BL::NKP, NKT = BL::NKT;
+    constexpr int NVT = DV / kVT2;
+    constexpr int LDV = 16 + 8;                 // value staging rows (bf16)
+    constexpr int SLOTS = 3;
+    constexpr int NBL = BL::bytes / 1024;       // 1 KB copy instructions per blob
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SLOTS * BL::bytes + kChainWaves * 2 * kC2 * LDV * 2];
+    const int x = blockIdx.x;
+    const int groups = (p.B * p.H + 7) / 8;
+    const int vt = (x / 8) % NVT;
+    const int bh = (x % 8) * groups + x / (8 * NVT);
+    if (bh >= p.B * p.H) return;
+    const int b = bh / p.H, h = bh % p.H;
+    const int T = p.T, H = p.H;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int vc0 = vt * kVT2 + 16 * w;
+    uint16_t* sV = reinterpret_cast<uint16_t*>(smem + SLOTS * BL::bytes) + w * 2 * kC2 * LDV;   // v, then w
+    const unsigned char* wsh = ws + static_cast<int64_t>(bh) * NC * BL::bytes;
+    auto slot = [&](int n) { return smem + (n % SLOTS) * BL::bytes; };
+    auto copy_blob = [&](int n) {   // both waves; instruction j copies bytes 1024 j .. + 1023
+        const unsigned char* src = wsh + static_cast<int64_t>(n) * BL::bytes + 16 * lane;
+        unsigned char* dst = slot(n);
+        for (int j = w; j < NBL; j += kChainWaves) blob_to_lds(src + 1024 * j, dst + 1024 * j);
+    };
+
+    f32x4 ST[NKT];
+    {
+        const float* s0 = p.S0 ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            if (s0) {
+                const float4 v4 = *reinterpret_cast<const float4*>(s0 + perm_chan(t, g, 0));
+                ST[t] = f32x4{v4.x, v4.y, v4.z, v4.w};
+            } else {
+                ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the state has landed before the loop
+    }
+    // value (and write-gate) rows: lane = 2 row + half, 8 columns per lane
+    uint4 pv = make_uint4(0, 0, 0, 0), pw = pv;
+    auto vload = [&](int n) {
+        const int row = lane >> 1;
+        const int t = min(n * kC2 + row, T - 1);
+        const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * DV + vc0 + 8 * (lane & 1);
+        pv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + off);
+        if constexpr (SPLIT) pw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.wgate) + off);
+    };
+    const int vvo = (4 * g + (c >> 2)) * LDV + 4 * (c & 3);   // transpose reads of the staged rows
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    if (NC > 0) copy_blob(0);
+    if (NC > 1) copy_blob(1);
+    if (NC > 0) vload(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    for (int n = 0; n < NC; ++n) {
+        if (n + 2 < NC) copy_blob(n + 2);
+        const int Cn = min(kC2, T - n * kC2);
+        {   // stage this sub-chunk's value rows (rows past the end are zero)
+            // (component-wise selects: a whole-vector select sends the
+            // registers through scratch memory)
+            const bool ok = (lane >> 1) < Cn;
+            auto sel = [ok](uint4 v) { return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u); };
+            *reinterpret_cast<uint4*>(sV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pv);
+            if constexpr (SPLIT) *reinterpret_cast<uint4*>(sV + kC2 * LDV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pw);
+        }
+        if (n + 1 < NC) vload(n + 1);
+        const unsigned char* bl = slot(n);
+        auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(bl + off + 16 * lane); };
+        const float* vec = reinterpret_cast<const float*>(bl + BL::oVec);
+        bf16x4 vv[2], wr[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            vv[m] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sV + 16 * m * LDV + vvo)));
+            if constexpr (SPLIT)
+                wr[m] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sV + kC2 * LDV + 16 * m * LDV + vvo)));
+        }
+        // the state, and the state decayed to the start of block 1, as B operands
+        bf16x8 SP0[NKP], SP1[NKP];
+#pragma unroll
+        for (int q = 0; q < NKP; ++q) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(vec + BL::vE1 + 32 * q + 4 * g);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + BL::vE1 + 32 * q + 16 + 4 * g);
+            SP0[q] = cat(to_bf4(ST[2 * q]), to_bf4(ST[2 * q + 1]));
+            SP1[q] = cat(to_bf4(ST[2 * q] * e0), to_bf4(ST[2 * q + 1] * e1));
+        }
+        // X_m = Kh_m S_m^T (accumulator layout), Y_m = (Qh + Ql)_m S_m^T
+        // transposed (lane (g, c): row 16 m + c, value columns 4 g .. + 3)
+        f32x4 X[2] = {zero, zero}, Yt[2] = {zero, zero};
+#pragma unroll
+        for (int q = 0; q < NKP; ++q) {
+            X[0] = mfma32(frag(BL::oKh + q * 1024), SP0[q], X[0]);
+            Yt[0] = mfma32(SP0[q], frag(BL::oQh + q * 1024), Yt[0]);
+            Yt[0] = mfma32(SP0[q], frag(BL::oQl + q * 1024), Yt[0]);
+            X[1] = mfma32(frag(BL::oKh + (NKP + q) * 1024), SP1[q], X[1]);
+            Yt[1] = mfma32(SP1[q], frag(BL::oQh + (NKP + q) * 1024), Yt[1]);
+            Yt[1] = mfma32(SP1[q], frag(BL::oQl + (NKP + q) * 1024), Yt[1]);
+        }
+        bf16x8 U01, Wn01;   // the value-side operand of the state update (and -Y~)
+        f32x4 Ot[2];
+        if constexpr (!SPLIT) {
+            bf16x4 Rb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + BL::vBeta + 16 * m + 4 * g);
+                f32x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = bt[i] * (static_cast<float>(vv[m][i]) - X[m][i]);
+                Rb[m] = to_bf4(r);
+            }
+            const bf16x8 R01 = cat(Rb[0], Rb[1]);
+            const f32x4 Vt0 = mfma32(frag(BL::oT), R01, zero);
+            const f32x4 Vt1 = mfma32(frag(BL::oT + 1024), R01, zero);
+            U01 = cat(to_bf4(Vt0), to_bf4(Vt1));
+#pragma unroll
+            for (int m = 0; m < 2; ++m) Ot[m] = mfma32(U01, frag(BL::oP + m * 1024), Yt[m]);
+        } else {
+            bf16x4 Wb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                f32x4 wv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wv[i] = static_cast<float>(vv[m][i]) * static_cast<float>(wr[m][i]);
+                Wb[m] = to_bf4(wv);
+            }
+            U01 = cat(Wb[0], Wb[1]);
+            // Z = X + A_k W, Y~ = T Z
+            const f32x4 Z0 = mfma32(frag(BL::oAk), U01, X[0]);
+            const f32x4 Z1 = mfma32(frag(BL::oAk + 1024), U01, X[1]);
+            const bf16x8 Z01 = cat(to_bf4(Z0), to_bf4(Z1));
+            const f32x4 Y0 = mfma32(frag(BL::oT), Z01, zero);
+            const f32x4 Y1 = mfma32(frag(BL::oT + 1024), Z01, zero);
+            Wn01 = cat(to_bf4(-Y0), to_bf4(-Y1));
+            // O = Y + M_k W - M_e Y~
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                Ot[m] = mfma32(Wn01, frag(BL::oMe + m * 1024), mfma32(U01, frag(BL::oP + m * 1024), Yt[m]));
+        }
+        // S^T <- Diag(e^G_C) S^T + Kb^T U (- Eb^T Y~)
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + BL::vGam + 16 * t + 4 * g);
+            f32x4 s = mfma32(frag(BL::oKb + t * 1024), U01, ST[t] * gm);
+            if constexpr (SPLIT) s = mfma32(frag(BL::oEb + t * 1024), Wn01, s);
+            ST[t] = s;
+        }
+        // outputs: row 16 m + c, value columns vc0 + 4 g .. + 3
+        uint16_t* orow = static_cast<uint16_t*>(p.o) + ((static_cast<int64_t>(b) * T + n * kC2 + c) * H + h) * DV + vc0 + 4 * g;
+        const int64_t mstride = static_cast<int64_t>(16) * H * DV;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = to_bf4(Ot[m]);
+        // the next blob has landed and every wave is done with this one
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+    }
+    if (p.ST) {
+        float* st = p.ST + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+            *reinterpret_cast<float4*>(st + perm_chan(t, g, 0)) = make_float4(ST[t][0], ST[t][1], ST[t][2], ST[t][3]);
+    }
+}
+
+// The workspace comes from a library-owned, stream-ordered memory pool per
+// device that keeps freed memory for reuse (release threshold: unlimited), so
+// repeated calls do not return to the driver for it.
+hipError_t workspace_pool(hipMemPool_t* pool) {
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = ~uint64_t(0);
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return e;
+        pools[dev] = p;
+    }
+    *pool = pools[dev];
+    return hipSuccess;
+}
+
+template <int DK, int DV, bool SPLIT>
+hipError_t launch_two_pass(const FwdArgs& a, hipStream_t s) {
+    typedef Blob<DK, SPLIT> BL;
+    const int NC = (a.T + kC2 - 1) / kC2;
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    unsigned char* ws = nullptr;
+    if (NC > 0) {
+        hipMemPool_t pool;
+        hipError_t e = workspace_pool(&pool);
+        if (e != hipSuccess) return e;
+        e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(heads * NC * BL::bytes), pool, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((cw_prep_kernel<DK, SPLIT>), dim3(static_cast<unsigned>(heads * NC)), dim3(kPrepThreads), 0, s, a, ws, NC);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int NVT = DV / kVT2;
+    const int groups = static_cast<int>((heads + 7) / 8);
+    hipLaunchKernelGGL((cw_chain_kernel<DK, DV, SPLIT>), dim3(static_cast<unsigned>(groups) * 8u * NVT), dim3(64 * kChainWaves), 0, s, a,
+                       ws, NC);
+    hipError_t e = hipGetLastError();
+    if (ws) {
+        const hipError_t f = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
+}
+
+template <bool SPLIT>
+hipError_t launch_two_pass_dims(const FwdArgs& a, hipStream_t s) {
+    if (a.dk == 128 && a.dv == 128) return launch_two_pass<128, 128, SPLIT>(a, s);
+    if (a.dk == 128 && a.dv == 64) return launch_two_pass<128, 64, SPLIT>(a, s);
+    if (a.dk == 64 && a.dv == 128) return launch_two_pass<64, 128, SPLIT>(a, s);
+    return launch_two_pass<64, 64, SPLIT>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t s) {
+    return variant == 2 ? launch_two_pass_dims<false>(a, s) : launch_two_pass_dims<true>(a, s);
+}
+
+}  // namespace dr
