@@ -24,10 +24,11 @@
 // workspace as the exact LDS image that pass 2 reads (a "blob": MFMA operand
 // fragments of 16 bytes per lane, 1 KB per fragment, lane-linear, plus the
 // per-channel decay vectors).  Pass 2 runs the recurrence per (batch, head, 32
-// value columns): two waves, each carrying a 128 x 16 slice of S^T in fp32
-// accumulators, copy the blob of sub-chunk n + 2 into LDS with
-// global_load_lds while they run sub-chunk n, so the copy is one linear
-// stream and no address arithmetic.
+// value columns): two waves each carry a 128 x 16 slice of S^T in fp32
+// accumulators and run sub-chunk n, while a third wave copies the blob of
+// sub-chunk n + 2 into LDS with global_load_lds: one linear stream, no
+// address arithmetic, and no copy instructions in the waves that carry the
+// state (issuing them there stalled those waves by about 2K cycles a step).
 //
 // The state's key channels are held in a permuted order (tile t, lane (g, c),
 // element i <-> channel 32 (t / 2) + 8 g + 4 (t % 2) + i), so that two state
@@ -429,7 +430,7 @@ __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
 }
 
 template <int DK, int DV, bool SPLIT>
-__global__ __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (kChainWaves + 1)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     typedef Blob<DK, SPLIT> BL;
     constexpr int NKP = BL::NKP, NKT = BL::NKT;
@@ -448,15 +449,31 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
+    auto slot = [&](int n) { return smem + (n % SLOTS) * BL::bytes; };
+    if (w == kChainWaves) {
+        // ---- loader: the blob of sub-chunk n + 2 during step n; instruction
+        // j copies bytes 1024 j .. + 1023 (lane l: 16 l .. + 15).  One barrier
+        // per step, matching the chain waves'.
+        const unsigned char* wsh = ws + static_cast<int64_t>(bh) * NC * BL::bytes + 16 * lane;
+        auto copy_blob = [&](int n) {
+            const unsigned char* src = wsh + static_cast<int64_t>(n) * BL::bytes;
+            unsigned char* dst = slot(n);
+#pragma unroll
+            for (int j = 0; j < NBL; ++j) blob_to_lds(src + 1024 * j, dst + 1024 * j);
+        };
+        if (NC > 0) copy_blob(0);
+        if (NC > 1) copy_blob(1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+        for (int n = 0; n < NC; ++n) {
+            if (n + 2 < NC) copy_blob(n + 2);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): landed before the barrier
+            __syncthreads();
+        }
+        return;
+    }
     const int vc0 = vt * kVT2 + 16 * w;
     uint16_t* sV = reinterpret_cast<uint16_t*>(smem + SLOTS * BL::bytes) + w * 2 * kC2 * LDV;   // v, then w
-    const unsigned char* wsh = ws + static_cast<int64_t>(bh) * NC * BL::bytes;
-    auto slot = [&](int n) { return smem + (n % SLOTS) * BL::bytes; };
-    auto copy_blob = [&](int n) {   // both waves; instruction j copies bytes 1024 j .. + 1023
-        const unsigned char* src = wsh + static_cast<int64_t>(n) * BL::bytes + 16 * lane;
-        unsigned char* dst = slot(n);
-        for (int j = w; j < NBL; j += kChainWaves) blob_to_lds(src + 1024 * j, dst + 1024 * j);
-    };
 
     f32x4 ST[NKT];
     {
@@ -484,13 +501,11 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     const int vvo = (4 * g + (c >> 2)) * LDV + 4 * (c & 3);   // transpose reads of the staged rows
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    if (NC > 0) copy_blob(0);
-    if (NC > 1) copy_blob(1);
     if (NC > 0) vload(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
+    bf16x4 od[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // output rows being stored
+    uint16_t* oad[2] = {nullptr, nullptr};          // and their addresses
     for (int n = 0; n < NC; ++n) {
-        if (n + 2 < NC) copy_blob(n + 2);
         const int Cn = min(kC2, T - n * kC2);
         {   // stage this sub-chunk's value rows (rows past the end are zero)
             // (component-wise selects: a whole-vector select sends the
@@ -580,15 +595,21 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
             if constexpr (SPLIT) s = mfma32(frag(BL::oEb + t * 1024), Wn01, s);
             ST[t] = s;
         }
-        // outputs: row 16 m + c, value columns vc0 + 4 g .. + 3
+        // outputs: row 16 m + c, value columns vc0 + 4 g .. + 3.  The store
+        // registers (data and address) stay reserved until the next step
+        // refills them, so no instruction waits for the stores to drain.
+        asm volatile("" ::"v"(od[0]), "v"(od[1]), "v"(oad[0]), "v"(oad[1]));
         uint16_t* orow = static_cast<uint16_t*>(p.o) + ((static_cast<int64_t>(b) * T + n * kC2 + c) * H + h) * DV + vc0 + 4 * g;
         const int64_t mstride = static_cast<int64_t>(16) * H * DV;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(orow + m * mstride) = to_bf4(Ot[m]);
-        // the next blob has landed and every wave is done with this one
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
+        for (int m = 0; m < 2; ++m) {
+            od[m] = to_bf4(Ot[m]);
+            oad[m] = orow + m * mstride;
+            if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(oad[m]) = od[m];
+        }
+        // this wave's reads of the slot are done (the loader refills it in
+        // the next step); the blob of sub-chunk n + 1 has landed
+        lds_barrier();
     }
     if (p.ST) {
         float* st = p.ST + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK;
@@ -644,7 +665,7 @@ hipError_t launch_two_pass(const FwdArgs& a, hipStream_t s) {
     }
     constexpr int NVT = DV / kVT2;
     const int groups = static_cast<int>((heads + 7) / 8);
-    hipLaunchKernelGGL((cw_chain_kernel<DK, DV, SPLIT>), dim3(static_cast<unsigned>(groups) * 8u * NVT), dim3(64 * kChainWaves), 0, s, a,
+    hipLaunchKernelGGL((cw_chain_kernel<DK, DV, SPLIT>), dim3(static_cast<unsigned>(groups) * 8u * NVT), dim3(64 * (kChainWaves + 1)), 0, s, a,
                        ws, NC);
     hipError_t e = hipGetLastError();
     if (ws) {
