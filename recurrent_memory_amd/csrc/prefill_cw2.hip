@@ -461,14 +461,25 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
 #pragma unroll
             for (int j = 0; j < NBL; ++j) blob_to_lds(src + 1024 * j, dst + 1024 * j);
         };
+        // The copy of blob n + 2 gets two steps: the wait at the end of step
+        // n leaves this step's NBL copies in flight (vector memory operations
+        // complete in issue order) and only requires blob n + 1, which the
+        // chain reads in step n + 1.  Slot (n + 2) % 3 is not read before step
+        // n + 2.
+        constexpr int kWaitPrev = (NBL & 0xF) | ((NBL >> 4) << 14) | (0x7 << 4) | (0xF << 8);   // vmcnt(NBL)
+        static_assert(NBL < 64, "vmcnt range");
         if (NC > 0) copy_blob(0);
         if (NC > 1) copy_blob(1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
         for (int n = 0; n < NC; ++n) {
-            if (n + 2 < NC) copy_blob(n + 2);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): landed before the barrier
-            __syncthreads();
+            if (n + 2 < NC) {
+                copy_blob(n + 2);
+                __builtin_amdgcn_s_waitcnt(kWaitPrev);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            }
+            lds_barrier();
         }
         return;
     }
@@ -501,70 +512,117 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     const int vvo = (4 * g + (c >> 2)) * LDV + 4 * (c & 3);   // transpose reads of the staged rows
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    if (NC > 0) vload(0);
-    __syncthreads();
-    bf16x4 od[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // output rows being stored
-    uint16_t* oad[2] = {nullptr, nullptr};          // and their addresses
-    for (int n = 0; n < NC; ++n) {
-        const int Cn = min(kC2, T - n * kC2);
-        {   // stage this sub-chunk's value rows (rows past the end are zero)
-            // (component-wise selects: a whole-vector select sends the
-            // registers through scratch memory)
-            const bool ok = (lane >> 1) < Cn;
-            auto sel = [ok](uint4 v) { return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u); };
-            *reinterpret_cast<uint4*>(sV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pv);
-            if constexpr (SPLIT) *reinterpret_cast<uint4*>(sV + kC2 * LDV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pw);
+    // Operands of sub-chunk n that open its step (the key/query fragments
+    // and decay vector of X and Y, and the staged value rows) are read during
+    // step n - 1, right after their registers are last used: blob n is
+    // complete from the start of step n - 1, and the value rows are the
+    // wave's own.
+    bf16x8 kh[2 * NKP], qh[2 * NKP], ql[2 * NKP];
+    f32x4 e1v[NKT];
+    bf16x4 vv[2], wr[2];
+    // the rest of sub-chunk n's operands, read during step n - 1 after the
+    // state update, when their registers are free
+    bf16x8 tf[2], pf[2], af[2], mf[2], kbt[NKT], ebt[NKT];
+    f32x4 gmv[NKT], btv[2];
+    auto read_rest = [&](int n) {
+        const unsigned char* bl = slot(n) + 16 * lane;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            tf[m] = *reinterpret_cast<const bf16x8*>(bl + BL::oT + m * 1024);
+            pf[m] = *reinterpret_cast<const bf16x8*>(bl + BL::oP + m * 1024);
+            if constexpr (SPLIT) {
+                af[m] = *reinterpret_cast<const bf16x8*>(bl + BL::oAk + m * 1024);
+                mf[m] = *reinterpret_cast<const bf16x8*>(bl + BL::oMe + m * 1024);
+            }
         }
-        if (n + 1 < NC) vload(n + 1);
-        const unsigned char* bl = slot(n);
-        auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(bl + off + 16 * lane); };
-        const float* vec = reinterpret_cast<const float*>(bl + BL::oVec);
-        bf16x4 vv[2], wr[2];
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) {
+            kbt[t] = *reinterpret_cast<const bf16x8*>(bl + BL::oKb + t * 1024);
+            if constexpr (SPLIT) ebt[t] = *reinterpret_cast<const bf16x8*>(bl + BL::oEb + t * 1024);
+        }
+        const float* vec = reinterpret_cast<const float*>(slot(n) + BL::oVec);
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) gmv[t] = *reinterpret_cast<const f32x4*>(vec + BL::vGam + 16 * t + 4 * g);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) btv[m] = *reinterpret_cast<const f32x4*>(vec + BL::vBeta + 16 * m + 4 * g);
+    };
+    auto read_xy = [&](int n) {
+        const unsigned char* bl = slot(n) + 16 * lane;
+#pragma unroll
+        for (int f = 0; f < 2 * NKP; ++f) {
+            kh[f] = *reinterpret_cast<const bf16x8*>(bl + BL::oKh + f * 1024);
+            qh[f] = *reinterpret_cast<const bf16x8*>(bl + BL::oQh + f * 1024);
+            ql[f] = *reinterpret_cast<const bf16x8*>(bl + BL::oQl + f * 1024);
+        }
+        const float* vec = reinterpret_cast<const float*>(slot(n) + BL::oVec);
+#pragma unroll
+        for (int t = 0; t < NKT; ++t) e1v[t] = *reinterpret_cast<const f32x4*>(vec + BL::vE1 + 16 * t + 4 * g);
+    };
+    // stage the value rows of sub-chunk n (rows past the end are zero;
+    // component-wise selects, since a whole-vector select sends the registers
+    // through scratch memory) and read them back in accumulator layout
+    auto stage_v = [&](int n) {
+        const bool ok = (lane >> 1) < min(kC2, T - n * kC2);
+        auto sel = [ok](uint4 v) { return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u); };
+        *reinterpret_cast<uint4*>(sV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pv);
+        if constexpr (SPLIT) *reinterpret_cast<uint4*>(sV + kC2 * LDV + (lane >> 1) * LDV + 8 * (lane & 1)) = sel(pw);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             vv[m] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sV + 16 * m * LDV + vvo)));
             if constexpr (SPLIT)
                 wr[m] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(sV + kC2 * LDV + 16 * m * LDV + vvo)));
         }
+    };
+    if (NC > 0) vload(0);
+    __syncthreads();
+    if (NC > 0) {
+        read_xy(0);
+        read_rest(0);
+        stage_v(0);
+        if (NC > 1) vload(1);
+    }
+    bf16x4 od[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // output rows being stored
+    uint16_t* oad[2] = {nullptr, nullptr};          // and their addresses
+    for (int n = 0; n < NC; ++n) {
+        const int Cn = min(kC2, T - n * kC2);
         // the state, and the state decayed to the start of block 1, as B operands
         bf16x8 SP0[NKP], SP1[NKP];
 #pragma unroll
         for (int q = 0; q < NKP; ++q) {
-            const f32x4 e0 = *reinterpret_cast<const f32x4*>(vec + BL::vE1 + 32 * q + 4 * g);
-            const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + BL::vE1 + 32 * q + 16 + 4 * g);
             SP0[q] = cat(to_bf4(ST[2 * q]), to_bf4(ST[2 * q + 1]));
-            SP1[q] = cat(to_bf4(ST[2 * q] * e0), to_bf4(ST[2 * q + 1] * e1));
+            SP1[q] = cat(to_bf4(ST[2 * q] * e1v[2 * q]), to_bf4(ST[2 * q + 1] * e1v[2 * q + 1]));
         }
         // X_m = Kh_m S_m^T (accumulator layout), Y_m = (Qh + Ql)_m S_m^T
         // transposed (lane (g, c): row 16 m + c, value columns 4 g .. + 3)
         f32x4 X[2] = {zero, zero}, Yt[2] = {zero, zero};
 #pragma unroll
         for (int q = 0; q < NKP; ++q) {
-            X[0] = mfma32(frag(BL::oKh + q * 1024), SP0[q], X[0]);
-            Yt[0] = mfma32(SP0[q], frag(BL::oQh + q * 1024), Yt[0]);
-            Yt[0] = mfma32(SP0[q], frag(BL::oQl + q * 1024), Yt[0]);
-            X[1] = mfma32(frag(BL::oKh + (NKP + q) * 1024), SP1[q], X[1]);
-            Yt[1] = mfma32(SP1[q], frag(BL::oQh + (NKP + q) * 1024), Yt[1]);
-            Yt[1] = mfma32(SP1[q], frag(BL::oQl + (NKP + q) * 1024), Yt[1]);
+            X[0] = mfma32(kh[q], SP0[q], X[0]);
+            Yt[0] = mfma32(SP0[q], qh[q], Yt[0]);
+            Yt[0] = mfma32(SP0[q], ql[q], Yt[0]);
+            X[1] = mfma32(kh[NKP + q], SP1[q], X[1]);
+            Yt[1] = mfma32(SP1[q], qh[NKP + q], Yt[1]);
+            Yt[1] = mfma32(SP1[q], ql[NKP + q], Yt[1]);
         }
+        // (the last step reads a slot that nothing writes any more)
+        read_xy(n + 1 < NC ? n + 1 : n);
         bf16x8 U01, Wn01;   // the value-side operand of the state update (and -Y~)
         f32x4 Ot[2];
         if constexpr (!SPLIT) {
             bf16x4 Rb[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const f32x4 bt = *reinterpret_cast<const f32x4*>(vec + BL::vBeta + 16 * m + 4 * g);
                 f32x4 r;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) r[i] = bt[i] * (static_cast<float>(vv[m][i]) - X[m][i]);
+                for (int i = 0; i < 4; ++i) r[i] = btv[m][i] * (static_cast<float>(vv[m][i]) - X[m][i]);
                 Rb[m] = to_bf4(r);
             }
             const bf16x8 R01 = cat(Rb[0], Rb[1]);
-            const f32x4 Vt0 = mfma32(frag(BL::oT), R01, zero);
-            const f32x4 Vt1 = mfma32(frag(BL::oT + 1024), R01, zero);
+            const f32x4 Vt0 = mfma32(tf[0], R01, zero);
+            const f32x4 Vt1 = mfma32(tf[1], R01, zero);
             U01 = cat(to_bf4(Vt0), to_bf4(Vt1));
 #pragma unroll
-            for (int m = 0; m < 2; ++m) Ot[m] = mfma32(U01, frag(BL::oP + m * 1024), Yt[m]);
+            for (int m = 0; m < 2; ++m) Ot[m] = mfma32(U01, pf[m], Yt[m]);
         } else {
             bf16x4 Wb[2];
 #pragma unroll
@@ -576,25 +634,24 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
             }
             U01 = cat(Wb[0], Wb[1]);
             // Z = X + A_k W, Y~ = T Z
-            const f32x4 Z0 = mfma32(frag(BL::oAk), U01, X[0]);
-            const f32x4 Z1 = mfma32(frag(BL::oAk + 1024), U01, X[1]);
+            const f32x4 Z0 = mfma32(af[0], U01, X[0]);
+            const f32x4 Z1 = mfma32(af[1], U01, X[1]);
             const bf16x8 Z01 = cat(to_bf4(Z0), to_bf4(Z1));
-            const f32x4 Y0 = mfma32(frag(BL::oT), Z01, zero);
-            const f32x4 Y1 = mfma32(frag(BL::oT + 1024), Z01, zero);
+            const f32x4 Y0 = mfma32(tf[0], Z01, zero);
+            const f32x4 Y1 = mfma32(tf[1], Z01, zero);
             Wn01 = cat(to_bf4(-Y0), to_bf4(-Y1));
             // O = Y + M_k W - M_e Y~
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                Ot[m] = mfma32(Wn01, frag(BL::oMe + m * 1024), mfma32(U01, frag(BL::oP + m * 1024), Yt[m]));
+            for (int m = 0; m < 2; ++m) Ot[m] = mfma32(Wn01, mf[m], mfma32(U01, pf[m], Yt[m]));
         }
         // S^T <- Diag(e^G_C) S^T + Kb^T U (- Eb^T Y~)
 #pragma unroll
         for (int t = 0; t < NKT; ++t) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(vec + BL::vGam + 16 * t + 4 * g);
-            f32x4 s = mfma32(frag(BL::oKb + t * 1024), U01, ST[t] * gm);
-            if constexpr (SPLIT) s = mfma32(frag(BL::oEb + t * 1024), Wn01, s);
+            f32x4 s = mfma32(kbt[t], U01, ST[t] * gmv[t]);
+            if constexpr (SPLIT) s = mfma32(ebt[t], Wn01, s);
             ST[t] = s;
         }
+        read_rest(n + 1 < NC ? n + 1 : n);
         // outputs: row 16 m + c, value columns vc0 + 4 g .. + 3.  The store
         // registers (data and address) stay reserved until the next step
         // refills them, so no instruction waits for the stores to drain.
@@ -606,6 +663,10 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
             od[m] = to_bf4(Ot[m]);
             oad[m] = orow + m * mstride;
             if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(oad[m]) = od[m];
+        }
+        if (n + 1 < NC) {
+            stage_v(n + 1);
+            if (n + 2 < NC) vload(n + 2);
         }
         // this wave's reads of the slot are done (the loader refills it in
         // the next step); the blob of sub-chunk n + 1 has landed
