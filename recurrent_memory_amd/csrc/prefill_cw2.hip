@@ -34,6 +34,7 @@
 // element i <-> channel 32 (t / 2) + 8 g + 4 (t % 2) + i), so that two state
 // tiles paired as one B operand cover 8 consecutive channels and a key/query
 // fragment is one contiguous 16-byte piece of a row.
+#include <algorithm>
 #include <mutex>
 
 #include "chunk_ops.h"
@@ -106,8 +107,11 @@ struct PrepLds {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
+// Persistent: workgroup i handles units i, i + gridDim.x, ... (unit = head *
+// NC + sub-chunk) and loads the raw inputs of its next unit into registers
+// while it works on the current one.
 template <int DK, bool SPLIT>
-__global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsigned char* ws, int NC) {
+__global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsigned char* ws, int NC, int total) {
     typedef PrepLds<DK, SPLIT> L;
     typedef Blob<DK, SPLIT> BL;
     constexpr int C = kC2;
@@ -134,41 +138,61 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
     float* sEgb = sBeta + C;          // [NB][DK]
     float* sGam = sEgb + NB * DK;     // [DK]
 
-    const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
-    const int b = bh / p.H, h = bh % p.H;
     const int T = p.T, H = p.H;
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int t0 = n * C;
-    const int Cn = min(C, T - t0);
-    const int64_t tokb = static_cast<int64_t>(b) * T + t0;
-
-    // ---- raw q, k, g (and the erase gate) of the sub-chunk; rows past the
-    // end are zero (zero decay, no key, no query)
-    {
-        constexpr int PPR = DK / 8;   // 16-byte pieces per row
-        for (int idx = tid; idx < C * PPR; idx += kPrepThreads) {
+    // raw q, k, g (and the erase gate) of a unit: 16-byte pieces; rows past
+    // the end of the sequence are zero (zero decay, no key, no query)
+    constexpr int PPR = DK / 8;                       // pieces per row
+    constexpr int NPC = C * PPR / kPrepThreads;       // pieces per thread
+    static_assert(C * PPR % kPrepThreads == 0, "piece split");
+    uint4 rq[NPC], rk[NPC], rg[NPC], rb[NPC];
+    uint16_t rbeta = 0;
+    auto fetch = [&](int unit) {
+        const int ubh = unit / NC, un = unit % NC;
+        const int ub = ubh / H, uh = ubh % H;
+        const int ucn = min(C, T - un * C);
+        const int64_t utok = static_cast<int64_t>(ub) * T + un * C;
+#pragma unroll
+        for (int j = 0; j < NPC; ++j) {
+            const int idx = tid + kPrepThreads * j;
             const int row = idx / PPR, cc = idx % PPR;
-            uint4 vq = make_uint4(0, 0, 0, 0), vk = vq, vg = vq, vb = vq;
-            if (row < Cn) {
-                const int64_t off = ((tokb + row) * H + h) * DK + 8 * cc;
-                vq = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
-                vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
-                vg = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.g) + off);
-                if constexpr (SPLIT) vb = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
+            rq[j] = make_uint4(0, 0, 0, 0);
+            rk[j] = rq[j];
+            rg[j] = rq[j];
+            rb[j] = rq[j];
+            if (row < ucn) {
+                const int64_t off = ((utok + row) * H + uh) * DK + 8 * cc;
+                rq[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
+                rk[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
+                rg[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.g) + off);
+                if constexpr (SPLIT) rb[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
             }
-            *reinterpret_cast<uint4*>(sQh + row * L::LDK + 8 * cc) = vq;
-            *reinterpret_cast<uint4*>(sKh + row * L::LDK + 8 * cc) = vk;
-            *reinterpret_cast<uint4*>(sRawG + row * L::LDK + 8 * cc) = vg;
-            if constexpr (SPLIT) *reinterpret_cast<uint4*>(sRawB + row * L::LDK + 8 * cc) = vb;
         }
         if constexpr (!SPLIT) {
-            if (tid < C)
-                sBeta[tid] = tid < Cn ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.beta)[(tokb + tid) * H + h]) : 0.f;
+            rbeta = 0;
+            if (tid < ucn) rbeta = static_cast<const uint16_t*>(p.beta)[(utok + tid) * H + uh];
         }
+    };
+    if (static_cast<int>(blockIdx.x) < total) fetch(blockIdx.x);
+    for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+    const int bh = unit / NC, n = unit % NC;
+    // ---- commit the raw inputs, then start fetching the next unit's
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+        const int idx = tid + kPrepThreads * j;
+        const int row = idx / PPR, cc = idx % PPR;
+        *reinterpret_cast<uint4*>(sQh + row * L::LDK + 8 * cc) = rq[j];
+        *reinterpret_cast<uint4*>(sKh + row * L::LDK + 8 * cc) = rk[j];
+        *reinterpret_cast<uint4*>(sRawG + row * L::LDK + 8 * cc) = rg[j];
+        if constexpr (SPLIT) *reinterpret_cast<uint4*>(sRawB + row * L::LDK + 8 * cc) = rb[j];
+    }
+    if constexpr (!SPLIT) {
+        if (tid < C) sBeta[tid] = bf16_bits_to_f32(rbeta);
     }
     __syncthreads();
+    if (unit + static_cast<int>(gridDim.x) < total) fetch(unit + gridDim.x);
 
     // ---- per channel: cumulative decay and the decay-carrying copies.
     // Thread (channel pair cp, row group rq): channels 2 cp, 2 cp + 1 and RPT
@@ -411,6 +435,9 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
         vec[BL::vGam + k] = sGam[ch];
     }
     if (tid < C) vec[BL::vBeta + tid] = SPLIT ? 0.f : sBeta[tid];
+    // the next unit's commit overwrites the LDS read above
+    __syncthreads();
+    }
 }
 
 // ----------------------------------------------------------------- pass 2
@@ -720,7 +747,21 @@ hipError_t launch_two_pass(const FwdArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(heads * NC * BL::bytes), pool, s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((cw_prep_kernel<DK, SPLIT>), dim3(static_cast<unsigned>(heads * NC)), dim3(kPrepThreads), 0, s, a, ws, NC);
+        // persistent pass 1: as many workgroups as fit on the device at once
+        static int resident = 0;   // per template instance; MI355X only
+        if (resident == 0) {
+            int dev = 0, cus = 0, per_cu = 0;
+            e = hipGetDevice(&dev);
+            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e == hipSuccess)
+                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cw_prep_kernel<DK, SPLIT>, kPrepThreads, 0);
+            if (e != hipSuccess) return e;
+            resident = std::max(1, cus * per_cu);
+        }
+        const int64_t total = heads * NC;
+        if (total > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
+        const unsigned grid = static_cast<unsigned>(std::min<int64_t>(total, resident));
+        hipLaunchKernelGGL((cw_prep_kernel<DK, SPLIT>), dim3(grid), dim3(kPrepThreads), 0, s, a, ws, NC, static_cast<int>(total));
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
