@@ -31,8 +31,14 @@
  * Conventions shared by every entry point
  *  - All tensor arguments are DEVICE pointers on the current HIP device, dense
  *    and row-major with the shapes given below (no strides).  Every pointer
- *    must be 16-byte aligned.  The caller owns every buffer; the library
- *    allocates no device memory and keeps no per-call state.
+ *    must be 16-byte aligned.  The caller owns every buffer, and no per-call
+ *    state is kept.  The only memory the library allocates is the temporary
+ *    workspace of delta_fwd for DR_KDA and DR_GDN2 with DR_BF16 operands:
+ *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2: 50 KiB) for d_k = 128,
+ *    21 KiB (29 KiB) for d_k = 64, taken from a library-owned stream-ordered
+ *    memory pool of the current device and returned to it on the call's
+ *    stream after use; the pool keeps freed memory for reuse until the
+ *    process ends.  A failed workspace allocation is reported as DR_E_LAUNCH.
  *  - dtype (dr_desc.dtype) is the element type of q, k, v, beta, wgate, g and
  *    o.  The state (S0, S_T, S) is always fp32.
  *  - The stream argument is a hipStream_t (NULL = the null stream).  Calls are

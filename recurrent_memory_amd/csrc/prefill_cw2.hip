@@ -35,6 +35,7 @@
 // tiles paired as one B operand cover 8 consecutive channels and a key/query
 // fragment is one contiguous 16-byte piece of a row.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "chunk_ops.h"
@@ -735,35 +736,48 @@ hipError_t workspace_pool(hipMemPool_t* pool) {
     return hipSuccess;
 }
 
+// Workgroups of pass 1 resident on the device at once (it is persistent).
+template <int DK, bool SPLIT>
+hipError_t prep_resident(int* out) {
+    static std::atomic<int> cached{0};   // per template instance; one device model
+    int r = cached.load(std::memory_order_relaxed);
+    if (r == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cw_prep_kernel<DK, SPLIT>, kPrepThreads, 0);
+        if (e != hipSuccess) return e;
+        r = std::max(1, cus * per_cu);
+        cached.store(r, std::memory_order_relaxed);
+    }
+    *out = r;
+    return hipSuccess;
+}
+
 template <int DK, int DV, bool SPLIT>
 hipError_t launch_two_pass(const FwdArgs& a, hipStream_t s) {
     typedef Blob<DK, SPLIT> BL;
     const int NC = (a.T + kC2 - 1) / kC2;
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    const int64_t total = heads * NC;   // pass-1 units
+    if (total > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
     unsigned char* ws = nullptr;
     if (NC > 0) {
+        int resident = 0;
+        hipError_t e = prep_resident<DK, SPLIT>(&resident);
+        if (e != hipSuccess) return e;
         hipMemPool_t pool;
-        hipError_t e = workspace_pool(&pool);
+        e = workspace_pool(&pool);
         if (e != hipSuccess) return e;
-        e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(heads * NC * BL::bytes), pool, s);
+        e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total * BL::bytes), pool, s);
         if (e != hipSuccess) return e;
-        // persistent pass 1: as many workgroups as fit on the device at once
-        static int resident = 0;   // per template instance; MI355X only
-        if (resident == 0) {
-            int dev = 0, cus = 0, per_cu = 0;
-            e = hipGetDevice(&dev);
-            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (e == hipSuccess)
-                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cw_prep_kernel<DK, SPLIT>, kPrepThreads, 0);
-            if (e != hipSuccess) return e;
-            resident = std::max(1, cus * per_cu);
-        }
-        const int64_t total = heads * NC;
-        if (total > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
         const unsigned grid = static_cast<unsigned>(std::min<int64_t>(total, resident));
         hipLaunchKernelGGL((cw_prep_kernel<DK, SPLIT>), dim3(grid), dim3(kPrepThreads), 0, s, a, ws, NC, static_cast<int>(total));
         e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(ws, s);
+            return e;
+        }
     }
     constexpr int NVT = DV / kVT2;
     const int groups = static_cast<int>((heads + 7) / 8);
