@@ -489,24 +489,16 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
 #pragma unroll
             for (int j = 0; j < NBL; ++j) blob_to_lds(src + 1024 * j, dst + 1024 * j);
         };
-        // The copy of blob n + 2 gets two steps: the wait at the end of step
-        // n leaves this step's NBL copies in flight (vector memory operations
-        // complete in issue order) and only requires blob n + 1, which the
-        // chain reads in step n + 1.  Slot (n + 2) % 3 is not read before step
-        // n + 2.
-        constexpr int kWaitPrev = (NBL & 0xF) | ((NBL >> 4) << 14) | (0x7 << 4) | (0xF << 8);   // vmcnt(NBL)
-        static_assert(NBL < 64, "vmcnt range");
+        // The copy of blob n + 2 issued in step n must have landed by the end
+        // of step n: the chain waves read blob n + 2 into registers during
+        // step n + 1, one step ahead of its use.
         if (NC > 0) copy_blob(0);
         if (NC > 1) copy_blob(1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
         for (int n = 0; n < NC; ++n) {
-            if (n + 2 < NC) {
-                copy_blob(n + 2);
-                __builtin_amdgcn_s_waitcnt(kWaitPrev);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            }
+            if (n + 2 < NC) copy_blob(n + 2);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             lds_barrier();
         }
         return;
