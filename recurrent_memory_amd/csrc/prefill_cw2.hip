@@ -86,24 +86,32 @@ struct PrepLds {
     static constexpr int KE = 16 * LDK * 2;
     static constexpr int MM = C * LDM * 2;
     static constexpr int MF = C * LDF * 4;
+    // live for the whole unit: the copies that go into the blob
     static constexpr int oKh = 0;
     static constexpr int oQh = oKh + KM;
     static constexpr int oQl = oQh + KM;
-    static constexpr int oKi = oQl + KM;
-    static constexpr int oKb = oKi + KM;
-    static constexpr int oKe = oKb + KM;
-    static constexpr int oEi = oKe + KE;
-    static constexpr int oEb = oEi + (SPLIT ? KM : 0);
-    static constexpr int oEe = oEb + (SPLIT ? KM : 0);
-    static constexpr int oRawG = oEe + (SPLIT ? KE : 0);
+    static constexpr int oKb = oQl + KM;
+    static constexpr int oEb = oKb + KM;
+    // one region used three times, separated by barriers: the raw gates,
+    // then the copies that only the C x C products read, then their results
+    static constexpr int oR = oEb + (SPLIT ? KM : 0);
+    static constexpr int oRawG = oR;
     static constexpr int oRawB = oRawG + KM;
-    static constexpr int oA = oRawB + (SPLIT ? KM : 0);   // A or A_e (fp32)
+    static constexpr int oKi = oR;
+    static constexpr int oKe = oKi + KM;
+    static constexpr int oEi = oKe + KE;
+    static constexpr int oEe = oEi + (SPLIT ? KM : 0);
+    static constexpr int oA = oR;                         // A or A_e (fp32)
     static constexpr int oT = oA + MF;                    // T (fp32)
     static constexpr int oTe = oT + MF;                   // T (bf16)
     static constexpr int oP = oTe + MM;                   // P or M_k
     static constexpr int oAk = oP + MM;
     static constexpr int oMe = oAk + (SPLIT ? MM : 0);
-    static constexpr int oVec = oMe + (SPLIT ? MM : 0);   // beta[C], e^G_b [2][DK], e^G_C [DK]
+    static constexpr int R1 = (SPLIT ? 2 : 1) * KM;
+    static constexpr int R2 = (SPLIT ? 2 : 1) * (KM + KE);
+    static constexpr int R3 = 2 * MF + (SPLIT ? 4 : 2) * MM;
+    static constexpr int RB = R1 > R2 ? (R1 > R3 ? R1 : R3) : (R2 > R3 ? R2 : R3);
+    static constexpr int oVec = oR + RB;                  // beta[C], e^G_b [2][DK], e^G_C [DK]
     static constexpr int bytes = oVec + (C + 3 * DK) * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
@@ -112,7 +120,7 @@ struct PrepLds {
 // NC + sub-chunk) and loads the raw inputs of its next unit into registers
 // while it works on the current one.
 template <int DK, bool SPLIT>
-__global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsigned char* ws, int NC, int total) {
+__global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, unsigned char* ws, int NC, int total) {
     typedef PrepLds<DK, SPLIT> L;
     typedef Blob<DK, SPLIT> BL;
     constexpr int C = kC2;
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
             *reinterpret_cast<uint32_t*>(m + r * L::LDK + ch) =
                 static_cast<uint32_t>(f32_to_bf16_bits(x0)) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16);
         };
-        float g0[RPT], g1[RPT];
+        float g0[RPT], g1[RPT], b0[RPT], b1[RPT];
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
@@ -223,7 +231,14 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
             g1[j] = v.y;
             p0 += v.x;
             p1 += v.y;
+            if constexpr (SPLIT) {
+                const float2 bv = ld2(sRawB, r0 + j);
+                b0[j] = bv.x;
+                b1[j] = bv.y;
+            }
         }
+        // the copies below overwrite the raw gates
+        __syncthreads();
         float e0 = 0.f, e1 = 0.f, tot0 = 0.f, tot1 = 0.f, bs0 = 0.f, bs1 = 0.f, end0 = 0.f, end1 = 0.f;
         const int my_block = r0 / 16;
 #pragma unroll
@@ -259,8 +274,7 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
             const float fe0 = fi0 * eb0, fe1 = fi1 * eb1;
             if (my_block == 0) st2(sKe, r, kv.x * fe0, kv.y * fe1);
             if constexpr (SPLIT) {
-                const float2 bv = ld2(sRawB, r);
-                const float ev0 = bv.x * kv.x, ev1 = bv.y * kv.y;
+                const float ev0 = b0[j] * kv.x, ev1 = b1[j] * kv.y;
                 st2(sEi, r, ev0 * fi0, ev1 * fi1);
                 st2(sEb, r, ev0 * fc0, ev1 * fc1);
                 if (my_block == 0) st2(sEe, r, ev0 * fe0, ev1 * fe1);
@@ -308,6 +322,8 @@ __global__ __launch_bounds__(kPrepThreads) void cw_prep_kernel(FwdArgs p, unsign
                 if (useQ) acc[k] = Ops<BF16>::template nat<DK>(acc[k], sQl + (16 * Rr + c) * L::LDK, brow, g);
             }
         }
+        // the results below overwrite the copies read above
+        __syncthreads();
 #pragma unroll
         for (int k = 0; k < MAXT; ++k) {
             const int task = w + NW * k;
