@@ -173,3 +173,56 @@ def test_decode_continues_prefill():
     torch.cuda.synchronize()
     assert slice_rel_err(host(o), o_full[:, 128], (0, 1)) <= 1e-5
     assert slice_rel_err(host(S), S_full, (0, 1)) <= 1e-5
+
+
+def _per_token(x, lo, hi):
+    return {n: (None if x.get(n) is None else x[n][:, lo:hi]) for n in ("q", "k", "v", "beta", "wgate", "g")}
+
+
+@pytest.mark.parametrize("variant", BUILT_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_sequence_in_place_all_forms(variant, dtype):
+    """Chunked prefill from a cached state: [0, 100) then [100, 261) with the
+    state updated in place (S_T = S0) matches the oracle over [0, 261).  The
+    split falls inside a chunk of both calls."""
+    announce("prefill_split_in_place", variant, dtype)
+    w = Workload("t", variant, dtype, B=2, H=3, T=261, dk=128, dv=64, random_s0=True, seed=21)
+    x = make_forward_inputs(w, gate_scale=1 / 4)
+    o_ref, S_ref = oracle_fwd(variant, **x)
+    S = dev(x["S0"], "f32")
+    outs = []
+    for lo, hi in ((0, 100), (100, 261)):
+        part = _per_token(x, lo, hi)
+        o, _ = ops.delta_fwd(variant, *(dev(part[n], dtype) for n in ("q", "k", "v", "beta")),
+                             wgate=dev(part["wgate"], dtype), g=dev(part["g"], dtype), S0=S, S_T=S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_split = np.concatenate([host(t) for t in outs], axis=1)
+    eo, es = errs(o_split, host(S), o_ref, S_ref)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+@pytest.mark.parametrize("variant", BUILT_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_continues_prefill_all_forms(variant, dtype):
+    """Prefill of 97 tokens hands its state to three decode steps; the four
+    outputs of the decode steps and the final state match the oracle over 100
+    tokens."""
+    announce("decode_after_prefill_all", variant, dtype)
+    w = Workload("t", variant, dtype, B=2, H=2, T=100, dk=64, dv=128, random_s0=True, seed=22)
+    x = make_forward_inputs(w, gate_scale=1 / 2)
+    o_ref, S_ref = oracle_fwd(variant, **x)
+    pre = _per_token(x, 0, 97)
+    S = dev(x["S0"], "f32")
+    ops.delta_fwd(variant, *(dev(pre[n], dtype) for n in ("q", "k", "v", "beta")),
+                  wgate=dev(pre["wgate"], dtype), g=dev(pre["g"], dtype), S0=S, S_T=S)
+    outs = []
+    for t in range(97, 100):
+        step = {n: (None if x.get(n) is None else x[n][:, t]) for n in ("q", "k", "v", "beta", "wgate", "g")}
+        o = ops.delta_decode(variant, *(dev(step[n], dtype) for n in ("q", "k", "v", "beta")), S,
+                             wgate=dev(step["wgate"], dtype), g=dev(step["g"], dtype))
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    o_dec = np.stack(outs, axis=1)
+    eo, es = errs(o_dec, host(S), o_ref[:, 97:], S_ref)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
