@@ -592,13 +592,16 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
                         *reinterpret_cast<bf16x4*>(Tm + (16 * Rt + c) * L::LDP + 16 * Jt + 4 * g) = to_bf16x4(acc);
                     }
                 }
+                // column-oriented: once y_m is final it is subtracted from every
+                // y_i, i < m, so each level is 15 - m independent FMAs rather
+                // than one chain of 120 dependent ones
                 float y[16];
 #pragma unroll
-                for (int i = 15; i >= 0; --i) {
-                    float acc = (i == j) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) y[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                    for (int m = i + 1; m < 16; ++m) acc -= col[i][m / 4][m % 4] * y[m];
-                    y[i] = acc;
+                for (int m = 15; m >= 1; --m) {
+#pragma unroll
+                    for (int i = 0; i < m; ++i) y[i] -= col[i][m / 4][m % 4] * y[m];
                 }
                 // bf16 diagonal block of T: row j of block rb, 16 columns
                 uint16_t* Te = teslot(nb) + (16 * rb + j) * L::LDP + 16 * rb;
