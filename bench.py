@@ -38,13 +38,21 @@ PREFILL_KERNEL = "prefill_pipe_kernel"
 DECODE_KERNEL = "decode_kernel"
 
 
-def prefill_bytes(variant, B, T, H, dk, dv, elem=2, with_state_in=False, with_state_out=True):
+def prefill_bytes(variant, B, T, H, dk, dv, elem=2, with_state_in=False, with_state_out=True,
+                  Hk=None):
     """Algorithmic HBM bytes of one forward: every per-token input read once, o
-    written once, the fp32 initial state read and the final state written once."""
-    per_tok = {"deltanet": 2 * dk + dv + 1, "gdn": 2 * dk + dv + 2,
-               "kda": 3 * dk + dv + 1, "gdn2": 4 * dk + 2 * dv}[variant] + dv
+    written once, the fp32 initial state read and the final state written once.
+    With Hk query/key heads (grouped value heads) q and k count Hk heads."""
+    Hk = H if Hk is None else Hk
+    per_head = {"deltanet": dv + 1, "gdn": dv + 2, "kda": dk + dv + 1,
+                "gdn2": 2 * dk + 2 * dv}[variant] + dv      # v, gates, o
     state = 4 * dv * dk * (int(with_state_in) + int(with_state_out))
-    return B * T * H * elem * per_tok + B * H * state
+    return B * T * elem * (H * per_head + Hk * 2 * dk) + B * H * state
+
+
+def efla_bytes(B, T, H, Hk, dk, elem=2):
+    """Exact-flow step sizes: k read once, beta read and beta_eff written once."""
+    return B * T * elem * (Hk * dk + 2 * H)
 
 
 def prefill_flops(variant, B, T, H, dk, dv, C=64):
@@ -137,7 +145,7 @@ def cpu_baseline(variant, x, B, T, H, max_workers=16):
                 wall_s=wall)
 
 
-def time_forward(w, steps, warmup, n_sets, stream):
+def time_forward(w, steps, warmup, n_sets, stream, qk_heads=None):
     """Time delta_fwd on workload ``w`` with ``n_sets`` input copies cycled.
 
     The ``steps`` launches go back to back under ONE HIP-event span on the launch
@@ -150,7 +158,7 @@ def time_forward(w, steps, warmup, n_sets, stream):
     from recurrent_memory_amd.inputs import make_forward_inputs
     dt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
     dev = torch.device("cuda:0")
-    x = make_forward_inputs(w)
+    x = make_forward_inputs(w, qk_heads=qk_heads)
 
     def up(a, d=dt):
         return None if a is None else torch.from_numpy(a).to(d).to(dev)
@@ -268,6 +276,33 @@ def main():
                            "hbm_GBs": nb / t_s / 1e9, "hbm_frac": nb / t_s / 1e9 / HBM_PEAK_GBS,
                            "tflops": nf / t_s / 1e12, "flops_chunk_length": chunk,
                            "algorithmic_bytes_per_launch": nb})
+        # grouped value heads: the headline shape with 8 query/key heads (pairs of value heads)
+        t_s, _, _ = time_forward(w, 5, 2, 2, stream, qk_heads=8)
+        nb = prefill_bytes("gdn", B, T, H, dk, dv, Hk=8)
+        others.append({"workload": "gdn_bf16_b4_h16_t4096_d128_hk8", "variant": "gdn",
+                       "dtype": "bf16", "qk_heads": 8, "kernel_avg_us": t_s * 1e6,
+                       "tokens_per_s": B * T / t_s, "hbm_GBs": nb / t_s / 1e9,
+                       "hbm_frac": nb / t_s / 1e9 / HBM_PEAK_GBS,
+                       "tflops": nflops / t_s / 1e12, "algorithmic_bytes_per_launch": nb})
+        # exact-flow step sizes on the headline shape (an HBM-bound pass over k)
+        xe = make_forward_inputs(w)
+        esets = [(up(xe["k"]), up(xe["beta"]), torch.empty((B, T, H), dtype=bf, device=dev))
+                 for _ in range(3)]
+        for i in range(3):
+            ops.efla_beta("gdn", *esets[i][:2], out=esets[i][2], stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(30):
+            ops.efla_beta("gdn", *esets[i % 3][:2], out=esets[i % 3][2], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_e = e0.elapsed_time(e1) / 1e3 / 30
+        nb = efla_bytes(B, T, H, H, dk)
+        others.append({"workload": "efla_beta_bf16_b4_h16_t4096_d128", "kernel": "efla_beta_kernel",
+                       "kernel_avg_us": t_e * 1e6, "hbm_GBs": nb / t_e / 1e9,
+                       "hbm_frac": nb / t_e / 1e9 / HBM_PEAK_GBS,
+                       "algorithmic_bytes_per_launch": nb})
         result["other_workloads"] = others
 
     if not args.no_decode:

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 1
+#define DR_ABI_VERSION 2
 
 typedef enum {
     DR_DELTANET = 0, /* a = 1: no decay, g must be NULL                          */
@@ -73,7 +73,8 @@ typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
 typedef enum {
     DR_OK = 0,
     DR_E_NULLPTR = 1,     /* a required pointer (or the descriptor) is NULL       */
-    DR_E_SHAPE = 2,       /* a size is out of range (B, T, H < 1, decode T != 1)  */
+    DR_E_SHAPE = 2,       /* a size is out of range (B, T, H < 1, decode T != 1,
+                             H_k < 0, H_k > H or H_k not dividing H)             */
     DR_E_UNSUPPORTED = 3, /* unknown variant/dtype, unsupported d_k/d_v/chunk, or
                              a pointer given that the variant does not take     */
     DR_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
@@ -91,12 +92,19 @@ typedef struct {
     int32_t chunk;   /* chunk length of the chunkwise evaluation; must be 64   */
     int32_t variant; /* dr_variant                                             */
     int32_t dtype;   /* dr_dtype                                               */
+    int32_t H_k;     /* query/key heads; 0 means H.  Otherwise H_k must divide
+                        H: q and k are [.., H_k, d_k] and value head h reads
+                        query/key head h / (H / H_k), so each group of H / H_k
+                        consecutive value heads shares one query/key head
+                        (Grouped Value Attention: "Delta-Rule Linear Attention"
+                        topic page, GDN FPGA decode card).  beta, wgate, g, o
+                        and the state stay per value head (H).                 */
 } dr_desc;
 
 /*
  * delta_fwd — chunkwise-parallel forward pass over whole sequences.
  *
- *   q, k   [B, T, H, d_k]   dtype
+ *   q, k   [B, T, H_k, d_k] dtype (H_k = H unless desc->H_k says otherwise)
  *   v      [B, T, H, d_v]   dtype
  *   beta   DR_DELTANET/GDN/KDA: step size beta [B, T, H];
  *          DR_GDN2: erase gate b [B, T, H, d_k]                         dtype
@@ -123,7 +131,7 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
  * delta_decode — one token per sequence, state updated in place.
  *
  *   desc->T must be 1; shapes as delta_fwd with the T axis removed:
- *   q, k [B, H, d_k]; v [B, H, d_v]; beta [B, H] (DR_GDN2: b [B, H, d_k]);
+ *   q, k [B, H_k, d_k]; v [B, H, d_v]; beta [B, H] (DR_GDN2: b [B, H, d_k]);
  *   wgate [B, H, d_v] (DR_GDN2 only); g NULL / [B, H] / [B, H, d_k];
  *   S      state [B, H, d_v, d_k] fp32, read and overwritten in place
  *   o      output [B, H, d_v] dtype; must not overlap any input or S
@@ -133,6 +141,31 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
 dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const void* v,
                        const void* beta, const void* wgate, const void* g, float* S, void* o,
                        void* stream);
+
+/*
+ * delta_efla_beta — step sizes of the exact-flow form of the delta rule (EFLA:
+ * "Delta-Rule Linear Attention" topic page, EFLA card).  The delta-rule write
+ * is one explicit Euler step of length beta of the flow dS/dtau = (v - S k) k^T;
+ * because k k^T has rank one, the flow over that length has the closed form of
+ * a delta-rule write with the step size
+ *
+ *   beta_eff = (1 - exp(-beta ||k||^2)) / ||k||^2      (beta_eff = beta if k = 0)
+ *
+ * so an EFLA layer is delta_fwd / delta_decode called with beta_eff in place of
+ * beta.  Decay, where the variant has one, is applied before the write as usual.
+ *
+ *   desc     variant DR_DELTANET, DR_GDN or DR_KDA (a single step size per
+ *            token; DR_GDN2 returns DR_E_UNSUPPORTED); T = 1 serves decode
+ *   k        [B, T, H_k, d_k] dtype
+ *   beta     [B, T, H] dtype, beta >= 0
+ *   beta_eff [B, T, H] dtype (written, rounded to nearest even for bf16);
+ *            may be the same pointer as beta (in place), must not overlap k
+ *
+ * ||k||^2 is summed in fp32 over the dtype values of k; exp(-x) - 1 is
+ * evaluated without cancellation for small beta ||k||^2.
+ */
+dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, void* beta_eff,
+                          void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* dr_status_str(int status);

@@ -3,4 +3,5 @@
 TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
 cpu_baseline leg import this package.  It shares no code with the HIP path.
 """
-from .delta_oracle import VARIANTS, delta_decode, delta_fwd, run_recurrence  # noqa: F401
+from .delta_oracle import (VARIANTS, delta_decode, delta_fwd, efla_step_size,  # noqa: F401
+                           group_heads, run_recurrence)

@@ -34,6 +34,18 @@ The erase placement ``r (b ⊙ k)^T`` for Gated DeltaNet-2 is a reading: the
 abstract names the two gates but prints no formula.  That reading is parity
 unpinned beyond the reduction to KDA at b = w = beta.
 
+Two further forms from the same topic page:
+
+* Grouped Value Attention (GDN FPGA decode card): fewer query/key heads than
+  value heads.  Reading: with H value heads and H_k query/key heads, value
+  head h uses query/key head h // (H / H_k), so consecutive value heads form
+  a group; each value head keeps its own state, step size and decay.
+* EFLA (EFLA card): the delta-rule write is an explicit Euler step of the flow
+  dS/dtau = (v - S k) k^T over a length beta; EFLA takes the exact flow
+  instead.  ``efla_step_size`` gives the step size that makes one delta-rule
+  write equal that flow (derived in its docstring); the decay is applied
+  before the flow, as before the write (a reading: the card names no gate).
+
 ``run_recurrence`` works on any numpy dtype, including ``object`` arrays of
 ``fractions.Fraction`` for exact-arithmetic tests; the public wrappers use
 float64.
@@ -105,20 +117,58 @@ def _to_heads(x: Optional[np.ndarray]) -> Optional[np.ndarray]:
     return x.reshape((B * H, T) + x.shape[3:])
 
 
+def group_heads(x: np.ndarray, H: int) -> np.ndarray:
+    """Query/key tensor [B, T, H_k, d] -> [B, T, H, d]: value head h reads
+    query/key head h // (H / H_k) (Grouped Value Attention, reading above)."""
+    Hk = x.shape[2]
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"{Hk} query/key heads do not divide {H} value heads")
+    return np.repeat(x, H // Hk, axis=2)
+
+
+def efla_step_size(k, beta) -> np.ndarray:
+    """EFLA step size per value head, float64.
+
+    k: [B, T, H_k, dk] (or [B, H_k, dk]); beta: [B, T, H] (or [B, H]).
+
+    With kappa = |k|^2 and M = k k^T (eigenvalue kappa along k, 0 across it),
+    exp(-u M) = I - (1 - e^{-u kappa}) / kappa * M, so k^T exp(-u M) =
+    e^{-u kappa} k^T.  The flow of dS/dtau = (v - S k) k^T = -S M + v k^T from
+    S' over a length beta is
+
+        S' exp(-beta M) + int_0^beta v k^T exp(-(beta - s) M) ds
+          = S' - c (S' k) k^T + c v k^T,   c = (1 - e^{-beta kappa}) / kappa,
+
+    a delta-rule write with step size c (c -> beta as kappa -> 0).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    kappa = np.sum(k * k, axis=-1)
+    H = beta.shape[-1]
+    Hk = kappa.shape[-1]
+    if H % Hk != 0:
+        raise ValueError(f"{Hk} query/key heads do not divide {H} value heads")
+    kappa = np.repeat(kappa, H // Hk, axis=-1)
+    safe = np.where(kappa > 0, kappa, 1.0)
+    return np.where(kappa > 0, -np.expm1(-beta * kappa) / safe, beta)
+
+
 def delta_fwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None
               ) -> Tuple[np.ndarray, np.ndarray]:
     """Forward pass over a whole sequence, argument layout of the C boundary.
 
-    q, k: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H] (for gdn2 the erase
+    q, k: [B, T, H_k, dk] with H_k dividing H (H_k = H unless the value heads
+    are grouped); v: [B, T, H, dv]; beta: [B, T, H] (for gdn2 the erase
     gate [B, T, H, dk]); wgate: gdn2 write gate [B, T, H, dv], else None;
     g: log-decay, None / [B, T, H] / [B, T, H, dk]; S0: [B, H, dv, dk] or None
     (zero state).  Returns o [B, T, H, dv] and S_T [B, H, dv, dk], float64.
     """
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
-    q = np.asarray(q, dtype=np.float64)
-    B, T, H, dk = q.shape
-    dv = np.shape(v)[3]
+    B, T, H, dv = np.shape(v)
+    q = group_heads(np.asarray(q, dtype=np.float64), H)
+    k = group_heads(np.asarray(k, dtype=np.float64), H)
+    dk = q.shape[3]
     a = _to_heads(_decay(variant, g, (B, T, H), dk))
     if S0 is None:
         S = np.zeros((B * H, dv, dk), dtype=np.float64)
@@ -140,8 +190,8 @@ def delta_fwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None
 
 def delta_decode(variant: str, q, k, v, beta=None, wgate=None, g=None, S=None
                  ) -> Tuple[np.ndarray, np.ndarray]:
-    """One decode step: per-token tensors [B, H, d] (beta/g [B, H] or [B, H, dk]),
-    state S [B, H, dv, dk].  Returns o [B, H, dv] and the new state, float64."""
+    """One decode step: per-token tensors [B, H, d] (q, k [B, H_k, dk]; beta/g
+    [B, H] or [B, H, dk]), state S [B, H, dv, dk].  Returns o [B, H, dv] and the new state, float64."""
     add_t = (lambda x: None if x is None else np.asarray(x)[:, None])
     o, S_new = delta_fwd(variant, add_t(q), add_t(k), add_t(v), add_t(beta), add_t(wgate),
                          add_t(g), S)

@@ -30,9 +30,11 @@ bool overlap(const Span& a, const Span& b) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Elements of each operand for a descriptor (T tokens per sequence).
+// Elements of each operand for a descriptor (T tokens per sequence), and the
+// number of query/key heads.
 struct Sizes {
     int64_t qk, v, beta, wgate, g, state;
+    int Hk;
 };
 
 dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
@@ -43,11 +45,13 @@ dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
     if (decode && d->T != 1) return DR_E_SHAPE;
     if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128)) return DR_E_UNSUPPORTED;
     if (d->chunk != 64) return DR_E_UNSUPPORTED;
+    if (d->H_k < 0 || d->H_k > d->H || (d->H_k > 0 && d->H % d->H_k != 0)) return DR_E_SHAPE;
+    sz->Hk = d->H_k == 0 ? d->H : d->H_k;
     const int64_t tok = static_cast<int64_t>(d->B) * d->T * d->H;
     // Keep every element index well inside int64 and every grid within limits.
     if (tok > (int64_t(1) << 34) || static_cast<int64_t>(d->B) * d->H > (int64_t(1) << 30))
         return DR_E_SHAPE;
-    sz->qk = tok * d->d_k;
+    sz->qk = static_cast<int64_t>(d->B) * d->T * sz->Hk * d->d_k;
     sz->v = tok * d->d_v;
     sz->beta = d->variant == DR_GDN2 ? tok * d->d_k : tok;
     sz->wgate = d->variant == DR_GDN2 ? tok * d->d_v : 0;
@@ -130,7 +134,7 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
         st = check_device();
         if (st != DR_OK) return st;
         dr::FwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g,
-                      S0, o, S_T};
+                      S0, o, S_T, sz.Hk};
         const hipError_t e = dr::launch_fwd(desc->variant, desc->dtype, a,
                                             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
@@ -166,9 +170,35 @@ dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const 
 
         st = check_device();
         if (st != DR_OK) return st;
-        dr::DecodeArgs a{desc->B, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g, S, o};
+        dr::DecodeArgs a{desc->B, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g, S, o,
+                         sz.Hk};
         const hipError_t e = dr::launch_decode(desc->variant, desc->dtype, a,
                                                static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
+dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, void* beta_eff,
+                          void* stream) {
+    try {
+        Sizes sz;
+        dr_status st = check_desc(desc, false, &sz);
+        if (st != DR_OK) return st;
+        if (desc->variant == DR_GDN2) return DR_E_UNSUPPORTED;
+        if (k == nullptr || beta == nullptr || beta_eff == nullptr) return DR_E_NULLPTR;
+        if (!aligned16(k) || !aligned16(beta) || !aligned16(beta_eff)) return DR_E_ALIGN;
+        const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
+        const Span sk = span_of(k, sz.qk, eb), sb = span_of(beta, sz.beta, eb);
+        const Span so = span_of(beta_eff, sz.beta, eb);
+        if (overlap(so, sk)) return DR_E_ALIAS;
+        if (overlap(so, sb) && beta_eff != beta) return DR_E_ALIAS;
+
+        st = check_device();
+        if (st != DR_OK) return st;
+        dr::EflaArgs a{desc->B, desc->T, desc->H, sz.Hk, desc->d_k, k, beta, beta_eff};
+        const hipError_t e = dr::launch_efla_beta(desc->dtype, a, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
     } catch (...) {
         return DR_E_LAUNCH;

@@ -35,6 +35,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     const int grp = threadIdx.x >> 5;  // 0..7
     const int li = threadIdx.x & 31;
     const int64_t tok = bh;            // token index in [B, H] layouts
+    // its query/key row in [B, Hk]: value heads share a query/key head in groups
+    const int64_t qtok = static_cast<int64_t>(bh / p.H) * p.Hk + (bh % p.H) / (p.H / p.Hk);
     const int c0 = li * CPL;
 
     float* S = p.S + static_cast<int64_t>(bh) * DV * DK;
@@ -44,8 +46,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     float kk[CPL], qq[CPL], aa[CPL], bk[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        kk[c] = load_elem<E>(p.k, tok * DK + c0 + c);
-        qq[c] = load_elem<E>(p.q, tok * DK + c0 + c);
+        kk[c] = load_elem<E>(p.k, qtok * DK + c0 + c);
+        qq[c] = load_elem<E>(p.q, qtok * DK + c0 + c);
         if constexpr (VAR == 0) {
             aa[c] = 0.0f;
         } else if constexpr (VAR == 1) {

@@ -19,6 +19,8 @@ struct FwdArgs {
     const float* S0;    // [B,H,dv,dk] or nullptr (zero state)
     void* o;            // [B,T,H,dv]
     float* ST;          // [B,H,dv,dk] or nullptr
+    int Hk;             // query/key heads (divides H): q, k are [B,T,Hk,dk] and
+                        // value head h reads query/key head h / (H / Hk)
 };
 
 struct DecodeArgs {
@@ -31,6 +33,14 @@ struct DecodeArgs {
     const void* g;
     float* S;  // [B,H,dv,dk], in place
     void* o;   // [B,H,dv]
+    int Hk;    // query/key heads (divides H): q, k are [B,Hk,dk]
+};
+
+struct EflaArgs {
+    int B, T, H, Hk, dk;
+    const void* k;     // [B,T,Hk,dk]
+    const void* beta;  // [B,T,H]
+    void* beta_eff;    // [B,T,H]; may equal beta
 };
 
 // variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
@@ -45,5 +55,7 @@ hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStrea
 // launch_fwd_channel
 hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);
+// exact-flow step sizes (dtype 0 fp32, 1 bf16)
+hipError_t launch_efla_beta(int dtype, const EflaArgs& a, hipStream_t stream);
 
 }  // namespace dr

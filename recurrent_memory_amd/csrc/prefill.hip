@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
     const int bh = (x % 8) + 8 * (x / (8 * NVT));
     if (bh >= p.B * p.H) return;
     const int b = bh / p.H, h = bh % p.H;
+    const int Hk = p.Hk, hk = h / (p.H / p.Hk);   // this value head's query/key head
     const int T = p.T, H = p.H;
 
     const int tid = threadIdx.x;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(FwdArgs p) {
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
             const int pidx = tid + kThreads * j;
-            const int64_t off = ((tokb + min(pidx / CPR, last)) * H + h) * DK + (pidx % CPR) * EPC;
+            const int64_t off = ((tokb + min(pidx / CPR, last)) * Hk + hk) * DK + (pidx % CPR) * EPC;
             pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
             pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
         }

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
     if (bh >= p.B * p.H) return;
     const int b = bh / p.H, h = bh % p.H;
     const int T = p.T, H = p.H;
+    const int Hk = p.Hk, hk = h / (p.H / p.Hk);   // this value head's query/key head
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -176,12 +177,13 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
     const int nchunks = (T + C - 1) / C;
     // per-thread element offsets relative to the first token of a sub-chunk
     // (32-bit, computed once); only the last, partial sub-chunk clamps rows
-    uint32_t koff[NPK], voff[NPV];
+    uint32_t koff[NPK], qkoff[NPK], voff[NPV];
 #pragma unroll
     for (int j = 0; j < NPK; ++j) {
         const int pidx = tid + kThreadsCW * j;
         const int row = min(pidx / CPR, C - 1), cc = pidx % CPR;
         koff[j] = static_cast<uint32_t>(row * H * DK + cc * EPC);
+        qkoff[j] = static_cast<uint32_t>(row * Hk * DK + cc * EPC);
     }
 #pragma unroll
     for (int j = 0; j < NPV; ++j) {
@@ -195,10 +197,11 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
         const int64_t tokb = static_cast<int64_t>(b) * T + t0;
         if (last == C - 1) {   // whole sub-chunk: uniform base + thread offset
             const int64_t kb = (tokb * H + h) * DK, vb = (tokb * H + h) * DV + vt * kVTCW;
+            const int64_t qb = (tokb * Hk + hk) * DK;
 #pragma unroll
             for (int j = 0; j < NPK; ++j) {
-                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + kb + koff[j]);
-                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + kb + koff[j]);
+                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + qb + qkoff[j]);
+                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + qb + qkoff[j]);
                 pg[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.g) + kb + koff[j]);
                 if constexpr (SPLIT) pb[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.beta) + kb + koff[j]);
             }
@@ -213,8 +216,9 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
                 const int pidx = tid + kThreadsCW * j;
                 const int row = min(min(pidx / CPR, C - 1), last), cc = pidx % CPR;
                 const int64_t off = ((tokb + row) * H + h) * DK + cc * EPC;
-                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + off);
-                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + off);
+                const int64_t qoff = ((tokb + row) * Hk + hk) * DK + cc * EPC;
+                pq[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.q) + qoff);
+                pk[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.k) + qoff);
                 pg[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.g) + off);
                 if constexpr (SPLIT) pb[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.beta) + off);
             }

@@ -161,6 +161,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
     auto fetch = [&](int unit) {
         const int ubh = unit / NC, un = unit % NC;
         const int ub = ubh / H, uh = ubh % H;
+        const int uhk = uh / (H / p.Hk);   // the value head's query/key head
         const int ucn = min(C, T - un * C);
         const int64_t utok = static_cast<int64_t>(ub) * T + un * C;
 #pragma unroll
@@ -173,8 +174,9 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
             rb[j] = rq[j];
             if (row < ucn) {
                 const int64_t off = ((utok + row) * H + uh) * DK + 8 * cc;
-                rq[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + off);
-                rk[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off);
+                const int64_t qoff = ((utok + row) * p.Hk + uhk) * DK + 8 * cc;
+                rq[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
+                rk[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + qoff);
                 rg[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.g) + off);
                 if constexpr (SPLIT) rb[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
             }

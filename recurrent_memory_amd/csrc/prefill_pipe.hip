@@ -461,15 +461,17 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
     constexpr int RPI = 512 / DK;   // rows per 1 KB instruction
     constexpr int PPR = DK / 8;     // 16-byte pieces per row
     constexpr int NJ = kCP / RPI;   // instructions per tile
+    // q and k rows: value heads share a query/key head in groups of H / Hk
+    const int Hk = p.Hk, hk = h / (H / Hk);
     uint32_t qk_lane_off[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int r = j * RPI + lane / PPR;
-        qk_lane_off[j] = static_cast<uint32_t>(r * H * DK + 8 * ((lane % PPR) ^ swz<DK>(r)));
+        qk_lane_off[j] = static_cast<uint32_t>(r * Hk * DK + 8 * ((lane % PPR) ^ swz<DK>(r)));
     }
     auto load_tile = [&](const uint16_t* src, uint16_t* dst, int n) {
         if (n * kCP + kCP <= T) {   // whole chunk: wave-uniform base + lane offset
-            const uint16_t* base = src + ((tokb + n * kCP) * H + h) * DK;
+            const uint16_t* base = src + ((tokb + n * kCP) * Hk + hk) * DK;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) load_to_lds16(base + qk_lane_off[j], dst + 512 * j);
         } else {                    // last, partial chunk: rows clamped to the sequence
@@ -477,7 +479,8 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
             for (int j = 0; j < NJ; ++j) {
                 const int r = j * RPI + lane / PPR;
                 const int piece = (lane % PPR) ^ swz<DK>(r);
-                load_to_lds16(src + token(n, r) * DK + 8 * piece, dst + 512 * j);
+                const int64_t tq = (tokb + min(n * kCP + r, T - 1)) * Hk + hk;
+                load_to_lds16(src + tq * DK + 8 * piece, dst + 512 * j);
             }
         }
     };

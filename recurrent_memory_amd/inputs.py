@@ -16,6 +16,10 @@ Recipe (one generator per workload, ``numpy.random.PCG64(seed)``):
 * step sizes and split gates are ``sigmoid(z)``; log-decays are
   ``-softplus(z)`` (so the per-token decay ``exp(g)`` lies in (0, 1));
 * S0 is ``0.02 * z`` where the workload asks for a random initial state;
+* grouped value heads (``qk_heads`` < H): q and k are drawn with ``qk_heads``
+  heads instead of H, in the same draw order;
+* ``key_norm`` scales the normalised keys (1 by default; larger values give
+  the high-energy keys of the exact-flow step-size tests);
 * everything is then rounded to the workload dtype (round-to-nearest-even
   for bfloat16).  The rounded arrays are *the* inputs for every consumer.
 
@@ -105,7 +109,8 @@ def _neg_softplus(z: np.ndarray) -> np.ndarray:
 
 
 def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: int, dv: int,
-         gate_scale: float = 1.0) -> Dict[str, Optional[np.ndarray]]:
+         gate_scale: float = 1.0, qk_heads: Optional[int] = None,
+         key_norm: float = 1.0) -> Dict[str, Optional[np.ndarray]]:
     """Draw one set of per-token tensors with leading shape ``lead`` (e.g. (B, T, H)).
 
     Returns q, k, v, beta, wgate, g following the boundary's argument names:
@@ -114,11 +119,16 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
     ``lead`` and ``wgate`` is None.  ``g`` is None for the ungated form,
     shape ``lead`` for a scalar gate and ``lead + (dk,)`` for channel gates.
     ``gate_scale`` multiplies the log-decays (e.g. 1/16 for weak decay).
+    ``qk_heads`` replaces the last entry of ``lead`` for q and k (grouped value
+    heads); ``key_norm`` is the L2 norm of every key before rounding.
     """
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
-    q = _unit(rng.standard_normal(lead + (dk,), dtype=np.float32))
-    k = _unit(rng.standard_normal(lead + (dk,), dtype=np.float32))
+    qk_lead = lead if qk_heads is None else lead[:-1] + (qk_heads,)
+    q = _unit(rng.standard_normal(qk_lead + (dk,), dtype=np.float32))
+    k = _unit(rng.standard_normal(qk_lead + (dk,), dtype=np.float32))
+    if key_norm != 1.0:
+        k = (k * np.float32(key_norm)).astype(np.float32)
     v = rng.standard_normal(lead + (dv,), dtype=np.float32)
     if variant == "gdn2":
         beta = _sigmoid(rng.standard_normal(lead + (dk,), dtype=np.float32))
@@ -137,14 +147,15 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
 
 
 def make_forward_inputs(w: Workload, seed: Optional[int] = None, T: Optional[int] = None,
-                        gate_scale: float = 1.0, random_s0: Optional[bool] = None
+                        gate_scale: float = 1.0, random_s0: Optional[bool] = None,
+                        qk_heads: Optional[int] = None, key_norm: float = 1.0
                         ) -> Dict[str, Optional[np.ndarray]]:
     """Inputs of one chunkwise forward: layout [B, T, H, d] per token, S0 [B, H, dv, dk]."""
     seed = w.seed if seed is None else seed
     T = w.T if T is None else T
     random_s0 = w.random_s0 if random_s0 is None else random_s0
     rng = np.random.Generator(np.random.PCG64(seed))
-    out = draw(rng, w.variant, w.dtype, (w.B, T, w.H), w.dk, w.dv, gate_scale)
+    out = draw(rng, w.variant, w.dtype, (w.B, T, w.H), w.dk, w.dv, gate_scale, qk_heads, key_norm)
     if random_s0:
         out["S0"] = (np.float32(0.02) * rng.standard_normal((w.B, w.H, w.dv, w.dk),
                                                             dtype=np.float32)).astype(np.float32)
@@ -154,12 +165,13 @@ def make_forward_inputs(w: Workload, seed: Optional[int] = None, T: Optional[int
 
 
 def make_decode_inputs(w: Workload, n_steps: int, seed: Optional[int] = None,
-                       gate_scale: float = 1.0) -> Dict[str, object]:
+                       gate_scale: float = 1.0, qk_heads: Optional[int] = None,
+                       key_norm: float = 1.0) -> Dict[str, object]:
     """A random fp32 state [B, H, dv, dk] and ``n_steps`` per-step input sets [B, H, d]."""
     seed = w.seed if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     S = (np.float32(0.02) * rng.standard_normal((w.B, w.H, w.dv, w.dk),
                                                 dtype=np.float32)).astype(np.float32)
-    steps = [draw(rng, w.variant, w.dtype, (w.B, w.H), w.dk, w.dv, gate_scale)
+    steps = [draw(rng, w.variant, w.dtype, (w.B, w.H), w.dk, w.dv, gate_scale, qk_heads, key_norm)
              for _ in range(n_steps)]
     return dict(S=S, steps=steps)

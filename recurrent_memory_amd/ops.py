@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltarule.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "deltarule.h")
 
+ABI_VERSION = 2   # DR_ABI_VERSION of the header this binding follows
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "DR_OK", 1: "DR_E_NULLPTR", 2: "DR_E_SHAPE", 3: "DR_E_UNSUPPORTED",
@@ -28,7 +29,7 @@ STATUS = {0: "DR_OK", 1: "DR_E_NULLPTR", 2: "DR_E_SHAPE", 3: "DR_E_UNSUPPORTED",
 class DrDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32), ("H_k", ctypes.c_int32)]
 
 
 class DeltaRuleError(RuntimeError):
@@ -53,10 +54,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.delta_fwd.restype = ctypes.c_int
     lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.delta_decode.restype = ctypes.c_int
+    lib.delta_efla_beta.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp]
+    lib.delta_efla_beta.restype = ctypes.c_int
     lib.dr_status_str.argtypes = [ctypes.c_int]
     lib.dr_status_str.restype = ctypes.c_char_p
     lib.dr_abi_version.argtypes = []
     lib.dr_abi_version.restype = ctypes.c_int
+    if lib.dr_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.dr_abi_version()}, the binding expects "
+                          f"{ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -104,18 +110,19 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward; tensors as in include/deltarule.h ([B, T, H, d] per token).
 
+    q and k may have fewer heads than v (H_k dividing H: grouped value heads).
     Returns (o, S_T).  ``S_T`` is allocated when ``want_state`` and not given;
     passing ``S_T=S0`` updates the state in place.
     """
     lib = load_library()
     var = VARIANTS[variant]
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[-1]
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    _check("q", q, (B, T, H, dk), dt, dev)
-    _check("k", k, (B, T, H, dk), dt, dev)
+    _check("q", q, (B, T, Hk, dk), dt, dev)
+    _check("k", k, (B, T, Hk, dk), dt, dev)
     _check("v", v, (B, T, H, dv), dt, dev)
     _check("beta", beta, (B, T, H, dk) if variant == "gdn2" else (B, T, H), dt, dev)
     if variant == "gdn2":
@@ -136,7 +143,7 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if S_T is not None:
         _check("S_T", S_T, (B, H, dv, dk), torch.float32, dev)
-    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt])
+    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
     st = lib.delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
                        _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
     if st != 0:
@@ -148,16 +155,16 @@ def delta_decode(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                  beta: torch.Tensor, S: torch.Tensor, wgate: Optional[torch.Tensor] = None,
                  g: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
-    """One decode step; q, k [B, H, dk], v [B, H, dv]; S [B, H, dv, dk] fp32 updated in place."""
+    """One decode step; q, k [B, H_k, dk], v [B, H, dv]; S [B, H, dv, dk] fp32 updated in place."""
     lib = load_library()
     var = VARIANTS[variant]
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    B, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[-1]
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    _check("q", q, (B, H, dk), dt, dev)
-    _check("k", k, (B, H, dk), dt, dev)
+    _check("q", q, (B, Hk, dk), dt, dev)
+    _check("k", k, (B, Hk, dk), dt, dev)
     _check("v", v, (B, H, dv), dt, dev)
     _check("beta", beta, (B, H, dk) if variant == "gdn2" else (B, H), dt, dev)
     if variant == "gdn2":
@@ -173,9 +180,40 @@ def delta_decode(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     if o is None:
         o = torch.empty((B, H, dv), dtype=dt, device=dev)
     _check("o", o, (B, H, dv), dt, dev)
-    desc = DrDesc(B, 1, H, dk, dv, 64, var, DTYPES[dt])
+    desc = DrDesc(B, 1, H, dk, dv, 64, var, DTYPES[dt], Hk)
     st = lib.delta_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
                           _ptr(g), _ptr(S), _ptr(o), _stream(stream))
     if st != 0:
         _raise(st)
     return o
+
+
+def efla_beta(variant: str, k: torch.Tensor, beta: torch.Tensor,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Exact-flow step sizes (1 - exp(-beta |k|^2)) / |k|^2.
+
+    k [B, T, H_k, dk] with beta [B, T, H], or the decode layout k [B, H_k, dk]
+    with beta [B, H].  ``out`` may be ``beta`` itself (in place).
+    """
+    lib = load_library()
+    var = VARIANTS[variant]
+    if k.dim() == 3:
+        B, Hk, dk = k.shape
+        T, H = 1, beta.shape[1]
+        bshape = (B, H)
+    else:
+        B, T, Hk, dk = k.shape
+        H = beta.shape[2]
+        bshape = (B, T, H)
+    dt, dev = k.dtype, k.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check("beta", beta, bshape, dt, dev)
+    if out is None:
+        out = torch.empty_like(beta)
+    _check("out", out, bshape, dt, dev)
+    desc = DrDesc(B, T, H, dk, 64, 64, var, DTYPES[dt], Hk)
+    st = lib.delta_efla_beta(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(out), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return out

@@ -18,13 +18,14 @@ FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(12)]
 
 def test_exports_every_header_symbol():
     names = ops.header_functions()
-    assert set(names) == {"delta_fwd", "delta_decode", "dr_status_str", "dr_abi_version"}
+    assert set(names) == {"delta_fwd", "delta_decode", "delta_efla_beta", "dr_status_str",
+                          "dr_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
-    assert lib.dr_abi_version() == 1
+    assert lib.dr_abi_version() == ops.ABI_VERSION == 2
     assert lib.dr_status_str(0) == b"ok"
     assert lib.dr_status_str(99) == b"unknown status"
     for s in range(8):
@@ -55,6 +56,7 @@ def dec(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5],
     (dict(d_v=256), DR_E_UNSUPPORTED), (dict(chunk=32), DR_E_UNSUPPORTED),
     (dict(B=0), DR_E_SHAPE), (dict(T=0), DR_E_SHAPE), (dict(H=-1), DR_E_SHAPE),
     (dict(T=1 << 30, B=1 << 10), DR_E_SHAPE),
+    (dict(H_k=2), DR_E_SHAPE), (dict(H_k=4), DR_E_SHAPE), (dict(H_k=-1), DR_E_SHAPE),
 ])
 def test_bad_descriptor(kw, status):
     assert fwd(desc(**kw)) == status
@@ -91,6 +93,35 @@ def test_aliasing():
     assert dec(desc(T=1), S=FAKE[0]) == DR_E_ALIAS              # S == q
 
 
+def efla(d, k=FAKE[1], beta=FAKE[3], out=FAKE[9]):
+    return lib.delta_efla_beta(ctypes.byref(d) if d is not None else None, k, beta, out, None)
+
+
+def test_efla_validation():
+    assert efla(None) == DR_E_NULLPTR
+    assert efla(desc(), k=None) == DR_E_NULLPTR
+    assert efla(desc(), out=None) == DR_E_NULLPTR
+    assert efla(desc(variant=3)) == DR_E_UNSUPPORTED            # split gates have no single step
+    assert efla(desc(H_k=2)) == DR_E_SHAPE
+    assert efla(desc(), beta=ctypes.c_void_p(FAKE[3].value + 2)) == DR_E_ALIGN
+    assert efla(desc(), out=FAKE[1]) == DR_E_ALIAS              # beta_eff over k
+    assert efla(desc(), out=ctypes.c_void_p(FAKE[3].value + 16)) == DR_E_ALIAS  # shifted onto beta
+
+
+def test_grouped_heads_size_the_query_key_operands():
+    """With H_k query/key heads, q and k span B*T*H_k*d_k elements: an output
+    over the last 16 bytes of k is rejected, one right after k is accepted (it
+    would lie inside k if k were sized with H heads)."""
+    d = desc(H=4, H_k=2, T=64, B=1)
+    qk_bytes = 1 * 64 * 2 * 128 * 2
+    after_k = ctypes.c_void_p(FAKE[1].value + qk_bytes)
+    inside_ungrouped = ctypes.c_void_p(FAKE[1].value + qk_bytes - 16)
+    assert fwd(d, o=inside_ungrouped) == DR_E_ALIAS
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd(d, o=after_k) == DR_E_DEVICE
+
+
 def test_decode_requires_one_token():
     assert dec(desc(T=2)) == DR_E_SHAPE
 
@@ -102,3 +133,5 @@ def test_no_device_returns_device_error():
         pytest.skip("a GPU is present: valid arguments would launch on fake pointers")
     assert fwd(desc(), S0=FAKE[8], ST=FAKE[8]) == DR_E_DEVICE
     assert dec(desc(T=1)) == DR_E_DEVICE
+    assert efla(desc(T=1)) == DR_E_DEVICE
+    assert efla(desc(), out=FAKE[3]) == DR_E_DEVICE             # in place is allowed

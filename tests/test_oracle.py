@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle.delta_oracle as od
-from oracle import delta_decode, delta_fwd, run_recurrence
+from oracle import delta_decode, delta_fwd, efla_step_size, run_recurrence
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -320,9 +320,108 @@ def pin_decode_is_one_token():
         assert np.array_equal(od_, o[:, 0]) and np.array_equal(Sd, S)
 
 
+def pin_grouped_heads_one_token():
+    """4 value heads over 2 query/key heads, one token, written out per head: value
+    head h reads the query and key of head h // 2 (Grouped Value Attention reading)."""
+    rng = np.random.default_rng(11)
+    B, H, Hk, dk, dv = 2, 4, 2, 5, 3
+    q = rng.standard_normal((B, 1, Hk, dk))
+    k = rng.standard_normal((B, 1, Hk, dk))
+    v = rng.standard_normal((B, 1, H, dv))
+    beta = rng.uniform(0, 1, (B, 1, H))
+    g = -rng.uniform(0, 1, (B, 1, H))
+    S0 = rng.standard_normal((B, H, dv, dk))
+    o, S = delta_fwd("gdn", q, k, v, beta, g=g, S0=S0)
+    assert o.shape == (B, 1, H, dv) and S.shape == (B, H, dv, dk)
+    for b in range(B):
+        for h in range(H):
+            kk, qq = k[b, 0, h // 2], q[b, 0, h // 2]
+            Sp = np.exp(g[b, 0, h]) * S0[b, h]
+            S1 = Sp + beta[b, 0, h] * np.outer(v[b, 0, h] - Sp @ kk, kk)
+            np.testing.assert_allclose(S[b, h], S1, rtol=1e-13, atol=1e-14)
+            np.testing.assert_allclose(o[b, 0, h], S1 @ qq, rtol=1e-13, atol=1e-14)
+
+
+def pin_grouped_heads_share():
+    """Value heads of one group given the same v, gates and S0 produce the same outputs
+    over a whole sequence; heads of different groups, given the same, do not."""
+    rng = np.random.default_rng(12)
+    for variant in od.VARIANTS:
+        x = _rand_inputs(rng, variant, 1, 9, 6, 4, 3)
+        G = 3   # 6 value heads over 2 query/key heads
+        x["q"], x["k"] = x["q"][:, :, ::G], x["k"][:, :, ::G]
+        for name in ("v", "beta", "wgate", "g"):
+            if x[name] is not None:
+                x[name][:, :, :] = x[name][:, :, :1]
+        x["S0"][:, :] = x["S0"][:, :1]
+        o, S = delta_fwd(variant, **x)
+        for h in range(6):
+            same = h // G == 0
+            assert np.array_equal(o[:, :, h], o[:, :, 0]) == same, (variant, h)
+            assert np.array_equal(S[:, h], S[:, 0]) == same, (variant, h)
+
+
+def _rk4_flow(S, k, v, length, steps=400):
+    """Integrate dS/dtau = (v - S k) k^T over [0, length] with classical RK4."""
+    f = lambda X: np.outer(v - X @ k, k)  # noqa: E731
+    h = length / steps
+    for _ in range(steps):
+        a1 = f(S)
+        a2 = f(S + 0.5 * h * a1)
+        a3 = f(S + 0.5 * h * a2)
+        a4 = f(S + h * a3)
+        S = S + h / 6 * (a1 + 2 * a2 + 2 * a3 + a4)
+    return S
+
+
+def pin_efla_exact_flow():
+    """EFLA = the exact flow of dS/dtau = (v - S k) k^T over the length beta, after
+    the decay: the oracle with efla_step_size matches an RK4 integration of that flow,
+    token by token over a sequence, for key norms 0.3, 1 and 2.5."""
+    rng = np.random.default_rng(13)
+    dk, dv, T = 5, 3, 6
+    for norm in (0.3, 1.0, 2.5):
+        q = rng.standard_normal((1, T, 1, dk))
+        k = rng.standard_normal((1, T, 1, dk))
+        k *= norm / np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((1, T, 1, dv))
+        beta = rng.uniform(0.2, 1, (1, T, 1))
+        g = -rng.uniform(0, 1, (1, T, 1))
+        S0 = rng.standard_normal((1, 1, dv, dk))
+        o, S_T = delta_fwd("gdn", q, k, v, efla_step_size(k, beta), g=g, S0=S0)
+        S = S0[0, 0]
+        for t in range(T):
+            S = _rk4_flow(np.exp(g[0, t, 0]) * S, k[0, t, 0], v[0, t, 0], beta[0, t, 0])
+            np.testing.assert_allclose(o[0, t, 0], S @ q[0, t, 0], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(S_T[0, 0], S, rtol=1e-9, atol=1e-11)
+
+
+def pin_efla_limits():
+    """k = 0 gives beta; |k| = 1 gives 1 - e^{-beta}; beta |k|^2 -> 0 gives beta to first
+    order; in general 0 < c <= min(beta, 1 / |k|^2).  Grouped heads share the norm."""
+    beta = np.array([[0.0, 0.3, 1.0, 5.0]])
+    zero = np.zeros((1, 1, 3))
+    np.testing.assert_array_equal(efla_step_size(zero, beta), beta)
+    unit = np.array([[[0.6, 0.8, 0.0]]])
+    np.testing.assert_allclose(efla_step_size(unit, beta), 1 - np.exp(-beta), rtol=1e-15)
+    tiny = np.array([[[1e-9, 0.0, 0.0]]])
+    np.testing.assert_allclose(efla_step_size(tiny, beta), beta, rtol=1e-15)
+    rng = np.random.default_rng(14)
+    k = rng.standard_normal((3, 7, 2, 4)) * rng.uniform(0.1, 4, (3, 7, 2, 1))
+    b = rng.uniform(0.01, 2, (3, 7, 6))
+    c = efla_step_size(k, b)
+    kappa = np.repeat(np.sum(k * k, axis=-1), 3, axis=-1)
+    assert (c > 0).all() and (c <= b).all() and (c <= 1 / kappa + 1e-15).all()
+    for h in range(6):   # value head h reads key head h // 3
+        kap = np.sum(k[..., h // 3, :] ** 2, axis=-1)
+        np.testing.assert_allclose(c[..., h], -np.expm1(-b[..., h] * kap) / kap, rtol=1e-14)
+
+
 PINS = [pin_hand_worked, pin_exact_product_form, pin_beta_zero, pin_gate_zero_is_deltanet,
         pin_reductions, pin_unit_write, pin_orthonormal_keys, pin_one_token_by_hand,
-        pin_linearity, pin_norm_bound, pin_split_sequence, pin_decode_is_one_token]
+        pin_linearity, pin_norm_bound, pin_split_sequence, pin_decode_is_one_token,
+        pin_grouped_heads_one_token, pin_grouped_heads_share, pin_efla_exact_flow,
+        pin_efla_limits]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
