@@ -196,3 +196,125 @@ def delta_decode(variant: str, q, k, v, beta=None, wgate=None, g=None, S=None
     o, S_new = delta_fwd(variant, add_t(q), add_t(k), add_t(v), add_t(beta), add_t(wgate),
                          add_t(g), S)
     return o[:, 0], S_new
+
+
+def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=None):
+    """Reverse mode of ``run_recurrence`` (same argument layout, float64).
+
+    Runs the recurrence forward keeping every state, then walks back one token
+    at a time applying the chain rule to each line of the token update (order
+    of the module docstring).  ``dO`` [N, T, dv] and ``dST`` [N, dv, dk] (or
+    None) are the gradients arriving at o and at the final state.  Returns a
+    dict with dq, dk, dv [N, T, d], da [N, T, dk] (gradient of the decay
+    factors), dbeta [N, T] or (derase [N, T, dk], dwrite [N, T, dv]) and dS0.
+    """
+    split = erase is not None
+    N, T, dk = q.shape
+    S = np.array(S0, dtype=np.float64, copy=True)
+    states = [S]
+    for t in range(T):
+        kt = k[:, t, :]
+        Sp = S * a[:, t, None, :]
+        r = (Sp @ kt[:, :, None])[:, :, 0]
+        if split:
+            S = (Sp - r[:, :, None] * (erase[:, t, :] * kt)[:, None, :]
+                 + (write[:, t, :] * v[:, t, :])[:, :, None] * kt[:, None, :])
+        else:
+            S = Sp + beta[:, t, None, None] * (v[:, t, :] - r)[:, :, None] * kt[:, None, :]
+        states.append(S)
+    lam = np.zeros_like(S) if dST is None else np.array(dST, dtype=np.float64, copy=True)
+    g = {name: np.zeros_like(x) for name, x in (("dq", q), ("dk", k), ("dv", v), ("da", a))}
+    if split:
+        g["derase"] = np.zeros_like(erase)
+        g["dwrite"] = np.zeros_like(write)
+    else:
+        g["dbeta"] = np.zeros_like(beta)
+    for t in range(T - 1, -1, -1):
+        kt, qt, vt = k[:, t, :], q[:, t, :], v[:, t, :]
+        S_prev, S_t = states[t], states[t + 1]
+        Sp = S_prev * a[:, t, None, :]
+        r = (Sp @ kt[:, :, None])[:, :, 0]
+        # o_t = S_t q_t
+        lam = lam + dO[:, t, :, None] * qt[:, None, :]
+        g["dq"][:, t] = (np.swapaxes(S_t, 1, 2) @ dO[:, t, :, None])[:, :, 0]
+        lam_k = (lam @ kt[:, :, None])[:, :, 0]                       # Λ k        [N, dv]
+        if split:
+            # S_t = S' - r (b ⊙ k)^T + (w ⊙ v) k^T
+            eb = erase[:, t, :] * kt
+            lamT_r = (np.swapaxes(lam, 1, 2) @ r[:, :, None])[:, :, 0]  # Λ^T r      [N, dk]
+            wv = write[:, t, :] * vt
+            g["derase"][:, t] = -lamT_r * kt
+            g["dwrite"][:, t] = lam_k * vt
+            g["dv"][:, t] = lam_k * write[:, t, :]
+            dk_t = -lamT_r * erase[:, t, :] + (np.swapaxes(lam, 1, 2) @ wv[:, :, None])[:, :, 0]
+            dr = -(lam @ eb[:, :, None])[:, :, 0]
+        else:
+            # S_t = S' + u k^T with u = beta (v - r)
+            e = vt - r
+            u = beta[:, t, None] * e
+            g["dbeta"][:, t] = np.sum(lam_k * e, axis=1)
+            g["dv"][:, t] = beta[:, t, None] * lam_k
+            dk_t = (np.swapaxes(lam, 1, 2) @ u[:, :, None])[:, :, 0]
+            dr = -beta[:, t, None] * lam_k
+        # r = S' k: adds dr k^T to dS' and S'^T dr to dk
+        dSp = lam + dr[:, :, None] * kt[:, None, :]
+        g["dk"][:, t] = dk_t + (np.swapaxes(Sp, 1, 2) @ dr[:, :, None])[:, :, 0]
+        # S' = S_prev Diag(a_t)
+        g["da"][:, t] = np.sum(S_prev * dSp, axis=1)
+        lam = dSp * a[:, t, None, :]
+    g["dS0"] = lam
+    return g
+
+
+def _from_heads(x: np.ndarray, B: int, H: int) -> np.ndarray:
+    """[B*H, T, ...] -> [B, T, H, ...]."""
+    x = x.reshape((B, H) + x.shape[1:])
+    return np.ascontiguousarray(np.moveaxis(x, 1, 2))
+
+
+def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=None, dS_T=None
+              ) -> dict:
+    """Gradients of the forward pass, float64, argument layout of delta_fwd.
+
+    Given the gradient ``dO`` [B, T, H, dv] arriving at o and ``dS_T``
+    [B, H, dv, dk] (None = zero) arriving at the final state, returns a dict
+    with dq, dk (of the query/key heads given, summed over each group of value
+    heads), dv, dbeta (for gdn2 the erase-gate gradient [B, T, H, dk]),
+    dwgate (gdn2 only, else None), dg (None for deltanet; [B, T, H] for gdn,
+    [B, T, H, dk] for kda/gdn2) and dS0 [B, H, dv, dk].  The decay factor is
+    a = exp(g), so dg = a * dL/da per channel, summed over channels for gdn.
+    """
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    B, T, H, dv = np.shape(v)
+    q0 = np.asarray(q, dtype=np.float64)
+    Hk = q0.shape[2]
+    qh = _to_heads(group_heads(q0, H))
+    kh = _to_heads(group_heads(np.asarray(k, dtype=np.float64), H))
+    dk_ = qh.shape[2]
+    a = _to_heads(_decay(variant, g, (B, T, H), dk_))
+    S = (np.zeros((B * H, dv, dk_)) if S0 is None
+         else np.asarray(S0, dtype=np.float64).reshape(B * H, dv, dk_))
+    dST = None if dS_T is None else np.asarray(dS_T, dtype=np.float64).reshape(B * H, dv, dk_)
+    dOh = _to_heads(dO)
+    if variant == "gdn2":
+        gr = _recurrence_backward(S, qh, kh, _to_heads(v), a, dOh, dST,
+                                  erase=_to_heads(beta), write=_to_heads(wgate))
+    else:
+        gr = _recurrence_backward(S, qh, kh, _to_heads(v), a, dOh, dST, beta=_to_heads(beta))
+
+    def ungroup(x):   # [B, T, H, d] -> sum over each group of value heads -> [B, T, Hk, d]
+        return x.reshape(B, T, Hk, H // Hk, -1).sum(axis=3)
+
+    out = {"dq": ungroup(_from_heads(gr["dq"], B, H)), "dk": ungroup(_from_heads(gr["dk"], B, H)),
+           "dv": _from_heads(gr["dv"], B, H), "dwgate": None, "dg": None,
+           "dS0": gr["dS0"].reshape(B, H, dv, dk_)}
+    if variant == "gdn2":
+        out["dbeta"] = _from_heads(gr["derase"], B, H)
+        out["dwgate"] = _from_heads(gr["dwrite"], B, H)
+    else:
+        out["dbeta"] = _from_heads(gr["dbeta"], B, H)
+    if variant != "deltanet":
+        dgc = _from_heads(gr["da"] * a, B, H)          # d/dg of exp(g), per channel
+        out["dg"] = dgc.sum(axis=-1) if variant == "gdn" else dgc
+    return out
