@@ -43,6 +43,24 @@ struct EflaArgs {
     void* beta_eff;    // [B,T,H]; may equal beta
 };
 
+struct BwdArgs {
+    int B, T, H, dk, dv;
+    const void* q;       // [B,T,H,dk]
+    const void* k;
+    const void* v;       // [B,T,H,dv]
+    const void* beta;    // [B,T,H]
+    const void* g;       // nullptr, [B,T,H] or [B,T,H,dk]
+    const float* S0;     // [B,H,dv,dk] or nullptr
+    const void* dO;      // [B,T,H,dv]
+    const float* dST;    // [B,H,dv,dk] or nullptr
+    void* gq;            // gradients, same layouts as the inputs
+    void* gk;
+    void* gv;
+    void* gbeta;
+    void* gg;            // nullptr for the ungated form
+    float* gS0;          // [B,H,dv,dk] or nullptr
+};
+
 // variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
 // dtype: 0 fp32, 1 bf16.
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
@@ -57,5 +75,9 @@ hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_
 hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);
 // exact-flow step sizes (dtype 0 fp32, 1 bf16)
 hipError_t launch_efla_beta(int dtype, const EflaArgs& a, hipStream_t stream);
+// backward of the single-step-size forms (variant 0, 1 or 2)
+hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t stream);
+// library-owned stream-ordered memory pool of the current device (workspaces)
+hipError_t workspace_pool(hipMemPool_t* pool);
 
 }  // namespace dr

@@ -718,33 +718,6 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     }
 }
 
-// The workspace comes from a library-owned, stream-ordered memory pool per
-// device that keeps freed memory for reuse (release threshold: unlimited), so
-// repeated calls do not return to the driver for it.
-hipError_t workspace_pool(hipMemPool_t* pool) {
-    static std::mutex mu;
-    static hipMemPool_t pools[64] = {};
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!pools[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t p = nullptr;
-        e = hipMemPoolCreate(&p, &props);
-        if (e != hipSuccess) return e;
-        uint64_t keep = ~uint64_t(0);
-        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess) return e;
-        pools[dev] = p;
-    }
-    *pool = pools[dev];
-    return hipSuccess;
-}
 
 // Workgroups of pass 1 resident on the device at once (it is persistent).
 template <int DK, bool SPLIT>
@@ -810,6 +783,34 @@ hipError_t launch_two_pass_dims(const FwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// The workspace comes from a library-owned, stream-ordered memory pool per
+// device that keeps freed memory for reuse (release threshold: unlimited), so
+// repeated calls do not return to the driver for it.
+hipError_t workspace_pool(hipMemPool_t* pool) {
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = ~uint64_t(0);
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) return e;
+        pools[dev] = p;
+    }
+    *pool = pools[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t s) {
     return variant == 2 ? launch_two_pass_dims<false>(a, s) : launch_two_pass_dims<true>(a, s);

@@ -54,6 +54,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.delta_fwd.restype = ctypes.c_int
     lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.delta_decode.restype = ctypes.c_int
+    lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 15
+    lib.delta_bwd.restype = ctypes.c_int
     lib.delta_efla_beta.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp]
     lib.delta_efla_beta.restype = ctypes.c_int
     lib.dr_status_str.argtypes = [ctypes.c_int]
@@ -214,6 +216,43 @@ def efla_beta(variant: str, k: torch.Tensor, beta: torch.Tensor,
     _check("out", out, bshape, dt, dev)
     desc = DrDesc(B, T, H, dk, 64, 64, var, DTYPES[dt], Hk)
     st = lib.delta_efla_beta(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(out), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return out
+
+
+def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+              beta: torch.Tensor, dO: torch.Tensor, g: Optional[torch.Tensor] = None,
+              S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None,
+              want_dS0: bool = True, chunk: int = 64, stream=None) -> dict:
+    """Gradients of delta_fwd (DeltaNet, GDN, KDA): dict of dq, dk, dv, dbeta, dg
+    (None for deltanet) in the input dtype and dS0 (fp32, None unless wanted)."""
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t, shape in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                           ("beta", beta, (B, T, H)), ("dO", dO, (B, T, H, dv))):
+        _check(name, t, shape, dt, dev)
+    gshape = None if variant == "deltanet" else ((B, T, H) if variant == "gdn" else (B, T, H, dk))
+    if gshape is not None:
+        _check("g", g, gshape, dt, dev)
+    elif g is not None:
+        raise ValueError("deltanet takes no decay")
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _check(name, t, (B, H, dv, dk), torch.float32, dev)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty_like(beta),
+           "dg": None if gshape is None else torch.empty(gshape, dtype=dt, device=dev),
+           "dS0": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None}
+    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], H)
+    st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
+                       _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                       _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]), _stream(stream))
     if st != 0:
         _raise(st)
     return out

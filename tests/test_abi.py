@@ -18,8 +18,8 @@ FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(12)]
 
 def test_exports_every_header_symbol():
     names = ops.header_functions()
-    assert set(names) == {"delta_fwd", "delta_decode", "delta_efla_beta", "dr_status_str",
-                          "dr_abi_version"}
+    assert set(names) == {"delta_fwd", "delta_decode", "delta_bwd", "delta_efla_beta",
+                          "dr_status_str", "dr_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -120,6 +120,30 @@ def test_grouped_heads_size_the_query_key_operands():
     import torch
     if not torch.cuda.is_available():
         assert fwd(d, o=after_k) == DR_E_DEVICE
+
+
+def bwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], g=FAKE[5], S0=None, dO=FAKE[4],
+        dST=None, dq=FAKE[7], dk=FAKE[8], dv=FAKE[9], dbeta=FAKE[10], dg=FAKE[11], dS0=None):
+    return lib.delta_bwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, g, S0, dO, dST,
+                         dq, dk, dv, dbeta, dg, dS0, None)
+
+
+def test_bwd_validation():
+    assert bwd(None) == DR_E_NULLPTR
+    for name in ("q", "k", "v", "beta", "dO", "dq", "dk", "dv", "dbeta"):
+        assert bwd(desc(), **{name: None}) == DR_E_NULLPTR, name
+    assert bwd(desc(variant=1), g=None) == DR_E_NULLPTR
+    assert bwd(desc(variant=1), dg=None) == DR_E_NULLPTR
+    assert bwd(desc(variant=0), g=None) == DR_E_UNSUPPORTED     # dg given to the ungated form
+    assert bwd(desc(variant=3)) == DR_E_UNSUPPORTED             # split gates: not supported
+    assert bwd(desc(H=4, H_k=2)) == DR_E_UNSUPPORTED            # grouped heads: not supported
+    assert bwd(desc(), dq=FAKE[0]) == DR_E_ALIAS                # dq over q
+    assert bwd(desc(), dv=FAKE[8]) == DR_E_ALIAS                # dv over dk
+    assert bwd(desc(), dS0=ctypes.c_void_p(FAKE[6].value + 4)) == DR_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert bwd(desc()) == DR_E_DEVICE
+        assert bwd(desc(variant=0), g=None, dg=None) == DR_E_DEVICE
 
 
 def test_decode_requires_one_token():
