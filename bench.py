@@ -50,6 +50,21 @@ def prefill_bytes(variant, B, T, H, dk, dv, elem=2, with_state_in=False, with_st
     return B * T * elem * (H * per_head + Hk * 2 * dk) + B * H * state
 
 
+def bwd_bytes(variant, B, T, H, dk, dv, elem=2):
+    """Algorithmic HBM bytes of one backward: the forward inputs and dO read once,
+    every gradient written once, the fp32 dS_T read and dS0 written once."""
+    gate = {"deltanet": 0, "gdn": 1, "kda": dk}[variant]
+    per_tok = 2 * dk + dv + 1 + gate + dv          # q, k, v, beta, g, dO
+    per_tok += 2 * dk + dv + 1 + gate              # dq, dk, dv, dbeta, dg
+    return B * T * H * elem * per_tok + B * H * 4 * dv * dk * 3
+
+
+def bwd_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic flops of the chunkwise backward (the forward recomputed once plus
+    its reverse): 3x the forward's per-token count."""
+    return 3 * (B * T * H * (6 * dk * dv + 3 * C * dk + 2 * C * dv + C * C / 3.0))
+
+
 def efla_bytes(B, T, H, Hk, dk, elem=2):
     """Exact-flow step sizes: k read once, beta read and beta_eff written once."""
     return B * T * elem * (Hk * dk + 2 * H)
@@ -303,6 +318,28 @@ def main():
                        "kernel_avg_us": t_e * 1e6, "hbm_GBs": nb / t_e / 1e9,
                        "hbm_frac": nb / t_e / 1e9 / HBM_PEAK_GBS,
                        "algorithmic_bytes_per_launch": nb})
+        # backward of the headline forward
+        xb = make_forward_inputs(w)
+        bsets = []
+        for _ in range(2):
+            bsets.append([up(xb[n]) for n in ("q", "k", "v", "beta", "g")] +
+                         [torch.randn((B, T, H, dv), device=dev).to(bf)])
+        ops.delta_bwd("gdn", *bsets[0][:4], bsets[0][5], g=bsets[0][4], stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(4):
+            bs = bsets[i % 2]
+            ops.delta_bwd("gdn", *bs[:4], bs[5], g=bs[4], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_b = e0.elapsed_time(e1) / 1e3 / 4
+        nb, nf = bwd_bytes("gdn", B, T, H, dk, dv), bwd_flops(B, T, H, dk, dv)
+        others.append({"workload": "gdn_bwd_bf16_b4_h16_t4096_d128", "kernel": "bwd_* (4 launches)",
+                       "kernel_avg_us": t_b * 1e6, "tokens_per_s": B * T / t_b,
+                       "hbm_GBs": nb / t_b / 1e9, "hbm_frac": nb / t_b / 1e9 / HBM_PEAK_GBS,
+                       "tflops": nf / t_b / 1e12, "algorithmic_bytes_per_launch": nb,
+                       "algorithmic_flops_per_launch": nf})
         result["other_workloads"] = others
 
     if not args.no_decode:

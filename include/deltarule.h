@@ -174,25 +174,27 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * a backward that keeps training chunkwise-parallel).  The forward states are
  * recomputed from the inputs; nothing from a delta_fwd call is needed.
  *
- *   desc, q, k, v, beta, g, S0   exactly as given to delta_fwd
+ *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd
  *   dO     [B, T, H, d_v] dtype: gradient arriving at o
  *   dS_T   [B, H, d_v, d_k] fp32: gradient arriving at the final state; NULL = 0
- *   dq, dk [B, T, H, d_k], dv [B, T, H, d_v], dbeta [B, T, H]       dtype (written)
- *   dg     DR_DELTANET: must be NULL; DR_GDN [B, T, H]; DR_KDA [B, T, H, d_k]
+ *   dq, dk [B, T, H, d_k], dv [B, T, H, d_v]                       dtype (written)
+ *   dbeta  [B, T, H]; DR_GDN2: gradient of the erase gate [B, T, H, d_k]   dtype (written)
+ *   dwgate DR_GDN2: gradient of the write gate [B, T, H, d_v]; otherwise must be NULL
+ *   dg     DR_DELTANET: must be NULL; DR_GDN [B, T, H]; DR_KDA/DR_GDN2 [B, T, H, d_k]
  *          dtype (written): gradient of the log-decay g
  *   dS0    [B, H, d_v, d_k] fp32 (written), gradient of S0; NULL if not wanted
  *
- * Supported: DR_DELTANET, DR_GDN and DR_KDA with H_k = H (0); DR_GDN2 and
- * grouped query/key heads return DR_E_UNSUPPORTED.  Outputs must not overlap
- * any input or one another.  Arithmetic is fp32 throughout.  Workspace: B * H *
- * ceil(T / 64) records of 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25
- * KiB for d_k/d_v = 128/64, 64/128, 64/64) from the same pool as delta_fwd's,
- * returned on the call's stream.
+ * Supported: every variant with H_k = H (0); grouped query/key heads return
+ * DR_E_UNSUPPORTED.  Outputs must not overlap any input or one another.
+ * Arithmetic is fp32 throughout.  Workspace: B * H * ceil(T / 64) records of
+ * 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB for d_k/d_v = 128/64,
+ * 64/128, 64/64), for DR_GDN2 768.5 KiB (640.5, 464.5, 384.25), from the same
+ * pool as delta_fwd's, returned on the call's stream.
  */
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
-                    const void* beta, const void* g, const float* S0, const void* dO,
-                    const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dg,
-                    float* dS0, void* stream);
+                    const void* beta, const void* wgate, const void* g, const float* S0,
+                    const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                    void* dbeta, void* dwgate, void* dg, float* dS0, void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* dr_status_str(int status);

@@ -206,32 +206,35 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
 }
 
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
-                    const void* beta, const void* g, const float* S0, const void* dO,
-                    const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dg,
-                    float* dS0, void* stream) {
+                    const void* beta, const void* wgate, const void* g, const float* S0,
+                    const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                    void* dbeta, void* dwgate, void* dg, float* dS0, void* stream) {
     try {
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
         if (st != DR_OK) return st;
-        if (desc->variant == DR_GDN2 || sz.Hk != desc->H) return DR_E_UNSUPPORTED;
+        if (sz.Hk != desc->H) return DR_E_UNSUPPORTED;
         if (q == nullptr || k == nullptr || v == nullptr || dO == nullptr || dq == nullptr ||
             dk == nullptr || dv == nullptr || dbeta == nullptr)
             return DR_E_NULLPTR;
-        st = check_gate_ptrs(desc, beta, nullptr, g);
+        st = check_gate_ptrs(desc, beta, wgate, g);
         if (st != DR_OK) return st;
         if ((desc->variant == DR_DELTANET) != (dg == nullptr))
             return desc->variant == DR_DELTANET ? DR_E_UNSUPPORTED : DR_E_NULLPTR;
-        const void* ptrs[] = {q, k, v, beta, g, S0, dO, dS_T, dq, dk, dv, dbeta, dg, dS0};
+        if ((desc->variant == DR_GDN2) != (dwgate != nullptr))
+            return desc->variant == DR_GDN2 ? DR_E_NULLPTR : DR_E_UNSUPPORTED;
+        const void* ptrs[] = {q, k, v, beta, wgate, g, S0, dO, dS_T, dq, dk, dv, dbeta, dwgate, dg, dS0};
         for (const void* p : ptrs)
             if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
         const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
         const Span in[] = {span_of(q, sz.qk, eb),   span_of(k, sz.qk, eb),  span_of(v, sz.v, eb),
-                           span_of(beta, sz.beta, eb), span_of(g, sz.g, eb), span_of(S0, sz.state, 4),
+                           span_of(beta, sz.beta, eb), span_of(wgate, sz.wgate, eb),
+                           span_of(g, sz.g, eb),    span_of(S0, sz.state, 4),
                            span_of(dO, sz.v, eb),   span_of(dS_T, sz.state, 4)};
         const Span out[] = {span_of(dq, sz.qk, eb), span_of(dk, sz.qk, eb), span_of(dv, sz.v, eb),
-                            span_of(dbeta, sz.beta, eb), span_of(dg, sz.g, eb),
-                            span_of(dS0, sz.state, 4)};
-        for (int i = 0; i < 6; ++i) {
+                            span_of(dbeta, sz.beta, eb), span_of(dwgate, sz.wgate, eb),
+                            span_of(dg, sz.g, eb),   span_of(dS0, sz.state, 4)};
+        for (int i = 0; i < 7; ++i) {
             for (const Span& s : in)
                 if (overlap(out[i], s)) return DR_E_ALIAS;
             for (int j = 0; j < i; ++j)
@@ -241,7 +244,7 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
         st = check_device();
         if (st != DR_OK) return st;
         dr::BwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, g, S0, dO,
-                      dS_T, dq, dk, dv, dbeta, dg, dS0};
+                      dS_T, dq, dk, dv, dbeta, dg, dS0, wgate, dwgate};
         const hipError_t e = dr::launch_bwd(desc->variant, desc->dtype, a,
                                             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;

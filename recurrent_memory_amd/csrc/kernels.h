@@ -59,6 +59,8 @@ struct BwdArgs {
     void* gbeta;
     void* gg;            // nullptr for the ungated form
     float* gS0;          // [B,H,dv,dk] or nullptr
+    const void* wgate;   // split gates: write gate [B,T,H,dv] (beta is then the
+    void* gw;            // erase gate [B,T,H,dk]) and its gradient; else nullptr
 };
 
 // variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
@@ -75,7 +77,7 @@ hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_
 hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_t stream);
 // exact-flow step sizes (dtype 0 fp32, 1 bf16)
 hipError_t launch_efla_beta(int dtype, const EflaArgs& a, hipStream_t stream);
-// backward of the single-step-size forms (variant 0, 1 or 2)
+// backward of every form (variant 0 .. 3)
 hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t stream);
 // library-owned stream-ordered memory pool of the current device (workspaces)
 hipError_t workspace_pool(hipMemPool_t* pool);

@@ -54,7 +54,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.delta_fwd.restype = ctypes.c_int
     lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.delta_decode.restype = ctypes.c_int
-    lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 15
+    lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 17
     lib.delta_bwd.restype = ctypes.c_int
     lib.delta_efla_beta.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp]
     lib.delta_efla_beta.restype = ctypes.c_int
@@ -224,9 +224,11 @@ def efla_beta(variant: str, k: torch.Tensor, beta: torch.Tensor,
 def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               beta: torch.Tensor, dO: torch.Tensor, g: Optional[torch.Tensor] = None,
               S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None,
-              want_dS0: bool = True, chunk: int = 64, stream=None) -> dict:
-    """Gradients of delta_fwd (DeltaNet, GDN, KDA): dict of dq, dk, dv, dbeta, dg
-    (None for deltanet) in the input dtype and dS0 (fp32, None unless wanted)."""
+              wgate: Optional[torch.Tensor] = None, want_dS0: bool = True, chunk: int = 64,
+              stream=None) -> dict:
+    """Gradients of delta_fwd: dict of dq, dk, dv, dbeta (gdn2: the erase gate's),
+    dwgate (gdn2 only), dg (None for deltanet) in the input dtype and dS0 (fp32,
+    None unless wanted)."""
     lib = load_library()
     var = VARIANTS[variant]
     B, T, H, dk = q.shape
@@ -234,9 +236,14 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
+    bshape = (B, T, H, dk) if variant == "gdn2" else (B, T, H)
     for name, t, shape in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
-                           ("beta", beta, (B, T, H)), ("dO", dO, (B, T, H, dv))):
+                           ("beta", beta, bshape), ("dO", dO, (B, T, H, dv))):
         _check(name, t, shape, dt, dev)
+    if variant == "gdn2":
+        _check("wgate", wgate, (B, T, H, dv), dt, dev)
+    elif wgate is not None:
+        raise ValueError("only gdn2 takes a write gate")
     gshape = None if variant == "deltanet" else ((B, T, H) if variant == "gdn" else (B, T, H, dk))
     if gshape is not None:
         _check("g", g, gshape, dt, dev)
@@ -247,12 +254,14 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             _check(name, t, (B, H, dv, dk), torch.float32, dev)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dbeta": torch.empty_like(beta),
+           "dwgate": torch.empty_like(wgate) if variant == "gdn2" else None,
            "dg": None if gshape is None else torch.empty(gshape, dtype=dt, device=dev),
            "dS0": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None}
     desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], H)
-    st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
-                       _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                       _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]), _stream(stream))
+    st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate), _ptr(g),
+                       _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
+                       _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dwgate"]), _ptr(out["dg"]),
+                       _ptr(out["dS0"]), _stream(stream))
     if st != 0:
         _raise(st)
     return out

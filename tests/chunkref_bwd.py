@@ -1,5 +1,5 @@
 """fp64 CPU model of the chunkwise backward that the HIP kernels implement
-(single step size: DeltaNet, GDN, KDA).  Test infrastructure only: it shares no
+(single step size: DeltaNet, GDN, KDA; split gates: Gated DeltaNet-2 below).  Test infrastructure only: it shares no
 code with the oracle or the kernels and is compared with the oracle's token-level
 reverse mode in test_chunkref_bwd.py.
 
@@ -101,3 +101,107 @@ def chunk_backward(q, k, v, beta, g, S0, dO, dST, C=64):
         dg[sl] = np.cumsum(dG[::-1], axis=0)[::-1]
         dSn = dS
     return dq, dkk, dv, dbeta, dg, dSn
+
+
+# ------------------------------------------------------------- split gates
+# Gated DeltaNet-2 (erase gate b on the key side, write gate w on the value
+# side), pairwise like the above:
+#     Ae = StrictTril(sum_c k_r (b k)_j E),  Ak = StrictTril(sum_c k_r k_j E),
+#     T = (I + Ae)^-1,  X = w v,  Z = Ak X,  W = T Khat,  Ut = T Z
+#     Me = Tril0(sum_c q_r (b k)_j E),  Mk = Tril0(sum_c q_r k_j E)
+#     Ebar = (b k) e^{G_C - G}
+#     Y = W S^T + Ut,  O = Qhat S^T - Me Y + Mk X,
+#     S_next = S Diag(gamma) - Y^T Ebar + X^T Kbar
+
+
+def _chunk_factors2(q, k, v, b, w, g):
+    C = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    diff = G[:, None, :] - G[None, :, :]
+    low = np.tril(np.ones((C, C), dtype=bool))
+    E = np.where(low[:, :, None], np.exp(np.where(low[:, :, None], diff, 0.0)), 0.0)
+    bk = b * k
+    strict = np.tril(np.ones((C, C)), -1)
+    Ae = np.einsum("rc,jc,rjc->rj", k, bk, E) * strict
+    Ak = np.einsum("rc,jc,rjc->rj", k, k, E) * strict
+    T = np.linalg.inv(np.eye(C) + Ae)
+    eG = np.exp(G)
+    ebar = np.exp(G[-1][None, :] - G)
+    X = w * v
+    Z = Ak @ X
+    Khat = k * eG
+    return dict(G=G, E=E, bk=bk, Ae=Ae, Ak=Ak, T=T, eG=eG, ebar=ebar, X=X, Z=Z, Khat=Khat,
+                Qhat=q * eG, Kbar=k * ebar, Ebar=bk * ebar, gamma=np.exp(G[-1]), W=T @ Khat,
+                Ut=T @ Z, Me=np.einsum("rc,jc,rjc->rj", q, bk, E) * low,
+                Mk=np.einsum("rc,jc,rjc->rj", q, k, E) * low)
+
+
+def chunk_forward2(q, k, v, b, w, g, S0, C=64):
+    T = q.shape[0]
+    S = np.array(S0, dtype=np.float64)
+    o = np.zeros((T, v.shape[1]))
+    saved = []
+    for t0 in range(0, T, C):
+        sl = slice(t0, min(T, t0 + C))
+        f = _chunk_factors2(q[sl], k[sl], v[sl], b[sl], w[sl], g[sl])
+        Y = f["W"] @ S.T + f["Ut"]
+        o[sl] = f["Qhat"] @ S.T - f["Me"] @ Y + f["Mk"] @ f["X"]
+        saved.append((sl, f, S, Y))
+        S = S * f["gamma"][None, :] - Y.T @ f["Ebar"] + f["X"].T @ f["Kbar"]
+    return o, S, saved
+
+
+def chunk_backward2(q, k, v, b, w, g, S0, dO, dST, C=64):
+    """Gradients for one head of the split-gate form: dq, dk, dv, db, dw, dg
+    (per channel) and dS0."""
+    _, _, saved = chunk_forward2(q, k, v, b, w, g, S0, C)
+    T, dk = q.shape
+    out = {n: np.zeros_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("db", b), ("dw", w))}
+    dgs = np.zeros((T, dk))
+    dSn = np.zeros((v.shape[1], dk)) if dST is None else np.array(dST, dtype=np.float64)
+    for sl, f, S, Y in reversed(saved):
+        qc, kc, vc, bc, wc, dOc = q[sl], k[sl], v[sl], b[sl], w[sl], dO[sl]
+        E, Tm, X = f["E"], f["T"], f["X"]
+        # reverse state chain
+        dY = -f["Me"].T @ dOc - f["Ebar"] @ dSn.T
+        dS = dSn * f["gamma"][None, :] + dOc.T @ f["Qhat"] + dY.T @ f["W"]
+        # per-chunk gradients
+        dMe = -np.tril(dOc @ Y.T)
+        dMk = np.tril(dOc @ X.T)
+        dQhat = dOc @ S
+        dW = dY @ S
+        dUt = dY
+        dEbar = -Y @ dSn
+        dKbar = X @ dSn
+        dZ = Tm.T @ dUt
+        dT = dW @ f["Khat"].T + dUt @ f["Z"].T
+        dAe = np.tril(-Tm.T @ dT @ Tm.T, -1)
+        dAk = np.tril(dZ @ X.T, -1)
+        dX = f["Mk"].T @ dOc + f["Kbar"] @ dSn.T + f["Ak"].T @ dZ
+        dKhat = Tm.T @ dW
+        out["dv"][sl] = wc * dX
+        out["dw"][sl] = vc * dX
+        # pairwise sums, per channel: "row" terms index r (left factor), "col" terms j
+        def row(M, R):   # sum_j M[r, j] R_j E[r, j]
+            return np.einsum("rj,jc,rjc->rc", M, R, E)
+
+        def col(M, L):   # sum_r M[r, j] L_r E[r, j]
+            return np.einsum("rj,rc,rjc->jc", M, L, E)
+
+        dq_ = dQhat * f["eG"] + row(dMe, f["bk"]) + row(dMk, kc)
+        dk_ = (row(dAe, f["bk"]) + row(dAk, kc) + col(dAk, kc) + col(dMk, qc)
+               + dKhat * f["eG"] + dKbar * f["ebar"])
+        dbk = col(dAe, kc) + col(dMe, qc) + dEbar * f["ebar"]
+        dG = (qc * row(dMe, f["bk"]) - f["bk"] * col(dMe, qc) + qc * row(dMk, kc) - kc * col(dMk, qc)
+              + kc * row(dAe, f["bk"]) - f["bk"] * col(dAe, kc) + kc * row(dAk, kc) - kc * col(dAk, kc)
+              + dKhat * f["Khat"] + dQhat * f["Qhat"] - dKbar * f["Kbar"] - dEbar * f["Ebar"])
+        dG[-1] += (np.sum(dKbar * f["Kbar"], axis=0) + np.sum(dEbar * f["Ebar"], axis=0)
+                   + f["gamma"] * np.sum(S * dSn, axis=0))
+        out["dq"][sl] = dq_
+        out["dk"][sl] = dk_ + dbk * bc
+        out["db"][sl] = dbk * kc
+        dgs[sl] = np.cumsum(dG[::-1], axis=0)[::-1]
+        dSn = dS
+    out["dg"] = dgs
+    out["dS0"] = dSn
+    return out

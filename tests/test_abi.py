@@ -122,10 +122,11 @@ def test_grouped_heads_size_the_query_key_operands():
         assert fwd(d, o=after_k) == DR_E_DEVICE
 
 
-def bwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], g=FAKE[5], S0=None, dO=FAKE[4],
-        dST=None, dq=FAKE[7], dk=FAKE[8], dv=FAKE[9], dbeta=FAKE[10], dg=FAKE[11], dS0=None):
-    return lib.delta_bwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, g, S0, dO, dST,
-                         dq, dk, dv, dbeta, dg, dS0, None)
+def bwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S0=None,
+        dO=FAKE[4], dST=None, dq=FAKE[7], dk=FAKE[8], dv=FAKE[9], dbeta=FAKE[10], dwgate=None,
+        dg=FAKE[11], dS0=None):
+    return lib.delta_bwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g, S0,
+                         dO, dST, dq, dk, dv, dbeta, dwgate, dg, dS0, None)
 
 
 def test_bwd_validation():
@@ -135,7 +136,9 @@ def test_bwd_validation():
     assert bwd(desc(variant=1), g=None) == DR_E_NULLPTR
     assert bwd(desc(variant=1), dg=None) == DR_E_NULLPTR
     assert bwd(desc(variant=0), g=None) == DR_E_UNSUPPORTED     # dg given to the ungated form
-    assert bwd(desc(variant=3)) == DR_E_UNSUPPORTED             # split gates: not supported
+    assert bwd(desc(variant=3)) == DR_E_NULLPTR                 # split gates need the write gate
+    assert bwd(desc(variant=3), wgate=FAKE[6]) == DR_E_NULLPTR  # ... and its gradient
+    assert bwd(desc(variant=1), dwgate=FAKE[6]) == DR_E_UNSUPPORTED
     assert bwd(desc(H=4, H_k=2)) == DR_E_UNSUPPORTED            # grouped heads: not supported
     assert bwd(desc(), dq=FAKE[0]) == DR_E_ALIAS                # dq over q
     assert bwd(desc(), dv=FAKE[8]) == DR_E_ALIAS                # dv over dk

@@ -56,3 +56,33 @@ def test_chunk_backward_matches_oracle(variant, C, T):
         np.testing.assert_allclose(dg.sum(axis=1), ref["dg"][0, :, 0], **tol)
     elif variant == "kda":
         np.testing.assert_allclose(dg, ref["dg"][0, :, 0], **tol)
+
+
+@pytest.mark.parametrize("C,T", [(1, 7), (16, 40), (37, 80), (64, 150)])
+def test_split_gate_chunk_backward_matches_oracle(C, T):
+    from chunkref_bwd import chunk_backward2, chunk_forward2
+    rng = np.random.default_rng(C * 77 + T)
+    dk, dv = 6, 5
+    q = rng.standard_normal((1, T, 1, dk)) / np.sqrt(dk)
+    k = rng.standard_normal((1, T, 1, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, T, 1, dv))
+    b = rng.uniform(0, 1, (1, T, 1, dk))
+    w = rng.uniform(0, 1, (1, T, 1, dv))
+    g = -rng.uniform(0, 0.5, (1, T, 1, dk))
+    S0 = rng.standard_normal((1, 1, dv, dk)) * 0.3
+    dO = rng.standard_normal((1, T, 1, dv))
+    dST = rng.standard_normal((1, 1, dv, dk))
+    x = dict(q=q, k=k, v=v, beta=b, wgate=w, g=g, S0=S0)
+    h = lambda a: a[0, :, 0]  # noqa: E731
+    o, S, _ = chunk_forward2(h(q), h(k), h(v), h(b), h(w), h(g), S0[0, 0], C)
+    o_ref, S_ref = delta_fwd("gdn2", **x)
+    np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-10, atol=1e-12)
+    got = chunk_backward2(h(q), h(k), h(v), h(b), h(w), h(g), S0[0, 0], h(dO), dST[0, 0], C)
+    ref = delta_bwd("gdn2", **x, dO=dO, dS_T=dST)
+    tol = dict(rtol=1e-9, atol=1e-11)
+    for mine, theirs in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("db", "dbeta"),
+                         ("dw", "dwgate"), ("dg", "dg")):
+        np.testing.assert_allclose(got[mine], h(ref[theirs]), err_msg=mine, **tol)
+    np.testing.assert_allclose(got["dS0"], ref["dS0"][0, 0], **tol)

@@ -1,6 +1,6 @@
 """Backward pass on the GPU (delta_bwd) against the oracle's reverse mode.
 
-Every gradient of DeltaNet, GDN and KDA in fp32 and bf16, at every head width,
+Every gradient of DeltaNet, GDN, KDA and GDN-2 in fp32 and bf16, at every head width,
 for sequence lengths 1, 63, 64, 65 and 200 (ragged last chunk), with a random
 initial state and a gradient arriving at the final state; plus a case with no
 final-state gradient and dS0 not requested, and a larger sampled case.
@@ -16,7 +16,7 @@ from recurrent_memory_amd.inputs import Workload, make_forward_inputs
 
 pytestmark = pytest.mark.gpu
 
-VARS = ["deltanet", "gdn", "kda"]
+VARS = ["deltanet", "gdn", "kda", "gdn2"]
 
 
 def _upstream(w, seed):
@@ -32,7 +32,8 @@ def _upstream(w, seed):
 def _run(variant, dtype, w, x, dO, dST, want_dS0=True):
     gr = ops.delta_bwd(variant, dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype),
                        dev(x["beta"], dtype), dev(dO, dtype), g=dev(x["g"], dtype),
-                       S0=dev(x["S0"], "f32"), dS_T=dev(dST, "f32"), want_dS0=want_dS0)
+                       S0=dev(x["S0"], "f32"), dS_T=dev(dST, "f32"), wgate=dev(x["wgate"], dtype),
+                       want_dS0=want_dS0)
     torch.cuda.synchronize()
     return {n: host(t) for n, t in gr.items()}
 
@@ -43,6 +44,8 @@ def _check(variant, dtype, gr, ref, heads_axes=(0, 2)):
     for n in ("dq", "dk", "dv"):
         errs[n] = slice_rel_err(gr[n], ref[n], heads_axes)
     errs["dbeta"] = slice_rel_err(gr["dbeta"], ref["dbeta"], heads_axes)
+    if variant == "gdn2":
+        errs["dwgate"] = slice_rel_err(gr["dwgate"], ref["dwgate"], heads_axes)
     if variant != "deltanet":
         errs["dg"] = slice_rel_err(gr["dg"], ref["dg"], heads_axes)
     if gr.get("dS0") is not None:
@@ -61,7 +64,7 @@ def test_bwd_small(variant, dtype, dk, dv, T):
     x = make_forward_inputs(w)
     dO, dST = _upstream(w, 7 + T)
     gr = _run(variant, dtype, w, x, dO, dST)
-    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], None, x["g"], x["S0"], dO, dST)
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
     _check(variant, dtype, gr, ref)
 
 
@@ -73,15 +76,15 @@ def test_bwd_no_state_gradient(variant):
     x = make_forward_inputs(w)
     dO, _ = _upstream(w, 9)
     gr = ops.delta_bwd(variant, dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["beta"]), dev(dO),
-                       g=dev(x["g"]), want_dS0=False)
+                       g=dev(x["g"]), wgate=dev(x["wgate"]), want_dS0=False)
     torch.cuda.synchronize()
     assert gr["dS0"] is None
     gr = {n: host(t) for n, t in gr.items()}
-    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], None, x["g"], None, dO, None)
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], None, dO, None)
     _check(variant, "f32", gr, ref)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "kda"])
+@pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2"])
 def test_bwd_long_sampled_heads(variant):
     """bf16, B=2, H=16, T=1024, d=128: two heads checked against the oracle."""
     announce("bwd_long", variant)
@@ -91,7 +94,7 @@ def test_bwd_long_sampled_heads(variant):
     gr = _run(variant, "bf16", w, x, dO, dST)
     for b, h in [(0, 3), (1, 14)]:
         sl = lambda a: None if a is None else a[[b]][:, :, [h]]  # noqa: E731
-        ref = oracle_bwd(variant, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), None,
+        ref = oracle_bwd(variant, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["wgate"]),
                          sl(x["g"]), x["S0"][[b]][:, [h]], sl(dO), dST[[b]][:, [h]])
         got = {n: (None if a is None else (a[[b]][:, [h]] if n == "dS0" else sl(a)))
                for n, a in gr.items()}
