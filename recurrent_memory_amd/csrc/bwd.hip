@@ -34,6 +34,43 @@ constexpr int kBC = 64;     // chunk length
 constexpr int kBT = 256;    // threads per workgroup
 constexpr int kBVT = 32;    // value rows per chain workgroup
 
+// One 16 x 16 output tile of an fp32 product on the matrix cores:
+// acc += A[i0, i0 + 16) x [k0, k1)  *  B[k0, k1) x [j0, j0 + 16), k1 - k0 a multiple
+// of 4; A(i, k) and B(k, j) read the operands in whatever layout they have.
+// v_mfma_f32_16x16x4f32: lane l supplies A(i0 + l % 16, k + l / 16) and
+// B(k + l / 16, j0 + l % 16); element q of the result is row i0 + 4 (l / 16) + q,
+// column j0 + l % 16.
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int k1, const FA& A,
+                                         const FB& B) {
+    const int l = threadIdx.x & 63;
+    const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
+#pragma unroll 4
+    for (int k = k0; k < k1; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
+    return acc;
+}
+
+// T = (I + diag(rs) A)^-1 for a strictly lower C x C matrix A (row stride lda;
+// rs = nullptr means no row scale).  Called by the 64 lanes of one wave, lane col
+// computing column col by forward substitution with the column held in registers
+// (fully unrolled), each row's sum split over four independent accumulators.
+__device__ __forceinline__ void unit_lower_inverse(const float* A, int lda, const float* rs, float* T,
+                                                   int ldt, int col) {
+    float t[kBC];
+#pragma unroll
+    for (int r = 0; r < kBC; ++r) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < r; ++j) acc[j & 3] = fmaf(A[r * lda + j], t[j], acc[j & 3]);
+        float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        if (rs) sum *= rs[r];
+        t[r] = (r == col ? 1.f : 0.f) - sum;
+    }
+#pragma unroll
+    for (int r = 0; r < kBC; ++r) T[r * ldt + col] = t[r];
+}
+
 // Workspace record of one (batch, head, chunk), in floats.
 template <int DK, int DV>
 struct BwdWs {
@@ -140,49 +177,50 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     for (int e = tid; e < kBC * DK; e += kBT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
     // Abar (strictly lower) and Mq (lower, diagonal included)
-    for (int e = tid; e < kBC * kBC; e += kBT) {
-        const int r = e / kBC, j = e % kBC;
-        float ab = 0.f, mq = 0.f;
-        if (j <= r) {
-            const float* kr = sK + r * (DK + 1);
-            const float* kj = sK + j * (DK + 1);
-            const float* qr = sX + r * LD;
-            if constexpr (VAR == 2) {
+    const int w = tid >> 6, l = tid & 63;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (VAR == 2) {   // a factor per channel: pairwise sums on the VALU
+        for (int e = tid; e < kBC * kBC; e += kBT) {
+            const int r = e / kBC, j = e % kBC;
+            float ab = 0.f, mq = 0.f;
+            if (j <= r) {
+                const float* kr = sK + r * (DK + 1);
+                const float* kj = sK + j * (DK + 1);
+                const float* qr = sX + r * LD;
                 const float* gr = sG + r * (DK + 1);
                 const float* gj = sG + j * (DK + 1);
                 for (int c = 0; c < DK; ++c) {
-                    const float w = kj[c] * __expf(gr[c] - gj[c]);
-                    ab = fmaf(kr[c], w, ab);
-                    mq = fmaf(qr[c], w, mq);
+                    const float wv = kj[c] * __expf(gr[c] - gj[c]);
+                    ab = fmaf(kr[c], wv, ab);
+                    mq = fmaf(qr[c], wv, mq);
                 }
-            } else {
-                for (int c = 0; c < DK; ++c) {
-                    ab = fmaf(kr[c], kj[c], ab);
-                    mq = fmaf(qr[c], kj[c], mq);
-                }
-                if constexpr (VAR == 1) {
-                    const float ex = __expf(sG[r * (DK + 1)] - sG[j * (DK + 1)]);
-                    ab *= ex;
-                    mq *= ex;
-                }
+                if (j == r) ab = 0.f;
             }
-            if (j == r) ab = 0.f;
+            sA[r * (kBC + 1) + j] = ab;
+            R[L::oAb + e] = ab;
+            R[L::oMq + e] = mq;
         }
-        sA[r * (kBC + 1) + j] = ab;
-        R[L::oAb + e] = ab;
-        R[L::oMq + e] = mq;
+    } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
+        for (int t = w; t < 16; t += 4) {
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            const f32x4 ab = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 1) + c]; },
+                                     [&](int c, int j) { return sK[j * (DK + 1) + c]; });
+            const f32x4 mq = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sX[r * LD + c]; },
+                                     [&](int c, int j) { return sK[j * (DK + 1) + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
+                const float ex = (VAR == 1 && j <= r) ? __expf(sG[r * (DK + 1)] - sG[j * (DK + 1)]) : 1.f;
+                const float a_ = j < r ? ab[q] * ex : 0.f;
+                sA[r * (kBC + 1) + j] = a_;
+                R[L::oAb + r * kBC + j] = a_;
+                R[L::oMq + r * kBC + j] = j <= r ? mq[q] * ex : 0.f;
+            }
+        }
     }
     __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution, one column per thread
-    if (tid < kBC) {
-        const int col = tid;
-        for (int r = 0; r < kBC; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
-            const float br = sBeta[r];
-            for (int j = col; j < r; ++j) acc = fmaf(-br * sA[r * (kBC + 1) + j], sT[j * (kBC + 1) + col], acc);
-            sT[r * (kBC + 1) + col] = acc;
-        }
-    }
+    if (tid < kBC) unit_lower_inverse(sA, kBC + 1, sBeta, sT, kBC + 1, tid);
     __syncthreads();
     for (int e = tid; e < kBC * kBC; e += kBT) R[L::oT + e] = sT[(e / kBC) * (kBC + 1) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
@@ -197,11 +235,12 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         sX[r * LD + c] = sBeta[r] * kk * eg;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kBT) {   // W = T X
-        const int r = e / DK, c = e % DK;
-        float acc = 0.f;
-        for (int j = 0; j <= r; ++j) acc = fmaf(sT[r * (kBC + 1) + j], sX[j * LD + c], acc);
-        R[L::oW + e] = acc;
+    for (int t = w; t < (kBC / 16) * (DK / 16); t += 4) {   // W = T X
+        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
+                                  [&](int j, int c) { return sX[j * LD + c]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
     for (int e = tid; e < kBC * DV; e += kBT) {   // Y = beta v
@@ -209,11 +248,12 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         sX[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tok_index(p, b, t0 + r, h) * DV + i) : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // U = T Y
-        const int r = e / DV, i = e % DV;
-        float acc = 0.f;
-        for (int j = 0; j <= r; ++j) acc = fmaf(sT[r * (kBC + 1) + j], sX[j * LD + i], acc);
-        R[L::oU + e] = acc;
+    for (int t = w; t < (kBC / 16) * (DV / 16); t += 4) {   // U = T Y
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
+                                  [&](int j, int i) { return sX[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
     }
 }
 
@@ -237,14 +277,54 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         const int i = e / DK, c = e % DK;
         sS[i * (DK + 1) + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
+    // the next chunk's operands are fetched into registers while this chunk's
+    // products run, and written to LDS at the top of the next step
+    const int w = tid >> 6, l = tid & 63;
+    constexpr int NP = kBC * DK / 4 / kBT;          // 16-byte pieces per thread per operand
+    constexpr int MT = (kBC / 16) * (kBVT / 16) / 4;  // Vt tiles per wave
+    float4 pW[NP], pK[NP], pE[SPLIT ? NP : 1];
+    float pU[MT][4];
+    float pG = 0.f;
+    auto fetch = [&](int n) {
+        const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kBT * j);
+            pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
+            pK[j] = *reinterpret_cast<const float4*>(R + L::oKb + idx);
+            if constexpr (SPLIT) pE[j] = *reinterpret_cast<const float4*>(R + L::oEb + idx);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int t = w + 4 * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pU[m][q] = R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + i0 + c0 + (l & 15)];
+        }
+        pG = tid < DK ? R[L::oGam + tid] : 0.f;
+    };
+    auto put4 = [&](float* dst, int idx, float4 v) {
+        float* d = dst + (idx / DK) * (DK + 1) + idx % DK;
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
+    };
+    fetch(0);
     for (int n = 0; n < N; ++n) {
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
-        for (int e = tid; e < kBC * DK; e += kBT) {
-            const int r = e / DK, c = e % DK;
-            sW[r * (DK + 1) + c] = R[L::oW + e];
-            sKb[r * (DK + 1) + c] = R[L::oKb + e];
-            if constexpr (SPLIT) sEb[r * (DK + 1) + c] = R[L::oEb + e];
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kBT * j);
+            put4(sW, idx, pW[j]);
+            put4(sKb, idx, pK[j]);
+            if constexpr (SPLIT) put4(sEb, idx, pE[j]);
         }
+        float uu[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) uu[m][q] = pU[m][q];
+        if (tid < DK) sGam[tid] = pG;
         if constexpr (SPLIT) {   // X = w v for this tile's value columns
             const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
             for (int e = tid; e < kBC * kBVT; e += kBT) {
@@ -257,33 +337,45 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
                 sXt[r * (kBVT + 1) + i] = x;
             }
         }
-        if (tid < DK) sGam[tid] = R[L::oGam + tid];
         __syncthreads();
+        if (n + 1 < N) fetch(n + 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
             R[L::oS + (i0 + i) * DK + c] = sS[i * (DK + 1) + c];
         }
         constexpr float sgn = SPLIT ? 1.f : -1.f;
-        for (int e = tid; e < kBC * kBVT; e += kBT) {   // Vt = U - W S^T  /  Y = Ut + W S^T
-            const int r = e / kBVT, i = e % kBVT;
-            float acc = R[L::oU + r * DV + i0 + i];
-            for (int c = 0; c < DK; ++c) acc = fmaf(sgn * sW[r * (DK + 1) + c], sS[i * (DK + 1) + c], acc);
-            sVt[r * (kBVT + 1) + i] = acc;
-            R[L::oVt + r * DV + i0 + i] = acc;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {   // Vt = U - W S^T  /  Y = Ut + W S^T
+            const int t = w + 4 * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+            const f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
+                                      [&](int r, int c) { return sW[r * (DK + 1) + c]; },
+                                      [&](int c, int i) { return sS[i * (DK + 1) + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
+                const float val = uu[m][q] + sgn * acc[q];
+                sVt[r * (kBVT + 1) + i] = val;
+                R[L::oVt + r * DV + i0 + i] = val;
+            }
         }
         __syncthreads();
-        for (int e = tid; e < kBVT * DK; e += kBT) {
-            const int i = e / DK, c = e % DK;
-            float acc = sS[i * (DK + 1) + c] * sGam[c];
-            if constexpr (SPLIT) {
-                for (int r = 0; r < kBC; ++r) {
-                    acc = fmaf(-sVt[r * (kBVT + 1) + i], sEb[r * (DK + 1) + c], acc);
-                    acc = fmaf(sXt[r * (kBVT + 1) + i], sKb[r * (DK + 1) + c], acc);
-                }
-            } else {
-                for (int r = 0; r < kBC; ++r) acc = fmaf(sVt[r * (kBVT + 1) + i], sKb[r * (DK + 1) + c], acc);
+        for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // S = S Diag(gamma) + ...
+            const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (SPLIT) {   // - Y^T Ebar + X^T Kbar
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return -sVt[r * (kBVT + 1) + i]; },
+                              [&](int r, int c) { return sEb[r * (DK + 1) + c]; });
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sXt[r * (kBVT + 1) + i]; },
+                              [&](int r, int c) { return sKb[r * (DK + 1) + c]; });
+            } else {                 // + Vt^T Kbar
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sVt[r * (kBVT + 1) + i]; },
+                              [&](int r, int c) { return sKb[r * (DK + 1) + c]; });
             }
-            sS[i * (DK + 1) + c] = acc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
+                sS[i * (DK + 1) + c] = fmaf(sS[i * (DK + 1) + c], sGam[c], acc[q]);
+            }
         }
         __syncthreads();
     }
@@ -301,6 +393,7 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     __shared__ float sM[kBC * (kBC + 1)];
     __shared__ float sA1[kBC * (DK + 1)];
     __shared__ float sA2[kBC * (DK + 1)];
+    __shared__ float sQh[kBC * (DK + 1)];
     __shared__ float sGam[DK];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NVT, i0 = (blockIdx.x % NVT) * kBVT;
@@ -309,46 +402,93 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         const int i = e / DK, c = e % DK;
         sdS[i * (DK + 1) + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
+    // the previous chunk's operands are fetched into registers during this step
+    constexpr int NP = kBC * DK / 4 / kBT;
+    constexpr int NM = kBC * kBC / 4 / kBT;
+    constexpr int NO = kBC * kBVT / kBT;
+    float4 pM[NM], pA[NP], pQ[NP], pW[NP];
+    float pO[NO];
+    float pG = 0.f;
+    auto fetch = [&](int n) {
+        const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
+#pragma unroll
+        for (int j = 0; j < NM; ++j) pM[j] = *reinterpret_cast<const float4*>(R + L::oMq + 4 * (tid + kBT * j));
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kBT * j);
+            pA[j] = *reinterpret_cast<const float4*>(R + (SPLIT ? L::oEb : L::oKb) + idx);
+            pQ[j] = *reinterpret_cast<const float4*>(R + L::oQh + idx);
+            pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
+        }
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int e = tid + kBT * j, r = e / kBVT, i = e % kBVT;
+            pO[j] = r < Cn ? load_elem<E>(p.dO, tok_index(p, b, t0 + r, h) * DV + i0 + i) : 0.f;
+        }
+        pG = tid < DK ? R[L::oGam + tid] : 0.f;
+    };
+    auto put4 = [&](float* dst, int idx, int ld, int row, float4 v) {
+        float* d = dst + (idx / row) * ld + idx % row;
+        d[0] = v.x;
+        d[1] = v.y;
+        d[2] = v.z;
+        d[3] = v.w;
+    };
+    fetch(N - 1);
     for (int n = N - 1; n >= 0; --n) {
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
-        const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
-        for (int e = tid; e < kBC * kBC; e += kBT) sM[(e / kBC) * (kBC + 1) + e % kBC] = R[L::oMq + e];
-        for (int e = tid; e < kBC * DK; e += kBT)
-            sA1[(e / DK) * (DK + 1) + e % DK] = R[(SPLIT ? L::oEb : L::oKb) + e];
-        for (int e = tid; e < kBC * kBVT; e += kBT) {
-            const int r = e / kBVT, i = e % kBVT;
-            sdO[r * (kBVT + 1) + i] = r < Cn ? load_elem<E>(p.dO, tok_index(p, b, t0 + r, h) * DV + i0 + i) : 0.f;
+#pragma unroll
+        for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kBT * j), kBC + 1, kBC, pM[j]);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kBT * j);
+            put4(sA1, idx, DK + 1, DK, pA[j]);
+            put4(sQh, idx, DK + 1, DK, pQ[j]);
+            put4(sA2, idx, DK + 1, DK, pW[j]);
         }
-        if (tid < DK) sGam[tid] = R[L::oGam + tid];
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int e = tid + kBT * j;
+            sdO[(e / kBVT) * (kBVT + 1) + e % kBVT] = pO[j];
+        }
+        if (tid < DK) sGam[tid] = pG;
         __syncthreads();
+        if (n > 0) fetch(n - 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
             R[L::odS + (i0 + i) * DK + c] = sdS[i * (DK + 1) + c];
         }
-        for (int e = tid; e < kBC * kBVT; e += kBT) {   // dVt = Mq^T dO + Kbar dS^T
-            const int r = e / kBVT, i = e % kBVT;
-            float acc = 0.f;
-            for (int m = r; m < kBC; ++m) acc = fmaf(sM[m * (kBC + 1) + r], sdO[m * (kBVT + 1) + i], acc);
-            for (int c = 0; c < DK; ++c) acc = fmaf(sA1[r * (DK + 1) + c], sdS[i * (DK + 1) + c], acc);
-            if constexpr (SPLIT) acc = -acc;
-            sdVt[r * (kBVT + 1) + i] = acc;
-            R[L::odVt + r * DV + i0 + i] = acc;
-        }
-        __syncthreads();
-        for (int e = tid; e < kBC * DK; e += kBT) {
-            const int r = e / DK, c = e % DK;
-            sA1[r * (DK + 1) + c] = R[L::oQh + e];
-            sA2[r * (DK + 1) + c] = R[L::oW + e];
-        }
-        __syncthreads();
-        for (int e = tid; e < kBVT * DK; e += kBT) {    // dS = dS Diag(gamma) + dO^T Qhat - dVt^T W
-            const int i = e / DK, c = e % DK;
-            float acc = sdS[i * (DK + 1) + c] * sGam[c];
-            for (int r = 0; r < kBC; ++r) {
-                acc = fmaf(sdO[r * (kBVT + 1) + i], sA1[r * (DK + 1) + c], acc);
-                acc = fmaf((SPLIT ? 1.f : -1.f) * sdVt[r * (kBVT + 1) + i], sA2[r * (DK + 1) + c], acc);
+        const int w = tid >> 6, l = tid & 63;
+        for (int t = w; t < (kBC / 16) * (kBVT / 16); t += 4) {   // dVt = Mq^T dO + Kbar dS^T
+            const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+            f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
+                                [&](int r, int m) { return sM[m * (kBC + 1) + r]; },
+                                [&](int m, int i) { return sdO[m * (kBVT + 1) + i]; });
+            acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * (DK + 1) + c]; },
+                          [&](int c, int i) { return sdS[i * (DK + 1) + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
+                const float val = SPLIT ? -acc[q] : acc[q];
+                sdVt[r * (kBVT + 1) + i] = val;
+                R[L::odVt + r * DV + i0 + i] = val;
             }
-            sdS[i * (DK + 1) + c] = acc;
+        }
+        __syncthreads();
+        for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // dS = dS Diag(gamma) + dO^T Qhat -/+ dVt^T W
+            const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
+            f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, ii0, cc0, 0, kBC,
+                                [&](int i, int r) { return sdO[r * (kBVT + 1) + i]; },
+                                [&](int r, int c) { return sQh[r * (DK + 1) + c]; });
+            acc = mm_tile(acc, ii0, cc0, 0, kBC,
+                          [&](int i, int r) { return (SPLIT ? 1.f : -1.f) * sdVt[r * (kBVT + 1) + i]; },
+                          [&](int r, int c) { return sA2[r * (DK + 1) + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
+                sdS[i * (DK + 1) + c] = fmaf(sdS[i * (DK + 1) + c], sGam[c], acc[q]);
+            }
         }
         __syncthreads();
     }
@@ -361,25 +501,37 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
 }
 
 // ------------------------------------------------------------ 4. gradients
+// Products run on the matrix cores as 16 x 16 tiles spread over the four waves;
+// the per-element pairwise sums of the channel-wise decay stay on the VALU.
 template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
     constexpr int CP = kBC + 1;
     constexpr int LD = (DK > DV ? DK : DV) + 1;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;   // region size
-    __shared__ float sM1[kBC * CP];   // dMq
-    __shared__ float sM2[kBC * CP];   // dT, then dA, then dAbar
+    constexpr int QR = 32;            // rows of S (or dS') staged at a time
+    static_assert(QR * (DK + 1) <= kBC * CP, "S quarter must fit the second C x C buffer");
+    __shared__ float sM1[kBC * CP];   // dMq (then dMq E)
+    __shared__ float sM2[kBC * CP];   // S quarters; dT; dA; dAbar (then dAbar E)
     __shared__ float sR[3 * RS];      // three staging regions
     __shared__ float sBeta[kBC];
-    __shared__ float sCol[5 * DK];    // column terms of the last row of dG
+    __shared__ float sCol[2 * DK];    // column terms of the last row of dG
+    __shared__ float sPart[kBT];      // per-thread partial column sums
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // element q of a tile at (i0, j0) in this lane
+    auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
+    auto tj = [&](int j0) { return j0 + (l & 15); };
+    constexpr int TCD = (kBC / 16) * (DK / 16);   // C x DK tiles
+    constexpr int TCV = (kBC / 16) * (DV / 16);   // C x DV tiles
+    constexpr int TCC = (kBC / 16) * (kBC / 16);  // C x C tiles
 
     if (tid < kBC) sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tix(tid)) : 0.f;
     for (int e = tid; e < kBC * DV; e += kBT) {   // dO -> R0, Vt -> R1, dVt -> R2
@@ -388,50 +540,86 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         R1[r * LD + i] = R[L::oVt + e];
         R2[r * LD + i] = R[L::odVt + e];
     }
-    __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // dMq = Tril0(dO Vt^T)
-        const int r = e / kBC, j = e % kBC;
+    constexpr int TPC = kBT / DK;   // threads per column for column sums
+    {   // sum_i S dS' per column, TPC partial sums combined in a fixed order
+        const int c = tid % DK, part = tid / DK;
         float acc = 0.f;
-        if (j <= r)
-            for (int i = 0; i < DV; ++i) acc = fmaf(R0[r * LD + i], R1[j * LD + i], acc);
-        sM1[r * CP + j] = acc;
+#pragma unroll 8
+        for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
+            acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
+        sPart[tid] = acc;
     }
-    // dQhat = dO S, dW = -dVt S, dKbar = Vt dS': thread owns column c, rows rr
-    {
-        constexpr int TPC = kBT / DK;             // threads per column
-        constexpr int NR = kBC / TPC;             // rows per thread
-        const int c = tid % DK, rq = tid / DK;
-        float aq[NR], aw[NR], ak[NR];
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
+        sCol[tid] = R[L::oGam + tid] * acc;
+    }
+    for (int t = w; t < TCC; t += 4) {            // dMq = Tril0(dO Vt^T)
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 acc = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+                                  [&](int i, int j) { return R1[j * LD + i]; });
 #pragma unroll
-        for (int m = 0; m < NR; ++m) aq[m] = aw[m] = ak[m] = 0.f;
-        float sds = 0.f;
-        for (int i = 0; i < DV; ++i) {
-            const float s = R[L::oS + i * DK + c];
-            const float ds = R[L::odS + i * DK + c];
-            sds = fmaf(s, ds, sds);
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), j = tj(j0);
+            sM1[r * CP + j] = j <= r ? acc[q] : 0.f;
+        }
+    }
+    {   // dQhat = dO S, dW = -dVt S, then dKbar = Vt dS', with S and dS' staged by rows
+        constexpr int MT = TCD / 4;   // tiles per wave
+        f32x4 aq[MT], aw[MT];
 #pragma unroll
-            for (int m = 0; m < NR; ++m) {
-                const int r = rq + TPC * m;
-                aq[m] = fmaf(R0[r * LD + i], s, aq[m]);
-                aw[m] = fmaf(-R2[r * LD + i], s, aw[m]);
-                ak[m] = fmaf(R1[r * LD + i], ds, ak[m]);
+        for (int m = 0; m < MT; ++m) aq[m] = aw[m] = z4;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int64_t src = pass == 0 ? L::oS : L::odS;
+            for (int i0 = 0; i0 < DV; i0 += QR) {
+                __syncthreads();
+                for (int e = tid; e < QR * DK; e += kBT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
+                __syncthreads();
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const int t = w + 4 * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                    auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; };
+                    if (pass == 0) {
+                        aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
+                        aw[m] = mm_tile(aw[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R2[r * LD + i]; }, Bs);
+                    } else {
+                        aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R1[r * LD + i]; }, Bs);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int t = w + 4 * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = ti(r0, q), c = tj(c0);
+                    if (pass == 0) {
+                        R[L::odQh + r * DK + c] = aq[m][q];
+                        R[L::odW + r * DK + c] = aw[m][q];
+                    } else {
+                        R[L::odKb + r * DK + c] = aq[m][q];
+                    }
+                }
+                aq[m] = z4;
             }
         }
-        float kbsum = 0.f;
-#pragma unroll
-        for (int m = 0; m < NR; ++m) {
-            const int r = rq + TPC * m;
-            R[L::odQh + r * DK + c] = aq[m];
-            R[L::odW + r * DK + c] = aw[m];
-            R[L::odKb + r * DK + c] = ak[m];
-            kbsum = fmaf(ak[m], R[L::oKb + r * DK + c], kbsum);
-        }
-        // the last row's column terms: gamma * sum_i S dS' (same in every thread of
-        // the column) and this thread's part of sum_r dKbar Kbar
-        if (rq == 0) sCol[c] = R[L::oGam + c] * sds;
-        sCol[DK * (1 + rq) + c] = kbsum;
     }
     __syncthreads();
+    {   // sum_r dKbar Kbar per column
+        const int c = tid % DK, part = tid / DK;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int r = part * (kBC / TPC); r < (part + 1) * (kBC / TPC); ++r)
+            acc = fmaf(R[L::odKb + r * DK + c], R[L::oKb + r * DK + c], acc);
+        sPart[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
+        sCol[DK + tid] = acc;
+    }
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
     for (int e = tid; e < kBC * DK; e += kBT) {   // dW -> R0, X -> R1
         const int r = e / DK, c = e % DK;
@@ -439,11 +627,12 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         R1[r * LD + c] = sBeta[r] * R[L::oKh + e];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {
-        const int r = e / kBC, j = e % kBC;
-        float acc = 0.f;
-        for (int c = 0; c < DK; ++c) acc = fmaf(R0[r * LD + c], R1[j * LD + c], acc);
-        sM2[r * CP + j] = acc;
+    f32x4 adt[TCC / 4];
+#pragma unroll
+    for (int m = 0; m < TCC / 4; ++m) {
+        const int t = w + 4 * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        adt[m] = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
+                         [&](int c, int j) { return R1[j * LD + c]; });
     }
     __syncthreads();
     for (int e = tid; e < kBC * DV; e += kBT) {   // Y -> R1
@@ -451,11 +640,13 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         R1[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tix(r) * DV + i) : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {
-        const int r = e / kBC, j = e % kBC;
-        float acc = sM2[r * CP + j];
-        for (int i = 0; i < DV; ++i) acc = fmaf(R2[r * LD + i], R1[j * LD + i], acc);
-        sM2[r * CP + j] = acc;
+#pragma unroll
+    for (int m = 0; m < TCC / 4; ++m) {
+        const int t = w + 4 * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        adt[m] = mm_tile(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
+                         [&](int i, int j) { return R1[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sM2[ti(r0, q) * CP + tj(j0)] = adt[m][q];
     }
     __syncthreads();
     // dA = -T^T dT T^T (strictly lower); T -> R1[0 .. C*CP), tmp -> R1[C*CP ..)
@@ -463,40 +654,52 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     float* sTmp = R1 + kBC * CP;
     for (int e = tid; e < kBC * kBC; e += kBT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // tmp = dT T^T
-        const int r = e / kBC, j = e % kBC;
-        float acc = 0.f;
-        for (int m = 0; m <= j; ++m) acc = fmaf(sM2[r * CP + m], sT[j * CP + m], acc);
-        sTmp[r * CP + j] = acc;
+    for (int t = w; t < TCC; t += 4) {            // tmp = dT T^T
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
+                                  [&](int m, int j) { return sT[j * CP + m]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // dA = -T^T tmp, masked
-        const int r = e / kBC, j = e % kBC;
-        float acc = 0.f;
-        if (j < r)
-            for (int m = r; m < kBC; ++m) acc = fmaf(-sT[m * CP + r], sTmp[m * CP + j], acc);
-        sM2[r * CP + j] = acc;
+    for (int t = w; t < TCC; t += 4) {            // dA = -T^T tmp, masked
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                  [&](int m, int j) { return sTmp[m * CP + j]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), j = tj(j0);
+            sM2[r * CP + j] = j < r ? -acc[q] : 0.f;
+        }
+    }
+    for (int t = w; t < TCD; t += 4) {            // dX = T^T dW (dKhat = beta dX)
+        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                  [&](int m, int c) { return R0[m * LD + c]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
     }
     __syncthreads();
-    // dX = T^T dW (kept for dKhat), dY = T^T dVt -> dv, and dbeta; 4 threads per row
-    {
+    for (int t = w; t < TCV; t += 4) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                  [&](int m, int i) { return R2[m * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), i = tj(c0);
+            R0[r * LD + i] = acc[q];
+            if (r < Cn) store_elem<E>(p.gv, tix(r) * DV + i, sBeta[r] * acc[q]);
+        }
+    }
+    __syncthreads();
+    {   // dbeta: 4 threads per row, fixed-order sums
         const int r = tid / 4, qt = tid % 4;
         float db = 0.f;
-        for (int c = qt * (DK / 4); c < (qt + 1) * (DK / 4); ++c) {
-            float acc = 0.f;
-            for (int m = r; m < kBC; ++m) acc = fmaf(sT[m * CP + r], R0[m * LD + c], acc);
-            R[L::odX + r * DK + c] = acc;
-            db = fmaf(acc, R[L::oKh + r * DK + c], db);
-        }
-        for (int i = qt * (DV / 4); i < (qt + 1) * (DV / 4); ++i) {
-            float acc = 0.f;
-            for (int m = r; m < kBC; ++m) acc = fmaf(sT[m * CP + r], R2[m * LD + i], acc);
-            if (r < Cn) {
-                const float vv = load_elem<E>(p.v, tix(r) * DV + i);
-                db = fmaf(acc, vv, db);
-                store_elem<E>(p.gv, tix(r) * DV + i, sBeta[r] * acc);
-            }
-        }
+        for (int c = qt * (DK / 4); c < (qt + 1) * (DK / 4); ++c)
+            db = fmaf(R[L::odX + r * DK + c], R[L::oKh + r * DK + c], db);
+        if (r < Cn)
+            for (int i = qt * (DV / 4); i < (qt + 1) * (DV / 4); ++i)
+                db = fmaf(R0[r * LD + i], load_elem<E>(p.v, tix(r) * DV + i), db);
         for (int j = qt * (kBC / 4); j < (qt + 1) * (kBC / 4); ++j)
             db = fmaf(sM2[r * CP + j], R[L::oAb + r * kBC + j], db);
         db += __shfl_xor(db, 1);
@@ -504,8 +707,8 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         if (qt == 0 && r < Cn) store_elem<E>(p.gbeta, tix(r), db);
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];   // dAbar
-    // q, k, G -> R0, R1, R2
+    // q, k, G -> R0, R1, R2; dAbar = beta dA
+    for (int e = tid; e < kBC * kBC; e += kBT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];
     for (int e = tid; e < kBC * DK; e += kBT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
@@ -514,28 +717,14 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         R2[r * LD + c] = R[L::oG + e];
     }
     __syncthreads();
-    // per element (r, c): pairwise sums with E = exp(G_r - G_j)
-    for (int e = tid; e < kBC * DK; e += kBT) {
-        const int r = e / DK, c = e % DK;
+    // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
+    // a3 = sum_{j<r} dAbar[r,j] k_j E,  a4 = sum_{j>r} dAbar[j,r] k_j E,  E = e^{G_r - G_j} (row r >= j)
+    auto finish = [&](int r, int c, float a1, float a2, float a3, float a4) {
         const float Gr = R2[r * LD + c];
         const float qr = R0[r * LD + c], kr = R1[r * LD + c];
-        float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
-        for (int j = 0; j < kBC; ++j) {
-            const float Gj = R2[j * LD + c];
-            if (j <= r) {
-                const float ex = (VAR == 0) ? 1.f : __expf(Gr - Gj);
-                const float kj = R1[j * LD + c] * ex;
-                a1 = fmaf(sM1[r * CP + j], kj, a1);
-                a3 = fmaf(sM2[r * CP + j], kj, a3);   // dAbar is zero on the diagonal
-            }
-            if (j >= r) {
-                const float ex = (VAR == 0) ? 1.f : __expf(Gj - Gr);
-                a2 = fmaf(sM1[j * CP + r], R0[j * LD + c] * ex, a2);
-                a4 = fmaf(sM2[j * CP + r], R1[j * LD + c] * ex, a4);
-            }
-        }
         const float eg = (VAR == 0) ? 1.f : __expf(Gr);
         const float ebar = (VAR == 0) ? 1.f : __expf(R2[(kBC - 1) * LD + c] - Gr);
+        const int e = r * DK + c;
         const float dQh = R[L::odQh + e];
         const float dKh = sBeta[r] * R[L::odX + e];
         const float dKb = R[L::odKb + e];
@@ -543,19 +732,68 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             store_elem<E>(p.gq, tix(r) * DK + c, fmaf(dQh, eg, a1));
             store_elem<E>(p.gk, tix(r) * DK + c, a2 + a3 + a4 + dKh * eg + dKb * ebar);
         }
-        // dG: pairwise terms plus the row factors (Khat, Qhat, Kbar); overwrites dQhat
-        const float dG = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg
+        R[L::odQh + e] = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg
                          - dKb * kr * ebar;
-        R[L::odQh + e] = dG;
+    };
+    if constexpr (VAR == 2) {
+        for (int e = tid; e < kBC * DK; e += kBT) {
+            const int r = e / DK, c = e % DK;
+            const float Gr = R2[r * LD + c];
+            float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
+            for (int j = 0; j < kBC; ++j) {
+                const float Gj = R2[j * LD + c];
+                if (j <= r) {
+                    const float kj = R1[j * LD + c] * __expf(Gr - Gj);
+                    a1 = fmaf(sM1[r * CP + j], kj, a1);
+                    a3 = fmaf(sM2[r * CP + j], kj, a3);
+                }
+                if (j >= r) {
+                    const float ex = __expf(Gj - Gr);
+                    a2 = fmaf(sM1[j * CP + r], R0[j * LD + c] * ex, a2);
+                    a4 = fmaf(sM2[j * CP + r], R1[j * LD + c] * ex, a4);
+                }
+            }
+            finish(r, c, a1, a2, a3, a4);
+        }
+    } else {
+        // the decay factor is one number per (r, j): fold it into dMq and dAbar and
+        // take the four sums as products
+        if constexpr (VAR == 1) {
+            for (int e = tid; e < kBC * kBC; e += kBT) {
+                const int r = e / kBC, j = e % kBC;
+                if (j <= r) {
+                    const float ex = __expf(R2[r * LD] - R2[j * LD]);
+                    sM1[r * CP + j] *= ex;
+                    sM2[r * CP + j] *= ex;
+                }
+            }
+            __syncthreads();
+        }
+        for (int t = w; t < TCD; t += 4) {
+            const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const f32x4 a1 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
+                                     [&](int j, int c) { return R1[j * LD + c]; });
+            const f32x4 a2 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[j * CP + r]; },
+                                     [&](int j, int c) { return R0[j * LD + c]; });
+            const f32x4 a3 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[r * CP + j]; },
+                                     [&](int j, int c) { return R1[j * LD + c]; });
+            const f32x4 a4 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
+                                     [&](int j, int c) { return R1[j * LD + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q]);
+        }
     }
     if constexpr (VAR != 0) {
         __syncthreads();
         if (tid < DK) {   // reverse cumulative sum over rows; G_C's terms enter at the last row
             const int c = tid;
-            float acc = sCol[c];
-            for (int q2 = 0; q2 < kBT / DK; ++q2) acc += sCol[DK * (1 + q2) + c];
+            float dgv[kBC];
+#pragma unroll
+            for (int r = 0; r < kBC; ++r) dgv[r] = R[L::odQh + r * DK + c];
+            float acc = sCol[c] + sCol[DK + c];
+#pragma unroll
             for (int r = kBC - 1; r >= 0; --r) {
-                acc += R[L::odQh + r * DK + c];
+                acc += dgv[r];
                 if constexpr (VAR == 2) {
                     if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, acc);
                 } else {
@@ -628,14 +866,7 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     }
     __syncthreads();
     float* sT = sR2;
-    if (tid < kBC) {   // T = (I + Ae)^-1
-        const int col = tid;
-        for (int r = 0; r < kBC; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
-            for (int j = col; j < r; ++j) acc = fmaf(-sM[r * CP + j], sT[j * CP + col], acc);
-            sT[r * CP + col] = acc;
-        }
-    }
+    if (tid < kBC) unit_lower_inverse(sM, CP, nullptr, sT, CP, tid);   // T = (I + Ae)^-1
     __syncthreads();
     for (int e = tid; e < kBC * kBC; e += kBT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
     for (int e = tid; e < kBC * DK; e += kBT) {   // Ebar, Kbar, Khat; Khat -> sR1
