@@ -33,6 +33,9 @@ namespace {
 constexpr int kBC = 64;     // chunk length
 constexpr int kBT = 256;    // threads per workgroup
 constexpr int kBVT = 32;    // value rows per chain workgroup
+constexpr int kGT = 512;    // threads of the gradient workgroup
+constexpr int kGW = kGT / 64;
+constexpr int kRT = kGT / 64;   // its threads per row for row sums
 
 // One 16 x 16 output tile of an fp32 product on the matrix cores:
 // acc += A[i0, i0 + 16) x [k0, k1)  *  B[k0, k1) x [j0, j0 + 16), k1 - k0 a multiple
@@ -139,7 +142,7 @@ __device__ __forceinline__ int64_t tok_index(const BwdArgs& p, int b, int t, int
 
 // ---------------------------------------------------------------- 1. factors
 template <int VAR, typename E, int DK, int DV>
-__global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
     constexpr int LD = (DK > DV ? DK : DV) + 1;   // padded row stride
     __shared__ float sK[kBC * (DK + 1)];
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
 
-    for (int e = tid; e < kBC * DK; e += kBT) {
+    for (int e = tid; e < kBC * DK; e += kGT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const int64_t ti = tok_index(p, b, t0 + min(r, Cn - 1), h);
@@ -174,13 +177,13 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kBT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
+    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
     // Abar (strictly lower) and Mq (lower, diagonal included)
     const int w = tid >> 6, l = tid & 63;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (VAR == 2) {   // a factor per channel: pairwise sums on the VALU
-        for (int e = tid; e < kBC * kBC; e += kBT) {
+        for (int e = tid; e < kBC * kBC; e += kGT) {
             const int r = e / kBC, j = e % kBC;
             float ab = 0.f, mq = 0.f;
             if (j <= r) {
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
             R[L::oMq + e] = mq;
         }
     } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
-        for (int t = w; t < 16; t += 4) {
+        for (int t = w; t < 16; t += kGW) {
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
             const f32x4 ab = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 1) + c]; },
                                      [&](int c, int j) { return sK[j * (DK + 1) + c]; });
@@ -222,9 +225,9 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     // T = (I + diag(beta) Abar)^-1 by forward substitution, one column per thread
     if (tid < kBC) unit_lower_inverse(sA, kBC + 1, sBeta, sT, kBC + 1, tid);
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) R[L::oT + e] = sT[(e / kBC) * (kBC + 1) + e % kBC];
+    for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 1) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
-    for (int e = tid; e < kBC * DK; e += kBT) {
+    for (int e = tid; e < kBC * DK; e += kGT) {
         const int r = e / DK, c = e % DK;
         const float G = sG[r * (DK + 1) + c];
         const float eg = __expf(G);
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         sX[r * LD + c] = sBeta[r] * kk * eg;
     }
     __syncthreads();
-    for (int t = w; t < (kBC / 16) * (DK / 16); t += 4) {   // W = T X
+    for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T X
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
         const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
                                   [&](int j, int c) { return sX[j * LD + c]; });
@@ -243,12 +246,12 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // Y = beta v
+    for (int e = tid; e < kBC * DV; e += kGT) {   // Y = beta v
         const int r = e / DV, i = e % DV;
         sX[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tok_index(p, b, t0 + r, h) * DV + i) : 0.f;
     }
     __syncthreads();
-    for (int t = w; t < (kBC / 16) * (DV / 16); t += 4) {   // U = T Y
+    for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // U = T Y
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
         const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
                                   [&](int j, int i) { return sX[j * LD + i]; });
@@ -501,10 +504,10 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
 }
 
 // ------------------------------------------------------------ 4. gradients
-// Products run on the matrix cores as 16 x 16 tiles spread over the four waves;
+// Products run on the matrix cores as 16 x 16 tiles spread over the eight waves;
 // the per-element pairwise sums of the channel-wise decay stay on the VALU.
 template <int VAR, typename E, int DK, int DV>
-__global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
     constexpr int CP = kBC + 1;
     constexpr int LD = (DK > DV ? DK : DV) + 1;
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __shared__ float sR[3 * RS];      // three staging regions
     __shared__ float sBeta[kBC];
     __shared__ float sCol[2 * DK];    // column terms of the last row of dG
-    __shared__ float sPart[kBT];      // per-thread partial column sums
+    __shared__ float sPart[kGT];      // per-thread partial column sums
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
@@ -534,13 +537,13 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     constexpr int TCC = (kBC / 16) * (kBC / 16);  // C x C tiles
 
     if (tid < kBC) sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tix(tid)) : 0.f;
-    for (int e = tid; e < kBC * DV; e += kBT) {   // dO -> R0, Vt -> R1, dVt -> R2
+    for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Vt -> R1, dVt -> R2
         const int r = e / DV, i = e % DV;
         R0[r * LD + i] = r < Cn ? load_elem<E>(p.dO, tix(r) * DV + i) : 0.f;
         R1[r * LD + i] = R[L::oVt + e];
         R2[r * LD + i] = R[L::odVt + e];
     }
-    constexpr int TPC = kBT / DK;   // threads per column for column sums
+    constexpr int TPC = kGT / DK;   // threads per column for column sums
     {   // sum_i S dS' per column, TPC partial sums combined in a fixed order
         const int c = tid % DK, part = tid / DK;
         float acc = 0.f;
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
         sCol[tid] = R[L::oGam + tid] * acc;
     }
-    for (int t = w; t < TCC; t += 4) {            // dMq = Tril0(dO Vt^T)
+    for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 acc = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                   [&](int i, int j) { return R1[j * LD + i]; });
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
     }
     {   // dQhat = dO S, dW = -dVt S, then dKbar = Vt dS', with S and dS' staged by rows
-        constexpr int MT = TCD / 4;   // tiles per wave
+        constexpr int MT = TCD / kGW;   // tiles per wave
         f32x4 aq[MT], aw[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) aq[m] = aw[m] = z4;
@@ -574,11 +577,11 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             const int64_t src = pass == 0 ? L::oS : L::odS;
             for (int i0 = 0; i0 < DV; i0 += QR) {
                 __syncthreads();
-                for (int e = tid; e < QR * DK; e += kBT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
+                for (int e = tid; e < QR * DK; e += kGT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
                 __syncthreads();
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const int t = w + 4 * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                    const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                     auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; };
                     if (pass == 0) {
                         aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const int t = w + 4 * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int r = ti(r0, q), c = tj(c0);
@@ -621,28 +624,28 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         sCol[DK + tid] = acc;
     }
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
-    for (int e = tid; e < kBC * DK; e += kBT) {   // dW -> R0, X -> R1
+    for (int e = tid; e < kBC * DK; e += kGT) {   // dW -> R0, X -> R1
         const int r = e / DK, c = e % DK;
         R0[r * LD + c] = R[L::odW + e];
         R1[r * LD + c] = sBeta[r] * R[L::oKh + e];
     }
     __syncthreads();
-    f32x4 adt[TCC / 4];
+    f32x4 adt[TCC / kGW];
 #pragma unroll
-    for (int m = 0; m < TCC / 4; ++m) {
-        const int t = w + 4 * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+    for (int m = 0; m < TCC / kGW; ++m) {
+        const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         adt[m] = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
                          [&](int c, int j) { return R1[j * LD + c]; });
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // Y -> R1
+    for (int e = tid; e < kBC * DV; e += kGT) {   // Y -> R1
         const int r = e / DV, i = e % DV;
         R1[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tix(r) * DV + i) : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < TCC / 4; ++m) {
-        const int t = w + 4 * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+    for (int m = 0; m < TCC / kGW; ++m) {
+        const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         adt[m] = mm_tile(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
                          [&](int i, int j) { return R1[j * LD + i]; });
 #pragma unroll
@@ -652,9 +655,9 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     // dA = -T^T dT T^T (strictly lower); T -> R1[0 .. C*CP), tmp -> R1[C*CP ..)
     float* sT = R1;
     float* sTmp = R1 + kBC * CP;
-    for (int e = tid; e < kBC * kBC; e += kBT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    for (int e = tid; e < kBC * kBC; e += kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
     __syncthreads();
-    for (int t = w; t < TCC; t += 4) {            // tmp = dT T^T
+    for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
                                   [&](int m, int j) { return sT[j * CP + m]; });
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
     }
     __syncthreads();
-    for (int t = w; t < TCC; t += 4) {            // dA = -T^T tmp, masked
+    for (int t = w; t < TCC; t += kGW) {            // dA = -T^T tmp, masked
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int j) { return sTmp[m * CP + j]; });
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             sM2[r * CP + j] = j < r ? -acc[q] : 0.f;
         }
     }
-    for (int t = w; t < TCD; t += 4) {            // dX = T^T dW (dKhat = beta dX)
+    for (int t = w; t < TCD; t += kGW) {            // dX = T^T dW (dKhat = beta dX)
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
         const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int c) { return R0[m * LD + c]; });
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
     }
     __syncthreads();
-    for (int t = w; t < TCV; t += 4) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
+    for (int t = w; t < TCV; t += kGW) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
         const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int i) { return R2[m * LD + i]; });
@@ -692,24 +695,24 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    {   // dbeta: 4 threads per row, fixed-order sums
-        const int r = tid / 4, qt = tid % 4;
+    {   // dbeta: kRT threads per row, fixed-order sums
+        const int r = tid / kRT, qt = tid % kRT;
         float db = 0.f;
-        for (int c = qt * (DK / 4); c < (qt + 1) * (DK / 4); ++c)
+        for (int c = qt * (DK / kRT); c < (qt + 1) * (DK / kRT); ++c)
             db = fmaf(R[L::odX + r * DK + c], R[L::oKh + r * DK + c], db);
         if (r < Cn)
-            for (int i = qt * (DV / 4); i < (qt + 1) * (DV / 4); ++i)
+            for (int i = qt * (DV / kRT); i < (qt + 1) * (DV / kRT); ++i)
                 db = fmaf(R0[r * LD + i], load_elem<E>(p.v, tix(r) * DV + i), db);
-        for (int j = qt * (kBC / 4); j < (qt + 1) * (kBC / 4); ++j)
+        for (int j = qt * (kBC / kRT); j < (qt + 1) * (kBC / kRT); ++j)
             db = fmaf(sM2[r * CP + j], R[L::oAb + r * kBC + j], db);
-        db += __shfl_xor(db, 1);
-        db += __shfl_xor(db, 2);
+#pragma unroll
+        for (int m = 1; m < kRT; m <<= 1) db += __shfl_xor(db, m);
         if (qt == 0 && r < Cn) store_elem<E>(p.gbeta, tix(r), db);
     }
     __syncthreads();
     // q, k, G -> R0, R1, R2; dAbar = beta dA
-    for (int e = tid; e < kBC * kBC; e += kBT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];
-    for (int e = tid; e < kBC * DK; e += kBT) {
+    for (int e = tid; e < kBC * kBC; e += kGT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];
+    for (int e = tid; e < kBC * DK; e += kGT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         R0[r * LD + c] = ok ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
@@ -736,7 +739,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                          - dKb * kr * ebar;
     };
     if constexpr (VAR == 2) {
-        for (int e = tid; e < kBC * DK; e += kBT) {
+        for (int e = tid; e < kBC * DK; e += kGT) {
             const int r = e / DK, c = e % DK;
             const float Gr = R2[r * LD + c];
             float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         // the decay factor is one number per (r, j): fold it into dMq and dAbar and
         // take the four sums as products
         if constexpr (VAR == 1) {
-            for (int e = tid; e < kBC * kBC; e += kBT) {
+            for (int e = tid; e < kBC * kBC; e += kGT) {
                 const int r = e / kBC, j = e % kBC;
                 if (j <= r) {
                     const float ex = __expf(R2[r * LD] - R2[j * LD]);
@@ -769,7 +772,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             }
             __syncthreads();
         }
-        for (int t = w; t < TCD; t += 4) {
+        for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
             const f32x4 a1 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
@@ -803,11 +806,11 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
         if constexpr (VAR == 1) {   // scalar decay: sum over channels, 4 threads per row
             __syncthreads();
-            const int r = tid / 4, qt = tid % 4;
+            const int r = tid / kRT, qt = tid % kRT;
             float s = 0.f;
-            for (int c = qt * (DK / 4); c < (qt + 1) * (DK / 4); ++c) s += R[L::odQh + r * DK + c];
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
+            for (int c = qt * (DK / kRT); c < (qt + 1) * (DK / kRT); ++c) s += R[L::odQh + r * DK + c];
+#pragma unroll
+            for (int m = 1; m < kRT; m <<= 1) s += __shfl_xor(s, m);
             if (qt == 0 && r < Cn) store_elem<E>(p.gg, tix(r), s);
         }
     }
@@ -1260,7 +1263,7 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const dim3 blk(kBT);
     const unsigned chains = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (DV / kBVT);
-    hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), blk, 0, s, a, ws, N);
+    hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
     if (e == hipSuccess) {
         hipLaunchKernelGGL((bwd_fchain_kernel<L, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
@@ -1271,7 +1274,7 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_grads_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_grads_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
         e = hipGetLastError();
     }
     const hipError_t f = hipFreeAsync(ws, s);
