@@ -54,6 +54,12 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
     return acc;
 }
 
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its global loads (the chains keep next-chunk loads in flight across it).
+__device__ __forceinline__ void lds_only_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // T = (I + diag(rs) A)^-1 for a strictly lower C x C matrix A (row stride lda;
 // rs = nullptr means no row scale).  Called by the 64 lanes of one wave, lane col
 // computing column col by forward substitution with the column held in registers
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
                 sXt[r * (kBVT + 1) + i] = x;
             }
         }
-        __syncthreads();
+        lds_only_barrier();
         if (n + 1 < N) fetch(n + 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
                 R[L::oVt + r * DV + i0 + i] = val;
             }
         }
-        __syncthreads();
+        lds_only_barrier();
         for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // S = S Diag(gamma) + ...
             const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
                 sS[i * (DK + 1) + c] = fmaf(sS[i * (DK + 1) + c], sGam[c], acc[q]);
             }
         }
-        __syncthreads();
+        lds_only_barrier();
     }
 }
 
@@ -456,7 +462,7 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             sdO[(e / kBVT) * (kBVT + 1) + e % kBVT] = pO[j];
         }
         if (tid < DK) sGam[tid] = pG;
-        __syncthreads();
+        lds_only_barrier();
         if (n > 0) fetch(n - 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
                 R[L::odVt + r * DV + i0 + i] = val;
             }
         }
-        __syncthreads();
+        lds_only_barrier();
         for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // dS = dS Diag(gamma) + dO^T Qhat -/+ dVt^T W
             const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
             f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, ii0, cc0, 0, kBC,
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
                 sdS[i * (DK + 1) + c] = fmaf(sdS[i * (DK + 1) + c], sGam[c], acc[q]);
             }
         }
-        __syncthreads();
+        lds_only_barrier();
     }
     if (p.gS0) {
         for (int e = tid; e < kBVT * DK; e += kBT) {
