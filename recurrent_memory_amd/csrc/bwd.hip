@@ -824,7 +824,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 
 // --------------------------------------------- split gates: 1. factors
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs2<DK, DV> L;
     constexpr int LD = (DK > DV ? DK : DV) + 1;
     constexpr int CP = kBC + 1;
@@ -834,13 +834,14 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     __shared__ float sR1[RS];
     __shared__ float sR2[RS];
     __shared__ float sM[kBC * CP];
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
 
-    for (int e = tid; e < kBC * DK; e += kBT) {   // k, b k, g
+    for (int e = tid; e < kBC * DK; e += kGT) {   // k, b k, g
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const float kk = ok ? load_elem<E>(p.k, tix(r) * DK + c) : 0.f;
@@ -857,9 +858,9 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kBT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
+    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // Ae -> sM, Ak -> workspace (strictly lower)
+    for (int e = tid; e < kBC * kBC; e += kGT) {  // Ae -> sM, Ak -> workspace (strictly lower)
         const int r = e / kBC, j = e % kBC;
         float ae = 0.f, ak = 0.f;
         if (j < r) {
@@ -877,8 +878,8 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     float* sT = sR2;
     if (tid < kBC) unit_lower_inverse(sM, CP, nullptr, sT, CP, tid);   // T = (I + Ae)^-1
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
-    for (int e = tid; e < kBC * DK; e += kBT) {   // Ebar, Kbar, Khat; Khat -> sR1
+    for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
+    for (int e = tid; e < kBC * DK; e += kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
         const int r = e / DK, c = e % DK;
         const float G = sG[r * (DK + 1) + c];
         const float eg = __expf(G), eb = __expf(sG[(kBC - 1) * (DK + 1) + c] - G);
@@ -889,36 +890,39 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         sR1[r * LD + c] = kk * eg;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kBT) {   // W = T Khat
-        const int r = e / DK, c = e % DK;
-        float acc = 0.f;
-        for (int j = 0; j <= r; ++j) acc = fmaf(sT[r * CP + j], sR1[j * LD + c], acc);
-        R[L::oW + e] = acc;
+    for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T Khat
+        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
+                                  [&](int j, int c) { return sR1[j * LD + c]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // X = w v -> sR1
+    for (int e = tid; e < kBC * DV; e += kGT) {   // X = w v -> sR1
         const int r = e / DV, i = e % DV;
         float x = 0.f;
         if (r < Cn) x = load_elem<E>(p.wgate, tix(r) * DV + i) * load_elem<E>(p.v, tix(r) * DV + i);
         sR1[r * LD + i] = x;
     }
-    for (int e = tid; e < kBC * kBC; e += kBT) sM[(e / kBC) * CP + e % kBC] = R[L::oAk + e];
+    for (int e = tid; e < kBC * kBC; e += kGT) sM[(e / kBC) * CP + e % kBC] = R[L::oAk + e];
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // Z = Ak X
-        const int r = e / DV, i = e % DV;
-        float acc = 0.f;
-        for (int j = 0; j < r; ++j) acc = fmaf(sM[r * CP + j], sR1[j * LD + i], acc);
-        R[L::oZ + e] = acc;
+    for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Z = Ak X
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM[r * CP + j]; },
+                                  [&](int j, int i) { return sR1[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oZ + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // Ut = T Z
-        const int r = e / DV, i = e % DV;
-        float acc = 0.f;
-        for (int j = 0; j <= r; ++j) acc = fmaf(sT[r * CP + j], R[L::oZ + j * DV + i], acc);
-        R[L::oU + e] = acc;
+    for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Ut = T Z
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
+                                  [&](int j, int i) { return R[L::oZ + j * DV + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kBT) {   // q -> sR1, b k -> sR2, Qhat
+    for (int e = tid; e < kBC * DK; e += kGT) {   // q -> sR1, b k -> sR2, Qhat
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const float qq = ok ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
@@ -927,7 +931,7 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         R[L::oQh + e] = qq * __expf(sG[r * (DK + 1) + c]);
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // Me, Mk (lower, diagonal included)
+    for (int e = tid; e < kBC * kBC; e += kGT) {  // Me, Mk (lower, diagonal included)
         const int r = e / kBC, j = e % kBC;
         float me = 0.f, mk = 0.f;
         if (j <= r) {
@@ -944,159 +948,239 @@ __global__ __launch_bounds__(kBT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
 
 // ------------------------------------------ split gates: 4. gradients
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs2<DK, DV> L;
     constexpr int CP = kBC + 1;
     constexpr int LD = (DK > DV ? DK : DV) + 1;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
-    constexpr int NE = kBC * DK / kBT;   // (r, c) entries per thread
+    constexpr int NE = kBC * DK / kGT;   // (r, c) entries per thread in the pairwise passes
+    constexpr int QR = 32;
+    constexpr int TPC = kGT / DK;
+    constexpr int TCD = (kBC / 16) * (DK / 16);
+    constexpr int TCV = (kBC / 16) * (DV / 16);
+    constexpr int TCC = (kBC / 16) * (kBC / 16);
+    constexpr int MT = TCD / kGW;
     __shared__ float sM1[kBC * CP];
     __shared__ float sM2[kBC * CP];
     __shared__ float sR[3 * RS];
-    __shared__ float sCol[5 * DK];
+    __shared__ float sCol[2 * DK];
+    __shared__ float sPart[kGT];
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
+    auto tj = [&](int j0) { return j0 + (l & 15); };
     auto xval = [&](int r, int i) {   // X = w v (zero past the sequence)
         if (r >= Cn) return 0.f;
         const int64_t vi = tix(r) * DV + i;
         return load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
     };
+    // stage rows [i0, i0 + QR) of a [DV][DK] workspace matrix into sM2
+    auto stage_rows = [&](int64_t src, int i0) {
+        for (int e = tid; e < QR * DK; e += kGT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
+    };
 
-    for (int e = tid; e < kBC * DV; e += kBT) {   // dO -> R0, Y -> R1, X -> R2
+    for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Y -> R1, X -> R2
         const int r = e / DV, i = e % DV;
         R0[r * LD + i] = r < Cn ? load_elem<E>(p.dO, tix(r) * DV + i) : 0.f;
         R1[r * LD + i] = R[L::oVt + e];
         R2[r * LD + i] = xval(r, i);
     }
-    __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // dMe = -Tril0(dO Y^T), dMk = Tril0(dO X^T)
-        const int r = e / kBC, j = e % kBC;
-        float me = 0.f, mk = 0.f;
-        if (j <= r) {
-            for (int i = 0; i < DV; ++i) {
-                me = fmaf(-R0[r * LD + i], R1[j * LD + i], me);
-                mk = fmaf(R0[r * LD + i], R2[j * LD + i], mk);
-            }
-        }
-        R[L::odMe + e] = me;
-        R[L::odMk + e] = mk;
-    }
-    constexpr int TPC = kBT / DK;
-    constexpr int NR = kBC / TPC;
-    const int cc = tid % DK, rq = tid / DK;
-    {   // dQhat = dO S, dEbar = -Y dS', dKbar = X dS'; column terms of the last row
-        float aq[NR], ae[NR], ak[NR];
-#pragma unroll
-        for (int m = 0; m < NR; ++m) aq[m] = ae[m] = ak[m] = 0.f;
-        float sds = 0.f;
-        for (int i = 0; i < DV; ++i) {
-            const float s_ = R[L::oS + i * DK + cc];
-            const float ds = R[L::odS + i * DK + cc];
-            sds = fmaf(s_, ds, sds);
-#pragma unroll
-            for (int m = 0; m < NR; ++m) {
-                const int r = rq + TPC * m;
-                aq[m] = fmaf(R0[r * LD + i], s_, aq[m]);
-                ae[m] = fmaf(-R1[r * LD + i], ds, ae[m]);
-                ak[m] = fmaf(R2[r * LD + i], ds, ak[m]);
-            }
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int m = 0; m < NR; ++m) {
-            const int r = rq + TPC * m;
-            R[L::odQh + r * DK + cc] = aq[m];
-            R[L::odEb + r * DK + cc] = ae[m];
-            R[L::odKb + r * DK + cc] = ak[m];
-            part = fmaf(ak[m], R[L::oKb + r * DK + cc], part);
-            part = fmaf(ae[m], R[L::oEb + r * DK + cc], part);
-        }
-        if (rq == 0) sCol[cc] = R[L::oGam + cc] * sds;
-        sCol[DK * (1 + rq) + cc] = part;
+    {   // sum_i S dS' per column
+        const int c = tid % DK, part = tid / DK;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
+            acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
+        sPart[tid] = acc;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) R0[(e / DV) * LD + e % DV] = R[L::odVt + e];   // dY -> R0
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
+        sCol[tid] = R[L::oGam + tid] * acc;
+    }
+    for (int t = w; t < TCC; t += kGW) {          // dMe = -Tril0(dO Y^T), dMk = Tril0(dO X^T)
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 me = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+                                 [&](int i, int j) { return R1[j * LD + i]; });
+        const f32x4 mk = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+                                 [&](int i, int j) { return R2[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), j = tj(j0);
+            R[L::odMe + r * kBC + j] = j <= r ? -me[q] : 0.f;
+            R[L::odMk + r * kBC + j] = j <= r ? mk[q] : 0.f;
+        }
+    }
+    {   // dQhat = dO S; then dEbar = -Y dS', dKbar = X dS'
+        f32x4 a1[MT], a2[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a1[m] = a2[m] = z4;
+        for (int i0 = 0; i0 < DV; i0 += QR) {
+            __syncthreads();
+            stage_rows(L::oS, i0);
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                                [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; });
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R[L::odQh + ti(r0, q) * DK + tj(c0)] = a1[m][q];
+            a1[m] = z4;
+        }
+        for (int i0 = 0; i0 < DV; i0 += QR) {
+            __syncthreads();
+            stage_rows(L::odS, i0);
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; };
+                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R1[r * LD + i]; }, Bs);
+                a2[m] = mm_tile(a2[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R2[r * LD + i]; }, Bs);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                R[L::odEb + ti(r0, q) * DK + tj(c0)] = a1[m][q];
+                R[L::odKb + ti(r0, q) * DK + tj(c0)] = a2[m][q];
+            }
+        }
+    }
     __syncthreads();
+    {   // sum_r (dKbar Kbar + dEbar Ebar) per column
+        const int c = tid % DK, part = tid / DK;
+        float acc = 0.f;
+        for (int r = part * (kBC / TPC); r < (part + 1) * (kBC / TPC); ++r) {
+            acc = fmaf(R[L::odKb + r * DK + c], R[L::oKb + r * DK + c], acc);
+            acc = fmaf(R[L::odEb + r * DK + c], R[L::oEb + r * DK + c], acc);
+        }
+        sPart[tid] = acc;
+    }
+    for (int e = tid; e < kBC * DV; e += kGT) R0[(e / DV) * LD + e % DV] = R[L::odVt + e];   // dY -> R0
+    __syncthreads();
+    if (tid < DK) {
+        float acc = 0.f;
+        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
+        sCol[DK + tid] = acc;
+    }
     {   // dW = dY S
-        float aw[NR];
+        f32x4 a1[MT];
 #pragma unroll
-        for (int m = 0; m < NR; ++m) aw[m] = 0.f;
-        for (int i = 0; i < DV; ++i) {
-            const float s_ = R[L::oS + i * DK + cc];
+        for (int m = 0; m < MT; ++m) a1[m] = z4;
+        for (int i0 = 0; i0 < DV; i0 += QR) {
+            __syncthreads();
+            stage_rows(L::oS, i0);
+            __syncthreads();
 #pragma unroll
-            for (int m = 0; m < NR; ++m) aw[m] = fmaf(R0[(rq + TPC * m) * LD + i], s_, aw[m]);
+            for (int m = 0; m < MT; ++m) {
+                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                                [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; });
+            }
         }
 #pragma unroll
-        for (int m = 0; m < NR; ++m) R[L::odW + (rq + TPC * m) * DK + cc] = aw[m];
+        for (int m = 0; m < MT; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R[L::odW + ti(r0, q) * DK + tj(c0)] = a1[m][q];
+        }
     }
     float* sT = R1;   // Y is no longer needed
-    for (int e = tid; e < kBC * kBC; e += kBT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    float* sTmp = R1 + kBC * CP;
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // dZ = T^T dY
-        const int r = e / DV, i = e % DV;
-        float acc = 0.f;
-        for (int m = r; m < kBC; ++m) acc = fmaf(sT[m * CP + r], R0[m * LD + i], acc);
-        R[L::odZ + e] = acc;
-    }
-    for (int e = tid; e < kBC * DK; e += kBT) {   // dKhat = T^T dW
-        const int r = e / DK, c = e % DK;
-        float acc = 0.f;
-        for (int m = r; m < kBC; ++m) acc = fmaf(sT[m * CP + r], R[L::odW + m * DK + c], acc);
-        R[L::odKh + e] = acc;
-    }
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // dT = dW Khat^T + dY Z^T
-        const int r = e / kBC, j = e % kBC;
-        float acc = 0.f;
-        for (int c = 0; c < DK; ++c) acc = fmaf(R[L::odW + r * DK + c], R[L::oKh + j * DK + c], acc);
-        for (int i = 0; i < DV; ++i) acc = fmaf(R0[r * LD + i], R[L::oZ + j * DV + i], acc);
-        sM1[r * CP + j] = acc;
-    }
+    for (int e = tid; e < kBC * kBC; e += kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // tmp = dT T^T
-        const int r = e / kBC, j = e % kBC;
-        float acc = 0.f;
-        for (int m = 0; m <= j; ++m) acc = fmaf(sM1[r * CP + m], sT[j * CP + m], acc);
-        sM2[r * CP + j] = acc;
+    for (int t = w; t < TCV; t += kGW) {          // dZ = T^T dY
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                  [&](int m, int i) { return R0[m * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::odZ + ti(r0, q) * DV + tj(c0)] = acc[q];
     }
-    __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kBT) {  // dAe = -T^T tmp; dAk = StrictTril(dZ X^T)
-        const int r = e / kBC, j = e % kBC;
-        float dae = 0.f, dak = 0.f;
-        if (j < r) {
-            for (int m = r; m < kBC; ++m) dae = fmaf(-sT[m * CP + r], sM2[m * CP + j], dae);
-            for (int i = 0; i < DV; ++i) dak = fmaf(R[L::odZ + r * DV + i], R2[j * LD + i], dak);
-        }
-        R[L::odAe + e] = dae;
-        R[L::odAk + e] = dak;
+    for (int t = w; t < TCD; t += kGW) {          // dKhat = T^T dW
+        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                  [&](int m, int c) { return R[L::odW + m * DK + c]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::odKh + ti(r0, q) * DK + tj(c0)] = acc[q];
+    }
+    for (int t = w; t < TCC; t += kGW) {          // dT = dW Khat^T + dY Z^T
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        f32x4 acc = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return R[L::odW + r * DK + c]; },
+                            [&](int c, int j) { return R[L::oKh + j * DK + c]; });
+        acc = mm_tile(acc, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+                      [&](int i, int j) { return R[L::oZ + j * DV + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sM1[ti(r0, q) * CP + tj(j0)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) R0[(e / DV) * LD + e % DV] = (e / DV) < Cn ? load_elem<E>(p.dO, tix(e / DV) * DV + e % DV) : 0.f;
+    for (int t = w; t < TCC; t += kGW) {          // tmp = dT T^T
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM1[r * CP + m]; },
+                                  [&](int m, int j) { return sT[j * CP + m]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
+    }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kBT) {   // dX = Mk^T dO + Kbar dS'^T + Ak^T dZ -> dv, dw
-        const int r = e / DV, i = e % DV;
-        float acc = 0.f;
-        for (int m = r; m < kBC; ++m) acc = fmaf(R[L::oMk + m * kBC + r], R0[m * LD + i], acc);
-        for (int c = 0; c < DK; ++c) acc = fmaf(R[L::oKb + r * DK + c], R[L::odS + i * DK + c], acc);
-        for (int m = r + 1; m < kBC; ++m) acc = fmaf(R[L::oAk + m * kBC + r], R[L::odZ + m * DV + i], acc);
-        if (r < Cn) {
-            const int64_t vi = tix(r) * DV + i;
-            store_elem<E>(p.gv, vi, load_elem<E>(p.wgate, vi) * acc);
-            store_elem<E>(p.gw, vi, load_elem<E>(p.v, vi) * acc);
+    for (int t = w; t < TCC; t += kGW) {          // dAe = -T^T tmp, dAk = StrictTril(dZ X^T)
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const f32x4 ae = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                 [&](int m, int j) { return sTmp[m * CP + j]; });
+        const f32x4 ak = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R[L::odZ + r * DV + i]; },
+                                 [&](int i, int j) { return R2[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), j = tj(j0);
+            R[L::odAe + r * kBC + j] = j < r ? -ae[q] : 0.f;
+            R[L::odAk + r * kBC + j] = j < r ? ak[q] : 0.f;
         }
     }
     __syncthreads();
-    // pairwise passes; thread entries e = tid + kBT m: (r, c) = (e / DK, e % DK)
+    for (int e = tid; e < kBC * DV; e += kGT)
+        R0[(e / DV) * LD + e % DV] = (e / DV) < Cn ? load_elem<E>(p.dO, tix(e / DV) * DV + e % DV) : 0.f;
+    __syncthreads();
+    for (int t = w; t < TCV; t += kGW) {          // dX = Mk^T dO + Kbar dS'^T + Ak^T dZ -> dv, dw
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return R[L::oMk + m * kBC + r]; },
+                            [&](int m, int i) { return R0[m * LD + i]; });
+        acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return R[L::oKb + r * DK + c]; },
+                      [&](int c, int i) { return R[L::odS + i * DK + c]; });
+        acc = mm_tile(acc, r0, c0, 0, kBC, [&](int r, int m) { return R[L::oAk + m * kBC + r]; },
+                      [&](int m, int i) { return R[L::odZ + m * DV + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), i = tj(c0);
+            if (r < Cn) {
+                const int64_t vi = tix(r) * DV + i;
+                store_elem<E>(p.gv, vi, load_elem<E>(p.wgate, vi) * acc[q]);
+                store_elem<E>(p.gw, vi, load_elem<E>(p.v, vi) * acc[q]);
+            }
+        }
+    }
+    __syncthreads();
+    // pairwise passes; thread entries e = tid + kGT m: (r, c) = (e / DK, e % DK)
     float aq[NE], ak[NE], abk[NE], ag[NE];
 #pragma unroll
     for (int m = 0; m < NE; ++m) aq[m] = ak[m] = abk[m] = ag[m] = 0.f;
     auto stage = [&](float* dst, int what) {   // 0 q, 1 k, 2 b k, 3 G
-        for (int e = tid; e < kBC * DK; e += kBT) {
+        for (int e = tid; e < kBC * DK; e += kGT) {
             const int r = e / DK, c = e % DK;
             float x;
             if (what == 3) {
@@ -1113,7 +1197,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
     };
     // pass 1: Me (q, b k) and Mk (q, k) with G
-    for (int e = tid; e < kBC * kBC; e += kBT) {
+    for (int e = tid; e < kBC * kBC; e += kGT) {
         sM1[(e / kBC) * CP + e % kBC] = R[L::odMe + e];
         sM2[(e / kBC) * CP + e % kBC] = R[L::odMk + e];
     }
@@ -1123,7 +1207,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NE; ++m) {   // Me terms
-        const int e = tid + kBT * m, r = e / DK, c = e % DK;
+        const int e = tid + kGT * m, r = e / DK, c = e % DK;
         const float Gr = R2[r * LD + c];
         float row = 0.f, col = 0.f;
         for (int j = 0; j < kBC; ++j) {
@@ -1140,7 +1224,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NE; ++m) {   // Mk terms
-        const int e = tid + kBT * m, r = e / DK, c = e % DK;
+        const int e = tid + kGT * m, r = e / DK, c = e % DK;
         const float Gr = R2[r * LD + c];
         float row = 0.f, col = 0.f;
         for (int j = 0; j < kBC; ++j) {
@@ -1154,7 +1238,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     }
     __syncthreads();
     // pass 2: Ae (k, b k) and Ak (k, k); b k -> R0
-    for (int e = tid; e < kBC * kBC; e += kBT) {
+    for (int e = tid; e < kBC * kBC; e += kGT) {
         sM1[(e / kBC) * CP + e % kBC] = R[L::odAe + e];
         sM2[(e / kBC) * CP + e % kBC] = R[L::odAk + e];
     }
@@ -1162,7 +1246,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NE; ++m) {
-        const int e = tid + kBT * m, r = e / DK, c = e % DK;
+        const int e = tid + kGT * m, r = e / DK, c = e % DK;
         const float Gr = R2[r * LD + c];
         float rowe = 0.f, cole = 0.f, rowk = 0.f, colk = 0.f;
         for (int j = 0; j < kBC; ++j) {
@@ -1184,7 +1268,7 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     // row factors, outputs, dG
 #pragma unroll
     for (int m = 0; m < NE; ++m) {
-        const int e = tid + kBT * m, r = e / DK, c = e % DK;
+        const int e = tid + kGT * m, r = e / DK, c = e % DK;
         const float Gr = R2[r * LD + c];
         const float eg = __expf(Gr), eb = __expf(R2[(kBC - 1) * LD + c] - Gr);
         const float kr = R1[r * LD + c], bkr = R0[r * LD + c];
@@ -1206,10 +1290,13 @@ __global__ __launch_bounds__(kBT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
     if (tid < DK) {
         const int c = tid;
-        float acc = sCol[c];
-        for (int q2 = 0; q2 < TPC; ++q2) acc += sCol[DK * (1 + q2) + c];
+        float dgv[kBC];
+#pragma unroll
+        for (int r = 0; r < kBC; ++r) dgv[r] = R[L::odQh + r * DK + c];
+        float acc = sCol[c] + sCol[DK + c];
+#pragma unroll
         for (int r = kBC - 1; r >= 0; --r) {
-            acc += R[L::odQh + r * DK + c];
+            acc += dgv[r];
             if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, acc);
         }
     }
@@ -1229,7 +1316,7 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const dim3 blk(kBT);
     const unsigned chains = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (DV / kBVT);
-    hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), blk, 0, s, a, ws, N);
+    hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
     if (e == hipSuccess) {
         hipLaunchKernelGGL((bwd_fchain_kernel<L, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
@@ -1240,7 +1327,7 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd2_grads_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd2_grads_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
         e = hipGetLastError();
     }
     const hipError_t f = hipFreeAsync(ws, s);
