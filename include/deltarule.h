@@ -184,6 +184,10 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *          dtype (written): gradient of the log-decay g
  *   dS0    [B, H, d_v, d_k] fp32 (written), gradient of S0; NULL if not wanted
  *
+ * Channel-wise decays (DR_KDA, DR_GDN2) obey the same bound as in delta_fwd: the
+ * log-decay of a channel summed over any 16 consecutive tokens must stay above
+ * about -85 (pairwise factors are split at a reference row of each 16-token block).
+ *
  * Supported: every variant with H_k = H (0); grouped query/key heads return
  * DR_E_UNSUPPORTED.  Outputs must not overlap any input or one another.
  * Arithmetic is fp32 throughout.  Workspace: B * H * ceil(T / 64) records of

@@ -54,6 +54,35 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
     return acc;
 }
 
+// Pairwise sums with a per-channel factor, as products: for the 16 x 16 tile at
+// rows r0, channels c0,
+//   ROW:  sum_{j <= r} M(r, j) X(j, c) e^{G(r, c) - G(j, c)}
+//   !ROW: sum_{j >= r} M(j, r) X(j, c) e^{G(j, c) - G(r, c)}
+// (M is zero outside those ranges).  Each 16-row block J of j contributes one
+// product over its rows, with e^{...} split at a reference row of J: the last
+// row for ROW and the first for !ROW, so that the factor inside the product is
+// at most 1 and the one applied afterwards exceeds 1 only within block J (at most
+// e^{85} under the decay bound).
+template <bool ROW, class FM, class FX, class FG>
+__device__ __forceinline__ f32x4 pair_tile(int r0, int c0, const FM& M, const FX& X, const FG& G) {
+    const int l = threadIdx.x & 63;
+    const int I = r0 / 16;
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    for (int J = ROW ? 0 : I; ROW ? (J <= I) : (J < kBC / 16); ++J) {
+        const int ref = ROW ? 16 * J + 15 : 16 * J;
+        const f32x4 acc = mm_tile(
+            f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 16 * J, 16 * J + 16,
+            [&](int r, int j) { return ROW ? M(r, j) : M(j, r); },
+            [&](int j, int c) { return X(j, c) * __expf(ROW ? G(ref, c) - G(j, c) : G(j, c) - G(ref, c)); });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * (l >> 4) + q, c = c0 + (l & 15);
+            out[q] = fmaf(acc[q], __expf(ROW ? G(r, c) - G(ref, c) : G(ref, c) - G(r, c)), out[q]);
+        }
+    }
+    return out;
+}
+
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its global loads (the chains keep next-chunk loads in flight across it).
 __device__ __forceinline__ void lds_only_barrier() {
@@ -188,26 +217,29 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     // Abar (strictly lower) and Mq (lower, diagonal included)
     const int w = tid >> 6, l = tid & 63;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (VAR == 2) {   // a factor per channel: pairwise sums on the VALU
-        for (int e = tid; e < kBC * kBC; e += kGT) {
-            const int r = e / kBC, j = e % kBC;
-            float ab = 0.f, mq = 0.f;
-            if (j <= r) {
-                const float* kr = sK + r * (DK + 1);
-                const float* kj = sK + j * (DK + 1);
-                const float* qr = sX + r * LD;
-                const float* gr = sG + r * (DK + 1);
-                const float* gj = sG + j * (DK + 1);
-                for (int c = 0; c < DK; ++c) {
-                    const float wv = kj[c] * __expf(gr[c] - gj[c]);
-                    ab = fmaf(kr[c], wv, ab);
-                    mq = fmaf(qr[c], wv, mq);
-                }
-                if (j == r) ab = 0.f;
+    if constexpr (VAR == 2) {
+        // a factor per channel: e^{G_r - G_j} = e^{G_r - G_ref} e^{G_ref - G_j} with the
+        // reference at the last row of j's 16-row block, folded into the operands of
+        // each tile product (at most e^{85} inside one block under the decay bound)
+        for (int t = w; t < 16; t += kGW) {
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            f32x4 ab = z4, mq = z4;
+            if (j0 <= r0) {
+                const float* gref = sG + (j0 + 15) * (DK + 1);
+                auto Bk = [&](int c, int j) { return sK[j * (DK + 1) + c] * __expf(gref[c] - sG[j * (DK + 1) + c]); };
+                ab = mm_tile(z4, r0, j0, 0, DK,
+                             [&](int r, int c) { return sK[r * (DK + 1) + c] * __expf(sG[r * (DK + 1) + c] - gref[c]); }, Bk);
+                mq = mm_tile(z4, r0, j0, 0, DK,
+                             [&](int r, int c) { return sX[r * LD + c] * __expf(sG[r * (DK + 1) + c] - gref[c]); }, Bk);
             }
-            sA[r * (kBC + 1) + j] = ab;
-            R[L::oAb + e] = ab;
-            R[L::oMq + e] = mq;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
+                const float a_ = j < r ? ab[q] : 0.f;
+                sA[r * (kBC + 1) + j] = a_;
+                R[L::oAb + r * kBC + j] = a_;
+                R[L::oMq + r * kBC + j] = j <= r ? mq[q] : 0.f;
+            }
         }
     } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
         for (int t = w; t < 16; t += kGW) {
@@ -745,24 +777,19 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                          - dKb * kr * ebar;
     };
     if constexpr (VAR == 2) {
-        for (int e = tid; e < kBC * DK; e += kGT) {
-            const int r = e / DK, c = e % DK;
-            const float Gr = R2[r * LD + c];
-            float a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f;
-            for (int j = 0; j < kBC; ++j) {
-                const float Gj = R2[j * LD + c];
-                if (j <= r) {
-                    const float kj = R1[j * LD + c] * __expf(Gr - Gj);
-                    a1 = fmaf(sM1[r * CP + j], kj, a1);
-                    a3 = fmaf(sM2[r * CP + j], kj, a3);
-                }
-                if (j >= r) {
-                    const float ex = __expf(Gj - Gr);
-                    a2 = fmaf(sM1[j * CP + r], R0[j * LD + c] * ex, a2);
-                    a4 = fmaf(sM2[j * CP + r], R1[j * LD + c] * ex, a4);
-                }
-            }
-            finish(r, c, a1, a2, a3, a4);
+        auto Gf = [&](int r, int c) { return R2[r * LD + c]; };
+        auto M1 = [&](int r, int j) { return sM1[r * CP + j]; };
+        auto M2 = [&](int r, int j) { return sM2[r * CP + j]; };
+        auto Qf = [&](int j, int c) { return R0[j * LD + c]; };
+        auto Kf = [&](int j, int c) { return R1[j * LD + c]; };
+        for (int t = w; t < TCD; t += kGW) {
+            const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const f32x4 a1 = pair_tile<true>(r0, c0, M1, Kf, Gf);
+            const f32x4 a2 = pair_tile<false>(r0, c0, M1, Qf, Gf);
+            const f32x4 a3 = pair_tile<true>(r0, c0, M2, Kf, Gf);
+            const f32x4 a4 = pair_tile<false>(r0, c0, M2, Kf, Gf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q]);
         }
     } else {
         // the decay factor is one number per (r, j): fold it into dMq and dAbar and
@@ -860,19 +887,24 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
-    for (int e = tid; e < kBC * kBC; e += kGT) {  // Ae -> sM, Ak -> workspace (strictly lower)
-        const int r = e / kBC, j = e % kBC;
-        float ae = 0.f, ak = 0.f;
-        if (j < r) {
-            for (int c = 0; c < DK; ++c) {
-                const float ex = __expf(sG[r * (DK + 1) + c] - sG[j * (DK + 1) + c]);
-                const float kr = sK[r * (DK + 1) + c] * ex;
-                ae = fmaf(kr, sR1[j * LD + c], ae);
-                ak = fmaf(kr, sK[j * (DK + 1) + c], ak);
-            }
+    // pairwise factors with the reference at the last row of j's 16-row block
+    auto aexp = [&](int r, int c, const float* gref) { return __expf(sG[r * (DK + 1) + c] - gref[c]); };
+    auto bexp = [&](int j, int c, const float* gref) { return __expf(gref[c] - sG[j * (DK + 1) + c]); };
+    for (int t = w; t < 16; t += kGW) {           // Ae -> sM, Ak -> workspace (strictly lower)
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        f32x4 ae = z4, ak = z4;
+        if (j0 <= r0) {
+            const float* gref = sG + (j0 + 15) * (DK + 1);
+            auto Ak_ = [&](int r, int c) { return sK[r * (DK + 1) + c] * aexp(r, c, gref); };
+            ae = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sR1[j * LD + c] * bexp(j, c, gref); });
+            ak = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sK[j * (DK + 1) + c] * bexp(j, c, gref); });
         }
-        sM[r * CP + j] = ae;
-        R[L::oAk + e] = ak;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
+            sM[r * CP + j] = j < r ? ae[q] : 0.f;
+            R[L::oAk + r * kBC + j] = j < r ? ak[q] : 0.f;
+        }
     }
     __syncthreads();
     float* sT = sR2;
@@ -931,18 +963,21 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         R[L::oQh + e] = qq * __expf(sG[r * (DK + 1) + c]);
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kGT) {  // Me, Mk (lower, diagonal included)
-        const int r = e / kBC, j = e % kBC;
-        float me = 0.f, mk = 0.f;
-        if (j <= r) {
-            for (int c = 0; c < DK; ++c) {
-                const float qe = sR1[r * LD + c] * __expf(sG[r * (DK + 1) + c] - sG[j * (DK + 1) + c]);
-                me = fmaf(qe, sR2[j * LD + c], me);
-                mk = fmaf(qe, sK[j * (DK + 1) + c], mk);
-            }
+    for (int t = w; t < 16; t += kGW) {           // Me, Mk (lower, diagonal included)
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        f32x4 me = z4, mk = z4;
+        if (j0 <= r0) {
+            const float* gref = sG + (j0 + 15) * (DK + 1);
+            auto Aq = [&](int r, int c) { return sR1[r * LD + c] * aexp(r, c, gref); };
+            me = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sR2[j * LD + c] * bexp(j, c, gref); });
+            mk = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sK[j * (DK + 1) + c] * bexp(j, c, gref); });
         }
-        R[L::oMq + e] = me;
-        R[L::oMk + e] = mk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
+            R[L::oMq + r * kBC + j] = j <= r ? me[q] : 0.f;
+            R[L::oMk + r * kBC + j] = j <= r ? mk[q] : 0.f;
+        }
     }
 }
 
@@ -953,7 +988,6 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     constexpr int CP = kBC + 1;
     constexpr int LD = (DK > DV ? DK : DV) + 1;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
-    constexpr int NE = kBC * DK / kGT;   // (r, c) entries per thread in the pairwise passes
     constexpr int QR = 32;
     constexpr int TPC = kGT / DK;
     constexpr int TCD = (kBC / 16) * (DK / 16);
@@ -1175,10 +1209,10 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
     }
     __syncthreads();
-    // pairwise passes; thread entries e = tid + kGT m: (r, c) = (e / DK, e % DK)
-    float aq[NE], ak[NE], abk[NE], ag[NE];
+    // pairwise passes on 16 x 16 tiles of (r, c); accumulators per tile element
+    f32x4 aq[MT], ak[MT], abk[MT], ag[MT];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) aq[m] = ak[m] = abk[m] = ag[m] = 0.f;
+    for (int m = 0; m < MT; ++m) aq[m] = ak[m] = abk[m] = ag[m] = z4;
     auto stage = [&](float* dst, int what) {   // 0 q, 1 k, 2 b k, 3 G
         for (int e = tid; e < kBC * DK; e += kGT) {
             const int r = e / DK, c = e % DK;
@@ -1196,7 +1230,17 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             dst[r * LD + c] = x;
         }
     };
-    // pass 1: Me (q, b k) and Mk (q, k) with G
+    auto Gf = [&](int r, int c) { return R2[r * LD + c]; };
+    auto M1 = [&](int r, int j) { return sM1[r * CP + j]; };
+    auto M2 = [&](int r, int j) { return sM2[r * CP + j]; };
+    auto X0 = [&](int j, int c) { return R0[j * LD + c]; };
+    auto X1 = [&](int j, int c) { return R1[j * LD + c]; };
+    auto tile_of = [&](int m, int& r0, int& c0) {
+        const int t = w + kGW * m;
+        r0 = 16 * (t / (DK / 16));
+        c0 = 16 * (t % (DK / 16));
+    };
+    // pass 1: Me (q, b k) and Mk (q, k) with G; q -> R0, b k -> R1, G -> R2
     for (int e = tid; e < kBC * kBC; e += kGT) {
         sM1[(e / kBC) * CP + e % kBC] = R[L::odMe + e];
         sM2[(e / kBC) * CP + e % kBC] = R[L::odMk + e];
@@ -1206,35 +1250,35 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     stage(R1, 2);
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {   // Me terms
-        const int e = tid + kGT * m, r = e / DK, c = e % DK;
-        const float Gr = R2[r * LD + c];
-        float row = 0.f, col = 0.f;
-        for (int j = 0; j < kBC; ++j) {
-            const float ex = __expf(j <= r ? Gr - R2[j * LD + c] : R2[j * LD + c] - Gr);
-            if (j <= r) row = fmaf(sM1[r * CP + j], R1[j * LD + c] * ex, row);
-            if (j >= r) col = fmaf(sM1[j * CP + r], R0[j * LD + c] * ex, col);
+    for (int m = 0; m < MT; ++m) {   // Me terms
+        int r0, c0;
+        tile_of(m, r0, c0);
+        const f32x4 row = pair_tile<true>(r0, c0, M1, X1, Gf);
+        const f32x4 col = pair_tile<false>(r0, c0, M1, X0, Gf);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), c = tj(c0);
+            aq[m][q] += row[q];
+            abk[m][q] += col[q];
+            ag[m][q] += R0[r * LD + c] * row[q] - R1[r * LD + c] * col[q];
         }
-        aq[m] += row;
-        abk[m] += col;
-        ag[m] += R0[r * LD + c] * row - R1[r * LD + c] * col;
     }
     __syncthreads();
     stage(R1, 1);
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {   // Mk terms
-        const int e = tid + kGT * m, r = e / DK, c = e % DK;
-        const float Gr = R2[r * LD + c];
-        float row = 0.f, col = 0.f;
-        for (int j = 0; j < kBC; ++j) {
-            const float ex = __expf(j <= r ? Gr - R2[j * LD + c] : R2[j * LD + c] - Gr);
-            if (j <= r) row = fmaf(sM2[r * CP + j], R1[j * LD + c] * ex, row);
-            if (j >= r) col = fmaf(sM2[j * CP + r], R0[j * LD + c] * ex, col);
+    for (int m = 0; m < MT; ++m) {   // Mk terms; k -> R1
+        int r0, c0;
+        tile_of(m, r0, c0);
+        const f32x4 row = pair_tile<true>(r0, c0, M2, X1, Gf);
+        const f32x4 col = pair_tile<false>(r0, c0, M2, X0, Gf);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), c = tj(c0);
+            aq[m][q] += row[q];
+            ak[m][q] += col[q];
+            ag[m][q] += R0[r * LD + c] * row[q] - R1[r * LD + c] * col[q];
         }
-        aq[m] += row;
-        ak[m] += col;
-        ag[m] += R0[r * LD + c] * row - R1[r * LD + c] * col;
     }
     __syncthreads();
     // pass 2: Ae (k, b k) and Ak (k, k); b k -> R0
@@ -1245,47 +1289,48 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     stage(R0, 2);
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + kGT * m, r = e / DK, c = e % DK;
-        const float Gr = R2[r * LD + c];
-        float rowe = 0.f, cole = 0.f, rowk = 0.f, colk = 0.f;
-        for (int j = 0; j < kBC; ++j) {
-            if (j == r) continue;
-            const float ex = __expf(j < r ? Gr - R2[j * LD + c] : R2[j * LD + c] - Gr);
-            if (j < r) {
-                rowe = fmaf(sM1[r * CP + j], R0[j * LD + c] * ex, rowe);
-                rowk = fmaf(sM2[r * CP + j], R1[j * LD + c] * ex, rowk);
-            } else {
-                cole = fmaf(sM1[j * CP + r], R1[j * LD + c] * ex, cole);
-                colk = fmaf(sM2[j * CP + r], R1[j * LD + c] * ex, colk);
-            }
+    for (int m = 0; m < MT; ++m) {
+        int r0, c0;
+        tile_of(m, r0, c0);
+        const f32x4 rowe = pair_tile<true>(r0, c0, M1, X0, Gf);
+        const f32x4 cole = pair_tile<false>(r0, c0, M1, X1, Gf);
+        const f32x4 rowk = pair_tile<true>(r0, c0, M2, X1, Gf);
+        const f32x4 colk = pair_tile<false>(r0, c0, M2, X1, Gf);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), c = tj(c0);
+            const float kr = R1[r * LD + c], bkr = R0[r * LD + c];
+            ak[m][q] += rowe[q] + rowk[q] + colk[q];
+            abk[m][q] += cole[q];
+            ag[m][q] += kr * rowe[q] - bkr * cole[q] + kr * rowk[q] - kr * colk[q];
         }
-        const float kr = R1[r * LD + c], bkr = R0[r * LD + c];
-        ak[m] += rowe + rowk + colk;
-        abk[m] += cole;
-        ag[m] += kr * rowe - bkr * cole + kr * rowk - kr * colk;
     }
     // row factors, outputs, dG
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-        const int e = tid + kGT * m, r = e / DK, c = e % DK;
-        const float Gr = R2[r * LD + c];
-        const float eg = __expf(Gr), eb = __expf(R2[(kBC - 1) * LD + c] - Gr);
-        const float kr = R1[r * LD + c], bkr = R0[r * LD + c];
-        const float dQh = R[L::odQh + e], dKh = R[L::odKh + e];
-        const float dKb = R[L::odKb + e], dEb = R[L::odEb + e];
-        const float q_ = aq[m] + dQh * eg;
-        const float kpart = ak[m] + dKh * eg + dKb * eb;
-        const float dbk = abk[m] + dEb * eb;
-        const float qr = r < Cn ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
-        ag[m] += dKh * kr * eg + dQh * qr * eg - dKb * kr * eb - dEb * bkr * eb;
-        if (r < Cn) {
-            const float br = load_elem<E>(p.beta, tix(r) * DK + c);
-            store_elem<E>(p.gq, tix(r) * DK + c, q_);
-            store_elem<E>(p.gk, tix(r) * DK + c, kpart + dbk * br);
-            store_elem<E>(p.gbeta, tix(r) * DK + c, dbk * kr);
+    for (int m = 0; m < MT; ++m) {
+        int r0, c0;
+        tile_of(m, r0, c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = ti(r0, q), c = tj(c0), e = r * DK + c;
+            const float Gr = R2[r * LD + c];
+            const float eg = __expf(Gr), eb = __expf(R2[(kBC - 1) * LD + c] - Gr);
+            const float kr = R1[r * LD + c], bkr = R0[r * LD + c];
+            const float dQh = R[L::odQh + e], dKh = R[L::odKh + e];
+            const float dKb = R[L::odKb + e], dEb = R[L::odEb + e];
+            const float q_ = aq[m][q] + dQh * eg;
+            const float kpart = ak[m][q] + dKh * eg + dKb * eb;
+            const float dbk = abk[m][q] + dEb * eb;
+            const float qr = r < Cn ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
+            const float dg = ag[m][q] + dKh * kr * eg + dQh * qr * eg - dKb * kr * eb - dEb * bkr * eb;
+            if (r < Cn) {
+                const float br = load_elem<E>(p.beta, tix(r) * DK + c);
+                store_elem<E>(p.gq, tix(r) * DK + c, q_);
+                store_elem<E>(p.gk, tix(r) * DK + c, kpart + dbk * br);
+                store_elem<E>(p.gbeta, tix(r) * DK + c, dbk * kr);
+            }
+            R[L::odQh + e] = dg;
         }
-        R[L::odQh + e] = ag[m];
     }
     __syncthreads();
     if (tid < DK) {

@@ -109,3 +109,17 @@ def test_bwd_deterministic():
     b = _run("kda", "bf16", w, x, dO, dST)
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_strong_channel_gates(variant, dtype):
+    """Log-decays scaled by 3 (16-token sums near -35): the block-reference factors
+    of the pairwise sums then reach e^{35} inside a block."""
+    announce("bwd_strong_gates", variant, dtype)
+    w = Workload("t", variant, dtype, B=1, H=2, T=200, dk=128, dv=128, random_s0=True, seed=46)
+    x = make_forward_inputs(w, gate_scale=3.0)
+    dO, dST = _upstream(w, 13)
+    gr = _run(variant, dtype, w, x, dO, dST)
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
+    _check(variant, dtype, gr, ref)
