@@ -177,7 +177,7 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd
  *   dO     [B, T, H, d_v] dtype: gradient arriving at o
  *   dS_T   [B, H, d_v, d_k] fp32: gradient arriving at the final state; NULL = 0
- *   dq, dk [B, T, H, d_k], dv [B, T, H, d_v]                       dtype (written)
+ *   dq, dk [B, T, H_k, d_k], dv [B, T, H, d_v]                     dtype (written)
  *   dbeta  [B, T, H]; DR_GDN2: gradient of the erase gate [B, T, H, d_k]   dtype (written)
  *   dwgate DR_GDN2: gradient of the write gate [B, T, H, d_v]; otherwise must be NULL
  *   dg     DR_DELTANET: must be NULL; DR_GDN [B, T, H]; DR_KDA/DR_GDN2 [B, T, H, d_k]
@@ -188,8 +188,9 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * log-decay of a channel summed over any 16 consecutive tokens must stay above
  * about -85 (pairwise factors are split at a reference row of each 16-token block).
  *
- * Supported: every variant with H_k = H (0); grouped query/key heads return
- * DR_E_UNSUPPORTED.  Outputs must not overlap any input or one another.
+ * Grouped query/key heads (H_k < H): q, k, dq and dk are [B, T, H_k, d_k]; dq and
+ * dk are summed over each group of value heads, through two extra fp32 buffers of
+ * [B, T, H, d_k] from the pool.  Outputs must not overlap any input or one another.
  * Arithmetic is fp32 throughout.  Workspace: B * H * ceil(T / 64) records of
  * 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB for d_k/d_v = 128/64,
  * 64/128, 64/64), for DR_GDN2 768.5 KiB (640.5, 464.5, 384.25), from the same

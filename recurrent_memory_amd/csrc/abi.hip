@@ -213,7 +213,6 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
         if (st != DR_OK) return st;
-        if (sz.Hk != desc->H) return DR_E_UNSUPPORTED;
         if (q == nullptr || k == nullptr || v == nullptr || dO == nullptr || dq == nullptr ||
             dk == nullptr || dv == nullptr || dbeta == nullptr)
             return DR_E_NULLPTR;
@@ -244,7 +243,7 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
         st = check_device();
         if (st != DR_OK) return st;
         dr::BwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, g, S0, dO,
-                      dS_T, dq, dk, dv, dbeta, dg, dS0, wgate, dwgate};
+                      dS_T, dq, dk, dv, dbeta, dg, dS0, wgate, dwgate, sz.Hk, nullptr, nullptr};
         const hipError_t e = dr::launch_bwd(desc->variant, desc->dtype, a,
                                             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;

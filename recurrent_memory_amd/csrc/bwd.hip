@@ -174,6 +174,17 @@ struct BwdWs2 {
 __device__ __forceinline__ int64_t tok_index(const BwdArgs& p, int b, int t, int h) {
     return (static_cast<int64_t>(b) * p.T + t) * p.H + h;
 }
+// the query/key row of value head h (groups of H / Hk consecutive value heads)
+__device__ __forceinline__ int64_t qk_index(const BwdArgs& p, int b, int t, int h) {
+    return (static_cast<int64_t>(b) * p.T + t) * p.Hk + h / (p.H / p.Hk);
+}
+// dq or dk of value head h at token index vi ([B, T, H] order): straight to the
+// output, or to the fp32 per-value-head buffer that is summed over groups later
+template <typename E>
+__device__ __forceinline__ void store_qk_grad(void* out, float* out32, int64_t vi, int DK, int c, float x) {
+    if (out32) out32[vi * DK + c] = x;
+    else store_elem<E>(out, vi * DK + c, x);
+}
 
 // ---------------------------------------------------------------- 1. factors
 template <int VAR, typename E, int DK, int DV>
@@ -195,8 +206,9 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const int64_t ti = tok_index(p, b, t0 + min(r, Cn - 1), h);
-        sK[r * (DK + 1) + c] = ok ? load_elem<E>(p.k, ti * DK + c) : 0.f;
-        sX[r * LD + c] = ok ? load_elem<E>(p.q, ti * DK + c) : 0.f;
+        const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h);
+        sK[r * (DK + 1) + c] = ok ? load_elem<E>(p.k, qi * DK + c) : 0.f;
+        sX[r * LD + c] = ok ? load_elem<E>(p.q, qi * DK + c) : 0.f;
         float gv = 0.f;
         if constexpr (VAR == 1) gv = ok ? load_elem<E>(p.g, ti) : 0.f;
         if constexpr (VAR == 2) gv = ok ? load_elem<E>(p.g, ti * DK + c) : 0.f;
@@ -753,8 +765,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     for (int e = tid; e < kBC * DK; e += kGT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        R0[r * LD + c] = ok ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
-        R1[r * LD + c] = ok ? load_elem<E>(p.k, tix(r) * DK + c) : 0.f;
+        R0[r * LD + c] = ok ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
+        R1[r * LD + c] = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
         R2[r * LD + c] = R[L::oG + e];
     }
     __syncthreads();
@@ -770,8 +782,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         const float dKh = sBeta[r] * R[L::odX + e];
         const float dKb = R[L::odKb + e];
         if (r < Cn) {
-            store_elem<E>(p.gq, tix(r) * DK + c, fmaf(dQh, eg, a1));
-            store_elem<E>(p.gk, tix(r) * DK + c, a2 + a3 + a4 + dKh * eg + dKb * ebar);
+            store_qk_grad<E>(p.gq, p.gq32, tix(r), DK, c, fmaf(dQh, eg, a1));
+            store_qk_grad<E>(p.gk, p.gk32, tix(r), DK, c, a2 + a3 + a4 + dKh * eg + dKb * ebar);
         }
         R[L::odQh + e] = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg
                          - dKb * kr * ebar;
@@ -871,7 +883,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     for (int e = tid; e < kBC * DK; e += kGT) {   // k, b k, g
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        const float kk = ok ? load_elem<E>(p.k, tix(r) * DK + c) : 0.f;
+        const float kk = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
         sK[r * (DK + 1) + c] = kk;
         sR1[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * kk : 0.f;
         sG[r * (DK + 1) + c] = ok ? load_elem<E>(p.g, tix(r) * DK + c) : 0.f;
@@ -957,7 +969,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     for (int e = tid; e < kBC * DK; e += kGT) {   // q -> sR1, b k -> sR2, Qhat
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        const float qq = ok ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
+        const float qq = ok ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
         sR1[r * LD + c] = qq;
         sR2[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * sK[r * (DK + 1) + c] : 0.f;
         R[L::oQh + e] = qq * __expf(sG[r * (DK + 1) + c]);
@@ -1222,9 +1234,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             } else if (r >= Cn) {
                 x = 0.f;
             } else if (what == 0) {
-                x = load_elem<E>(p.q, tix(r) * DK + c);
+                x = load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c);
             } else {
-                x = load_elem<E>(p.k, tix(r) * DK + c);
+                x = load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c);
                 if (what == 2) x *= load_elem<E>(p.beta, tix(r) * DK + c);
             }
             dst[r * LD + c] = x;
@@ -1321,12 +1333,12 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             const float q_ = aq[m][q] + dQh * eg;
             const float kpart = ak[m][q] + dKh * eg + dKb * eb;
             const float dbk = abk[m][q] + dEb * eb;
-            const float qr = r < Cn ? load_elem<E>(p.q, tix(r) * DK + c) : 0.f;
+            const float qr = r < Cn ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
             const float dg = ag[m][q] + dKh * kr * eg + dQh * qr * eg - dKb * kr * eb - dEb * bkr * eb;
             if (r < Cn) {
                 const float br = load_elem<E>(p.beta, tix(r) * DK + c);
-                store_elem<E>(p.gq, tix(r) * DK + c, q_);
-                store_elem<E>(p.gk, tix(r) * DK + c, kpart + dbk * br);
+                store_qk_grad<E>(p.gq, p.gq32, tix(r), DK, c, q_);
+                store_qk_grad<E>(p.gk, p.gk32, tix(r), DK, c, kpart + dbk * br);
                 store_elem<E>(p.gbeta, tix(r) * DK + c, dbk * kr);
             }
             R[L::odQh + e] = dg;
@@ -1387,6 +1399,54 @@ hipError_t launch_bwd2_dtype(const BwdArgs& a, hipStream_t s) {
     return launch_bwd2_dims<E, 64, 64>(a, s);
 }
 
+// dq, dk of grouped query/key heads: the sum over each group of value heads
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs p, int64_t n) {
+    const int G = p.H / p.Hk;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+        const int c = static_cast<int>(e % p.dk);
+        const int64_t row = e / p.dk;                 // (b * T + t) * Hk + hk
+        const int64_t tok = row / p.Hk, hk = row % p.Hk;
+        float sq = 0.f, sk = 0.f;
+        for (int g2 = 0; g2 < G; ++g2) {
+            const int64_t vi = (tok * p.H + hk * G + g2) * p.dk + c;
+            sq += p.gq32[vi];
+            sk += p.gk32[vi];
+        }
+        store_elem<E>(p.gq, e, sq);
+        store_elem<E>(p.gk, e, sk);
+    }
+}
+
+// With grouped query/key heads the kernels write per-value-head dq, dk to fp32
+// buffers from the pool, summed into the outputs by one more launch.
+template <typename E>
+hipError_t bwd_with_groups(BwdArgs a, hipStream_t s, hipError_t (*run)(const BwdArgs&, hipStream_t)) {
+    if (a.Hk == a.H) {
+        a.gq32 = a.gk32 = nullptr;
+        return run(a, s);
+    }
+    hipMemPool_t pool;
+    hipError_t e = workspace_pool(&pool);
+    if (e != hipSuccess) return e;
+    const int64_t per = static_cast<int64_t>(a.B) * a.T * a.H * a.dk;
+    float* buf = nullptr;
+    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&buf), static_cast<size_t>(2 * per * 4), pool, s);
+    if (e != hipSuccess) return e;
+    a.gq32 = buf;
+    a.gk32 = buf + per;
+    e = run(a, s);
+    if (e == hipSuccess) {
+        const int64_t n = static_cast<int64_t>(a.B) * a.T * a.Hk * a.dk;
+        const int64_t blocks = std::min<int64_t>((n + 255) / 256, int64_t(1) << 16);
+        hipLaunchKernelGGL((bwd_group_sum_kernel<E>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, n);
+        e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(buf, s);
+    return e == hipSuccess ? f : e;
+}
+
 template <int VAR, typename E, int DK, int DV>
 hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     typedef BwdWs<DK, DV> L;
@@ -1429,7 +1489,8 @@ hipError_t launch_bwd_var(const BwdArgs& a, hipStream_t s) {
 
 template <int VAR>
 hipError_t launch_bwd_dtype(int dtype, const BwdArgs& a, hipStream_t s) {
-    return dtype == 0 ? launch_bwd_var<VAR, F32>(a, s) : launch_bwd_var<VAR, BF16>(a, s);
+    return dtype == 0 ? bwd_with_groups<F32>(a, s, launch_bwd_var<VAR, F32>)
+                      : bwd_with_groups<BF16>(a, s, launch_bwd_var<VAR, BF16>);
 }
 
 }  // namespace
@@ -1439,7 +1500,8 @@ hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t s) {
         case 0: return launch_bwd_dtype<0>(dtype, a, s);
         case 1: return launch_bwd_dtype<1>(dtype, a, s);
         case 2: return launch_bwd_dtype<2>(dtype, a, s);
-        default: return dtype == 0 ? launch_bwd2_dtype<F32>(a, s) : launch_bwd2_dtype<BF16>(a, s);
+        default: return dtype == 0 ? bwd_with_groups<F32>(a, s, launch_bwd2_dtype<F32>)
+                                   : bwd_with_groups<BF16>(a, s, launch_bwd2_dtype<BF16>);
     }
 }
 

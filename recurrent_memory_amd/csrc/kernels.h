@@ -61,6 +61,9 @@ struct BwdArgs {
     float* gS0;          // [B,H,dv,dk] or nullptr
     const void* wgate;   // split gates: write gate [B,T,H,dv] (beta is then the
     void* gw;            // erase gate [B,T,H,dk]) and its gradient; else nullptr
+    int Hk;              // query/key heads (divides H); q, k, dq, dk are [B,T,Hk,dk]
+    float* gq32;         // grouped heads only: per-value-head dq, dk [B,T,H,dk] fp32,
+    float* gk32;         // summed over each group into gq, gk afterwards; else nullptr
 };
 
 // variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.

@@ -231,13 +231,13 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     None unless wanted)."""
     lib = load_library()
     var = VARIANTS[variant]
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[-1]
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
     bshape = (B, T, H, dk) if variant == "gdn2" else (B, T, H)
-    for name, t, shape in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+    for name, t, shape in (("q", q, (B, T, Hk, dk)), ("k", k, (B, T, Hk, dk)), ("v", v, (B, T, H, dv)),
                            ("beta", beta, bshape), ("dO", dO, (B, T, H, dv))):
         _check(name, t, shape, dt, dev)
     if variant == "gdn2":
@@ -257,7 +257,7 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            "dwgate": torch.empty_like(wgate) if variant == "gdn2" else None,
            "dg": None if gshape is None else torch.empty(gshape, dtype=dt, device=dev),
            "dS0": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None}
-    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], H)
+    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
     st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate), _ptr(g),
                        _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
                        _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dwgate"]), _ptr(out["dg"]),

@@ -123,3 +123,18 @@ def test_bwd_strong_channel_gates(variant, dtype):
     gr = _run(variant, dtype, w, x, dO, dST)
     ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
     _check(variant, dtype, gr, ref)
+
+
+@pytest.mark.parametrize("variant", VARS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H,Hk", [(4, 2), (4, 1)])
+def test_bwd_grouped_heads(variant, dtype, H, Hk):
+    """Grouped query/key heads: dq and dk summed over each group of value heads."""
+    announce("bwd_grouped", variant, dtype, H, Hk)
+    w = Workload("t", variant, dtype, B=2, H=H, T=130, dk=128, dv=64, random_s0=True, seed=47)
+    x = make_forward_inputs(w, qk_heads=Hk)
+    dO, dST = _upstream(w, 14)
+    gr = _run(variant, dtype, w, x, dO, dST)
+    assert gr["dq"].shape == (2, 130, Hk, 128)
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
+    _check(variant, dtype, gr, ref)
