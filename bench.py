@@ -221,7 +221,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU: the path shards by "
+        print(json.dumps({"error": "bench.py runs on exactly one GPU: the path shards by "
                                    "(batch, head) with no communication, but no multi-GPU run is "
                                    "part of it; use --gpus 1"}))
         sys.exit(2)
