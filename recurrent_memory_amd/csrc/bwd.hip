@@ -48,7 +48,7 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
                                          const FB& B) {
     const int l = threadIdx.x & 63;
     const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
-#pragma unroll 4
+#pragma unroll 16
     for (int k = k0; k < k1; k += 4)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
     return acc;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     {   // sum_i S dS' per column, TPC partial sums combined in a fixed order
         const int c = tid % DK, part = tid / DK;
         float acc = 0.f;
-#pragma unroll 8
+#pragma unroll 16
         for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
             acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
         sPart[tid] = acc;
@@ -623,12 +623,26 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         f32x4 aq[MT], aw[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) aq[m] = aw[m] = z4;
+        // row blocks of S, then of dS', double-buffered through registers: the next
+        // block's loads are in flight while the current block's products run
+        constexpr int NPF = QR * DK / kGT;
+        float pf[NPF];
+        auto fetch_rows = [&](int64_t src, int i0) {
+#pragma unroll
+            for (int j = 0; j < NPF; ++j) pf[j] = R[src + i0 * DK + tid + kGT * j];
+        };
+        fetch_rows(L::oS, 0);
         for (int pass = 0; pass < 2; ++pass) {
-            const int64_t src = pass == 0 ? L::oS : L::odS;
             for (int i0 = 0; i0 < DV; i0 += QR) {
                 __syncthreads();
-                for (int e = tid; e < QR * DK; e += kGT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
+#pragma unroll
+                for (int j = 0; j < NPF; ++j) {
+                    const int e = tid + kGT * j;
+                    sM2[(e / DK) * (DK + 1) + e % DK] = pf[j];
+                }
                 __syncthreads();
+                if (i0 + QR < DV) fetch_rows(pass == 0 ? L::oS : L::odS, i0 + QR);
+                else if (pass == 0) fetch_rows(L::odS, 0);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     {   // sum_r dKbar Kbar per column
         const int c = tid % DK, part = tid / DK;
         float acc = 0.f;
-#pragma unroll 8
+#pragma unroll 16
         for (int r = part * (kBC / TPC); r < (part + 1) * (kBC / TPC); ++r)
             acc = fmaf(R[L::odKb + r * DK + c], R[L::oKb + r * DK + c], acc);
         sPart[tid] = acc;
@@ -1028,8 +1042,20 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         return load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
     };
     // stage rows [i0, i0 + QR) of a [DV][DK] workspace matrix into sM2
-    auto stage_rows = [&](int64_t src, int i0) {
-        for (int e = tid; e < QR * DK; e += kGT) sM2[(e / DK) * (DK + 1) + e % DK] = R[src + i0 * DK + e];
+    // row blocks of a [DV][DK] workspace matrix, double-buffered through registers:
+    // fetch_rows issues the loads, put_rows writes them to sM2 (after a barrier)
+    constexpr int NPF = QR * DK / kGT;
+    float pf[NPF];
+    auto fetch_rows = [&](int64_t src, int i0) {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) pf[j] = R[src + i0 * DK + tid + kGT * j];
+    };
+    auto put_rows = [&]() {
+#pragma unroll
+        for (int j = 0; j < NPF; ++j) {
+            const int e = tid + kGT * j;
+            sM2[(e / DK) * (DK + 1) + e % DK] = pf[j];
+        }
     };
 
     for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Y -> R1, X -> R2
@@ -1041,7 +1067,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     {   // sum_i S dS' per column
         const int c = tid % DK, part = tid / DK;
         float acc = 0.f;
-#pragma unroll 8
+#pragma unroll 16
         for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
             acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
         sPart[tid] = acc;
@@ -1069,10 +1095,12 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         f32x4 a1[MT], a2[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) a1[m] = a2[m] = z4;
+        fetch_rows(L::oS, 0);
         for (int i0 = 0; i0 < DV; i0 += QR) {
             __syncthreads();
-            stage_rows(L::oS, i0);
+            put_rows();
             __syncthreads();
+            fetch_rows(i0 + QR < DV ? L::oS : L::odS, i0 + QR < DV ? i0 + QR : 0);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
@@ -1089,8 +1117,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
         for (int i0 = 0; i0 < DV; i0 += QR) {
             __syncthreads();
-            stage_rows(L::odS, i0);
+            put_rows();
             __syncthreads();
+            if (i0 + QR < DV) fetch_rows(L::odS, i0 + QR);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
@@ -1130,10 +1159,12 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         f32x4 a1[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) a1[m] = z4;
+        fetch_rows(L::oS, 0);
         for (int i0 = 0; i0 < DV; i0 += QR) {
             __syncthreads();
-            stage_rows(L::oS, i0);
+            put_rows();
             __syncthreads();
+            if (i0 + QR < DV) fetch_rows(L::oS, i0 + QR);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
