@@ -316,19 +316,24 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
 template <class L, typename E, int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, int N) {
     constexpr int NVT = DV / kBVT;
-    __shared__ float sS[kBVT * (DK + 1)];
-    __shared__ float sVt[kBC * (kBVT + 1)];
-    __shared__ float sW[kBC * (DK + 1)];
-    __shared__ float sKb[kBC * (DK + 1)];
-    __shared__ float sEb[SPLIT ? kBC * (DK + 1) : 1];
-    __shared__ float sXt[SPLIT ? kBC * (kBVT + 1) : 1];
+    // Row strides against LDS bank conflicts in the matrix-core operand reads:
+    // an operand read along its rows by the 16 lanes of a group (sS, sW) takes a
+    // stride of 4 mod 64 words; one read down its columns (sKb, sEb, sVt, sXt)
+    // takes 16 mod 64, so the four k-rows of one read fall in different banks.
+    constexpr int SS = DK + 4, SW = DK + 4, SK = DK + 16, SV = kBVT + 16;
+    __shared__ __attribute__((aligned(16))) float sS[kBVT * SS];
+    __shared__ __attribute__((aligned(16))) float sVt[kBC * SV];
+    __shared__ __attribute__((aligned(16))) float sW[kBC * SW];
+    __shared__ __attribute__((aligned(16))) float sKb[kBC * SK];
+    __shared__ __attribute__((aligned(16))) float sEb[SPLIT ? kBC * SK : 4];
+    __shared__ __attribute__((aligned(16))) float sXt[SPLIT ? kBC * SV : 4];
     __shared__ float sGam[DK];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NVT, i0 = (blockIdx.x % NVT) * kBVT;
     const int b = bh / p.H, h = bh % p.H;
     for (int e = tid; e < kBVT * DK; e += kBT) {
         const int i = e / DK, c = e % DK;
-        sS[i * (DK + 1) + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
+        sS[i * SS + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
     // the next chunk's operands are fetched into registers while this chunk's
     // products run, and written to LDS at the top of the next step
@@ -355,12 +360,8 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         }
         pG = tid < DK ? R[L::oGam + tid] : 0.f;
     };
-    auto put4 = [&](float* dst, int idx, float4 v) {
-        float* d = dst + (idx / DK) * (DK + 1) + idx % DK;
-        d[0] = v.x;
-        d[1] = v.y;
-        d[2] = v.z;
-        d[3] = v.w;
+    auto put4 = [&](float* dst, int ld, int idx, float4 v) {
+        *reinterpret_cast<float4*>(dst + (idx / DK) * ld + idx % DK) = v;
     };
     fetch(0);
     for (int n = 0; n < N; ++n) {
@@ -368,9 +369,9 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kBT * j);
-            put4(sW, idx, pW[j]);
-            put4(sKb, idx, pK[j]);
-            if constexpr (SPLIT) put4(sEb, idx, pE[j]);
+            put4(sW, SW, idx, pW[j]);
+            put4(sKb, SK, idx, pK[j]);
+            if constexpr (SPLIT) put4(sEb, SK, idx, pE[j]);
         }
         float uu[MT][4];
 #pragma unroll
@@ -387,27 +388,27 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
                     const int64_t vi = tok_index(p, b, t0 + r, h) * DV + i0 + i;
                     x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
                 }
-                sXt[r * (kBVT + 1) + i] = x;
+                sXt[r * SV + i] = x;
             }
         }
         lds_only_barrier();
         if (n + 1 < N) fetch(n + 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
-            R[L::oS + (i0 + i) * DK + c] = sS[i * (DK + 1) + c];
+            R[L::oS + (i0 + i) * DK + c] = sS[i * SS + c];
         }
         constexpr float sgn = SPLIT ? 1.f : -1.f;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {   // Vt = U - W S^T  /  Y = Ut + W S^T
             const int t = w + 4 * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
             const f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
-                                      [&](int r, int c) { return sW[r * (DK + 1) + c]; },
-                                      [&](int c, int i) { return sS[i * (DK + 1) + c]; });
+                                      [&](int r, int c) { return sW[r * SW + c]; },
+                                      [&](int c, int i) { return sS[i * SS + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
                 const float val = uu[m][q] + sgn * acc[q];
-                sVt[r * (kBVT + 1) + i] = val;
+                sVt[r * SV + i] = val;
                 R[L::oVt + r * DV + i0 + i] = val;
             }
         }
@@ -416,18 +417,18 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
             const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if constexpr (SPLIT) {   // - Y^T Ebar + X^T Kbar
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return -sVt[r * (kBVT + 1) + i]; },
-                              [&](int r, int c) { return sEb[r * (DK + 1) + c]; });
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sXt[r * (kBVT + 1) + i]; },
-                              [&](int r, int c) { return sKb[r * (DK + 1) + c]; });
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return -sVt[r * SV + i]; },
+                              [&](int r, int c) { return sEb[r * SK + c]; });
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sXt[r * SV + i]; },
+                              [&](int r, int c) { return sKb[r * SK + c]; });
             } else {                 // + Vt^T Kbar
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sVt[r * (kBVT + 1) + i]; },
-                              [&](int r, int c) { return sKb[r * (DK + 1) + c]; });
+                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sVt[r * SV + i]; },
+                              [&](int r, int c) { return sKb[r * SK + c]; });
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
-                sS[i * (DK + 1) + c] = fmaf(sS[i * (DK + 1) + c], sGam[c], acc[q]);
+                sS[i * SS + c] = fmaf(sS[i * SS + c], sGam[c], acc[q]);
             }
         }
         lds_only_barrier();
@@ -440,20 +441,24 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 template <class L, typename E, int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, int N) {
     constexpr int NVT = DV / kBVT;
-    __shared__ float sdS[kBVT * (DK + 1)];
-    __shared__ float sdVt[kBC * (kBVT + 1)];
-    __shared__ float sdO[kBC * (kBVT + 1)];
-    __shared__ float sM[kBC * (kBC + 1)];
-    __shared__ float sA1[kBC * (DK + 1)];
-    __shared__ float sA2[kBC * (DK + 1)];
-    __shared__ float sQh[kBC * (DK + 1)];
+    // row strides against bank conflicts (see the forward chain), within the LDS:
+    // 4 mod 64 words for operands read along rows (sdS, sA1), 8 mod 64 for those
+    // read down columns (at most two-way conflicts)
+    constexpr int SD = DK + 4, SA = DK + 4, SB = DK + 8, SO = kBVT + 8, SMQ = kBC + 8;
+    __shared__ __attribute__((aligned(16))) float sdS[kBVT * SD];
+    __shared__ __attribute__((aligned(16))) float sdVt[kBC * SO];
+    __shared__ __attribute__((aligned(16))) float sdO[kBC * SO];
+    __shared__ __attribute__((aligned(16))) float sM[kBC * SMQ];
+    __shared__ __attribute__((aligned(16))) float sA1[kBC * SA];
+    __shared__ __attribute__((aligned(16))) float sA2[kBC * SB];
+    __shared__ __attribute__((aligned(16))) float sQh[kBC * SB];
     __shared__ float sGam[DK];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NVT, i0 = (blockIdx.x % NVT) * kBVT;
     const int b = bh / p.H, h = bh % p.H;
     for (int e = tid; e < kBVT * DK; e += kBT) {
         const int i = e / DK, c = e % DK;
-        sdS[i * (DK + 1) + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
+        sdS[i * SD + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
     // the previous chunk's operands are fetched into registers during this step
     constexpr int NP = kBC * DK / 4 / kBT;
@@ -482,49 +487,45 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         pG = tid < DK ? R[L::oGam + tid] : 0.f;
     };
     auto put4 = [&](float* dst, int idx, int ld, int row, float4 v) {
-        float* d = dst + (idx / row) * ld + idx % row;
-        d[0] = v.x;
-        d[1] = v.y;
-        d[2] = v.z;
-        d[3] = v.w;
+        *reinterpret_cast<float4*>(dst + (idx / row) * ld + idx % row) = v;
     };
     fetch(N - 1);
     for (int n = N - 1; n >= 0; --n) {
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
 #pragma unroll
-        for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kBT * j), kBC + 1, kBC, pM[j]);
+        for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kBT * j), SMQ, kBC, pM[j]);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kBT * j);
-            put4(sA1, idx, DK + 1, DK, pA[j]);
-            put4(sQh, idx, DK + 1, DK, pQ[j]);
-            put4(sA2, idx, DK + 1, DK, pW[j]);
+            put4(sA1, idx, SA, DK, pA[j]);
+            put4(sQh, idx, SB, DK, pQ[j]);
+            put4(sA2, idx, SB, DK, pW[j]);
         }
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
             const int e = tid + kBT * j;
-            sdO[(e / kBVT) * (kBVT + 1) + e % kBVT] = pO[j];
+            sdO[(e / kBVT) * SO + e % kBVT] = pO[j];
         }
         if (tid < DK) sGam[tid] = pG;
         lds_only_barrier();
         if (n > 0) fetch(n - 1);
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
-            R[L::odS + (i0 + i) * DK + c] = sdS[i * (DK + 1) + c];
+            R[L::odS + (i0 + i) * DK + c] = sdS[i * SD + c];
         }
         const int w = tid >> 6, l = tid & 63;
         for (int t = w; t < (kBC / 16) * (kBVT / 16); t += 4) {   // dVt = Mq^T dO + Kbar dS^T
             const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
             f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
-                                [&](int r, int m) { return sM[m * (kBC + 1) + r]; },
-                                [&](int m, int i) { return sdO[m * (kBVT + 1) + i]; });
-            acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * (DK + 1) + c]; },
-                          [&](int c, int i) { return sdS[i * (DK + 1) + c]; });
+                                [&](int r, int m) { return sM[m * SMQ + r]; },
+                                [&](int m, int i) { return sdO[m * SO + i]; });
+            acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
+                          [&](int c, int i) { return sdS[i * SD + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
                 const float val = SPLIT ? -acc[q] : acc[q];
-                sdVt[r * (kBVT + 1) + i] = val;
+                sdVt[r * SO + i] = val;
                 R[L::odVt + r * DV + i0 + i] = val;
             }
         }
@@ -532,15 +533,15 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // dS = dS Diag(gamma) + dO^T Qhat -/+ dVt^T W
             const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
             f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, ii0, cc0, 0, kBC,
-                                [&](int i, int r) { return sdO[r * (kBVT + 1) + i]; },
-                                [&](int r, int c) { return sQh[r * (DK + 1) + c]; });
+                                [&](int i, int r) { return sdO[r * SO + i]; },
+                                [&](int r, int c) { return sQh[r * SB + c]; });
             acc = mm_tile(acc, ii0, cc0, 0, kBC,
-                          [&](int i, int r) { return (SPLIT ? 1.f : -1.f) * sdVt[r * (kBVT + 1) + i]; },
-                          [&](int r, int c) { return sA2[r * (DK + 1) + c]; });
+                          [&](int i, int r) { return (SPLIT ? 1.f : -1.f) * sdVt[r * SO + i]; },
+                          [&](int r, int c) { return sA2[r * SB + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
-                sdS[i * (DK + 1) + c] = fmaf(sdS[i * (DK + 1) + c], sGam[c], acc[q]);
+                sdS[i * SD + c] = fmaf(sdS[i * SD + c], sGam[c], acc[q]);
             }
         }
         lds_only_barrier();
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     if (p.gS0) {
         for (int e = tid; e < kBVT * DK; e += kBT) {
             const int i = e / DK, c = e % DK;
-            p.gS0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] = sdS[i * (DK + 1) + c];
+            p.gS0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] = sdS[i * SD + c];
         }
     }
 }
