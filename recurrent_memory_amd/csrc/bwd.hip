@@ -190,12 +190,12 @@ __device__ __forceinline__ void store_qk_grad(void* out, float* out32, int64_t v
 template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
-    constexpr int LD = (DK > DV ? DK : DV) + 1;   // padded row stride
-    __shared__ float sK[kBC * (DK + 1)];
+    constexpr int LD = (DK > DV ? DK : DV) + 4;   // padded row stride (4 mod 64 words)
+    __shared__ float sK[kBC * (DK + 4)];
     __shared__ float sX[kBC * LD];                // q, then beta Khat, then beta v
-    __shared__ float sG[kBC * (DK + 1)];
-    __shared__ float sA[kBC * (kBC + 1)];
-    __shared__ float sT[kBC * (kBC + 1)];
+    __shared__ float sG[kBC * (DK + 4)];
+    __shared__ float sA[kBC * (kBC + 4)];
+    __shared__ float sT[kBC * (kBC + 4)];
     __shared__ float sBeta[kBC];
     const int u = blockIdx.x, tid = threadIdx.x;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
@@ -207,25 +207,25 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         const bool ok = r < Cn;
         const int64_t ti = tok_index(p, b, t0 + min(r, Cn - 1), h);
         const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h);
-        sK[r * (DK + 1) + c] = ok ? load_elem<E>(p.k, qi * DK + c) : 0.f;
+        sK[r * (DK + 4) + c] = ok ? load_elem<E>(p.k, qi * DK + c) : 0.f;
         sX[r * LD + c] = ok ? load_elem<E>(p.q, qi * DK + c) : 0.f;
         float gv = 0.f;
         if constexpr (VAR == 1) gv = ok ? load_elem<E>(p.g, ti) : 0.f;
         if constexpr (VAR == 2) gv = ok ? load_elem<E>(p.g, ti * DK + c) : 0.f;
-        sG[r * (DK + 1) + c] = gv;
+        sG[r * (DK + 4) + c] = gv;
     }
     if (tid < kBC) sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tok_index(p, b, t0 + tid, h)) : 0.f;
     __syncthreads();
     if (tid < DK) {   // in-chunk cumulative log-decay per channel
         float acc = 0.f;
         for (int r = 0; r < kBC; ++r) {
-            acc += sG[r * (DK + 1) + tid];
-            sG[r * (DK + 1) + tid] = acc;
+            acc += sG[r * (DK + 4) + tid];
+            sG[r * (DK + 4) + tid] = acc;
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
-    if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
+    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 4) + e % DK];
+    if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 4) + tid]);
     // Abar (strictly lower) and Mq (lower, diagonal included)
     const int w = tid >> 6, l = tid & 63;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -237,18 +237,18 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
             f32x4 ab = z4, mq = z4;
             if (j0 <= r0) {
-                const float* gref = sG + (j0 + 15) * (DK + 1);
-                auto Bk = [&](int c, int j) { return sK[j * (DK + 1) + c] * __expf(gref[c] - sG[j * (DK + 1) + c]); };
+                const float* gref = sG + (j0 + 15) * (DK + 4);
+                auto Bk = [&](int c, int j) { return sK[j * (DK + 4) + c] * __expf(gref[c] - sG[j * (DK + 4) + c]); };
                 ab = mm_tile(z4, r0, j0, 0, DK,
-                             [&](int r, int c) { return sK[r * (DK + 1) + c] * __expf(sG[r * (DK + 1) + c] - gref[c]); }, Bk);
+                             [&](int r, int c) { return sK[r * (DK + 4) + c] * __expf(sG[r * (DK + 4) + c] - gref[c]); }, Bk);
                 mq = mm_tile(z4, r0, j0, 0, DK,
-                             [&](int r, int c) { return sX[r * LD + c] * __expf(sG[r * (DK + 1) + c] - gref[c]); }, Bk);
+                             [&](int r, int c) { return sX[r * LD + c] * __expf(sG[r * (DK + 4) + c] - gref[c]); }, Bk);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
                 const float a_ = j < r ? ab[q] : 0.f;
-                sA[r * (kBC + 1) + j] = a_;
+                sA[r * (kBC + 4) + j] = a_;
                 R[L::oAb + r * kBC + j] = a_;
                 R[L::oMq + r * kBC + j] = j <= r ? mq[q] : 0.f;
             }
@@ -256,16 +256,16 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
         for (int t = w; t < 16; t += kGW) {
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-            const f32x4 ab = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 1) + c]; },
-                                     [&](int c, int j) { return sK[j * (DK + 1) + c]; });
+            const f32x4 ab = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 4) + c]; },
+                                     [&](int c, int j) { return sK[j * (DK + 4) + c]; });
             const f32x4 mq = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sX[r * LD + c]; },
-                                     [&](int c, int j) { return sK[j * (DK + 1) + c]; });
+                                     [&](int c, int j) { return sK[j * (DK + 4) + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
-                const float ex = (VAR == 1 && j <= r) ? __expf(sG[r * (DK + 1)] - sG[j * (DK + 1)]) : 1.f;
+                const float ex = (VAR == 1 && j <= r) ? __expf(sG[r * (DK + 4)] - sG[j * (DK + 4)]) : 1.f;
                 const float a_ = j < r ? ab[q] * ex : 0.f;
-                sA[r * (kBC + 1) + j] = a_;
+                sA[r * (kBC + 4) + j] = a_;
                 R[L::oAb + r * kBC + j] = a_;
                 R[L::oMq + r * kBC + j] = j <= r ? mq[q] * ex : 0.f;
             }
@@ -273,24 +273,24 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     }
     __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution, one column per thread
-    if (tid < kBC) unit_lower_inverse(sA, kBC + 1, sBeta, sT, kBC + 1, tid);
+    if (tid < kBC) unit_lower_inverse(sA, kBC + 4, sBeta, sT, kBC + 4, tid);
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 1) + e % kBC];
+    for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 4) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
     for (int e = tid; e < kBC * DK; e += kGT) {
         const int r = e / DK, c = e % DK;
-        const float G = sG[r * (DK + 1) + c];
+        const float G = sG[r * (DK + 4) + c];
         const float eg = __expf(G);
-        const float kk = sK[r * (DK + 1) + c];
+        const float kk = sK[r * (DK + 4) + c];
         R[L::oKh + e] = kk * eg;
         R[L::oQh + e] = sX[r * LD + c] * eg;
-        R[L::oKb + e] = kk * __expf(sG[(kBC - 1) * (DK + 1) + c] - G);
+        R[L::oKb + e] = kk * __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
         sX[r * LD + c] = sBeta[r] * kk * eg;
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T X
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
                                   [&](int j, int c) { return sX[j * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // U = T Y
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 1) + j]; },
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
                                   [&](int j, int i) { return sX[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
@@ -560,11 +560,11 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
 template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
-    constexpr int CP = kBC + 1;
-    constexpr int LD = (DK > DV ? DK : DV) + 1;
+    constexpr int CP = kBC + 4;
+    constexpr int LD = (DK > DV ? DK : DV) + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;   // region size
     constexpr int QR = 32;            // rows of S (or dS') staged at a time
-    static_assert(QR * (DK + 1) <= kBC * CP, "S quarter must fit the second C x C buffer");
+    static_assert(QR * (DK + 4) <= kBC * CP, "S quarter must fit the second C x C buffer");
     __shared__ float sM1[kBC * CP];   // dMq (then dMq E)
     __shared__ float sM2[kBC * CP];   // S quarters; dT; dA; dAbar (then dAbar E)
     __shared__ float sR[3 * RS];      // three staging regions
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
                 for (int j = 0; j < NPF; ++j) {
                     const int e = tid + kGT * j;
-                    sM2[(e / DK) * (DK + 1) + e % DK] = pf[j];
+                    sM2[(e / DK) * (DK + 4) + e % DK] = pf[j];
                 }
                 __syncthreads();
                 if (i0 + QR < DV) fetch_rows(pass == 0 ? L::oS : L::odS, i0 + QR);
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                    auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; };
+                    auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; };
                     if (pass == 0) {
                         aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
                         aw[m] = mm_tile(aw[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R2[r * LD + i]; }, Bs);
@@ -880,11 +880,11 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs2<DK, DV> L;
-    constexpr int LD = (DK > DV ? DK : DV) + 1;
-    constexpr int CP = kBC + 1;
+    constexpr int LD = (DK > DV ? DK : DV) + 4;
+    constexpr int CP = kBC + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
-    __shared__ float sK[kBC * (DK + 1)];
-    __shared__ float sG[kBC * (DK + 1)];
+    __shared__ float sK[kBC * (DK + 4)];
+    __shared__ float sG[kBC * (DK + 4)];
     __shared__ float sR1[RS];
     __shared__ float sR2[RS];
     __shared__ float sM[kBC * CP];
@@ -899,32 +899,32 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const float kk = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
-        sK[r * (DK + 1) + c] = kk;
+        sK[r * (DK + 4) + c] = kk;
         sR1[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * kk : 0.f;
-        sG[r * (DK + 1) + c] = ok ? load_elem<E>(p.g, tix(r) * DK + c) : 0.f;
+        sG[r * (DK + 4) + c] = ok ? load_elem<E>(p.g, tix(r) * DK + c) : 0.f;
     }
     __syncthreads();
     if (tid < DK) {
         float acc = 0.f;
         for (int r = 0; r < kBC; ++r) {
-            acc += sG[r * (DK + 1) + tid];
-            sG[r * (DK + 1) + tid] = acc;
+            acc += sG[r * (DK + 4) + tid];
+            sG[r * (DK + 4) + tid] = acc;
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 1) + e % DK];
-    if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 1) + tid]);
+    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 4) + e % DK];
+    if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 4) + tid]);
     // pairwise factors with the reference at the last row of j's 16-row block
-    auto aexp = [&](int r, int c, const float* gref) { return __expf(sG[r * (DK + 1) + c] - gref[c]); };
-    auto bexp = [&](int j, int c, const float* gref) { return __expf(gref[c] - sG[j * (DK + 1) + c]); };
+    auto aexp = [&](int r, int c, const float* gref) { return __expf(sG[r * (DK + 4) + c] - gref[c]); };
+    auto bexp = [&](int j, int c, const float* gref) { return __expf(gref[c] - sG[j * (DK + 4) + c]); };
     for (int t = w; t < 16; t += kGW) {           // Ae -> sM, Ak -> workspace (strictly lower)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         f32x4 ae = z4, ak = z4;
         if (j0 <= r0) {
-            const float* gref = sG + (j0 + 15) * (DK + 1);
-            auto Ak_ = [&](int r, int c) { return sK[r * (DK + 1) + c] * aexp(r, c, gref); };
+            const float* gref = sG + (j0 + 15) * (DK + 4);
+            auto Ak_ = [&](int r, int c) { return sK[r * (DK + 4) + c] * aexp(r, c, gref); };
             ae = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sR1[j * LD + c] * bexp(j, c, gref); });
-            ak = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sK[j * (DK + 1) + c] * bexp(j, c, gref); });
+            ak = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -940,9 +940,9 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
     for (int e = tid; e < kBC * DK; e += kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
         const int r = e / DK, c = e % DK;
-        const float G = sG[r * (DK + 1) + c];
-        const float eg = __expf(G), eb = __expf(sG[(kBC - 1) * (DK + 1) + c] - G);
-        const float kk = sK[r * (DK + 1) + c];
+        const float G = sG[r * (DK + 4) + c];
+        const float eg = __expf(G), eb = __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
+        const float kk = sK[r * (DK + 4) + c];
         R[L::oEb + e] = sR1[r * LD + c] * eb;
         R[L::oKb + e] = kk * eb;
         R[L::oKh + e] = kk * eg;
@@ -986,18 +986,18 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         const bool ok = r < Cn;
         const float qq = ok ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
         sR1[r * LD + c] = qq;
-        sR2[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * sK[r * (DK + 1) + c] : 0.f;
-        R[L::oQh + e] = qq * __expf(sG[r * (DK + 1) + c]);
+        sR2[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * sK[r * (DK + 4) + c] : 0.f;
+        R[L::oQh + e] = qq * __expf(sG[r * (DK + 4) + c]);
     }
     __syncthreads();
     for (int t = w; t < 16; t += kGW) {           // Me, Mk (lower, diagonal included)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         f32x4 me = z4, mk = z4;
         if (j0 <= r0) {
-            const float* gref = sG + (j0 + 15) * (DK + 1);
+            const float* gref = sG + (j0 + 15) * (DK + 4);
             auto Aq = [&](int r, int c) { return sR1[r * LD + c] * aexp(r, c, gref); };
             me = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sR2[j * LD + c] * bexp(j, c, gref); });
-            mk = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sK[j * (DK + 1) + c] * bexp(j, c, gref); });
+            mk = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1012,8 +1012,8 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs2<DK, DV> L;
-    constexpr int CP = kBC + 1;
-    constexpr int LD = (DK > DV ? DK : DV) + 1;
+    constexpr int CP = kBC + 4;
+    constexpr int LD = (DK > DV ? DK : DV) + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
     constexpr int QR = 32;
     constexpr int TPC = kGT / DK;
@@ -1055,7 +1055,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
             const int e = tid + kGT * j;
-            sM2[(e / DK) * (DK + 1) + e % DK] = pf[j];
+            sM2[(e / DK) * (DK + 4) + e % DK] = pf[j];
         }
     };
 
@@ -1106,7 +1106,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                 a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
-                                [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; });
+                                [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
 #pragma unroll
@@ -1124,7 +1124,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; };
+                auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; };
                 a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R1[r * LD + i]; }, Bs);
                 a2[m] = mm_tile(a2[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R2[r * LD + i]; }, Bs);
             }
@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                 a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
-                                [&](int i, int c) { return sM2[(i - i0) * (DK + 1) + c]; });
+                                [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
 #pragma unroll
