@@ -138,3 +138,26 @@ def test_bwd_grouped_heads(variant, dtype, H, Hk):
     assert gr["dq"].shape == (2, 130, Hk, 128)
     ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
     _check(variant, dtype, gr, ref)
+
+
+@pytest.mark.parametrize("variant", VARS)
+def test_autograd_function(variant):
+    """torch.autograd through delta_rule (forward and backward in the library's kernels)
+    against the oracle's reverse mode, with grouped query/key heads."""
+    from recurrent_memory_amd.autograd import delta_rule
+    announce("autograd", variant)
+    w = Workload("t", variant, "f32", B=1, H=4, T=100, dk=64, dv=64, random_s0=True, seed=48)
+    x = make_forward_inputs(w, qk_heads=2)
+    dO, dST = _upstream(w, 15)
+    leaves = {n: (None if a is None else dev(a).requires_grad_(True))
+              for n, a in x.items() if n != "S0"}
+    S0 = dev(x["S0"]).requires_grad_(True)
+    o, S = delta_rule(variant, leaves["q"], leaves["k"], leaves["v"], leaves["beta"], g=leaves["g"],
+                      wgate=leaves["wgate"], S0=S0)
+    (o * dev(dO)).sum().backward(retain_graph=True)
+    (S * dev(dST)).sum().backward()
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], x["g"], x["S0"], dO, dST)
+    got = {"dq": leaves["q"].grad, "dk": leaves["k"].grad, "dv": leaves["v"].grad,
+           "dbeta": leaves["beta"].grad, "dwgate": None if leaves["wgate"] is None else leaves["wgate"].grad,
+           "dg": None if leaves["g"] is None else leaves["g"].grad, "dS0": S0.grad}
+    _check(variant, "f32", {n: (None if t is None else host(t)) for n, t in got.items()}, ref)
