@@ -787,15 +787,29 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
     // a3 = sum_{j<r} dAbar[r,j] k_j E,  a4 = sum_{j>r} dAbar[j,r] k_j E,  E = e^{G_r - G_j} (row r >= j)
-    auto finish = [&](int r, int c, float a1, float a2, float a3, float a4) {
+    // the workspace terms of a tile's four elements are loaded before its products
+    struct Pre {
+        float dQh[4], dX[4], dKb[4];
+    };
+    auto preload = [&](int r0, int c0) {
+        Pre pr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = ti(r0, q) * DK + tj(c0);
+            pr.dQh[q] = R[L::odQh + e];
+            pr.dX[q] = R[L::odX + e];
+            pr.dKb[q] = R[L::odKb + e];
+        }
+        return pr;
+    };
+    auto finish = [&](int r, int c, float a1, float a2, float a3, float a4, float dQh, float dX_,
+                      float dKb) {
         const float Gr = R2[r * LD + c];
         const float qr = R0[r * LD + c], kr = R1[r * LD + c];
         const float eg = (VAR == 0) ? 1.f : __expf(Gr);
         const float ebar = (VAR == 0) ? 1.f : __expf(R2[(kBC - 1) * LD + c] - Gr);
         const int e = r * DK + c;
-        const float dQh = R[L::odQh + e];
-        const float dKh = sBeta[r] * R[L::odX + e];
-        const float dKb = R[L::odKb + e];
+        const float dKh = sBeta[r] * dX_;
         if (r < Cn) {
             store_qk_grad<E>(p.gq, p.gq32, tix(r), DK, c, fmaf(dQh, eg, a1));
             store_qk_grad<E>(p.gk, p.gk32, tix(r), DK, c, a2 + a3 + a4 + dKh * eg + dKb * ebar);
@@ -811,12 +825,14 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         auto Kf = [&](int j, int c) { return R1[j * LD + c]; };
         for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const Pre pr = preload(r0, c0);
             const f32x4 a1 = pair_tile<true>(r0, c0, M1, Kf, Gf);
             const f32x4 a2 = pair_tile<false>(r0, c0, M1, Qf, Gf);
             const f32x4 a3 = pair_tile<true>(r0, c0, M2, Kf, Gf);
             const f32x4 a4 = pair_tile<false>(r0, c0, M2, Kf, Gf);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q]);
+            for (int q = 0; q < 4; ++q)
+                finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
         }
     } else {
         // the decay factor is one number per (r, j): fold it into dMq and dAbar and
@@ -834,6 +850,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
         for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const Pre pr = preload(r0, c0);
             const f32x4 a1 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
             const f32x4 a2 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[j * CP + r]; },
@@ -843,7 +860,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             const f32x4 a4 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
 #pragma unroll
-            for (int q = 0; q < 4; ++q) finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q]);
+            for (int q = 0; q < 4; ++q)
+                finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
         }
     }
     if constexpr (VAR != 0) {
