@@ -19,7 +19,15 @@ time, on the exact (already rounded) input values the GPU receives:
   head-wise decay gate into channel-wise decay);
 * Gated DeltaNet-2 replaces the single step size by a channel-wise erase gate
   b (key side) and a channel-wise write gate w (value side), and reduces to
-  KDA when both equal the same scalar (Gated DeltaNet-2 abstract).
+  KDA when both equal the same scalar (Gated DeltaNet-2 abstract);
+* FG^2-GDN ("Delta-Rule Linear Attention" topic page, FG^2-GDN card) turns the
+  scalar step size of KDA into a channel-wise vector, as a per-coordinate
+  optimizer turns one learning rate into one per coordinate.  Reading: the
+  coordinates are the key channels, so the step is the gradient of
+  1/2 ||S' k - v||^2, which is (S' k - v) k^T, scaled column by column by
+  beta_t: the residual is written along beta_t ⊙ k_t.  The card's FG^2-GDN+
+  (separate erase and write scales for keys and values) is the split-gate
+  form above.
 
 With S of shape [d_v, d_k] and a_t the decay (1, a scalar, or a d_k-vector),
 one token does, in this order:
@@ -28,11 +36,15 @@ one token does, in this order:
     r   = S' k_t                                  read
     S   = S' + beta_t (v_t - r) k_t^T             DeltaNet, GDN, KDA
     S   = S' - r (b_t ⊙ k_t)^T + (w_t ⊙ v_t) k_t^T   Gated DeltaNet-2
+    S   = S' + (v_t - r) (beta_t ⊙ k_t)^T         FG^2-GDN (beta_t a d_k-vector)
     o_t = S q_t                                   readout after the write
 
 The erase placement ``r (b ⊙ k)^T`` for Gated DeltaNet-2 is a reading: the
 abstract names the two gates but prints no formula.  That reading is parity
-unpinned beyond the reduction to KDA at b = w = beta.
+unpinned beyond the reduction to KDA at b = w = beta.  The FG^2-GDN reading is
+pinned to the per-coordinate gradient step it is named after and to its
+reduction to KDA at beta_t = beta·1; which axis carries the vector is the
+reading.  (No reverse mode is given for FG^2-GDN.)
 
 Two further forms from the same topic page:
 
@@ -56,23 +68,25 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-VARIANTS = ("deltanet", "gdn", "kda", "gdn2")
+VARIANTS = ("deltanet", "gdn", "kda", "gdn2", "fg2")
 
 
 def run_recurrence(S0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
                    a: np.ndarray, beta: Optional[np.ndarray] = None,
-                   erase: Optional[np.ndarray] = None, write: Optional[np.ndarray] = None
-                   ) -> Tuple[np.ndarray, np.ndarray]:
+                   erase: Optional[np.ndarray] = None, write: Optional[np.ndarray] = None,
+                   keystep: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Sequential recurrence over a batch of independent sequences.
 
     S0: [N, dv, dk]; q, k: [N, T, dk]; v: [N, T, dv]; a: [N, T, dk] decay
-    factors (already broadcast over key channels).  Either ``beta`` [N, T]
-    (single step size) or both ``erase`` [N, T, dk] and ``write`` [N, T, dv]
-    (split gates).  Returns o [N, T, dv] and the final state [N, dv, dk].
+    factors (already broadcast over key channels).  Exactly one of: ``beta``
+    [N, T] (single step size), both ``erase`` [N, T, dk] and ``write``
+    [N, T, dv] (split gates), or ``keystep`` [N, T, dk] (a step size per key
+    channel, FG^2-GDN).  Returns o [N, T, dv] and the final state [N, dv, dk].
     """
     split = erase is not None
-    if split != (write is not None) or split == (beta is not None):
-        raise ValueError("pass either beta, or both erase and write")
+    modes = (beta is not None) + split + (keystep is not None)
+    if split != (write is not None) or modes != 1:
+        raise ValueError("pass either beta, or both erase and write, or keystep")
     S = np.array(S0, copy=True)
     N, T, _ = q.shape
     o = np.empty((N, T, v.shape[2]), dtype=S.dtype)
@@ -83,6 +97,8 @@ def run_recurrence(S0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
         if split:
             S = (Sp - r[:, :, None] * (erase[:, t, :] * kt)[:, None, :]
                  + (write[:, t, :] * v[:, t, :])[:, :, None] * kt[:, None, :])
+        elif keystep is not None:
+            S = Sp + (v[:, t, :] - r)[:, :, None] * (keystep[:, t, :] * kt)[:, None, :]
         else:
             S = Sp + beta[:, t, None, None] * (v[:, t, :] - r)[:, :, None] * kt[:, None, :]
         o[:, t, :] = (S @ q[:, t, :, None])[:, :, 0]
@@ -159,7 +175,8 @@ def delta_fwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None
 
     q, k: [B, T, H_k, dk] with H_k dividing H (H_k = H unless the value heads
     are grouped); v: [B, T, H, dv]; beta: [B, T, H] (for gdn2 the erase
-    gate [B, T, H, dk]); wgate: gdn2 write gate [B, T, H, dv], else None;
+    gate, for fg2 the channel-wise step size: [B, T, H, dk]); wgate: gdn2
+    write gate [B, T, H, dv], else None;
     g: log-decay, None / [B, T, H] / [B, T, H, dk]; S0: [B, H, dv, dk] or None
     (zero state).  Returns o [B, T, H, dv] and S_T [B, H, dv, dk], float64.
     """
@@ -179,6 +196,13 @@ def delta_fwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None
             raise ValueError("gdn2 needs the write gate")
         o, S = run_recurrence(S, _to_heads(q), _to_heads(k), _to_heads(v), a,
                               erase=_to_heads(beta), write=_to_heads(wgate))
+    elif variant == "fg2":
+        if wgate is not None:
+            raise ValueError("only gdn2 takes a write gate")
+        if np.shape(beta) != (B, T, H, dk):
+            raise ValueError(f"fg2 step sizes must have shape {(B, T, H, dk)}")
+        o, S = run_recurrence(S, _to_heads(q), _to_heads(k), _to_heads(v), a,
+                              keystep=_to_heads(beta))
     else:
         if wgate is not None:
             raise ValueError("only gdn2 takes a write gate")
@@ -286,6 +310,8 @@ def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=
     """
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
+    if variant == "fg2":
+        raise ValueError("no reverse mode for fg2")
     B, T, H, dv = np.shape(v)
     q0 = np.asarray(q, dtype=np.float64)
     Hk = q0.shape[2]

@@ -13,8 +13,9 @@ Recipe (one generator per workload, ``numpy.random.PCG64(seed)``):
   erase logits, then write logits), then the decay logits, then S0;
 * every draw is float32 ``standard_normal``;
 * q and k are divided by their L2 norm per (batch, token, head) in float32;
-* step sizes and split gates are ``sigmoid(z)``; log-decays are
-  ``-softplus(z)`` (so the per-token decay ``exp(g)`` lies in (0, 1));
+* step sizes (per key channel for fg2) and split gates are ``sigmoid(z)``;
+  log-decays are ``-softplus(z)`` (so the per-token decay ``exp(g)`` lies in
+  (0, 1));
 * S0 is ``0.02 * z`` where the workload asks for a random initial state;
 * grouped value heads (``qk_heads`` < H): q and k are drawn with ``qk_heads``
   heads instead of H, in the same draw order;
@@ -34,7 +35,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-VARIANTS = ("deltanet", "gdn", "kda", "gdn2")
+VARIANTS = ("deltanet", "gdn", "kda", "gdn2", "fg2")
 DTYPES = ("f32", "bf16")
 
 
@@ -115,8 +116,9 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
 
     Returns q, k, v, beta, wgate, g following the boundary's argument names:
     for the split-gate form ``beta`` carries the erase gate (last dim dk) and
-    ``wgate`` the write gate (last dim dv); otherwise ``beta`` has shape
-    ``lead`` and ``wgate`` is None.  ``g`` is None for the ungated form,
+    ``wgate`` the write gate (last dim dv); for fg2 ``beta`` is the step size
+    per key channel (last dim dk); otherwise ``beta`` has shape ``lead``; and
+    ``wgate`` is None except for the split-gate form.  ``g`` is None for the ungated form,
     shape ``lead`` for a scalar gate and ``lead + (dk,)`` for channel gates.
     ``gate_scale`` multiplies the log-decays (e.g. 1/16 for weak decay).
     ``qk_heads`` replaces the last entry of ``lead`` for q and k (grouped value
@@ -133,6 +135,9 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
     if variant == "gdn2":
         beta = _sigmoid(rng.standard_normal(lead + (dk,), dtype=np.float32))
         wgate = _sigmoid(rng.standard_normal(lead + (dv,), dtype=np.float32))
+    elif variant == "fg2":
+        beta = _sigmoid(rng.standard_normal(lead + (dk,), dtype=np.float32))
+        wgate = None
     else:
         beta = _sigmoid(rng.standard_normal(lead, dtype=np.float32))
         wgate = None

@@ -29,6 +29,14 @@ the value side, X = w ⊙ V, E = b ⊙ K):
     O = Q^ S^T + M_k X - M_e Y
     S^T <- Diag(e^G_C) S^T + K-^T X - E-^T Y    (E- = E ⊙ e^(G_C - G))
 
+step size per key channel (FG^2-GDN, E = beta ⊙ K): the split form with the
+write along E instead of K and no write gate, i.e. X = V, A_k -> A_e,
+M_k -> M_e and K- -> E-:
+
+    Y = T (K^ S^T + A_e V)
+    O = Q^ S^T + M_e (V - Y)
+    S^T <- Diag(e^G_C) S^T + E-^T (V - Y)
+
 These follow the chunkwise WY description of the Gated DeltaNet-2 abstract
 (thelatestinai.com/papers/2607.07953), derived here from the token update.
 """
@@ -58,9 +66,11 @@ def chunk_fwd(variant, q, k, v, beta=None, wgate=None, g=None, S0=None, chunk=64
         G_tok = np.broadcast_to(_heads(g)[..., None], (N, T, dk))
     else:
         G_tok = _heads(g)
-    split = variant == "gdn2"
+    split = variant in ("gdn2", "fg2")
+    keywrite = variant == "fg2"
     if split:
-        E_all, W_all = _heads(beta), _heads(wgate)
+        E_all = _heads(beta)
+        W_all = None if keywrite else _heads(wgate)
     else:
         Bt = _heads(beta)
     S_T = np.zeros((N, dk, dv)) if S0 is None else np.swapaxes(
@@ -91,13 +101,16 @@ def chunk_fwd(variant, q, k, v, beta=None, wgate=None, g=None, S0=None, chunk=64
             S_T = np.exp(GC[:, 0, :])[:, :, None] * S_T + np.swapaxes(Kb, 1, 2) @ Vt
         else:
             Ec = E_all[:, n0:n1] * Kc
-            X = W_all[:, n0:n1] * Vc
             Ae = np.einsum("nrc,njc,nrjc->nrj", Kc, Ec, diff) * lower
             Me = np.einsum("nrc,njc,nrjc->nrj", Qc, Ec, diff) * lower0
+            Eb = Ec * np.exp(GC - G)
+            if keywrite:
+                X, Ak, Mk, Kb = Vc, Ae, Me, Eb
+            else:
+                X = W_all[:, n0:n1] * Vc
             Tm = np.linalg.inv(eye + Ae)
             Y = Tm @ (XS + Ak @ X)
             O[:, n0:n1] = Qh @ S_T + Mk @ X - Me @ Y
-            Eb = Ec * np.exp(GC - G)
             S_T = (np.exp(GC[:, 0, :])[:, :, None] * S_T + np.swapaxes(Kb, 1, 2) @ X
                    - np.swapaxes(Eb, 1, 2) @ Y)
     o = np.moveaxis(O.reshape(B, H, T, dv), 1, 2)

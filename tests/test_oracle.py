@@ -33,13 +33,17 @@ def _rand_inputs(rng, variant, B, T, H, dk, dv, unit_k=True):
     if variant == "gdn2":
         beta = rng.uniform(0, 1, (B, T, H, dk))
         wgate = rng.uniform(0, 1, (B, T, H, dv))
+    elif variant == "fg2":
+        beta = rng.uniform(0, 1, (B, T, H, dk))
+        wgate = None
     else:
         beta = rng.uniform(0, 1, (B, T, H))
         wgate = None
     g = {"deltanet": None,
          "gdn": -rng.uniform(0, 1, (B, T, H)),
          "kda": -rng.uniform(0, 1, (B, T, H, dk)),
-         "gdn2": -rng.uniform(0, 1, (B, T, H, dk))}[variant]
+         "gdn2": -rng.uniform(0, 1, (B, T, H, dk)),
+         "fg2": -rng.uniform(0, 1, (B, T, H, dk))}[variant]
     S0 = 0.3 * rng.standard_normal((B, H, dv, dk))
     return dict(q=q, k=k, v=v, beta=beta, wgate=wgate, g=g, S0=S0)
 
@@ -88,9 +92,10 @@ def _madd(A, B):
 
 def pin_exact_product_form(seed=0):
     """Exact rationals: S_t = S_0 M_1..M_t + sum_s W_s M_{s+1}..M_t with explicit
-    d_k×d_k transition matrices M_t = Diag(a_t)(I - beta_t k_t k_t^T) (split gates:
-    Diag(a_t)(I - k_t (b_t ⊙ k_t)^T)) and writes W_t = beta_t v_t k_t^T (split:
-    (w_t ⊙ v_t) k_t^T), o_t = S_t q_t.  Must agree exactly."""
+    d_k×d_k transition matrices M_t = Diag(a_t)(I - beta_t k_t k_t^T) (split gates
+    and FG^2-GDN: Diag(a_t)(I - k_t (b_t ⊙ k_t)^T)) and writes W_t = beta_t v_t k_t^T
+    (split: (w_t ⊙ v_t) k_t^T; FG^2-GDN: v_t (b_t ⊙ k_t)^T), o_t = S_t q_t.  Must
+    agree exactly."""
     rng = np.random.default_rng(seed)
 
     def rq(lo=-3, hi=4, den=(1, 2, 3, 4, 5)):
@@ -115,16 +120,21 @@ def pin_exact_product_form(seed=0):
                 if variant == "gdn2":
                     t["b"] = [rpos() for _ in range(dk)]
                     t["w"] = [rpos() for _ in range(dv)]
+                elif variant == "fg2":
+                    t["b"] = [rpos() for _ in range(dk)]
                 else:
                     t["beta"] = rpos()
                 toks.append(t)
             Ms, Ws = [], []
             for t in toks:
                 D = _mat(dk, dk, lambda i, j: t["a"][i] if i == j else F(0))
-                if variant == "gdn2":
+                if variant in ("gdn2", "fg2"):
                     E = _mat(dk, dk, lambda i, j: (F(1) if i == j else F(0))
                              - t["k"][i] * t["b"][j] * t["k"][j])
-                    Wt = _mat(dv, dk, lambda i, j: t["w"][i] * t["v"][i] * t["k"][j])
+                    if variant == "gdn2":
+                        Wt = _mat(dv, dk, lambda i, j: t["w"][i] * t["v"][i] * t["k"][j])
+                    else:
+                        Wt = _mat(dv, dk, lambda i, j: t["v"][i] * t["b"][j] * t["k"][j])
                 else:
                     E = _mat(dk, dk, lambda i, j: (F(1) if i == j else F(0))
                              - t["beta"] * t["k"][i] * t["k"][j])
@@ -147,6 +157,9 @@ def pin_exact_product_form(seed=0):
             if variant == "gdn2":
                 o, S_fin = od.run_recurrence(np.array([S0], dtype=object), arr("q"), arr("k"),
                                              arr("v"), arr("a"), erase=arr("b"), write=arr("w"))
+            elif variant == "fg2":
+                o, S_fin = od.run_recurrence(np.array([S0], dtype=object), arr("q"), arr("k"),
+                                             arr("v"), arr("a"), keystep=arr("b"))
             else:
                 o, S_fin = od.run_recurrence(np.array([S0], dtype=object), arr("q"), arr("k"),
                                              arr("v"), arr("a"), beta=arr("beta"))
@@ -185,7 +198,9 @@ def pin_gate_zero_is_deltanet():
 
 def pin_reductions():
     """KDA with a channel-constant decay is Gated DeltaNet; Gated DeltaNet-2 with
-    b = beta·1 and w = beta·1 is KDA (Gated DeltaNet-2 abstract)."""
+    b = beta·1 and w = beta·1 is KDA (Gated DeltaNet-2 abstract); FG^2-GDN with
+    a channel-constant step size beta·1 is KDA (FG^2-GDN card: the vector
+    generalises KDA's scalar step size)."""
     rng = np.random.default_rng(3)
     x = _rand_inputs(rng, "gdn", 2, 11, 3, 6, 5)
     o_gdn, S_gdn = delta_fwd("gdn", **x)
@@ -200,6 +215,9 @@ def pin_reductions():
     o2, S2 = delta_fwd("gdn2", **{**x, "beta": b, "wgate": w})
     np.testing.assert_allclose(o2, o_kda, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(S2, S_kda, rtol=1e-12, atol=1e-13)
+    o3, S3 = delta_fwd("fg2", **{**x, "beta": b})
+    np.testing.assert_allclose(o3, o_kda, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S3, S_kda, rtol=1e-12, atol=1e-13)
 
 
 def pin_unit_write():
@@ -245,6 +263,8 @@ def pin_orthonormal_keys():
             for s in range(t + 1):
                 if variant == "gdn2":
                     wv = x["wgate"][0, s, 0] * x["v"][0, s, 0]
+                elif variant == "fg2":   # the write along beta_s ⊙ e_s keeps channel s only
+                    wv = x["beta"][0, s, 0, s] * x["v"][0, s, 0]
                 else:
                     wv = x["beta"][0, s, 0] * x["v"][0, s, 0]
                 exp[t] += wv * x["q"][0, t, 0, s] * np.prod(a[s + 1:t + 1, s])
@@ -417,11 +437,40 @@ def pin_efla_limits():
         np.testing.assert_allclose(c[..., h], -np.expm1(-b[..., h] * kap) / kap, rtol=1e-14)
 
 
+def pin_fg2_per_coordinate_step():
+    """One FG^2-GDN token is one gradient step on L(S) = 1/2 ||S k - v||^2 from the
+    decayed state S' with its own step size per key channel (FG^2-GDN card: per-
+    coordinate step sizes as in AdaGrad/Adam): S_1 = S' - (dL/dS at S') Diag(beta),
+    o = S_1 q.  The gradient is taken by central differences, which are exact for a
+    quadratic up to rounding, so the formula of the update is not retyped here."""
+    rng = np.random.default_rng(12)
+    dk, dv = 5, 4
+    x = _rand_inputs(rng, "fg2", 1, 1, 1, dk, dv, unit_k=False)
+    o, S = delta_fwd("fg2", **x)
+    Sp = x["S0"][0, 0] * np.exp(x["g"][0, 0, 0])[None, :]
+    k, v = x["k"][0, 0, 0], x["v"][0, 0, 0]
+
+    def loss(M):
+        r = M @ k - v
+        return 0.5 * float(r @ r)
+
+    grad = np.zeros((dv, dk))
+    h = 1e-3
+    for i in range(dv):
+        for j in range(dk):
+            E = np.zeros((dv, dk))
+            E[i, j] = h
+            grad[i, j] = (loss(Sp + E) - loss(Sp - E)) / (2 * h)
+    expect = Sp - grad * x["beta"][0, 0, 0][None, :]
+    np.testing.assert_allclose(S[0, 0], expect, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(o[0, 0, 0], expect @ x["q"][0, 0, 0], rtol=1e-9, atol=1e-11)
+
+
 PINS = [pin_hand_worked, pin_exact_product_form, pin_beta_zero, pin_gate_zero_is_deltanet,
         pin_reductions, pin_unit_write, pin_orthonormal_keys, pin_one_token_by_hand,
         pin_linearity, pin_norm_bound, pin_split_sequence, pin_decode_is_one_token,
         pin_grouped_heads_one_token, pin_grouped_heads_share, pin_efla_exact_flow,
-        pin_efla_limits]
+        pin_efla_limits, pin_fg2_per_coordinate_step]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -435,7 +484,7 @@ def test_pin(pin):
 def _mutant(kind):
     """A copy of the oracle's recurrence with one plausible mistake planted."""
 
-    def rec(S0, q, k, v, a, beta=None, erase=None, write=None):
+    def rec(S0, q, k, v, a, beta=None, erase=None, write=None, keystep=None):
         split = erase is not None
         S = np.array(S0, copy=True)
         N, T, _ = q.shape
@@ -460,6 +509,18 @@ def _mutant(kind):
                 if kind == "write_gate_dropped":
                     wv = v[:, t, :]
                 Snew = Sp + upd + wv[:, :, None] * kt[:, None, :]
+            elif keystep is not None:
+                ek = keystep[:, t, :] * kt
+                res = v[:, t, :] - r
+                if kind == "sign":
+                    res = v[:, t, :] + r
+                if kind == "keystep_write_along_k":
+                    Snew = Sp - r[:, :, None] * ek[:, None, :] + v[:, t, :, None] * kt[:, None, :]
+                elif kind == "keystep_read_scaled":
+                    res = v[:, t, :] - (Sp @ ek[:, :, None])[:, :, 0]
+                    Snew = Sp + res[:, :, None] * ek[:, None, :]
+                else:
+                    Snew = Sp + res[:, :, None] * ek[:, None, :]
             else:
                 res = v[:, t, :] - r
                 if kind == "sign":
@@ -485,7 +546,7 @@ def _mutant(kind):
 
 MUTANTS = ["decay_after_read", "decay_rows", "erase_swapped", "write_gate_dropped", "sign",
            "beta_dropped_on_read", "transposed_write", "readout_before_write",
-           "readout_decayed_only"]
+           "readout_decayed_only", "keystep_write_along_k", "keystep_read_scaled"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)
