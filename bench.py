@@ -22,6 +22,7 @@ The JSON line also carries
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -45,7 +46,7 @@ def prefill_bytes(variant, B, T, H, dk, dv, elem=2, with_state_in=False, with_st
     With Hk query/key heads (grouped value heads) q and k count Hk heads."""
     Hk = H if Hk is None else Hk
     per_head = {"deltanet": dv + 1, "gdn": dv + 2, "kda": dk + dv + 1,
-                "gdn2": 2 * dk + 2 * dv}[variant] + dv      # v, gates, o
+                "gdn2": 2 * dk + 2 * dv, "fg2": 2 * dk + dv}[variant] + dv      # v, gates, o
     state = 4 * dv * dk * (int(with_state_in) + int(with_state_out))
     return B * T * elem * (H * per_head + Hk * 2 * dk) + B * H * state
 
@@ -73,7 +74,8 @@ def efla_bytes(B, T, H, Hk, dk, elem=2):
 def prefill_flops(variant, B, T, H, dk, dv, C=64):
     """Algorithmic flops of one forward with chunk length C (triangular blocks
     counted once): 6 dk dv + 3 C dk + 2 C dv + C^2/3 per token and head for one
-    step size, 8 dk dv + 5 C dk + 4 C dv + C^2/3 for split gates."""
+    step size (FG^2-GDN counted the same way), 8 dk dv + 5 C dk + 4 C dv + C^2/3
+    for split gates."""
     if variant == "gdn2":
         per = 8 * dk * dv + 5 * C * dk + 4 * C * dv + C * C / 3.0
     else:
@@ -277,9 +279,14 @@ def main():
     if not args.no_other:
         # the other forward workloads: parity-test shapes, reported beside the headline
         others = []
-        for name, sub_c in [("deltanet_fp32_t256_d64", 16), ("kda_bf16_b2_h16_t8192_d128", 32),
-                            ("gdn2_bf16_b1_h16_t32768_d128", 32)]:
+        for name, sub_c, form in [("deltanet_fp32_t256_d64", 16, None),
+                                  ("kda_bf16_b2_h16_t8192_d128", 32, None),
+                                  ("gdn2_bf16_b1_h16_t32768_d128", 32, None),
+                                  ("kda_bf16_b2_h16_t8192_d128", 32, "fg2")]:
             wo = WORKLOADS[name]
+            if form is not None:   # another form on the same shape and seed
+                wo = dataclasses.replace(wo, variant=form)
+                name = name.replace(name.split("_")[0], form, 1)
             t_s, _, _ = time_forward(wo, 5, 2, 2, stream)
             elem = 4 if wo.dtype == "f32" else 2
             nb = prefill_bytes(wo.variant, wo.B, wo.T, wo.H, wo.dk, wo.dv, elem=elem,

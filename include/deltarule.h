@@ -9,6 +9,7 @@
  *   r  = S' k_t                                read the memory at the key
  *   S  = S' + beta_t (v_t - r) k_t^T           DR_DELTANET, DR_GDN, DR_KDA
  *   S  = S' - r (b_t ⊙ k_t)^T + (w_t ⊙ v_t) k_t^T      DR_GDN2
+ *   S  = S' + (v_t - r) (beta_t ⊙ k_t)^T                 DR_FG2 (beta_t per key channel)
  *   o_t = S q_t                                readout after the write
  *
  * Sources (web pages):
@@ -21,6 +22,13 @@
  *  - split channel-wise erase gate b_t and write gate w_t, reducing to KDA when
  *    both are the same scalar: Gated DeltaNet-2 abstract.  The placement of b on
  *    the key side of the erase term is this library's reading of that abstract;
+ *  - a channel-wise step size (FG^2-GDN): "Delta-Rule Linear Attention" topic
+ *    page, FG^2-GDN card, which likens it to per-coordinate optimizers.  Taking
+ *    the key channels as the coordinates of the gradient step on
+ *    1/2 ||S' k - v||^2 gives the DR_FG2 line above, which equals DR_KDA when
+ *    beta_t is a constant vector; that choice of axis is this library's reading.
+ *    The card's FG^2-GDN+ (separate key-side erase and value-side write scales)
+ *    is DR_GDN2;
  *  - the update is affine in the previous memory, so chunks of tokens can be
  *    evaluated in parallel (DeltaTTT summary, §2), by a chunkwise WY algorithm
  *    with channel-wise decay absorbed into the erase factors (Gated DeltaNet-2
@@ -33,8 +41,8 @@
  *    and row-major with the shapes given below (no strides).  Every pointer
  *    must be 16-byte aligned.  The caller owns every buffer, and no per-call
  *    state is kept.  The only memory the library allocates is the temporary
- *    workspace of delta_fwd for DR_KDA and DR_GDN2 with DR_BF16 operands:
- *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2: 50 KiB) for d_k = 128,
+ *    workspace of delta_fwd for DR_KDA, DR_GDN2 and DR_FG2 with DR_BF16 operands:
+ *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2, DR_FG2: 50 KiB) for d_k = 128,
  *    21 KiB (29 KiB) for d_k = 64, taken from a library-owned stream-ordered
  *    memory pool of the current device and returned to it on the call's
  *    stream after use; the pool keeps freed memory for reuse until the
@@ -60,13 +68,14 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 2
+#define DR_ABI_VERSION 3
 
 typedef enum {
     DR_DELTANET = 0, /* a = 1: no decay, g must be NULL                          */
     DR_GDN = 1,      /* scalar decay per (token, head): g is [B,T,H]             */
     DR_KDA = 2,      /* channel-wise decay: g is [B,T,H,d_k]                     */
-    DR_GDN2 = 3      /* channel-wise decay + erase gate b + write gate w         */
+    DR_GDN2 = 3,     /* channel-wise decay + erase gate b + write gate w         */
+    DR_FG2 = 4       /* channel-wise decay + step size per key channel (FG^2-GDN) */
 } dr_variant;
 
 typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
@@ -108,17 +117,18 @@ typedef struct {
  *   q, k   [B, T, H_k, d_k] dtype (H_k = H unless desc->H_k says otherwise)
  *   v      [B, T, H, d_v]   dtype
  *   beta   DR_DELTANET/GDN/KDA: step size beta [B, T, H];
- *          DR_GDN2: erase gate b [B, T, H, d_k]                         dtype
+ *          DR_GDN2: erase gate b [B, T, H, d_k];
+ *          DR_FG2: step size per key channel [B, T, H, d_k]              dtype
  *   wgate  DR_GDN2: write gate w [B, T, H, d_v]; otherwise must be NULL  dtype
  *   g      log-decay log(a) <= 0: DR_DELTANET must be NULL; DR_GDN
- *          [B, T, H]; DR_KDA/DR_GDN2 [B, T, H, d_k]                       dtype
+ *          [B, T, H]; DR_KDA/DR_GDN2/DR_FG2 [B, T, H, d_k]                dtype
  *   S0     initial state [B, H, d_v, d_k] fp32; NULL means zero
  *   o      output [B, T, H, d_v] dtype (written); must not overlap any input
  *   S_T    final state [B, H, d_v, d_k] fp32 (written); NULL if not wanted;
  *          may be the same pointer as S0 (in-place update) but must not
  *          otherwise overlap an input
  *
- * Channel-wise decays (DR_KDA, DR_GDN2) are evaluated with exponents taken
+ * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) are evaluated with exponents taken
  * relative to the boundaries of 16-token blocks: the log-decay of one channel
  * summed over any 16 consecutive tokens must stay above about -85 (a decay
  * factor of e^-85), otherwise a split factor leaves the fp32 range and the
@@ -132,7 +142,8 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
  * delta_decode — one token per sequence, state updated in place.
  *
  *   desc->T must be 1; shapes as delta_fwd with the T axis removed:
- *   q, k [B, H_k, d_k]; v [B, H, d_v]; beta [B, H] (DR_GDN2: b [B, H, d_k]);
+ *   q, k [B, H_k, d_k]; v [B, H, d_v]; beta [B, H] (DR_GDN2: b, DR_FG2: the
+ *   step sizes, [B, H, d_k]);
  *   wgate [B, H, d_v] (DR_GDN2 only); g NULL / [B, H] / [B, H, d_k];
  *   S      state [B, H, d_v, d_k] fp32, read and overwritten in place
  *   o      output [B, H, d_v] dtype; must not overlap any input or S
@@ -156,7 +167,8 @@ dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const 
  * beta.  Decay, where the variant has one, is applied before the write as usual.
  *
  *   desc     variant DR_DELTANET, DR_GDN or DR_KDA (a single step size per
- *            token; DR_GDN2 returns DR_E_UNSUPPORTED); T = 1 serves decode
+ *            token; DR_GDN2 and DR_FG2 return DR_E_UNSUPPORTED); T = 1 serves
+ *            decode
  *   k        [B, T, H_k, d_k] dtype
  *   beta     [B, T, H] dtype, beta >= 0
  *   beta_eff [B, T, H] dtype (written, rounded to nearest even for bf16);
@@ -174,7 +186,8 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * a backward that keeps training chunkwise-parallel).  The forward states are
  * recomputed from the inputs; nothing from a delta_fwd call is needed.
  *
- *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd
+ *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd; DR_FG2
+ *          returns DR_E_UNSUPPORTED (no backward for it)
  *   dO     [B, T, H, d_v] dtype: gradient arriving at o
  *   dS_T   [B, H, d_v, d_k] fp32: gradient arriving at the final state; NULL = 0
  *   dq, dk [B, T, H_k, d_k], dv [B, T, H, d_v]                     dtype (written)

@@ -39,7 +39,7 @@ struct Sizes {
 
 dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
     if (d == nullptr) return DR_E_NULLPTR;
-    if (d->variant < DR_DELTANET || d->variant > DR_GDN2) return DR_E_UNSUPPORTED;
+    if (d->variant < DR_DELTANET || d->variant > DR_FG2) return DR_E_UNSUPPORTED;
     if (d->dtype != DR_F32 && d->dtype != DR_BF16) return DR_E_UNSUPPORTED;
     if (d->B < 1 || d->H < 1 || d->T < 1) return DR_E_SHAPE;
     if (decode && d->T != 1) return DR_E_SHAPE;
@@ -53,7 +53,7 @@ dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
         return DR_E_SHAPE;
     sz->qk = static_cast<int64_t>(d->B) * d->T * sz->Hk * d->d_k;
     sz->v = tok * d->d_v;
-    sz->beta = d->variant == DR_GDN2 ? tok * d->d_k : tok;
+    sz->beta = (d->variant == DR_GDN2 || d->variant == DR_FG2) ? tok * d->d_k : tok;
     sz->wgate = d->variant == DR_GDN2 ? tok * d->d_v : 0;
     sz->g = d->variant == DR_DELTANET ? 0 : (d->variant == DR_GDN ? tok : tok * d->d_k);
     sz->state = static_cast<int64_t>(d->B) * d->H * d->d_v * d->d_k;
@@ -186,7 +186,7 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
         if (st != DR_OK) return st;
-        if (desc->variant == DR_GDN2) return DR_E_UNSUPPORTED;
+        if (desc->variant == DR_GDN2 || desc->variant == DR_FG2) return DR_E_UNSUPPORTED;
         if (k == nullptr || beta == nullptr || beta_eff == nullptr) return DR_E_NULLPTR;
         if (!aligned16(k) || !aligned16(beta) || !aligned16(beta_eff)) return DR_E_ALIGN;
         const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
@@ -213,6 +213,7 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
         if (st != DR_OK) return st;
+        if (desc->variant == DR_FG2) return DR_E_UNSUPPORTED;
         if (q == nullptr || k == nullptr || v == nullptr || dO == nullptr || dq == nullptr ||
             dk == nullptr || dv == nullptr || dbeta == nullptr)
             return DR_E_NULLPTR;

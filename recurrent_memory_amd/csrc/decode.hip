@@ -17,6 +17,9 @@
 //                      o_i = s_i + u_i (k·q)
 //   split gates:       x_i = w_i v_i;  S_i = S'_i - r_i (b ⊙ k) + x_i k
 //                      o_i = s_i - r_i ((b ⊙ k)·q) + x_i (k·q)
+//   step size per key channel (FG^2-GDN):
+//                      u_i = v_i - r_i;  S_i = S'_i + u_i (beta ⊙ k)
+//                      o_i = s_i + u_i ((beta ⊙ k)·q)
 // which is o = S q read after the write, without a second pass over S.
 #include "common.h"
 #include "kernels.h"
@@ -55,11 +58,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
         } else {
             aa[c] = load_elem<E>(p.g, tok * DK + c0 + c);
         }
-        if constexpr (VAR == 3) bk[c] = load_elem<E>(p.beta, tok * DK + c0 + c);
+        if constexpr (VAR >= 3) bk[c] = load_elem<E>(p.beta, tok * DK + c0 + c);
         else bk[c] = 0.0f;
     }
     float beta_s = 0.f;
-    if constexpr (VAR != 3) beta_s = load_elem<E>(p.beta, tok);
+    if constexpr (VAR < 3) beta_s = load_elem<E>(p.beta, tok);
     float st[RPG][CPL];
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         aa[c] = VAR == 0 ? 1.0f : __expf(aa[c]);
-        if constexpr (VAR == 3) bk[c] *= kk[c];
+        if constexpr (VAR >= 3) bk[c] *= kk[c];
     }
     float kq = 0.f, bkq = 0.f;
 #pragma unroll
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
         bkq += bk[c] * qq[c];
     }
     kq = half_wave_sum(kq);
-    if constexpr (VAR == 3) bkq = half_wave_sum(bkq);
+    if constexpr (VAR >= 3) bkq = half_wave_sum(bkq);
 
     // Rows in four batches: a batch is reduced, updated and written back while
     // the loads of the later batches are still arriving.
@@ -142,6 +145,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
                 coef_u = r;
                 coef_x = x;
                 o = s - r * bkq + x * kq;
+            } else if constexpr (VAR == 4) {
+                const float u = vi - r;
+                coef_u = u;
+                o = s + u * bkq;
             } else {
                 const float u = beta_s * (vi - r);
                 coef_u = u;
@@ -161,6 +168,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 if constexpr (VAR == 3) out[c] = st[j][c] - u * bk[c] + x * kk[c];
+                else if constexpr (VAR == 4) out[c] = st[j][c] + u * bk[c];
                 else out[c] = st[j][c] + u * kk[c];
             }
             if constexpr (CPL == 4) {
@@ -195,7 +203,8 @@ hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_
         case 0: return launch_decode_dtype<0>(dtype, a, s);
         case 1: return launch_decode_dtype<1>(dtype, a, s);
         case 2: return launch_decode_dtype<2>(dtype, a, s);
-        default: return launch_decode_dtype<3>(dtype, a, s);
+        case 3: return launch_decode_dtype<3>(dtype, a, s);
+        default: return launch_decode_dtype<4>(dtype, a, s);
     }
 }
 

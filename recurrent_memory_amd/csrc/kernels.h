@@ -13,7 +13,8 @@ struct FwdArgs {
     const void* q;
     const void* k;
     const void* v;
-    const void* beta;   // beta [B,T,H], or the erase gate [B,T,H,dk] (split gates)
+    const void* beta;   // beta [B,T,H], or [B,T,H,dk]: the erase gate (split gates)
+                        // or the step size per key channel (keywrite)
     const void* wgate;  // write gate [B,T,H,dv] (split gates) or nullptr
     const void* g;      // log-decay: nullptr, [B,T,H] or [B,T,H,dk]
     const float* S0;    // [B,H,dv,dk] or nullptr (zero state)
@@ -21,6 +22,9 @@ struct FwdArgs {
     float* ST;          // [B,H,dv,dk] or nullptr
     int Hk;             // query/key heads (divides H): q, k are [B,T,Hk,dk] and
                         // value head h reads query/key head h / (H / Hk)
+    int keywrite = 0;   // split-gate kernels only: 1 = FG^2-GDN, the residual is
+                        // written along E = beta ⊙ k and there is no write gate
+                        // (the split form with W = V, A_k = A_e, M_k = M_e, Kb = Eb)
 };
 
 struct DecodeArgs {

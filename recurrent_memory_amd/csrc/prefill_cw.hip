@@ -33,6 +33,10 @@
 //   O = Y + M_k W - M_e Y~,  M_k = Tril(Qh Kx^T), M_e = Tril(Qh Ex^T)
 //   S^T <- Diag(e^G_C) S^T + Kb^T W - Eb^T Y~
 // (Kx, Ex: Ki/Ei on diagonal blocks, Ke/Ee below them.)
+// A step size per key channel (FG^2-GDN: the residual is written along
+// E = beta ⊙ K, "Delta-Rule Linear Attention" topic page, FG^2-GDN card) is the
+// split form with the write along E and no write gate: W = V, and A_k, M_k
+// and Kb are replaced by A_e, M_e and Eb (FwdArgs::keywrite).
 //
 // With bf16 operands the decay-scaled queries are kept as a hi + lo pair of
 // bf16 values (two MFMAs per query-side product): a single rounding of
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
 #pragma unroll
             for (int j = 0; j < NPV; ++j) {
                 pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + vb + voff[j]);
-                if constexpr (SPLIT) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + vb + voff[j]);
+                if (SPLIT && !p.keywrite) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + vb + voff[j]);
             }
         } else {
 #pragma unroll
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
                 const int row = min(min(pidx / VPR, C - 1), last), cc = pidx % VPR;
                 const int64_t off = ((tokb + row) * H + h) * DV + vt * kVTCW + cc * EPC;
                 pv[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.v) + off);
-                if constexpr (SPLIT) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + off);
+                if (SPLIT && !p.keywrite) pw[j] = *reinterpret_cast<const uint4*>(static_cast<const S*>(p.wgate) + off);
             }
         }
         if constexpr (!SPLIT) {
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
                 if (pidx < C * VPR) {
                     const int row = pidx / VPR, cc = pidx % VPR;
                     uint4 v = sel(row < Cn, pv[j]);
-                    if constexpr (SPLIT) {
+                    if (SPLIT && !p.keywrite) {
                         // W = w ⊙ v, rounded once to the operand dtype
                         const S* ve = reinterpret_cast<const S*>(&v);
                         const uint4 wv = pw[j];
@@ -392,6 +396,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
                     st2(sEi, r, ev0 * fi0, ev1 * fi1);
                     st2(sEb, r, ev0 * fc0, ev1 * fc1);
                     if (my_block < NB - 1) st2(sEe, r, ev0 * fe0, ev1 * fe1);
+                    if (p.keywrite) st2(sKb, r, ev0 * fc0, ev1 * fc1);   // Kb = Eb
                 }
             }
             if (rq == 0) {
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
                     int Rr, Jr;
                     task_rj(tix, Rr, Jr);
                     const bool useQ = mat == 1 || mat == 3;
-                    const bool useE = SPLIT && (mat == 0 || mat == 3);
+                    const bool useE = SPLIT && (mat == 0 || mat == 3 || p.keywrite);
                     const S* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
                     const S* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
                     const S* brow = bsrc + (16 * Jr + c) * L::LDK;
@@ -649,11 +654,15 @@ hipError_t launch_cw_dims(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// variant 2: one step size (KDA); 3: split gates (Gated DeltaNet-2); 4: a step
+// size per key channel (FG^2-GDN), run as the split form with keywrite set
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
     if (dtype == 1) return launch_fwd_channel_two_pass(variant, a, s);
     if (variant == 2)
         return dtype == 0 ? launch_cw_dims<2, F32>(a, s) : launch_cw_dims<2, BF16>(a, s);
-    return dtype == 0 ? launch_cw_dims<3, F32>(a, s) : launch_cw_dims<3, BF16>(a, s);
+    FwdArgs b = a;
+    b.keywrite = variant == 4 ? 1 : 0;
+    return dtype == 0 ? launch_cw_dims<3, F32>(b, s) : launch_cw_dims<3, BF16>(b, s);
 }
 
 }  // namespace dr

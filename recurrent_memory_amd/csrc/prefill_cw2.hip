@@ -17,6 +17,9 @@
 //   A_e = StrictTril(Kh Ex^T), A_k = StrictTril(Kh Kx^T), T = (I + A_e)^-1
 //   Z = X + A_k W, Y~ = T Z, O = Y + M_k W - M_e Y~
 //   S^T <- Diag(e^G_C) S^T + Kb^T W - Eb^T Y~
+// A step size per key channel (FG^2-GDN, FwdArgs::keywrite) is the split form
+// with the write along E = beta ⊙ K and no write gate: pass 1 stores A_e, M_e
+// and Eb where the split form has A_k, M_k and Kb, and pass 2 takes W = V.
 //
 // Everything above except X, Y and the state lines is the same for every
 // value tile of a head, and it is most of the work.  Pass 1 computes it once
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
                 st2(sEi, r, ev0 * fi0, ev1 * fi1);
                 st2(sEb, r, ev0 * fc0, ev1 * fc1);
                 if (my_block == 0) st2(sEe, r, ev0 * fe0, ev1 * fe1);
+                if (p.keywrite) st2(sKb, r, ev0 * fc0, ev1 * fc1);   // Kb = Eb
             }
         }
         if (rq == 0) {
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
                 int Rr, Jr;
                 task_rj(tix, Rr, Jr);
                 const bool useQ = mat == 1 || mat == 3;
-                const bool useE = SPLIT && (mat == 0 || mat == 3);
+                const bool useE = SPLIT && (mat == 0 || mat == 3 || p.keywrite);
                 const uint16_t* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
                 const uint16_t* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
                 const uint16_t* brow = bsrc + (16 * Jr + c) * L::LDK;
@@ -545,7 +549,11 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
         const int t = min(n * kC2 + row, T - 1);
         const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * DV + vc0 + 8 * (lane & 1);
         pv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + off);
-        if constexpr (SPLIT) pw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.wgate) + off);
+        if constexpr (SPLIT) {
+            // no write gate (keywrite): w = 1, so W = V exactly
+            pw = p.keywrite ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
+                            : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.wgate) + off);
+        }
     };
     const int vvo = (4 * g + (c >> 2)) * LDV + 4 * (c & 3);   // transpose reads of the staged rows
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -813,7 +821,10 @@ hipError_t workspace_pool(hipMemPool_t* pool) {
 }
 
 hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t s) {
-    return variant == 2 ? launch_two_pass_dims<false>(a, s) : launch_two_pass_dims<true>(a, s);
+    if (variant == 2) return launch_two_pass_dims<false>(a, s);
+    FwdArgs b = a;
+    b.keywrite = variant == 4 ? 1 : 0;
+    return launch_two_pass_dims<true>(b, s);
 }
 
 }  // namespace dr

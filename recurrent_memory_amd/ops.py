@@ -19,8 +19,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltarule.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "deltarule.h")
 
-ABI_VERSION = 2   # DR_ABI_VERSION of the header this binding follows
-VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3}
+ABI_VERSION = 3   # DR_ABI_VERSION of the header this binding follows
+VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3, "fg2": 4}
+# forms whose beta is one value per key channel (the erase gate, or the step sizes)
+_CHANNEL_BETA = ("gdn2", "fg2")
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "DR_OK", 1: "DR_E_NULLPTR", 2: "DR_E_SHAPE", 3: "DR_E_UNSUPPORTED",
           4: "DR_E_ALIGN", 5: "DR_E_DEVICE", 6: "DR_E_LAUNCH", 7: "DR_E_ALIAS"}
@@ -126,7 +128,7 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check("q", q, (B, T, Hk, dk), dt, dev)
     _check("k", k, (B, T, Hk, dk), dt, dev)
     _check("v", v, (B, T, H, dv), dt, dev)
-    _check("beta", beta, (B, T, H, dk) if variant == "gdn2" else (B, T, H), dt, dev)
+    _check("beta", beta, (B, T, H, dk) if variant in _CHANNEL_BETA else (B, T, H), dt, dev)
     if variant == "gdn2":
         _check("wgate", wgate, (B, T, H, dv), dt, dev)
     elif wgate is not None:
@@ -168,7 +170,7 @@ def delta_decode(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     _check("q", q, (B, Hk, dk), dt, dev)
     _check("k", k, (B, Hk, dk), dt, dev)
     _check("v", v, (B, H, dv), dt, dev)
-    _check("beta", beta, (B, H, dk) if variant == "gdn2" else (B, H), dt, dev)
+    _check("beta", beta, (B, H, dk) if variant in _CHANNEL_BETA else (B, H), dt, dev)
     if variant == "gdn2":
         _check("wgate", wgate, (B, H, dv), dt, dev)
     elif wgate is not None:
@@ -236,6 +238,8 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
+    if variant == "fg2":
+        raise ValueError("no backward for fg2")
     bshape = (B, T, H, dk) if variant == "gdn2" else (B, T, H)
     for name, t, shape in (("q", q, (B, T, Hk, dk)), ("k", k, (B, T, Hk, dk)), ("v", v, (B, T, H, dv)),
                            ("beta", beta, bshape), ("dO", dO, (B, T, H, dv))):

@@ -25,7 +25,7 @@ def test_exports_every_header_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib.dr_abi_version() == ops.ABI_VERSION == 2
+    assert lib.dr_abi_version() == ops.ABI_VERSION == 3
     assert lib.dr_status_str(0) == b"ok"
     assert lib.dr_status_str(99) == b"unknown status"
     for s in range(8):
@@ -51,7 +51,7 @@ def dec(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5],
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(variant=4), DR_E_UNSUPPORTED), (dict(variant=-1), DR_E_UNSUPPORTED),
+    (dict(variant=5), DR_E_UNSUPPORTED), (dict(variant=-1), DR_E_UNSUPPORTED),
     (dict(dtype=2), DR_E_UNSUPPORTED), (dict(d_k=96), DR_E_UNSUPPORTED),
     (dict(d_v=256), DR_E_UNSUPPORTED), (dict(chunk=32), DR_E_UNSUPPORTED),
     (dict(B=0), DR_E_SHAPE), (dict(T=0), DR_E_SHAPE), (dict(H=-1), DR_E_SHAPE),
@@ -75,6 +75,18 @@ def test_null_descriptor_and_pointers():
 def test_arguments_the_variant_does_not_take():
     assert fwd(desc(variant=0)) == DR_E_UNSUPPORTED            # decay given to the ungated form
     assert fwd(desc(variant=1), wgate=FAKE[4]) == DR_E_UNSUPPORTED
+    assert fwd(desc(variant=4), wgate=FAKE[4]) == DR_E_UNSUPPORTED   # FG^2-GDN has no write gate
+    assert dec(desc(variant=4, T=1), wgate=FAKE[4]) == DR_E_UNSUPPORTED
+
+
+def test_channel_step_sizes_are_sized_per_key_channel():
+    """For FG^2-GDN beta spans B*T*H*d_k elements: an output over its last 16 bytes
+    is rejected (it would lie past beta with one step size per token)."""
+    d = desc(variant=4, T=64, B=1)
+    inside = ctypes.c_void_p(FAKE[3].value + 1 * 64 * 3 * 128 * 2 - 16)
+    assert fwd(d, o=inside) == DR_E_ALIAS
+    inside_scalar = ctypes.c_void_p(FAKE[3].value + 1 * 64 * 3 * 2 - 16)
+    assert fwd(desc(variant=2, T=64, B=1), o=inside_scalar) == DR_E_ALIAS
 
 
 def test_alignment():
@@ -102,6 +114,7 @@ def test_efla_validation():
     assert efla(desc(), k=None) == DR_E_NULLPTR
     assert efla(desc(), out=None) == DR_E_NULLPTR
     assert efla(desc(variant=3)) == DR_E_UNSUPPORTED            # split gates have no single step
+    assert efla(desc(variant=4)) == DR_E_UNSUPPORTED            # nor do per-channel step sizes
     assert efla(desc(H_k=2)) == DR_E_SHAPE
     assert efla(desc(), beta=ctypes.c_void_p(FAKE[3].value + 2)) == DR_E_ALIGN
     assert efla(desc(), out=FAKE[1]) == DR_E_ALIAS              # beta_eff over k
@@ -139,6 +152,7 @@ def test_bwd_validation():
     assert bwd(desc(variant=3)) == DR_E_NULLPTR                 # split gates need the write gate
     assert bwd(desc(variant=3), wgate=FAKE[6]) == DR_E_NULLPTR  # ... and its gradient
     assert bwd(desc(variant=1), dwgate=FAKE[6]) == DR_E_UNSUPPORTED
+    assert bwd(desc(variant=4)) == DR_E_UNSUPPORTED             # no backward for FG^2-GDN
     assert bwd(desc(), dq=FAKE[0]) == DR_E_ALIAS                # dq over q
     assert bwd(desc(), dv=FAKE[8]) == DR_E_ALIAS                # dv over dk
     assert bwd(desc(), dS0=ctypes.c_void_p(FAKE[6].value + 4)) == DR_E_ALIGN

@@ -37,7 +37,7 @@ def _oracle_steps(variant, d, n_steps, heads=None):
     return outs, S
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gdn", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["deltanet", "gdn", "kda", "gdn2", "fg2"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 def test_decode_small(variant, dtype, dk, dv):

@@ -1,4 +1,6 @@
 """Chunkwise forward on the GPU against the token-by-token oracle."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs
 
 pytestmark = pytest.mark.gpu
 
-BUILT_VARIANTS = ["deltanet", "gdn", "kda", "gdn2"]
+BUILT_VARIANTS = ["deltanet", "gdn", "kda", "gdn2", "fg2"]
 
 
 def _check(variant, dtype, x, tol=None, **kw):
@@ -67,12 +69,14 @@ def test_gdn_bf16_workload_full_sampled_heads():
 
 
 @pytest.mark.parametrize("name,variant,n_sample", [("kda_bf16_b2_h16_t8192_d128", "kda", 4),
-                                                    ("gdn2_bf16_b1_h16_t32768_d128", "gdn2", 2)])
+                                                    ("gdn2_bf16_b1_h16_t32768_d128", "gdn2", 2),
+                                                    ("kda_bf16_b2_h16_t8192_d128", "fg2", 2)])
 def test_channel_decay_workloads_full_sampled_heads(name, variant, n_sample):
-    """KDA and Gated DeltaNet-2 workloads at full size: every output is computed on
-    the GPU; the oracle checks sampled (batch, head) sequences end to end."""
-    w = WORKLOADS[name]
-    announce("prefill_full", w.name)
+    """KDA and Gated DeltaNet-2 workloads at full size (FG^2-GDN at the KDA shape):
+    every output is computed on the GPU; the oracle checks sampled (batch, head)
+    sequences end to end."""
+    w = dataclasses.replace(WORKLOADS[name], variant=variant)
+    announce("prefill_full", w.name, variant)
     x = make_forward_inputs(w)
     o, S = gpu_fwd(variant, x, "bf16")
     rng = np.random.default_rng(2)
@@ -100,7 +104,21 @@ def test_gdn2_reduces_to_kda_on_gpu(dtype):
     assert slice_rel_err(S2, S_kda, (0, 1)) <= tol
 
 
-@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fg2_reduces_to_kda_on_gpu(dtype):
+    """FG^2-GDN with the step size beta repeated over the key channels reproduces KDA."""
+    announce("fg2_reduction", dtype)
+    w = Workload("t", "kda", dtype, B=2, H=3, T=300, dk=128, dv=128, random_s0=True, seed=14)
+    x = make_forward_inputs(w, gate_scale=1 / 4)
+    o_kda, S_kda = gpu_fwd("kda", x, dtype)
+    x2 = {**x, "beta": np.repeat(x["beta"][..., None], 128, axis=-1)}
+    o2, S2 = gpu_fwd("fg2", x2, dtype)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert slice_rel_err(o2, o_kda, (0, 2)) <= tol
+    assert slice_rel_err(S2, S_kda, (0, 1)) <= tol
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
 def test_channel_decay_strong_gates(variant):
     """Per-channel log-decays down to -4 per token (decay e^-4, so up to -64 summed
     over a 16-token block): the split exponentials stay inside the fp32 range
