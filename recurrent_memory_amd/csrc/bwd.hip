@@ -310,6 +310,22 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     }
 }
 
+// Workgroup -> (head, value tile) of the two chain kernels.  Workgroups are
+// dispatched round-robin over the 8 XCDs; the NVT value tiles of one head get
+// ids 8 apart, so they run on the same XCD and share its L2 for the chunk
+// records they all read (with tiles of one head on different XCDs every tile
+// fetched the records from HBM).  The grid is chain_grid(); ids past the last
+// head return at once.
+__device__ __forceinline__ bool chain_block(const BwdArgs& p, int NVT, int& bh, int& i0) {
+    const int x = blockIdx.x, groups = (p.B * p.H + 7) / 8;
+    bh = (x % 8) * groups + x / (8 * NVT);
+    i0 = ((x / 8) % NVT) * kBVT;
+    return bh < p.B * p.H;
+}
+inline unsigned chain_grid(const BwdArgs& a, int DV) {
+    return static_cast<unsigned>((a.B * a.H + 7) / 8) * 8u * static_cast<unsigned>(DV / kBVT);
+}
+
 // ------------------------------------------------------ 2. forward state chain
 // Single step size:  Vt = U - W S^T,   S = S Diag(gamma) + Vt^T Kbar.
 // Split gates:       Y = Ut + W S^T,   S = S Diag(gamma) - Y^T Ebar + X^T Kbar.
@@ -329,7 +345,8 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     __shared__ __attribute__((aligned(16))) float sXt[SPLIT ? kBC * SV : 4];
     __shared__ float sGam[DK];
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / NVT, i0 = (blockIdx.x % NVT) * kBVT;
+    int bh, i0;
+    if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
     for (int e = tid; e < kBVT * DK; e += kBT) {
         const int i = e / DK, c = e % DK;
@@ -454,7 +471,8 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     __shared__ __attribute__((aligned(16))) float sQh[kBC * SB];
     __shared__ float sGam[DK];
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / NVT, i0 = (blockIdx.x % NVT) * kBVT;
+    int bh, i0;
+    if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
     for (int e = tid; e < kBVT * DK; e += kBT) {
         const int i = e / DK, c = e % DK;
@@ -1422,7 +1440,7 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
     e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
     if (e != hipSuccess) return e;
     const dim3 blk(kBT);
-    const unsigned chains = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (DV / kBVT);
+    const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
     if (e == hipSuccess) {
@@ -1510,7 +1528,7 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
     if (e != hipSuccess) return e;
     const dim3 blk(kBT);
-    const unsigned chains = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H) * (DV / kBVT);
+    const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
     if (e == hipSuccess) {
