@@ -344,3 +344,79 @@ def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=
         dgc = _from_heads(gr["da"] * a, B, H)          # d/dg of exp(g), per channel
         out["dg"] = dgc.sum(axis=-1) if variant == "gdn" else dgc
     return out
+
+
+# ------------------------------------------------------------------ DeltaTTT-pre
+
+
+def _silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def _unit_rows(x: np.ndarray) -> np.ndarray:
+    """x / ||x|| over the last axis; a zero vector stays zero."""
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+
+
+def ttt_pre_fwd(variant: str, q, k, v, beta1, g1=None, beta2=None, g2=None, A0=None, B0=None,
+                internals: bool = False):
+    """DeltaTTT-pre: a two-layer memory whose layers learn by delta-rule steps
+    (DeltaTTT summary, paperlayer.ai, §4.1 "Layerwise memory optimization" and
+    §4.1 on the Pre schedule; Appendix A, chunkwise scan).
+
+    The first layer A [dv, dk] learns keys -> values; the second layer
+    B [dv, dv] learns intermediate representation -> value, so that it can
+    correct the first layer's prediction.  In the Pre schedule the
+    intermediate representation of token t is formed from the first layer's
+    state before token t's write, so the two writes of a token are independent.
+    Readings (the summary prints no formulas): the nonlinearity is SiLU (the
+    two-layer SiLU memories of its Appendix B); the second layer's write key is
+    the unit-normalised SiLU of the first layer's prediction, like the unit keys
+    of the first layer; the query goes through the first layer after its write
+    (readout after write, as in the delta rule) and the same SiLU and
+    normalisation; each layer has its own step size and decay of the given
+    variant ("deltanet" or "gdn").  Per token, float64:
+
+        A' = A a1_t;       r = A' k_t;     A = A' + beta1_t (v_t - r) k_t^T
+        h  = unit(silu(r));                z = unit(silu(A q_t))
+        B' = B a2_t;       s = B' h;       B = B' + beta2_t (v_t - s) h^T
+        o_t = B z
+
+    q, k [B, T, H, dk]; v [B, T, H, dv]; beta1, beta2 [B, T, H]; g1, g2 [B, T, H]
+    for "gdn" (None for "deltanet"); A0 [B, H, dv, dk] and B0 [B, H, dv, dv] or
+    None (zero).  Returns o [B, T, H, dv], A_T, B_T; with ``internals`` also the
+    per-token h and z [B, T, H, dv].
+    """
+    if variant not in ("deltanet", "gdn"):
+        raise ValueError("DeltaTTT-pre takes the deltanet or gdn form")
+    B, T, H, dv = np.shape(v)
+    dk = np.shape(q)[3]
+    q, k, v = (_to_heads(x) for x in (q, k, v))
+    b1, b2 = _to_heads(beta1), _to_heads(beta2)
+    a1 = _to_heads(_decay(variant, g1, (B, T, H), dk))
+    a2 = _to_heads(_decay(variant, g2, (B, T, H), dv))
+    A = (np.zeros((B * H, dv, dk)) if A0 is None
+         else np.asarray(A0, dtype=np.float64).reshape(B * H, dv, dk).copy())
+    Bm = (np.zeros((B * H, dv, dv)) if B0 is None
+          else np.asarray(B0, dtype=np.float64).reshape(B * H, dv, dv).copy())
+    o = np.empty((B * H, T, dv))
+    hs = np.empty((B * H, T, dv))
+    zs = np.empty((B * H, T, dv))
+    for t in range(T):
+        kt, qt, vt = k[:, t], q[:, t], v[:, t]
+        Ap = A * a1[:, t, None, :]
+        r = (Ap @ kt[:, :, None])[:, :, 0]
+        A = Ap + b1[:, t, None, None] * (vt - r)[:, :, None] * kt[:, None, :]
+        h = _unit_rows(_silu(r))
+        z = _unit_rows(_silu((A @ qt[:, :, None])[:, :, 0]))
+        Bp = Bm * a2[:, t, None, :]
+        s = (Bp @ h[:, :, None])[:, :, 0]
+        Bm = Bp + b2[:, t, None, None] * (vt - s)[:, :, None] * h[:, None, :]
+        o[:, t] = (Bm @ z[:, :, None])[:, :, 0]
+        hs[:, t], zs[:, t] = h, z
+    back = lambda x: np.ascontiguousarray(np.moveaxis(x.reshape(B, H, T, -1), 1, 2))  # noqa: E731
+    out = (back(o), A.reshape(B, H, dv, dk), Bm.reshape(B, H, dv, dv))
+    if internals:
+        out = out + (back(hs), back(zs))
+    return out

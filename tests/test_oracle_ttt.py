@@ -1,0 +1,89 @@
+"""Pins of the oracle's DeltaTTT-pre (ttt_pre_fwd) against the delta-rule oracle and
+the structure the DeltaTTT summary states.
+
+- The second layer with no writes and B0 = I passes the query representation
+  through: o_t = unit(silu(A_t q_t)), with A_t from the delta-rule oracle.
+- Pre schedule (DeltaTTT summary, §4.1): the second layer's write key of token t
+  is formed from the first layer's state before token t's write: it equals
+  unit(silu(A_{t-1} D_t k_t)) with A_{t-1} the delta-rule oracle's state after
+  t - 1 tokens.
+- Two scans (Appendix A, chunkwise scan): the token-interleaved definition
+  equals a first scan over A followed by an ordinary delta-rule scan over B with
+  the formed keys and queries.
+"""
+import numpy as np
+import pytest
+
+from oracle import delta_fwd, ttt_pre_fwd
+
+
+def _inputs(rng, variant, B=2, T=9, H=2, dk=5, dv=4):
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)  # noqa: E731
+    x = dict(q=unit(rng.standard_normal((B, T, H, dk))), k=unit(rng.standard_normal((B, T, H, dk))),
+             v=rng.standard_normal((B, T, H, dv)), beta1=rng.uniform(0, 1, (B, T, H)),
+             beta2=rng.uniform(0, 1, (B, T, H)),
+             A0=0.3 * rng.standard_normal((B, H, dv, dk)), B0=0.3 * rng.standard_normal((B, H, dv, dv)))
+    if variant == "gdn":
+        x["g1"] = -rng.uniform(0, 1, (B, T, H))
+        x["g2"] = -rng.uniform(0, 1, (B, T, H))
+    return x
+
+
+def _silu_unit(x):
+    s = x / (1 + np.exp(-x))
+    return s / np.linalg.norm(s, axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gdn"])
+def test_identity_second_layer_passes_the_query_representation(variant):
+    rng = np.random.default_rng(1)
+    x = _inputs(rng, variant)
+    x["beta2"] = np.zeros_like(x["beta2"])
+    if variant == "gdn":
+        x["g2"] = np.zeros_like(x["g2"])
+    x["B0"] = np.broadcast_to(np.eye(4), x["B0"].shape).copy()
+    o, A_T, _ = ttt_pre_fwd(variant, **x)
+    o1, S1 = delta_fwd(variant, x["q"], x["k"], x["v"], x["beta1"], g=x.get("g1"), S0=x["A0"])
+    np.testing.assert_allclose(o, _silu_unit(o1), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(A_T, S1, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gdn"])
+def test_pre_schedule_write_key_uses_the_previous_state(variant):
+    rng = np.random.default_rng(2)
+    x = _inputs(rng, variant)
+    _, _, _, h, z = ttt_pre_fwd(variant, **x, internals=True)
+    o1, _ = delta_fwd(variant, x["q"], x["k"], x["v"], x["beta1"], g=x.get("g1"), S0=x["A0"])
+    np.testing.assert_allclose(z, _silu_unit(o1), rtol=1e-12, atol=1e-13)   # read after the write
+    for t in (0, 1, 5, 8):
+        if t == 0:
+            A_prev = x["A0"]
+        else:
+            cut = lambda a: None if a is None else a[:, :t]  # noqa: E731
+            _, A_prev = delta_fwd(variant, cut(x["q"]), cut(x["k"]), cut(x["v"]), cut(x["beta1"]),
+                                  g=cut(x.get("g1")), S0=x["A0"])
+        a = np.exp(x["g1"][:, t]) if variant == "gdn" else np.ones(x["beta1"].shape[::2])
+        r = np.einsum("bhvk,bhk->bhv", A_prev, x["k"][:, t]) * a[..., None]
+        np.testing.assert_allclose(h[:, t], _silu_unit(r), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gdn"])
+def test_two_scans_equal_the_interleaved_definition(variant):
+    rng = np.random.default_rng(3)
+    x = _inputs(rng, variant, T=13)
+    o, _, B_T, h, z = ttt_pre_fwd(variant, **x, internals=True)
+    o2, S2 = delta_fwd(variant, z, h, x["v"], x["beta2"], g=x.get("g2"), S0=x["B0"])
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(B_T, S2, rtol=1e-12, atol=1e-13)
+
+
+def test_changing_the_current_value_leaves_the_current_write_key():
+    """Pre: the write key of token t does not see token t's first-layer write."""
+    rng = np.random.default_rng(4)
+    x = _inputs(rng, "gdn")
+    _, _, _, h, _ = ttt_pre_fwd("gdn", **x, internals=True)
+    x2 = {n: (a.copy() if isinstance(a, np.ndarray) else a) for n, a in x.items()}
+    x2["v"][:, 4] += 3.0
+    _, _, _, h2, _ = ttt_pre_fwd("gdn", **x2, internals=True)
+    np.testing.assert_array_equal(h2[:, :5], h[:, :5])
+    assert np.abs(h2[:, 5] - h[:, 5]).max() > 1e-3
