@@ -347,6 +347,32 @@ def main():
                        "hbm_GBs": nb / t_b / 1e9, "hbm_frac": nb / t_b / 1e9 / HBM_PEAK_GBS,
                        "tflops": nf / t_b / 1e12, "algorithmic_bytes_per_launch": nb,
                        "algorithmic_flops_per_launch": nf})
+        # DeltaTTT-pre (two memory layers) on the headline shape
+        from recurrent_memory_amd.inputs import make_ttt_inputs
+        xt = make_ttt_inputs(w)
+        tsets = []
+        for _ in range(2):
+            tsets.append({n: (None if a is None else (torch.from_numpy(a).to(dev) if n in ("A0", "B0") else up(a)))
+                          for n, a in xt.items()})
+
+        def ttt_call(ts):
+            return ops.ttt_pre("gdn", ts["q"], ts["k"], ts["v"], ts["beta1"], ts["beta2"], g1=ts["g1"],
+                               g2=ts["g2"], A0=ts["A0"], B0=ts["B0"], stream=stream)
+        ttt_call(tsets[0])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(10):
+            ttt_call(tsets[i % 2])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_t = e0.elapsed_time(e1) / 1e3 / 10
+        # algorithmic bytes: q, k, v, beta1, g1, beta2, g2 read, o written, both states in and out
+        nb = B * T * H * 2 * (2 * dk + 2 * dv + 4) + B * H * 4 * (dv * dk + dv * dv) * 2
+        others.append({"workload": "ttt_pre_gdn_bf16_b4_h16_t4096_d128", "kernel": "delta_ttt_pre (6 launches)",
+                       "kernel_avg_us": t_t * 1e6, "tokens_per_s": B * T / t_t,
+                       "hbm_GBs": nb / t_t / 1e9, "hbm_frac": nb / t_t / 1e9 / HBM_PEAK_GBS,
+                       "algorithmic_bytes_per_launch": nb})
         result["other_workloads"] = others
 
     if not args.no_decode:

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 3
+#define DR_ABI_VERSION 4
 
 typedef enum {
     DR_DELTANET = 0, /* a = 1: no decay, g must be NULL                          */
@@ -213,6 +213,49 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
                     const void* beta, const void* wgate, const void* g, const float* S0,
                     const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
                     void* dbeta, void* dwgate, void* dg, float* dS0, void* stream);
+
+/*
+ * delta_ttt_pre — DeltaTTT-pre: a two-layer memory whose layers each learn by
+ * delta-rule steps ("DeltaTTT: Layerwise Optimization for Nonlinear Recurrent
+ * Memory" summary, paperlayer.ai, §4.1 layerwise memory optimization and the
+ * Pre schedule; Appendix A, chunkwise scan).  The first layer A [d_v, d_k]
+ * learns keys -> values; the second layer B [d_v, d_v] learns the intermediate
+ * representation -> value.  In the Pre schedule the intermediate representation
+ * of token t comes from the first layer's state before token t's write.  Per
+ * token, with silu(x) = x / (1 + e^-x) and unit(x) = x / ||x|| (0 stays 0):
+ *
+ *   A' = A Diag(a1_t); r = A' k_t; A = A' + beta1_t (v_t - r) k_t^T
+ *   h  = unit(silu(r));            z = unit(silu(A q_t))
+ *   B' = B a2_t;       s = B' h;   B = B' + beta2_t (v_t - s) h^T
+ *   o_t = B z
+ *
+ * The summary prints none of these formulas: SiLU, the unit-normalised second-
+ * layer key and query, and the readout after the write are this library's
+ * readings (SiLU is the nonlinearity of its two-layer memories).  Evaluated as
+ * two chunkwise first-layer scans (one of them on shifted queries, whose
+ * readouts are the pre-write reads r), a key/query transform and one chunkwise
+ * second-layer scan; every scan is delta_fwd's kernel.
+ *
+ *   desc   variant DR_DELTANET or DR_GDN (both layers); H_k must be 0 or H;
+ *          d_k the key width of the first layer, d_v the value width (and both
+ *          widths of the second layer)
+ *   q, k   [B, T, H, d_k] dtype;  v [B, T, H, d_v] dtype
+ *   beta1, beta2  step sizes of the two layers [B, T, H] dtype
+ *   g1, g2 log-decays of the two layers [B, T, H] dtype (DR_GDN), NULL (DR_DELTANET)
+ *   A0     [B, H, d_v, d_k] fp32 or NULL (zero);  B0 [B, H, d_v, d_v] fp32 or NULL
+ *   o      [B, T, H, d_v] dtype (written); must not overlap any input
+ *   A_T, B_T  final states, fp32 (written) or NULL; A_T may be A0 and B_T may be
+ *          B0 (in place), otherwise no output may overlap an input or another output
+ *
+ * The intermediate tensors (shifted queries, reads, first-layer readouts, keys
+ * and queries of the second layer) are kept in the input dtype, in a workspace
+ * of 2 * B * T * H * (d_k + 4 d_v) + 2 * B * H * d_v bytes (bf16; twice that for
+ * fp32) from the pool of delta_fwd, returned on the call's stream.  No backward.
+ */
+dr_status delta_ttt_pre(const dr_desc* desc, const void* q, const void* k, const void* v,
+                        const void* beta1, const void* g1, const void* beta2, const void* g2,
+                        const float* A0, const float* B0, void* o, float* A_T, float* B_T,
+                        void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* dr_status_str(int status);

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdeltarule.so")
-SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "prefill_cw.hip", "prefill_cw2.hip", "efla.hip", "bwd.hip"]
+SOURCES = ["abi.hip", "decode.hip", "prefill.hip", "prefill_pipe.hip", "prefill_cw.hip", "prefill_cw2.hip", "efla.hip", "bwd.hip", "ttt.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -amdgpu-mfma-vgpr-form: MFMA results go to VGPRs, where the epilogues read

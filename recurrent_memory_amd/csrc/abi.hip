@@ -180,6 +180,56 @@ dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const 
     }
 }
 
+dr_status delta_ttt_pre(const dr_desc* desc, const void* q, const void* k, const void* v,
+                        const void* beta1, const void* g1, const void* beta2, const void* g2,
+                        const float* A0, const float* B0, void* o, float* A_T, float* B_T,
+                        void* stream) {
+    try {
+        Sizes sz;
+        dr_status st = check_desc(desc, false, &sz);
+        if (st != DR_OK) return st;
+        if (desc->variant != DR_DELTANET && desc->variant != DR_GDN) return DR_E_UNSUPPORTED;
+        if (sz.Hk != desc->H) return DR_E_UNSUPPORTED;
+        if (q == nullptr || k == nullptr || v == nullptr || beta1 == nullptr || beta2 == nullptr ||
+            o == nullptr)
+            return DR_E_NULLPTR;
+        if (desc->variant == DR_GDN) {
+            if (g1 == nullptr || g2 == nullptr) return DR_E_NULLPTR;
+        } else if (g1 != nullptr || g2 != nullptr) {
+            return DR_E_UNSUPPORTED;
+        }
+        const void* ptrs[] = {q, k, v, beta1, g1, beta2, g2, A0, B0, o, A_T, B_T};
+        for (const void* p : ptrs)
+            if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
+        const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
+        const int64_t bstate = static_cast<int64_t>(desc->B) * desc->H * desc->d_v * desc->d_v;
+        const Span in[] = {span_of(q, sz.qk, eb),      span_of(k, sz.qk, eb),
+                           span_of(v, sz.v, eb),       span_of(beta1, sz.beta, eb),
+                           span_of(g1, sz.g, eb),      span_of(beta2, sz.beta, eb),
+                           span_of(g2, sz.g, eb),      span_of(A0, sz.state, 4),
+                           span_of(B0, bstate, 4)};
+        const Span so = span_of(o, sz.v, eb), sa = span_of(A_T, sz.state, 4), sb = span_of(B_T, bstate, 4);
+        for (const Span& s : in)
+            if (overlap(so, s)) return DR_E_ALIAS;
+        for (int i = 0; i < 9; ++i) {
+            if (overlap(sa, in[i]) && !(i == 7 && static_cast<const void*>(A_T) == static_cast<const void*>(A0)))
+                return DR_E_ALIAS;
+            if (overlap(sb, in[i]) && !(i == 8 && static_cast<const void*>(B_T) == static_cast<const void*>(B0)))
+                return DR_E_ALIAS;
+        }
+        if (overlap(sa, so) || overlap(sb, so) || overlap(sa, sb)) return DR_E_ALIAS;
+
+        st = check_device();
+        if (st != DR_OK) return st;
+        dr::TttArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta1, g1, beta2, g2,
+                      A0, B0, o, A_T, B_T};
+        const hipError_t e = dr::launch_ttt_pre(desc->variant, desc->dtype, a, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
 dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, void* beta_eff,
                           void* stream) {
     try {

@@ -89,4 +89,29 @@ hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t stre
 // library-owned stream-ordered memory pool of the current device (workspaces)
 hipError_t workspace_pool(hipMemPool_t* pool);
 
+// DeltaTTT-pre: two chained delta-rule memory layers (variant 0 or 1 for both)
+struct TttArgs {
+    int B, T, H, dk, dv;
+    const void* q;       // [B,T,H,dk]
+    const void* k;
+    const void* v;       // [B,T,H,dv]
+    const void* beta1;   // [B,T,H] first layer
+    const void* g1;      // [B,T,H] or nullptr
+    const void* beta2;   // [B,T,H] second layer
+    const void* g2;      // [B,T,H] or nullptr
+    const float* A0;     // [B,H,dv,dk] or nullptr
+    const float* B0;     // [B,H,dv,dv] or nullptr
+    void* o;             // [B,T,H,dv]
+    float* AT;           // [B,H,dv,dk] or nullptr (may equal A0)
+    float* BT;           // [B,H,dv,dv] or nullptr (may equal B0)
+    // workspace (set by the launcher)
+    void* qs = nullptr;  // [B,T,H,dk] shifted queries a1 ⊙ k of the next token
+    void* rd = nullptr;  // [B,T,H,dv] their readouts: pre-write reads of tokens 1..T
+    void* r0 = nullptr;  // [B,H,dv] pre-write read of token 0
+    void* o1 = nullptr;  // [B,T,H,dv] first-layer readout after the write
+    void* hk = nullptr;  // [B,T,H,dv] second-layer write keys
+    void* zq = nullptr;  // [B,T,H,dv] second-layer queries
+};
+hipError_t launch_ttt_pre(int variant, int dtype, const TttArgs& a, hipStream_t stream);
+
 }  // namespace dr

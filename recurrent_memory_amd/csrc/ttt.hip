@@ -1,0 +1,172 @@
+// DeltaTTT-pre: a two-layer memory whose layers each learn by delta-rule steps
+// (DeltaTTT summary, paperlayer.ai, §4.1 "Layerwise memory optimization" and
+// the Pre schedule; Appendix A, chunkwise scan of DeltaTTT).
+//
+// The first layer A [dv, dk] learns keys -> values.  In the Pre schedule the
+// second layer's write key for token t comes from the first layer's state
+// before token t's write, so the second layer is an ordinary delta-rule scan
+// whose keys and queries are known once the first scan is done:
+//   r_t = A'_t k_t            (A'_t = A_{t-1} Diag(a1_t), the first layer's prediction)
+//   h_t = unit(silu(r_t)),    z_t = unit(silu(A_t q_t))
+//   B_t = B'_t + beta2_t (v_t - B'_t h_t) h_t^T,   o_t = B_t z_t
+// The pre-write reads r_t come from a second first-layer scan with shifted
+// queries: its readout after token s is A_s (a1_{s+1} ⊙ k_{s+1}) = r_{s+1}, and
+// r_0 = A'_0 k_0 is one matrix-vector product per head.  So the whole layer is
+// five launches: r_0, the shifted queries, the two first-layer scans and the
+// key/query transform, then the second-layer scan, each scan being delta_fwd's
+// chunkwise kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace dr {
+namespace {
+
+constexpr int kTttThreads = 256;
+
+// q_s[b, s, h, :] = a1(b, s + 1, h) k[b, s + 1, h, :] for s < T - 1; zero at s = T - 1
+template <typename E, int VAR>
+__global__ __launch_bounds__(kTttThreads) void ttt_shift_kernel(TttArgs p, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kTttThreads;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kTttThreads + threadIdx.x; e < n; e += stride) {
+        const int64_t row = e / p.dk;              // (b, s, h)
+        const int s = static_cast<int>((row / p.H) % p.T);
+        float x = 0.f;
+        if (s + 1 < p.T) {
+            const int64_t next = row + p.H;        // (b, s + 1, h)
+            x = load_elem<E>(p.k, next * p.dk + e % p.dk);
+            if constexpr (VAR == 1) x *= __expf(load_elem<E>(p.g1, next));
+        }
+        store_elem<E>(p.qs, e, x);
+    }
+}
+
+// r0[b, h, i] = a1(b, 0, h) sum_c A0[b, h, i, c] k[b, 0, h, c]; zero without A0.
+// One workgroup per (b, h), one value row per thread.
+template <typename E, int VAR>
+__global__ __launch_bounds__(kTttThreads) void ttt_r0_kernel(TttArgs p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh % p.H;
+    const int64_t krow = static_cast<int64_t>(b) * p.T * p.H + h;   // token 0 of sequence b
+    float a = 1.f;
+    if constexpr (VAR == 1) a = __expf(load_elem<E>(p.g1, krow));
+    for (int i = threadIdx.x; i < p.dv; i += kTttThreads) {
+        float acc = 0.f;
+        if (p.A0) {
+            const float* row = p.A0 + (static_cast<int64_t>(bh) * p.dv + i) * p.dk;
+            for (int c = 0; c < p.dk; ++c) acc = fmaf(row[c], load_elem<E>(p.k, krow * p.dk + c), acc);
+        }
+        store_elem<E>(p.r0, static_cast<int64_t>(bh) * p.dv + i, a * acc);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s, 64);
+    return x;
+}
+__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+
+// Per row (b, t, h), one wave: r = r_t (r0 at t = 0, else the shifted scan's
+// readout of token t - 1), h = unit(silu(r)), z = unit(silu(o1)); a zero
+// vector stays zero.
+template <typename E, int DV>
+__global__ __launch_bounds__(kTttThreads) void ttt_glue_kernel(TttArgs p, int64_t rows) {
+    constexpr int EPL = DV / 64;
+    constexpr int WPB = kTttThreads / 64;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * WPB;
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * WPB + w; row < rows; row += stride) {
+        const int h = static_cast<int>(row % p.H);
+        const int64_t bt = row / p.H;
+        const int t = static_cast<int>(bt % p.T);
+        const int64_t b = bt / p.T;
+        float r[EPL], z[EPL];
+        float sr = 0.f, sz = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int i = l * EPL + j;
+            const float rv = t == 0 ? load_elem<E>(p.r0, (b * p.H + h) * DV + i)
+                                    : load_elem<E>(p.rd, (row - p.H) * DV + i);
+            r[j] = silu(rv);
+            z[j] = silu(load_elem<E>(p.o1, row * DV + i));
+            sr += r[j] * r[j];
+            sz += z[j] * z[j];
+        }
+        sr = wave_sum(sr);
+        sz = wave_sum(sz);
+        const float ir = sr > 0.f ? rsqrtf(sr) : 0.f, iz = sz > 0.f ? rsqrtf(sz) : 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int i = l * EPL + j;
+            store_elem<E>(p.hk, row * DV + i, r[j] * ir);
+            store_elem<E>(p.zq, row * DV + i, z[j] * iz);
+        }
+    }
+}
+
+unsigned grid_for(int64_t work, int per_block) {
+    const int64_t blocks = (work + per_block - 1) / per_block;
+    return static_cast<unsigned>(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
+}
+
+template <typename E, int VAR>
+hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
+    const int64_t eb = E::bytes;
+    const int64_t tok = static_cast<int64_t>(a.B) * a.T * a.H;
+    const int64_t nq = tok * a.dk, nv = tok * a.dv, n0 = static_cast<int64_t>(a.B) * a.H * a.dv;
+    // one allocation: qs, rd, o1, hk, zq, r0 (each 256-byte aligned)
+    auto up = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
+    const int64_t total = up(nq * eb) + 4 * up(nv * eb) + up(n0 * eb);
+    hipMemPool_t pool;
+    hipError_t e = workspace_pool(&pool);
+    if (e != hipSuccess) return e;
+    unsigned char* ws = nullptr;
+    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total), pool, s);
+    if (e != hipSuccess) return e;
+    unsigned char* cur = ws;
+    auto take = [&](int64_t bytes) { void* p = cur; cur += up(bytes); return p; };
+    a.qs = take(nq * eb);
+    a.rd = take(nv * eb);
+    a.o1 = take(nv * eb);
+    a.hk = take(nv * eb);
+    a.zq = take(nv * eb);
+    a.r0 = take(n0 * eb);
+    // the two reads of A0 come before the first-layer scan that may overwrite it
+    hipLaunchKernelGGL((ttt_r0_kernel<E, VAR>), dim3(static_cast<unsigned>(a.B * a.H)), dim3(kTttThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL((ttt_shift_kernel<E, VAR>), dim3(grid_for(nq, kTttThreads)), dim3(kTttThreads), 0, s, a, nq);
+        e = hipGetLastError();
+    }
+    const int dt = E::bytes == 4 ? 0 : 1;
+    if (e == hipSuccess) {   // pre-write reads: readouts of the shifted queries
+        FwdArgs f{a.B, a.T, a.H, a.dk, a.dv, a.qs, a.k, a.v, a.beta1, nullptr, a.g1, a.A0, a.rd, nullptr, a.H};
+        e = launch_fwd(VAR, dt, f, s);
+    }
+    if (e == hipSuccess) {   // first layer: readout after the write, final state
+        FwdArgs f{a.B, a.T, a.H, a.dk, a.dv, a.q, a.k, a.v, a.beta1, nullptr, a.g1, a.A0, a.o1, a.AT, a.H};
+        e = launch_fwd(VAR, dt, f, s);
+    }
+    if (e == hipSuccess) {
+        if (a.dv == 128)
+            hipLaunchKernelGGL((ttt_glue_kernel<E, 128>), dim3(grid_for(tok, kTttThreads / 64)), dim3(kTttThreads), 0, s, a, tok);
+        else
+            hipLaunchKernelGGL((ttt_glue_kernel<E, 64>), dim3(grid_for(tok, kTttThreads / 64)), dim3(kTttThreads), 0, s, a, tok);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {   // second layer: keys h, queries z, the same values
+        FwdArgs f{a.B, a.T, a.H, a.dv, a.dv, a.zq, a.hk, a.v, a.beta2, nullptr, a.g2, a.B0, a.o, a.BT, a.H};
+        e = launch_fwd(VAR, dt, f, s);
+    }
+    const hipError_t f = hipFreeAsync(ws, s);
+    return e == hipSuccess ? f : e;
+}
+
+}  // namespace
+
+hipError_t launch_ttt_pre(int variant, int dtype, const TttArgs& a, hipStream_t s) {
+    if (dtype == 0) return variant == 0 ? launch_ttt_typed<F32, 0>(a, s) : launch_ttt_typed<F32, 1>(a, s);
+    return variant == 0 ? launch_ttt_typed<BF16, 0>(a, s) : launch_ttt_typed<BF16, 1>(a, s);
+}
+
+}  // namespace dr

@@ -180,3 +180,28 @@ def make_decode_inputs(w: Workload, n_steps: int, seed: Optional[int] = None,
     steps = [draw(rng, w.variant, w.dtype, (w.B, w.H), w.dk, w.dv, gate_scale, qk_heads, key_norm)
              for _ in range(n_steps)]
     return dict(S=S, steps=steps)
+
+
+def make_ttt_inputs(w: Workload, seed: Optional[int] = None, T: Optional[int] = None,
+                    random_states: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Inputs of DeltaTTT-pre (two memory layers): the forward inputs of ``w``
+    (q, k, v, beta1 = beta, g1 = g; "deltanet" or "gdn"), then beta2 and g2
+    drawn the same way, then A0 [B, H, dv, dk] and B0 [B, H, dv, dv] as
+    0.02 * z (or None)."""
+    if w.variant not in ("deltanet", "gdn"):
+        raise ValueError("DeltaTTT-pre takes the deltanet or gdn form")
+    seed = w.seed if seed is None else seed
+    T = w.T if T is None else T
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = draw(rng, w.variant, w.dtype, (w.B, T, w.H), w.dk, w.dv)
+    lead = (w.B, T, w.H)
+    beta2 = _sigmoid(rng.standard_normal(lead, dtype=np.float32))
+    g2 = None if w.variant == "deltanet" else _neg_softplus(rng.standard_normal(lead, dtype=np.float32))
+    out = dict(q=x["q"], k=x["k"], v=x["v"], beta1=x["beta"], g1=x["g"],
+               beta2=cast(beta2, w.dtype), g2=None if g2 is None else cast(g2, w.dtype))
+    if random_states:
+        out["A0"] = (np.float32(0.02) * rng.standard_normal((w.B, w.H, w.dv, w.dk), dtype=np.float32))
+        out["B0"] = (np.float32(0.02) * rng.standard_normal((w.B, w.H, w.dv, w.dv), dtype=np.float32))
+    else:
+        out["A0"] = out["B0"] = None
+    return out

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltarule.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "deltarule.h")
 
-ABI_VERSION = 3   # DR_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4   # DR_ABI_VERSION of the header this binding follows
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3, "fg2": 4}
 # forms whose beta is one value per key channel (the erase gate, or the step sizes)
 _CHANNEL_BETA = ("gdn2", "fg2")
@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.delta_bwd.restype = ctypes.c_int
     lib.delta_efla_beta.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp]
     lib.delta_efla_beta.restype = ctypes.c_int
+    lib.delta_ttt_pre.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 13
+    lib.delta_ttt_pre.restype = ctypes.c_int
     lib.dr_status_str.argtypes = [ctypes.c_int]
     lib.dr_status_str.restype = ctypes.c_char_p
     lib.dr_abi_version.argtypes = []
@@ -269,3 +271,56 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != 0:
         _raise(st)
     return out
+
+
+def ttt_pre(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta1: torch.Tensor,
+            beta2: torch.Tensor, g1: Optional[torch.Tensor] = None, g2: Optional[torch.Tensor] = None,
+            A0: Optional[torch.Tensor] = None, B0: Optional[torch.Tensor] = None,
+            o: Optional[torch.Tensor] = None, A_T: Optional[torch.Tensor] = None,
+            B_T: Optional[torch.Tensor] = None, want_state: bool = True, stream=None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """DeltaTTT-pre (two delta-rule memory layers; include/deltarule.h, delta_ttt_pre).
+
+    q, k [B, T, H, dk]; v [B, T, H, dv]; beta1, beta2 (and g1, g2 for "gdn")
+    [B, T, H]; A0 [B, H, dv, dk], B0 [B, H, dv, dv] fp32 or None.  Returns
+    (o, A_T, B_T); passing ``A_T=A0`` / ``B_T=B0`` updates the states in place.
+    """
+    if variant not in ("deltanet", "gdn"):
+        raise ValueError("DeltaTTT-pre takes the deltanet or gdn form")
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t, shape in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("v", v, (B, T, H, dv)),
+                           ("beta1", beta1, (B, T, H)), ("beta2", beta2, (B, T, H))):
+        _check(name, t, shape, dt, dev)
+    for name, t in (("g1", g1), ("g2", g2)):
+        if variant == "gdn":
+            _check(name, t, (B, T, H), dt, dev)
+        elif t is not None:
+            raise ValueError("deltanet takes no decay")
+    if A0 is not None:
+        _check("A0", A0, (B, H, dv, dk), torch.float32, dev)
+    if B0 is not None:
+        _check("B0", B0, (B, H, dv, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if want_state:
+        if A_T is None:
+            A_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        if B_T is None:
+            B_T = torch.empty((B, H, dv, dv), dtype=torch.float32, device=dev)
+    if A_T is not None:
+        _check("A_T", A_T, (B, H, dv, dk), torch.float32, dev)
+    if B_T is not None:
+        _check("B_T", B_T, (B, H, dv, dv), torch.float32, dev)
+    desc = DrDesc(B, T, H, dk, dv, 64, VARIANTS[variant], DTYPES[dt], H)
+    st = lib.delta_ttt_pre(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta1), _ptr(g1),
+                           _ptr(beta2), _ptr(g2), _ptr(A0), _ptr(B0), _ptr(o), _ptr(A_T), _ptr(B_T),
+                           _stream(stream))
+    if st != 0:
+        _raise(st)
+    return o, A_T, B_T

@@ -19,13 +19,13 @@ FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(12)]
 def test_exports_every_header_symbol():
     names = ops.header_functions()
     assert set(names) == {"delta_fwd", "delta_decode", "delta_bwd", "delta_efla_beta",
-                          "dr_status_str", "dr_abi_version"}
+                          "delta_ttt_pre", "dr_status_str", "dr_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
-    assert lib.dr_abi_version() == ops.ABI_VERSION == 3
+    assert lib.dr_abi_version() == ops.ABI_VERSION == 4
     assert lib.dr_status_str(0) == b"ok"
     assert lib.dr_status_str(99) == b"unknown status"
     for s in range(8):
@@ -175,3 +175,27 @@ def test_no_device_returns_device_error():
     assert dec(desc(T=1)) == DR_E_DEVICE
     assert efla(desc(T=1)) == DR_E_DEVICE
     assert efla(desc(), out=FAKE[3]) == DR_E_DEVICE             # in place is allowed
+
+
+def ttt(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta1=FAKE[3], g1=FAKE[4], beta2=FAKE[5], g2=FAKE[6],
+        A0=None, B0=None, o=FAKE[9], AT=None, BT=None):
+    return lib.delta_ttt_pre(ctypes.byref(d) if d is not None else None, q, k, v, beta1, g1, beta2, g2,
+                             A0, B0, o, AT, BT, None)
+
+
+def test_ttt_pre_validation():
+    assert ttt(None) == DR_E_NULLPTR
+    for name in ("q", "k", "v", "beta1", "beta2", "o", "g1", "g2"):
+        assert ttt(desc(), **{name: None}) == DR_E_NULLPTR, name
+    assert ttt(desc(variant=0)) == DR_E_UNSUPPORTED             # decays given to the ungated form
+    for var in (2, 3, 4):
+        assert ttt(desc(variant=var)) == DR_E_UNSUPPORTED       # deltanet or gdn only
+    assert ttt(desc(H=4, H_k=2)) == DR_E_UNSUPPORTED            # no grouped heads
+    assert ttt(desc(), o=FAKE[2]) == DR_E_ALIAS                 # o over v
+    assert ttt(desc(), AT=FAKE[10], BT=FAKE[10]) == DR_E_ALIAS  # the two final states overlap
+    assert ttt(desc(), A0=FAKE[10], BT=FAKE[10]) == DR_E_ALIAS  # B_T over A0
+    assert ttt(desc(), B0=ctypes.c_void_p(FAKE[11].value + 4)) == DR_E_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert ttt(desc(), A0=FAKE[10], AT=FAKE[10], B0=FAKE[11], BT=FAKE[11]) == DR_E_DEVICE  # in place
+        assert ttt(desc(variant=0), g1=None, g2=None) == DR_E_DEVICE
