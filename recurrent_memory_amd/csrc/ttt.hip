@@ -23,20 +23,61 @@ namespace {
 
 constexpr int kTttThreads = 256;
 
-// q_s[b, s, h, :] = a1(b, s + 1, h) k[b, s + 1, h, :] for s < T - 1; zero at s = T - 1
+// 16 bytes of dtype elements <-> fp32
+template <typename E>
+struct Vec16 {
+    static constexpr int N = 16 / E::bytes;
+    __device__ static void unpack(const uint4& u, float (&x)[N]) {
+        if constexpr (E::bytes == 4) {
+            x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+            x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+        } else {
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = bf16_bits_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+                x[2 * i + 1] = bf16_bits_to_f32(static_cast<uint16_t>(w[i] >> 16));
+            }
+        }
+    }
+    __device__ static uint4 pack(const float (&x)[N]) {
+        if constexpr (E::bytes == 4) {
+            return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i])) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(x[2 * i + 1])) << 16);
+            return make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+};
+
+// q_s[b, s, h, :] = a1(b, s + 1, h) k[b, s + 1, h, :] for s < T - 1; zero at s = T - 1.
+// 16 bytes per thread (d_k is a multiple of 64, so a piece never straddles rows).
 template <typename E, int VAR>
-__global__ __launch_bounds__(kTttThreads) void ttt_shift_kernel(TttArgs p, int64_t n) {
+__global__ __launch_bounds__(kTttThreads) void ttt_shift_kernel(TttArgs p, int64_t npieces) {
+    typedef Vec16<E> V;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kTttThreads;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kTttThreads + threadIdx.x; e < n; e += stride) {
+    for (int64_t iv = static_cast<int64_t>(blockIdx.x) * kTttThreads + threadIdx.x; iv < npieces; iv += stride) {
+        const int64_t e = iv * V::N;
         const int64_t row = e / p.dk;              // (b, s, h)
         const int s = static_cast<int>((row / p.H) % p.T);
-        float x = 0.f;
+        uint4 out = make_uint4(0u, 0u, 0u, 0u);
         if (s + 1 < p.T) {
             const int64_t next = row + p.H;        // (b, s + 1, h)
-            x = load_elem<E>(p.k, next * p.dk + e % p.dk);
-            if constexpr (VAR == 1) x *= __expf(load_elem<E>(p.g1, next));
+            out = *reinterpret_cast<const uint4*>(static_cast<const typename E::T*>(p.k) + next * p.dk + e % p.dk);
+            if constexpr (VAR == 1) {
+                const float a = __expf(load_elem<E>(p.g1, next));
+                float x[V::N];
+                V::unpack(out, x);
+#pragma unroll
+                for (int i = 0; i < V::N; ++i) x[i] *= a;
+                out = V::pack(x);
+            }
         }
-        store_elem<E>(p.qs, e, x);
+        *reinterpret_cast<uint4*>(static_cast<typename E::T*>(p.qs) + e) = out;
     }
 }
 
@@ -59,48 +100,51 @@ __global__ __launch_bounds__(kTttThreads) void ttt_r0_kernel(TttArgs p) {
     }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s, 64);
-    return x;
-}
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
 
-// Per row (b, t, h), one wave: r = r_t (r0 at t = 0, else the shifted scan's
-// readout of token t - 1), h = unit(silu(r)), z = unit(silu(o1)); a zero
-// vector stays zero.
+// Per row (b, t, h): r = r_t (r0 at t = 0, else the shifted scan's readout of
+// token t - 1), h = unit(silu(r)), z = unit(silu(o1)); a zero vector stays
+// zero.  LPR lanes per row, 16 bytes each; the row sums are xor butterflies
+// within the LPR lanes.
 template <typename E, int DV>
 __global__ __launch_bounds__(kTttThreads) void ttt_glue_kernel(TttArgs p, int64_t rows) {
-    constexpr int EPL = DV / 64;
-    constexpr int WPB = kTttThreads / 64;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * WPB;
-    for (int64_t row = static_cast<int64_t>(blockIdx.x) * WPB + w; row < rows; row += stride) {
+    typedef Vec16<E> V;
+    typedef typename E::T Raw;
+    constexpr int LPR = DV / V::N;                 // 8, 16 or 32
+    constexpr int RPB = kTttThreads / LPR;
+    const int sub = threadIdx.x % LPR;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * RPB;
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR; row < rows; row += stride) {
         const int h = static_cast<int>(row % p.H);
         const int64_t bt = row / p.H;
         const int t = static_cast<int>(bt % p.T);
         const int64_t b = bt / p.T;
-        float r[EPL], z[EPL];
+        const Raw* rsrc = t == 0 ? static_cast<const Raw*>(p.r0) + (b * p.H + h) * DV
+                                 : static_cast<const Raw*>(p.rd) + (row - p.H) * DV;
+        float r[V::N], z[V::N];
+        V::unpack(*reinterpret_cast<const uint4*>(rsrc + sub * V::N), r);
+        V::unpack(*reinterpret_cast<const uint4*>(static_cast<const Raw*>(p.o1) + row * DV + sub * V::N), z);
         float sr = 0.f, sz = 0.f;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int i = l * EPL + j;
-            const float rv = t == 0 ? load_elem<E>(p.r0, (b * p.H + h) * DV + i)
-                                    : load_elem<E>(p.rd, (row - p.H) * DV + i);
-            r[j] = silu(rv);
-            z[j] = silu(load_elem<E>(p.o1, row * DV + i));
-            sr += r[j] * r[j];
-            sz += z[j] * z[j];
+        for (int i = 0; i < V::N; ++i) {
+            r[i] = silu(r[i]);
+            z[i] = silu(z[i]);
+            sr += r[i] * r[i];
+            sz += z[i] * z[i];
         }
-        sr = wave_sum(sr);
-        sz = wave_sum(sz);
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+            sr += __shfl_xor(sr, m, LPR);
+            sz += __shfl_xor(sz, m, LPR);
+        }
         const float ir = sr > 0.f ? rsqrtf(sr) : 0.f, iz = sz > 0.f ? rsqrtf(sz) : 0.f;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int i = l * EPL + j;
-            store_elem<E>(p.hk, row * DV + i, r[j] * ir);
-            store_elem<E>(p.zq, row * DV + i, z[j] * iz);
+        for (int i = 0; i < V::N; ++i) {
+            r[i] *= ir;
+            z[i] *= iz;
         }
+        *reinterpret_cast<uint4*>(static_cast<Raw*>(p.hk) + row * DV + sub * V::N) = V::pack(r);
+        *reinterpret_cast<uint4*>(static_cast<Raw*>(p.zq) + row * DV + sub * V::N) = V::pack(z);
     }
 }
 
@@ -135,7 +179,8 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
     hipLaunchKernelGGL((ttt_r0_kernel<E, VAR>), dim3(static_cast<unsigned>(a.B * a.H)), dim3(kTttThreads), 0, s, a);
     e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((ttt_shift_kernel<E, VAR>), dim3(grid_for(nq, kTttThreads)), dim3(kTttThreads), 0, s, a, nq);
+        const int64_t pieces = nq / Vec16<E>::N;
+        hipLaunchKernelGGL((ttt_shift_kernel<E, VAR>), dim3(grid_for(pieces, kTttThreads)), dim3(kTttThreads), 0, s, a, pieces);
         e = hipGetLastError();
     }
     const int dt = E::bytes == 4 ? 0 : 1;
@@ -148,10 +193,11 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
         e = launch_fwd(VAR, dt, f, s);
     }
     if (e == hipSuccess) {
+        constexpr int N = Vec16<E>::N;
         if (a.dv == 128)
-            hipLaunchKernelGGL((ttt_glue_kernel<E, 128>), dim3(grid_for(tok, kTttThreads / 64)), dim3(kTttThreads), 0, s, a, tok);
+            hipLaunchKernelGGL((ttt_glue_kernel<E, 128>), dim3(grid_for(tok, kTttThreads / (128 / N))), dim3(kTttThreads), 0, s, a, tok);
         else
-            hipLaunchKernelGGL((ttt_glue_kernel<E, 64>), dim3(grid_for(tok, kTttThreads / 64)), dim3(kTttThreads), 0, s, a, tok);
+            hipLaunchKernelGGL((ttt_glue_kernel<E, 64>), dim3(grid_for(tok, kTttThreads / (64 / N))), dim3(kTttThreads), 0, s, a, tok);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {   // second layer: keys h, queries z, the same values
