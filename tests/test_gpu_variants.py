@@ -20,7 +20,7 @@ from recurrent_memory_amd.inputs import Workload, make_decode_inputs, make_forwa
 
 pytestmark = pytest.mark.gpu
 
-ALL = ["deltanet", "gdn", "kda", "gdn2"]
+ALL = ["deltanet", "gdn", "kda", "gdn2", "fg2"]
 
 
 def _oracle(variant, x, heads=None):
