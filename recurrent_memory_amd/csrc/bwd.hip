@@ -31,8 +31,10 @@ namespace dr {
 namespace {
 
 constexpr int kBC = 64;     // chunk length
-constexpr int kBT = 256;    // threads per workgroup
 constexpr int kBVT = 32;    // value rows per chain workgroup
+constexpr int kCW = 8;      // waves per chain workgroup (two per SIMD: one hides the
+                            // other's LDS and matrix-core latency)
+constexpr int kCT = 64 * kCW;
 constexpr int kGT = 512;    // threads of the gradient workgroup
 constexpr int kGW = kGT / 64;
 constexpr int kRT = kGT / 64;   // its threads per row for row sums
@@ -52,6 +54,37 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
     for (int k = k0; k < k1; k += 4)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
     return acc;
+}
+
+// mm_tile with the k range split into two interleaved accumulation chains
+// (k1 - k0 a multiple of 8), which the matrix core runs back to back.
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mm_tile_k2(f32x4 acc, int i0, int j0, int k0, int k1, const FA& A,
+                                            const FB& B) {
+    const int l = threadIdx.x & 63;
+    const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
+    f32x4 other = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = k0; k < k1; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
+        other = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + 4 + kk), B(k + 4 + kk, bj), other, 0, 0, 0);
+    }
+    return acc + other;
+}
+
+// Two tiles with the same rows i0 and columns j0, j1: one A read feeds both
+// accumulation chains.
+template <class FA, class FB>
+__device__ __forceinline__ void mm_tile2(f32x4& acc0, f32x4& acc1, int i0, int j0, int j1, int k0, int k1,
+                                         const FA& A, const FB& B) {
+    const int l = threadIdx.x & 63;
+    const int ai = i0 + (l & 15), b0 = j0 + (l & 15), b1 = j1 + (l & 15), kk = l >> 4;
+#pragma unroll 16
+    for (int k = k0; k < k1; k += 4) {
+        const float a = A(ai, k + kk);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + kk, b0), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + kk, b1), acc1, 0, 0, 0);
+    }
 }
 
 // Pairwise sums with a per-channel factor, as products: for the 16 x 16 tile at
@@ -330,7 +363,7 @@ inline unsigned chain_grid(const BwdArgs& a, int DV) {
 // Single step size:  Vt = U - W S^T,   S = S Diag(gamma) + Vt^T Kbar.
 // Split gates:       Y = Ut + W S^T,   S = S Diag(gamma) - Y^T Ebar + X^T Kbar.
 template <class L, typename E, int DK, int DV, bool SPLIT>
-__global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, int N) {
     constexpr int NVT = DV / kBVT;
     // Row strides against LDS bank conflicts in the matrix-core operand reads:
     // an operand read along its rows by the 16 lanes of a group (sS, sW) takes a
@@ -348,15 +381,15 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    for (int e = tid; e < kBVT * DK; e += kBT) {
+    for (int e = tid; e < kBVT * DK; e += kCT) {
         const int i = e / DK, c = e % DK;
         sS[i * SS + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
     // the next chunk's operands are fetched into registers while this chunk's
     // products run, and written to LDS at the top of the next step
     const int w = tid >> 6, l = tid & 63;
-    constexpr int NP = kBC * DK / 4 / kBT;          // 16-byte pieces per thread per operand
-    constexpr int MT = (kBC / 16) * (kBVT / 16) / 4;  // Vt tiles per wave
+    constexpr int NP = kBC * DK / 4 / kCT;          // 16-byte pieces per thread per operand
+    constexpr int MT = (kBC / 16) * (kBVT / 16) / kCW;  // Vt tiles per wave
     float4 pW[NP], pK[NP], pE[SPLIT ? NP : 1];
     float pU[MT][4];
     float pG = 0.f;
@@ -364,14 +397,14 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int idx = 4 * (tid + kBT * j);
+            const int idx = 4 * (tid + kCT * j);
             pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
             pK[j] = *reinterpret_cast<const float4*>(R + L::oKb + idx);
             if constexpr (SPLIT) pE[j] = *reinterpret_cast<const float4*>(R + L::oEb + idx);
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int t = w + 4 * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+            const int t = w + kCW * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
 #pragma unroll
             for (int q = 0; q < 4; ++q) pU[m][q] = R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + i0 + c0 + (l & 15)];
         }
@@ -385,7 +418,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int idx = 4 * (tid + kBT * j);
+            const int idx = 4 * (tid + kCT * j);
             put4(sW, SW, idx, pW[j]);
             put4(sKb, SK, idx, pK[j]);
             if constexpr (SPLIT) put4(sEb, SK, idx, pE[j]);
@@ -398,7 +431,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         if (tid < DK) sGam[tid] = pG;
         if constexpr (SPLIT) {   // X = w v for this tile's value columns
             const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
-            for (int e = tid; e < kBC * kBVT; e += kBT) {
+            for (int e = tid; e < kBC * kBVT; e += kCT) {
                 const int r = e / kBVT, i = e % kBVT;
                 float x = 0.f;
                 if (r < Cn) {
@@ -410,17 +443,17 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         }
         lds_only_barrier();
         if (n + 1 < N) fetch(n + 1);
-        for (int e = tid; e < kBVT * DK; e += kBT) {
+        for (int e = tid; e < kBVT * DK; e += kCT) {
             const int i = e / DK, c = e % DK;
             R[L::oS + (i0 + i) * DK + c] = sS[i * SS + c];
         }
         constexpr float sgn = SPLIT ? 1.f : -1.f;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {   // Vt = U - W S^T  /  Y = Ut + W S^T
-            const int t = w + 4 * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            const f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
-                                      [&](int r, int c) { return sW[r * SW + c]; },
-                                      [&](int c, int i) { return sS[i * SS + c]; });
+            const int t = w + kCW * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+            const f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
+                                         [&](int r, int c) { return sW[r * SW + c]; },
+                                         [&](int c, int i) { return sS[i * SS + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
@@ -430,22 +463,43 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
             }
         }
         lds_only_barrier();
-        for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // S = S Diag(gamma) + ...
-            const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (SPLIT) {   // - Y^T Ebar + X^T Kbar
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return -sVt[r * SV + i]; },
-                              [&](int r, int c) { return sEb[r * SK + c]; });
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sXt[r * SV + i]; },
-                              [&](int r, int c) { return sKb[r * SK + c]; });
-            } else {                 // + Vt^T Kbar
-                acc = mm_tile(acc, ii0, cc0, 0, kBC, [&](int i, int r) { return sVt[r * SV + i]; },
-                              [&](int r, int c) { return sKb[r * SK + c]; });
+        // S = S Diag(gamma) + Vt^T Kbar  /  - Y^T Ebar + X^T Kbar.  Tile t covers state
+        // rows 16 (t % 2), channels 16 (t / 2); with two tiles per wave, t and t + kCW
+        // share their rows and run as one pair of chains.
+        constexpr int NTS = (kBVT / 16) * (DK / 16);
+        static_assert(NTS == kCW || NTS == 2 * kCW, "state tiles per wave");
+        {
+            const int t = w, ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
+            const int cc1 = cc0 + 16 * (kCW / (kBVT / 16));
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+            auto vt = [&](int i, int r) { return sVt[r * SV + i]; };
+            auto nvt = [&](int i, int r) { return -sVt[r * SV + i]; };
+            auto xt = [&](int i, int r) { return sXt[r * SV + i]; };
+            auto kb = [&](int r, int c) { return sKb[r * SK + c]; };
+            auto eb = [&](int r, int c) { return sEb[r * SK + c]; };
+            if constexpr (NTS == 2 * kCW) {
+                if constexpr (SPLIT) {
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, nvt, eb);
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, xt, kb);
+                } else {
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, vt, kb);
+                }
+            } else {
+                if constexpr (SPLIT) {
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, nvt, eb);
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, xt, kb);
+                } else {
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, vt, kb);
+                }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
-                sS[i * SS + c] = fmaf(sS[i * SS + c], sGam[c], acc[q]);
+                sS[i * SS + c] = fmaf(sS[i * SS + c], sGam[c], acc0[q]);
+                if constexpr (NTS == 2 * kCW) {
+                    const int c1 = cc1 + (l & 15);
+                    sS[i * SS + c1] = fmaf(sS[i * SS + c1], sGam[c1], acc1[q]);
+                }
             }
         }
         lds_only_barrier();
@@ -456,7 +510,7 @@ __global__ __launch_bounds__(kBT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 // Single step size:  dVt = Mq^T dO + Kbar dS'^T,     dS = dS' Diag(gamma) + dO^T Qhat - dVt^T W.
 // Split gates:       dY = -(Me^T dO + Ebar dS'^T),   dS = dS' Diag(gamma) + dO^T Qhat + dY^T W.
 template <class L, typename E, int DK, int DV, bool SPLIT>
-__global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, int N) {
+__global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, int N) {
     constexpr int NVT = DV / kBVT;
     // row strides against bank conflicts (see the forward chain), within the LDS:
     // 4 mod 64 words for operands read along rows (sdS, sA1), 8 mod 64 for those
@@ -474,14 +528,14 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    for (int e = tid; e < kBVT * DK; e += kBT) {
+    for (int e = tid; e < kBVT * DK; e += kCT) {
         const int i = e / DK, c = e % DK;
         sdS[i * SD + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
     // the previous chunk's operands are fetched into registers during this step
-    constexpr int NP = kBC * DK / 4 / kBT;
-    constexpr int NM = kBC * kBC / 4 / kBT;
-    constexpr int NO = kBC * kBVT / kBT;
+    constexpr int NP = kBC * DK / 4 / kCT;
+    constexpr int NM = kBC * kBC / 4 / kCT;
+    constexpr int NO = kBC * kBVT / kCT;
     float4 pM[NM], pA[NP], pQ[NP], pW[NP];
     float pO[NO];
     float pG = 0.f;
@@ -489,17 +543,17 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
         const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
 #pragma unroll
-        for (int j = 0; j < NM; ++j) pM[j] = *reinterpret_cast<const float4*>(R + L::oMq + 4 * (tid + kBT * j));
+        for (int j = 0; j < NM; ++j) pM[j] = *reinterpret_cast<const float4*>(R + L::oMq + 4 * (tid + kCT * j));
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int idx = 4 * (tid + kBT * j);
+            const int idx = 4 * (tid + kCT * j);
             pA[j] = *reinterpret_cast<const float4*>(R + (SPLIT ? L::oEb : L::oKb) + idx);
             pQ[j] = *reinterpret_cast<const float4*>(R + L::oQh + idx);
             pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
         }
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
-            const int e = tid + kBT * j, r = e / kBVT, i = e % kBVT;
+            const int e = tid + kCT * j, r = e / kBVT, i = e % kBVT;
             pO[j] = r < Cn ? load_elem<E>(p.dO, tok_index(p, b, t0 + r, h) * DV + i0 + i) : 0.f;
         }
         pG = tid < DK ? R[L::oGam + tid] : 0.f;
@@ -511,34 +565,34 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     for (int n = N - 1; n >= 0; --n) {
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
 #pragma unroll
-        for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kBT * j), SMQ, kBC, pM[j]);
+        for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kCT * j), SMQ, kBC, pM[j]);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int idx = 4 * (tid + kBT * j);
+            const int idx = 4 * (tid + kCT * j);
             put4(sA1, idx, SA, DK, pA[j]);
             put4(sQh, idx, SB, DK, pQ[j]);
             put4(sA2, idx, SB, DK, pW[j]);
         }
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
-            const int e = tid + kBT * j;
+            const int e = tid + kCT * j;
             sdO[(e / kBVT) * SO + e % kBVT] = pO[j];
         }
         if (tid < DK) sGam[tid] = pG;
         lds_only_barrier();
         if (n > 0) fetch(n - 1);
-        for (int e = tid; e < kBVT * DK; e += kBT) {
+        for (int e = tid; e < kBVT * DK; e += kCT) {
             const int i = e / DK, c = e % DK;
             R[L::odS + (i0 + i) * DK + c] = sdS[i * SD + c];
         }
         const int w = tid >> 6, l = tid & 63;
-        for (int t = w; t < (kBC / 16) * (kBVT / 16); t += 4) {   // dVt = Mq^T dO + Kbar dS^T
+        for (int t = w; t < (kBC / 16) * (kBVT / 16); t += kCW) {   // dVt = Mq^T dO + Kbar dS^T
             const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
-                                [&](int r, int m) { return sM[m * SMQ + r]; },
-                                [&](int m, int i) { return sdO[m * SO + i]; });
-            acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
-                          [&](int c, int i) { return sdS[i * SD + c]; });
+            f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
+                                   [&](int r, int m) { return sM[m * SMQ + r]; },
+                                   [&](int m, int i) { return sdO[m * SO + i]; });
+            acc = mm_tile_k2(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
+                             [&](int c, int i) { return sdS[i * SD + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, i = c0 + (l & 15);
@@ -548,24 +602,38 @@ __global__ __launch_bounds__(kBT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             }
         }
         lds_only_barrier();
-        for (int t = w; t < (kBVT / 16) * (DK / 16); t += 4) {   // dS = dS Diag(gamma) + dO^T Qhat -/+ dVt^T W
-            const int ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
-            f32x4 acc = mm_tile(f32x4{0.f, 0.f, 0.f, 0.f}, ii0, cc0, 0, kBC,
-                                [&](int i, int r) { return sdO[r * SO + i]; },
-                                [&](int r, int c) { return sQh[r * SB + c]; });
-            acc = mm_tile(acc, ii0, cc0, 0, kBC,
-                          [&](int i, int r) { return (SPLIT ? 1.f : -1.f) * sdVt[r * SO + i]; },
-                          [&](int r, int c) { return sA2[r * SB + c]; });
+        // dS = dS Diag(gamma) + dO^T Qhat -/+ dVt^T W, tiles paired as in the forward chain
+        constexpr int NTS = (kBVT / 16) * (DK / 16);
+        static_assert(NTS == kCW || NTS == 2 * kCW, "state tiles per wave");
+        {
+            const int t = w, ii0 = 16 * (t % (kBVT / 16)), cc0 = 16 * (t / (kBVT / 16));
+            const int cc1 = cc0 + 16 * (kCW / (kBVT / 16));
+            auto dot = [&](int i, int r) { return sdO[r * SO + i]; };
+            auto qh = [&](int r, int c) { return sQh[r * SB + c]; };
+            auto dvt = [&](int i, int r) { return (SPLIT ? 1.f : -1.f) * sdVt[r * SO + i]; };
+            auto wm = [&](int r, int c) { return sA2[r * SB + c]; };
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+            if constexpr (NTS == 2 * kCW) {
+                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dot, qh);
+                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dvt, wm);
+            } else {
+                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dot, qh);
+                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dvt, wm);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = ii0 + 4 * (l >> 4) + q, c = cc0 + (l & 15);
-                sdS[i * SD + c] = fmaf(sdS[i * SD + c], sGam[c], acc[q]);
+                sdS[i * SD + c] = fmaf(sdS[i * SD + c], sGam[c], acc0[q]);
+                if constexpr (NTS == 2 * kCW) {
+                    const int c1 = cc1 + (l & 15);
+                    sdS[i * SD + c1] = fmaf(sdS[i * SD + c1], sGam[c1], acc1[q]);
+                }
             }
         }
         lds_only_barrier();
     }
     if (p.gS0) {
-        for (int e = tid; e < kBVT * DK; e += kBT) {
+        for (int e = tid; e < kBVT * DK; e += kCT) {
             const int i = e / DK, c = e % DK;
             p.gS0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] = sdS[i * SD + c];
         }
@@ -1439,7 +1507,7 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
     float* ws = nullptr;
     e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
     if (e != hipSuccess) return e;
-    const dim3 blk(kBT);
+    const dim3 blk(kCT);
     const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
@@ -1527,7 +1595,7 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     float* ws = nullptr;
     e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
     if (e != hipSuccess) return e;
-    const dim3 blk(kBT);
+    const dim3 blk(kCT);
     const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     e = hipGetLastError();
