@@ -42,7 +42,7 @@
  *    must be 16-byte aligned.  The caller owns every buffer, and no per-call
  *    state is kept.  The only memory the library allocates is the temporary
  *    workspace of delta_fwd for DR_KDA, DR_GDN2 and DR_FG2 with DR_BF16 operands:
- *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2, DR_FG2: 50 KiB) for d_k = 128,
+ *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2: 50 KiB) for d_k = 128,
  *    21 KiB (29 KiB) for d_k = 64, taken from a library-owned stream-ordered
  *    memory pool of the current device and returned to it on the call's
  *    stream after use; the pool keeps freed memory for reuse until the

@@ -22,9 +22,10 @@ struct FwdArgs {
     float* ST;          // [B,H,dv,dk] or nullptr
     int Hk;             // query/key heads (divides H): q, k are [B,T,Hk,dk] and
                         // value head h reads query/key head h / (H / Hk)
-    int keywrite = 0;   // split-gate kernels only: 1 = FG^2-GDN, the residual is
+    int keywrite = 0;   // channel-decay kernels: 1 = FG^2-GDN, the residual is
                         // written along E = beta ⊙ k and there is no write gate
-                        // (the split form with W = V, A_k = A_e, M_k = M_e, Kb = Eb)
+                        // (the split form with W = V, A_k = A_e, M_k = M_e, Kb = Eb,
+                        // or the one-step-size form with E on the key side)
 };
 
 struct DecodeArgs {

@@ -17,9 +17,11 @@
 //   A_e = StrictTril(Kh Ex^T), A_k = StrictTril(Kh Kx^T), T = (I + A_e)^-1
 //   Z = X + A_k W, Y~ = T Z, O = Y + M_k W - M_e Y~
 //   S^T <- Diag(e^G_C) S^T + Kb^T W - Eb^T Y~
-// A step size per key channel (FG^2-GDN, FwdArgs::keywrite) is the split form
-// with the write along E = beta ⊙ K and no write gate: pass 1 stores A_e, M_e
-// and Eb where the split form has A_k, M_k and Kb, and pass 2 takes W = V.
+// A step size per key channel (FG^2-GDN, FwdArgs::keywrite) writes along
+// E = beta ⊙ K with no write gate.  As the split form it has W = V, A_k = A_e,
+// M_k = M_e and Kb = Eb, so Y~ = T (X + A_e V) and V - Y~ = T (V - X): it is the
+// one-step-size form with beta = 1 on the rows and E in place of K on the key
+// side of A, P and the state update, which is how it runs here.
 //
 // Everything above except X, Y and the state lines is the same for every
 // value tile of a head, and it is most of the work.  Pass 1 computes it once
@@ -110,7 +112,7 @@ struct PrepLds {
     static constexpr int oP = oTe + MM;                   // P or M_k
     static constexpr int oAk = oP + MM;
     static constexpr int oMe = oAk + (SPLIT ? MM : 0);
-    static constexpr int R1 = (SPLIT ? 2 : 1) * KM;
+    static constexpr int R1 = 2 * KM;   // raw g and raw b (split gates, or FG^2-GDN's step sizes)
     static constexpr int R2 = (SPLIT ? 2 : 1) * (KM + KE);
     static constexpr int R3 = 2 * MF + (SPLIT ? 4 : 2) * MM;
     static constexpr int RB = R1 > R2 ? (R1 > R3 ? R1 : R3) : (R2 > R3 ? R2 : R3);
@@ -181,12 +183,13 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
                 rq[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
                 rk[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + qoff);
                 rg[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.g) + off);
-                if constexpr (SPLIT) rb[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
+                if (SPLIT || p.keywrite) rb[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.beta) + off);
             }
         }
         if constexpr (!SPLIT) {
             rbeta = 0;
-            if (tid < ucn) rbeta = static_cast<const uint16_t*>(p.beta)[(utok + tid) * H + uh];
+            if (tid < ucn)   // FG^2-GDN: the step sizes sit on the key side, rows take 1
+                rbeta = p.keywrite ? uint16_t(0x3F80) : static_cast<const uint16_t*>(p.beta)[(utok + tid) * H + uh];
         }
     };
     if (static_cast<int>(blockIdx.x) < total) fetch(blockIdx.x);
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
         *reinterpret_cast<uint4*>(sQh + row * L::LDK + 8 * cc) = rq[j];
         *reinterpret_cast<uint4*>(sKh + row * L::LDK + 8 * cc) = rk[j];
         *reinterpret_cast<uint4*>(sRawG + row * L::LDK + 8 * cc) = rg[j];
-        if constexpr (SPLIT) *reinterpret_cast<uint4*>(sRawB + row * L::LDK + 8 * cc) = rb[j];
+        if (SPLIT || p.keywrite) *reinterpret_cast<uint4*>(sRawB + row * L::LDK + 8 * cc) = rb[j];
     }
     if constexpr (!SPLIT) {
         if (tid < C) sBeta[tid] = bf16_bits_to_f32(rbeta);
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
             g1[j] = v.y;
             p0 += v.x;
             p1 += v.y;
-            if constexpr (SPLIT) {
+            if (SPLIT || p.keywrite) {
                 const float2 bv = ld2(sRawB, r0 + j);
                 b0[j] = bv.x;
                 b1[j] = bv.y;
@@ -273,17 +276,20 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
             const float qh0 = qv.x * fh0, qh1 = qv.y * fh1;
             st2(sQh, r, qh0, qh1);
             st2(sQl, r, qh0 - bf16_bits_to_f32(f32_to_bf16_bits(qh0)), qh1 - bf16_bits_to_f32(f32_to_bf16_bits(qh1)));
-            st2(sKi, r, kv.x * fi0, kv.y * fi1);
-            st2(sKb, r, kv.x * fc0, kv.y * fc1);
+            // FG^2-GDN in the one-step-size form: the key-side copies (the columns of
+            // A and P, and the state update) carry the step sizes, E = beta ⊙ k
+            const bool kw = !SPLIT && p.keywrite;
+            const float kc0 = kw ? b0[j] * kv.x : kv.x, kc1 = kw ? b1[j] * kv.y : kv.y;
+            st2(sKi, r, kc0 * fi0, kc1 * fi1);
+            st2(sKb, r, kc0 * fc0, kc1 * fc1);
             // e^(G_end - G_r) = e^(G_b - G_r) e^(G_end - G_b), both within one block
             const float fe0 = fi0 * eb0, fe1 = fi1 * eb1;
-            if (my_block == 0) st2(sKe, r, kv.x * fe0, kv.y * fe1);
+            if (my_block == 0) st2(sKe, r, kc0 * fe0, kc1 * fe1);
             if constexpr (SPLIT) {
                 const float ev0 = b0[j] * kv.x, ev1 = b1[j] * kv.y;
                 st2(sEi, r, ev0 * fi0, ev1 * fi1);
                 st2(sEb, r, ev0 * fc0, ev1 * fc1);
                 if (my_block == 0) st2(sEe, r, ev0 * fe0, ev1 * fe1);
-                if (p.keywrite) st2(sKb, r, ev0 * fc0, ev1 * fc1);   // Kb = Eb
             }
         }
         if (rq == 0) {
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
                 int Rr, Jr;
                 task_rj(tix, Rr, Jr);
                 const bool useQ = mat == 1 || mat == 3;
-                const bool useE = SPLIT && (mat == 0 || mat == 3 || p.keywrite);
+                const bool useE = SPLIT && (mat == 0 || mat == 3);
                 const uint16_t* arow = (useQ ? sQh : sKh) + (16 * Rr + c) * L::LDK;
                 const uint16_t* bsrc = Jr == Rr ? (useE ? sEi : sKi) : (useE ? sEe : sKe);
                 const uint16_t* brow = bsrc + (16 * Jr + c) * L::LDK;
@@ -549,11 +555,7 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
         const int t = min(n * kC2 + row, T - 1);
         const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * DV + vc0 + 8 * (lane & 1);
         pv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + off);
-        if constexpr (SPLIT) {
-            // no write gate (keywrite): w = 1, so W = V exactly
-            pw = p.keywrite ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u)
-                            : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.wgate) + off);
-        }
+        if constexpr (SPLIT) pw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.wgate) + off);
     };
     const int vvo = (4 * g + (c >> 2)) * LDV + 4 * (c & 3);   // transpose reads of the staged rows
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -821,10 +823,10 @@ hipError_t workspace_pool(hipMemPool_t* pool) {
 }
 
 hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t s) {
-    if (variant == 2) return launch_two_pass_dims<false>(a, s);
     FwdArgs b = a;
     b.keywrite = variant == 4 ? 1 : 0;
-    return launch_two_pass_dims<true>(b, s);
+    if (variant == 3) return launch_two_pass_dims<true>(b, s);
+    return launch_two_pass_dims<false>(b, s);   // KDA, and FG^2-GDN in the one-step-size form
 }
 
 }  // namespace dr
