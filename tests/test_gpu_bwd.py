@@ -161,3 +161,21 @@ def test_autograd_function(variant):
            "dbeta": leaves["beta"].grad, "dwgate": None if leaves["wgate"] is None else leaves["wgate"].grad,
            "dg": None if leaves["g"] is None else leaves["g"].grad, "dS0": S0.grad}
     _check(variant, "f32", {n: (None if t is None else host(t)) for n, t in got.items()}, ref)
+
+
+@pytest.mark.parametrize("variant", VARS)
+def test_bwd_many_heads(variant):
+    """B*H = 330 heads: the chain kernels' XCD-aware head map with a partial last
+    group of 8 and more workgroups than CUs; 4 heads sampled against the oracle."""
+    announce("bwd_many_heads", variant)
+    w = Workload("t", variant, "bf16", B=6, H=55, T=70, dk=64, dv=64, random_s0=True, seed=49)
+    x = make_forward_inputs(w)
+    dO, dST = _upstream(w, 16)
+    gr = _run(variant, "bf16", w, x, dO, dST)
+    for b, h in [(0, 0), (2, 17), (5, 54), (4, 31)]:
+        sl = lambda a: None if a is None else a[[b]][:, :, [h]]  # noqa: E731
+        ref = oracle_bwd(variant, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["wgate"]),
+                         sl(x["g"]), x["S0"][[b]][:, [h]], sl(dO), dST[[b]][:, [h]])
+        got = {n: (None if a is None else (a[[b]][:, [h]] if n == "dS0" else sl(a)))
+               for n, a in gr.items()}
+        _check(variant, "bf16", got, ref)

@@ -244,3 +244,23 @@ def test_decode_continues_prefill_all_forms(variant, dtype):
     o_dec = np.stack(outs, axis=1)
     eo, es = errs(o_dec, host(S), o_ref[:, 97:], S_ref)
     assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+@pytest.mark.parametrize("variant", BUILT_VARIANTS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_heads_several_dispatch_rounds(variant, dtype):
+    """B*H = 330 heads (not a multiple of 8), so every kernel's grid holds more
+    workgroups than there are CUs and the XCD-aware head map has a partial last
+    group; 9 heads sampled against the oracle."""
+    announce("prefill_many_heads", variant, dtype)
+    w = Workload("t", variant, dtype, B=6, H=55, T=70, dk=64, dv=64, random_s0=True, seed=31)
+    x = make_forward_inputs(w)
+    o, S = gpu_fwd(variant, x, dtype)
+    rng = np.random.default_rng(3)
+    for b, h in zip(rng.integers(0, w.B, 9), rng.integers(0, w.H, 9)):
+        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
+               for n, a in x.items()}
+        o_ref, S_ref = oracle_fwd(variant, **sub)
+        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
+        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
+        assert eo <= TOL[dtype] and es <= TOL[dtype], (b, h, eo, es)
