@@ -513,9 +513,10 @@ template <class L, typename E, int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, int N) {
     constexpr int NVT = DV / kBVT;
     // row strides against bank conflicts (see the forward chain), within the LDS:
-    // 4 mod 64 words for operands read along rows (sdS, sA1), 8 mod 64 for those
-    // read down columns (at most two-way conflicts)
-    constexpr int SD = DK + 4, SA = DK + 4, SB = DK + 8, SO = kBVT + 8, SMQ = kBC + 8;
+    // 4 mod 64 words for operands read along rows (sdS, sA1); 16 mod 64 for dO and
+    // dVt, read down columns in both products (conflict-free); 8 mod 64 for the
+    // other column-read operands (at most two-way: 16 would not fit in 160 KB)
+    constexpr int SD = DK + 4, SA = DK + 4, SB = DK + 8, SO = kBVT + 16, SMQ = kBC + 8;
     __shared__ __attribute__((aligned(16))) float sdS[kBVT * SD];
     __shared__ __attribute__((aligned(16))) float sdVt[kBC * SO];
     __shared__ __attribute__((aligned(16))) float sdO[kBC * SO];
