@@ -376,7 +376,10 @@ def ttt_pre_fwd(variant: str, q, k, v, beta1, g1=None, beta2=None, g2=None, A0=N
     of the first layer; the query goes through the first layer after its write
     (readout after write, as in the delta rule) and the same SiLU and
     normalisation; each layer has its own step size and decay of the given
-    variant ("deltanet" or "gdn").  Per token, float64:
+    variant ("deltanet" or "gdn").  The structure (two delta-rule layers, the
+    Pre write key, two scans) is pinned; the choice of SiLU and of the unit
+    normalisation of h and z is parity unpinned: nothing on the pages fixes
+    them.  Per token, float64:
 
         A' = A a1_t;       r = A' k_t;     A = A' + beta1_t (v_t - r) k_t^T
         h  = unit(silu(r));                z = unit(silu(A q_t))
