@@ -3,7 +3,7 @@ import numpy as np
 import torch
 
 from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_decode_inputs, \
-    make_forward_inputs, round_to_bf16
+    make_forward_inputs, make_ttt_inputs, round_to_bf16
 
 
 def test_round_to_bf16_matches_torch():
@@ -33,7 +33,7 @@ def test_forward_inputs_shapes_and_ranges():
 
 def test_variant_layouts():
     for variant, bshape, gshape in [("deltanet", (1, 5, 2), None), ("gdn", (1, 5, 2), (1, 5, 2)),
-                                    ("kda", (1, 5, 2), (1, 5, 2, 4))]:
+                                    ("kda", (1, 5, 2), (1, 5, 2, 4)), ("fg2", (1, 5, 2, 4), (1, 5, 2, 4))]:
         x = make_forward_inputs(Workload("t", variant, "f32", 1, 2, 5, 4, 4, seed=1))
         assert x["beta"].shape == bshape and x["wgate"] is None and x["S0"] is None
         assert (x["g"] is None) == (gshape is None) and (gshape is None or x["g"].shape == gshape)
@@ -45,3 +45,22 @@ def test_decode_inputs():
     d = make_decode_inputs(small, 3)
     assert d["S"].shape == (3, 2, 8, 8) and len(d["steps"]) == 3
     assert d["steps"][0]["q"].shape == (3, 2, 8) and d["steps"][0]["g"].shape == (3, 2)
+
+
+def test_ttt_inputs():
+    w = Workload("t", "gdn", "bf16", B=2, H=3, T=7, dk=8, dv=4, seed=9)
+    x = make_ttt_inputs(w)
+    assert x["q"].shape == (2, 7, 3, 8) and x["v"].shape == (2, 7, 3, 4)
+    for n in ("beta1", "beta2", "g1", "g2"):
+        assert x[n].shape == (2, 7, 3)
+        assert np.array_equal(round_to_bf16(x[n]), x[n])
+    assert (x["beta2"] > 0).all() and (x["beta2"] < 1).all() and (x["g2"] <= 0).all()
+    assert x["A0"].shape == (2, 3, 4, 8) and x["B0"].shape == (2, 3, 4, 4)
+    # the first layer's inputs are the forward draw of the same seed
+    f = make_forward_inputs(w)
+    for a, b in (("q", "q"), ("k", "k"), ("v", "v"), ("beta1", "beta"), ("g1", "g")):
+        assert np.array_equal(x[a], f[b])
+    y = make_ttt_inputs(w)
+    assert all(np.array_equal(x[n], y[n]) for n in x)
+    z = make_ttt_inputs(Workload("t", "deltanet", "f32", B=1, H=1, T=3, dk=4, dv=4, seed=1), random_states=False)
+    assert z["g1"] is None and z["g2"] is None and z["A0"] is None and z["B0"] is None
