@@ -76,3 +76,18 @@ def test_decode_full_size_thousand_steps_sampled_heads():
     for i in (0, 1, 500, 999):
         assert slice_rel_err(outs[i][bs, hs], ref_outs[i][:, 0], (0,)) <= TOL["bf16"]
     assert slice_rel_err(S[bs, hs], S_ref[:, 0], (0,)) <= 1e-4
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
+def test_decode_full_size_channel_forms(variant):
+    """The decode batch (256 x 16 heads, d = 128, bf16) for the channel-decay forms:
+    3 steps, every head against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["gdn_decode_bf16_b256_h16_d128"], variant=variant)
+    announce("decode_full_channel", variant)
+    d = make_decode_inputs(w, 3)
+    outs, S = _run_steps(variant, "bf16", d, 3)
+    ref_outs, S_ref = _oracle_steps(variant, d, 3)
+    for o, r in zip(outs, ref_outs):
+        assert slice_rel_err(o, r, (0, 1)) <= TOL["bf16"]
+    assert slice_rel_err(S, S_ref, (0, 1)) <= 1e-5
