@@ -44,7 +44,7 @@ abstract names the two gates but prints no formula.  That reading is parity
 unpinned beyond the reduction to KDA at b = w = beta.  The FG^2-GDN reading is
 pinned to the per-coordinate gradient step it is named after and to its
 reduction to KDA at beta_t = beta·1; which axis carries the vector is the
-reading.  (No reverse mode is given for FG^2-GDN.)
+reading.
 
 Two further forms from the same topic page:
 
@@ -222,7 +222,7 @@ def delta_decode(variant: str, q, k, v, beta=None, wgate=None, g=None, S=None
     return o[:, 0], S_new
 
 
-def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=None):
+def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=None, keystep=None):
     """Reverse mode of ``run_recurrence`` (same argument layout, float64).
 
     Runs the recurrence forward keeping every state, then walks back one token
@@ -230,7 +230,8 @@ def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=N
     of the module docstring).  ``dO`` [N, T, dv] and ``dST`` [N, dv, dk] (or
     None) are the gradients arriving at o and at the final state.  Returns a
     dict with dq, dk, dv [N, T, d], da [N, T, dk] (gradient of the decay
-    factors), dbeta [N, T] or (derase [N, T, dk], dwrite [N, T, dv]) and dS0.
+    factors), dbeta [N, T] or (derase [N, T, dk], dwrite [N, T, dv]) or
+    dkeystep [N, T, dk], and dS0.
     """
     split = erase is not None
     N, T, dk = q.shape
@@ -243,6 +244,8 @@ def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=N
         if split:
             S = (Sp - r[:, :, None] * (erase[:, t, :] * kt)[:, None, :]
                  + (write[:, t, :] * v[:, t, :])[:, :, None] * kt[:, None, :])
+        elif keystep is not None:
+            S = Sp + (v[:, t, :] - r)[:, :, None] * (keystep[:, t, :] * kt)[:, None, :]
         else:
             S = Sp + beta[:, t, None, None] * (v[:, t, :] - r)[:, :, None] * kt[:, None, :]
         states.append(S)
@@ -251,6 +254,8 @@ def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=N
     if split:
         g["derase"] = np.zeros_like(erase)
         g["dwrite"] = np.zeros_like(write)
+    elif keystep is not None:
+        g["dkeystep"] = np.zeros_like(keystep)
     else:
         g["dbeta"] = np.zeros_like(beta)
     for t in range(T - 1, -1, -1):
@@ -272,6 +277,16 @@ def _recurrence_backward(S0, q, k, v, a, dO, dST, beta=None, erase=None, write=N
             g["dv"][:, t] = lam_k * write[:, t, :]
             dk_t = -lamT_r * erase[:, t, :] + (np.swapaxes(lam, 1, 2) @ wv[:, :, None])[:, :, 0]
             dr = -(lam @ eb[:, :, None])[:, :, 0]
+        elif keystep is not None:
+            # S_t = S' + u e^T with u = v - r, e = beta ⊙ k (beta per key channel)
+            ek = keystep[:, t, :] * kt
+            u = vt - r
+            lam_e = (lam @ ek[:, :, None])[:, :, 0]                    # Λ e        [N, dv]
+            de = (np.swapaxes(lam, 1, 2) @ u[:, :, None])[:, :, 0]     # Λ^T u      [N, dk]
+            g["dkeystep"][:, t] = de * kt
+            g["dv"][:, t] = lam_e
+            dk_t = de * keystep[:, t, :]
+            dr = -lam_e
         else:
             # S_t = S' + u k^T with u = beta (v - r)
             e = vt - r
@@ -310,8 +325,6 @@ def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=
     """
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
-    if variant == "fg2":
-        raise ValueError("no reverse mode for fg2")
     B, T, H, dv = np.shape(v)
     q0 = np.asarray(q, dtype=np.float64)
     Hk = q0.shape[2]
@@ -326,6 +339,8 @@ def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=
     if variant == "gdn2":
         gr = _recurrence_backward(S, qh, kh, _to_heads(v), a, dOh, dST,
                                   erase=_to_heads(beta), write=_to_heads(wgate))
+    elif variant == "fg2":
+        gr = _recurrence_backward(S, qh, kh, _to_heads(v), a, dOh, dST, keystep=_to_heads(beta))
     else:
         gr = _recurrence_backward(S, qh, kh, _to_heads(v), a, dOh, dST, beta=_to_heads(beta))
 
@@ -338,6 +353,8 @@ def delta_bwd(variant: str, q, k, v, beta=None, wgate=None, g=None, S0=None, dO=
     if variant == "gdn2":
         out["dbeta"] = _from_heads(gr["derase"], B, H)
         out["dwgate"] = _from_heads(gr["dwrite"], B, H)
+    elif variant == "fg2":
+        out["dbeta"] = _from_heads(gr["dkeystep"], B, H)
     else:
         out["dbeta"] = _from_heads(gr["dbeta"], B, H)
     if variant != "deltanet":

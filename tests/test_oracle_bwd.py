@@ -13,7 +13,7 @@ import torch
 
 from oracle import delta_bwd, delta_fwd
 
-VARIANTS = ["deltanet", "gdn", "kda", "gdn2"]
+VARIANTS = ["deltanet", "gdn", "kda", "gdn2", "fg2"]
 
 
 def _inputs(rng, variant, B=2, T=7, H=2, Hk=None, dk=4, dv=3):
@@ -23,12 +23,16 @@ def _inputs(rng, variant, B=2, T=7, H=2, Hk=None, dk=4, dv=3):
     if variant == "gdn2":
         x["beta"] = rng.uniform(0.1, 0.9, (B, T, H, dk))
         x["wgate"] = rng.uniform(0.1, 0.9, (B, T, H, dv))
+    elif variant == "fg2":
+        x["beta"] = rng.uniform(0.1, 0.9, (B, T, H, dk))
+        x["wgate"] = None
     else:
         x["beta"] = rng.uniform(0.1, 0.9, (B, T, H))
         x["wgate"] = None
     x["g"] = {"deltanet": None, "gdn": -rng.uniform(0, 1, (B, T, H)),
               "kda": -rng.uniform(0, 1, (B, T, H, dk)),
-              "gdn2": -rng.uniform(0, 1, (B, T, H, dk))}[variant]
+              "gdn2": -rng.uniform(0, 1, (B, T, H, dk)),
+              "fg2": -rng.uniform(0, 1, (B, T, H, dk))}[variant]
     dO = rng.standard_normal((B, T, H, dv))
     dST = rng.standard_normal((B, H, dv, dk))
     return x, dO, dST
@@ -84,6 +88,8 @@ def _torch_forward(variant, x):
         if variant == "gdn2":
             S = (Sp - r[..., :, None] * (x["beta"][:, t] * kt)[..., None, :]
                  + (x["wgate"][:, t] * vt)[..., :, None] * kt[..., None, :])
+        elif variant == "fg2":
+            S = Sp + (vt - r)[..., :, None] * (x["beta"][:, t] * kt)[..., None, :]
         else:
             S = Sp + x["beta"][:, t][..., None, None] * (vt - r)[..., :, None] * kt[..., None, :]
         outs.append(torch.einsum("bhij,bhj->bhi", S, qt))
