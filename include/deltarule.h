@@ -186,14 +186,14 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * a backward that keeps training chunkwise-parallel).  The forward states are
  * recomputed from the inputs; nothing from a delta_fwd call is needed.
  *
- *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd; DR_FG2
- *          returns DR_E_UNSUPPORTED (no backward for it)
+ *   desc, q, k, v, beta, wgate, g, S0   exactly as given to delta_fwd
  *   dO     [B, T, H, d_v] dtype: gradient arriving at o
  *   dS_T   [B, H, d_v, d_k] fp32: gradient arriving at the final state; NULL = 0
  *   dq, dk [B, T, H_k, d_k], dv [B, T, H, d_v]                     dtype (written)
- *   dbeta  [B, T, H]; DR_GDN2: gradient of the erase gate [B, T, H, d_k]   dtype (written)
+ *   dbeta  [B, T, H]; DR_GDN2: gradient of the erase gate, DR_FG2: of the step
+ *          sizes, [B, T, H, d_k]                                          dtype (written)
  *   dwgate DR_GDN2: gradient of the write gate [B, T, H, d_v]; otherwise must be NULL
- *   dg     DR_DELTANET: must be NULL; DR_GDN [B, T, H]; DR_KDA/DR_GDN2 [B, T, H, d_k]
+ *   dg     DR_DELTANET: must be NULL; DR_GDN [B, T, H]; DR_KDA/DR_GDN2/DR_FG2 [B, T, H, d_k]
  *          dtype (written): gradient of the log-decay g
  *   dS0    [B, H, d_v, d_k] fp32 (written), gradient of S0; NULL if not wanted
  *

@@ -263,7 +263,6 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
         if (st != DR_OK) return st;
-        if (desc->variant == DR_FG2) return DR_E_UNSUPPORTED;
         if (q == nullptr || k == nullptr || v == nullptr || dO == nullptr || dq == nullptr ||
             dk == nullptr || dv == nullptr || dbeta == nullptr)
             return DR_E_NULLPTR;

@@ -244,10 +244,12 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         sX[r * LD + c] = ok ? load_elem<E>(p.q, qi * DK + c) : 0.f;
         float gv = 0.f;
         if constexpr (VAR == 1) gv = ok ? load_elem<E>(p.g, ti) : 0.f;
-        if constexpr (VAR == 2) gv = ok ? load_elem<E>(p.g, ti * DK + c) : 0.f;
+        if constexpr (VAR >= 2) gv = ok ? load_elem<E>(p.g, ti * DK + c) : 0.f;
         sG[r * (DK + 4) + c] = gv;
     }
-    if (tid < kBC) sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tok_index(p, b, t0 + tid, h)) : 0.f;
+    // FG^2-GDN (VAR 4): the step sizes sit on the key side (E = beta ⊙ k in the
+    // columns of Abar and Mq and in Kbar); the rows take 1
+    if (tid < kBC) sBeta[tid] = tid < Cn ? (VAR == 4 ? 1.f : load_elem<E>(p.beta, tok_index(p, b, t0 + tid, h))) : 0.f;
     __syncthreads();
     if (tid < DK) {   // in-chunk cumulative log-decay per channel
         float acc = 0.f;
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     // Abar (strictly lower) and Mq (lower, diagonal included)
     const int w = tid >> 6, l = tid & 63;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (VAR == 2) {
+    if constexpr (VAR >= 2) {
         // a factor per channel: e^{G_r - G_j} = e^{G_r - G_ref} e^{G_ref - G_j} with the
         // reference at the last row of j's 16-row block, folded into the operands of
         // each tile product (at most e^{85} inside one block under the decay bound)
@@ -271,7 +273,11 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
             f32x4 ab = z4, mq = z4;
             if (j0 <= r0) {
                 const float* gref = sG + (j0 + 15) * (DK + 4);
-                auto Bk = [&](int c, int j) { return sK[j * (DK + 4) + c] * __expf(gref[c] - sG[j * (DK + 4) + c]); };
+                auto Bk = [&](int c, int j) {
+                    float x = sK[j * (DK + 4) + c] * __expf(gref[c] - sG[j * (DK + 4) + c]);
+                    if constexpr (VAR == 4) x *= load_elem<E>(p.beta, tok_index(p, b, t0 + min(j, Cn - 1), h) * DK + c);
+                    return x;
+                };
                 ab = mm_tile(z4, r0, j0, 0, DK,
                              [&](int r, int c) { return sK[r * (DK + 4) + c] * __expf(sG[r * (DK + 4) + c] - gref[c]); }, Bk);
                 mq = mm_tile(z4, r0, j0, 0, DK,
@@ -317,7 +323,9 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         const float kk = sK[r * (DK + 4) + c];
         R[L::oKh + e] = kk * eg;
         R[L::oQh + e] = sX[r * LD + c] * eg;
-        R[L::oKb + e] = kk * __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
+        float kb = kk * __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
+        if constexpr (VAR == 4) kb *= load_elem<E>(p.beta, tok_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
+        R[L::oKb + e] = kb;
         sX[r * LD + c] = sBeta[r] * kk * eg;
     }
     __syncthreads();
@@ -674,7 +682,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     constexpr int TCV = (kBC / 16) * (DV / 16);   // C x DV tiles
     constexpr int TCC = (kBC / 16) * (kBC / 16);  // C x C tiles
 
-    if (tid < kBC) sBeta[tid] = tid < Cn ? load_elem<E>(p.beta, tix(tid)) : 0.f;
+    if (tid < kBC) sBeta[tid] = tid < Cn ? (VAR == 4 ? 1.f : load_elem<E>(p.beta, tix(tid))) : 0.f;
     for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Vt -> R1, dVt -> R2
         const int r = e / DV, i = e % DV;
         R0[r * LD + i] = r < Cn ? load_elem<E>(p.dO, tix(r) * DV + i) : 0.f;
@@ -847,7 +855,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    {   // dbeta: kRT threads per row, fixed-order sums
+    if constexpr (VAR != 4) {   // dbeta: kRT threads per row, fixed-order sums
         const int r = tid / kRT, qt = tid % kRT;
         float db = 0.f;
         for (int c = qt * (DK / kRT); c < (qt + 1) * (DK / kRT); ++c)
@@ -904,7 +912,58 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         R[L::odQh + e] = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg
                          - dKb * kr * ebar;
     };
-    if constexpr (VAR == 2) {
+    if constexpr (VAR == 4) {
+        // FG^2-GDN: the key is k on the row side (Khat, the rows of Abar) and
+        // e = beta ⊙ k on the column side (the columns of Abar and Mq, Kbar).
+        // a2 and a4 (sums over the column index) are gradients of e; a1 and a3
+        // take e as their operand.  Pass 1 forms a2 + a4 with q and k in R0, R1;
+        // R1 then becomes e for pass 2.
+        auto Gf = [&](int r, int c) { return R2[r * LD + c]; };
+        auto M1 = [&](int r, int j) { return sM1[r * CP + j]; };
+        auto M2 = [&](int r, int j) { return sM2[r * CP + j]; };
+        auto Qf = [&](int j, int c) { return R0[j * LD + c]; };
+        auto Kf = [&](int j, int c) { return R1[j * LD + c]; };
+        constexpr int MTG = TCD / kGW;
+        static_assert(TCD % kGW == 0, "tiles per wave");
+        f32x4 colg[MTG];
+#pragma unroll
+        for (int m = 0; m < MTG; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            colg[m] = pair_tile<false>(r0, c0, M1, Qf, Gf) + pair_tile<false>(r0, c0, M2, Kf, Gf);
+        }
+        __syncthreads();
+        for (int e = tid; e < kBC * DK; e += kGT) {
+            const int r = e / DK, c = e % DK;
+            R1[r * LD + c] *= r < Cn ? load_elem<E>(p.beta, tix(r) * DK + c) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MTG; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const Pre pr = preload(r0, c0);
+            const f32x4 a1 = pair_tile<true>(r0, c0, M1, Kf, Gf);
+            const f32x4 a3 = pair_tile<true>(r0, c0, M2, Kf, Gf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = ti(r0, q), c = tj(c0);
+                const float Gr = R2[r * LD + c];
+                const float qr = R0[r * LD + c], er = R1[r * LD + c];
+                const bool ok = r < Cn;
+                const float kr = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
+                const float br = ok ? load_elem<E>(p.beta, tix(r) * DK + c) : 0.f;
+                const float eg = __expf(Gr), ebar = __expf(R2[(kBC - 1) * LD + c] - Gr);
+                const float dKh = pr.dX[q];                     // rows carry beta = 1
+                const float dE = colg[m][q] + pr.dKb[q] * ebar;  // gradient of e_r
+                if (ok) {
+                    store_qk_grad<E>(p.gq, p.gq32, tix(r), DK, c, fmaf(pr.dQh[q], eg, a1[q]));
+                    store_qk_grad<E>(p.gk, p.gk32, tix(r), DK, c, a3[q] + dKh * eg + br * dE);
+                    store_elem<E>(p.gbeta, tix(r) * DK + c, kr * dE);
+                }
+                R[L::odQh + r * DK + c] = qr * a1[q] - er * colg[m][q] + kr * a3[q] + dKh * kr * eg +
+                                          pr.dQh[q] * qr * eg - pr.dKb[q] * er * ebar;
+            }
+        }
+    } else if constexpr (VAR == 2) {
         auto Gf = [&](int r, int c) { return R2[r * LD + c]; };
         auto M1 = [&](int r, int j) { return sM1[r * CP + j]; };
         auto M2 = [&](int r, int j) { return sM2[r * CP + j]; };
@@ -962,7 +1021,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
             for (int r = kBC - 1; r >= 0; --r) {
                 acc += dgv[r];
-                if constexpr (VAR == 2) {
+                if constexpr (VAR >= 2) {
                     if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, acc);
                 } else {
                     R[L::odQh + r * DK + c] = acc;
@@ -1637,6 +1696,7 @@ hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t s) {
         case 0: return launch_bwd_dtype<0>(dtype, a, s);
         case 1: return launch_bwd_dtype<1>(dtype, a, s);
         case 2: return launch_bwd_dtype<2>(dtype, a, s);
+        case 4: return launch_bwd_dtype<4>(dtype, a, s);
         default: return dtype == 0 ? bwd_with_groups<F32>(a, s, launch_bwd2_dtype<F32>)
                                    : bwd_with_groups<BF16>(a, s, launch_bwd2_dtype<BF16>);
     }

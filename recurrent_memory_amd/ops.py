@@ -240,9 +240,7 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dt, dev = q.dtype, q.device
     if dt not in DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    if variant == "fg2":
-        raise ValueError("no backward for fg2")
-    bshape = (B, T, H, dk) if variant == "gdn2" else (B, T, H)
+    bshape = (B, T, H, dk) if variant in _CHANNEL_BETA else (B, T, H)
     for name, t, shape in (("q", q, (B, T, Hk, dk)), ("k", k, (B, T, Hk, dk)), ("v", v, (B, T, H, dv)),
                            ("beta", beta, bshape), ("dO", dO, (B, T, H, dv))):
         _check(name, t, shape, dt, dev)

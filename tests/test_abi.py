@@ -152,7 +152,7 @@ def test_bwd_validation():
     assert bwd(desc(variant=3)) == DR_E_NULLPTR                 # split gates need the write gate
     assert bwd(desc(variant=3), wgate=FAKE[6]) == DR_E_NULLPTR  # ... and its gradient
     assert bwd(desc(variant=1), dwgate=FAKE[6]) == DR_E_UNSUPPORTED
-    assert bwd(desc(variant=4)) == DR_E_UNSUPPORTED             # no backward for FG^2-GDN
+    assert bwd(desc(variant=4), wgate=FAKE[6]) == DR_E_UNSUPPORTED   # FG^2-GDN has no write gate
     assert bwd(desc(), dq=FAKE[0]) == DR_E_ALIAS                # dq over q
     assert bwd(desc(), dv=FAKE[8]) == DR_E_ALIAS                # dv over dk
     assert bwd(desc(), dS0=ctypes.c_void_p(FAKE[6].value + 4)) == DR_E_ALIGN

@@ -16,7 +16,7 @@ from recurrent_memory_amd.inputs import Workload, make_forward_inputs
 
 pytestmark = pytest.mark.gpu
 
-VARS = ["deltanet", "gdn", "kda", "gdn2"]
+VARS = ["deltanet", "gdn", "kda", "gdn2", "fg2"]
 
 
 def _upstream(w, seed):
@@ -84,7 +84,7 @@ def test_bwd_no_state_gradient(variant):
     _check(variant, "f32", gr, ref)
 
 
-@pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2", "fg2"])
 def test_bwd_long_sampled_heads(variant):
     """bf16, B=2, H=16, T=1024, d=128: two heads checked against the oracle."""
     announce("bwd_long", variant)
@@ -111,7 +111,7 @@ def test_bwd_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
-@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_strong_channel_gates(variant, dtype):
     """Log-decays scaled by 3 (16-token sums near -35): the block-reference factors
