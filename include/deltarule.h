@@ -197,17 +197,18 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *          dtype (written): gradient of the log-decay g
  *   dS0    [B, H, d_v, d_k] fp32 (written), gradient of S0; NULL if not wanted
  *
- * Channel-wise decays (DR_KDA, DR_GDN2) obey the same bound as in delta_fwd: the
- * log-decay of a channel summed over any 16 consecutive tokens must stay above
- * about -85 (pairwise factors are split at a reference row of each 16-token block).
+ * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) obey the same bound as in
+ * delta_fwd: the log-decay of a channel summed over any 16 consecutive tokens
+ * must stay above about -85 (pairwise factors are split at a reference row of
+ * each 16-token block).
  *
  * Grouped query/key heads (H_k < H): q, k, dq and dk are [B, T, H_k, d_k]; dq and
  * dk are summed over each group of value heads, through two extra fp32 buffers of
  * [B, T, H, d_k] from the pool.  Outputs must not overlap any input or one another.
  * Arithmetic is fp32 throughout.  Workspace: B * H * ceil(T / 64) records of
  * 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB for d_k/d_v = 128/64,
- * 64/128, 64/64), for DR_GDN2 768.5 KiB (640.5, 464.5, 384.25), from the same
- * pool as delta_fwd's, returned on the call's stream.
+ * 64/128, 64/64; DR_FG2 the same), for DR_GDN2 768.5 KiB (640.5, 464.5,
+ * 384.25), from the same pool as delta_fwd's, returned on the call's stream.
  */
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,
