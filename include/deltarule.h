@@ -40,35 +40,41 @@
  *  - All tensor arguments are DEVICE pointers on the current HIP device, dense
  *    and row-major with the shapes given below (no strides).  Every pointer
  *    must be 16-byte aligned.  The caller owns every buffer, and no per-call
- *    state is kept.  The only memory the library allocates is the temporary
- *    workspace of delta_fwd for DR_KDA, DR_GDN2 and DR_FG2 with DR_BF16 operands:
- *    B * H * ceil(T / 32) blocks of 38 KiB (DR_GDN2: 50 KiB) for d_k = 128,
- *    21 KiB (29 KiB) for d_k = 64, taken from a library-owned stream-ordered
- *    memory pool of the current device and returned to it on the call's
- *    stream after use; the pool keeps freed memory for reuse until the
- *    process ends.  A failed workspace allocation is reported as DR_E_LAUNCH.
+ *    state is kept.  The library allocates no device memory.
+ *  - Workspace.  delta_fwd (channel-wise decay forms with DR_BF16 operands),
+ *    delta_bwd and delta_ttt_pre need temporary device memory, which the caller
+ *    passes as (workspace, workspace_bytes).  The matching *_workspace_bytes
+ *    query returns the size for a descriptor (0 when none is needed; then
+ *    workspace may be NULL).  A needed workspace must be 256-byte aligned, at
+ *    least that large (DR_E_WORKSPACE otherwise) and disjoint from every tensor
+ *    argument (DR_E_ALIAS).  Its contents on entry do not matter and are
+ *    undefined on return; calls that share one workspace must be ordered (one
+ *    stream, or events), otherwise they race.
  *  - dtype (dr_desc.dtype) is the element type of q, k, v, beta, wgate, g and
  *    o.  The state (S0, S_T, S) is always fp32.
  *  - The stream argument is a hipStream_t (NULL = the null stream).  Calls are
  *    asynchronous: they enqueue kernels and return without synchronising.
- *    delta_bwd takes a larger workspace from the same pool (see there).
  *  - Every argument is validated on the host before any HIP call.  Errors are
  *    returned as a dr_status and never abort; C++ exceptions never cross the
  *    ABI.  On an error nothing has been enqueued and no output was touched.
  *  - Results are deterministic: no atomics, fixed reduction order.
  *  - Supported sizes: d_k, d_v in {64, 128}; chunk = 64; any T >= 1 (the
- *    last chunk is masked when T is not a multiple of 64).
+ *    last chunk is masked when T is not a multiple of 64).  Limits (DR_E_SHAPE
+ *    beyond them): B * T * H <= 2^34, B * H <= 2^20, B * H * ceil(T / 64)
+ *    <= 2^22 and H <= 2^18 - 1, which keep every grid and every 32-bit offset
+ *    inside a chunk within range.
  */
 #ifndef DELTARULE_H
 #define DELTARULE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 4
+#define DR_ABI_VERSION 5
 
 typedef enum {
     DR_DELTANET = 0, /* a = 1: no decay, g must be NULL                          */
@@ -84,13 +90,17 @@ typedef enum {
     DR_OK = 0,
     DR_E_NULLPTR = 1,     /* a required pointer (or the descriptor) is NULL       */
     DR_E_SHAPE = 2,       /* a size is out of range (B, T, H < 1, decode T != 1,
-                             H_k < 0, H_k > H or H_k not dividing H)             */
+                             H_k < 0, H_k > H or H_k not dividing H, or beyond
+                             the limits stated above)                           */
     DR_E_UNSUPPORTED = 3, /* unknown variant/dtype, unsupported d_k/d_v/chunk, or
                              a pointer given that the variant does not take     */
-    DR_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
+    DR_E_ALIGN = 4,       /* a pointer is not 16-byte aligned (the workspace: not
+                             256-byte aligned)                                  */
     DR_E_DEVICE = 5,      /* no HIP device, or the current device is not gfx950   */
     DR_E_LAUNCH = 6,      /* the kernel launch failed (hipGetLastError)           */
-    DR_E_ALIAS = 7        /* an output overlaps an input it may not alias         */
+    DR_E_ALIAS = 7,       /* an output overlaps an input it may not alias, or the
+                             workspace overlaps a tensor argument                */
+    DR_E_WORKSPACE = 8    /* workspace NULL or smaller than the size query says  */
 } dr_status;
 
 typedef struct {
@@ -128,15 +138,23 @@ typedef struct {
  *          may be the same pointer as S0 (in-place update) but must not
  *          otherwise overlap an input
  *
+ *   workspace, workspace_bytes
+ *          device workspace of at least delta_fwd_workspace_bytes(desc) bytes
+ *          (see the conventions above); NULL and 0 when that is 0.  Only the
+ *          channel-wise forms with DR_BF16 operands use one: B * H * ceil(T / 32)
+ *          blocks of 38 KiB (DR_GDN2: 50 KiB) for d_k = 128, 21 KiB (29 KiB) for
+ *          d_k = 64, rounded up to 256 bytes
+ *
  * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) are evaluated with exponents taken
  * relative to the boundaries of 16-token blocks: the log-decay of one channel
  * summed over any 16 consecutive tokens must stay above about -85 (a decay
  * factor of e^-85), otherwise a split factor leaves the fp32 range and the
  * outputs become inf/NaN.  Per-token decays down to e^-5 always satisfy this.
  */
+dr_status delta_fwd_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,
-                    void* o, float* S_T, void* stream);
+                    void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * delta_decode — one token per sequence, state updated in place.
@@ -203,17 +221,23 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * each 16-token block).
  *
  * Grouped query/key heads (H_k < H): q, k, dq and dk are [B, T, H_k, d_k]; dq and
- * dk are summed over each group of value heads, through two extra fp32 buffers of
- * [B, T, H, d_k] from the pool.  Outputs must not overlap any input or one another.
- * Arithmetic is fp32 throughout.  Workspace: B * H * ceil(T / 64) records of
- * 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB for d_k/d_v = 128/64,
- * 64/128, 64/64; DR_FG2 the same), for DR_GDN2 768.5 KiB (640.5, 464.5,
- * 384.25), from the same pool as delta_fwd's, returned on the call's stream.
+ * dk are summed over each group of value heads, through two fp32 buffers of
+ * [B, T, H, d_k] at the end of the workspace.  Outputs must not overlap any input
+ * or one another.  Arithmetic is fp32 throughout.
+ *
+ *   workspace, workspace_bytes
+ *          at least delta_bwd_workspace_bytes(desc) bytes: B * H * ceil(T / 64)
+ *          records of 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB
+ *          for d_k/d_v = 128/64, 64/128, 64/64; DR_FG2 the same), for DR_GDN2
+ *          768.5 KiB (640.5, 464.5, 384.25), rounded up to 256 bytes, plus the
+ *          two grouped-head buffers when H_k < H
  */
+dr_status delta_bwd_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,
                     const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
-                    void* dbeta, void* dwgate, void* dg, float* dS0, void* stream);
+                    void* dbeta, void* dwgate, void* dg, float* dS0, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * delta_ttt_pre — DeltaTTT-pre: a two-layer memory whose layers each learn by
@@ -248,15 +272,18 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
  *   A_T, B_T  final states, fp32 (written) or NULL; A_T may be A0 and B_T may be
  *          B0 (in place), otherwise no output may overlap an input or another output
  *
- * The intermediate tensors (shifted queries, reads, first-layer readouts, keys
- * and queries of the second layer) are kept in the input dtype, in a workspace
- * of 2 * B * T * H * (d_k + 4 d_v) + 2 * B * H * d_v bytes (bf16; twice that for
- * fp32) from the pool of delta_fwd, returned on the call's stream.  No backward.
+ *   workspace, workspace_bytes
+ *          at least delta_ttt_pre_workspace_bytes(desc) bytes: the intermediate
+ *          tensors (shifted queries, reads, first-layer readouts, keys and
+ *          queries of the second layer), each rounded up to 256 bytes.
+ *
+ * No backward.
  */
+dr_status delta_ttt_pre_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_ttt_pre(const dr_desc* desc, const void* q, const void* k, const void* v,
                         const void* beta1, const void* g1, const void* beta2, const void* g2,
                         const float* A0, const float* B0, void* o, float* A_T, float* B_T,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* dr_status_str(int status);

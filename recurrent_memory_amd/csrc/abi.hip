@@ -48,9 +48,16 @@ dr_status check_desc(const dr_desc* d, bool decode, Sizes* sz) {
     if (d->H_k < 0 || d->H_k > d->H || (d->H_k > 0 && d->H % d->H_k != 0)) return DR_E_SHAPE;
     sz->Hk = d->H_k == 0 ? d->H : d->H_k;
     const int64_t tok = static_cast<int64_t>(d->B) * d->T * d->H;
-    // Keep every element index well inside int64 and every grid within limits.
-    if (tok > (int64_t(1) << 34) || static_cast<int64_t>(d->B) * d->H > (int64_t(1) << 30))
-        return DR_E_SHAPE;
+    // Keep every element index inside int64, every grid below 2^31 threads
+    // (the widest grids: 8 value tiles of 256 threads per head, and one
+    // 512-thread workgroup per 64-token chunk of every head in the backward)
+    // and the kernels' 32-bit offsets within a chunk (64 rows of H_k heads of
+    // d_k elements) below 2^31.
+    if (tok > (int64_t(1) << 34)) return DR_E_SHAPE;
+    const int64_t heads = static_cast<int64_t>(d->B) * d->H;
+    if (heads > (int64_t(1) << 20)) return DR_E_SHAPE;
+    if (heads * ((d->T + 63) / 64) > (int64_t(1) << 22)) return DR_E_SHAPE;
+    if (static_cast<int64_t>(d->H) * 64 * 128 > (int64_t(1) << 31) - 1) return DR_E_SHAPE;
     sz->qk = static_cast<int64_t>(d->B) * d->T * sz->Hk * d->d_k;
     sz->v = tok * d->d_v;
     sz->beta = (d->variant == DR_GDN2 || d->variant == DR_FG2) ? tok * d->d_k : tok;
@@ -72,6 +79,20 @@ dr_status check_gate_ptrs(const dr_desc* d, const void* beta, const void* wgate,
     } else if (g == nullptr) {
         return DR_E_NULLPTR;
     }
+    return DR_OK;
+}
+
+// The caller's workspace: present and large enough when one is needed,
+// 256-byte aligned, and disjoint from every tensor argument.
+dr_status check_workspace(size_t need, const void* ws, size_t ws_bytes, const Span* spans, int n) {
+    if (need == 0) return DR_OK;
+    if (ws == nullptr || ws_bytes < need) return DR_E_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DR_E_ALIGN;
+    Span w;
+    w.lo = reinterpret_cast<uintptr_t>(ws);
+    w.hi = w.lo + need;
+    for (int i = 0; i < n; ++i)
+        if (overlap(w, spans[i])) return DR_E_ALIAS;
     return DR_OK;
 }
 
@@ -102,9 +123,23 @@ dr_status check_device() {
 
 extern "C" {
 
+dr_status delta_fwd_workspace_bytes(const dr_desc* desc, size_t* bytes) {
+    try {
+        if (bytes == nullptr) return DR_E_NULLPTR;
+        Sizes sz;
+        const dr_status st = check_desc(desc, false, &sz);
+        if (st != DR_OK) return st;
+        *bytes = dr::fwd_workspace_bytes(desc->variant, desc->dtype, desc->B, desc->T, desc->H,
+                                         desc->d_k, desc->d_v);
+        return DR_OK;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
 dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,
-                    void* o, float* S_T, void* stream) {
+                    void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
     try {
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
@@ -130,11 +165,17 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
         if (overlap(sst, in[6]) && static_cast<const void*>(S_T) != static_cast<const void*>(S0))
             return DR_E_ALIAS;
         if (overlap(sst, so)) return DR_E_ALIAS;
+        const size_t need = dr::fwd_workspace_bytes(desc->variant, desc->dtype, desc->B, desc->T,
+                                                    desc->H, desc->d_k, desc->d_v);
+        const Span all[] = {in[0], in[1], in[2], in[3], in[4], in[5], in[6], so, sst};
+        st = check_workspace(need, workspace, workspace_bytes, all, 9);
+        if (st != DR_OK) return st;
 
         st = check_device();
         if (st != DR_OK) return st;
         dr::FwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g,
                       S0, o, S_T, sz.Hk};
+        a.ws = need ? workspace : nullptr;
         const hipError_t e = dr::launch_fwd(desc->variant, desc->dtype, a,
                                             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
@@ -180,16 +221,36 @@ dr_status delta_decode(const dr_desc* desc, const void* q, const void* k, const 
     }
 }
 
+// DeltaTTT-pre's extra shape rules (both layers DeltaNet or GDN, no grouped heads)
+dr_status check_ttt_desc(const dr_desc* desc, Sizes* sz) {
+    const dr_status st = check_desc(desc, false, sz);
+    if (st != DR_OK) return st;
+    if (desc->variant != DR_DELTANET && desc->variant != DR_GDN) return DR_E_UNSUPPORTED;
+    if (sz->Hk != desc->H) return DR_E_UNSUPPORTED;
+    return DR_OK;
+}
+
+dr_status delta_ttt_pre_workspace_bytes(const dr_desc* desc, size_t* bytes) {
+    try {
+        if (bytes == nullptr) return DR_E_NULLPTR;
+        Sizes sz;
+        const dr_status st = check_ttt_desc(desc, &sz);
+        if (st != DR_OK) return st;
+        *bytes = dr::ttt_workspace_bytes(desc->dtype, desc->B, desc->T, desc->H, desc->d_k, desc->d_v);
+        return DR_OK;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
 dr_status delta_ttt_pre(const dr_desc* desc, const void* q, const void* k, const void* v,
                         const void* beta1, const void* g1, const void* beta2, const void* g2,
                         const float* A0, const float* B0, void* o, float* A_T, float* B_T,
-                        void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream) {
     try {
         Sizes sz;
-        dr_status st = check_desc(desc, false, &sz);
+        dr_status st = check_ttt_desc(desc, &sz);
         if (st != DR_OK) return st;
-        if (desc->variant != DR_DELTANET && desc->variant != DR_GDN) return DR_E_UNSUPPORTED;
-        if (sz.Hk != desc->H) return DR_E_UNSUPPORTED;
         if (q == nullptr || k == nullptr || v == nullptr || beta1 == nullptr || beta2 == nullptr ||
             o == nullptr)
             return DR_E_NULLPTR;
@@ -218,11 +279,17 @@ dr_status delta_ttt_pre(const dr_desc* desc, const void* q, const void* k, const
                 return DR_E_ALIAS;
         }
         if (overlap(sa, so) || overlap(sb, so) || overlap(sa, sb)) return DR_E_ALIAS;
+        const size_t need = dr::ttt_workspace_bytes(desc->dtype, desc->B, desc->T, desc->H, desc->d_k,
+                                                    desc->d_v);
+        const Span all[] = {in[0], in[1], in[2], in[3], in[4], in[5], in[6], in[7], in[8], so, sa, sb};
+        st = check_workspace(need, workspace, workspace_bytes, all, 12);
+        if (st != DR_OK) return st;
 
         st = check_device();
         if (st != DR_OK) return st;
         dr::TttArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta1, g1, beta2, g2,
                       A0, B0, o, A_T, B_T};
+        a.ws = workspace;
         const hipError_t e = dr::launch_ttt_pre(desc->variant, desc->dtype, a, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
     } catch (...) {
@@ -255,10 +322,25 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
     }
 }
 
+dr_status delta_bwd_workspace_bytes(const dr_desc* desc, size_t* bytes) {
+    try {
+        if (bytes == nullptr) return DR_E_NULLPTR;
+        Sizes sz;
+        const dr_status st = check_desc(desc, false, &sz);
+        if (st != DR_OK) return st;
+        *bytes = dr::bwd_workspace_bytes(desc->variant, desc->B, desc->T, desc->H, sz.Hk, desc->d_k,
+                                         desc->d_v);
+        return DR_OK;
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,
                     const void* beta, const void* wgate, const void* g, const float* S0,
                     const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
-                    void* dbeta, void* dwgate, void* dg, float* dS0, void* stream) {
+                    void* dbeta, void* dwgate, void* dg, float* dS0, void* workspace,
+                    size_t workspace_bytes, void* stream) {
     try {
         Sizes sz;
         dr_status st = check_desc(desc, false, &sz);
@@ -289,11 +371,18 @@ dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const voi
             for (int j = 0; j < i; ++j)
                 if (overlap(out[i], out[j])) return DR_E_ALIAS;
         }
+        const size_t need = dr::bwd_workspace_bytes(desc->variant, desc->B, desc->T, desc->H, sz.Hk,
+                                                    desc->d_k, desc->d_v);
+        const Span all[] = {in[0], in[1], in[2], in[3], in[4], in[5], in[6], in[7], in[8],
+                            out[0], out[1], out[2], out[3], out[4], out[5], out[6]};
+        st = check_workspace(need, workspace, workspace_bytes, all, 16);
+        if (st != DR_OK) return st;
 
         st = check_device();
         if (st != DR_OK) return st;
         dr::BwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, g, S0, dO,
                       dS_T, dq, dk, dv, dbeta, dg, dS0, wgate, dwgate, sz.Hk, nullptr, nullptr};
+        a.ws = workspace;
         const hipError_t e = dr::launch_bwd(desc->variant, desc->dtype, a,
                                             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
@@ -312,6 +401,7 @@ const char* dr_status_str(int s) {
         case DR_E_DEVICE: return "no gfx950 HIP device";
         case DR_E_LAUNCH: return "kernel launch failed";
         case DR_E_ALIAS: return "output overlaps an input";
+        case DR_E_WORKSPACE: return "workspace missing or smaller than the size query reports";
         default: return "unknown status";
     }
 }

@@ -1557,34 +1557,27 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 
 template <typename E, int DK, int DV>
 hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
-    typedef BwdWs2<DK, DV> L;
     const int N = (a.T + kBC - 1) / kBC;
     const int64_t units = static_cast<int64_t>(a.B) * a.H * N;
     if (units > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
-    hipMemPool_t pool;
-    hipError_t e = workspace_pool(&pool);
-    if (e != hipSuccess) return e;
-    float* ws = nullptr;
-    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
-    if (e != hipSuccess) return e;
+    float* ws = static_cast<float*>(a.ws);   // one record per unit (bwd_workspace_bytes)
     const dim3 blk(kCT);
     const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_fchain_kernel<L, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_rchain_kernel<L, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
         hipLaunchKernelGGL((bwd2_grads_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
         e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(ws, s);
-    return e == hipSuccess ? f : e;
+    return e;
 }
 
 template <typename E>
@@ -1615,64 +1608,52 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs p, int64_t n
     }
 }
 
-// With grouped query/key heads the kernels write per-value-head dq, dk to fp32
-// buffers from the pool, summed into the outputs by one more launch.
+// With grouped query/key heads the kernels write per-value-head dq, dk to two
+// fp32 buffers at the end of the workspace, summed into the outputs by one more
+// launch.
 template <typename E>
-hipError_t bwd_with_groups(BwdArgs a, hipStream_t s, hipError_t (*run)(const BwdArgs&, hipStream_t)) {
+hipError_t bwd_with_groups(int variant, BwdArgs a, hipStream_t s, hipError_t (*run)(const BwdArgs&, hipStream_t)) {
     if (a.Hk == a.H) {
         a.gq32 = a.gk32 = nullptr;
         return run(a, s);
     }
-    hipMemPool_t pool;
-    hipError_t e = workspace_pool(&pool);
-    if (e != hipSuccess) return e;
-    const int64_t per = static_cast<int64_t>(a.B) * a.T * a.H * a.dk;
-    float* buf = nullptr;
-    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&buf), static_cast<size_t>(2 * per * 4), pool, s);
-    if (e != hipSuccess) return e;
-    a.gq32 = buf;
-    a.gk32 = buf + per;
-    e = run(a, s);
+    const size_t per = round_up_256(static_cast<size_t>(a.B) * a.T * a.H * a.dk * 4);
+    unsigned char* buf = static_cast<unsigned char*>(a.ws) + bwd_workspace_bytes(variant, a.B, a.T, a.H, a.H, a.dk, a.dv);
+    a.gq32 = reinterpret_cast<float*>(buf);
+    a.gk32 = reinterpret_cast<float*>(buf + per);
+    hipError_t e = run(a, s);
     if (e == hipSuccess) {
         const int64_t n = static_cast<int64_t>(a.B) * a.T * a.Hk * a.dk;
         const int64_t blocks = std::min<int64_t>((n + 255) / 256, int64_t(1) << 16);
         hipLaunchKernelGGL((bwd_group_sum_kernel<E>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, n);
         e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(buf, s);
-    return e == hipSuccess ? f : e;
+    return e;
 }
 
 template <int VAR, typename E, int DK, int DV>
 hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
-    typedef BwdWs<DK, DV> L;
     const int N = (a.T + kBC - 1) / kBC;
     const int64_t units = static_cast<int64_t>(a.B) * a.H * N;
     if (units > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
-    hipMemPool_t pool;
-    hipError_t e = workspace_pool(&pool);
-    if (e != hipSuccess) return e;
-    float* ws = nullptr;
-    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(units * L::size * 4), pool, s);
-    if (e != hipSuccess) return e;
+    float* ws = static_cast<float*>(a.ws);   // one record per unit (bwd_workspace_bytes)
     const dim3 blk(kCT);
     const unsigned chains = chain_grid(a, DV);
     hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_fchain_kernel<L, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs<DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_rchain_kernel<L, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs<DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
         hipLaunchKernelGGL((bwd_grads_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
         e = hipGetLastError();
     }
-    const hipError_t f = hipFreeAsync(ws, s);
-    return e == hipSuccess ? f : e;
+    return e;
 }
 
 template <int VAR, typename E>
@@ -1685,11 +1666,27 @@ hipError_t launch_bwd_var(const BwdArgs& a, hipStream_t s) {
 
 template <int VAR>
 hipError_t launch_bwd_dtype(int dtype, const BwdArgs& a, hipStream_t s) {
-    return dtype == 0 ? bwd_with_groups<F32>(a, s, launch_bwd_var<VAR, F32>)
-                      : bwd_with_groups<BF16>(a, s, launch_bwd_var<VAR, BF16>);
+    return dtype == 0 ? bwd_with_groups<F32>(VAR, a, s, launch_bwd_var<VAR, F32>)
+                      : bwd_with_groups<BF16>(VAR, a, s, launch_bwd_var<VAR, BF16>);
 }
 
 }  // namespace
+
+template <int DK, int DV>
+size_t bwd_records_bytes(bool split, int64_t units) {
+    const int64_t rec = split ? BwdWs2<DK, DV>::size : BwdWs<DK, DV>::size;
+    return round_up_256(static_cast<size_t>(units * rec * 4));
+}
+
+size_t bwd_workspace_bytes(int variant, int B, int T, int H, int Hk, int dk, int dv) {
+    const int64_t units = static_cast<int64_t>(B) * H * ((T + kBC - 1) / kBC);
+    const bool split = variant == 3;
+    size_t n;
+    if (dk == 128) n = dv == 128 ? bwd_records_bytes<128, 128>(split, units) : bwd_records_bytes<128, 64>(split, units);
+    else n = dv == 128 ? bwd_records_bytes<64, 128>(split, units) : bwd_records_bytes<64, 64>(split, units);
+    if (Hk != H) n += 2 * round_up_256(static_cast<size_t>(B) * T * H * dk * 4);   // per-value-head dq, dk
+    return n;
+}
 
 hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t s) {
     switch (variant) {
@@ -1697,8 +1694,8 @@ hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t s) {
         case 1: return launch_bwd_dtype<1>(dtype, a, s);
         case 2: return launch_bwd_dtype<2>(dtype, a, s);
         case 4: return launch_bwd_dtype<4>(dtype, a, s);
-        default: return dtype == 0 ? bwd_with_groups<F32>(a, s, launch_bwd2_dtype<F32>)
-                                   : bwd_with_groups<BF16>(a, s, launch_bwd2_dtype<BF16>);
+        default: return dtype == 0 ? bwd_with_groups<F32>(3, a, s, launch_bwd2_dtype<F32>)
+                                   : bwd_with_groups<BF16>(3, a, s, launch_bwd2_dtype<BF16>);
     }
 }
 

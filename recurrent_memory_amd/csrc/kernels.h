@@ -26,6 +26,8 @@ struct FwdArgs {
                         // written along E = beta ⊙ k and there is no write gate
                         // (the split form with W = V, A_k = A_e, M_k = M_e, Kb = Eb,
                         // or the one-step-size form with E on the key side)
+    void* ws = nullptr; // device workspace of fwd_workspace_bytes() bytes (256-byte
+                        // aligned) when that is not zero
 };
 
 struct DecodeArgs {
@@ -69,10 +71,19 @@ struct BwdArgs {
     int Hk;              // query/key heads (divides H); q, k, dq, dk are [B,T,Hk,dk]
     float* gq32;         // grouped heads only: per-value-head dq, dk [B,T,H,dk] fp32,
     float* gk32;         // summed over each group into gq, gk afterwards; else nullptr
+    void* ws = nullptr;  // device workspace of bwd_workspace_bytes() bytes (256-byte aligned)
 };
 
-// variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates.
-// dtype: 0 fp32, 1 bf16.
+// variant: 0 ungated, 1 scalar decay, 2 channel decay, 3 split gates,
+// 4 a step size per key channel (FG^2-GDN).  dtype: 0 fp32, 1 bf16.
+//
+// Device workspace of each entry point in bytes (0 when it needs none).  The
+// caller allocates it; the launchers carve it into 256-byte aligned pieces.
+size_t fwd_workspace_bytes(int variant, int dtype, int B, int T, int H, int dk, int dv);
+size_t bwd_workspace_bytes(int variant, int B, int T, int H, int Hk, int dk, int dv);
+size_t ttt_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv);
+inline size_t round_up_256(size_t n) { return (n + 255) / 256 * 256; }
+
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
 // software-pipelined bf16 kernel for variants 0 and 1, called by launch_fwd
 hipError_t launch_fwd_pipelined(int variant, const FwdArgs& a, hipStream_t stream);
@@ -87,8 +98,6 @@ hipError_t launch_decode(int variant, int dtype, const DecodeArgs& a, hipStream_
 hipError_t launch_efla_beta(int dtype, const EflaArgs& a, hipStream_t stream);
 // backward of every form (variant 0 .. 3)
 hipError_t launch_bwd(int variant, int dtype, const BwdArgs& a, hipStream_t stream);
-// library-owned stream-ordered memory pool of the current device (workspaces)
-hipError_t workspace_pool(hipMemPool_t* pool);
 
 // DeltaTTT-pre: two chained delta-rule memory layers (variant 0 or 1 for both)
 struct TttArgs {
@@ -105,7 +114,8 @@ struct TttArgs {
     void* o;             // [B,T,H,dv]
     float* AT;           // [B,H,dv,dk] or nullptr (may equal A0)
     float* BT;           // [B,H,dv,dv] or nullptr (may equal B0)
-    // workspace (set by the launcher)
+    void* ws = nullptr;  // device workspace of ttt_workspace_bytes() bytes
+    // pieces of the workspace (set by the launcher)
     void* qs = nullptr;  // [B,T,H,dk] shifted queries a1 ⊙ k of the next token
     void* rd = nullptr;  // [B,T,H,dv] their readouts: pre-write reads of tokens 1..T
     void* r0 = nullptr;  // [B,H,dv] pre-write read of token 0

@@ -456,20 +456,12 @@ hipError_t launch_dims(const FwdArgs& a, hipStream_t s) {
     return launch_one<VAR, E, 64, 64>(a, s);
 }
 
-template <int VAR>
-hipError_t launch_dtype(int dtype, const FwdArgs& a, hipStream_t s) {
-    return dtype == 0 ? launch_dims<VAR, F32>(a, s) : launch_dims<VAR, BF16>(a, s);
-}
-
 }  // namespace
 
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
     if (variant >= 2) return launch_fwd_channel(variant, dtype, a, s);
     if (dtype == 1) return launch_fwd_pipelined(variant, a, s);   // bf16: pipelined kernel
-    switch (variant) {
-        case 0: return launch_dtype<0>(dtype, a, s);
-        default: return launch_dtype<1>(dtype, a, s);
-    }
+    return variant == 0 ? launch_dims<0, F32>(a, s) : launch_dims<1, F32>(a, s);   // fp32
 }
 
 }  // namespace dr

@@ -657,12 +657,11 @@ hipError_t launch_cw_dims(const FwdArgs& a, hipStream_t s) {
 // variant 2: one step size (KDA); 3: split gates (Gated DeltaNet-2); 4: a step
 // size per key channel (FG^2-GDN), run as the split form with keywrite set
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
-    if (dtype == 1) return launch_fwd_channel_two_pass(variant, a, s);
-    if (variant == 2)
-        return dtype == 0 ? launch_cw_dims<2, F32>(a, s) : launch_cw_dims<2, BF16>(a, s);
+    if (dtype == 1) return launch_fwd_channel_two_pass(variant, a, s);   // bf16: two passes
+    if (variant == 2) return launch_cw_dims<2, F32>(a, s);
     FwdArgs b = a;
     b.keywrite = variant == 4 ? 1 : 0;
-    return dtype == 0 ? launch_cw_dims<3, F32>(b, s) : launch_cw_dims<3, BF16>(b, s);
+    return launch_cw_dims<3, F32>(b, s);
 }
 
 }  // namespace dr

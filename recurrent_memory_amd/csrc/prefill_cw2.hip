@@ -41,7 +41,6 @@
 // fragment is one contiguous 16-byte piece of a row.
 #include <algorithm>
 #include <atomic>
-#include <mutex>
 
 #include "chunk_ops.h"
 #include "common.h"
@@ -749,39 +748,26 @@ hipError_t prep_resident(int* out) {
 
 template <int DK, int DV, bool SPLIT>
 hipError_t launch_two_pass(const FwdArgs& a, hipStream_t s) {
-    typedef Blob<DK, SPLIT> BL;
+    // the blobs live in the caller's workspace (fwd_workspace_bytes)
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
     const int NC = (a.T + kC2 - 1) / kC2;
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
     const int64_t total = heads * NC;   // pass-1 units
     if (total > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
-    unsigned char* ws = nullptr;
     if (NC > 0) {
         int resident = 0;
         hipError_t e = prep_resident<DK, SPLIT>(&resident);
         if (e != hipSuccess) return e;
-        hipMemPool_t pool;
-        e = workspace_pool(&pool);
-        if (e != hipSuccess) return e;
-        e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total * BL::bytes), pool, s);
-        if (e != hipSuccess) return e;
         const unsigned grid = static_cast<unsigned>(std::min<int64_t>(total, resident));
         hipLaunchKernelGGL((cw_prep_kernel<DK, SPLIT>), dim3(grid), dim3(kPrepThreads), 0, s, a, ws, NC, static_cast<int>(total));
         e = hipGetLastError();
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(ws, s);
-            return e;
-        }
+        if (e != hipSuccess) return e;
     }
     constexpr int NVT = DV / kVT2;
     const int groups = static_cast<int>((heads + 7) / 8);
     hipLaunchKernelGGL((cw_chain_kernel<DK, DV, SPLIT>), dim3(static_cast<unsigned>(groups) * 8u * NVT), dim3(64 * (kChainWaves + 1)), 0, s, a,
                        ws, NC);
-    hipError_t e = hipGetLastError();
-    if (ws) {
-        const hipError_t f = hipFreeAsync(ws, s);
-        if (e == hipSuccess) e = f;
-    }
-    return e;
+    return hipGetLastError();
 }
 
 template <bool SPLIT>
@@ -794,32 +780,18 @@ hipError_t launch_two_pass_dims(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// The workspace comes from a library-owned, stream-ordered memory pool per
-// device that keeps freed memory for reuse (release threshold: unlimited), so
-// repeated calls do not return to the driver for it.
-hipError_t workspace_pool(hipMemPool_t* pool) {
-    static std::mutex mu;
-    static hipMemPool_t pools[64] = {};
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!pools[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t p = nullptr;
-        e = hipMemPoolCreate(&p, &props);
-        if (e != hipSuccess) return e;
-        uint64_t keep = ~uint64_t(0);
-        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess) return e;
-        pools[dev] = p;
-    }
-    *pool = pools[dev];
-    return hipSuccess;
+template <int DK, bool SPLIT>
+size_t blob_workspace(int B, int T, int H) {
+    const int64_t NC = (T + kC2 - 1) / kC2;
+    return round_up_256(static_cast<size_t>(static_cast<int64_t>(B) * H * NC) * Blob<DK, SPLIT>::bytes);
+}
+
+size_t fwd_workspace_bytes(int variant, int dtype, int B, int T, int H, int dk, int dv) {
+    (void)dv;
+    if (variant < 2 || dtype != 1) return 0;   // only the two-pass channel-wise forward has one
+    const bool split = variant == 3;
+    if (dk == 128) return split ? blob_workspace<128, true>(B, T, H) : blob_workspace<128, false>(B, T, H);
+    return split ? blob_workspace<64, true>(B, T, H) : blob_workspace<64, false>(B, T, H);
 }
 
 hipError_t launch_fwd_channel_two_pass(int variant, const FwdArgs& a, hipStream_t s) {

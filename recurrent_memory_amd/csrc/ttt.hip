@@ -153,28 +153,38 @@ unsigned grid_for(int64_t work, int per_block) {
     return static_cast<unsigned>(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
 }
 
+// Pieces of the workspace: shifted queries, their readouts, the first-layer
+// readouts, the second layer's keys and queries, the token-0 reads.
+struct TttPieces {
+    int64_t qs, rd, o1, hk, zq, r0, total;
+};
+TttPieces ttt_pieces(int64_t eb, int B, int T, int H, int dk, int dv) {
+    const int64_t tok = static_cast<int64_t>(B) * T * H;
+    auto up = [](int64_t bytes) { return static_cast<int64_t>(round_up_256(static_cast<size_t>(bytes))); };
+    TttPieces p;
+    p.qs = 0;
+    p.rd = p.qs + up(tok * dk * eb);
+    p.o1 = p.rd + up(tok * dv * eb);
+    p.hk = p.o1 + up(tok * dv * eb);
+    p.zq = p.hk + up(tok * dv * eb);
+    p.r0 = p.zq + up(tok * dv * eb);
+    p.total = p.r0 + up(static_cast<int64_t>(B) * H * dv * eb);
+    return p;
+}
+
 template <typename E, int VAR>
 hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
-    const int64_t eb = E::bytes;
     const int64_t tok = static_cast<int64_t>(a.B) * a.T * a.H;
-    const int64_t nq = tok * a.dk, nv = tok * a.dv, n0 = static_cast<int64_t>(a.B) * a.H * a.dv;
-    // one allocation: qs, rd, o1, hk, zq, r0 (each 256-byte aligned)
-    auto up = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
-    const int64_t total = up(nq * eb) + 4 * up(nv * eb) + up(n0 * eb);
-    hipMemPool_t pool;
-    hipError_t e = workspace_pool(&pool);
-    if (e != hipSuccess) return e;
-    unsigned char* ws = nullptr;
-    e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(total), pool, s);
-    if (e != hipSuccess) return e;
-    unsigned char* cur = ws;
-    auto take = [&](int64_t bytes) { void* p = cur; cur += up(bytes); return p; };
-    a.qs = take(nq * eb);
-    a.rd = take(nv * eb);
-    a.o1 = take(nv * eb);
-    a.hk = take(nv * eb);
-    a.zq = take(nv * eb);
-    a.r0 = take(n0 * eb);
+    const int64_t nq = tok * a.dk;
+    const TttPieces pc = ttt_pieces(E::bytes, a.B, a.T, a.H, a.dk, a.dv);
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
+    a.qs = ws + pc.qs;
+    a.rd = ws + pc.rd;
+    a.o1 = ws + pc.o1;
+    a.hk = ws + pc.hk;
+    a.zq = ws + pc.zq;
+    a.r0 = ws + pc.r0;
+    hipError_t e;
     // the two reads of A0 come before the first-layer scan that may overwrite it
     hipLaunchKernelGGL((ttt_r0_kernel<E, VAR>), dim3(static_cast<unsigned>(a.B * a.H)), dim3(kTttThreads), 0, s, a);
     e = hipGetLastError();
@@ -204,11 +214,14 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
         FwdArgs f{a.B, a.T, a.H, a.dv, a.dv, a.zq, a.hk, a.v, a.beta2, nullptr, a.g2, a.B0, a.o, a.BT, a.H};
         e = launch_fwd(VAR, dt, f, s);
     }
-    const hipError_t f = hipFreeAsync(ws, s);
-    return e == hipSuccess ? f : e;
+    return e;
 }
 
 }  // namespace
+
+size_t ttt_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv) {
+    return static_cast<size_t>(ttt_pieces(dtype == 0 ? 4 : 2, B, T, H, dk, dv).total);
+}
 
 hipError_t launch_ttt_pre(int variant, int dtype, const TttArgs& a, hipStream_t s) {
     if (dtype == 0) return variant == 0 ? launch_ttt_typed<F32, 0>(a, s) : launch_ttt_typed<F32, 1>(a, s);

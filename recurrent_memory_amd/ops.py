@@ -19,13 +19,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltarule.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "deltarule.h")
 
-ABI_VERSION = 4   # DR_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5   # DR_ABI_VERSION of the header this binding follows
 VARIANTS = {"deltanet": 0, "gdn": 1, "kda": 2, "gdn2": 3, "fg2": 4}
 # forms whose beta is one value per key channel (the erase gate, or the step sizes)
 _CHANNEL_BETA = ("gdn2", "fg2")
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "DR_OK", 1: "DR_E_NULLPTR", 2: "DR_E_SHAPE", 3: "DR_E_UNSUPPORTED",
-          4: "DR_E_ALIGN", 5: "DR_E_DEVICE", 6: "DR_E_LAUNCH", 7: "DR_E_ALIAS"}
+          4: "DR_E_ALIGN", 5: "DR_E_DEVICE", 6: "DR_E_LAUNCH", 7: "DR_E_ALIAS",
+          8: "DR_E_WORKSPACE"}
 
 
 class DrDesc(ctypes.Structure):
@@ -52,15 +53,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is missing: build it with `python -m recurrent_memory_amd.build`")
     lib = ctypes.CDLL(path)
     vp = ctypes.c_void_p
-    lib.delta_fwd.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    sz = ctypes.c_size_t
+    for name in ("delta_fwd_workspace_bytes", "delta_bwd_workspace_bytes",
+                 "delta_ttt_pre_workspace_bytes"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(DrDesc), ctypes.POINTER(sz)]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.delta_fwd.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.delta_fwd.restype = ctypes.c_int
     lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.delta_decode.restype = ctypes.c_int
-    lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 17
+    lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 17 + [sz, vp]
     lib.delta_bwd.restype = ctypes.c_int
     lib.delta_efla_beta.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp]
     lib.delta_efla_beta.restype = ctypes.c_int
-    lib.delta_ttt_pre.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 13
+    lib.delta_ttt_pre.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 13 + [sz, vp]
     lib.delta_ttt_pre.restype = ctypes.c_int
     lib.dr_status_str.argtypes = [ctypes.c_int]
     lib.dr_status_str.restype = ctypes.c_char_p
@@ -102,6 +108,35 @@ def _raise(status: int):
     raise DeltaRuleError(status, lib.dr_status_str(status).decode())
 
 
+def workspace_bytes(entry: str, desc: "DrDesc") -> int:
+    """Device workspace a call needs (``entry`` is "fwd", "bwd" or "ttt_pre")."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    st = getattr(lib, f"delta_{entry}_workspace_bytes")(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        _raise(st)
+    return n.value
+
+
+def _workspace(entry: str, desc: "DrDesc", device, workspace: Optional[torch.Tensor], stream=None):
+    """(pointer, bytes) of the call's workspace: the caller's tensor when given,
+    otherwise a fresh uint8 tensor from torch's allocator (None when no
+    workspace is needed).  Returns the tensor too, to keep it alive.  A fresh
+    tensor is marked as used on ``stream``, so torch does not hand its memory
+    to another allocation before the call's kernels have finished."""
+    need = workspace_bytes(entry, desc)
+    if need == 0:
+        return None, 0, None
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the call's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    return ctypes.c_void_p(workspace.data_ptr()), nbytes, workspace
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -112,13 +147,16 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               beta: torch.Tensor, wgate: Optional[torch.Tensor] = None,
               g: Optional[torch.Tensor] = None, S0: Optional[torch.Tensor] = None,
               o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
-              want_state: bool = True, chunk: int = 64, stream=None
+              want_state: bool = True, chunk: int = 64, stream=None,
+              workspace: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward; tensors as in include/deltarule.h ([B, T, H, d] per token).
 
     q and k may have fewer heads than v (H_k dividing H: grouped value heads).
     Returns (o, S_T).  ``S_T`` is allocated when ``want_state`` and not given;
-    passing ``S_T=S0`` updates the state in place.
+    passing ``S_T=S0`` updates the state in place.  ``workspace`` (a uint8
+    device tensor of at least ``workspace_bytes("fwd", desc)`` bytes) is
+    allocated with torch when needed and not given.
     """
     lib = load_library()
     var = VARIANTS[variant]
@@ -150,8 +188,9 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if S_T is not None:
         _check("S_T", S_T, (B, H, dv, dk), torch.float32, dev)
     desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
+    wp, wn, _keep = _workspace("fwd", desc, dev, workspace, stream)
     st = lib.delta_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
-                       _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
+                       _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T), wp, wn, _stream(stream))
     if st != 0:
         _raise(st)
     return o, S_T
@@ -229,7 +268,7 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               beta: torch.Tensor, dO: torch.Tensor, g: Optional[torch.Tensor] = None,
               S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None,
               wgate: Optional[torch.Tensor] = None, want_dS0: bool = True, chunk: int = 64,
-              stream=None) -> dict:
+              stream=None, workspace: Optional[torch.Tensor] = None) -> dict:
     """Gradients of delta_fwd: dict of dq, dk, dv, dbeta (gdn2: the erase gate's),
     dwgate (gdn2 only), dg (None for deltanet) in the input dtype and dS0 (fp32,
     None unless wanted)."""
@@ -262,10 +301,11 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            "dg": None if gshape is None else torch.empty(gshape, dtype=dt, device=dev),
            "dS0": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None}
     desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
+    wp, wn, _keep = _workspace("bwd", desc, dev, workspace, stream)
     st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate), _ptr(g),
                        _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
                        _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dwgate"]), _ptr(out["dg"]),
-                       _ptr(out["dS0"]), _stream(stream))
+                       _ptr(out["dS0"]), wp, wn, _stream(stream))
     if st != 0:
         _raise(st)
     return out
@@ -275,7 +315,8 @@ def ttt_pre(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bet
             beta2: torch.Tensor, g1: Optional[torch.Tensor] = None, g2: Optional[torch.Tensor] = None,
             A0: Optional[torch.Tensor] = None, B0: Optional[torch.Tensor] = None,
             o: Optional[torch.Tensor] = None, A_T: Optional[torch.Tensor] = None,
-            B_T: Optional[torch.Tensor] = None, want_state: bool = True, stream=None
+            B_T: Optional[torch.Tensor] = None, want_state: bool = True, stream=None,
+            workspace: Optional[torch.Tensor] = None
             ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """DeltaTTT-pre (two delta-rule memory layers; include/deltarule.h, delta_ttt_pre).
 
@@ -316,9 +357,10 @@ def ttt_pre(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, bet
     if B_T is not None:
         _check("B_T", B_T, (B, H, dv, dv), torch.float32, dev)
     desc = DrDesc(B, T, H, dk, dv, 64, VARIANTS[variant], DTYPES[dt], H)
+    wp, wn, _keep = _workspace("ttt_pre", desc, dev, workspace, stream)
     st = lib.delta_ttt_pre(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta1), _ptr(g1),
                            _ptr(beta2), _ptr(g2), _ptr(A0), _ptr(B0), _ptr(o), _ptr(A_T), _ptr(B_T),
-                           _stream(stream))
+                           wp, wn, _stream(stream))
     if st != 0:
         _raise(st)
     return o, A_T, B_T

@@ -12,23 +12,28 @@ from recurrent_memory_amd import ops
 
 lib = ops.load_library()
 
-DR_OK, DR_E_NULLPTR, DR_E_SHAPE, DR_E_UNSUPPORTED, DR_E_ALIGN, DR_E_DEVICE, DR_E_LAUNCH, DR_E_ALIAS = range(8)
-FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(12)]
+(DR_OK, DR_E_NULLPTR, DR_E_SHAPE, DR_E_UNSUPPORTED, DR_E_ALIGN, DR_E_DEVICE, DR_E_LAUNCH, DR_E_ALIAS,
+ DR_E_WORKSPACE) = range(9)
+FAKE = [ctypes.c_void_p(0x7f0000000000 + (i << 32)) for i in range(16)]
+WS = FAKE[15]          # a fake 256-byte aligned workspace, far from every tensor
+WS_BYTES = 1 << 31
 
 
 def test_exports_every_header_symbol():
     names = ops.header_functions()
     assert set(names) == {"delta_fwd", "delta_decode", "delta_bwd", "delta_efla_beta",
-                          "delta_ttt_pre", "dr_status_str", "dr_abi_version"}
+                          "delta_ttt_pre", "dr_status_str", "dr_abi_version",
+                          "delta_fwd_workspace_bytes", "delta_bwd_workspace_bytes",
+                          "delta_ttt_pre_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
-    assert lib.dr_abi_version() == ops.ABI_VERSION == 4
+    assert lib.dr_abi_version() == ops.ABI_VERSION == 5
     assert lib.dr_status_str(0) == b"ok"
     assert lib.dr_status_str(99) == b"unknown status"
-    for s in range(8):
+    for s in range(9):
         assert lib.dr_status_str(s) and lib.dr_status_str(s) != b"unknown status"
 
 
@@ -39,9 +44,9 @@ def desc(**kw):
 
 
 def fwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S0=None,
-        o=FAKE[7], ST=None):
+        o=FAKE[7], ST=None, ws=WS, ws_bytes=WS_BYTES):
     return lib.delta_fwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g, S0,
-                         o, ST, None)
+                         o, ST, ws, ws_bytes, None)
 
 
 def dec(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S=FAKE[6],
@@ -56,6 +61,9 @@ def dec(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5],
     (dict(d_v=256), DR_E_UNSUPPORTED), (dict(chunk=32), DR_E_UNSUPPORTED),
     (dict(B=0), DR_E_SHAPE), (dict(T=0), DR_E_SHAPE), (dict(H=-1), DR_E_SHAPE),
     (dict(T=1 << 30, B=1 << 10), DR_E_SHAPE),
+    # grid and 32-bit offset limits: B*H <= 2^20, B*H*ceil(T/64) <= 2^22, H < 2^18
+    (dict(B=1 << 18, H=5, T=1), DR_E_SHAPE), (dict(B=1 << 10, H=1 << 6, T=65 * 64), DR_E_SHAPE),
+    (dict(B=1, H=1 << 18, T=1), DR_E_SHAPE),
     (dict(H_k=2), DR_E_SHAPE), (dict(H_k=4), DR_E_SHAPE), (dict(H_k=-1), DR_E_SHAPE),
 ])
 def test_bad_descriptor(kw, status):
@@ -137,9 +145,9 @@ def test_grouped_heads_size_the_query_key_operands():
 
 def bwd(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S0=None,
         dO=FAKE[4], dST=None, dq=FAKE[7], dk=FAKE[8], dv=FAKE[9], dbeta=FAKE[10], dwgate=None,
-        dg=FAKE[11], dS0=None):
+        dg=FAKE[11], dS0=None, ws=WS, ws_bytes=WS_BYTES):
     return lib.delta_bwd(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g, S0,
-                         dO, dST, dq, dk, dv, dbeta, dwgate, dg, dS0, None)
+                         dO, dST, dq, dk, dv, dbeta, dwgate, dg, dS0, ws, ws_bytes, None)
 
 
 def test_bwd_validation():
@@ -178,9 +186,9 @@ def test_no_device_returns_device_error():
 
 
 def ttt(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta1=FAKE[3], g1=FAKE[4], beta2=FAKE[5], g2=FAKE[6],
-        A0=None, B0=None, o=FAKE[9], AT=None, BT=None):
+        A0=None, B0=None, o=FAKE[9], AT=None, BT=None, ws=WS, ws_bytes=WS_BYTES):
     return lib.delta_ttt_pre(ctypes.byref(d) if d is not None else None, q, k, v, beta1, g1, beta2, g2,
-                             A0, B0, o, AT, BT, None)
+                             A0, B0, o, AT, BT, ws, ws_bytes, None)
 
 
 def test_ttt_pre_validation():
@@ -199,3 +207,59 @@ def test_ttt_pre_validation():
     if not torch.cuda.is_available():
         assert ttt(desc(), A0=FAKE[10], AT=FAKE[10], B0=FAKE[11], BT=FAKE[11]) == DR_E_DEVICE  # in place
         assert ttt(desc(variant=0), g1=None, g2=None) == DR_E_DEVICE
+
+
+def ws_bytes(entry, d):
+    n = ctypes.c_size_t(0)
+    st = getattr(lib, f"delta_{entry}_workspace_bytes")(ctypes.byref(d) if d is not None else None,
+                                                        ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_queries():
+    """Sizes follow the header's statement: none for the scalar-decay forward and
+    for fp32 channel-wise forms; one 38 KiB (split gates: 50 KiB) block per 32
+    tokens of a head for the bf16 channel-wise forward; one 560.5 KiB (768.5 KiB)
+    record per 64 tokens of a head for the backward, plus two fp32 [B,T,H,d_k]
+    buffers with grouped heads; the DeltaTTT-pre intermediates."""
+    up = lambda n: (n + 255) // 256 * 256
+    assert ws_bytes("fwd", None)[0] == DR_E_NULLPTR
+    assert lib.delta_fwd_workspace_bytes(ctypes.byref(desc()), None) == DR_E_NULLPTR
+    assert ws_bytes("fwd", desc(d_k=96))[0] == DR_E_UNSUPPORTED
+    assert ws_bytes("fwd", desc(variant=1)) == (DR_OK, 0)
+    assert ws_bytes("fwd", desc(variant=2, dtype=0)) == (DR_OK, 0)
+    nc = (100 + 31) // 32
+    assert ws_bytes("fwd", desc(variant=2)) == (DR_OK, up(2 * 3 * nc * 38 * 1024))
+    assert ws_bytes("fwd", desc(variant=4)) == (DR_OK, up(2 * 3 * nc * 38 * 1024))
+    assert ws_bytes("fwd", desc(variant=3)) == (DR_OK, up(2 * 3 * nc * 50 * 1024))
+    assert ws_bytes("fwd", desc(variant=2, d_k=64)) == (DR_OK, up(2 * 3 * nc * 21 * 1024))
+    assert ws_bytes("fwd", desc(variant=3, d_k=64)) == (DR_OK, up(2 * 3 * nc * 29 * 1024))
+    n64 = (100 + 63) // 64
+    assert ws_bytes("bwd", desc(variant=1)) == (DR_OK, up(2 * 3 * n64 * 5605 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=3)) == (DR_OK, up(2 * 3 * n64 * 7685 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 27225 * 1024 // 100))
+    grouped = ws_bytes("bwd", desc(variant=1, H=4, H_k=2))[1]
+    assert grouped == up(2 * 4 * n64 * 5605 * 1024 // 10) + 2 * up(2 * 100 * 4 * 128 * 4)
+    tok = 2 * 100 * 3
+    assert ws_bytes("ttt_pre", desc(variant=1)) == (DR_OK, up(tok * 128 * 2) + 4 * up(tok * 128 * 2) + up(2 * 3 * 128 * 2))
+    assert ws_bytes("ttt_pre", desc(variant=2))[0] == DR_E_UNSUPPORTED
+
+
+def test_workspace_validation():
+    """A needed workspace that is missing, too small, misaligned or over a tensor
+    is refused before any HIP call; one that is not needed may be NULL."""
+    d = desc(variant=2)
+    need = ws_bytes("fwd", d)[1]
+    assert fwd(d, ws=None, ws_bytes=0) == DR_E_WORKSPACE
+    assert fwd(d, ws_bytes=need - 1) == DR_E_WORKSPACE
+    assert fwd(d, ws=ctypes.c_void_p(WS.value + 16)) == DR_E_ALIGN
+    assert fwd(d, ws=FAKE[2]) == DR_E_ALIAS                            # over v
+    assert fwd(d, ws=ctypes.c_void_p(FAKE[7].value - 256), ws_bytes=need) == DR_E_ALIAS   # runs into o
+    assert bwd(desc(), ws=None, ws_bytes=0) == DR_E_WORKSPACE
+    assert bwd(desc(), ws=FAKE[9]) == DR_E_ALIAS                       # over dv
+    assert ttt(desc(), ws=None, ws_bytes=0) == DR_E_WORKSPACE
+    assert ttt(desc(), ws=FAKE[0]) == DR_E_ALIAS                       # over q
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd(desc(variant=1), ws=None, ws_bytes=0) == DR_E_DEVICE   # none needed
+        assert fwd(d, ws_bytes=need) == DR_E_DEVICE
