@@ -15,6 +15,12 @@
 // five launches: r_0, the shifted queries, the two first-layer scans and the
 // key/query transform, then the second-layer scan, each scan being delta_fwd's
 // chunkwise kernel.
+//
+// bf16 operands are first widened to fp32 and the whole layer runs on the fp32
+// path; only the output is rounded back to bf16.  The intermediate reads, keys
+// and queries then carry no bf16 rounding: with bf16 keys and queries the
+// second layer's readout B_t z_t picks up a rounding error of the size of what
+// B_t stores, which is large next to |o_t| when z_t is nearly orthogonal to it.
 #include "common.h"
 #include "kernels.h"
 
@@ -148,6 +154,34 @@ __global__ __launch_bounds__(kTttThreads) void ttt_glue_kernel(TttArgs p, int64_
     }
 }
 
+// dst[i] = src[i] between bf16 and fp32 (either direction), 8 elements per
+// thread and step; the last n % 8 elements one by one.
+template <typename From, typename To>
+__global__ __launch_bounds__(kTttThreads) void ttt_convert_kernel(const void* src, void* dst, int64_t n) {
+    const int64_t n8 = n / 8, stride = static_cast<int64_t>(gridDim.x) * kTttThreads;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kTttThreads + threadIdx.x;
+    for (int64_t i = i0; i < n8; i += stride) {
+        float x[8];
+        if constexpr (From::bytes == 2) {
+            Vec16<BF16>::unpack(reinterpret_cast<const uint4*>(src)[i], x);
+        } else {
+            float y[4];
+            Vec16<F32>::unpack(reinterpret_cast<const uint4*>(src)[2 * i], y);
+            for (int j = 0; j < 4; ++j) x[j] = y[j];
+            Vec16<F32>::unpack(reinterpret_cast<const uint4*>(src)[2 * i + 1], y);
+            for (int j = 0; j < 4; ++j) x[4 + j] = y[j];
+        }
+        if constexpr (To::bytes == 2) {
+            reinterpret_cast<uint4*>(dst)[i] = Vec16<BF16>::pack(x);
+        } else {
+            const float lo[4] = {x[0], x[1], x[2], x[3]}, hi[4] = {x[4], x[5], x[6], x[7]};
+            reinterpret_cast<uint4*>(dst)[2 * i] = Vec16<F32>::pack(lo);
+            reinterpret_cast<uint4*>(dst)[2 * i + 1] = Vec16<F32>::pack(hi);
+        }
+    }
+    for (int64_t i = 8 * n8 + i0; i < n; i += stride) store_elem<To>(dst, i, load_elem<From>(src, i));
+}
+
 unsigned grid_for(int64_t work, int per_block) {
     const int64_t blocks = (work + per_block - 1) / per_block;
     return static_cast<unsigned>(blocks < 16384 ? (blocks > 0 ? blocks : 1) : 16384);
@@ -217,15 +251,71 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
     return e;
 }
 
+// bf16 operands: fp32 copies of q, k, v, beta1, g1, beta2, g2 and of the output
+// come first in the workspace, then the fp32 path's own pieces.
+struct TttWide {
+    int64_t q, k, v, b1, g1, b2, g2, o, rest, total;
+};
+TttWide ttt_wide(int B, int T, int H, int dk, int dv) {
+    const int64_t tok = static_cast<int64_t>(B) * T * H;
+    auto up = [](int64_t bytes) { return static_cast<int64_t>(round_up_256(static_cast<size_t>(bytes))); };
+    TttWide w;
+    w.q = 0;
+    w.k = w.q + up(tok * dk * 4);
+    w.v = w.k + up(tok * dk * 4);
+    w.b1 = w.v + up(tok * dv * 4);
+    w.g1 = w.b1 + up(tok * 4);
+    w.b2 = w.g1 + up(tok * 4);
+    w.g2 = w.b2 + up(tok * 4);
+    w.o = w.g2 + up(tok * 4);
+    w.rest = w.o + up(tok * dv * 4);
+    w.total = w.rest + ttt_pieces(4, B, T, H, dk, dv).total;
+    return w;
+}
+
+hipError_t ttt_convert(bool to_f32, const void* src, void* dst, int64_t n, hipStream_t s) {
+    const unsigned grid = grid_for((n + 7) / 8, kTttThreads);
+    if (to_f32) hipLaunchKernelGGL((ttt_convert_kernel<BF16, F32>), dim3(grid), dim3(kTttThreads), 0, s, src, dst, n);
+    else hipLaunchKernelGGL((ttt_convert_kernel<F32, BF16>), dim3(grid), dim3(kTttThreads), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
+template <int VAR>
+hipError_t launch_ttt_wide(const TttArgs& a, hipStream_t s) {
+    const int64_t tok = static_cast<int64_t>(a.B) * a.T * a.H;
+    const TttWide w = ttt_wide(a.B, a.T, a.H, a.dk, a.dv);
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
+    TttArgs f = a;
+    f.q = ws + w.q;
+    f.k = ws + w.k;
+    f.v = ws + w.v;
+    f.beta1 = ws + w.b1;
+    f.beta2 = ws + w.b2;
+    f.g1 = VAR == 1 ? ws + w.g1 : nullptr;
+    f.g2 = VAR == 1 ? ws + w.g2 : nullptr;
+    f.o = ws + w.o;
+    f.ws = ws + w.rest;
+    const void* from[] = {a.q, a.k, a.v, a.beta1, a.beta2, a.g1, a.g2};
+    const void* to[] = {f.q, f.k, f.v, f.beta1, f.beta2, f.g1, f.g2};
+    const int64_t n[] = {tok * a.dk, tok * a.dk, tok * a.dv, tok, tok, tok, tok};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < (VAR == 1 ? 7 : 5) && e == hipSuccess; ++i)
+        e = ttt_convert(true, from[i], const_cast<void*>(to[i]), n[i], s);
+    if (e == hipSuccess) e = launch_ttt_typed<F32, VAR>(f, s);
+    if (e == hipSuccess) e = ttt_convert(false, f.o, a.o, tok * a.dv, s);
+    return e;
+}
+
 }  // namespace
 
 size_t ttt_workspace_bytes(int dtype, int B, int T, int H, int dk, int dv) {
-    return static_cast<size_t>(ttt_pieces(dtype == 0 ? 4 : 2, B, T, H, dk, dv).total);
+    if (dtype == 0) return static_cast<size_t>(ttt_pieces(4, B, T, H, dk, dv).total);
+    return static_cast<size_t>(ttt_wide(B, T, H, dk, dv).total);
 }
 
 hipError_t launch_ttt_pre(int variant, int dtype, const TttArgs& a, hipStream_t s) {
     if (dtype == 0) return variant == 0 ? launch_ttt_typed<F32, 0>(a, s) : launch_ttt_typed<F32, 1>(a, s);
-    return variant == 0 ? launch_ttt_typed<BF16, 0>(a, s) : launch_ttt_typed<BF16, 1>(a, s);
+    return variant == 0 ? launch_ttt_wide<0>(a, s) : launch_ttt_wide<1>(a, s);
 }
 
 }  // namespace dr

@@ -268,10 +268,12 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
               beta: torch.Tensor, dO: torch.Tensor, g: Optional[torch.Tensor] = None,
               S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None,
               wgate: Optional[torch.Tensor] = None, want_dS0: bool = True, chunk: int = 64,
-              stream=None, workspace: Optional[torch.Tensor] = None) -> dict:
+              stream=None, workspace: Optional[torch.Tensor] = None,
+              out: Optional[dict] = None) -> dict:
     """Gradients of delta_fwd: dict of dq, dk, dv, dbeta (gdn2: the erase gate's),
     dwgate (gdn2 only), dg (None for deltanet) in the input dtype and dS0 (fp32,
-    None unless wanted)."""
+    None unless wanted).  ``out`` may supply any of these tensors; the rest are
+    allocated."""
     lib = load_library()
     var = VARIANTS[variant]
     B, T, Hk, dk = q.shape
@@ -295,11 +297,17 @@ def delta_bwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     for name, t in (("S0", S0), ("dS_T", dS_T)):
         if t is not None:
             _check(name, t, (B, H, dv, dk), torch.float32, dev)
+    given = dict(out or {})
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dbeta": torch.empty_like(beta),
            "dwgate": torch.empty_like(wgate) if variant == "gdn2" else None,
            "dg": None if gshape is None else torch.empty(gshape, dtype=dt, device=dev),
            "dS0": torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_dS0 else None}
+    for name, t in given.items():
+        if name not in out or out[name] is None:
+            raise ValueError(f"{name} is not an output of this call")
+        _check(name, t, tuple(out[name].shape), out[name].dtype, dev)
+        out[name] = t
     desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
     wp, wn, _keep = _workspace("bwd", desc, dev, workspace, stream)
     st = lib.delta_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate), _ptr(g),

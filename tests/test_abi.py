@@ -241,7 +241,11 @@ def test_workspace_size_queries():
     grouped = ws_bytes("bwd", desc(variant=1, H=4, H_k=2))[1]
     assert grouped == up(2 * 4 * n64 * 5605 * 1024 // 10) + 2 * up(2 * 100 * 4 * 128 * 4)
     tok = 2 * 100 * 3
-    assert ws_bytes("ttt_pre", desc(variant=1)) == (DR_OK, up(tok * 128 * 2) + 4 * up(tok * 128 * 2) + up(2 * 3 * 128 * 2))
+    f32_pieces = up(tok * 128 * 4) + 4 * up(tok * 128 * 4) + up(2 * 3 * 128 * 4)
+    assert ws_bytes("ttt_pre", desc(variant=1, dtype=0)) == (DR_OK, f32_pieces)
+    # bf16: fp32 copies of q, k, v, the four per-token scalars and the output, then the fp32 pieces
+    wide = 4 * up(tok * 128 * 4) + 4 * up(tok * 4)
+    assert ws_bytes("ttt_pre", desc(variant=1)) == (DR_OK, wide + f32_pieces)
     assert ws_bytes("ttt_pre", desc(variant=2))[0] == DR_E_UNSUPPORTED
 
 

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle_pool import bwd_all_heads
 from gpu_util import TOL, announce, dev, host, slice_rel_err
 from oracle import delta_bwd as oracle_bwd
 from recurrent_memory_amd import ops
@@ -85,20 +86,15 @@ def test_bwd_no_state_gradient(variant):
 
 
 @pytest.mark.parametrize("variant", ["gdn", "kda", "gdn2", "fg2"])
-def test_bwd_long_sampled_heads(variant):
-    """bf16, B=2, H=16, T=1024, d=128: two heads checked against the oracle."""
+def test_bwd_long_all_heads(variant):
+    """bf16, B=2, H=16, T=1024, d=128: every head checked against the oracle."""
     announce("bwd_long", variant)
     w = Workload("t", variant, "bf16", B=2, H=16, T=1024, dk=128, dv=128, random_s0=True, seed=44)
     x = make_forward_inputs(w)
     dO, dST = _upstream(w, 11)
     gr = _run(variant, "bf16", w, x, dO, dST)
-    for b, h in [(0, 3), (1, 14)]:
-        sl = lambda a: None if a is None else a[[b]][:, :, [h]]  # noqa: E731
-        ref = oracle_bwd(variant, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["wgate"]),
-                         sl(x["g"]), x["S0"][[b]][:, [h]], sl(dO), dST[[b]][:, [h]])
-        got = {n: (None if a is None else (a[[b]][:, [h]] if n == "dS0" else sl(a)))
-               for n, a in gr.items()}
-        _check(variant, "bf16", got, ref)
+    ref = bwd_all_heads(variant, {**x, "dO": dO, "dS_T": dST}, w.B, w.H)
+    _check(variant, "bf16", gr, ref)
 
 
 def test_bwd_deterministic():
@@ -166,16 +162,11 @@ def test_autograd_function(variant):
 @pytest.mark.parametrize("variant", VARS)
 def test_bwd_many_heads(variant):
     """B*H = 330 heads: the chain kernels' XCD-aware head map with a partial last
-    group of 8 and more workgroups than CUs; 4 heads sampled against the oracle."""
+    group of 8 and more workgroups than CUs; every head checked against the oracle."""
     announce("bwd_many_heads", variant)
     w = Workload("t", variant, "bf16", B=6, H=55, T=70, dk=64, dv=64, random_s0=True, seed=49)
     x = make_forward_inputs(w)
     dO, dST = _upstream(w, 16)
     gr = _run(variant, "bf16", w, x, dO, dST)
-    for b, h in [(0, 0), (2, 17), (5, 54), (4, 31)]:
-        sl = lambda a: None if a is None else a[[b]][:, :, [h]]  # noqa: E731
-        ref = oracle_bwd(variant, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["wgate"]),
-                         sl(x["g"]), x["S0"][[b]][:, [h]], sl(dO), dST[[b]][:, [h]])
-        got = {n: (None if a is None else (a[[b]][:, [h]] if n == "dS0" else sl(a)))
-               for n, a in gr.items()}
-        _check(variant, "bf16", got, ref)
+    ref = bwd_all_heads(variant, {**x, "dO": dO, "dS_T": dST}, w.B, w.H)
+    _check(variant, "bf16", gr, ref)

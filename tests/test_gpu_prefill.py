@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from gpu_util import TOL, announce, dev, errs, gpu_fwd, host, slice_rel_err
+from oracle_pool import fwd_all_heads
 from oracle import delta_fwd as oracle_fwd
 from recurrent_memory_amd import ops
 from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs, round_to_bf16
@@ -51,42 +52,31 @@ def test_deltanet_fp32_workload_full():
     assert eo <= 1e-4
 
 
-def test_gdn_bf16_workload_full_sampled_heads():
-    """The headline workload at full size; every output is computed on the GPU,
-    the oracle checks 6 sampled (batch, head) sequences end to end."""
+def test_gdn_bf16_workload_full_all_heads():
+    """The headline workload at full size, every (batch, head) sequence checked
+    against the oracle end to end (oracle heads in a process pool)."""
     w = WORKLOADS["gdn_bf16_b4_h16_t4096_d128"]
     announce("prefill_full", w.name)
     x = make_forward_inputs(w)
     o, S = gpu_fwd("gdn", x, "bf16")
-    rng = np.random.default_rng(1)
-    for b, h in zip(rng.integers(0, w.B, 6), rng.integers(0, w.H, 6)):
-        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
-               for n, a in x.items()}
-        o_ref, S_ref = oracle_fwd("gdn", **sub)
-        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
-        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (b, h, eo, es)
+    o_ref, S_ref = fwd_all_heads("gdn", x, w.B, w.H)
+    eo, es = errs(o, S, o_ref, S_ref)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
 
 
-@pytest.mark.parametrize("name,variant,n_sample", [("kda_bf16_b2_h16_t8192_d128", "kda", 4),
-                                                    ("gdn2_bf16_b1_h16_t32768_d128", "gdn2", 2),
-                                                    ("kda_bf16_b2_h16_t8192_d128", "fg2", 2)])
-def test_channel_decay_workloads_full_sampled_heads(name, variant, n_sample):
-    """KDA and Gated DeltaNet-2 workloads at full size (FG^2-GDN at the KDA shape):
-    every output is computed on the GPU; the oracle checks sampled (batch, head)
-    sequences end to end."""
+@pytest.mark.parametrize("name,variant", [("kda_bf16_b2_h16_t8192_d128", "kda"),
+                                          ("gdn2_bf16_b1_h16_t32768_d128", "gdn2"),
+                                          ("kda_bf16_b2_h16_t8192_d128", "fg2")])
+def test_channel_decay_workloads_full_all_heads(name, variant):
+    """KDA and Gated DeltaNet-2 workloads at full size (FG^2-GDN at the KDA shape),
+    every (batch, head) sequence checked against the oracle end to end."""
     w = dataclasses.replace(WORKLOADS[name], variant=variant)
     announce("prefill_full", w.name, variant)
     x = make_forward_inputs(w)
     o, S = gpu_fwd(variant, x, "bf16")
-    rng = np.random.default_rng(2)
-    for b, h in zip(rng.integers(0, w.B, n_sample), rng.integers(0, w.H, n_sample)):
-        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
-               for n, a in x.items()}
-        o_ref, S_ref = oracle_fwd(variant, **sub)
-        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
-        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
-        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (b, h, eo, es)
+    o_ref, S_ref = fwd_all_heads(variant, x, w.B, w.H)
+    eo, es = errs(o, S, o_ref, S_ref)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -251,16 +241,11 @@ def test_decode_continues_prefill_all_forms(variant, dtype):
 def test_many_heads_several_dispatch_rounds(variant, dtype):
     """B*H = 330 heads (not a multiple of 8), so every kernel's grid holds more
     workgroups than there are CUs and the XCD-aware head map has a partial last
-    group; 9 heads sampled against the oracle."""
+    group; every head checked against the oracle."""
     announce("prefill_many_heads", variant, dtype)
     w = Workload("t", variant, dtype, B=6, H=55, T=70, dk=64, dv=64, random_s0=True, seed=31)
     x = make_forward_inputs(w)
     o, S = gpu_fwd(variant, x, dtype)
-    rng = np.random.default_rng(3)
-    for b, h in zip(rng.integers(0, w.B, 9), rng.integers(0, w.H, 9)):
-        sub = {n: (None if a is None else (a[b:b + 1, :, h:h + 1] if n != "S0" else a[b:b + 1, h:h + 1]))
-               for n, a in x.items()}
-        o_ref, S_ref = oracle_fwd(variant, **sub)
-        eo = slice_rel_err(o[b:b + 1, :, h:h + 1], o_ref, (0, 2))
-        es = slice_rel_err(S[b:b + 1, h:h + 1], S_ref, (0, 1))
-        assert eo <= TOL[dtype] and es <= TOL[dtype], (b, h, eo, es)
+    o_ref, S_ref = fwd_all_heads(variant, x, w.B, w.H)
+    eo, es = errs(o, S, o_ref, S_ref)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)

@@ -87,3 +87,54 @@ def test_changing_the_current_value_leaves_the_current_write_key():
     _, _, _, h2, _ = ttt_pre_fwd("gdn", **x2, internals=True)
     np.testing.assert_array_equal(h2[:, :5], h[:, :5])
     assert np.abs(h2[:, 5] - h[:, 5]).max() > 1e-3
+
+
+# ---- the nonlinearity and the normalisation, pinned by values the mathematics fixes
+
+def test_silu_values_fixed_by_the_definition():
+    """silu(x) = x * sigmoid(x): silu(0) = 0, silu(ln 3) = (3/4) ln 3 (sigmoid(ln 3) =
+    3/4), silu(-ln 3) = -(1/4) ln 3, silu(x) - silu(-x) = x, silu(x) -> x for large x
+    and -> 0 for large -x."""
+    from oracle.delta_oracle import _silu
+    l3 = np.log(3.0)
+    got = _silu(np.array([0.0, l3, -l3, 40.0, -40.0]))
+    np.testing.assert_allclose(got[:3], [0.0, 0.75 * l3, -0.25 * l3], rtol=1e-15, atol=0)
+    assert abs(got[3] - 40.0) < 1e-15 * 40 + 40 * np.exp(-40) and abs(got[4]) < 41 * np.exp(-40)
+    x = np.linspace(-6, 6, 25)
+    np.testing.assert_allclose(_silu(x) - _silu(-x), x, rtol=0, atol=1e-14)
+
+
+def test_unit_rows_values_fixed_by_the_definition():
+    """unit(x) = x / ||x||: (3, 4) -> (0.6, 0.8), norm 1, positive scaling leaves it,
+    a zero row stays zero (no division by zero)."""
+    from oracle.delta_oracle import _unit_rows
+    got = _unit_rows(np.array([[3.0, 4.0], [0.0, 0.0], [-5.0, 0.0]]))
+    np.testing.assert_allclose(got, [[0.6, 0.8], [0.0, 0.0], [-1.0, 0.0]], rtol=1e-15, atol=0)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 9))
+    np.testing.assert_allclose(np.linalg.norm(_unit_rows(x), axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(_unit_rows(2.5 * x), _unit_rows(x), rtol=1e-14)
+
+
+def test_ttt_keys_and_queries_on_a_worked_example():
+    """One token, d = 2, first layer A0 = [[ln 3, 0], [-ln 3, 0]], k = q = e_0, no
+    first-layer write (beta1 = 0): the pre-write read is r = (ln 3, -ln 3), so the
+    second layer's key and query are unit((3/4 ln 3, -1/4 ln 3)) = (3, -1)/sqrt(10);
+    with B0 = 0 and beta2 = 1 the second layer stores v h^T and reads back v (h.z = 1)."""
+    l3 = np.log(3.0)
+    x = dict(q=np.array([1.0, 0.0]).reshape(1, 1, 1, 2), k=np.array([1.0, 0.0]).reshape(1, 1, 1, 2),
+             v=np.array([0.7, -1.3]).reshape(1, 1, 1, 2), beta1=np.zeros((1, 1, 1)),
+             beta2=np.ones((1, 1, 1)), A0=np.array([[l3, 0.0], [-l3, 0.0]]).reshape(1, 1, 2, 2),
+             B0=np.zeros((1, 1, 2, 2)))
+    o, A_T, B_T, h, z = ttt_pre_fwd("deltanet", **x, internals=True)
+    e = np.array([3.0, -1.0]) / np.sqrt(10.0)
+    np.testing.assert_allclose(h[0, 0, 0], e, rtol=1e-15)
+    np.testing.assert_allclose(z[0, 0, 0], e, rtol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 0], [0.7, -1.3], rtol=1e-15)
+    np.testing.assert_allclose(B_T[0, 0], np.outer([0.7, -1.3], e), rtol=1e-15)
+    # a zero read makes a zero key: the second layer is left as it was
+    x["A0"] = np.zeros((1, 1, 2, 2))
+    x["B0"] = np.array([[0.5, 0.25], [-1.0, 2.0]]).reshape(1, 1, 2, 2)
+    o, _, B_T, h, z = ttt_pre_fwd("deltanet", **x, internals=True)
+    assert np.array_equal(h, np.zeros_like(h)) and np.array_equal(z, np.zeros_like(z))
+    assert np.array_equal(B_T, x["B0"]) and np.array_equal(o, np.zeros_like(o))
