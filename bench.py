@@ -83,6 +83,17 @@ def prefill_flops(variant, B, T, H, dk, dv, C=64):
     return B * T * H * per
 
 
+def prefill_flops_dense(variant, B, T, H, dk, dv, C=64):
+    """Flops the chunk products issue with every C x C tile dense (no triangular
+    tile skipped): 6 dk dv + 6 C dk + 4 C dv + C^2/3 per token and head (split
+    gates: 8 dk dv + 10 C dk + 8 C dv + C^2/3)."""
+    if variant == "gdn2":
+        per = 8 * dk * dv + 10 * C * dk + 8 * C * dv + C * C / 3.0
+    else:
+        per = 6 * dk * dv + 6 * C * dk + 4 * C * dv + C * C / 3.0
+    return B * T * H * per
+
+
 def decode_bytes(B, H, dk, dv, elem=2):
     """Per decode step: the fp32 state read and written once, plus q, k, v, beta, g
     read and o written."""
@@ -124,20 +135,17 @@ def _oracle_worker(args):
     variant, x = args
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        delta_fwd(variant, **x)
-        return time.perf_counter() - t0
+        o, S = delta_fwd(variant, **x)
+        return time.perf_counter() - t0, o, S
 
 
-def cpu_baseline(variant, x, B, T, H, max_workers=16):
-    """Time the float64 oracle on this host: one worker per group of (batch, head)
-    sequences over the first ``T`` tokens, BLAS limited to one thread per worker."""
-    import multiprocessing as mp
-    ncpu = len(os.sched_getaffinity(0))
-    workers = max(1, min(max_workers, ncpu, B * H))
+def _head_groups(x, B, H, T, groups):
+    """Split the inputs into ``groups`` jobs of whole (batch, head) sequences
+    (first T tokens), [len, T, 1, ...] each; returns (jobs, pairs per job)."""
     pairs = [(b, h) for b in range(B) for h in range(H)]
-    groups = [pairs[i::workers] for i in range(workers)]
+    parts = [pairs[i::groups] for i in range(groups)]
     jobs = []
-    for grp in groups:
+    for grp in parts:
         bs = [p[0] for p in grp]
         hs = [p[1] for p in grp]
         sub = {}
@@ -146,20 +154,72 @@ def cpu_baseline(variant, x, B, T, H, max_workers=16):
                 sub[n] = None
             elif n == "S0":
                 sub[n] = np.ascontiguousarray(a[bs, hs][:, None])
-            else:  # [B, T, H, ...] -> [len(grp), T, 1, ...]
-                sub[n] = np.ascontiguousarray(a[bs, :T, hs][:, :, None])
-        jobs.append((variant, sub))
+            else:  # [B, T, heads, ...] -> [len(grp), T, 1, ...]
+                hh = [h // (H // a.shape[2]) for h in hs]
+                sub[n] = np.ascontiguousarray(a[bs, :T, hh][:, :, None])
+        jobs.append(sub)
+    return jobs, parts
+
+
+def oracle_all_heads(variant, x, B, T, H, workers):
+    """The float64 oracle over every (batch, head) sequence (first T tokens) in a
+    pool of ``workers`` processes, one BLAS thread each.  Returns (wall seconds
+    including worker start-up, o [B, T, H, dv], S_T [B, H, dv, dk])."""
+    import multiprocessing as mp
+    jobs, parts = _head_groups(x, B, H, T, workers)
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(workers) as pool:
-        pool.map(_oracle_worker, jobs)
+        res = pool.map(_oracle_worker, [(variant, j) for j in jobs])
     wall = time.perf_counter() - t0
-    head_tokens = B * H * T
-    return dict(value=head_tokens / H / wall, unit="tokens/s", cores=workers, kind="oracle",
+    o = S = None
+    for grp, (_, og, Sg) in zip(parts, res):
+        if o is None:
+            o = np.empty((B, T, H, og.shape[3]))
+            S = np.empty((B, H) + Sg.shape[2:])
+        for i, (b, h) in enumerate(grp):
+            o[b, :, h] = og[i, :, 0]
+            S[b, h] = Sg[i, 0]
+    return wall, o, S
+
+
+def max_rel_err(x, ref, head_axes):
+    """Max over (batch, head) slices of max|x - ref| / max|ref| (the parity metric)."""
+    x = np.asarray(x, np.float64)
+    axes = tuple(a for a in range(x.ndim) if a not in head_axes)
+    den = np.abs(ref).max(axis=axes)
+    return float((np.abs(x - ref).max(axis=axes) / np.where(den == 0, 1.0, den)).max())
+
+
+def cpu_baseline(variant, x, B, T, H, gpu_out, max_workers=16):
+    """Time the float64 oracle on this host over every (batch, head) sequence of
+    the workload (first ``T`` tokens), in a process pool, and once on a single
+    core for one sequence; check the GPU outputs against it (parity metric)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import delta_fwd
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(max_workers, host_cores, B * H))
+    # one core: the first (batch, head) sequence in this process
+    first = {n: (None if a is None else (a[:1, :1] if n == "S0" else a[:1, :T, :1])) for n, a in x.items()}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        delta_fwd(variant, **first)
+        one = time.perf_counter() - t0
+    wall, o_ref, S_ref = oracle_all_heads(variant, x, B, T, H, workers)
+    o, S = gpu_out
+    return dict(value=B * T / wall, unit="tokens/s", cores=workers, kind="oracle",
                 sample=f"float64 token-by-token oracle over all {B}x{H} (batch, head) sequences, "
                        f"first {T} tokens each, {workers} worker processes (1 BLAS thread each), "
                        f"wall {wall:.2f} s including worker start-up",
-                wall_s=wall)
+                wall_s=wall, host_cores=host_cores,
+                one_core={"tokens_per_s": T / one / H, "seconds_per_sequence": one,
+                          "sample": f"one (batch, head) sequence of {T} tokens, one process, "
+                                    f"one BLAS thread; a token carries all {H} heads, so "
+                                    f"tokens/s = T / (H x seconds per sequence)"},
+                parity={"o": max_rel_err(o[:, :T], o_ref, (0, 2)),
+                        "S_T": max_rel_err(S, S_ref, (0, 1)) if T == o.shape[1] else None,
+                        "metric": "max over (batch, head) of max|gpu - oracle| / max|oracle|",
+                        "heads_checked": B * H})
 
 
 def time_forward(w, steps, warmup, n_sets, stream, qk_heads=None):
@@ -202,7 +262,8 @@ def time_forward(w, steps, warmup, n_sets, stream, qk_heads=None):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / 1e3 / steps, wall, x
+    out = (sets[0]["o"].float().cpu().numpy(), sets[0]["ST"].cpu().numpy())
+    return e0.elapsed_time(e1) / 1e3 / steps, wall, x, out
 
 
 def main():
@@ -245,7 +306,7 @@ def main():
         return None if a is None else torch.from_numpy(a).to(bf).to(dev)
 
     n_sets = 3
-    kern_avg_s, wall, x = time_forward(w, args.steps, args.warmup, n_sets, stream)
+    kern_avg_s, wall, x, gpu_out = time_forward(w, args.steps, args.warmup, n_sets, stream)
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (wall / args.steps)
@@ -273,12 +334,17 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                 "algorithmic_flops_per_launch": nflops},
+                 "algorithmic_flops_per_launch": nflops,
+                 "dense_tile_achieved": prefill_flops_dense("gdn", B, T, H, dk, dv) / kern_avg_s / 1e12,
+                 "dense_tile_frac": prefill_flops_dense("gdn", B, T, H, dk, dv) / kern_avg_s / 1e12
+                 / MFMA_BF16_PEAK_TFLOPS,
+                 "dense_tile_flops_per_launch": prefill_flops_dense("gdn", B, T, H, dk, dv)},
     }
 
     if not args.no_other:
         # the other forward workloads: parity-test shapes, reported beside the headline
         others = []
+        other_out = {}
         for name, sub_c, form in [("deltanet_fp32_t256_d64", 16, None),
                                   ("kda_bf16_b2_h16_t8192_d128", 32, None),
                                   ("gdn2_bf16_b1_h16_t32768_d128", 32, None),
@@ -287,7 +353,8 @@ def main():
             if form is not None:   # another form on the same shape and seed
                 wo = dataclasses.replace(wo, variant=form)
                 name = name.replace(name.split("_")[0], form, 1)
-            t_s, _, _ = time_forward(wo, 5, 2, 2, stream)
+            t_s, _, xo, oo = time_forward(wo, 5, 2, 2, stream)
+            other_out[name] = (wo, xo, oo)
             elem = 4 if wo.dtype == "f32" else 2
             nb = prefill_bytes(wo.variant, wo.B, wo.T, wo.H, wo.dk, wo.dv, elem=elem,
                                with_state_in=wo.random_s0)
@@ -297,9 +364,12 @@ def main():
                            "kernel_avg_us": t_s * 1e6, "tokens_per_s": wo.B * wo.T / t_s,
                            "hbm_GBs": nb / t_s / 1e9, "hbm_frac": nb / t_s / 1e9 / HBM_PEAK_GBS,
                            "tflops": nf / t_s / 1e12, "flops_chunk_length": chunk,
+                           "tflops_dense_tile": prefill_flops_dense(wo.variant, wo.B, wo.T, wo.H, wo.dk,
+                                                                    wo.dv, C=chunk) / t_s / 1e12,
                            "algorithmic_bytes_per_launch": nb})
         # grouped value heads: the headline shape with 8 query/key heads (pairs of value heads)
-        t_s, _, _ = time_forward(w, 5, 2, 2, stream, qk_heads=8)
+        t_s, _, xg, og = time_forward(w, 5, 2, 2, stream, qk_heads=8)
+        other_out["gdn_bf16_b4_h16_t4096_d128_hk8"] = (w, xg, og)
         nb = prefill_bytes("gdn", B, T, H, dk, dv, Hk=8)
         others.append({"workload": "gdn_bf16_b4_h16_t4096_d128_hk8", "variant": "gdn",
                        "dtype": "bf16", "qk_heads": 8, "kernel_avg_us": t_s * 1e6,
@@ -423,7 +493,18 @@ def main():
 
     if not args.no_cpu_baseline:
         Tc = min(args.cpu_tokens, T)
-        result["cpu_baseline"] = cpu_baseline("gdn", x, B, Tc, H)
+        result["cpu_baseline"] = cpu_baseline("gdn", x, B, Tc, H, gpu_out)
+        if not args.no_other:
+            # parity of the other forward workloads on every (batch, head), same metric
+            workers = result["cpu_baseline"]["cores"]
+            for o_rec in result["other_workloads"]:
+                name = o_rec["workload"]
+                if name not in other_out:
+                    continue
+                wo, xo, (og, Sg) = other_out[name]
+                _, o_ref, S_ref = oracle_all_heads(wo.variant, xo, wo.B, wo.T, wo.H, workers)
+                o_rec["parity"] = {"o": max_rel_err(og, o_ref, (0, 2)), "S_T": max_rel_err(Sg, S_ref, (0, 1)),
+                                   "heads_checked": wo.B * wo.H}
 
     print(json.dumps(result), flush=True)
 

@@ -1,7 +1,8 @@
-"""Failure propagation on the GPU: a non-finite input in one (batch, head)
-sequence never leaks into another sequence, leaves everything before its
-64-token chunk exactly as in a clean run, and makes every later output and the
-final state non-finite (it is not silently absorbed)."""
+"""Failure propagation on the GPU: a non-finite value in one (batch, head)
+sequence never leaks into another sequence or into another value channel (value
+rows of the memory are independent), leaves everything before its 64-token chunk
+exactly as in a clean run, and makes every later output of its channel and its
+row of the final state non-finite (it is not silently absorbed)."""
 import numpy as np
 import pytest
 import torch
@@ -31,16 +32,20 @@ def test_non_finite_value_stays_in_its_sequence(variant, dtype, bad):
     o0, S0 = _fwd(variant, dtype, x)
     b, h, t = 1, 2, 137
     v = x["v"].copy()
-    v[b, t, h, 5] = bad
+    v[b, t, h, 5] = bad                                           # value channel 5
     o1, S1 = _fwd(variant, dtype, {**x, "v": v})
     others = np.ones((w.B, w.H), bool)
     others[b, h] = False
     assert np.array_equal(o1.transpose(0, 2, 1, 3)[others], o0.transpose(0, 2, 1, 3)[others])
     assert np.array_equal(S1[others], S0[others])
     c0 = (t // 64) * 64
+    col = 5
+    rest = [c for c in range(w.dv) if c != col]
+    assert np.array_equal(o1[b, :, h][:, rest], o0[b, :, h][:, rest])   # other value channels
+    assert np.array_equal(S1[b, h][rest], S0[b, h][rest])
     assert np.array_equal(o1[b, :c0, h], o0[b, :c0, h])          # earlier chunks untouched
-    assert not np.isfinite(o1[b, t:, h]).any()                    # every later output
-    assert not np.isfinite(S1[b, h]).any()                        # and the final state
+    assert not np.isfinite(o1[b, t:, h, col]).any()               # every later output of the channel
+    assert not np.isfinite(S1[b, h, col]).any()                   # and its row of the final state
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
