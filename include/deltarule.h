@@ -157,6 +157,24 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
                     void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * delta_fwd_noalloc — delta_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments and results are those of delta_fwd without the
+ * workspace: where delta_fwd needs one (channel-wise decay forms with DR_BF16
+ * operands), this entry point uses a scratch array of 64 MiB compiled into the
+ * library, one per GPU, held until the process ends; no call allocates or frees
+ * anything.  Descriptors whose delta_fwd_workspace_bytes exceed 64 MiB return
+ * DR_E_WORKSPACE (for d_k = 128: B * H * ceil(T / 32) <= 1724 blocks for
+ * DR_KDA and DR_FG2, 1310 for DR_GDN2).  Every call on one GPU shares that
+ * GPU's scratch: calls that may overlap in time on one GPU (different streams,
+ * several host threads) race and must be ordered by the caller.  The scratch
+ * needs no clearing: each call writes every byte it reads.
+ */
+dr_status delta_fwd_noalloc(const dr_desc* desc, const void* q, const void* k, const void* v,
+                            const void* beta, const void* wgate, const void* g, const float* S0,
+                            void* o, float* S_T, void* stream);
+
+/*
  * delta_decode — one token per sequence, state updated in place.
  *
  *   desc->T must be 1; shapes as delta_fwd with the T axis removed:

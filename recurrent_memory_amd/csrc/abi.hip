@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/deltarule.h"
 #include "kernels.h"
@@ -96,6 +97,52 @@ dr_status check_workspace(size_t need, const void* ws, size_t ws_bytes, const Sp
     return DR_OK;
 }
 
+// Every check of delta_fwd's tensor arguments (sizes, pointers, alignment,
+// aliasing); spans receives the byte ranges of the 9 tensors.
+constexpr int kFwdSpans = 9;
+dr_status check_fwd_args(const dr_desc* desc, const void* q, const void* k, const void* v,
+                         const void* beta, const void* wgate, const void* g, const float* S0,
+                         const void* o, const float* S_T, Sizes* szp, Span* spans) {
+    Sizes& sz = *szp;
+    dr_status st = check_desc(desc, false, &sz);
+    if (st != DR_OK) return st;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return DR_E_NULLPTR;
+    st = check_gate_ptrs(desc, beta, wgate, g);
+    if (st != DR_OK) return st;
+    const void* ptrs[] = {q, k, v, beta, wgate, g, S0, o, S_T};
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
+    const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
+    const Span in[] = {span_of(q, sz.qk, eb),       span_of(k, sz.qk, eb),
+                       span_of(v, sz.v, eb),        span_of(beta, sz.beta, eb),
+                       span_of(wgate, sz.wgate, eb), span_of(g, sz.g, eb),
+                       span_of(S0, sz.state, 4)};
+    const Span so = span_of(o, sz.v, eb);
+    const Span sst = span_of(S_T, sz.state, 4);
+    for (const Span& s : in) {
+        if (overlap(so, s)) return DR_E_ALIAS;
+    }
+    for (int i = 0; i < 6; ++i)
+        if (overlap(sst, in[i])) return DR_E_ALIAS;
+    if (overlap(sst, in[6]) && static_cast<const void*>(S_T) != static_cast<const void*>(S0))
+        return DR_E_ALIAS;
+    if (overlap(sst, so)) return DR_E_ALIAS;
+    for (int i = 0; i < 7; ++i) spans[i] = in[i];
+    spans[7] = so;
+    spans[8] = sst;
+    return DR_OK;
+}
+
+dr_status launch_forward(const dr_desc* desc, const Sizes& sz, const void* q, const void* k,
+                         const void* v, const void* beta, const void* wgate, const void* g,
+                         const float* S0, void* o, float* S_T, void* ws, void* stream) {
+    dr::FwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g,
+                  S0, o, S_T, sz.Hk};
+    a.ws = ws;
+    const hipError_t e = dr::launch_fwd(desc->variant, desc->dtype, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+}
+
 std::atomic<int> g_arch_state[64];  // per device: 0 unknown, 1 gfx950, 2 other
 
 dr_status check_device() {
@@ -117,6 +164,35 @@ dr_status check_device() {
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (dev < 64) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
     return ok ? DR_OK : DR_E_DEVICE;
+}
+
+// Device scratch of delta_fwd_noalloc: one array per GPU, part of the code
+// object, held until the process ends.  Host code never uses the name itself
+// (in host code it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// The scratch address of the current device (NULL if it cannot be resolved).
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -142,43 +218,40 @@ dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const voi
                     void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
     try {
         Sizes sz;
-        dr_status st = check_desc(desc, false, &sz);
+        Span spans[kFwdSpans];
+        dr_status st = check_fwd_args(desc, q, k, v, beta, wgate, g, S0, o, S_T, &sz, spans);
         if (st != DR_OK) return st;
-        if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return DR_E_NULLPTR;
-        st = check_gate_ptrs(desc, beta, wgate, g);
-        if (st != DR_OK) return st;
-        const void* ptrs[] = {q, k, v, beta, wgate, g, S0, o, S_T};
-        for (const void* p : ptrs)
-            if (p != nullptr && !aligned16(p)) return DR_E_ALIGN;
-        const int64_t eb = desc->dtype == DR_F32 ? 4 : 2;
-        const Span in[] = {span_of(q, sz.qk, eb),       span_of(k, sz.qk, eb),
-                           span_of(v, sz.v, eb),        span_of(beta, sz.beta, eb),
-                           span_of(wgate, sz.wgate, eb), span_of(g, sz.g, eb),
-                           span_of(S0, sz.state, 4)};
-        const Span so = span_of(o, sz.v, eb);
-        const Span sst = span_of(S_T, sz.state, 4);
-        for (const Span& s : in) {
-            if (overlap(so, s)) return DR_E_ALIAS;
-        }
-        for (int i = 0; i < 6; ++i)
-            if (overlap(sst, in[i])) return DR_E_ALIAS;
-        if (overlap(sst, in[6]) && static_cast<const void*>(S_T) != static_cast<const void*>(S0))
-            return DR_E_ALIAS;
-        if (overlap(sst, so)) return DR_E_ALIAS;
         const size_t need = dr::fwd_workspace_bytes(desc->variant, desc->dtype, desc->B, desc->T,
                                                     desc->H, desc->d_k, desc->d_v);
-        const Span all[] = {in[0], in[1], in[2], in[3], in[4], in[5], in[6], so, sst};
-        st = check_workspace(need, workspace, workspace_bytes, all, 9);
+        st = check_workspace(need, workspace, workspace_bytes, spans, kFwdSpans);
         if (st != DR_OK) return st;
-
         st = check_device();
         if (st != DR_OK) return st;
-        dr::FwdArgs a{desc->B, desc->T, desc->H, desc->d_k, desc->d_v, q, k, v, beta, wgate, g,
-                      S0, o, S_T, sz.Hk};
-        a.ws = need ? workspace : nullptr;
-        const hipError_t e = dr::launch_fwd(desc->variant, desc->dtype, a,
-                                            static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? DR_OK : DR_E_LAUNCH;
+        return launch_forward(desc, sz, q, k, v, beta, wgate, g, S0, o, S_T, need ? workspace : nullptr, stream);
+    } catch (...) {
+        return DR_E_LAUNCH;
+    }
+}
+
+dr_status delta_fwd_noalloc(const dr_desc* desc, const void* q, const void* k, const void* v,
+                            const void* beta, const void* wgate, const void* g, const float* S0,
+                            void* o, float* S_T, void* stream) {
+    try {
+        Sizes sz;
+        Span spans[kFwdSpans];
+        dr_status st = check_fwd_args(desc, q, k, v, beta, wgate, g, S0, o, S_T, &sz, spans);
+        if (st != DR_OK) return st;
+        const size_t need = dr::fwd_workspace_bytes(desc->variant, desc->dtype, desc->B, desc->T,
+                                                    desc->H, desc->d_k, desc->d_v);
+        if (need > kScratchBytes) return DR_E_WORKSPACE;
+        st = check_device();
+        if (st != DR_OK) return st;
+        void* ws = nullptr;
+        if (need > 0) {
+            ws = scratch_address();
+            if (ws == nullptr) return DR_E_DEVICE;
+        }
+        return launch_forward(desc, sz, q, k, v, beta, wgate, g, S0, o, S_T, ws, stream);
     } catch (...) {
         return DR_E_LAUNCH;
     }

@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.delta_fwd.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.delta_fwd.restype = ctypes.c_int
+    lib.delta_fwd_noalloc.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.delta_fwd_noalloc.restype = ctypes.c_int
     lib.delta_decode.argtypes = [ctypes.POINTER(DrDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.delta_decode.restype = ctypes.c_int
     lib.delta_bwd.argtypes = [ctypes.POINTER(DrDesc)] + [vp] * 17 + [sz, vp]
@@ -194,6 +196,40 @@ def delta_fwd(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != 0:
         _raise(st)
     return o, S_T
+
+
+def delta_fwd_noalloc(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      beta: torch.Tensor, o: torch.Tensor, wgate: Optional[torch.Tensor] = None,
+                      g: Optional[torch.Tensor] = None, S0: Optional[torch.Tensor] = None,
+                      S_T: Optional[torch.Tensor] = None, chunk: int = 64, stream=None) -> None:
+    """delta_fwd through the entry point that allocates nothing (the library's
+    built-in scratch replaces the workspace).  Outputs o (and S_T, if given)
+    must be supplied; this wrapper allocates nothing either."""
+    lib = load_library()
+    var = VARIANTS[variant]
+    B, T, Hk, dk = q.shape
+    H, dv = v.shape[2], v.shape[-1]
+    dt, dev = q.dtype, q.device
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check("q", q, (B, T, Hk, dk), dt, dev)
+    _check("k", k, (B, T, Hk, dk), dt, dev)
+    _check("v", v, (B, T, H, dv), dt, dev)
+    _check("beta", beta, (B, T, H, dk) if variant in _CHANNEL_BETA else (B, T, H), dt, dev)
+    if variant == "gdn2":
+        _check("wgate", wgate, (B, T, H, dv), dt, dev)
+    if variant != "deltanet":
+        _check("g", g, (B, T, H) if variant == "gdn" else (B, T, H, dk), dt, dev)
+    if S0 is not None:
+        _check("S0", S0, (B, H, dv, dk), torch.float32, dev)
+    _check("o", o, (B, T, H, dv), dt, dev)
+    if S_T is not None:
+        _check("S_T", S_T, (B, H, dv, dk), torch.float32, dev)
+    desc = DrDesc(B, T, H, dk, dv, chunk, var, DTYPES[dt], Hk)
+    st = lib.delta_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(wgate),
+                               _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream))
+    if st != 0:
+        _raise(st)
 
 
 def delta_decode(variant: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -24,7 +24,7 @@ def test_exports_every_header_symbol():
     assert set(names) == {"delta_fwd", "delta_decode", "delta_bwd", "delta_efla_beta",
                           "delta_ttt_pre", "dr_status_str", "dr_abi_version",
                           "delta_fwd_workspace_bytes", "delta_bwd_workspace_bytes",
-                          "delta_ttt_pre_workspace_bytes"}
+                          "delta_ttt_pre_workspace_bytes", "delta_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -267,3 +267,26 @@ def test_workspace_validation():
     if not torch.cuda.is_available():
         assert fwd(desc(variant=1), ws=None, ws_bytes=0) == DR_E_DEVICE   # none needed
         assert fwd(d, ws_bytes=need) == DR_E_DEVICE
+
+
+def fwd_noalloc(d, q=FAKE[0], k=FAKE[1], v=FAKE[2], beta=FAKE[3], wgate=None, g=FAKE[5], S0=None,
+                o=FAKE[7], ST=None):
+    return lib.delta_fwd_noalloc(ctypes.byref(d) if d is not None else None, q, k, v, beta, wgate, g,
+                                 S0, o, ST, None)
+
+
+def test_noalloc_validation():
+    """The entry point without a workspace validates like delta_fwd and refuses
+    descriptors whose workspace would exceed its 64 MiB scratch, before any HIP call."""
+    assert fwd_noalloc(None) == DR_E_NULLPTR
+    assert fwd_noalloc(desc(), o=FAKE[2]) == DR_E_ALIAS
+    assert fwd_noalloc(desc(d_k=96)) == DR_E_UNSUPPORTED
+    assert fwd_noalloc(desc(), q=ctypes.c_void_p(FAKE[0].value + 8)) == DR_E_ALIGN
+    big = desc(variant=2, B=1, H=1, T=1725 * 32)            # 1725 blocks of 38 KiB > 64 MiB
+    assert ws_bytes("fwd", big)[1] > (64 << 20)
+    assert fwd_noalloc(big) == DR_E_WORKSPACE
+    assert ws_bytes("fwd", desc(variant=2, B=1, H=1, T=1724 * 32))[1] <= (64 << 20)
+    import torch
+    if not torch.cuda.is_available():
+        assert fwd_noalloc(desc(variant=2, B=1, H=1, T=1724 * 32)) == DR_E_DEVICE
+        assert fwd_noalloc(desc(variant=1)) == DR_E_DEVICE
