@@ -699,6 +699,15 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
             ST[t] = s;
         }
         read_rest(n + 1 < NC ? n + 1 : n);
+        // The next value rows are staged before this step's outputs are
+        // stored: staging waits for the value load, and with the (masked,
+        // so uncounted) stores issued after it that wait becomes a wait for
+        // every store in flight.  Placed here it covers the stores of the
+        // previous step, which have had a whole step to drain.
+        if (n + 1 < NC) {
+            stage_v(n + 1);
+            if (n + 2 < NC) vload(n + 2);
+        }
         // outputs: row 16 m + c, value columns vc0 + 4 g .. + 3.  The store
         // registers (data and address) stay reserved until the next step
         // refills them, so no instruction waits for the stores to drain.
@@ -710,10 +719,6 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
             od[m] = to_bf4(Ot[m]);
             oad[m] = orow + m * mstride;
             if (16 * m + c < Cn) *reinterpret_cast<bf16x4*>(oad[m]) = od[m];
-        }
-        if (n + 1 < NC) {
-            stage_v(n + 1);
-            if (n + 2 < NC) vload(n + 2);
         }
         // this wave's reads of the slot are done (the loader refills it in
         // the next step); the blob of sub-chunk n + 1 has landed
