@@ -493,7 +493,8 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
     constexpr int LDV = 16 + 8;                 // value staging rows (bf16)
     constexpr int SLOTS = 3;
     constexpr int NBL = BL::bytes / 1024;       // 1 KB copy instructions per blob
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SLOTS * BL::bytes + kChainWaves * 2 * kC2 * LDV * 2];
+    constexpr int STAGE = kChainWaves * 2 * kC2 * LDV * 2;   // value staging
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SLOTS * BL::bytes + STAGE + 256];   // + touch sink
     const int x = blockIdx.x;
     const int groups = (p.B * p.H + 7) / 8;
     const int vt = (x / 8) % NVT;
@@ -510,11 +511,44 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
         // j copies bytes 1024 j .. + 1023 (lane l: 16 l .. + 15).  One barrier
         // per step, matching the chain waves'.
         const unsigned char* wsh = ws + static_cast<int64_t>(bh) * NC * BL::bytes + 16 * lane;
+        // blob min(n, NC - 1) into slot(n): past the end the copy repeats the
+        // last blob into a slot that no wave reads any more (it held blob
+        // n - 3), so every step issues the same loads
         auto copy_blob = [&](int n) {
-            const unsigned char* src = wsh + static_cast<int64_t>(n) * BL::bytes;
+            const unsigned char* src = wsh + static_cast<int64_t>(min(n, NC - 1)) * BL::bytes;
             unsigned char* dst = slot(n);
 #pragma unroll
             for (int j = 0; j < NBL; ++j) blob_to_lds(src + 1024 * j, dst + 1024 * j);
+        };
+        // Blobs come from HBM cold, and a stream of such copies held a step to
+        // about 30 bytes per ns per CU (misses in flight per CU over memory
+        // latency), while copies that hit L2 cost little.  So during step n
+        // each of the head's NVT value-tile workgroups (all on one XCD, sharing
+        // its L2) touches its share of blob n + 4, pieces j = vt (mod NVT), one
+        // 4-byte load per lane and piece (every 128-byte line of the piece).
+        // The blob is then in L2 when it is copied two steps later, and the
+        // cold reads are spread over NVT CUs.  The touches are global-to-LDS
+        // loads into a 256-byte area that nothing reads: with no register
+        // result, nothing ever waits for them except the counter below.
+        // Every touch is issued (piece and blob indices clamped), so each step
+        // issues the same loads.
+        constexpr int kTouch = (NBL + NVT - 1) / NVT;   // touch loads per step
+        static_assert(kTouch >= 1 && kTouch <= 63, "touch count");
+        constexpr int kWaitCopy = (kTouch & 15) | ((kTouch >> 4) << 14) | 0x0F70;   // vmcnt(kTouch)
+        const unsigned char* wsu = ws + static_cast<int64_t>(bh) * NC * BL::bytes;   // this head's blobs
+        uint32_t toff[kTouch];   // lane offset of each touch within a blob
+#pragma unroll
+        for (int i = 0; i < kTouch; ++i) toff[i] = 16 * lane + 1024 * min(vt + NVT * i, NBL - 1);
+        unsigned char* sink = smem + SLOTS * BL::bytes + STAGE;
+        auto step = [&](int n) {
+            copy_blob(n + 2);
+            const unsigned char* src = wsu + static_cast<int64_t>(min(n + 4, NC - 1)) * BL::bytes;
+#pragma unroll
+            for (int i = 0; i < kTouch; ++i) __builtin_amdgcn_global_load_lds(src + toff[i], (lds_void2*)(sink), 4, 0, 0);
+            // the copy (and the touches of step n - 1) have landed; this
+            // step's touches may not have
+            __builtin_amdgcn_s_waitcnt(kWaitCopy);
+            lds_barrier();
         };
         // The copy of blob n + 2 issued in step n must have landed by the end
         // of step n: the chain waves read blob n + 2 into registers during
@@ -523,11 +557,7 @@ void cw_chain_kernel(FwdArgs p, const unsigned char* ws, int NC) {
         if (NC > 1) copy_blob(1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
-        for (int n = 0; n < NC; ++n) {
-            if (n + 2 < NC) copy_blob(n + 2);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            lds_barrier();
-        }
+        for (int n = 0; n < NC; ++n) step(n);
         return;
     }
     const int vc0 = vt * kVT2 + 16 * w;
