@@ -420,7 +420,6 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
             constexpr int NMAT = SPLIT ? 4 : 2;
             constexpr int NTASK = NTILE * NMAT;
             constexpr int MAXT = (NTASK + kWavesCW - 1) / kWavesCW;
-            constexpr int NKF = DK / 32;
             // mat 0: A (or A_e)   1: P (or M_k)   2: A_k   3: M_e
             auto task_rj = [](int tix, int& Rr, int& Jr) {
                 Rr = tix == 0 ? 0 : 1;

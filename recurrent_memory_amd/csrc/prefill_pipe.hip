@@ -515,7 +515,6 @@ __global__ __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(1, 1)
         const int r = 16 * Rt + c;
         return *reinterpret_cast<const bf16x8*>(tile + qk_off<DK>(r, 32 * kk + 8 * g));
     };
-    const bf16x4 z4 = {0, 0, 0, 0};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     for (int s = -2; s < N; ++s) {
