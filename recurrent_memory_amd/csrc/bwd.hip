@@ -122,6 +122,17 @@ __device__ __forceinline__ void lds_only_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Loop over the elements e = tid, tid + STRIDE, ... < N of a tile with the trip
+// count fixed at compile time and the body unrolled, so that the global loads
+// of every iteration are issued before the first one is waited for (with a
+// run-time trip count each iteration waited for its own loads).  Loads in the
+// body read a valid address on every lane (rows past the end of the sequence
+// are clamped to its last row and the value is selected away afterwards): a
+// load under a branch is waited for inside the branch.
+#define DR_TILE_FOR(e, N, STRIDE)                         \
+    static_assert((N) % (STRIDE) == 0, "tile split");     \
+    _Pragma("unroll") for (int e##_it = 0, e = tid; e##_it < (N) / (STRIDE); ++e##_it, e += (STRIDE))
+
 // T = (I + diag(rs) A)^-1 for a strictly lower C x C matrix A (row stride lda;
 // rs = nullptr means no row scale).  Called by the 64 lanes of one wave, lane col
 // computing column col by forward substitution with the column held in registers
@@ -235,17 +246,18 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
 
-    for (int e = tid; e < kBC * DK; e += kGT) {
+    DR_TILE_FOR(e, kBC * DK, kGT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
         const int64_t ti = tok_index(p, b, t0 + min(r, Cn - 1), h);
         const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h);
-        sK[r * (DK + 4) + c] = ok ? load_elem<E>(p.k, qi * DK + c) : 0.f;
-        sX[r * LD + c] = ok ? load_elem<E>(p.q, qi * DK + c) : 0.f;
+        const float kv = load_elem<E>(p.k, qi * DK + c), qv = load_elem<E>(p.q, qi * DK + c);
         float gv = 0.f;
-        if constexpr (VAR == 1) gv = ok ? load_elem<E>(p.g, ti) : 0.f;
-        if constexpr (VAR >= 2) gv = ok ? load_elem<E>(p.g, ti * DK + c) : 0.f;
-        sG[r * (DK + 4) + c] = gv;
+        if constexpr (VAR == 1) gv = load_elem<E>(p.g, ti);
+        if constexpr (VAR >= 2) gv = load_elem<E>(p.g, ti * DK + c);
+        sK[r * (DK + 4) + c] = ok ? kv : 0.f;
+        sX[r * LD + c] = ok ? qv : 0.f;
+        sG[r * (DK + 4) + c] = ok ? gv : 0.f;
     }
     // FG^2-GDN (VAR 4): the step sizes sit on the key side (E = beta ⊙ k in the
     // columns of Abar and Mq and in Kbar); the rows take 1
@@ -337,9 +349,10 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kGT) {   // Y = beta v
+    DR_TILE_FOR(e, kBC * DV, kGT) {   // Y = beta v
         const int r = e / DV, i = e % DV;
-        sX[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tok_index(p, b, t0 + r, h) * DV + i) : 0.f;
+        const float vv = load_elem<E>(p.v, tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i);
+        sX[r * LD + i] = r < Cn ? sBeta[r] * vv : 0.f;
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // U = T Y
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    for (int e = tid; e < kBVT * DK; e += kCT) {
+    DR_TILE_FOR(e, kBVT * DK, kCT) {
         const int i = e / DK, c = e % DK;
         sS[i * SS + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
@@ -439,14 +452,11 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         if (tid < DK) sGam[tid] = pG;
         if constexpr (SPLIT) {   // X = w v for this tile's value columns
             const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
-            for (int e = tid; e < kBC * kBVT; e += kCT) {
+            DR_TILE_FOR(e, kBC * kBVT, kCT) {
                 const int r = e / kBVT, i = e % kBVT;
-                float x = 0.f;
-                if (r < Cn) {
-                    const int64_t vi = tok_index(p, b, t0 + r, h) * DV + i0 + i;
-                    x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
-                }
-                sXt[r * SV + i] = x;
+                const int64_t vi = tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i;
+                const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
+                sXt[r * SV + i] = r < Cn ? x : 0.f;
             }
         }
         lds_only_barrier();
@@ -537,7 +547,7 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    for (int e = tid; e < kBVT * DK; e += kCT) {
+    DR_TILE_FOR(e, kBVT * DK, kCT) {
         const int i = e / DK, c = e % DK;
         sdS[i * SD + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
     }
@@ -683,9 +693,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     constexpr int TCC = (kBC / 16) * (kBC / 16);  // C x C tiles
 
     if (tid < kBC) sBeta[tid] = tid < Cn ? (VAR == 4 ? 1.f : load_elem<E>(p.beta, tix(tid))) : 0.f;
-    for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Vt -> R1, dVt -> R2
+    DR_TILE_FOR(e, kBC * DV, kGT) {   // dO -> R0, Vt -> R1, dVt -> R2
         const int r = e / DV, i = e % DV;
-        R0[r * LD + i] = r < Cn ? load_elem<E>(p.dO, tix(r) * DV + i) : 0.f;
+        const float d = load_elem<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
+        R0[r * LD + i] = r < Cn ? d : 0.f;
         R1[r * LD + i] = R[L::oVt + e];
         R2[r * LD + i] = R[L::odVt + e];
     }
@@ -784,7 +795,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         sCol[DK + tid] = acc;
     }
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
-    for (int e = tid; e < kBC * DK; e += kGT) {   // dW -> R0, X -> R1
+    DR_TILE_FOR(e, kBC * DK, kGT) {   // dW -> R0, X -> R1
         const int r = e / DK, c = e % DK;
         R0[r * LD + c] = R[L::odW + e];
         R1[r * LD + c] = sBeta[r] * R[L::oKh + e];
@@ -798,9 +809,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                          [&](int c, int j) { return R1[j * LD + c]; });
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kGT) {   // Y -> R1
+    DR_TILE_FOR(e, kBC * DV, kGT) {   // Y -> R1
         const int r = e / DV, i = e % DV;
-        R1[r * LD + i] = r < Cn ? sBeta[r] * load_elem<E>(p.v, tix(r) * DV + i) : 0.f;
+        const float vv = load_elem<E>(p.v, tix(min(r, Cn - 1)) * DV + i);
+        R1[r * LD + i] = r < Cn ? sBeta[r] * vv : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -815,7 +827,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     // dA = -T^T dT T^T (strictly lower); T -> R1[0 .. C*CP), tmp -> R1[C*CP ..)
     float* sT = R1;
     float* sTmp = R1 + kBC * CP;
-    for (int e = tid; e < kBC * kBC; e += kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    DR_TILE_FOR(e, kBC * kBC, kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
@@ -872,11 +884,13 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     // q, k, G -> R0, R1, R2; dAbar = beta dA
     for (int e = tid; e < kBC * kBC; e += kGT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];
-    for (int e = tid; e < kBC * DK; e += kGT) {
+    DR_TILE_FOR(e, kBC * DK, kGT) {
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        R0[r * LD + c] = ok ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
-        R1[r * LD + c] = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
+        const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c;
+        const float qv = load_elem<E>(p.q, qi), kv = load_elem<E>(p.k, qi);
+        R0[r * LD + c] = ok ? qv : 0.f;
+        R1[r * LD + c] = ok ? kv : 0.f;
         R2[r * LD + c] = R[L::oG + e];
     }
     __syncthreads();
@@ -932,9 +946,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             colg[m] = pair_tile<false>(r0, c0, M1, Qf, Gf) + pair_tile<false>(r0, c0, M2, Kf, Gf);
         }
         __syncthreads();
-        for (int e = tid; e < kBC * DK; e += kGT) {
+        DR_TILE_FOR(e, kBC * DK, kGT) {
             const int r = e / DK, c = e % DK;
-            R1[r * LD + c] *= r < Cn ? load_elem<E>(p.beta, tix(r) * DK + c) : 0.f;
+            const float bv = load_elem<E>(p.beta, tix(min(r, Cn - 1)) * DK + c);
+            R1[r * LD + c] *= r < Cn ? bv : 0.f;
         }
         __syncthreads();
 #pragma unroll
