@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     __syncthreads();
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 4) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
-    for (int e = tid; e < kBC * DK; e += kGT) {
+    DR_TILE_FOR(e, kBC * DK, kGT) {
         const int r = e / DK, c = e % DK;
         const float G = sG[r * (DK + 4) + c];
         const float eg = __expf(G);
@@ -870,13 +870,24 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     if constexpr (VAR != 4) {   // dbeta: kRT threads per row, fixed-order sums
         const int r = tid / kRT, qt = tid % kRT;
         float db = 0.f;
-        for (int c = qt * (DK / kRT); c < (qt + 1) * (DK / kRT); ++c)
+#pragma unroll
+        for (int k = 0; k < DK / kRT; ++k) {
+            const int c = qt * (DK / kRT) + k;
             db = fmaf(R[L::odX + r * DK + c], R[L::oKh + r * DK + c], db);
-        if (r < Cn)
-            for (int i = qt * (DV / kRT); i < (qt + 1) * (DV / kRT); ++i)
-                db = fmaf(R0[r * LD + i], load_elem<E>(p.v, tix(r) * DV + i), db);
-        for (int j = qt * (kBC / kRT); j < (qt + 1) * (kBC / kRT); ++j)
+        }
+        const int64_t vrow = tix(min(r, Cn - 1)) * DV;
+        float dv_ = 0.f;
+#pragma unroll
+        for (int k = 0; k < DV / kRT; ++k) {
+            const int i = qt * (DV / kRT) + k;
+            dv_ = fmaf(R0[r * LD + i], load_elem<E>(p.v, vrow + i), dv_);
+        }
+        db += r < Cn ? dv_ : 0.f;
+#pragma unroll
+        for (int k = 0; k < kBC / kRT; ++k) {
+            const int j = qt * (kBC / kRT) + k;
             db = fmaf(sM2[r * CP + j], R[L::oAb + r * kBC + j], db);
+        }
 #pragma unroll
         for (int m = 1; m < kRT; m <<= 1) db += __shfl_xor(db, m);
         if (qt == 0 && r < Cn) store_elem<E>(p.gbeta, tix(r), db);
@@ -1074,13 +1085,16 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
 
-    for (int e = tid; e < kBC * DK; e += kGT) {   // k, b k, g
+    DR_TILE_FOR(e, kBC * DK, kGT) {   // k, b k, g
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        const float kk = ok ? load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
+        const int rc = min(r, Cn - 1);
+        const float kv = load_elem<E>(p.k, qk_index(p, b, t0 + rc, h) * DK + c);
+        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c), gv = load_elem<E>(p.g, tix(rc) * DK + c);
+        const float kk = ok ? kv : 0.f;
         sK[r * (DK + 4) + c] = kk;
-        sR1[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * kk : 0.f;
-        sG[r * (DK + 4) + c] = ok ? load_elem<E>(p.g, tix(r) * DK + c) : 0.f;
+        sR1[r * LD + c] = ok ? bv * kk : 0.f;
+        sG[r * (DK + 4) + c] = ok ? gv : 0.f;
     }
     __syncthreads();
     if (tid < DK) {
@@ -1117,7 +1131,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     if (tid < kBC) unit_lower_inverse(sM, CP, nullptr, sT, CP, tid);   // T = (I + Ae)^-1
     __syncthreads();
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
-    for (int e = tid; e < kBC * DK; e += kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
+    DR_TILE_FOR(e, kBC * DK, kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
         const int r = e / DK, c = e % DK;
         const float G = sG[r * (DK + 4) + c];
         const float eg = __expf(G), eb = __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
@@ -1136,13 +1150,13 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kGT) {   // X = w v -> sR1
+    DR_TILE_FOR(e, kBC * DV, kGT) {   // X = w v -> sR1
         const int r = e / DV, i = e % DV;
-        float x = 0.f;
-        if (r < Cn) x = load_elem<E>(p.wgate, tix(r) * DV + i) * load_elem<E>(p.v, tix(r) * DV + i);
-        sR1[r * LD + i] = x;
+        const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
+        const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
+        sR1[r * LD + i] = r < Cn ? x : 0.f;
     }
-    for (int e = tid; e < kBC * kBC; e += kGT) sM[(e / kBC) * CP + e % kBC] = R[L::oAk + e];
+    DR_TILE_FOR(e, kBC * kBC, kGT) sM[(e / kBC) * CP + e % kBC] = R[L::oAk + e];
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Z = Ak X
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
@@ -1160,12 +1174,15 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kGT) {   // q -> sR1, b k -> sR2, Qhat
+    DR_TILE_FOR(e, kBC * DK, kGT) {   // q -> sR1, b k -> sR2, Qhat
         const int r = e / DK, c = e % DK;
         const bool ok = r < Cn;
-        const float qq = ok ? load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c) : 0.f;
+        const int rc = min(r, Cn - 1);
+        const float qv = load_elem<E>(p.q, qk_index(p, b, t0 + rc, h) * DK + c);
+        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c);
+        const float qq = ok ? qv : 0.f;
         sR1[r * LD + c] = qq;
-        sR2[r * LD + c] = ok ? load_elem<E>(p.beta, tix(r) * DK + c) * sK[r * (DK + 4) + c] : 0.f;
+        sR2[r * LD + c] = ok ? bv * sK[r * (DK + 4) + c] : 0.f;
         R[L::oQh + e] = qq * __expf(sG[r * (DK + 4) + c]);
     }
     __syncthreads();
@@ -1217,9 +1234,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
     auto tj = [&](int j0) { return j0 + (l & 15); };
     auto xval = [&](int r, int i) {   // X = w v (zero past the sequence)
-        if (r >= Cn) return 0.f;
-        const int64_t vi = tix(r) * DV + i;
-        return load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
+        const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
+        const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
+        return r < Cn ? x : 0.f;
     };
     // stage rows [i0, i0 + QR) of a [DV][DK] workspace matrix into sM2
     // row blocks of a [DV][DK] workspace matrix, double-buffered through registers:
@@ -1238,9 +1255,10 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
     };
 
-    for (int e = tid; e < kBC * DV; e += kGT) {   // dO -> R0, Y -> R1, X -> R2
+    DR_TILE_FOR(e, kBC * DV, kGT) {   // dO -> R0, Y -> R1, X -> R2
         const int r = e / DV, i = e % DV;
-        R0[r * LD + i] = r < Cn ? load_elem<E>(p.dO, tix(r) * DV + i) : 0.f;
+        const float d = load_elem<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
+        R0[r * LD + i] = r < Cn ? d : 0.f;
         R1[r * LD + i] = R[L::oVt + e];
         R2[r * LD + i] = xval(r, i);
     }
@@ -1328,7 +1346,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
         sPart[tid] = acc;
     }
-    for (int e = tid; e < kBC * DV; e += kGT) R0[(e / DV) * LD + e % DV] = R[L::odVt + e];   // dY -> R0
+    DR_TILE_FOR(e, kBC * DV, kGT) R0[(e / DV) * LD + e % DV] = R[L::odVt + e];   // dY -> R0
     __syncthreads();
     if (tid < DK) {
         float acc = 0.f;
@@ -1362,7 +1380,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     float* sT = R1;   // Y is no longer needed
     float* sTmp = R1 + kBC * CP;
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    DR_TILE_FOR(e, kBC * kBC, kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
     __syncthreads();
     for (int t = w; t < TCV; t += kGW) {          // dZ = T^T dY
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
@@ -1410,8 +1428,10 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DV; e += kGT)
-        R0[(e / DV) * LD + e % DV] = (e / DV) < Cn ? load_elem<E>(p.dO, tix(e / DV) * DV + e % DV) : 0.f;
+    DR_TILE_FOR(e, kBC * DV, kGT) {
+        const float d = load_elem<E>(p.dO, tix(min(e / DV, Cn - 1)) * DV + e % DV);
+        R0[(e / DV) * LD + e % DV] = (e / DV) < Cn ? d : 0.f;
+    }
     __syncthreads();
     for (int t = w; t < TCV; t += kGW) {          // dX = Mk^T dO + Kbar dS'^T + Ak^T dZ -> dv, dw
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
@@ -1437,20 +1457,17 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
     for (int m = 0; m < MT; ++m) aq[m] = ak[m] = abk[m] = ag[m] = z4;
     auto stage = [&](float* dst, int what) {   // 0 q, 1 k, 2 b k, 3 G
-        for (int e = tid; e < kBC * DK; e += kGT) {
-            const int r = e / DK, c = e % DK;
-            float x;
-            if (what == 3) {
-                x = R[L::oG + e];
-            } else if (r >= Cn) {
-                x = 0.f;
-            } else if (what == 0) {
-                x = load_elem<E>(p.q, qk_index(p, b, t0 + r, h) * DK + c);
-            } else {
-                x = load_elem<E>(p.k, qk_index(p, b, t0 + r, h) * DK + c);
-                if (what == 2) x *= load_elem<E>(p.beta, tix(r) * DK + c);
+        if (what == 3) {
+            DR_TILE_FOR(e, kBC * DK, kGT) dst[(e / DK) * LD + e % DK] = R[L::oG + e];
+        } else {
+            const void* src = what == 0 ? p.q : p.k;
+            DR_TILE_FOR(e, kBC * DK, kGT) {
+                const int r = e / DK, c = e % DK;
+                const int rc = min(r, Cn - 1);
+                float x = load_elem<E>(src, qk_index(p, b, t0 + rc, h) * DK + c);
+                if (what == 2) x *= load_elem<E>(p.beta, tix(rc) * DK + c);
+                dst[r * LD + c] = r < Cn ? x : 0.f;
             }
-            dst[r * LD + c] = x;
         }
     };
     auto Gf = [&](int r, int c) { return R2[r * LD + c]; };
@@ -1464,7 +1481,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         c0 = 16 * (t % (DK / 16));
     };
     // pass 1: Me (q, b k) and Mk (q, k) with G; q -> R0, b k -> R1, G -> R2
-    for (int e = tid; e < kBC * kBC; e += kGT) {
+    DR_TILE_FOR(e, kBC * kBC, kGT) {
         sM1[(e / kBC) * CP + e % kBC] = R[L::odMe + e];
         sM2[(e / kBC) * CP + e % kBC] = R[L::odMk + e];
     }
@@ -1505,7 +1522,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     }
     __syncthreads();
     // pass 2: Ae (k, b k) and Ak (k, k); b k -> R0
-    for (int e = tid; e < kBC * kBC; e += kGT) {
+    DR_TILE_FOR(e, kBC * kBC, kGT) {
         sM1[(e / kBC) * CP + e % kBC] = R[L::odAe + e];
         sM2[(e / kBC) * CP + e % kBC] = R[L::odAk + e];
     }
