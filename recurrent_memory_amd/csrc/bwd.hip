@@ -123,15 +123,16 @@ __device__ __forceinline__ void lds_only_barrier() {
 }
 
 // Loop over the elements e = tid, tid + STRIDE, ... < N of a tile with the trip
-// count fixed at compile time and the body unrolled, so that the global loads
-// of every iteration are issued before the first one is waited for (with a
-// run-time trip count each iteration waited for its own loads).  Loads in the
-// body read a valid address on every lane (rows past the end of the sequence
-// are clamped to its last row and the value is selected away afterwards): a
-// load under a branch is waited for inside the branch.
+// count fixed at compile time and the body unrolled by 8, so that the global
+// loads of 8 iterations are issued before the first of them is waited for (with
+// a run-time trip count each iteration waited for its own loads; unrolling
+// completely made the gradient kernel spill registers).  Loads in the body read
+// a valid address on every lane (rows past the end of the sequence are clamped
+// to its last row and the value is selected away afterwards): a load under a
+// branch is waited for inside the branch.
 #define DR_TILE_FOR(e, N, STRIDE)                         \
     static_assert((N) % (STRIDE) == 0, "tile split");     \
-    _Pragma("unroll") for (int e##_it = 0, e = tid; e##_it < (N) / (STRIDE); ++e##_it, e += (STRIDE))
+    _Pragma("unroll 8") for (int e##_it = 0, e = tid; e##_it < (N) / (STRIDE); ++e##_it, e += (STRIDE))
 
 // T = (I + diag(rs) A)^-1 for a strictly lower C x C matrix A (row stride lda;
 // rs = nullptr means no row scale).  Called by the 64 lanes of one wave, lane col
