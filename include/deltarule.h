@@ -146,10 +146,13 @@ typedef struct {
  *          d_k = 64, rounded up to 256 bytes
  *
  * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) are evaluated with exponents taken
- * relative to the boundaries of 16-token blocks: the log-decay of one channel
- * summed over any 16 consecutive tokens must stay above about -85 (a decay
- * factor of e^-85), otherwise a split factor leaves the fp32 range and the
- * outputs become inf/NaN.  Per-token decays down to e^-5 always satisfy this.
+ * relative to the boundaries of 16-token blocks, which keeps every factor inside
+ * the fp32 range as long as one channel's log-decay summed over 16 tokens stays
+ * above about -85.  To guarantee that, every per-token channel log-decay is
+ * clamped to -85/16 = -5.3125 (a decay factor of about 0.0049 per token) when it
+ * is loaded, by delta_fwd, delta_decode and delta_bwd alike: a gate below the
+ * floor acts as the floor, and delta_bwd returns a zero dg for it.  Gates at or
+ * above the floor are used as given.  The scalar decay of DR_GDN needs no floor.
  */
 dr_status delta_fwd_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_fwd(const dr_desc* desc, const void* q, const void* k, const void* v,
@@ -233,10 +236,9 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *          dtype (written): gradient of the log-decay g
  *   dS0    [B, H, d_v, d_k] fp32 (written), gradient of S0; NULL if not wanted
  *
- * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) obey the same bound as in
- * delta_fwd: the log-decay of a channel summed over any 16 consecutive tokens
- * must stay above about -85 (pairwise factors are split at a reference row of
- * each 16-token block).
+ * Channel-wise decays (DR_KDA, DR_GDN2, DR_FG2) are clamped to the same floor
+ * as in delta_fwd, -85/16 per token (pairwise factors are split at a reference
+ * row of each 16-token block); dg is zero for a gate below the floor.
  *
  * Grouped query/key heads (H_k < H): q, k, dq and dk are [B, T, H_k, d_k]; dq and
  * dk are summed over each group of value heads, through two fp32 buffers of

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         const float kv = load_elem<E>(p.k, qi * DK + c), qv = load_elem<E>(p.q, qi * DK + c);
         float gv = 0.f;
         if constexpr (VAR == 1) gv = load_elem<E>(p.g, ti);
-        if constexpr (VAR >= 2) gv = load_elem<E>(p.g, ti * DK + c);
+        if constexpr (VAR >= 2) gv = fmaxf(load_elem<E>(p.g, ti * DK + c), kLogDecayFloor);
         sK[r * (DK + 4) + c] = ok ? kv : 0.f;
         sX[r * LD + c] = ok ? qv : 0.f;
         sG[r * (DK + 4) + c] = ok ? gv : 0.f;
@@ -685,6 +685,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
+    // the gate of (row r < Cn, channel c) is at or above the log-decay floor (a
+    // gate clamped to the floor has no gradient)
+    auto gate_kept = [&](int r, int c) { return load_elem<E>(p.g, tix(r) * DK + c) >= kLogDecayFloor; };
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     // element q of a tile at (i0, j0) in this lane
     auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
@@ -1049,7 +1052,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             for (int r = kBC - 1; r >= 0; --r) {
                 acc += dgv[r];
                 if constexpr (VAR >= 2) {
-                    if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, acc);
+                    // a gate clamped at the floor has no gradient
+                    if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, gate_kept(r, c) ? acc : 0.f);
                 } else {
                     R[L::odQh + r * DK + c] = acc;
                 }
@@ -1091,7 +1095,8 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         const bool ok = r < Cn;
         const int rc = min(r, Cn - 1);
         const float kv = load_elem<E>(p.k, qk_index(p, b, t0 + rc, h) * DK + c);
-        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c), gv = load_elem<E>(p.g, tix(rc) * DK + c);
+        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c);
+        const float gv = fmaxf(load_elem<E>(p.g, tix(rc) * DK + c), kLogDecayFloor);
         const float kk = ok ? kv : 0.f;
         sK[r * (DK + 4) + c] = kk;
         sR1[r * LD + c] = ok ? bv * kk : 0.f;
@@ -1231,6 +1236,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
+    // the gate of (row r < Cn, channel c) is at or above the log-decay floor (a
+    // gate clamped to the floor has no gradient)
+    auto gate_kept = [&](int r, int c) { return load_elem<E>(p.g, tix(r) * DK + c) >= kLogDecayFloor; };
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
     auto tj = [&](int j0) { return j0 + (l & 15); };
@@ -1583,7 +1591,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int r = kBC - 1; r >= 0; --r) {
             acc += dgv[r];
-            if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, acc);
+            if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, gate_kept(r, c) ? acc : 0.f);
         }
     }
 }

@@ -12,6 +12,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Floor applied to every per-token, per-channel log-decay (channel-wise forms)
+// when it is loaded.  Those kernels take exponents relative to 16-token block
+// boundaries; 16 tokens at the floor sum to -85, and e^85 stays inside fp32.
+// Below the floor the factors would overflow; a gate that is clamped gets a
+// zero gradient.  (-85/16 is exact in bf16.)
+constexpr float kLogDecayFloor = -85.0f / 16.0f;
+
 // Input element types: fp32 or bf16 (stored as raw 16-bit patterns).
 struct F32 {
     typedef float T;

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
         } else if constexpr (VAR == 1) {
             aa[c] = load_elem<E>(p.g, tok);
         } else {
-            aa[c] = load_elem<E>(p.g, tok * DK + c0 + c);
+            aa[c] = fmaxf(load_elem<E>(p.g, tok * DK + c0 + c), kLogDecayFloor);
         }
         if constexpr (VAR >= 3) bk[c] = load_elem<E>(p.beta, tok * DK + c0 + c);
         else bk[c] = 0.0f;

@@ -339,10 +339,10 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const float2 v = ld2(sRawG, r0 + j);
-                g0[j] = v.x;
-                g1[j] = v.y;
-                p0 += v.x;
-                p1 += v.y;
+                g0[j] = fmaxf(v.x, kLogDecayFloor);
+                g1[j] = fmaxf(v.y, kLogDecayFloor);
+                p0 += g0[j];
+                p1 += g1[j];
             }
             // exclusive prefix over the row groups, and the block-start and
             // chunk-end values (G is the running sum of the raw log-decays)

@@ -234,10 +234,10 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
             const float2 v = ld2(sRawG, r0 + j);
-            g0[j] = v.x;
-            g1[j] = v.y;
-            p0 += v.x;
-            p1 += v.y;
+            g0[j] = fmaxf(v.x, kLogDecayFloor);
+            g1[j] = fmaxf(v.y, kLogDecayFloor);
+            p0 += g0[j];
+            p1 += g1[j];
             if (SPLIT || p.keywrite) {
                 const float2 bv = ld2(sRawB, r0 + j);
                 b0[j] = bv.x;

@@ -109,6 +109,14 @@ def _neg_softplus(z: np.ndarray) -> np.ndarray:
     return (-np.logaddexp(np.float32(0.0), z)).astype(np.float32)
 
 
+# Channel log-decays are drawn at or above -85/16, the per-token floor that the
+# library applies when it loads a channel gate (include/deltarule.h), so both
+# sides of a comparison see the same gates.  At gate_scale 1 a draw falls below
+# it with probability about 5e-8 per entry; tests of the floor itself set gates
+# below it explicitly.
+CHANNEL_LOG_DECAY_FLOOR = np.float32(-85.0 / 16.0)
+
+
 def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: int, dv: int,
          gate_scale: float = 1.0, qk_heads: Optional[int] = None,
          key_norm: float = 1.0) -> Dict[str, Optional[np.ndarray]]:
@@ -120,7 +128,8 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
     per key channel (last dim dk); otherwise ``beta`` has shape ``lead``; and
     ``wgate`` is None except for the split-gate form.  ``g`` is None for the ungated form,
     shape ``lead`` for a scalar gate and ``lead + (dk,)`` for channel gates.
-    ``gate_scale`` multiplies the log-decays (e.g. 1/16 for weak decay).
+    ``gate_scale`` multiplies the log-decays (e.g. 1/16 for weak decay); channel
+    log-decays are then kept at or above CHANNEL_LOG_DECAY_FLOOR.
     ``qk_heads`` replaces the last entry of ``lead`` for q and k (grouped value
     heads); ``key_norm`` is the L2 norm of every key before rounding.
     """
@@ -147,6 +156,7 @@ def draw(rng: np.random.Generator, variant: str, dtype: str, lead: tuple, dk: in
         g = _neg_softplus(rng.standard_normal(lead, dtype=np.float32)) * np.float32(gate_scale)
     else:
         g = _neg_softplus(rng.standard_normal(lead + (dk,), dtype=np.float32)) * np.float32(gate_scale)
+        g = np.maximum(g, CHANNEL_LOG_DECAY_FLOOR)
     out = dict(q=q, k=k, v=v, beta=beta, wgate=wgate, g=g)
     return {name: (None if t is None else cast(t, dtype)) for name, t in out.items()}
 

@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 from recurrent_memory_amd import ops
+from recurrent_memory_amd.inputs import CHANNEL_LOG_DECAY_FLOOR
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 # max relative error per [batch, head] slice (max |x - ref| / max |ref|)
@@ -63,3 +64,17 @@ def announce(*parts):
     import sys
     sys.__stderr__.write("[gpu case] " + " ".join(str(p) for p in parts) + "\n")
     sys.__stderr__.flush()
+
+
+LOG_DECAY_FLOOR = float(CHANNEL_LOG_DECAY_FLOOR)   # per-token floor of channel log-decays (include/deltarule.h)
+
+
+def floor_gates(shape, dtype, seed):
+    """Channel log-decays in [-4, 0] with a share at -10 per token, below the
+    floor: every channel of tokens 20..39 and channel 3 of every token."""
+    from recurrent_memory_amd.inputs import round_to_bf16
+    rng = np.random.default_rng(seed)
+    g = (-rng.uniform(0, 4, shape)).astype(np.float32)
+    g[:, 20:40] = -10.0
+    g[..., 3] = -10.0
+    return g if dtype == "f32" else round_to_bf16(g)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle_pool import bwd_all_heads
-from gpu_util import TOL, announce, dev, host, slice_rel_err
+from gpu_util import LOG_DECAY_FLOOR, TOL, announce, dev, floor_gates, host, slice_rel_err
 from oracle import delta_bwd as oracle_bwd
 from recurrent_memory_amd import ops
 from recurrent_memory_amd.inputs import Workload, make_forward_inputs
@@ -69,6 +69,30 @@ def test_bwd_small(variant, dtype, dk, dv, T):
     _check(variant, dtype, gr, ref)
 
 
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_gate_floor(variant, dtype):
+    """Channel log-decays of -10 are clamped to -85/16 on load: every gradient
+    equals the oracle's reverse mode on the clamped gates, except dg, which is
+    zero where the gate was clamped (the clamp passes no gradient) and the
+    oracle's elsewhere."""
+    announce("bwd_gate_floor", variant, dtype)
+    w = Workload("t", variant, dtype, B=2, H=2, T=130, dk=128, dv=64, random_s0=True, seed=47)
+    x = make_forward_inputs(w)
+    x["g"] = floor_gates(x["g"].shape, dtype, 8)
+    dO, dST = _upstream(w, 13)
+    gr = _run(variant, dtype, w, x, dO, dST)
+    clamped = x["g"] < LOG_DECAY_FLOOR
+    gc = np.maximum(x["g"], LOG_DECAY_FLOOR)
+    ref = oracle_bwd(variant, x["q"], x["k"], x["v"], x["beta"], x["wgate"], gc, x["S0"], dO, dST)
+    for n in gr:
+        if gr[n] is not None:
+            assert np.isfinite(gr[n]).all(), n
+    assert (gr["dg"][clamped] == 0).all()
+    ref["dg"] = np.where(clamped, 0.0, ref["dg"])
+    _check(variant, dtype, gr, ref)
+
+
 @pytest.mark.parametrize("variant", VARS)
 def test_bwd_no_state_gradient(variant):
     """dS_T = NULL (zero) and dS0 not requested; zero initial state."""
@@ -110,8 +134,9 @@ def test_bwd_deterministic():
 @pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_strong_channel_gates(variant, dtype):
-    """Log-decays scaled by 3 (16-token sums near -35): the block-reference factors
-    of the pairwise sums then reach e^{35} inside a block."""
+    """Log-decays scaled by 3 (16-token sums near -35, single gates down to the
+    -85/16 floor): the block-reference factors of the pairwise sums then reach
+    e^{35} inside a block."""
     announce("bwd_strong_gates", variant, dtype)
     w = Workload("t", variant, dtype, B=1, H=2, T=200, dk=128, dv=128, random_s0=True, seed=46)
     x = make_forward_inputs(w, gate_scale=3.0)

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, announce, dev, host, slice_rel_err
+from gpu_util import LOG_DECAY_FLOOR, TOL, announce, dev, host, slice_rel_err
 from oracle import delta_decode as oracle_decode
 from recurrent_memory_amd import ops
 from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_decode_inputs
@@ -46,6 +46,30 @@ def test_decode_small(variant, dtype, dk, dv):
     d = make_decode_inputs(w, 4)
     outs, S = _run_steps(variant, dtype, d, 4)
     ref_outs, S_ref = _oracle_steps(variant, d, 4)
+    for o, r in zip(outs, ref_outs):
+        assert slice_rel_err(o, r, (0, 1)) <= TOL[dtype]
+    assert slice_rel_err(S, S_ref, (0, 1)) <= 1e-5
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_gate_floor(variant, dtype):
+    """Channel log-decays of -10 are clamped to -85/16 on load, as in the forward,
+    so decode continues a prefill on the same gates: equal to the oracle on the
+    clamped gates."""
+    announce("decode_gate_floor", variant, dtype)
+    w = Workload("t", variant, dtype, B=3, H=5, T=1, dk=128, dv=128, random_s0=True, seed=12)
+    d = make_decode_inputs(w, 3)
+    for i, st in enumerate(d["steps"]):
+        g = st["g"].copy()
+        g[..., 3] = -10.0
+        if i == 1:
+            g[...] = -10.0
+        st["g"] = g
+    outs, S = _run_steps(variant, dtype, d, 3)
+    for st in d["steps"]:
+        st["g"] = np.maximum(st["g"], LOG_DECAY_FLOOR)
+    ref_outs, S_ref = _oracle_steps(variant, d, 3)
     for o, r in zip(outs, ref_outs):
         assert slice_rel_err(o, r, (0, 1)) <= TOL[dtype]
     assert slice_rel_err(S, S_ref, (0, 1)) <= 1e-5

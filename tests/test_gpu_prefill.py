@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, announce, dev, errs, gpu_fwd, host, slice_rel_err
+from gpu_util import LOG_DECAY_FLOOR, TOL, announce, dev, errs, floor_gates, gpu_fwd, host, slice_rel_err
 from oracle_pool import fwd_all_heads
 from oracle import delta_fwd as oracle_fwd
 from recurrent_memory_amd import ops
@@ -121,6 +121,30 @@ def test_channel_decay_strong_gates(variant):
         g = (-rng.uniform(0, 4, x["g"].shape)).astype(np.float32)
         x["g"] = g if dtype == "f32" else round_to_bf16(g)
         _check(variant, dtype, x)
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "fg2"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_channel_decay_gate_floor(variant, dtype, dk):
+    """Per-token log-decays of -10 (16 tokens would sum to -160, past the range of
+    the block-relative split exponentials): every gate is clamped to -85/16 when
+    it is loaded, so the outputs are finite and equal the oracle's on the clamped
+    gates (in fp32 measurably closer to those than to the oracle's on the raw
+    gates)."""
+    announce("gate_floor", variant, dtype, dk)
+    w = Workload("t", variant, dtype, B=1, H=2, T=150, dk=dk, dv=dk, random_s0=True, seed=17)
+    x = make_forward_inputs(w)
+    x["g"] = floor_gates(x["g"].shape, dtype, 6)
+    o, S = gpu_fwd(variant, x, dtype)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    xc = dict(x, g=np.maximum(x["g"], LOG_DECAY_FLOOR))
+    o_ref, S_ref = oracle_fwd(variant, **xc)
+    eo, es = errs(o, S, o_ref, S_ref)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+    if dtype == "f32":   # the clamp is in effect: fp32 separates the two references
+        o_raw, S_raw = oracle_fwd(variant, **x)
+        assert max(errs(o, S, o_raw, S_raw)) > 10 * max(eo, es)
 
 
 def test_unit_write_full_size_no_oracle():
