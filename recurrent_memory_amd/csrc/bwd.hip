@@ -403,9 +403,13 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    DR_TILE_FOR(e, kBVT * DK, kCT) {
-        const int i = e / DK, c = e % DK;
-        sS[i * SS + c] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
+    if (p.S0) {   // (the branch outside the loop: inside, each load was waited for in turn)
+        DR_TILE_FOR(e, kBVT * DK, kCT) {
+            const int i = e / DK, c = e % DK;
+            sS[i * SS + c] = p.S0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c];
+        }
+    } else {
+        DR_TILE_FOR(e, kBVT * DK, kCT) sS[(e / DK) * SS + e % DK] = 0.f;
     }
     // the next chunk's operands are fetched into registers while this chunk's
     // products run, and written to LDS at the top of the next step
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) pU[m][q] = R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + i0 + c0 + (l & 15)];
         }
-        pG = tid < DK ? R[L::oGam + tid] : 0.f;
+        pG = R[L::oGam + min(tid, DK - 1)];   // every lane loads: no branch, no wait in it
     };
     auto put4 = [&](float* dst, int ld, int idx, float4 v) {
         *reinterpret_cast<float4*>(dst + (idx / DK) * ld + idx % DK) = v;
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int q = 0; q < 4; ++q) uu[m][q] = pU[m][q];
-        if (tid < DK) sGam[tid] = pG;
+        sGam[min(tid, DK - 1)] = pG;   // lanes past DK rewrite the last entry with its own value
         if constexpr (SPLIT) {   // X = w v for this tile's value columns
             const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
             DR_TILE_FOR(e, kBC * kBVT, kCT) {
@@ -548,9 +552,13 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     int bh, i0;
     if (!chain_block(p, NVT, bh, i0)) return;
     const int b = bh / p.H, h = bh % p.H;
-    DR_TILE_FOR(e, kBVT * DK, kCT) {
-        const int i = e / DK, c = e % DK;
-        sdS[i * SD + c] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] : 0.f;
+    if (p.dST) {
+        DR_TILE_FOR(e, kBVT * DK, kCT) {
+            const int i = e / DK, c = e % DK;
+            sdS[i * SD + c] = p.dST[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c];
+        }
+    } else {
+        DR_TILE_FOR(e, kBVT * DK, kCT) sdS[(e / DK) * SD + e % DK] = 0.f;
     }
     // the previous chunk's operands are fetched into registers during this step
     constexpr int NP = kBC * DK / 4 / kCT;
@@ -572,11 +580,11 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
         }
 #pragma unroll
-        for (int j = 0; j < NO; ++j) {
+        for (int j = 0; j < NO; ++j) {   // rows past the end: the last row, zeroed when stored
             const int e = tid + kCT * j, r = e / kBVT, i = e % kBVT;
-            pO[j] = r < Cn ? load_elem<E>(p.dO, tok_index(p, b, t0 + r, h) * DV + i0 + i) : 0.f;
+            pO[j] = load_elem<E>(p.dO, tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i);
         }
-        pG = tid < DK ? R[L::oGam + tid] : 0.f;
+        pG = R[L::oGam + min(tid, DK - 1)];   // every lane loads: no branch, no wait in it
     };
     auto put4 = [&](float* dst, int idx, int ld, int row, float4 v) {
         *reinterpret_cast<float4*>(dst + (idx / row) * ld + idx % row) = v;
@@ -593,12 +601,13 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             put4(sQh, idx, SB, DK, pQ[j]);
             put4(sA2, idx, SB, DK, pW[j]);
         }
+        const int Cn = min(kBC, p.T - n * kBC);
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
             const int e = tid + kCT * j;
-            sdO[(e / kBVT) * SO + e % kBVT] = pO[j];
+            sdO[(e / kBVT) * SO + e % kBVT] = e / kBVT < Cn ? pO[j] : 0.f;
         }
-        if (tid < DK) sGam[tid] = pG;
+        sGam[min(tid, DK - 1)] = pG;   // lanes past DK rewrite the last entry with its own value
         lds_only_barrier();
         if (n > 0) fetch(n - 1);
         for (int e = tid; e < kBVT * DK; e += kCT) {
