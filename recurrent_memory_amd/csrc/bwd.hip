@@ -134,24 +134,59 @@ __device__ __forceinline__ void lds_only_barrier() {
     static_assert((N) % (STRIDE) == 0, "tile split");     \
     _Pragma("unroll 8") for (int e##_it = 0, e = tid; e##_it < (N) / (STRIDE); ++e##_it, e += (STRIDE))
 
-// T = (I + diag(rs) A)^-1 for a strictly lower C x C matrix A (row stride lda;
-// rs = nullptr means no row scale).  Called by the 64 lanes of one wave, lane col
-// computing column col by forward substitution with the column held in registers
-// (fully unrolled), each row's sum split over four independent accumulators.
-__device__ __forceinline__ void unit_lower_inverse(const float* A, int lda, const float* rs, float* T,
-                                                   int ldt, int col) {
-    float t[kBC];
+// T = (I + diag(rs) A)^-1 for the strictly lower kBC x kBC matrix A (rs == nullptr:
+// no row scaling), called by every thread of the workgroup, in 16-row blocks:
+//   1. the four diagonal blocks T_ii = L_ii^-1 (L = I + diag(rs) A) by substitution
+//      in registers, one lane of wave 0 per column of one block;
+//   2. the blocks below the diagonal, T_ij = -T_ii sum_{j <= k < i} L_ik T_kj, for
+//      block column j on wave j, block rows i = j + 1, ... in turn, each as two
+//      matrix-core products with the partial sum passed through Z (16 x 20 floats
+//      per wave, 3 waves).
+// (Substituting whole 64-row columns, one lane per column, kept seven of the
+// eight waves idle for the length of the substitution.)
+__device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int lda, const float* rs, float* T,
+                                                           int ldt, float* Z) {
+    static_assert(kBC == 64, "four 16-row blocks");
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    if (w == 0) {
+        const int o = 16 * (l >> 4), col = l & 15;
+        float t[16];
 #pragma unroll
-    for (int r = 0; r < kBC; ++r) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 16; ++r) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < r; ++j) acc[j & 3] = fmaf(A[r * lda + j], t[j], acc[j & 3]);
-        float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        if (rs) sum *= rs[r];
-        t[r] = (r == col ? 1.f : 0.f) - sum;
+            for (int j = 0; j < r; ++j) acc[j & 3] = fmaf(A[(o + r) * lda + o + j], t[j], acc[j & 3]);
+            float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            if (rs) sum *= rs[o + r];
+            t[r] = (r == col ? 1.f : 0.f) - sum;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) T[(o + r) * ldt + o + col] = t[r];
     }
+    for (int e = tid; e < kBC * kBC; e += blockDim.x) {   // the blocks above the diagonal
+        const int r = e / kBC, c = e % kBC;
+        if (c / 16 > r / 16) T[r * ldt + c] = 0.f;
+    }
+    __syncthreads();
+    if (w < 3) {
+        const int j0 = 16 * w;
+        float* z = Z + w * (16 * 20);
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        for (int i0 = j0 + 16; i0 < kBC; i0 += 16) {
+            // Z = sum_{j <= k < i} L_ik T_kj: rows of L left of the diagonal block are rs A
+            const f32x4 zz = mm_tile(z4, i0, j0, j0, i0,
+                                     [&](int r, int k) { return rs ? rs[r] * A[r * lda + k] : A[r * lda + k]; },
+                                     [&](int k, int c) { return T[k * ldt + c]; });
 #pragma unroll
-    for (int r = 0; r < kBC; ++r) T[r * ldt + col] = t[r];
+            for (int q = 0; q < 4; ++q) z[(4 * (l >> 4) + q) * 20 + (l & 15)] = zz[q];
+            // T_ij = -T_ii Z (the wave's own LDS writes are seen by its later reads)
+            const f32x4 tt = mm_tile(z4, 0, 0, 0, 16, [&](int r, int k) { return T[(i0 + r) * ldt + i0 + k]; },
+                                     [&](int k, int c) { return z[k * 20 + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) T[(i0 + 4 * (l >> 4) + q) * ldt + j0 + (l & 15)] = -tt[q];
+        }
+    }
+    __syncthreads();
 }
 
 // Workspace record of one (batch, head, chunk), in floats.
@@ -242,6 +277,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     __shared__ float sA[kBC * (kBC + 4)];
     __shared__ float sT[kBC * (kBC + 4)];
     __shared__ float sBeta[kBC];
+    __shared__ float sZ[3 * 16 * 20];             // scratch of the blocked inverse
     const int u = blockIdx.x, tid = threadIdx.x;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
@@ -325,8 +361,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     }
     __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution, one column per thread
-    if (tid < kBC) unit_lower_inverse(sA, kBC + 4, sBeta, sT, kBC + 4, tid);
-    __syncthreads();
+    unit_lower_inverse_blocked(sA, kBC + 4, sBeta, sT, kBC + 4, sZ);
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 4) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
     DR_TILE_FOR(e, kBC * DK, kGT) {
@@ -1143,8 +1178,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     }
     __syncthreads();
     float* sT = sR2;
-    if (tid < kBC) unit_lower_inverse(sM, CP, nullptr, sT, CP, tid);   // T = (I + Ae)^-1
-    __syncthreads();
+    unit_lower_inverse_blocked(sM, CP, nullptr, sT, CP, sR2 + kBC * CP);   // T = (I + Ae)^-1
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
     DR_TILE_FOR(e, kBC * DK, kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
         const int r = e / DK, c = e % DK;
