@@ -271,34 +271,56 @@ template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int N) {
     typedef BwdWs<DK, DV> L;
     constexpr int LD = (DK > DV ? DK : DV) + 4;   // padded row stride (4 mod 64 words)
-    __shared__ float sK[kBC * (DK + 4)];
-    __shared__ float sX[kBC * LD];                // q, then beta Khat, then beta v
-    __shared__ float sG[kBC * (DK + 4)];
+    __shared__ __attribute__((aligned(16))) float sK[kBC * (DK + 4)];
+    __shared__ __attribute__((aligned(16))) float sX[kBC * LD];   // q, then beta Khat, then beta v
+    __shared__ __attribute__((aligned(16))) float sG[kBC * (DK + 4)];
     __shared__ float sA[kBC * (kBC + 4)];
     __shared__ float sT[kBC * (kBC + 4)];
-    __shared__ float sBeta[kBC];
+    __shared__ float sBeta[kBC + 1];              // (+ a spare slot, never read)
     __shared__ float sZ[3 * 16 * 20];             // scratch of the blocked inverse
     const int u = blockIdx.x, tid = threadIdx.x;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
 
-    DR_TILE_FOR(e, kBC * DK, kGT) {
-        const int r = e / DK, c = e % DK;
+    const float4 z4v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto put = [](float* dst, float4 x) { *reinterpret_cast<float4*>(dst) = x; };
+    // beta first, so that its wait is covered by the tile loads (every thread
+    // loads from a valid row: no load sits in a branch)
+    const float bt = VAR == 4 ? 1.f : load_elem<E>(p.beta, tok_index(p, b, t0 + min(tid % kBC, Cn - 1), h));
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // four consecutive channels per thread
+        const int r = 4 * e / DK, c = 4 * e % DK;
         const bool ok = r < Cn;
         const int64_t ti = tok_index(p, b, t0 + min(r, Cn - 1), h);
         const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h);
-        const float kv = load_elem<E>(p.k, qi * DK + c), qv = load_elem<E>(p.q, qi * DK + c);
-        float gv = 0.f;
-        if constexpr (VAR == 1) gv = load_elem<E>(p.g, ti);
-        if constexpr (VAR >= 2) gv = fmaxf(load_elem<E>(p.g, ti * DK + c), kLogDecayFloor);
-        sK[r * (DK + 4) + c] = ok ? kv : 0.f;
-        sX[r * LD + c] = ok ? qv : 0.f;
-        sG[r * (DK + 4) + c] = ok ? gv : 0.f;
+        const float4 kv = load4<E>(p.k, qi * DK + c), qv = load4<E>(p.q, qi * DK + c);
+        float4 gv = z4v;
+        if constexpr (VAR == 1) {
+            const float g1 = load_elem<E>(p.g, ti);
+            gv = make_float4(g1, g1, g1, g1);
+        }
+        if constexpr (VAR >= 2) {
+            gv = load4<E>(p.g, ti * DK + c);
+            gv = make_float4(fmaxf(gv.x, kLogDecayFloor), fmaxf(gv.y, kLogDecayFloor),
+                             fmaxf(gv.z, kLogDecayFloor), fmaxf(gv.w, kLogDecayFloor));
+        }
+        put(sK + r * (DK + 4) + c, ok ? kv : z4v);
+        put(sX + r * LD + c, ok ? qv : z4v);
+        put(sG + r * (DK + 4) + c, ok ? gv : z4v);
     }
     // FG^2-GDN (VAR 4): the step sizes sit on the key side (E = beta ⊙ k in the
     // columns of Abar and Mq and in Kbar); the rows take 1
-    if (tid < kBC) sBeta[tid] = tid < Cn ? (VAR == 4 ? 1.f : load_elem<E>(p.beta, tok_index(p, b, t0 + tid, h))) : 0.f;
+    // (threads past the chunk write a spare slot: a store under a branch would
+    // pull the load of bt into the branch and wait for it there)
+    sBeta[min(tid, kBC)] = tid < Cn ? bt : 0.f;
+    // v, loaded now and used after W: its loads overlap the factor products
+    constexpr int NV4 = kBC * DV / 4 / kGT;
+    float4 pv[NV4];
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {
+        const int e = tid + kGT * j, r = 4 * e / DV, i = 4 * e % DV;
+        pv[j] = load4<E>(p.v, tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i);
+    }
     __syncthreads();
     if (tid < DK) {   // in-chunk cumulative log-decay per channel
         float acc = 0.f;
@@ -308,7 +330,10 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 4) + e % DK];
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {
+        const int r = 4 * e / DK, c = 4 * e % DK;
+        put(R + L::oG + 4 * e, *reinterpret_cast<const float4*>(sG + r * (DK + 4) + c));
+    }
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 4) + tid]);
     // Abar (strictly lower) and Mq (lower, diagonal included)
     const int w = tid >> 6, l = tid & 63;
@@ -364,17 +389,25 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     unit_lower_inverse_blocked(sA, kBC + 4, sBeta, sT, kBC + 4, sZ);
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 4) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
-    DR_TILE_FOR(e, kBC * DK, kGT) {
-        const int r = e / DK, c = e % DK;
-        const float G = sG[r * (DK + 4) + c];
-        const float eg = __expf(G);
-        const float kk = sK[r * (DK + 4) + c];
-        R[L::oKh + e] = kk * eg;
-        R[L::oQh + e] = sX[r * LD + c] * eg;
-        float kb = kk * __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
-        if constexpr (VAR == 4) kb *= load_elem<E>(p.beta, tok_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
-        R[L::oKb + e] = kb;
-        sX[r * LD + c] = sBeta[r] * kk * eg;
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {
+        const int r = 4 * e / DK, c = 4 * e % DK;
+        const float4 G = *reinterpret_cast<const float4*>(sG + r * (DK + 4) + c);
+        const float4 GC = *reinterpret_cast<const float4*>(sG + (kBC - 1) * (DK + 4) + c);
+        const float4 kk = *reinterpret_cast<const float4*>(sK + r * (DK + 4) + c);
+        const float4 qq = *reinterpret_cast<const float4*>(sX + r * LD + c);
+        const float4 eg = make_float4(__expf(G.x), __expf(G.y), __expf(G.z), __expf(G.w));
+        float4 kb = make_float4(kk.x * __expf(GC.x - G.x), kk.y * __expf(GC.y - G.y), kk.z * __expf(GC.z - G.z),
+                                kk.w * __expf(GC.w - G.w));
+        if constexpr (VAR == 4) {
+            const float4 bv = load4<E>(p.beta, tok_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
+            kb = make_float4(kb.x * bv.x, kb.y * bv.y, kb.z * bv.z, kb.w * bv.w);
+        }
+        const float4 kh = make_float4(kk.x * eg.x, kk.y * eg.y, kk.z * eg.z, kk.w * eg.w);
+        put(R + L::oKh + 4 * e, kh);
+        put(R + L::oQh + 4 * e, make_float4(qq.x * eg.x, qq.y * eg.y, qq.z * eg.z, qq.w * eg.w));
+        put(R + L::oKb + 4 * e, kb);
+        const float br = sBeta[r];
+        put(sX + r * LD + c, make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w));
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T X
@@ -385,10 +418,11 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DV, kGT) {   // Y = beta v
-        const int r = e / DV, i = e % DV;
-        const float vv = load_elem<E>(p.v, tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i);
-        sX[r * LD + i] = r < Cn ? sBeta[r] * vv : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV4; ++j) {   // Y = beta v
+        const int e = tid + kGT * j, r = 4 * e / DV, i = 4 * e % DV;
+        const float br = sBeta[r];
+        put(sX + r * LD + i, r < Cn ? make_float4(br * pv[j].x, br * pv[j].y, br * pv[j].z, br * pv[j].w) : z4v);
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // U = T Y

@@ -50,6 +50,21 @@ __device__ __forceinline__ float load_elem<BF16>(const void* base, int64_t i) {
     return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
 }
 
+// Four consecutive elements from i (a multiple of 4 in a 16-byte-aligned tensor):
+// one 16-byte (fp32) or 8-byte (bf16) load.
+template <typename E>
+__device__ __forceinline__ float4 load4(const void* base, int64_t i);
+template <>
+__device__ __forceinline__ float4 load4<F32>(const void* base, int64_t i) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+}
+template <>
+__device__ __forceinline__ float4 load4<BF16>(const void* base, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 template <typename E>
 __device__ __forceinline__ void store_elem(void* base, int64_t i, float x);
 template <>
