@@ -749,12 +749,12 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;   // region size
     constexpr int QR = 32;            // rows of S (or dS') staged at a time
     static_assert(QR * (DK + 4) <= kBC * CP, "S quarter must fit the second C x C buffer");
-    __shared__ float sM1[kBC * CP];   // dMq (then dMq E)
-    __shared__ float sM2[kBC * CP];   // S quarters; dT; dA; dAbar (then dAbar E)
-    __shared__ float sR[3 * RS];      // three staging regions
-    __shared__ float sBeta[kBC];
+    __shared__ __attribute__((aligned(16))) float sM1[kBC * CP];   // dMq (then dMq E)
+    __shared__ __attribute__((aligned(16))) float sM2[kBC * CP];   // S quarters; dT; dA; dAbar (then dAbar E)
+    __shared__ __attribute__((aligned(16))) float sR[3 * RS];      // three staging regions
+    __shared__ float sBeta[kBC + 1];  // (+ a spare slot, never read)
     __shared__ float sCol[2 * DK];    // column terms of the last row of dG
-    __shared__ float sPart[kGT];      // per-thread partial column sums
+    __shared__ float4 sPart[kGT];     // per-thread partial sums of four columns
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
@@ -774,29 +774,48 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     constexpr int TCV = (kBC / 16) * (DV / 16);   // C x DV tiles
     constexpr int TCC = (kBC / 16) * (kBC / 16);  // C x C tiles
 
-    if (tid < kBC) sBeta[tid] = tid < Cn ? (VAR == 4 ? 1.f : load_elem<E>(p.beta, tix(tid))) : 0.f;
-    DR_TILE_FOR(e, kBC * DV, kGT) {   // dO -> R0, Vt -> R1, dVt -> R2
-        const int r = e / DV, i = e % DV;
-        const float d = load_elem<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
-        R0[r * LD + i] = r < Cn ? d : 0.f;
-        R1[r * LD + i] = R[L::oVt + e];
-        R2[r * LD + i] = R[L::odVt + e];
+    const float4 z4v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto put = [](float* dst, float4 x) { *reinterpret_cast<float4*>(dst) = x; };
+    auto get = [](const float* src) { return *reinterpret_cast<const float4*>(src); };
+    auto fma4 = [](float4 a, float4 b, float4 c) {
+        return make_float4(fmaf(a.x, b.x, c.x), fmaf(a.y, b.y, c.y), fmaf(a.z, b.z, c.z), fmaf(a.w, b.w, c.w));
+    };
+    // beta (every thread loads from a valid row and stores, threads past the
+    // chunk to a spare slot: no load sits in a branch)
+    {
+        const float bt = VAR == 4 ? 1.f : load_elem<E>(p.beta, tix(min(tid % kBC, Cn - 1)));
+        sBeta[min(tid, kBC)] = tid < Cn ? bt : 0.f;
     }
-    constexpr int TPC = kGT / DK;   // threads per column for column sums
-    {   // sum_i S dS' per column, TPC partial sums combined in a fixed order
-        const int c = tid % DK, part = tid / DK;
-        float acc = 0.f;
-#pragma unroll 16
-        for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
-            acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // dO -> R0, Vt -> R1, dVt -> R2 (four columns per thread)
+        const int r = 4 * e / DV, i = 4 * e % DV;
+        const float4 d = load4<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
+        put(R0 + r * LD + i, r < Cn ? d : z4v);
+        put(R1 + r * LD + i, get(R + L::oVt + 4 * e));
+        put(R2 + r * LD + i, get(R + L::odVt + 4 * e));
+    }
+    // column sums: thread (part, four columns); the parts combined in a fixed order
+    constexpr int CG = DK / 4, NPART = kGT / CG;
+    auto col_sums = [&](int64_t oa, int64_t ob, int rows) {   // sum_r a[r, c] b[r, c] -> sPart
+        const int c = 4 * (tid % CG), part = tid / CG, rp = rows / NPART;
+        float4 acc = z4v;
+#pragma unroll
+        for (int k = 0; k < rp; ++k) {
+            const int i = part * rp + k;
+            acc = fma4(get(R + oa + i * DK + c), get(R + ob + i * DK + c), acc);
+        }
         sPart[tid] = acc;
-    }
-    __syncthreads();
-    if (tid < DK) {
+    };
+    auto col_total = [&](int c) {
         float acc = 0.f;
-        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
-        sCol[tid] = R[L::oGam + tid] * acc;
-    }
+        for (int part = 0; part < NPART; ++part) {
+            const float4 v = sPart[part * CG + c / 4];
+            acc += (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
+        }
+        return acc;
+    };
+    col_sums(L::oS, L::odS, DV);   // sum_i S dS' per column
+    __syncthreads();
+    if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 acc = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
@@ -814,11 +833,11 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int m = 0; m < MT; ++m) aq[m] = aw[m] = z4;
         // row blocks of S, then of dS', double-buffered through registers: the next
         // block's loads are in flight while the current block's products run
-        constexpr int NPF = QR * DK / kGT;
-        float pf[NPF];
+        constexpr int NPF = QR * DK / 4 / kGT;
+        float4 pf[NPF];
         auto fetch_rows = [&](int64_t src, int i0) {
 #pragma unroll
-            for (int j = 0; j < NPF; ++j) pf[j] = R[src + i0 * DK + tid + kGT * j];
+            for (int j = 0; j < NPF; ++j) pf[j] = get(R + src + i0 * DK + 4 * (tid + kGT * j));
         };
         fetch_rows(L::oS, 0);
         for (int pass = 0; pass < 2; ++pass) {
@@ -826,8 +845,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < NPF; ++j) {
-                    const int e = tid + kGT * j;
-                    sM2[(e / DK) * (DK + 4) + e % DK] = pf[j];
+                    const int e = 4 * (tid + kGT * j);
+                    put(sM2 + (e / DK) * (DK + 4) + e % DK, pf[j]);
                 }
                 __syncthreads();
                 if (i0 + QR < DV) fetch_rows(pass == 0 ? L::oS : L::odS, i0 + QR);
@@ -862,25 +881,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    {   // sum_r dKbar Kbar per column
-        const int c = tid % DK, part = tid / DK;
-        float acc = 0.f;
-#pragma unroll 16
-        for (int r = part * (kBC / TPC); r < (part + 1) * (kBC / TPC); ++r)
-            acc = fmaf(R[L::odKb + r * DK + c], R[L::oKb + r * DK + c], acc);
-        sPart[tid] = acc;
-    }
+    col_sums(L::odKb, L::oKb, kBC);   // sum_r dKbar Kbar per column
     __syncthreads();
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
-        sCol[DK + tid] = acc;
-    }
+    if (tid < DK) sCol[DK + tid] = col_total(tid);
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
-    DR_TILE_FOR(e, kBC * DK, kGT) {   // dW -> R0, X -> R1
-        const int r = e / DK, c = e % DK;
-        R0[r * LD + c] = R[L::odW + e];
-        R1[r * LD + c] = sBeta[r] * R[L::oKh + e];
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // dW -> R0, X -> R1
+        const int r = 4 * e / DK, c = 4 * e % DK;
+        put(R0 + r * LD + c, get(R + L::odW + 4 * e));
+        const float4 kh = get(R + L::oKh + 4 * e);
+        const float br = sBeta[r];
+        put(R1 + r * LD + c, make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w));
     }
     __syncthreads();
     f32x4 adt[TCC / kGW];
@@ -891,10 +901,11 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                          [&](int c, int j) { return R1[j * LD + c]; });
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DV, kGT) {   // Y -> R1
-        const int r = e / DV, i = e % DV;
-        const float vv = load_elem<E>(p.v, tix(min(r, Cn - 1)) * DV + i);
-        R1[r * LD + i] = r < Cn ? sBeta[r] * vv : 0.f;
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // Y -> R1
+        const int r = 4 * e / DV, i = 4 * e % DV;
+        const float4 vv = load4<E>(p.v, tix(min(r, Cn - 1)) * DV + i);
+        const float br = sBeta[r];
+        put(R1 + r * LD + i, r < Cn ? make_float4(br * vv.x, br * vv.y, br * vv.z, br * vv.w) : z4v);
     }
     __syncthreads();
 #pragma unroll
@@ -909,7 +920,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     // dA = -T^T dT T^T (strictly lower); T -> R1[0 .. C*CP), tmp -> R1[C*CP ..)
     float* sT = R1;
     float* sTmp = R1 + kBC * CP;
-    DR_TILE_FOR(e, kBC * kBC, kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    DR_TILE_FOR(e, kBC * kBC / 4, kGT) put(sT + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::oT + 4 * e));
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
@@ -977,14 +988,14 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     // q, k, G -> R0, R1, R2; dAbar = beta dA
     for (int e = tid; e < kBC * kBC; e += kGT) sM2[(e / kBC) * CP + e % kBC] *= sBeta[e / kBC];
-    DR_TILE_FOR(e, kBC * DK, kGT) {
-        const int r = e / DK, c = e % DK;
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {
+        const int r = 4 * e / DK, c = 4 * e % DK;
         const bool ok = r < Cn;
         const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c;
-        const float qv = load_elem<E>(p.q, qi), kv = load_elem<E>(p.k, qi);
-        R0[r * LD + c] = ok ? qv : 0.f;
-        R1[r * LD + c] = ok ? kv : 0.f;
-        R2[r * LD + c] = R[L::oG + e];
+        const float4 qv = load4<E>(p.q, qi), kv = load4<E>(p.k, qi);
+        put(R0 + r * LD + c, ok ? qv : z4v);
+        put(R1 + r * LD + c, ok ? kv : z4v);
+        put(R2 + r * LD + c, get(R + L::oG + 4 * e));
     }
     __syncthreads();
     // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
