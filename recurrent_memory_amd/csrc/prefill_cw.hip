@@ -158,14 +158,17 @@ __global__ __launch_bounds__(kThreadsCW) void prefill_cw_kernel(FwdArgs p) {
     f32x4 ST[NKT];
     {
         const float* s0 = (p.S0 && chain) ? p.S0 + (static_cast<int64_t>(bh) * DV + vc0 + c) * DK : nullptr;
+        // (the test outside the loop: a load under a branch inside it was waited
+        // for before the next one was issued)
+        if (s0) {
 #pragma unroll
-        for (int t = 0; t < NKT; ++t) {
-            if (s0) {
+            for (int t = 0; t < NKT; ++t) {
                 const float4 v4 = *reinterpret_cast<const float4*>(s0 + 16 * t + 4 * g);
                 ST[t] = f32x4{v4.x, v4.y, v4.z, v4.w};
-            } else {
-                ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) ST[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 
