@@ -1167,29 +1167,34 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     constexpr int LD = (DK > DV ? DK : DV) + 4;
     constexpr int CP = kBC + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
-    __shared__ float sK[kBC * (DK + 4)];
-    __shared__ float sG[kBC * (DK + 4)];
-    __shared__ float sR1[RS];
-    __shared__ float sR2[RS];
-    __shared__ float sM[kBC * CP];
+    __shared__ __attribute__((aligned(16))) float sK[kBC * (DK + 4)];
+    __shared__ __attribute__((aligned(16))) float sG[kBC * (DK + 4)];
+    __shared__ __attribute__((aligned(16))) float sR1[RS];
+    __shared__ __attribute__((aligned(16))) float sR2[RS];
+    __shared__ __attribute__((aligned(16))) float sM[kBC * CP];
     const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
     float* R = ws + static_cast<int64_t>(u) * L::size;
     auto tix = [&](int r) { return tok_index(p, b, t0 + r, h); };
+    const float4 z4v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto put = [](float* dst, float4 x) { *reinterpret_cast<float4*>(dst) = x; };
+    auto get = [](const float* src) { return *reinterpret_cast<const float4*>(src); };
+    auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
 
-    DR_TILE_FOR(e, kBC * DK, kGT) {   // k, b k, g
-        const int r = e / DK, c = e % DK;
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // k, b k, g (four channels per thread)
+        const int r = 4 * e / DK, c = 4 * e % DK;
         const bool ok = r < Cn;
         const int rc = min(r, Cn - 1);
-        const float kv = load_elem<E>(p.k, qk_index(p, b, t0 + rc, h) * DK + c);
-        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c);
-        const float gv = fmaxf(load_elem<E>(p.g, tix(rc) * DK + c), kLogDecayFloor);
-        const float kk = ok ? kv : 0.f;
-        sK[r * (DK + 4) + c] = kk;
-        sR1[r * LD + c] = ok ? bv * kk : 0.f;
-        sG[r * (DK + 4) + c] = ok ? gv : 0.f;
+        const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + rc, h) * DK + c);
+        const float4 bv = load4<E>(p.beta, tix(rc) * DK + c);
+        const float4 g4 = load4<E>(p.g, tix(rc) * DK + c);
+        const float4 gv = make_float4(fmaxf(g4.x, kLogDecayFloor), fmaxf(g4.y, kLogDecayFloor),
+                                      fmaxf(g4.z, kLogDecayFloor), fmaxf(g4.w, kLogDecayFloor));
+        put(sK + r * (DK + 4) + c, ok ? kv : z4v);
+        put(sR1 + r * LD + c, ok ? mul4(bv, kv) : z4v);
+        put(sG + r * (DK + 4) + c, ok ? gv : z4v);
     }
     __syncthreads();
     if (tid < DK) {
@@ -1200,13 +1205,16 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    for (int e = tid; e < kBC * DK; e += kGT) R[L::oG + e] = sG[(e / DK) * (DK + 4) + e % DK];
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) put(R + L::oG + 4 * e, get(sG + (4 * e / DK) * (DK + 4) + 4 * e % DK));
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 4) + tid]);
     // pairwise factors with the reference at the last row of j's 16-row block
     auto aexp = [&](int r, int c, const float* gref) { return __expf(sG[r * (DK + 4) + c] - gref[c]); };
     auto bexp = [&](int j, int c, const float* gref) { return __expf(gref[c] - sG[j * (DK + 4) + c]); };
-    for (int t = w; t < 16; t += kGW) {           // Ae -> sM, Ak -> workspace (strictly lower)
-        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+    static_assert(16 % kGW == 0, "C x C tiles per wave");
+    f32x4 akr[16 / kGW];                          // Ak, kept for Z = Ak X
+#pragma unroll
+    for (int m = 0; m < 16 / kGW; ++m) {          // Ae -> sM, Ak -> workspace (strictly lower)
+        const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         f32x4 ae = z4, ak = z4;
         if (j0 <= r0) {
             const float* gref = sG + (j0 + 15) * (DK + 4);
@@ -1218,22 +1226,26 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) {
             const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
             sM[r * CP + j] = j < r ? ae[q] : 0.f;
-            R[L::oAk + r * kBC + j] = j < r ? ak[q] : 0.f;
+            ak[q] = j < r ? ak[q] : 0.f;
+            R[L::oAk + r * kBC + j] = ak[q];
         }
+        akr[m] = ak;
     }
     __syncthreads();
     float* sT = sR2;
     unit_lower_inverse_blocked(sM, CP, nullptr, sT, CP, sR2 + kBC * CP);   // T = (I + Ae)^-1
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
-    DR_TILE_FOR(e, kBC * DK, kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
-        const int r = e / DK, c = e % DK;
-        const float G = sG[r * (DK + 4) + c];
-        const float eg = __expf(G), eb = __expf(sG[(kBC - 1) * (DK + 4) + c] - G);
-        const float kk = sK[r * (DK + 4) + c];
-        R[L::oEb + e] = sR1[r * LD + c] * eb;
-        R[L::oKb + e] = kk * eb;
-        R[L::oKh + e] = kk * eg;
-        sR1[r * LD + c] = kk * eg;
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
+        const int r = 4 * e / DK, c = 4 * e % DK;
+        const float4 G = get(sG + r * (DK + 4) + c), GC = get(sG + (kBC - 1) * (DK + 4) + c);
+        const float4 eg = make_float4(__expf(G.x), __expf(G.y), __expf(G.z), __expf(G.w));
+        const float4 eb = make_float4(__expf(GC.x - G.x), __expf(GC.y - G.y), __expf(GC.z - G.z), __expf(GC.w - G.w));
+        const float4 kk = get(sK + r * (DK + 4) + c);
+        const float4 kh = mul4(kk, eg);
+        put(R + L::oEb + 4 * e, mul4(get(sR1 + r * LD + c), eb));
+        put(R + L::oKb + 4 * e, mul4(kk, eb));
+        put(R + L::oKh + 4 * e, kh);
+        put(sR1 + r * LD + c, kh);
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T Khat
@@ -1244,40 +1256,57 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DV, kGT) {   // X = w v -> sR1
-        const int r = e / DV, i = e % DV;
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // X = w v -> sR1
+        const int r = 4 * e / DV, i = 4 * e % DV;
         const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
-        const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
-        sR1[r * LD + i] = r < Cn ? x : 0.f;
+        const float4 x = mul4(load4<E>(p.wgate, vi), load4<E>(p.v, vi));
+        put(sR1 + r * LD + i, r < Cn ? x : z4v);
     }
-    DR_TILE_FOR(e, kBC * kBC, kGT) sM[(e / kBC) * CP + e % kBC] = R[L::oAk + e];
-    __syncthreads();
-    for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Z = Ak X
-        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM[r * CP + j]; },
-                                  [&](int j, int i) { return sR1[j * LD + i]; });
 #pragma unroll
-        for (int q = 0; q < 4; ++q) R[L::oZ + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
+    for (int m = 0; m < 16 / kGW; ++m) {   // Ak from registers -> sM (Ae is no longer needed)
+        const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sM[(r0 + 4 * (l >> 4) + q) * CP + j0 + (l & 15)] = akr[m][q];
+    }
+    __syncthreads();
+    constexpr int TZ = (kBC / 16) * (DV / 16) / kGW;   // Z tiles per wave
+    static_assert((kBC / 16) * (DV / 16) % kGW == 0, "Z tiles per wave");
+    f32x4 zr[TZ];
+#pragma unroll
+    for (int m = 0; m < TZ; ++m) {   // Z = Ak X
+        const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        zr[m] = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM[r * CP + j]; },
+                        [&](int j, int i) { return sR1[j * LD + i]; });
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oZ + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = zr[m][q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < TZ; ++m) {   // Z -> sR1 (X is no longer needed)
+        const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sR1[(r0 + 4 * (l >> 4) + q) * LD + c0 + (l & 15)] = zr[m][q];
     }
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Ut = T Z
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
         const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
-                                  [&](int j, int i) { return R[L::oZ + j * DV + i]; });
+                                  [&](int j, int i) { return sR1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DK, kGT) {   // q -> sR1, b k -> sR2, Qhat
-        const int r = e / DK, c = e % DK;
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // q -> sR1, b k -> sR2, Qhat
+        const int r = 4 * e / DK, c = 4 * e % DK;
         const bool ok = r < Cn;
         const int rc = min(r, Cn - 1);
-        const float qv = load_elem<E>(p.q, qk_index(p, b, t0 + rc, h) * DK + c);
-        const float bv = load_elem<E>(p.beta, tix(rc) * DK + c);
-        const float qq = ok ? qv : 0.f;
-        sR1[r * LD + c] = qq;
-        sR2[r * LD + c] = ok ? bv * sK[r * (DK + 4) + c] : 0.f;
-        R[L::oQh + e] = qq * __expf(sG[r * (DK + 4) + c]);
+        const float4 qv = load4<E>(p.q, qk_index(p, b, t0 + rc, h) * DK + c);
+        const float4 bv = load4<E>(p.beta, tix(rc) * DK + c);
+        const float4 qq = ok ? qv : z4v;
+        const float4 G = get(sG + r * (DK + 4) + c);
+        put(sR1 + r * LD + c, qq);
+        put(sR2 + r * LD + c, ok ? mul4(bv, get(sK + r * (DK + 4) + c)) : z4v);
+        put(R + L::oQh + 4 * e, mul4(qq, make_float4(__expf(G.x), __expf(G.y), __expf(G.z), __expf(G.w))));
     }
     __syncthreads();
     for (int t = w; t < 16; t += kGW) {           // Me, Mk (lower, diagonal included)
