@@ -1340,9 +1340,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     constexpr int TCV = (kBC / 16) * (DV / 16);
     constexpr int TCC = (kBC / 16) * (kBC / 16);
     constexpr int MT = TCD / kGW;
-    __shared__ float sM1[kBC * CP];
-    __shared__ float sM2[kBC * CP];
-    __shared__ float sR[3 * RS];
+    __shared__ __attribute__((aligned(16))) float sM1[kBC * CP];
+    __shared__ __attribute__((aligned(16))) float sM2[kBC * CP];
+    __shared__ __attribute__((aligned(16))) float sR[3 * RS];
     __shared__ float sCol[2 * DK];
     __shared__ float sPart[kGT];
     float* R0 = sR;
@@ -1357,6 +1357,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     // gate clamped to the floor has no gradient)
     auto gate_kept = [&](int r, int c) { return load_elem<E>(p.g, tix(r) * DK + c) >= kLogDecayFloor; };
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const float4 z4v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto put = [](float* dst, float4 x) { *reinterpret_cast<float4*>(dst) = x; };
+    auto get = [](const float* src) { return *reinterpret_cast<const float4*>(src); };
     auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
     auto tj = [&](int j0) { return j0 + (l & 15); };
     auto xval = [&](int r, int i) {   // X = w v (zero past the sequence)
@@ -1479,10 +1482,11 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
         sCol[DK + tid] = acc;
     }
-    {   // dW = dY S
-        f32x4 a1[MT];
+    // dW = dY S, kept in registers (the workspace copy is not needed)
+    f32x4 dWr[MT];
+    {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) a1[m] = z4;
+        for (int m = 0; m < MT; ++m) dWr[m] = z4;
         fetch_rows(L::oS, 0);
         for (int i0 = 0; i0 < DV; i0 += QR) {
             __syncthreads();
@@ -1492,44 +1496,86 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
-                                [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
+                dWr[m] = mm_tile(dWr[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                                 [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-#pragma unroll
-            for (int q = 0; q < 4; ++q) R[L::odW + ti(r0, q) * DK + tj(c0)] = a1[m][q];
-        }
     }
+    // Every operand of the products below is staged in LDS (read from the
+    // workspace inside the product loops they cost half the kernel's time):
+    // T and tmp in R1, dW in R2 in place of X (X = w v is staged again from
+    // the inputs for dAk), second operands of dT 64 columns at a time in sM2.
     float* sT = R1;   // Y is no longer needed
     float* sTmp = R1 + kBC * CP;
     __syncthreads();
-    DR_TILE_FOR(e, kBC * kBC, kGT) sT[(e / kBC) * CP + e % kBC] = R[L::oT + e];
+    DR_TILE_FOR(e, kBC * kBC / 4, kGT) put(sT + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::oT + 4 * e));
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {   // dW -> R2
+        const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R2[ti(r0, q) * LD + tj(c0)] = dWr[m][q];
+    }
     __syncthreads();
-    for (int t = w; t < TCV; t += kGW) {          // dZ = T^T dY
+    constexpr int MV = TCV / kGW;   // C x DV tiles per wave
+    static_assert(TCV % kGW == 0 && TCC % kGW == 0, "tiles per wave");
+    for (int t = w; t < TCV; t += kGW) {          // dZ = T^T dY (to the workspace until R0 is free)
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
-                                  [&](int m, int i) { return R0[m * LD + i]; });
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
+                                  [&](int k, int i) { return R0[k * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::odZ + ti(r0, q) * DV + tj(c0)] = acc[q];
     }
     for (int t = w; t < TCD; t += kGW) {          // dKhat = T^T dW
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
-                                  [&](int m, int c) { return R[L::odW + m * DK + c]; });
+        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
+                                  [&](int k, int c) { return R2[k * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::odKh + ti(r0, q) * DK + tj(c0)] = acc[q];
     }
-    for (int t = w; t < TCC; t += kGW) {          // dT = dW Khat^T + dY Z^T
-        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        f32x4 acc = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return R[L::odW + r * DK + c]; },
-                            [&](int c, int j) { return R[L::oKh + j * DK + c]; });
-        acc = mm_tile(acc, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
-                      [&](int i, int j) { return R[L::oZ + j * DV + i]; });
+    // dT = dW Khat^T + dY Z^T
+    f32x4 dTr[TCC / kGW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sM1[ti(r0, q) * CP + tj(j0)] = acc[q];
+    for (int m = 0; m < TCC / kGW; ++m) dTr[m] = z4;
+    for (int h0 = 0; h0 < DK; h0 += 64) {   // Khat[:, h0, h0 + 64) -> sM2
+        DR_TILE_FOR(e, kBC * 64 / 4, kGT) {
+            const int r = 4 * e / 64, c = 4 * e % 64;
+            put(sM2 + r * CP + c, get(R + L::oKh + r * DK + h0 + c));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TCC / kGW; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            dTr[m] = mm_tile(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int c) { return R2[r * LD + c]; },
+                             [&](int c, int j) { return sM2[j * CP + c - h0]; });
+        }
+        __syncthreads();
+    }
+    for (int h0 = 0; h0 < DV; h0 += 64) {   // Z[:, h0, h0 + 64) -> sM2
+        DR_TILE_FOR(e, kBC * 64 / 4, kGT) {
+            const int r = 4 * e / 64, i = 4 * e % 64;
+            put(sM2 + r * CP + i, get(R + L::oZ + r * DV + h0 + i));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TCC / kGW; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            dTr[m] = mm_tile(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int i) { return R0[r * LD + i]; },
+                             [&](int i, int j) { return sM2[j * CP + i - h0]; });
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int m = 0; m < TCC / kGW; ++m) {   // dT -> sM1; dZ -> R0 (dY is no longer needed)
+        const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sM1[ti(r0, q) * CP + tj(j0)] = dTr[m][q];
+    }
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) put(R0 + (4 * e / DV) * LD + 4 * e % DV, get(R + L::odZ + 4 * e));
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // X = w v -> R2 (nor is dW)
+        const int r = 4 * e / DV, i = 4 * e % DV;
+        const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
+        const float4 wv = load4<E>(p.wgate, vi), vv = load4<E>(p.v, vi);
+        put(R2 + r * LD + i, r < Cn ? make_float4(wv.x * vv.x, wv.y * vv.y, wv.z * vv.z, wv.w * vv.w) : z4v);
     }
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {          // tmp = dT T^T
@@ -1544,7 +1590,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 ae = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                  [&](int m, int j) { return sTmp[m * CP + j]; });
-        const f32x4 ak = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R[L::odZ + r * DV + i]; },
+        const f32x4 ak = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                  [&](int i, int j) { return R2[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1554,26 +1600,49 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         }
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DV, kGT) {
-        const float d = load_elem<E>(p.dO, tix(min(e / DV, Cn - 1)) * DV + e % DV);
-        R0[(e / DV) * LD + e % DV] = (e / DV) < Cn ? d : 0.f;
+    // dX = Mk^T dO + Ak^T dZ + Kbar dS'^T -> dv, dw: Mk -> sM1, Ak -> sM2, dO -> R2
+    // (X is no longer needed), Kbar -> R1 (nor are T and tmp); then dS' -> R0, R2
+    DR_TILE_FOR(e, kBC * kBC / 4, kGT) {
+        const int r = 4 * e / kBC, j = 4 * e % kBC;
+        put(sM1 + r * CP + j, get(R + L::oMk + 4 * e));
+        put(sM2 + r * CP + j, get(R + L::oAk + 4 * e));
+    }
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {
+        const int r = 4 * e / DV, i = 4 * e % DV;
+        const float4 d = load4<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
+        put(R2 + r * LD + i, r < Cn ? d : z4v);
+    }
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) put(R1 + (4 * e / DK) * LD + 4 * e % DK, get(R + L::oKb + 4 * e));
+    __syncthreads();
+    f32x4 dXr[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+        const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        dXr[m] = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sM1[k * CP + r]; },
+                         [&](int k, int i) { return R2[k * LD + i]; });
+        dXr[m] = mm_tile(dXr[m], r0, c0, 0, kBC, [&](int r, int k) { return sM2[k * CP + r]; },
+                         [&](int k, int i) { return R0[k * LD + i]; });
     }
     __syncthreads();
-    for (int t = w; t < TCV; t += kGW) {          // dX = Mk^T dO + Kbar dS'^T + Ak^T dZ -> dv, dw
-        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return R[L::oMk + m * kBC + r]; },
-                            [&](int m, int i) { return R0[m * LD + i]; });
-        acc = mm_tile(acc, r0, c0, 0, DK, [&](int r, int c) { return R[L::oKb + r * DK + c]; },
-                      [&](int c, int i) { return R[L::odS + i * DK + c]; });
-        acc = mm_tile(acc, r0, c0, 0, kBC, [&](int r, int m) { return R[L::oAk + m * kBC + r]; },
-                      [&](int m, int i) { return R[L::odZ + m * DV + i]; });
+    static_assert(DV <= 128 && kBC * LD <= RS, "dS' rows in R0 and R2");
+    DR_TILE_FOR(e, DV * DK / 4, kGT) {   // dS' rows [0, 64) -> R0, [64, DV) -> R2
+        const int i = 4 * e / DK, c = 4 * e % DK;
+        put((i < 64 ? R0 + i * LD : R2 + (i - 64) * LD) + c, get(R + L::odS + 4 * e));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+        const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        const float* dsb = c0 < 64 ? R0 : R2 - 64 * LD;   // row i of dS' at dsb + i LD
+        dXr[m] = mm_tile(dXr[m], r0, c0, 0, DK, [&](int r, int c) { return R1[r * LD + c]; },
+                         [&](int c, int i) { return dsb[i * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = ti(r0, q), i = tj(c0);
             if (r < Cn) {
                 const int64_t vi = tix(r) * DV + i;
-                store_elem<E>(p.gv, vi, load_elem<E>(p.wgate, vi) * acc[q]);
-                store_elem<E>(p.gw, vi, load_elem<E>(p.v, vi) * acc[q]);
+                store_elem<E>(p.gv, vi, load_elem<E>(p.wgate, vi) * dXr[m][q]);
+                store_elem<E>(p.gw, vi, load_elem<E>(p.v, vi) * dXr[m][q]);
             }
         }
     }
