@@ -1335,7 +1335,6 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     constexpr int LD = (DK > DV ? DK : DV) + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;
     constexpr int QR = 32;
-    constexpr int TPC = kGT / DK;
     constexpr int TCD = (kBC / 16) * (DK / 16);
     constexpr int TCV = (kBC / 16) * (DV / 16);
     constexpr int TCC = (kBC / 16) * (kBC / 16);
@@ -1344,7 +1343,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __shared__ __attribute__((aligned(16))) float sM2[kBC * CP];
     __shared__ __attribute__((aligned(16))) float sR[3 * RS];
     __shared__ float sCol[2 * DK];
-    __shared__ float sPart[kGT];
+    __shared__ float4 sPart[kGT];     // per-thread partial sums of four columns
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
@@ -1362,49 +1361,56 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     auto get = [](const float* src) { return *reinterpret_cast<const float4*>(src); };
     auto ti = [&](int i0, int q) { return i0 + 4 * (l >> 4) + q; };
     auto tj = [&](int j0) { return j0 + (l & 15); };
-    auto xval = [&](int r, int i) {   // X = w v (zero past the sequence)
-        const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
-        const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
-        return r < Cn ? x : 0.f;
-    };
     // stage rows [i0, i0 + QR) of a [DV][DK] workspace matrix into sM2
     // row blocks of a [DV][DK] workspace matrix, double-buffered through registers:
     // fetch_rows issues the loads, put_rows writes them to sM2 (after a barrier)
-    constexpr int NPF = QR * DK / kGT;
-    float pf[NPF];
+    constexpr int NPF = QR * DK / 4 / kGT;
+    float4 pf[NPF];
     auto fetch_rows = [&](int64_t src, int i0) {
 #pragma unroll
-        for (int j = 0; j < NPF; ++j) pf[j] = R[src + i0 * DK + tid + kGT * j];
+        for (int j = 0; j < NPF; ++j) pf[j] = get(R + src + i0 * DK + 4 * (tid + kGT * j));
     };
     auto put_rows = [&]() {
 #pragma unroll
         for (int j = 0; j < NPF; ++j) {
-            const int e = tid + kGT * j;
-            sM2[(e / DK) * (DK + 4) + e % DK] = pf[j];
+            const int e = 4 * (tid + kGT * j);
+            put(sM2 + (e / DK) * (DK + 4) + e % DK, pf[j]);
         }
     };
+    // column sums: thread (part, four columns); the parts combined in a fixed order
+    auto fma4 = [](float4 x, float4 y, float4 c) {
+        return make_float4(fmaf(x.x, y.x, c.x), fmaf(x.y, y.y, c.y), fmaf(x.z, y.z, c.z), fmaf(x.w, y.w, c.w));
+    };
+    constexpr int CG = DK / 4, NPART = kGT / CG;
+    auto col_total = [&](int c) {
+        float acc = 0.f;
+        for (int part = 0; part < NPART; ++part) {
+            const float4 v = sPart[part * CG + c / 4];
+            acc += (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
+        }
+        return acc;
+    };
 
-    DR_TILE_FOR(e, kBC * DV, kGT) {   // dO -> R0, Y -> R1, X -> R2
-        const int r = e / DV, i = e % DV;
-        const float d = load_elem<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
-        R0[r * LD + i] = r < Cn ? d : 0.f;
-        R1[r * LD + i] = R[L::oVt + e];
-        R2[r * LD + i] = xval(r, i);
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // dO -> R0, Y -> R1, X -> R2 (four columns per thread)
+        const int r = 4 * e / DV, i = 4 * e % DV;
+        const int64_t vi = tix(min(r, Cn - 1)) * DV + i;
+        const float4 d = load4<E>(p.dO, vi), wv = load4<E>(p.wgate, vi), vv = load4<E>(p.v, vi);
+        put(R0 + r * LD + i, r < Cn ? d : z4v);
+        put(R1 + r * LD + i, get(R + L::oVt + 4 * e));
+        put(R2 + r * LD + i, r < Cn ? make_float4(wv.x * vv.x, wv.y * vv.y, wv.z * vv.z, wv.w * vv.w) : z4v);
     }
     {   // sum_i S dS' per column
-        const int c = tid % DK, part = tid / DK;
-        float acc = 0.f;
-#pragma unroll 16
-        for (int i = part * (DV / TPC); i < (part + 1) * (DV / TPC); ++i)
-            acc = fmaf(R[L::oS + i * DK + c], R[L::odS + i * DK + c], acc);
+        const int c = 4 * (tid % CG), part = tid / CG, rp = DV / NPART;
+        float4 acc = z4v;
+#pragma unroll
+        for (int k = 0; k < rp; ++k) {
+            const int i = part * rp + k;
+            acc = fma4(get(R + L::oS + i * DK + c), get(R + L::odS + i * DK + c), acc);
+        }
         sPart[tid] = acc;
     }
     __syncthreads();
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
-        sCol[tid] = R[L::oGam + tid] * acc;
-    }
+    if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {          // dMe = -Tril0(dO Y^T), dMk = Tril0(dO X^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         const f32x4 me = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
@@ -1467,21 +1473,19 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     }
     __syncthreads();
     {   // sum_r (dKbar Kbar + dEbar Ebar) per column
-        const int c = tid % DK, part = tid / DK;
-        float acc = 0.f;
-        for (int r = part * (kBC / TPC); r < (part + 1) * (kBC / TPC); ++r) {
-            acc = fmaf(R[L::odKb + r * DK + c], R[L::oKb + r * DK + c], acc);
-            acc = fmaf(R[L::odEb + r * DK + c], R[L::oEb + r * DK + c], acc);
+        const int c = 4 * (tid % CG), part = tid / CG, rp = kBC / NPART;
+        float4 acc = z4v;
+#pragma unroll
+        for (int k = 0; k < rp; ++k) {
+            const int r = part * rp + k;
+            acc = fma4(get(R + L::odKb + r * DK + c), get(R + L::oKb + r * DK + c), acc);
+            acc = fma4(get(R + L::odEb + r * DK + c), get(R + L::oEb + r * DK + c), acc);
         }
         sPart[tid] = acc;
     }
-    DR_TILE_FOR(e, kBC * DV, kGT) R0[(e / DV) * LD + e % DV] = R[L::odVt + e];   // dY -> R0
+    DR_TILE_FOR(e, kBC * DV / 4, kGT) put(R0 + (4 * e / DV) * LD + 4 * e % DV, get(R + L::odVt + 4 * e));   // dY -> R0
     __syncthreads();
-    if (tid < DK) {
-        float acc = 0.f;
-        for (int part = 0; part < TPC; ++part) acc += sPart[part * DK + tid];
-        sCol[DK + tid] = acc;
-    }
+    if (tid < DK) sCol[DK + tid] = col_total(tid);
     // dW = dY S, kept in registers (the workspace copy is not needed)
     f32x4 dWr[MT];
     {
@@ -1653,15 +1657,18 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MT; ++m) aq[m] = ak[m] = abk[m] = ag[m] = z4;
     auto stage = [&](float* dst, int what) {   // 0 q, 1 k, 2 b k, 3 G
         if (what == 3) {
-            DR_TILE_FOR(e, kBC * DK, kGT) dst[(e / DK) * LD + e % DK] = R[L::oG + e];
+            DR_TILE_FOR(e, kBC * DK / 4, kGT) put(dst + (4 * e / DK) * LD + 4 * e % DK, get(R + L::oG + 4 * e));
         } else {
             const void* src = what == 0 ? p.q : p.k;
-            DR_TILE_FOR(e, kBC * DK, kGT) {
-                const int r = e / DK, c = e % DK;
+            DR_TILE_FOR(e, kBC * DK / 4, kGT) {
+                const int r = 4 * e / DK, c = 4 * e % DK;
                 const int rc = min(r, Cn - 1);
-                float x = load_elem<E>(src, qk_index(p, b, t0 + rc, h) * DK + c);
-                if (what == 2) x *= load_elem<E>(p.beta, tix(rc) * DK + c);
-                dst[r * LD + c] = r < Cn ? x : 0.f;
+                float4 x = load4<E>(src, qk_index(p, b, t0 + rc, h) * DK + c);
+                if (what == 2) {
+                    const float4 bv = load4<E>(p.beta, tix(rc) * DK + c);
+                    x = make_float4(x.x * bv.x, x.y * bv.y, x.z * bv.z, x.w * bv.w);
+                }
+                put(dst + r * LD + c, r < Cn ? x : z4v);
             }
         }
     };
@@ -1676,9 +1683,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
         c0 = 16 * (t % (DK / 16));
     };
     // pass 1: Me (q, b k) and Mk (q, k) with G; q -> R0, b k -> R1, G -> R2
-    DR_TILE_FOR(e, kBC * kBC, kGT) {
-        sM1[(e / kBC) * CP + e % kBC] = R[L::odMe + e];
-        sM2[(e / kBC) * CP + e % kBC] = R[L::odMk + e];
+    DR_TILE_FOR(e, kBC * kBC / 4, kGT) {
+        put(sM1 + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::odMe + 4 * e));
+        put(sM2 + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::odMk + 4 * e));
     }
     stage(R0, 0);
     stage(R2, 3);
@@ -1717,9 +1724,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     }
     __syncthreads();
     // pass 2: Ae (k, b k) and Ak (k, k); b k -> R0
-    DR_TILE_FOR(e, kBC * kBC, kGT) {
-        sM1[(e / kBC) * CP + e % kBC] = R[L::odAe + e];
-        sM2[(e / kBC) * CP + e % kBC] = R[L::odAk + e];
+    DR_TILE_FOR(e, kBC * kBC / 4, kGT) {
+        put(sM1 + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::odAe + 4 * e));
+        put(sM2 + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::odAk + 4 * e));
     }
     stage(R0, 2);
     __syncthreads();
