@@ -1027,9 +1027,18 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             store_qk_grad<E>(p.gq, p.gq32, tix(r), DK, c, fmaf(dQh, eg, a1));
             store_qk_grad<E>(p.gk, p.gk32, tix(r), DK, c, a2 + a3 + a4 + dKh * eg + dKb * ebar);
         }
-        R[L::odQh + e] = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg
-                         - dKb * kr * ebar;
+        float dG = qr * a1 - kr * a2 + kr * a3 - kr * a4 + dKh * kr * eg + dQh * qr * eg - dKb * kr * ebar;
+        if constexpr (VAR != 1) R[L::odQh + e] = dG;
+        // scalar decay: the G_C terms of channel c join its last row before the
+        // sum over channels (they largely cancel against it)
+        if constexpr (VAR == 1) dG += r == Cn - 1 ? sCol[c] + sCol[DK + c] : 0.f;
+        return dG;
     };
+    // scalar decay: the gate's gradient needs only the channel sums of dG per
+    // row; per 16-column tile they are reduced over its 16 lanes and kept in
+    // sRow[column tile][row] (sPart is free by now)
+    float* sRow = reinterpret_cast<float*>(sPart);
+    static_assert((DK / 16) * kBC <= 4 * kGT, "row sums fit sPart");
     if constexpr (VAR == 4) {
         // FG^2-GDN: the key is k on the row side (Khat, the rows of Abar) and
         // e = beta ⊙ k on the column side (the columns of Abar and Mq, Kbar).
@@ -1125,11 +1134,33 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             const f32x4 a4 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
+            for (int q = 0; q < 4; ++q) {
+                float x = finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
+                if constexpr (VAR == 1) {
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+                    if ((l & 15) == 0) sRow[(c0 / 16) * kBC + ti(r0, q)] = x;
+                }
+            }
         }
     }
-    if constexpr (VAR != 0) {
+    if constexpr (VAR == 1) {
+        // dg_r = sum_{r' >= r} sum_c dG[r', c] (the G_C terms are in the last row):
+        // the channel sums of the rows, then a reverse scan over the rows on wave 0
+        __syncthreads();
+        if (w == 0) {
+            float rs = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < DK / 16; ++cb) rs += sRow[cb * kBC + l];
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1) {
+                const float t = __shfl_down(rs, m);
+                if (l + m < 64) rs += t;
+            }
+            if (l < Cn) store_elem<E>(p.gg, tix(l), rs);
+        }
+    }
+    if constexpr (VAR >= 2) {
         __syncthreads();
         if (tid < DK) {   // reverse cumulative sum over rows; G_C's terms enter at the last row
             const int c = tid;
@@ -1140,22 +1171,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
             for (int r = kBC - 1; r >= 0; --r) {
                 acc += dgv[r];
-                if constexpr (VAR >= 2) {
-                    // a gate clamped at the floor has no gradient
-                    if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, gate_kept(r, c) ? acc : 0.f);
-                } else {
-                    R[L::odQh + r * DK + c] = acc;
-                }
+                // a gate clamped at the floor has no gradient
+                if (r < Cn) store_elem<E>(p.gg, tix(r) * DK + c, gate_kept(r, c) ? acc : 0.f);
             }
-        }
-        if constexpr (VAR == 1) {   // scalar decay: sum over channels, 4 threads per row
-            __syncthreads();
-            const int r = tid / kRT, qt = tid % kRT;
-            float s = 0.f;
-            for (int c = qt * (DK / kRT); c < (qt + 1) * (DK / kRT); ++c) s += R[L::odQh + r * DK + c];
-#pragma unroll
-            for (int m = 1; m < kRT; m <<= 1) s += __shfl_xor(s, m);
-            if (qt == 0 && r < Cn) store_elem<E>(p.gg, tix(r), s);
         }
     }
 }
