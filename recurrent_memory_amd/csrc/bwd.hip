@@ -488,8 +488,16 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     float4 pW[NP], pK[NP], pE[SPLIT ? NP : 1];
     float pU[MT][4];
     float pG = 0.f;
+    float4 pXw = make_float4(0.f, 0.f, 0.f, 0.f), pXv = pXw;   // split gates: w and v of X = w v
+    static_assert(kBC * kBVT == 4 * kCT, "X: four columns per thread");
     auto fetch = [&](int n) {
         const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        if constexpr (SPLIT) {   // this tile's value columns, rows past the end from the last row
+            const int t0 = n * kBC, Cn = min(kBC, p.T - t0), r = 4 * tid / kBVT, i = 4 * tid % kBVT;
+            const int64_t vi = tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i;
+            pXw = load4<E>(p.wgate, vi);
+            pXv = load4<E>(p.v, vi);
+        }
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kCT * j);
@@ -524,14 +532,11 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) uu[m][q] = pU[m][q];
         sGam[min(tid, DK - 1)] = pG;   // lanes past DK rewrite the last entry with its own value
-        if constexpr (SPLIT) {   // X = w v for this tile's value columns
-            const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
-            DR_TILE_FOR(e, kBC * kBVT, kCT) {
-                const int r = e / kBVT, i = e % kBVT;
-                const int64_t vi = tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i;
-                const float x = load_elem<E>(p.wgate, vi) * load_elem<E>(p.v, vi);
-                sXt[r * SV + i] = r < Cn ? x : 0.f;
-            }
+        if constexpr (SPLIT) {   // X = w v for this tile's value columns (fetched a step ahead)
+            const int Cn = min(kBC, p.T - n * kBC), r = 4 * tid / kBVT, i = 4 * tid % kBVT;
+            *reinterpret_cast<float4*>(sXt + r * SV + i) =
+                r < Cn ? make_float4(pXw.x * pXv.x, pXw.y * pXv.y, pXw.z * pXv.z, pXw.w * pXv.w)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         lds_only_barrier();
         if (n + 1 < N) fetch(n + 1);
