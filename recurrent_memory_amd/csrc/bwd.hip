@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -42,48 +43,137 @@ constexpr int kRT = kGT / 64;   // its threads per row for row sums
 // One 16 x 16 output tile of an fp32 product on the matrix cores:
 // acc += A[i0, i0 + 16) x [k0, k1)  *  B[k0, k1) x [j0, j0 + 16), k1 - k0 a multiple
 // of 4; A(i, k) and B(k, j) read the operands in whatever layout they have.
-// v_mfma_f32_16x16x4f32: lane l supplies A(i0 + l % 16, k + l / 16) and
-// B(k + l / 16, j0 + l % 16); element q of the result is row i0 + 4 (l / 16) + q,
-// column j0 + l % 16.
-template <class FA, class FB>
+// Element q of the result in lane l is row i0 + 4 (l / 16) + q, column j0 + l % 16.
+//
+// SM (bf16 inputs): each fp32 operand is split into two bf16 values, x = hi + lo + e
+// with hi and lo rounded to nearest even in turn, so |e| <= 2^-18 |x|, and the
+// product is taken as hi*hi + hi*lo + lo*hi on the bf16 matrix cores with fp32
+// accumulation.  The dropped lo*lo term and the split errors leave a relative
+// error of about 2^-17 per product term; a 32-deep k step takes 3 instructions of
+// the bf16 kind instead of 8 fp32 ones, each doing a quarter of the work per cycle.
+// Otherwise (fp32 inputs) the products run on the fp32 matrix instruction.
+// Operand layouts (g = l / 16, c = l % 16):
+//   v_mfma_f32_16x16x32_bf16: lane l supplies A(i0 + c, k + 8 g + e) and
+//     B(k + 8 g + e, j0 + c), e = 0..7;
+//   v_mfma_f32_16x16x16_bf16: the same with 4 g + e, e = 0..3;
+//   v_mfma_f32_16x16x4f32: A(i0 + c, k + g) and B(k + g, j0 + c).
+template <typename E>
+constexpr bool kSplitMM = std::is_same<E, BF16>::value;
+
+__device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+    hi = static_cast<bf16_t>(x);
+    lo = static_cast<bf16_t>(x - static_cast<float>(hi));
+}
+__device__ __forceinline__ f32x4 mfma_split8(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                             const bf16x8& bl, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_split4(const bf16x4& ah, const bf16x4& al, const bf16x4& bh,
+                                             const bf16x4& bl, f32x4 acc) {
+    auto s = [](const bf16x4& v) { return __builtin_bit_cast(s16x4, v); };
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(al), s(bh), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bl), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bh), acc, 0, 0, 0);
+}
+// operand pieces of lane (g, c) for a k step of 8 N: A(ai, k + N g + e) and B(k + N g + e, bj)
+template <int N, class V, class FA, class FB>
+__device__ __forceinline__ void split_operands(V& ah, V& al, V& bh, V& bl, int ai, int bj, int k, int g,
+                                               const FA& A, const FB& B) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        bf16_t h, lo;
+        split_bf16(A(ai, k + N * g + e), h, lo);
+        ah[e] = h;
+        al[e] = lo;
+        split_bf16(B(k + N * g + e, bj), h, lo);
+        bh[e] = h;
+        bl[e] = lo;
+    }
+}
+
+template <bool SM, class FA, class FB>
 __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int k1, const FA& A,
                                          const FB& B) {
     const int l = threadIdx.x & 63;
-    const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
+    const int ai = i0 + (l & 15), bj = j0 + (l & 15), g = l >> 4;
+    int k = k0;
+    if constexpr (SM) {
+#pragma unroll 4
+        for (; k + 32 <= k1; k += 32) {
+            bf16x8 ah, al, bh, bl;
+            split_operands<8>(ah, al, bh, bl, ai, bj, k, g, A, B);
+            acc = mfma_split8(ah, al, bh, bl, acc);
+        }
+        if (k + 16 <= k1) {
+            bf16x4 ah, al, bh, bl;
+            split_operands<4>(ah, al, bh, bl, ai, bj, k, g, A, B);
+            acc = mfma_split4(ah, al, bh, bl, acc);
+            k += 16;
+        }
+    }
 #pragma unroll 16
-    for (int k = k0; k < k1; k += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
+    for (; k < k1; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + g), B(k + g, bj), acc, 0, 0, 0);
     return acc;
 }
 
 // mm_tile with the k range split into two interleaved accumulation chains
-// (k1 - k0 a multiple of 8), which the matrix core runs back to back.
-template <class FA, class FB>
+// (k1 - k0 a multiple of 8), which the matrix core runs back to back (fp32); the
+// split form is short enough as one chain.
+template <bool SM, class FA, class FB>
 __device__ __forceinline__ f32x4 mm_tile_k2(f32x4 acc, int i0, int j0, int k0, int k1, const FA& A,
                                             const FB& B) {
-    const int l = threadIdx.x & 63;
-    const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
-    f32x4 other = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SM) {
+        return mm_tile<SM>(acc, i0, j0, k0, k1, A, B);
+    } else {
+        const int l = threadIdx.x & 63;
+        const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
+        f32x4 other = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int k = k0; k < k1; k += 8) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
-        other = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + 4 + kk), B(k + 4 + kk, bj), other, 0, 0, 0);
+        for (int k = k0; k < k1; k += 8) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
+            other = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + 4 + kk), B(k + 4 + kk, bj), other, 0, 0, 0);
+        }
+        return acc + other;
     }
-    return acc + other;
 }
 
-// Two tiles with the same rows i0 and columns j0, j1: one A read feeds both
-// accumulation chains.
-template <class FA, class FB>
+// Two tiles with the same rows i0 and columns j0, j1: one A read (and split) feeds
+// both accumulation chains.
+template <bool SM, class FA, class FB>
 __device__ __forceinline__ void mm_tile2(f32x4& acc0, f32x4& acc1, int i0, int j0, int j1, int k0, int k1,
                                          const FA& A, const FB& B) {
     const int l = threadIdx.x & 63;
-    const int ai = i0 + (l & 15), b0 = j0 + (l & 15), b1 = j1 + (l & 15), kk = l >> 4;
+    const int ai = i0 + (l & 15), b0 = j0 + (l & 15), b1 = j1 + (l & 15), g = l >> 4;
+    int k = k0;
+    if constexpr (SM) {
+#pragma unroll 4
+        for (; k + 32 <= k1; k += 32) {
+            bf16x8 ah, al, bh0, bl0, bh1, bl1;
+            split_operands<8>(ah, al, bh0, bl0, ai, b0, k, g, A, B);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16_t h, lo;
+                split_bf16(B(k + 8 * g + e, b1), h, lo);
+                bh1[e] = h;
+                bl1[e] = lo;
+            }
+            acc0 = mfma_split8(ah, al, bh0, bl0, acc0);
+            acc1 = mfma_split8(ah, al, bh1, bl1, acc1);
+        }
+        if (k < k1) {
+            acc0 = mm_tile<SM>(acc0, i0, j0, k, k1, A, B);
+            acc1 = mm_tile<SM>(acc1, i0, j1, k, k1, A, B);
+        }
+    } else {
 #pragma unroll 16
-    for (int k = k0; k < k1; k += 4) {
-        const float a = A(ai, k + kk);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + kk, b0), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + kk, b1), acc1, 0, 0, 0);
+        for (; k < k1; k += 4) {
+            const float a = A(ai, k + g);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b0), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b1), acc1, 0, 0, 0);
+        }
     }
 }
 
@@ -96,14 +186,14 @@ __device__ __forceinline__ void mm_tile2(f32x4& acc0, f32x4& acc1, int i0, int j
 // row for ROW and the first for !ROW, so that the factor inside the product is
 // at most 1 and the one applied afterwards exceeds 1 only within block J (at most
 // e^{85} under the decay bound).
-template <bool ROW, class FM, class FX, class FG>
+template <bool ROW, bool SM, class FM, class FX, class FG>
 __device__ __forceinline__ f32x4 pair_tile(int r0, int c0, const FM& M, const FX& X, const FG& G) {
     const int l = threadIdx.x & 63;
     const int I = r0 / 16;
     f32x4 out = {0.f, 0.f, 0.f, 0.f};
     for (int J = ROW ? 0 : I; ROW ? (J <= I) : (J < kBC / 16); ++J) {
         const int ref = ROW ? 16 * J + 15 : 16 * J;
-        const f32x4 acc = mm_tile(
+        const f32x4 acc = mm_tile<SM>(
             f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 16 * J, 16 * J + 16,
             [&](int r, int j) { return ROW ? M(r, j) : M(j, r); },
             [&](int j, int c) { return X(j, c) * __expf(ROW ? G(ref, c) - G(j, c) : G(j, c) - G(ref, c)); });
@@ -144,6 +234,7 @@ __device__ __forceinline__ void lds_only_barrier() {
 //      per wave, 3 waves).
 // (Substituting whole 64-row columns, one lane per column, kept seven of the
 // eight waves idle for the length of the substitution.)
+template <bool SM>
 __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int lda, const float* rs, float* T,
                                                            int ldt, float* Z) {
     static_assert(kBC == 64, "four 16-row blocks");
@@ -174,13 +265,13 @@ __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int l
         const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
         for (int i0 = j0 + 16; i0 < kBC; i0 += 16) {
             // Z = sum_{j <= k < i} L_ik T_kj: rows of L left of the diagonal block are rs A
-            const f32x4 zz = mm_tile(z4, i0, j0, j0, i0,
+            const f32x4 zz = mm_tile<SM>(z4, i0, j0, j0, i0,
                                      [&](int r, int k) { return rs ? rs[r] * A[r * lda + k] : A[r * lda + k]; },
                                      [&](int k, int c) { return T[k * ldt + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) z[(4 * (l >> 4) + q) * 20 + (l & 15)] = zz[q];
             // T_ij = -T_ii Z (the wave's own LDS writes are seen by its later reads)
-            const f32x4 tt = mm_tile(z4, 0, 0, 0, 16, [&](int r, int k) { return T[(i0 + r) * ldt + i0 + k]; },
+            const f32x4 tt = mm_tile<SM>(z4, 0, 0, 0, 16, [&](int r, int k) { return T[(i0 + r) * ldt + i0 + k]; },
                                      [&](int k, int c) { return z[k * 20 + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) T[(i0 + 4 * (l >> 4) + q) * ldt + j0 + (l & 15)] = -tt[q];
@@ -352,9 +443,9 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
                     if constexpr (VAR == 4) x *= load_elem<E>(p.beta, tok_index(p, b, t0 + min(j, Cn - 1), h) * DK + c);
                     return x;
                 };
-                ab = mm_tile(z4, r0, j0, 0, DK,
+                ab = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK,
                              [&](int r, int c) { return sK[r * (DK + 4) + c] * __expf(sG[r * (DK + 4) + c] - gref[c]); }, Bk);
-                mq = mm_tile(z4, r0, j0, 0, DK,
+                mq = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK,
                              [&](int r, int c) { return sX[r * LD + c] * __expf(sG[r * (DK + 4) + c] - gref[c]); }, Bk);
             }
 #pragma unroll
@@ -369,9 +460,9 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
         for (int t = w; t < 16; t += kGW) {
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-            const f32x4 ab = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 4) + c]; },
+            const f32x4 ab = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 4) + c]; },
                                      [&](int c, int j) { return sK[j * (DK + 4) + c]; });
-            const f32x4 mq = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return sX[r * LD + c]; },
+            const f32x4 mq = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return sX[r * LD + c]; },
                                      [&](int c, int j) { return sK[j * (DK + 4) + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -386,7 +477,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     }
     __syncthreads();
     // T = (I + diag(beta) Abar)^-1 by forward substitution, one column per thread
-    unit_lower_inverse_blocked(sA, kBC + 4, sBeta, sT, kBC + 4, sZ);
+    unit_lower_inverse_blocked<kSplitMM<E>>(sA, kBC + 4, sBeta, sT, kBC + 4, sZ);
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * (kBC + 4) + e % kBC];
     // key and query factors; sX becomes X = beta Khat
     DR_TILE_FOR(e, kBC * DK / 4, kGT) {
@@ -412,7 +503,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T X
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
                                   [&](int j, int c) { return sX[j * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
@@ -427,7 +518,7 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // U = T Y
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * (kBC + 4) + j]; },
                                   [&](int j, int i) { return sX[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
@@ -548,7 +639,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int m = 0; m < MT; ++m) {   // Vt = U - W S^T  /  Y = Ut + W S^T
             const int t = w + kCW * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            const f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
+            const f32x4 acc = mm_tile_k2<kSplitMM<E>>(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
                                          [&](int r, int c) { return sW[r * SW + c]; },
                                          [&](int c, int i) { return sS[i * SS + c]; });
 #pragma unroll
@@ -576,17 +667,17 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
             auto eb = [&](int r, int c) { return sEb[r * SK + c]; };
             if constexpr (NTS == 2 * kCW) {
                 if constexpr (SPLIT) {
-                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, nvt, eb);
-                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, xt, kb);
+                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, nvt, eb);
+                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, xt, kb);
                 } else {
-                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, vt, kb);
+                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, vt, kb);
                 }
             } else {
                 if constexpr (SPLIT) {
-                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, nvt, eb);
-                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, xt, kb);
+                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, nvt, eb);
+                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, xt, kb);
                 } else {
-                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, vt, kb);
+                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, vt, kb);
                 }
             }
 #pragma unroll
@@ -691,10 +782,10 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         const int w = tid >> 6, l = tid & 63;
         for (int t = w; t < (kBC / 16) * (kBVT / 16); t += kCW) {   // dVt = Mq^T dO + Kbar dS^T
             const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
+            f32x4 acc = mm_tile_k2<kSplitMM<E>>(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
                                    [&](int r, int m) { return sM[m * SMQ + r]; },
                                    [&](int m, int i) { return sdO[m * SO + i]; });
-            acc = mm_tile_k2(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
+            acc = mm_tile_k2<kSplitMM<E>>(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
                              [&](int c, int i) { return sdS[i * SD + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -717,11 +808,11 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             auto wm = [&](int r, int c) { return sA2[r * SB + c]; };
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
             if constexpr (NTS == 2 * kCW) {
-                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dot, qh);
-                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dvt, wm);
+                mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, dot, qh);
+                mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, dvt, wm);
             } else {
-                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dot, qh);
-                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dvt, wm);
+                acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, dot, qh);
+                acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, dvt, wm);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -823,7 +914,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                   [&](int i, int j) { return R1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -861,10 +952,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                     const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                     auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; };
                     if (pass == 0) {
-                        aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
-                        aw[m] = mm_tile(aw[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R2[r * LD + i]; }, Bs);
+                        aq[m] = mm_tile<kSplitMM<E>>(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
+                        aw[m] = mm_tile<kSplitMM<E>>(aw[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R2[r * LD + i]; }, Bs);
                     } else {
-                        aq[m] = mm_tile(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R1[r * LD + i]; }, Bs);
+                        aq[m] = mm_tile<kSplitMM<E>>(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R1[r * LD + i]; }, Bs);
                     }
                 }
             }
@@ -902,7 +993,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
     for (int m = 0; m < TCC / kGW; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        adt[m] = mm_tile(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
+        adt[m] = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
                          [&](int c, int j) { return R1[j * LD + c]; });
     }
     __syncthreads();
@@ -916,7 +1007,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
     for (int m = 0; m < TCC / kGW; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        adt[m] = mm_tile(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
+        adt[m] = mm_tile<kSplitMM<E>>(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
                          [&](int i, int j) { return R1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) sM2[ti(r0, q) * CP + tj(j0)] = adt[m][q];
@@ -929,7 +1020,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
                                   [&](int m, int j) { return sT[j * CP + m]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
@@ -937,7 +1028,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {            // dA = -T^T tmp, masked
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int j) { return sTmp[m * CP + j]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -947,7 +1038,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     }
     for (int t = w; t < TCD; t += kGW) {            // dX = T^T dW (dKhat = beta dX)
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int c) { return R0[m * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
@@ -955,7 +1046,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int t = w; t < TCV; t += kGW) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                   [&](int m, int i) { return R2[m * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1061,7 +1152,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
         for (int m = 0; m < MTG; ++m) {
             const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-            colg[m] = pair_tile<false>(r0, c0, M1, Qf, Gf) + pair_tile<false>(r0, c0, M2, Kf, Gf);
+            colg[m] = pair_tile<false, kSplitMM<E>>(r0, c0, M1, Qf, Gf) + pair_tile<false, kSplitMM<E>>(r0, c0, M2, Kf, Gf);
         }
         __syncthreads();
         DR_TILE_FOR(e, kBC * DK, kGT) {
@@ -1074,8 +1165,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int m = 0; m < MTG; ++m) {
             const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
             const Pre pr = preload(r0, c0);
-            const f32x4 a1 = pair_tile<true>(r0, c0, M1, Kf, Gf);
-            const f32x4 a3 = pair_tile<true>(r0, c0, M2, Kf, Gf);
+            const f32x4 a1 = pair_tile<true, kSplitMM<E>>(r0, c0, M1, Kf, Gf);
+            const f32x4 a3 = pair_tile<true, kSplitMM<E>>(r0, c0, M2, Kf, Gf);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = ti(r0, q), c = tj(c0);
@@ -1105,10 +1196,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
             const Pre pr = preload(r0, c0);
-            const f32x4 a1 = pair_tile<true>(r0, c0, M1, Kf, Gf);
-            const f32x4 a2 = pair_tile<false>(r0, c0, M1, Qf, Gf);
-            const f32x4 a3 = pair_tile<true>(r0, c0, M2, Kf, Gf);
-            const f32x4 a4 = pair_tile<false>(r0, c0, M2, Kf, Gf);
+            const f32x4 a1 = pair_tile<true, kSplitMM<E>>(r0, c0, M1, Kf, Gf);
+            const f32x4 a2 = pair_tile<false, kSplitMM<E>>(r0, c0, M1, Qf, Gf);
+            const f32x4 a3 = pair_tile<true, kSplitMM<E>>(r0, c0, M2, Kf, Gf);
+            const f32x4 a4 = pair_tile<false, kSplitMM<E>>(r0, c0, M2, Kf, Gf);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
@@ -1130,13 +1221,13 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
             const Pre pr = preload(r0, c0);
-            const f32x4 a1 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
+            const f32x4 a1 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
-            const f32x4 a2 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[j * CP + r]; },
+            const f32x4 a2 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[j * CP + r]; },
                                      [&](int j, int c) { return R0[j * LD + c]; });
-            const f32x4 a3 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[r * CP + j]; },
+            const f32x4 a3 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[r * CP + j]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
-            const f32x4 a4 = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
+            const f32x4 a4 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
                                      [&](int j, int c) { return R1[j * LD + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1242,8 +1333,8 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         if (j0 <= r0) {
             const float* gref = sG + (j0 + 15) * (DK + 4);
             auto Ak_ = [&](int r, int c) { return sK[r * (DK + 4) + c] * aexp(r, c, gref); };
-            ae = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sR1[j * LD + c] * bexp(j, c, gref); });
-            ak = mm_tile(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
+            ae = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sR1[j * LD + c] * bexp(j, c, gref); });
+            ak = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, Ak_, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1256,7 +1347,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     }
     __syncthreads();
     float* sT = sR2;
-    unit_lower_inverse_blocked(sM, CP, nullptr, sT, CP, sR2 + kBC * CP);   // T = (I + Ae)^-1
+    unit_lower_inverse_blocked<kSplitMM<E>>(sM, CP, nullptr, sT, CP, sR2 + kBC * CP);   // T = (I + Ae)^-1
     for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * CP + e % kBC];
     DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // Ebar, Kbar, Khat; Khat -> sR1
         const int r = 4 * e / DK, c = 4 * e % DK;
@@ -1273,7 +1364,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {   // W = T Khat
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
                                   [&](int j, int c) { return sR1[j * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * (l >> 4) + q) * DK + c0 + (l & 15)] = acc[q];
@@ -1298,7 +1389,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
 #pragma unroll
     for (int m = 0; m < TZ; ++m) {   // Z = Ak X
         const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        zr[m] = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM[r * CP + j]; },
+        zr[m] = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM[r * CP + j]; },
                         [&](int j, int i) { return sR1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oZ + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = zr[m][q];
@@ -1313,7 +1404,7 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
     __syncthreads();
     for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {   // Ut = T Z
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sT[r * CP + j]; },
                                   [&](int j, int i) { return sR1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
@@ -1338,8 +1429,8 @@ __global__ __launch_bounds__(kGT) void bwd2_prep_kernel(BwdArgs p, float* ws, in
         if (j0 <= r0) {
             const float* gref = sG + (j0 + 15) * (DK + 4);
             auto Aq = [&](int r, int c) { return sR1[r * LD + c] * aexp(r, c, gref); };
-            me = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sR2[j * LD + c] * bexp(j, c, gref); });
-            mk = mm_tile(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
+            me = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sR2[j * LD + c] * bexp(j, c, gref); });
+            mk = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, Aq, [&](int c, int j) { return sK[j * (DK + 4) + c] * bexp(j, c, gref); });
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1436,9 +1527,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {          // dMe = -Tril0(dO Y^T), dMk = Tril0(dO X^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 me = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 me = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                  [&](int i, int j) { return R1[j * LD + i]; });
-        const f32x4 mk = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 mk = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                  [&](int i, int j) { return R2[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1460,7 +1551,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                a1[m] = mm_tile<kSplitMM<E>>(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
                                 [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
@@ -1480,8 +1571,8 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                 auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; };
-                a1[m] = mm_tile(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R1[r * LD + i]; }, Bs);
-                a2[m] = mm_tile(a2[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R2[r * LD + i]; }, Bs);
+                a1[m] = mm_tile<kSplitMM<E>>(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R1[r * LD + i]; }, Bs);
+                a2[m] = mm_tile<kSplitMM<E>>(a2[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R2[r * LD + i]; }, Bs);
             }
         }
 #pragma unroll
@@ -1523,7 +1614,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                dWr[m] = mm_tile(dWr[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                dWr[m] = mm_tile<kSplitMM<E>>(dWr[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
                                  [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
@@ -1547,14 +1638,14 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     static_assert(TCV % kGW == 0 && TCC % kGW == 0, "tiles per wave");
     for (int t = w; t < TCV; t += kGW) {          // dZ = T^T dY (to the workspace until R0 is free)
         const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
                                   [&](int k, int i) { return R0[k * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::odZ + ti(r0, q) * DV + tj(c0)] = acc[q];
     }
     for (int t = w; t < TCD; t += kGW) {          // dKhat = T^T dW
         const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int k) { return sT[k * CP + r]; },
                                   [&](int k, int c) { return R2[k * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::odKh + ti(r0, q) * DK + tj(c0)] = acc[q];
@@ -1572,7 +1663,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int m = 0; m < TCC / kGW; ++m) {
             const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-            dTr[m] = mm_tile(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int c) { return R2[r * LD + c]; },
+            dTr[m] = mm_tile<kSplitMM<E>>(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int c) { return R2[r * LD + c]; },
                              [&](int c, int j) { return sM2[j * CP + c - h0]; });
         }
         __syncthreads();
@@ -1586,7 +1677,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int m = 0; m < TCC / kGW; ++m) {
             const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-            dTr[m] = mm_tile(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int i) { return R0[r * LD + i]; },
+            dTr[m] = mm_tile<kSplitMM<E>>(dTr[m], r0, j0, h0, h0 + 64, [&](int r, int i) { return R0[r * LD + i]; },
                              [&](int i, int j) { return sM2[j * CP + i - h0]; });
         }
         __syncthreads();
@@ -1607,7 +1698,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {          // tmp = dT T^T
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM1[r * CP + m]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM1[r * CP + m]; },
                                   [&](int m, int j) { return sT[j * CP + m]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
@@ -1615,9 +1706,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     __syncthreads();
     for (int t = w; t < TCC; t += kGW) {          // dAe = -T^T tmp, dAk = StrictTril(dZ X^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 ae = mm_tile(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+        const f32x4 ae = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
                                  [&](int m, int j) { return sTmp[m * CP + j]; });
-        const f32x4 ak = mm_tile(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 ak = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
                                  [&](int i, int j) { return R2[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1645,9 +1736,9 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
     for (int m = 0; m < MV; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        dXr[m] = mm_tile(z4, r0, c0, 0, kBC, [&](int r, int k) { return sM1[k * CP + r]; },
+        dXr[m] = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int k) { return sM1[k * CP + r]; },
                          [&](int k, int i) { return R2[k * LD + i]; });
-        dXr[m] = mm_tile(dXr[m], r0, c0, 0, kBC, [&](int r, int k) { return sM2[k * CP + r]; },
+        dXr[m] = mm_tile<kSplitMM<E>>(dXr[m], r0, c0, 0, kBC, [&](int r, int k) { return sM2[k * CP + r]; },
                          [&](int k, int i) { return R0[k * LD + i]; });
     }
     __syncthreads();
@@ -1661,7 +1752,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MV; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
         const float* dsb = c0 < 64 ? R0 : R2 - 64 * LD;   // row i of dS' at dsb + i LD
-        dXr[m] = mm_tile(dXr[m], r0, c0, 0, DK, [&](int r, int c) { return R1[r * LD + c]; },
+        dXr[m] = mm_tile<kSplitMM<E>>(dXr[m], r0, c0, 0, DK, [&](int r, int c) { return R1[r * LD + c]; },
                          [&](int c, int i) { return dsb[i * LD + c]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1718,8 +1809,8 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MT; ++m) {   // Me terms
         int r0, c0;
         tile_of(m, r0, c0);
-        const f32x4 row = pair_tile<true>(r0, c0, M1, X1, Gf);
-        const f32x4 col = pair_tile<false>(r0, c0, M1, X0, Gf);
+        const f32x4 row = pair_tile<true, kSplitMM<E>>(r0, c0, M1, X1, Gf);
+        const f32x4 col = pair_tile<false, kSplitMM<E>>(r0, c0, M1, X0, Gf);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = ti(r0, q), c = tj(c0);
@@ -1735,8 +1826,8 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MT; ++m) {   // Mk terms; k -> R1
         int r0, c0;
         tile_of(m, r0, c0);
-        const f32x4 row = pair_tile<true>(r0, c0, M2, X1, Gf);
-        const f32x4 col = pair_tile<false>(r0, c0, M2, X0, Gf);
+        const f32x4 row = pair_tile<true, kSplitMM<E>>(r0, c0, M2, X1, Gf);
+        const f32x4 col = pair_tile<false, kSplitMM<E>>(r0, c0, M2, X0, Gf);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = ti(r0, q), c = tj(c0);
@@ -1757,10 +1848,10 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MT; ++m) {
         int r0, c0;
         tile_of(m, r0, c0);
-        const f32x4 rowe = pair_tile<true>(r0, c0, M1, X0, Gf);
-        const f32x4 cole = pair_tile<false>(r0, c0, M1, X1, Gf);
-        const f32x4 rowk = pair_tile<true>(r0, c0, M2, X1, Gf);
-        const f32x4 colk = pair_tile<false>(r0, c0, M2, X1, Gf);
+        const f32x4 rowe = pair_tile<true, kSplitMM<E>>(r0, c0, M1, X0, Gf);
+        const f32x4 cole = pair_tile<false, kSplitMM<E>>(r0, c0, M1, X1, Gf);
+        const f32x4 rowk = pair_tile<true, kSplitMM<E>>(r0, c0, M2, X1, Gf);
+        const f32x4 colk = pair_tile<false, kSplitMM<E>>(r0, c0, M2, X1, Gf);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = ti(r0, q), c = tj(c0);
