@@ -247,10 +247,11 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *
  *   workspace, workspace_bytes
  *          at least delta_bwd_workspace_bytes(desc) bytes: B * H * ceil(T / 64)
- *          records of 560.5 KiB (d_k = d_v = 128; 448.5, 352.25 and 272.25 KiB
- *          for d_k/d_v = 128/64, 64/128, 64/64; DR_FG2 the same), for DR_GDN2
- *          768.5 KiB (640.5, 464.5, 384.25), rounded up to 256 bytes, plus the
- *          two grouped-head buffers when H_k < H
+ *          records, rounded up to 256 bytes, plus the two grouped-head buffers
+ *          when H_k < H.  A record is, for d_k/d_v = 128/128 (128/64, 64/128,
+ *          64/64): DR_DELTANET and DR_GDN 432.75 KiB (320.75, 288.5, 208.5);
+ *          DR_KDA and DR_FG2 560.5 KiB (448.5, 352.25, 272.25); DR_GDN2
+ *          768.5 KiB (640.5, 464.5, 384.25)
  */
 dr_status delta_bwd_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,

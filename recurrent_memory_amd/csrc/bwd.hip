@@ -283,6 +283,7 @@ __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int l
 // Workspace record of one (batch, head, chunk), in floats.
 template <int DK, int DV>
 struct BwdWs {
+    static constexpr bool kRowGate = false;
     static constexpr int64_t C = kBC;
     static constexpr int64_t oG = 0;                // G            [C][DK]
     static constexpr int64_t oT = oG + C * DK;      // T            [C][C]
@@ -306,11 +307,43 @@ struct BwdWs {
     static constexpr int64_t oEb = oKb;             // (the split-gate chains' Ebar; unused here)
 };
 
+// Workspace record of the ungated and scalar-decay forms.  Their decay is one
+// number per row, so G is kept per row and the decay-scaled copies of q and k
+// (Qhat = q e^G, Khat = k e^G, Kbar = k e^{G_C - G}) are rebuilt from the inputs
+// where they are read, with the same factors: a third less workspace than the
+// per-channel record, and that much less written by the factor kernel and read
+// by the others.
+template <int DK, int DV>
+struct BwdWsS {
+    static constexpr bool kRowGate = true;
+    static constexpr int64_t C = kBC;
+    static constexpr int64_t oG = 0;                // G            [C] (one value per row)
+    static constexpr int64_t oT = oG + C;           // T            [C][C]
+    static constexpr int64_t oAb = oT + C * C;      // Abar         [C][C]
+    static constexpr int64_t oMq = oAb + C * C;     // Mq           [C][C]
+    static constexpr int64_t oW = oMq + C * C;      // W            [C][DK]
+    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
+    static constexpr int64_t oGam = oU + C * DV;    // gamma        [DK]
+    static constexpr int64_t oS = oGam + DK;        // S entering   [DV][DK]
+    static constexpr int64_t odS = oS + DV * DK;    // dS leaving   [DV][DK]
+    static constexpr int64_t oVt = odS + DV * DK;   // Vt           [C][DV]
+    static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
+    static constexpr int64_t odW = odVt + C * DV;   // dW           [C][DK]
+    static constexpr int64_t odX = odW + C * DK;    // dX           [C][DK]
+    static constexpr int64_t odQh = odX + C * DK;   // dQhat, then dG [C][DK]
+    static constexpr int64_t odKb = odQh + C * DK;  // dKbar        [C][DK]
+    static constexpr int64_t size = odKb + C * DK;
+};
+// record layout of a one-step-size form
+template <int VAR, int DK, int DV>
+using BwdWs1 = typename std::conditional<(VAR <= 1), BwdWsS<DK, DV>, BwdWs<DK, DV>>::type;
+
 // Workspace record of the split-gate form (Gated DeltaNet-2).  The names the
 // state chains share with the single-step-size record carry the split-gate
 // factors: oU holds Ut, oVt holds Y, odVt holds dY and oMq holds Me.
 template <int DK, int DV>
 struct BwdWs2 {
+    static constexpr bool kRowGate = false;
     static constexpr int64_t C = kBC;
     static constexpr int64_t oG = 0;                // G        [C][DK]
     static constexpr int64_t oT = oG + C * DK;      // T        [C][C]
@@ -360,7 +393,7 @@ __device__ __forceinline__ void store_qk_grad(void* out, float* out32, int64_t v
 // ---------------------------------------------------------------- 1. factors
 template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int N) {
-    typedef BwdWs<DK, DV> L;
+    typedef BwdWs1<VAR, DK, DV> L;
     constexpr int LD = (DK > DV ? DK : DV) + 4;   // padded row stride (4 mod 64 words)
     __shared__ __attribute__((aligned(16))) float sK[kBC * (DK + 4)];
     __shared__ __attribute__((aligned(16))) float sX[kBC * LD];   // q, then beta Khat, then beta v
@@ -421,9 +454,13 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
         }
     }
     __syncthreads();
-    DR_TILE_FOR(e, kBC * DK / 4, kGT) {
-        const int r = 4 * e / DK, c = 4 * e % DK;
-        put(R + L::oG + 4 * e, *reinterpret_cast<const float4*>(sG + r * (DK + 4) + c));
+    if constexpr (L::kRowGate) {
+        if (tid < kBC) R[L::oG + tid] = sG[tid * (DK + 4)];
+    } else {
+        DR_TILE_FOR(e, kBC * DK / 4, kGT) {
+            const int r = 4 * e / DK, c = 4 * e % DK;
+            put(R + L::oG + 4 * e, *reinterpret_cast<const float4*>(sG + r * (DK + 4) + c));
+        }
     }
     if (tid < DK) R[L::oGam + tid] = __expf(sG[(kBC - 1) * (DK + 4) + tid]);
     // Abar (strictly lower) and Mq (lower, diagonal included)
@@ -494,9 +531,11 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
             kb = make_float4(kb.x * bv.x, kb.y * bv.y, kb.z * bv.z, kb.w * bv.w);
         }
         const float4 kh = make_float4(kk.x * eg.x, kk.y * eg.y, kk.z * eg.z, kk.w * eg.w);
-        put(R + L::oKh + 4 * e, kh);
-        put(R + L::oQh + 4 * e, make_float4(qq.x * eg.x, qq.y * eg.y, qq.z * eg.z, qq.w * eg.w));
-        put(R + L::oKb + 4 * e, kb);
+        if constexpr (!L::kRowGate) {
+            put(R + L::oKh + 4 * e, kh);
+            put(R + L::oQh + 4 * e, make_float4(qq.x * eg.x, qq.y * eg.y, qq.z * eg.z, qq.w * eg.w));
+            put(R + L::oKb + 4 * e, kb);
+        }
         const float br = sBeta[r];
         put(sX + r * LD + c, make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w));
     }
@@ -579,6 +618,8 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
     float4 pW[NP], pK[NP], pE[SPLIT ? NP : 1];
     float pU[MT][4];
     float pG = 0.f;
+    // per-row decay (row-gate record): Kbar = k e^{G_C - G_r}, k fetched raw
+    float pGr[L::kRowGate ? NP : 1], pGC = 0.f;
     float4 pXw = make_float4(0.f, 0.f, 0.f, 0.f), pXv = pXw;   // split gates: w and v of X = w v
     static_assert(kBC * kBVT == 4 * kCT, "X: four columns per thread");
     auto fetch = [&](int n) {
@@ -593,9 +634,16 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kCT * j);
             pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
-            pK[j] = *reinterpret_cast<const float4*>(R + L::oKb + idx);
+            if constexpr (L::kRowGate) {   // rows past the end from the last row, zeroed when stored
+                const int r = idx / DK, c = idx % DK, Cn = min(kBC, p.T - n * kBC);
+                pK[j] = load4<E>(p.k, qk_index(p, b, n * kBC + min(r, Cn - 1), h) * DK + c);
+                pGr[j] = R[L::oG + r];
+            } else {
+                pK[j] = *reinterpret_cast<const float4*>(R + L::oKb + idx);
+            }
             if constexpr (SPLIT) pE[j] = *reinterpret_cast<const float4*>(R + L::oEb + idx);
         }
+        if constexpr (L::kRowGate) pGC = R[L::oG + kBC - 1];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int t = w + kCW * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
@@ -614,7 +662,14 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kCT * j);
             put4(sW, SW, idx, pW[j]);
-            put4(sKb, SK, idx, pK[j]);
+            if constexpr (L::kRowGate) {
+                const bool ok = idx / DK < min(kBC, p.T - n * kBC);
+                const float f = __expf(pGC - pGr[j]);
+                const float4 kv = pK[j];
+                put4(sKb, SK, idx, ok ? make_float4(kv.x * f, kv.y * f, kv.z * f, kv.w * f) : make_float4(0.f, 0.f, 0.f, 0.f));
+            } else {
+                put4(sKb, SK, idx, pK[j]);
+            }
             if constexpr (SPLIT) put4(sEb, SK, idx, pE[j]);
         }
         float uu[MT][4];
@@ -732,6 +787,8 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
     float4 pM[NM], pA[NP], pQ[NP], pW[NP];
     float pO[NO];
     float pG = 0.f;
+    // per-row decay (row-gate record): Kbar = k e^{G_C - G_r}, Qhat = q e^{G_r}, q and k fetched raw
+    float pGr[L::kRowGate ? NP : 1], pGC = 0.f;
     auto fetch = [&](int n) {
         const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
         const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
@@ -740,10 +797,19 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kCT * j);
-            pA[j] = *reinterpret_cast<const float4*>(R + (SPLIT ? L::oEb : L::oKb) + idx);
-            pQ[j] = *reinterpret_cast<const float4*>(R + L::oQh + idx);
+            if constexpr (L::kRowGate) {   // rows past the end from the last row, zeroed when stored
+                const int r = idx / DK, c = idx % DK;
+                const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c;
+                pA[j] = load4<E>(p.k, qi);
+                pQ[j] = load4<E>(p.q, qi);
+                pGr[j] = R[L::oG + r];
+            } else {
+                pA[j] = *reinterpret_cast<const float4*>(R + (SPLIT ? L::oEb : L::oKb) + idx);
+                pQ[j] = *reinterpret_cast<const float4*>(R + L::oQh + idx);
+            }
             pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
         }
+        if constexpr (L::kRowGate) pGC = R[L::oG + kBC - 1];
 #pragma unroll
         for (int j = 0; j < NO; ++j) {   // rows past the end: the last row, zeroed when stored
             const int e = tid + kCT * j, r = e / kBVT, i = e % kBVT;
@@ -759,14 +825,22 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
 #pragma unroll
         for (int j = 0; j < NM; ++j) put4(sM, 4 * (tid + kCT * j), SMQ, kBC, pM[j]);
+        const int Cn = min(kBC, p.T - n * kBC);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int idx = 4 * (tid + kCT * j);
-            put4(sA1, idx, SA, DK, pA[j]);
-            put4(sQh, idx, SB, DK, pQ[j]);
+            if constexpr (L::kRowGate) {
+                const bool ok = idx / DK < Cn;
+                const float fb = __expf(pGC - pGr[j]), fq = __expf(pGr[j]);
+                const float4 kv = pA[j], qv = pQ[j], z = make_float4(0.f, 0.f, 0.f, 0.f);
+                put4(sA1, idx, SA, DK, ok ? make_float4(kv.x * fb, kv.y * fb, kv.z * fb, kv.w * fb) : z);
+                put4(sQh, idx, SB, DK, ok ? make_float4(qv.x * fq, qv.y * fq, qv.z * fq, qv.w * fq) : z);
+            } else {
+                put4(sA1, idx, SA, DK, pA[j]);
+                put4(sQh, idx, SB, DK, pQ[j]);
+            }
             put4(sA2, idx, SB, DK, pW[j]);
         }
-        const int Cn = min(kBC, p.T - n * kBC);
 #pragma unroll
         for (int j = 0; j < NO; ++j) {
             const int e = tid + kCT * j;
@@ -839,7 +913,7 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
 // the per-element pairwise sums of the channel-wise decay stay on the VALU.
 template <int VAR, typename E, int DK, int DV>
 __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, int N) {
-    typedef BwdWs<DK, DV> L;
+    typedef BwdWs1<VAR, DK, DV> L;
     constexpr int CP = kBC + 4;
     constexpr int LD = (DK > DV ? DK : DV) + 4;
     constexpr int RS = (kBC * LD > 2 * kBC * CP) ? kBC * LD : 2 * kBC * CP;   // region size
@@ -977,14 +1051,36 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
     }
     __syncthreads();
-    col_sums(L::odKb, L::oKb, kBC);   // sum_r dKbar Kbar per column
+    if constexpr (L::kRowGate) {   // sum_r dKbar Kbar per column, Kbar = k e^{G_C - G_r} (zero past the end)
+        const float GC = R[L::oG + kBC - 1];
+        const int c = 4 * (tid % CG), part = tid / CG, rp = kBC / NPART;
+        float4 acc = z4v;
+#pragma unroll
+        for (int k = 0; k < rp; ++k) {
+            const int i = part * rp + k;
+            const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + min(i, Cn - 1), h) * DK + c);
+            const float f = __expf(GC - R[L::oG + i]);
+            acc = fma4(get(R + L::odKb + i * DK + c),
+                       i < Cn ? make_float4(kv.x * f, kv.y * f, kv.z * f, kv.w * f) : z4v, acc);
+        }
+        sPart[tid] = acc;
+    } else {
+        col_sums(L::odKb, L::oKb, kBC);   // sum_r dKbar Kbar per column
+    }
     __syncthreads();
     if (tid < DK) sCol[DK + tid] = col_total(tid);
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
     DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // dW -> R0, X -> R1
         const int r = 4 * e / DK, c = 4 * e % DK;
         put(R0 + r * LD + c, get(R + L::odW + 4 * e));
-        const float4 kh = get(R + L::oKh + 4 * e);
+        float4 kh;
+        if constexpr (L::kRowGate) {   // Khat = k e^{G_r}, zero past the end
+            const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
+            const float f = __expf(R[L::oG + r]);
+            kh = r < Cn ? make_float4(kv.x * f, kv.y * f, kv.z * f, kv.w * f) : z4v;
+        } else {
+            kh = get(R + L::oKh + 4 * e);
+        }
         const float br = sBeta[r];
         put(R1 + r * LD + c, make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w));
     }
@@ -1059,10 +1155,26 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     if constexpr (VAR != 4) {   // dbeta: kRT threads per row, fixed-order sums
         const int r = tid / kRT, qt = tid % kRT;
         float db = 0.f;
+        if constexpr (L::kRowGate) {   // Khat = k e^{G_r} rebuilt, four channels per load
+            const int64_t krow = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + qt * (DK / kRT);
+            float4 kv[DK / kRT / 4];
 #pragma unroll
-        for (int k = 0; k < DK / kRT; ++k) {
-            const int c = qt * (DK / kRT) + k;
-            db = fmaf(R[L::odX + r * DK + c], R[L::oKh + r * DK + c], db);
+            for (int m = 0; m < DK / kRT / 4; ++m) kv[m] = load4<E>(p.k, krow + 4 * m);
+            const float khf = r < Cn ? __expf(R[L::oG + r]) : 0.f;
+#pragma unroll
+            for (int m = 0; m < DK / kRT / 4; ++m) {
+                const float4 dx = get(R + L::odX + r * DK + qt * (DK / kRT) + 4 * m);
+                db = fmaf(dx.x, kv[m].x * khf, db);
+                db = fmaf(dx.y, kv[m].y * khf, db);
+                db = fmaf(dx.z, kv[m].z * khf, db);
+                db = fmaf(dx.w, kv[m].w * khf, db);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < DK / kRT; ++k) {
+                const int c = qt * (DK / kRT) + k;
+                db = fmaf(R[L::odX + r * DK + c], R[L::oKh + r * DK + c], db);
+            }
         }
         const int64_t vrow = tix(min(r, Cn - 1)) * DV;
         float dv_ = 0.f;
@@ -1091,7 +1203,12 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         const float4 qv = load4<E>(p.q, qi), kv = load4<E>(p.k, qi);
         put(R0 + r * LD + c, ok ? qv : z4v);
         put(R1 + r * LD + c, ok ? kv : z4v);
-        put(R2 + r * LD + c, get(R + L::oG + 4 * e));
+        if constexpr (L::kRowGate) {
+            const float gr = R[L::oG + r];
+            put(R2 + r * LD + c, make_float4(gr, gr, gr, gr));
+        } else {
+            put(R2 + r * LD + c, get(R + L::oG + 4 * e));
+        }
     }
     __syncthreads();
     // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
@@ -1990,11 +2107,11 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs<DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs<DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
@@ -2021,17 +2138,16 @@ hipError_t launch_bwd_dtype(int dtype, const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 template <int DK, int DV>
-size_t bwd_records_bytes(bool split, int64_t units) {
-    const int64_t rec = split ? BwdWs2<DK, DV>::size : BwdWs<DK, DV>::size;
+size_t bwd_records_bytes(int variant, int64_t units) {
+    const int64_t rec = variant == 3 ? BwdWs2<DK, DV>::size : variant <= 1 ? BwdWsS<DK, DV>::size : BwdWs<DK, DV>::size;
     return round_up_256(static_cast<size_t>(units * rec * 4));
 }
 
 size_t bwd_workspace_bytes(int variant, int B, int T, int H, int Hk, int dk, int dv) {
     const int64_t units = static_cast<int64_t>(B) * H * ((T + kBC - 1) / kBC);
-    const bool split = variant == 3;
     size_t n;
-    if (dk == 128) n = dv == 128 ? bwd_records_bytes<128, 128>(split, units) : bwd_records_bytes<128, 64>(split, units);
-    else n = dv == 128 ? bwd_records_bytes<64, 128>(split, units) : bwd_records_bytes<64, 64>(split, units);
+    if (dk == 128) n = dv == 128 ? bwd_records_bytes<128, 128>(variant, units) : bwd_records_bytes<128, 64>(variant, units);
+    else n = dv == 128 ? bwd_records_bytes<64, 128>(variant, units) : bwd_records_bytes<64, 64>(variant, units);
     if (Hk != H) n += 2 * round_up_256(static_cast<size_t>(B) * T * H * dk * 4);   // per-value-head dq, dk
     return n;
 }
