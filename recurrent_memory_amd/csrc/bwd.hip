@@ -280,7 +280,11 @@ __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int l
     __syncthreads();
 }
 
-// Workspace record of one (batch, head, chunk), in floats.
+// Workspace record of one (batch, head, chunk), in floats.  The gradient
+// kernel, the record's last reader, keeps four [C][DK] intermediates (dW, dX,
+// dQhat, dKbar) in it; they occupy the fields it never reads (W, U) or has read
+// before writing them (Vt, dVt), so the record grows only where 4 DK exceeds
+// DK + 3 DV.
 template <int DK, int DV>
 struct BwdWs {
     static constexpr bool kRowGate = false;
@@ -289,30 +293,31 @@ struct BwdWs {
     static constexpr int64_t oT = oG + C * DK;      // T            [C][C]
     static constexpr int64_t oAb = oT + C * C;      // Abar         [C][C]
     static constexpr int64_t oMq = oAb + C * C;     // Mq           [C][C]
-    static constexpr int64_t oW = oMq + C * C;      // W            [C][DK]
-    static constexpr int64_t oQh = oW + C * DK;     // Qhat         [C][DK]
+    static constexpr int64_t oQh = oMq + C * C;     // Qhat         [C][DK]
     static constexpr int64_t oKb = oQh + C * DK;    // Kbar         [C][DK]
     static constexpr int64_t oKh = oKb + C * DK;    // Khat         [C][DK]
-    static constexpr int64_t oU = oKh + C * DK;     // U            [C][DV]
-    static constexpr int64_t oGam = oU + C * DV;    // gamma        [DK]
+    static constexpr int64_t oGam = oKh + C * DK;   // gamma        [DK]
     static constexpr int64_t oS = oGam + DK;        // S entering   [DV][DK]
     static constexpr int64_t odS = oS + DV * DK;    // dS leaving   [DV][DK]
-    static constexpr int64_t oVt = odS + DV * DK;   // Vt           [C][DV]
+    static constexpr int64_t oW = odS + DV * DK;    // W            [C][DK]
+    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
+    static constexpr int64_t oVt = oU + C * DV;     // Vt           [C][DV]
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
-    static constexpr int64_t odW = odVt + C * DV;   // dW           [C][DK]
+    // the gradient kernel's intermediates, over W, U, Vt, dVt
+    static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
+    static constexpr int64_t odW = odQh + C * DK;   // dW           [C][DK]
     static constexpr int64_t odX = odW + C * DK;    // dX           [C][DK]
-    static constexpr int64_t odQh = odX + C * DK;   // dQhat, then dG [C][DK]
-    static constexpr int64_t odKb = odQh + C * DK;  // dKbar        [C][DK]
-    static constexpr int64_t size = odKb + C * DK;
+    static constexpr int64_t odKb = odX + C * DK;   // dKbar        [C][DK]
+    static constexpr int64_t size = (odVt + C * DV > odKb + C * DK) ? odVt + C * DV : odKb + C * DK;
     static constexpr int64_t oEb = oKb;             // (the split-gate chains' Ebar; unused here)
 };
 
 // Workspace record of the ungated and scalar-decay forms.  Their decay is one
 // number per row, so G is kept per row and the decay-scaled copies of q and k
 // (Qhat = q e^G, Khat = k e^G, Kbar = k e^{G_C - G}) are rebuilt from the inputs
-// where they are read, with the same factors: a third less workspace than the
-// per-channel record, and that much less written by the factor kernel and read
-// by the others.
+// where they are read, with the same factors: less workspace, and that much less
+// written by the factor kernel and read by the others.  The gradient kernel's
+// intermediates overlay W, U, Vt and dVt as in BwdWs.
 template <int DK, int DV>
 struct BwdWsS {
     static constexpr bool kRowGate = true;
@@ -321,18 +326,18 @@ struct BwdWsS {
     static constexpr int64_t oT = oG + C;           // T            [C][C]
     static constexpr int64_t oAb = oT + C * C;      // Abar         [C][C]
     static constexpr int64_t oMq = oAb + C * C;     // Mq           [C][C]
-    static constexpr int64_t oW = oMq + C * C;      // W            [C][DK]
-    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
-    static constexpr int64_t oGam = oU + C * DV;    // gamma        [DK]
+    static constexpr int64_t oGam = oMq + C * C;    // gamma        [DK]
     static constexpr int64_t oS = oGam + DK;        // S entering   [DV][DK]
     static constexpr int64_t odS = oS + DV * DK;    // dS leaving   [DV][DK]
-    static constexpr int64_t oVt = odS + DV * DK;   // Vt           [C][DV]
+    static constexpr int64_t oW = odS + DV * DK;    // W            [C][DK]
+    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
+    static constexpr int64_t oVt = oU + C * DV;     // Vt           [C][DV]
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
-    static constexpr int64_t odW = odVt + C * DV;   // dW           [C][DK]
+    static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
+    static constexpr int64_t odW = odQh + C * DK;   // dW           [C][DK]
     static constexpr int64_t odX = odW + C * DK;    // dX           [C][DK]
-    static constexpr int64_t odQh = odX + C * DK;   // dQhat, then dG [C][DK]
-    static constexpr int64_t odKb = odQh + C * DK;  // dKbar        [C][DK]
-    static constexpr int64_t size = odKb + C * DK;
+    static constexpr int64_t odKb = odX + C * DK;   // dKbar        [C][DK]
+    static constexpr int64_t size = (odVt + C * DV > odKb + C * DK) ? odVt + C * DV : odKb + C * DK;
 };
 // record layout of a one-step-size form
 template <int VAR, int DK, int DV>
