@@ -251,7 +251,7 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *          when H_k < H.  A record is, for d_k/d_v = 128/128 (128/64, 64/128,
  *          64/64): DR_DELTANET and DR_GDN 304.75 KiB (240.75, 224.5, 144.5);
  *          DR_KDA and DR_FG2 432.5 KiB (368.5, 288.25, 208.25); DR_GDN2
- *          768.5 KiB (640.5, 464.5, 384.25)
+ *          560.5 KiB (464.5, 368.25, 304.25)
  */
 dr_status delta_bwd_workspace_bytes(const dr_desc* desc, size_t* bytes);
 dr_status delta_bwd(const dr_desc* desc, const void* q, const void* k, const void* v,

@@ -353,31 +353,37 @@ struct BwdWs2 {
     static constexpr int64_t oG = 0;                // G        [C][DK]
     static constexpr int64_t oT = oG + C * DK;      // T        [C][C]
     static constexpr int64_t oAk = oT + C * C;      // Ak       [C][C]
-    static constexpr int64_t oMq = oAk + C * C;     // Me       [C][C]
-    static constexpr int64_t oMk = oMq + C * C;     // Mk       [C][C]
-    static constexpr int64_t oW = oMk + C * C;      // W        [C][DK]
-    static constexpr int64_t oQh = oW + C * DK;     // Qhat
-    static constexpr int64_t oKb = oQh + C * DK;    // Kbar
+    static constexpr int64_t oMk = oAk + C * C;     // Mk       [C][C]
+    static constexpr int64_t oKb = oMk + C * C;     // Kbar     [C][DK]
     static constexpr int64_t oEb = oKb + C * DK;    // Ebar
     static constexpr int64_t oKh = oEb + C * DK;    // Khat
     static constexpr int64_t oZ = oKh + C * DK;     // Z = Ak X [C][DV]
-    static constexpr int64_t oU = oZ + C * DV;      // Ut = T Z [C][DV]
-    static constexpr int64_t oGam = oU + C * DV;    // gamma    [DK]
+    static constexpr int64_t oGam = oZ + C * DV;    // gamma    [DK]
     static constexpr int64_t oS = oGam + DK;        // S entering [DV][DK]
     static constexpr int64_t odS = oS + DV * DK;    // dS leaving [DV][DK]
-    static constexpr int64_t oVt = odS + DV * DK;   // Y        [C][DV]
-    static constexpr int64_t odVt = oVt + C * DV;   // dY       [C][DV]
-    static constexpr int64_t odMe = odVt + C * DV;  // scratch: dMe, dMk, dAe, dAk [C][C]
+    // fields the gradient kernel never reads (Me, W, Qhat, Ut) or reads first (Y,
+    // then dY): its intermediates overlay them, in the order they are first
+    // written.  Those written before dY is read (dMe, dMk, dQhat, dEbar, dKbar)
+    // must end before dY, hence the padding when C + DK > 2 DV.
+    static constexpr int64_t kPre = 2 * C * C + 3 * C * DK;
+    static constexpr int64_t kAvail = C * C + 2 * C * DK + 2 * C * DV;
+    static constexpr int64_t oMq = odS + DV * DK;   // Me       [C][C]
+    static constexpr int64_t oW = oMq + C * C;      // W        [C][DK]
+    static constexpr int64_t oQh = oW + C * DK;     // Qhat     [C][DK]
+    static constexpr int64_t oU = oQh + C * DK;     // Ut = T Z [C][DV]
+    static constexpr int64_t oVt = oU + C * DV;     // Y        [C][DV]
+    static constexpr int64_t odVt = oVt + C * DV + (kPre > kAvail ? kPre - kAvail : 0);   // dY [C][DV]
+    static constexpr int64_t odMe = oMq;            // dMe, dMk [C][C]
     static constexpr int64_t odMk = odMe + C * C;
-    static constexpr int64_t odAe = odMk + C * C;
+    static constexpr int64_t odQh = odMk + C * C;   // dQhat (then dG), dEbar, dKbar [C][DK]
+    static constexpr int64_t odEb = odQh + C * DK;
+    static constexpr int64_t odKb = odEb + C * DK;
+    static constexpr int64_t odZ = odKb + C * DK;   // dZ       [C][DV]
+    static constexpr int64_t odKh = odZ + C * DV;   // dKhat    [C][DK]
+    static constexpr int64_t odAe = odKh + C * DK;  // dAe, dAk [C][C]
     static constexpr int64_t odAk = odAe + C * C;
-    static constexpr int64_t odW = odAk + C * C;    // dW, dKhat, dQhat (then dG), dKbar, dEbar [C][DK]
-    static constexpr int64_t odKh = odW + C * DK;
-    static constexpr int64_t odQh = odKh + C * DK;
-    static constexpr int64_t odKb = odQh + C * DK;
-    static constexpr int64_t odEb = odKb + C * DK;
-    static constexpr int64_t odZ = odEb + C * DK;   // dZ       [C][DV]
-    static constexpr int64_t size = odZ + C * DV;
+    static constexpr int64_t size = (odVt + C * DV > odAk + C * C) ? odVt + C * DV : odAk + C * C;
+    static_assert(odKb + C * DK <= odVt, "intermediates written before dY is read end before it");
 };
 
 __device__ __forceinline__ int64_t tok_index(const BwdArgs& p, int b, int t, int h) {

@@ -221,7 +221,7 @@ def test_workspace_size_queries():
     for fp32 channel-wise forms; one 38 KiB (split gates: 50 KiB) block per 32
     tokens of a head for the bf16 channel-wise forward; one record per 64 tokens
     of a head for the backward (d = 128: 304.75 KiB for the ungated and scalar-decay
-    forms, 432.5 KiB for KDA and FG^2-GDN, 768.5 KiB for the split gates), plus two
+    forms, 432.5 KiB for KDA and FG^2-GDN, 560.5 KiB for the split gates), plus two
     fp32 [B,T,H,d_k] buffers with grouped heads; the DeltaTTT-pre intermediates."""
     up = lambda n: (n + 255) // 256 * 256
     assert ws_bytes("fwd", None)[0] == DR_E_NULLPTR
@@ -240,7 +240,9 @@ def test_workspace_size_queries():
     assert ws_bytes("bwd", desc(variant=0)) == (DR_OK, up(2 * 3 * n64 * 30475 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=2)) == (DR_OK, up(2 * 3 * n64 * 4325 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=4)) == (DR_OK, up(2 * 3 * n64 * 4325 * 1024 // 10))
-    assert ws_bytes("bwd", desc(variant=3)) == (DR_OK, up(2 * 3 * n64 * 7685 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=3)) == (DR_OK, up(2 * 3 * n64 * 5605 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=3, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 4645 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=3, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 30425 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 1445 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=2, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 20825 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=1, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 24075 * 1024 // 100))
