@@ -78,6 +78,17 @@ __device__ __forceinline__ f32x4 mfma_split4(const bf16x4& ah, const bf16x4& al,
     acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bl), acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bh), acc, 0, 0, 0);
 }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// LDS transpose load of 16-bit elements: within each group of 16 lanes, lane p
+// supplies the address of 4 consecutive elements and lane i receives element
+// i % 4 of the piece addressed by lane 4 j + i / 4, j = 0..3.  Lane p of group g
+// points at row r0 + 4 g + p / 4, columns c0 + 4 (p % 4) of a row-major array;
+// lane c then holds rows r0 + 4 g + j of column c0 + c.
+__device__ __forceinline__ bf16x4 tr_load_b16(const uint16_t* base, int ld, int r0, int c0, int g, int c) {
+    const uint16_t* q = base + (r0 + 4 * g + (c >> 2)) * ld + c0 + 4 * (c & 3);
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q)));
+}
 // operand pieces of lane (g, c) for a k step of 8 N: A(ai, k + N g + e) and B(k + N g + e, bj)
 template <int N, class V, class FA, class FB>
 __device__ __forceinline__ void split_operands(V& ah, V& al, V& bh, V& bl, int ai, int bj, int k, int g,
@@ -915,6 +926,218 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         for (int e = tid; e < kBVT * DK; e += kCT) {
             const int i = e / DK, c = e % DK;
             p.gS0[(static_cast<int64_t>(bh) * DV + i0 + i) * DK + c] = sdS[i * SD + c];
+        }
+    }
+}
+
+// The reverse chain with bf16 inputs: the operands are split into bf16 hi and lo
+// once, when they are staged in LDS (natural row-major layouts, 16-byte padded
+// rows), rather than by every lane at every read, and each product's k step of
+// 32 is three v_mfma_f32_16x16x32_bf16 on fragments read 8 bytes at a time.  A
+// contraction over the columns of a stored matrix reads its rows with plain
+// 8-byte loads; one over the rows uses the LDS transpose load.  Within a k step
+// of 32, lane (g, c) holds k = k0 + 4 g + e in slots e = 0..3 and
+// k0 + 16 + 4 g + (e - 4) in slots 4..7, the same order for both operands.  dS is
+// carried in fp32 accumulators by the waves that update it; LDS holds its split
+// copy for the products of the next step.
+struct Frag {
+    bf16x8 h, l;
+};
+__device__ __forceinline__ bf16x4 ld4(const uint16_t* q) { return *reinterpret_cast<const bf16x4*>(q); }
+// k along the columns of a row-major array: row `row`, k block k0
+__device__ __forceinline__ Frag frag_row(const uint16_t* hi, const uint16_t* lo, int ld, int row, int k0, int g) {
+    const int o = row * ld + k0 + 4 * g;
+    return Frag{cat8(ld4(hi + o), ld4(hi + o + 16)), cat8(ld4(lo + o), ld4(lo + o + 16))};
+}
+// k along the rows of a row-major array: rows k0 + 4 g .., column n0 + c
+__device__ __forceinline__ Frag frag_tr(const uint16_t* hi, const uint16_t* lo, int ld, int k0, int n0, int g, int c) {
+    return Frag{cat8(tr_load_b16(hi, ld, k0, n0, g, c), tr_load_b16(hi, ld, k0 + 16, n0, g, c)),
+                cat8(tr_load_b16(lo, ld, k0, n0, g, c), tr_load_b16(lo, ld, k0 + 16, n0, g, c))};
+}
+__device__ __forceinline__ f32x4 mma3(const Frag& a, const Frag& b, f32x4 acc) {
+    return mfma_split8(a.h, a.l, b.h, b.l, acc);
+}
+__device__ __forceinline__ uint32_t split_pair(float x, float y, uint32_t& lo) {
+    bf16_t xh, xl, yh, yl;
+    split_bf16(x, xh, xl);
+    split_bf16(y, yh, yl);
+    lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, xl)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, yl)) << 16);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, xh)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, yh)) << 16);
+}
+// four consecutive elements, split, to hi and lo (8 bytes each)
+__device__ __forceinline__ void put_split4(uint16_t* hi, uint16_t* lo, int o, float4 v) {
+    uint32_t l0, l1;
+    const uint32_t h0 = split_pair(v.x, v.y, l0), h1 = split_pair(v.z, v.w, l1);
+    *reinterpret_cast<uint2*>(hi + o) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2*>(lo + o) = make_uint2(l0, l1);
+}
+__device__ __forceinline__ void put_split1(uint16_t* hi, uint16_t* lo, int o, float x) {
+    bf16_t h, l;
+    split_bf16(x, h, l);
+    hi[o] = __builtin_bit_cast(uint16_t, h);
+    lo[o] = __builtin_bit_cast(uint16_t, l);
+}
+
+template <class L, typename E, int DK, int DV, bool SPLIT>
+__global__ __launch_bounds__(kCT) void bwd_rchain_split_kernel(BwdArgs p, float* ws, int N) {
+    constexpr int NVT = DV / kBVT;
+    constexpr int LM = kBC + 8, LO = kBVT + 8, LK = DK + 8, LT = kBC + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sMh[kBC * LM], sMl[kBC * LM];      // Mq (Me)   [m][r]
+    __shared__ __attribute__((aligned(16))) uint16_t sOh[kBC * LO], sOl[kBC * LO];      // dO        [m][i]
+    __shared__ __attribute__((aligned(16))) uint16_t sAh[kBC * LK], sAl[kBC * LK];      // Kbar (Ebar) [r][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sSh[kBVT * LK], sSl[kBVT * LK];    // dS'       [i][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sVh[kBVT * LT], sVl[kBVT * LT];    // -dVt (split gates: dY) [i][m]
+    __shared__ __attribute__((aligned(16))) uint16_t sQh[kBC * LK], sQl[kBC * LK];      // Qhat      [m][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sWh[kBC * LK], sWl[kBC * LK];      // W         [m][c]
+    __shared__ float sGam[DK];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, cl = l & 15;
+    int bh, i0;
+    if (!chain_block(p, NVT, bh, i0)) return;
+    const int b = bh / p.H, h = bh % p.H;
+    // dS tiles of this wave (accumulator layout): rows ii0 + 4 g + q, column cc + cl
+    constexpr int NTS = (kBVT / 16) * (DK / 16);
+    static_assert(NTS == kCW || NTS == 2 * kCW, "state tiles per wave");
+    constexpr int TW = NTS / kCW;
+    const int ii0 = 16 * (w % (kBVT / 16));
+    int cc[TW];
+    cc[0] = 16 * (w / (kBVT / 16));
+    if constexpr (TW == 2) cc[1] = cc[0] + 16 * (kCW / (kBVT / 16));
+    f32x4 dS[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dS[u][q] = p.dST ? p.dST[(static_cast<int64_t>(bh) * DV + i0 + ii0 + 4 * g + q) * DK + cc[u] + cl] : 0.f;
+    }
+    constexpr int NP = kBC * DK / 4 / kCT;
+    constexpr int NM = kBC * kBC / 4 / kCT;
+    constexpr int NO = kBC * kBVT / kCT;
+    float4 pM[NM], pA[NP], pQ[NP], pW[NP];
+    float pO[NO];
+    float pG = 0.f;
+    float pGr[L::kRowGate ? NP : 1], pGC = 0.f;
+    auto fetch = [&](int n) {
+        const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
+#pragma unroll
+        for (int j = 0; j < NM; ++j) pM[j] = *reinterpret_cast<const float4*>(R + L::oMq + 4 * (tid + kCT * j));
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kCT * j);
+            if constexpr (L::kRowGate) {   // rows past the end from the last row, zeroed when stored
+                const int r = idx / DK, c = idx % DK;
+                const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c;
+                pA[j] = load4<E>(p.k, qi);
+                pQ[j] = load4<E>(p.q, qi);
+                pGr[j] = R[L::oG + r];
+            } else {
+                pA[j] = *reinterpret_cast<const float4*>(R + (SPLIT ? L::oEb : L::oKb) + idx);
+                pQ[j] = *reinterpret_cast<const float4*>(R + L::oQh + idx);
+            }
+            pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
+        }
+        if constexpr (L::kRowGate) pGC = R[L::oG + kBC - 1];
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {   // rows past the end: the last row, zeroed when stored
+            const int e = tid + kCT * j, r = e / kBVT, i = e % kBVT;
+            pO[j] = load_elem<E>(p.dO, tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i);
+        }
+        pG = R[L::oGam + min(tid, DK - 1)];   // every lane loads: no branch, no wait in it
+    };
+    fetch(N - 1);
+    for (int n = N - 1; n >= 0; --n) {
+        float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        const int Cn = min(kBC, p.T - n * kBC);
+        // ---- stage this chunk's operands, split
+#pragma unroll
+        for (int j = 0; j < NM; ++j) {
+            const int idx = 4 * (tid + kCT * j);
+            put_split4(sMh, sMl, (idx / kBC) * LM + idx % kBC, pM[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kCT * j), o = (idx / DK) * LK + idx % DK;
+            float4 av = pA[j], qv = pQ[j];
+            if constexpr (L::kRowGate) {
+                const bool ok = idx / DK < Cn;
+                const float fb = __expf(pGC - pGr[j]), fq = __expf(pGr[j]);
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                av = ok ? make_float4(av.x * fb, av.y * fb, av.z * fb, av.w * fb) : z;
+                qv = ok ? make_float4(qv.x * fq, qv.y * fq, qv.z * fq, qv.w * fq) : z;
+            }
+            put_split4(sAh, sAl, o, av);
+            put_split4(sQh, sQl, o, qv);
+            put_split4(sWh, sWl, o, pW[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int e = tid + kCT * j;
+            put_split1(sOh, sOl, (e / kBVT) * LO + e % kBVT, e / kBVT < Cn ? pO[j] : 0.f);
+        }
+        sGam[min(tid, DK - 1)] = pG;   // lanes past DK rewrite the last entry with its own value
+        // dS' (leaving this chunk): to the record and, split, to LDS
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ii0 + 4 * g + q, c = cc[u] + cl;
+                R[L::odS + (i0 + i) * DK + c] = dS[u][q];
+                put_split1(sSh, sSl, i * LK + c, dS[u][q]);
+            }
+        }
+        lds_only_barrier();
+        if (n > 0) fetch(n - 1);
+        // ---- dVt = Mq^T dO + Kbar dS'^T (split gates: dY = -(Me^T dO + Ebar dS'^T)), one tile per wave
+        for (int t = w; t < (kBC / 16) * (kBVT / 16); t += kCW) {
+            const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32)
+                acc = mma3(frag_tr(sMh, sMl, LM, k0, r0, g, cl), frag_tr(sOh, sOl, LO, k0, c0, g, cl), acc);
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                acc = mma3(frag_row(sAh, sAl, LK, r0 + cl, k0, g), frag_row(sSh, sSl, LK, c0 + cl, k0, g), acc);
+            // record: dVt (dY); LDS: -acc for the dS products in both forms, as [i][m]
+            float4 nv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + 4 * g + q, i = c0 + cl;
+                R[L::odVt + r * DV + i0 + i] = SPLIT ? -acc[q] : acc[q];
+            }
+            nv = make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+            put_split4(sVh, sVl, (c0 + cl) * LT + r0 + 4 * g, nv);
+        }
+        lds_only_barrier();
+        // ---- dS = dS' Diag(gamma) + dO^T Qhat - dVt^T W  (split gates: + dY^T W)
+        {
+            f32x4 acc[TW];
+#pragma unroll
+            for (int u = 0; u < TW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32) {
+                const Frag ao = frag_tr(sOh, sOl, LO, k0, ii0, g, cl);
+                const Frag av = frag_row(sVh, sVl, LT, ii0 + cl, k0, g);
+#pragma unroll
+                for (int u = 0; u < TW; ++u) {
+                    acc[u] = mma3(ao, frag_tr(sQh, sQl, LK, k0, cc[u], g, cl), acc[u]);
+                    acc[u] = mma3(av, frag_tr(sWh, sWl, LK, k0, cc[u], g, cl), acc[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                const float gm = sGam[cc[u] + cl];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dS[u][q] = fmaf(dS[u][q], gm, acc[u][q]);
+            }
+        }
+        lds_only_barrier();
+    }
+    if (p.gS0) {
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                p.gS0[(static_cast<int64_t>(bh) * DV + i0 + ii0 + 4 * g + q) * DK + cc[u] + cl] = dS[u][q];
         }
     }
 }
@@ -2046,7 +2269,10 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        if constexpr (kSplitMM<E>)
+            hipLaunchKernelGGL((bwd_rchain_split_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        else
+            hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
@@ -2122,7 +2348,10 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        if constexpr (kSplitMM<E>)
+            hipLaunchKernelGGL((bwd_rchain_split_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        else
+            hipLaunchKernelGGL((bwd_rchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
