@@ -1142,6 +1142,160 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_split_kernel(BwdArgs p, float*
     }
 }
 
+// The forward chain with bf16 inputs, built like bwd_rchain_split_kernel: operands
+// split once at staging, S carried in fp32 accumulators by the waves that update
+// it, its split copy in LDS for the next step's W S^T.
+template <class L, typename E, int DK, int DV, bool SPLIT>
+__global__ __launch_bounds__(kCT) void bwd_fchain_split_kernel(BwdArgs p, float* ws, int N) {
+    constexpr int NVT = DV / kBVT;
+    constexpr int LK = DK + 8, LT = kBC + 8, LX = kBVT + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sWh[kBC * LK], sWl[kBC * LK];      // W         [r][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sKh[kBC * LK], sKl[kBC * LK];      // Kbar      [r][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sEh[SPLIT ? kBC * LK : 8], sEl[SPLIT ? kBC * LK : 8];   // Ebar
+    __shared__ __attribute__((aligned(16))) uint16_t sXh[SPLIT ? kBC * LX : 8], sXl[SPLIT ? kBC * LX : 8];   // X = w v [r][i]
+    __shared__ __attribute__((aligned(16))) uint16_t sSh[kBVT * LK], sSl[kBVT * LK];    // S entering [i][c]
+    __shared__ __attribute__((aligned(16))) uint16_t sVh[kBVT * LT], sVl[kBVT * LT];    // Vt (split gates: -Y) [i][r]
+    __shared__ float sGam[DK];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, cl = l & 15;
+    int bh, i0;
+    if (!chain_block(p, NVT, bh, i0)) return;
+    const int b = bh / p.H, h = bh % p.H;
+    constexpr int NTS = (kBVT / 16) * (DK / 16);
+    static_assert(NTS == kCW || NTS == 2 * kCW, "state tiles per wave");
+    constexpr int TW = NTS / kCW;
+    const int ii0 = 16 * (w % (kBVT / 16));
+    int cc[TW];
+    cc[0] = 16 * (w / (kBVT / 16));
+    if constexpr (TW == 2) cc[1] = cc[0] + 16 * (kCW / (kBVT / 16));
+    f32x4 S[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            S[u][q] = p.S0 ? p.S0[(static_cast<int64_t>(bh) * DV + i0 + ii0 + 4 * g + q) * DK + cc[u] + cl] : 0.f;
+    }
+    constexpr int NP = kBC * DK / 4 / kCT;
+    static_assert((kBC / 16) * (kBVT / 16) == kCW, "one Vt tile per wave");
+    float4 pW[NP], pK[NP], pE[SPLIT ? NP : 1];
+    float pU[4];
+    float pG = 0.f;
+    float pGr[L::kRowGate ? NP : 1], pGC = 0.f;
+    float4 pXw = make_float4(0.f, 0.f, 0.f, 0.f), pXv = pXw;
+    static_assert(kBC * kBVT == 4 * kCT, "X: four columns per thread");
+    const int vr0 = 16 * (w / (kBVT / 16)), vc0 = 16 * (w % (kBVT / 16));   // this wave's Vt tile
+    auto fetch = [&](int n) {
+        const float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
+        if constexpr (SPLIT) {   // this tile's value columns, rows past the end from the last row
+            const int r = 4 * tid / kBVT, i = 4 * tid % kBVT;
+            const int64_t vi = tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + i0 + i;
+            pXw = load4<E>(p.wgate, vi);
+            pXv = load4<E>(p.v, vi);
+        }
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kCT * j);
+            pW[j] = *reinterpret_cast<const float4*>(R + L::oW + idx);
+            if constexpr (L::kRowGate) {
+                const int r = idx / DK, c = idx % DK;
+                pK[j] = load4<E>(p.k, qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
+                pGr[j] = R[L::oG + r];
+            } else {
+                pK[j] = *reinterpret_cast<const float4*>(R + L::oKb + idx);
+            }
+            if constexpr (SPLIT) pE[j] = *reinterpret_cast<const float4*>(R + L::oEb + idx);
+        }
+        if constexpr (L::kRowGate) pGC = R[L::oG + kBC - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pU[q] = R[L::oU + (vr0 + 4 * g + q) * DV + i0 + vc0 + cl];
+        pG = R[L::oGam + min(tid, DK - 1)];
+    };
+    fetch(0);
+    for (int n = 0; n < N; ++n) {
+        float* R = ws + (static_cast<int64_t>(bh) * N + n) * L::size;
+        const int Cn = min(kBC, p.T - n * kBC);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int idx = 4 * (tid + kCT * j), o = (idx / DK) * LK + idx % DK;
+            put_split4(sWh, sWl, o, pW[j]);
+            float4 kv = pK[j];
+            if constexpr (L::kRowGate) {
+                const float f = __expf(pGC - pGr[j]);
+                kv = idx / DK < Cn ? make_float4(kv.x * f, kv.y * f, kv.z * f, kv.w * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            put_split4(sKh, sKl, o, kv);
+            if constexpr (SPLIT) put_split4(sEh, sEl, o, pE[j]);
+        }
+        if constexpr (SPLIT) {   // X = w v for this tile's value columns (fetched a step ahead)
+            const int r = 4 * tid / kBVT, i = 4 * tid % kBVT;
+            put_split4(sXh, sXl, r * LX + i,
+                       r < Cn ? make_float4(pXw.x * pXv.x, pXw.y * pXv.y, pXw.z * pXv.z, pXw.w * pXv.w)
+                              : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+        float uu[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) uu[q] = pU[q];
+        sGam[min(tid, DK - 1)] = pG;   // lanes past DK rewrite the last entry with its own value
+        // S entering this chunk: to the record and, split, to LDS
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = ii0 + 4 * g + q, c = cc[u] + cl;
+                R[L::oS + (i0 + i) * DK + c] = S[u][q];
+                put_split1(sSh, sSl, i * LK + c, S[u][q]);
+            }
+        }
+        lds_only_barrier();
+        if (n + 1 < N) fetch(n + 1);
+        // ---- Vt = U - W S^T  /  Y = Ut + W S^T, one tile per wave
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                acc = mma3(frag_row(sWh, sWl, LK, vr0 + cl, k0, g), frag_row(sSh, sSl, LK, vc0 + cl, k0, g), acc);
+            float4 vv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = vr0 + 4 * g + q, i = vc0 + cl;
+                const float val = SPLIT ? uu[q] + acc[q] : uu[q] - acc[q];
+                R[L::oVt + r * DV + i0 + i] = val;
+                vv[q] = SPLIT ? -val : val;   // the operand of the state update
+            }
+            put_split4(sVh, sVl, (vc0 + cl) * LT + vr0 + 4 * g, make_float4(vv[0], vv[1], vv[2], vv[3]));
+        }
+        lds_only_barrier();
+        // ---- S = S Diag(gamma) + Vt^T Kbar  /  - Y^T Ebar + X^T Kbar
+        {
+            f32x4 acc[TW];
+#pragma unroll
+            for (int u = 0; u < TW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32) {
+                const Frag av = frag_row(sVh, sVl, LT, ii0 + cl, k0, g);
+                if constexpr (SPLIT) {
+                    const Frag ax = frag_tr(sXh, sXl, LX, k0, ii0, g, cl);
+#pragma unroll
+                    for (int u = 0; u < TW; ++u) {
+                        acc[u] = mma3(av, frag_tr(sEh, sEl, LK, k0, cc[u], g, cl), acc[u]);
+                        acc[u] = mma3(ax, frag_tr(sKh, sKl, LK, k0, cc[u], g, cl), acc[u]);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < TW; ++u) acc[u] = mma3(av, frag_tr(sKh, sKl, LK, k0, cc[u], g, cl), acc[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                const float gm = sGam[cc[u] + cl];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) S[u][q] = fmaf(S[u][q], gm, acc[u][q]);
+            }
+        }
+        lds_only_barrier();
+    }
+}
+
 // ------------------------------------------------------------ 4. gradients
 // Products run on the matrix cores as 16 x 16 tiles spread over the eight waves;
 // the per-element pairwise sums of the channel-wise decay stay on the VALU.
@@ -2265,7 +2419,10 @@ hipError_t launch_bwd2_dims(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd2_prep_kernel<E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        if constexpr (kSplitMM<E>)
+            hipLaunchKernelGGL((bwd_fchain_split_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
+        else
+            hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs2<DK, DV>, E, DK, DV, true>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
@@ -2344,7 +2501,10 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        if constexpr (kSplitMM<E>)
+            hipLaunchKernelGGL((bwd_fchain_split_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
+        else
+            hipLaunchKernelGGL((bwd_fchain_kernel<BwdWs1<VAR, DK, DV>, E, DK, DV, false>), dim3(chains), blk, 0, s, a, ws, N);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
