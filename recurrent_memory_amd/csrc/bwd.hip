@@ -64,18 +64,21 @@ __device__ __forceinline__ void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
     hi = static_cast<bf16_t>(x);
     lo = static_cast<bf16_t>(x - static_cast<float>(hi));
 }
+// (AX, BX: the operand is exact in bf16, its lo part zero and its term skipped)
+template <bool AX = false, bool BX = false>
 __device__ __forceinline__ f32x4 mfma_split8(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
                                              const bf16x8& bl, f32x4 acc) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    if constexpr (!AX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    if constexpr (!BX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
 }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <bool AX = false, bool BX = false>
 __device__ __forceinline__ f32x4 mfma_split4(const bf16x4& ah, const bf16x4& al, const bf16x4& bh,
                                              const bf16x4& bl, f32x4 acc) {
     auto s = [](const bf16x4& v) { return __builtin_bit_cast(s16x4, v); };
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(al), s(bh), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bl), acc, 0, 0, 0);
+    if constexpr (!AX) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(al), s(bh), acc, 0, 0, 0);
+    if constexpr (!BX) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bl), acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(s(ah), s(bh), acc, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
@@ -89,6 +92,30 @@ __device__ __forceinline__ bf16x4 tr_load_b16(const uint16_t* base, int ld, int 
     const uint16_t* q = base + (r0 + 4 * g + (c >> 2)) * ld + c0 + 4 * (c & 3);
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q)));
 }
+// An operand accessor whose values are exact in bf16 (bf16 inputs as loaded, or
+// zero): its lo part is zero, so it is only rounded, and the products with its
+// lo part are skipped.
+template <class F>
+struct Exact {
+    F f;
+    __device__ __forceinline__ float operator()(int a, int b) const { return f(a, b); }
+};
+template <class F>
+__device__ __forceinline__ Exact<F> exact(const F& f) { return Exact<F>{f}; }
+template <class F>
+struct IsExact : std::false_type {};
+template <class F>
+struct IsExact<Exact<F>> : std::true_type {};
+
+template <class F>
+__device__ __forceinline__ void split_one(const F& A, int i, int j, bf16_t& h, bf16_t& lo) {
+    if constexpr (IsExact<F>::value) {
+        h = static_cast<bf16_t>(A(i, j));
+        lo = static_cast<bf16_t>(0.f);
+    } else {
+        split_bf16(A(i, j), h, lo);
+    }
+}
 // operand pieces of lane (g, c) for a k step of 8 N: A(ai, k + N g + e) and B(k + N g + e, bj)
 template <int N, class V, class FA, class FB>
 __device__ __forceinline__ void split_operands(V& ah, V& al, V& bh, V& bl, int ai, int bj, int k, int g,
@@ -96,10 +123,10 @@ __device__ __forceinline__ void split_operands(V& ah, V& al, V& bh, V& bl, int a
 #pragma unroll
     for (int e = 0; e < N; ++e) {
         bf16_t h, lo;
-        split_bf16(A(ai, k + N * g + e), h, lo);
+        split_one(A, ai, k + N * g + e, h, lo);
         ah[e] = h;
         al[e] = lo;
-        split_bf16(B(k + N * g + e, bj), h, lo);
+        split_one(B, k + N * g + e, bj, h, lo);
         bh[e] = h;
         bl[e] = lo;
     }
@@ -116,12 +143,12 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
         for (; k + 32 <= k1; k += 32) {
             bf16x8 ah, al, bh, bl;
             split_operands<8>(ah, al, bh, bl, ai, bj, k, g, A, B);
-            acc = mfma_split8(ah, al, bh, bl, acc);
+            acc = mfma_split8<IsExact<FA>::value, IsExact<FB>::value>(ah, al, bh, bl, acc);
         }
         if (k + 16 <= k1) {
             bf16x4 ah, al, bh, bl;
             split_operands<4>(ah, al, bh, bl, ai, bj, k, g, A, B);
-            acc = mfma_split4(ah, al, bh, bl, acc);
+            acc = mfma_split4<IsExact<FA>::value, IsExact<FB>::value>(ah, al, bh, bl, acc);
             k += 16;
         }
     }
@@ -519,10 +546,11 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
     } else {                    // K K^T and Q K^T on the matrix cores, then e^{G_r - G_j}
         for (int t = w; t < 16; t += kGW) {
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-            const f32x4 ab = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return sK[r * (DK + 4) + c]; },
-                                     [&](int c, int j) { return sK[j * (DK + 4) + c]; });
-            const f32x4 mq = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return sX[r * LD + c]; },
-                                     [&](int c, int j) { return sK[j * (DK + 4) + c]; });
+            // (q and k as loaded: exact in bf16 with bf16 inputs)
+            const f32x4 ab = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, exact([&](int r, int c) { return sK[r * (DK + 4) + c]; }),
+                                     exact([&](int c, int j) { return sK[j * (DK + 4) + c]; }));
+            const f32x4 mq = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, exact([&](int r, int c) { return sX[r * LD + c]; }),
+                                     exact([&](int c, int j) { return sK[j * (DK + 4) + c]; }));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = r0 + 4 * (l >> 4) + q, j = j0 + (l & 15);
@@ -1376,7 +1404,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, exact([&](int r, int i) { return R0[r * LD + i]; }),
                                   [&](int i, int j) { return R1[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1414,7 +1442,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                     const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                     auto Bs = [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; };
                     if (pass == 0) {
-                        aq[m] = mm_tile<kSplitMM<E>>(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; }, Bs);
+                        aq[m] = mm_tile<kSplitMM<E>>(aq[m], r0, c0, i0, i0 + QR, exact([&](int r, int i) { return R0[r * LD + i]; }), Bs);
                         aw[m] = mm_tile<kSplitMM<E>>(aw[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return -R2[r * LD + i]; }, Bs);
                     } else {
                         aq[m] = mm_tile<kSplitMM<E>>(aq[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R1[r * LD + i]; }, Bs);
@@ -1726,14 +1754,15 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int t = w; t < TCD; t += kGW) {
             const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
             const Pre pr = preload(r0, c0);
+            // (q and k as loaded: exact in bf16 with bf16 inputs)
             const f32x4 a1 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[r * CP + j]; },
-                                     [&](int j, int c) { return R1[j * LD + c]; });
+                                     exact([&](int j, int c) { return R1[j * LD + c]; }));
             const f32x4 a2 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM1[j * CP + r]; },
-                                     [&](int j, int c) { return R0[j * LD + c]; });
+                                     exact([&](int j, int c) { return R0[j * LD + c]; }));
             const f32x4 a3 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[r * CP + j]; },
-                                     [&](int j, int c) { return R1[j * LD + c]; });
+                                     exact([&](int j, int c) { return R1[j * LD + c]; }));
             const f32x4 a4 = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int j) { return sM2[j * CP + r]; },
-                                     [&](int j, int c) { return R1[j * LD + c]; });
+                                     exact([&](int j, int c) { return R1[j * LD + c]; }));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float x = finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
