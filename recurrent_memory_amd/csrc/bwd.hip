@@ -2061,9 +2061,10 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {          // dMe = -Tril0(dO Y^T), dMk = Tril0(dO X^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 me = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        // (dO as loaded: exact in bf16 with bf16 inputs)
+        const f32x4 me = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, exact([&](int r, int i) { return R0[r * LD + i]; }),
                                  [&](int i, int j) { return R1[j * LD + i]; });
-        const f32x4 mk = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, [&](int r, int i) { return R0[r * LD + i]; },
+        const f32x4 mk = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, exact([&](int r, int i) { return R0[r * LD + i]; }),
                                  [&](int i, int j) { return R2[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -2085,7 +2086,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-                a1[m] = mm_tile<kSplitMM<E>>(a1[m], r0, c0, i0, i0 + QR, [&](int r, int i) { return R0[r * LD + i]; },
+                a1[m] = mm_tile<kSplitMM<E>>(a1[m], r0, c0, i0, i0 + QR, exact([&](int r, int i) { return R0[r * LD + i]; }),
                                 [&](int i, int c) { return sM2[(i - i0) * (DK + 4) + c]; });
             }
         }
@@ -2271,7 +2272,7 @@ __global__ __launch_bounds__(kGT) void bwd2_grads_kernel(BwdArgs p, float* ws, i
     for (int m = 0; m < MV; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
         dXr[m] = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int k) { return sM1[k * CP + r]; },
-                         [&](int k, int i) { return R2[k * LD + i]; });
+                         exact([&](int k, int i) { return R2[k * LD + i]; }));   // dO as loaded
         dXr[m] = mm_tile<kSplitMM<E>>(dXr[m], r0, c0, 0, kBC, [&](int r, int k) { return sM2[k * CP + r]; },
                          [&](int k, int i) { return R0[k * LD + i]; });
     }
