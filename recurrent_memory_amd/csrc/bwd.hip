@@ -1429,14 +1429,60 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int pass = 0; pass < 2; ++pass) {
             for (int i0 = 0; i0 < DV; i0 += QR) {
                 __syncthreads();
+                // bf16 inputs: the rows are staged split (bf16 hi and lo, rows of
+                // DK + 8) and read by the LDS transpose load; the A rows are read
+                // 16 bytes at a time and split in registers
+                constexpr int LS = DK + 8;
+                uint16_t* sSh = reinterpret_cast<uint16_t*>(sM2);
+                uint16_t* sSl = sSh + QR * LS;
+                static_assert(2 * QR * LS * 2 <= kBC * CP * 4, "split rows fit the second C x C buffer");
 #pragma unroll
                 for (int j = 0; j < NPF; ++j) {
                     const int e = 4 * (tid + kGT * j);
-                    put(sM2 + (e / DK) * (DK + 4) + e % DK, pf[j]);
+                    if constexpr (kSplitMM<E>) put_split4(sSh, sSl, (e / DK) * LS + e % DK, pf[j]);
+                    else put(sM2 + (e / DK) * (DK + 4) + e % DK, pf[j]);
                 }
                 __syncthreads();
                 if (i0 + QR < DV) fetch_rows(pass == 0 ? L::oS : L::odS, i0 + QR);
                 else if (pass == 0) fetch_rows(L::odS, 0);
+                if constexpr (kSplitMM<E>) {
+                    static_assert(QR == 32, "one k step per row block");
+                    // A fragment: row r0 + c of X, k = i0 + 4 g + e and i0 + 16 + 4 g + e
+                    auto afrag = [&](const float* X, int r0, bool exact_, float sgn) {
+                        const float* xr = X + (r0 + (l & 15)) * LD + i0 + 4 * (l >> 4);
+                        const float4 a0 = get(xr), a1 = get(xr + 16);
+                        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                        Frag f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            bf16_t hh, ll;
+                            if (exact_) {
+                                hh = static_cast<bf16_t>(av[e]);
+                                ll = static_cast<bf16_t>(0.f);
+                            } else {
+                                split_bf16(sgn * av[e], hh, ll);
+                            }
+                            f.h[e] = hh;
+                            f.l[e] = ll;
+                        }
+                        return f;
+                    };
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+                        const Frag bs = frag_tr(sSh, sSl, LS, 0, c0, l >> 4, l & 15);
+                        if (pass == 0) {
+                            const Frag ao = afrag(R0, r0, true, 1.f);    // dO as loaded: exact in bf16
+                            aq[m] = mfma_split8<true, false>(ao.h, ao.l, bs.h, bs.l, aq[m]);
+                            const Frag av = afrag(R2, r0, false, -1.f);
+                            aw[m] = mfma_split8(av.h, av.l, bs.h, bs.l, aw[m]);
+                        } else {
+                            const Frag av = afrag(R1, r0, false, 1.f);
+                            aq[m] = mfma_split8(av.h, av.l, bs.h, bs.l, aq[m]);
+                        }
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
