@@ -170,5 +170,97 @@ struct Ops<F32> {
     }
 };
 
+// fp32 operands in LDS and registers; each product is hi*hi + hi*lo + lo*hi of
+// the bf16 split x = hi + lo + e (|e| <= 2^-18 |x|, both parts rounded to nearest
+// even), fp32 accumulation: a relative error of about 2^-17 per product term.
+struct SplitTile {
+    bf16x4 h, l;
+};
+template <>
+struct Ops<F32S> {
+    typedef float S;
+    typedef SplitTile R;
+    static constexpr int kPad = 4;
+    __device__ static __forceinline__ S enc(float x) { return x; }
+    __device__ static __forceinline__ void split(float x, bf16_t& h, bf16_t& l) {
+        h = static_cast<bf16_t>(x);
+        l = static_cast<bf16_t>(x - static_cast<float>(h));
+    }
+    __device__ static __forceinline__ R to_reg(f32x4 x) {
+        R r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16_t h, l;
+            split(x[i], h, l);
+            r.h[i] = h;
+            r.l[i] = l;
+        }
+        return r;
+    }
+    __device__ static __forceinline__ R split4(float4 v) { return to_reg(f32x4{v.x, v.y, v.z, v.w}); }
+    __device__ static __forceinline__ f32x4 mma(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                                const bf16x8& bl, f32x4 acc) {
+        acc = mfma32(al, bh, acc);
+        acc = mfma32(ah, bl, acc);
+        return mfma32(ah, bh, acc);
+    }
+    // acc += A[16 x K] · B[16 x K]^T, both row-major in LDS (lane slot e of group
+    // g holds k = 32 k0 + 8 g + e for both operands)
+    template <int K>
+    __device__ static __forceinline__ f32x4 nat(f32x4 acc, const S* arow, const S* brow, int g) {
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            const R a0 = split4(*reinterpret_cast<const float4*>(arow + k + 8 * g));
+            const R a1 = split4(*reinterpret_cast<const float4*>(arow + k + 8 * g + 4));
+            const R b0 = split4(*reinterpret_cast<const float4*>(brow + k + 8 * g));
+            const R b1 = split4(*reinterpret_cast<const float4*>(brow + k + 8 * g + 4));
+            acc = mma(cat(a0.h, a1.h), cat(a0.l, a1.l), cat(b0.h, b1.h), cat(b0.l, b1.l), acc);
+        }
+        return acc;
+    }
+    // contraction over the rows of register tiles, as Ops<BF16>::reg (two tiles
+    // per 16x16x32 step, an odd count padded with zeros)
+    template <int T0, int T1, int N>
+    __device__ static __forceinline__ f32x4 reg(f32x4 acc, const S* arow, const R (&X)[N], int g) {
+        const bf16x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = T0; t < T1; t += 2) {
+            const R a0 = split4(*reinterpret_cast<const float4*>(arow + 16 * t + 4 * g));
+            R a1 = {z, z};
+            if (t + 1 < T1) a1 = split4(*reinterpret_cast<const float4*>(arow + 16 * (t + 1) + 4 * g));
+            const bf16x4 x1h = t + 1 < T1 ? X[t + 1].h : z, x1l = t + 1 < T1 ? X[t + 1].l : z;
+            acc = mma(cat(a0.h, a1.h), cat(a0.l, a1.l), cat(X[t].h, x1h), cat(X[t].l, x1l), acc);
+        }
+        return acc;
+    }
+    // acc += M^T[rows c0 .. c0 + 15] · [X[0]; ...; X[NT - 1]], M row-major in LDS
+    template <int NT, int N>
+    __device__ static __forceinline__ f32x4 regT(f32x4 acc, const S* M, int ld, int c0, const R (&X)[N],
+                                               int g, int c) {
+        const bf16x4 z = {0, 0, 0, 0};
+        auto col = [&](int t) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = M[(16 * t + 4 * g + i) * ld + c0 + c];
+            return to_reg(v);
+        };
+#pragma unroll
+        for (int t = 0; t < NT; t += 2) {
+            const R a0 = col(t);
+            R a1 = {z, z};
+            if (t + 1 < NT) a1 = col(t + 1);
+            const bf16x4 x1h = t + 1 < NT ? X[t + 1].h : z, x1l = t + 1 < NT ? X[t + 1].l : z;
+            acc = mma(cat(a0.h, a1.h), cat(a0.l, a1.l), cat(X[t].h, x1h), cat(X[t].l, x1l), acc);
+        }
+        return acc;
+    }
+    __device__ static __forceinline__ f32x4 acc_tile(const S* M, int ld, int r0, int c0, int g, int c) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = M[(r0 + 4 * g + i) * ld + c0 + c];
+        return v;
+    }
+};
+
 }  // namespace
 }  // namespace dr

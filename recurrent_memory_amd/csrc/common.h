@@ -28,6 +28,13 @@ struct BF16 {
     typedef uint16_t T;
     static constexpr int bytes = 2;
 };
+// fp32 inputs whose chunk products run as three bf16 terms of split operands
+// (hi + lo, about 16 significant bits) on the bf16 matrix cores; for callers
+// whose tolerance is that of bf16 data (DeltaTTT-pre with bf16 inputs).
+struct F32S {
+    typedef float T;
+    static constexpr int bytes = 4;
+};
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

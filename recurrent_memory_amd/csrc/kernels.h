@@ -87,6 +87,8 @@ inline size_t round_up_256(size_t n) { return (n + 255) / 256 * 256; }
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
 // software-pipelined bf16 kernel for variants 0 and 1, called by launch_fwd
 hipError_t launch_fwd_pipelined(int variant, const FwdArgs& a, hipStream_t stream);
+// fp32 operands, products as three bf16 terms of split operands (variants 0, 1)
+hipError_t launch_fwd_split(int variant, const FwdArgs& a, hipStream_t stream);
 // channel-wise decay forms (variant 2 or 3), called by launch_fwd
 hipError_t launch_fwd_channel(int variant, int dtype, const FwdArgs& a, hipStream_t stream);
 // channel-wise decay forms with bf16 operands, two passes (state-independent

@@ -461,6 +461,10 @@ hipError_t launch_dims(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_fwd_split(int variant, const FwdArgs& a, hipStream_t s) {
+    return variant == 0 ? launch_dims<0, F32S>(a, s) : launch_dims<1, F32S>(a, s);
+}
+
 hipError_t launch_fwd(int variant, int dtype, const FwdArgs& a, hipStream_t s) {
     if (variant >= 2) return launch_fwd_channel(variant, dtype, a, s);
     if (dtype == 1) return launch_fwd_pipelined(variant, a, s);   // bf16: pipelined kernel

@@ -206,8 +206,10 @@ TttPieces ttt_pieces(int64_t eb, int B, int T, int H, int dk, int dv) {
     return p;
 }
 
+// split: the scans' products as three bf16 terms of the split fp32 operands (the
+// bf16-input path, whose tolerance is that of bf16 data)
 template <typename E, int VAR>
-hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
+hipError_t launch_ttt_typed(TttArgs a, hipStream_t s, bool split = false) {
     const int64_t tok = static_cast<int64_t>(a.B) * a.T * a.H;
     const int64_t nq = tok * a.dk;
     const TttPieces pc = ttt_pieces(E::bytes, a.B, a.T, a.H, a.dk, a.dv);
@@ -230,11 +232,11 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
     const int dt = E::bytes == 4 ? 0 : 1;
     if (e == hipSuccess) {   // pre-write reads: readouts of the shifted queries
         FwdArgs f{a.B, a.T, a.H, a.dk, a.dv, a.qs, a.k, a.v, a.beta1, nullptr, a.g1, a.A0, a.rd, nullptr, a.H};
-        e = launch_fwd(VAR, dt, f, s);
+        e = split ? launch_fwd_split(VAR, f, s) : launch_fwd(VAR, dt, f, s);
     }
     if (e == hipSuccess) {   // first layer: readout after the write, final state
         FwdArgs f{a.B, a.T, a.H, a.dk, a.dv, a.q, a.k, a.v, a.beta1, nullptr, a.g1, a.A0, a.o1, a.AT, a.H};
-        e = launch_fwd(VAR, dt, f, s);
+        e = split ? launch_fwd_split(VAR, f, s) : launch_fwd(VAR, dt, f, s);
     }
     if (e == hipSuccess) {
         constexpr int N = Vec16<E>::N;
@@ -246,7 +248,7 @@ hipError_t launch_ttt_typed(TttArgs a, hipStream_t s) {
     }
     if (e == hipSuccess) {   // second layer: keys h, queries z, the same values
         FwdArgs f{a.B, a.T, a.H, a.dv, a.dv, a.zq, a.hk, a.v, a.beta2, nullptr, a.g2, a.B0, a.o, a.BT, a.H};
-        e = launch_fwd(VAR, dt, f, s);
+        e = split ? launch_fwd_split(VAR, f, s) : launch_fwd(VAR, dt, f, s);
     }
     return e;
 }
@@ -301,7 +303,7 @@ hipError_t launch_ttt_wide(const TttArgs& a, hipStream_t s) {
     hipError_t e = hipSuccess;
     for (int i = 0; i < (VAR == 1 ? 7 : 5) && e == hipSuccess; ++i)
         e = ttt_convert(true, from[i], const_cast<void*>(to[i]), n[i], s);
-    if (e == hipSuccess) e = launch_ttt_typed<F32, VAR>(f, s);
+    if (e == hipSuccess) e = launch_ttt_typed<F32, VAR>(f, s, true);
     if (e == hipSuccess) e = ttt_convert(false, f.o, a.o, tok * a.dv, s);
     return e;
 }
