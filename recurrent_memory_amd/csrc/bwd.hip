@@ -18,8 +18,11 @@
 //                  dS = dS' Diag(gamma) + dO^T Qhat - dVt^T W;
 //   4. bwd_grads   (one workgroup per chunk) every input gradient from the
 //                  saved factors, states and dVt.
-// Everything is fp32; intermediates live in a workspace with one fixed-size
-// record per (batch, head, chunk).
+// Intermediates are fp32 and live in a workspace with one fixed-size record per
+// (batch, head, chunk).  With fp32 inputs the products run on the fp32 matrix
+// instruction; with bf16 inputs each fp32 operand is split into bf16 hi + lo and
+// a product is hi*hi + hi*lo + lo*hi on the bf16 matrix cores (the chains use
+// their own kernels for this, bwd_fchain_split / bwd_rchain_split).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -157,61 +160,36 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, int i0, int j0, int k0, int 
     return acc;
 }
 
+// The state chains with fp32 inputs (bwd_fchain_kernel, bwd_rchain_kernel; bf16
+// inputs take the split-operand chains below) use two more fp32 forms:
 // mm_tile with the k range split into two interleaved accumulation chains
-// (k1 - k0 a multiple of 8), which the matrix core runs back to back (fp32); the
-// split form is short enough as one chain.
-template <bool SM, class FA, class FB>
+// (k1 - k0 a multiple of 8), which the matrix core runs back to back,
+template <class FA, class FB>
 __device__ __forceinline__ f32x4 mm_tile_k2(f32x4 acc, int i0, int j0, int k0, int k1, const FA& A,
                                             const FB& B) {
-    if constexpr (SM) {
-        return mm_tile<SM>(acc, i0, j0, k0, k1, A, B);
-    } else {
-        const int l = threadIdx.x & 63;
-        const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
-        f32x4 other = {0.f, 0.f, 0.f, 0.f};
+    const int l = threadIdx.x & 63;
+    const int ai = i0 + (l & 15), bj = j0 + (l & 15), kk = l >> 4;
+    f32x4 other = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-        for (int k = k0; k < k1; k += 8) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
-            other = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + 4 + kk), B(k + 4 + kk, bj), other, 0, 0, 0);
-        }
-        return acc + other;
+    for (int k = k0; k < k1; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + kk), B(k + kk, bj), acc, 0, 0, 0);
+        other = __builtin_amdgcn_mfma_f32_16x16x4f32(A(ai, k + 4 + kk), B(k + 4 + kk, bj), other, 0, 0, 0);
     }
+    return acc + other;
 }
 
-// Two tiles with the same rows i0 and columns j0, j1: one A read (and split) feeds
+// and two tiles with the same rows i0 and columns j0, j1, one A read feeding
 // both accumulation chains.
-template <bool SM, class FA, class FB>
+template <class FA, class FB>
 __device__ __forceinline__ void mm_tile2(f32x4& acc0, f32x4& acc1, int i0, int j0, int j1, int k0, int k1,
                                          const FA& A, const FB& B) {
     const int l = threadIdx.x & 63;
     const int ai = i0 + (l & 15), b0 = j0 + (l & 15), b1 = j1 + (l & 15), g = l >> 4;
-    int k = k0;
-    if constexpr (SM) {
-#pragma unroll 4
-        for (; k + 32 <= k1; k += 32) {
-            bf16x8 ah, al, bh0, bl0, bh1, bl1;
-            split_operands<8>(ah, al, bh0, bl0, ai, b0, k, g, A, B);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16_t h, lo;
-                split_bf16(B(k + 8 * g + e, b1), h, lo);
-                bh1[e] = h;
-                bl1[e] = lo;
-            }
-            acc0 = mfma_split8(ah, al, bh0, bl0, acc0);
-            acc1 = mfma_split8(ah, al, bh1, bl1, acc1);
-        }
-        if (k < k1) {
-            acc0 = mm_tile<SM>(acc0, i0, j0, k, k1, A, B);
-            acc1 = mm_tile<SM>(acc1, i0, j1, k, k1, A, B);
-        }
-    } else {
 #pragma unroll 16
-        for (; k < k1; k += 4) {
-            const float a = A(ai, k + g);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b0), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b1), acc1, 0, 0, 0);
-        }
+    for (int k = k0; k < k1; k += 4) {
+        const float a = A(ai, k + g);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b0), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, B(k + g, b1), acc1, 0, 0, 0);
     }
 }
 
@@ -635,6 +613,7 @@ inline unsigned chain_grid(const BwdArgs& a, int DV) {
 // Split gates:       Y = Ut + W S^T,   S = S Diag(gamma) - Y^T Ebar + X^T Kbar.
 template <class L, typename E, int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, int N) {
+    static_assert(!kSplitMM<E>, "fp32 inputs; bf16 inputs take the split-operand chain");
     constexpr int NVT = DV / kBVT;
     // Row strides against LDS bank conflicts in the matrix-core operand reads:
     // an operand read along its rows by the 16 lanes of a group (sS, sW) takes a
@@ -744,7 +723,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 #pragma unroll
         for (int m = 0; m < MT; ++m) {   // Vt = U - W S^T  /  Y = Ut + W S^T
             const int t = w + kCW * m, r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            const f32x4 acc = mm_tile_k2<kSplitMM<E>>(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
+            const f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, DK,
                                          [&](int r, int c) { return sW[r * SW + c]; },
                                          [&](int c, int i) { return sS[i * SS + c]; });
 #pragma unroll
@@ -772,17 +751,17 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
             auto eb = [&](int r, int c) { return sEb[r * SK + c]; };
             if constexpr (NTS == 2 * kCW) {
                 if constexpr (SPLIT) {
-                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, nvt, eb);
-                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, xt, kb);
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, nvt, eb);
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, xt, kb);
                 } else {
-                    mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, vt, kb);
+                    mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, vt, kb);
                 }
             } else {
                 if constexpr (SPLIT) {
-                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, nvt, eb);
-                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, xt, kb);
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, nvt, eb);
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, xt, kb);
                 } else {
-                    acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, vt, kb);
+                    acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, vt, kb);
                 }
             }
 #pragma unroll
@@ -804,6 +783,7 @@ __global__ __launch_bounds__(kCT) void bwd_fchain_kernel(BwdArgs p, float* ws, i
 // Split gates:       dY = -(Me^T dO + Ebar dS'^T),   dS = dS' Diag(gamma) + dO^T Qhat + dY^T W.
 template <class L, typename E, int DK, int DV, bool SPLIT>
 __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, int N) {
+    static_assert(!kSplitMM<E>, "fp32 inputs; bf16 inputs take the split-operand chain");
     constexpr int NVT = DV / kBVT;
     // row strides against bank conflicts (see the forward chain), within the LDS:
     // 4 mod 64 words for operands read along rows (sdS, sA1); 16 mod 64 for dO and
@@ -906,10 +886,10 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
         const int w = tid >> 6, l = tid & 63;
         for (int t = w; t < (kBC / 16) * (kBVT / 16); t += kCW) {   // dVt = Mq^T dO + Kbar dS^T
             const int r0 = 16 * (t / (kBVT / 16)), c0 = 16 * (t % (kBVT / 16));
-            f32x4 acc = mm_tile_k2<kSplitMM<E>>(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
+            f32x4 acc = mm_tile_k2(f32x4{0.f, 0.f, 0.f, 0.f}, r0, c0, 0, kBC,
                                    [&](int r, int m) { return sM[m * SMQ + r]; },
                                    [&](int m, int i) { return sdO[m * SO + i]; });
-            acc = mm_tile_k2<kSplitMM<E>>(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
+            acc = mm_tile_k2(acc, r0, c0, 0, DK, [&](int r, int c) { return sA1[r * SA + c]; },
                              [&](int c, int i) { return sdS[i * SD + c]; });
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -932,11 +912,11 @@ __global__ __launch_bounds__(kCT) void bwd_rchain_kernel(BwdArgs p, float* ws, i
             auto wm = [&](int r, int c) { return sA2[r * SB + c]; };
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
             if constexpr (NTS == 2 * kCW) {
-                mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, dot, qh);
-                mm_tile2<kSplitMM<E>>(acc0, acc1, ii0, cc0, cc1, 0, kBC, dvt, wm);
+                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dot, qh);
+                mm_tile2(acc0, acc1, ii0, cc0, cc1, 0, kBC, dvt, wm);
             } else {
-                acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, dot, qh);
-                acc0 = mm_tile_k2<kSplitMM<E>>(acc0, ii0, cc0, 0, kBC, dvt, wm);
+                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dot, qh);
+                acc0 = mm_tile_k2(acc0, ii0, cc0, 0, kBC, dvt, wm);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
