@@ -212,13 +212,18 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
 
     // ---- per channel: cumulative decay and the decay-carrying copies.
     // Thread (channel pair cp, row group rq): channels 2 cp, 2 cp + 1 and RPT
-    // consecutive rows; the row groups of a channel pair are adjacent lanes,
-    // which exchange their partial decay sums by shuffles.
+    // consecutive rows.  A wave holds CPW channel pairs, and the row groups of a
+    // pair are lanes CPW apart, which exchange their partial decay sums by
+    // shuffles: the lanes of one half-wave then read and write CPW consecutive
+    // words of each of two row groups, rows 16 * 32 / DK apart, in different LDS
+    // banks (with the row groups of a pair in adjacent lanes, groups 0 and 2
+    // shared their banks).
     {
         constexpr int NRQ = 2 * kPrepThreads / DK;
         constexpr int RPT = C / NRQ;
+        constexpr int CPW = 64 / NRQ;
         static_assert(RPT >= 1 && C % NRQ == 0 && 16 % RPT == 0, "row split");
-        const int rq = tid % NRQ, cp = tid / NRQ;
+        const int rq = lane / CPW, cp = w * CPW + lane % CPW;
         const int ch = 2 * cp, r0 = rq * RPT;
         auto ld2 = [&](const uint16_t* m, int r) -> float2 {
             const uint32_t u = *reinterpret_cast<const uint32_t*>(m + r * L::LDK + ch);
@@ -250,8 +255,8 @@ __global__ __launch_bounds__(kPrepThreads, 2) void cw_prep_kernel(FwdArgs p, uns
         const int my_block = r0 / 16;
 #pragma unroll
         for (int q = 0; q < NRQ; ++q) {
-            const float s0 = __shfl(p0, (lane & ~(NRQ - 1)) + q, 64);
-            const float s1 = __shfl(p1, (lane & ~(NRQ - 1)) + q, 64);
+            const float s0 = __shfl(p0, q * CPW + lane % CPW, 64);
+            const float s1 = __shfl(p1, q * CPW + lane % CPW, 64);
             if (q < rq) { e0 += s0; e1 += s1; }
             if (q * RPT < 16 * my_block) { bs0 += s0; bs1 += s1; }
             if (q * RPT < 16) { end0 += s0; end1 += s1; }
