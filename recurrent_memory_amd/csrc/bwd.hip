@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "chunk_ops.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -589,6 +590,153 @@ __global__ __launch_bounds__(kGT) void bwd_prep_kernel(BwdArgs p, float* ws, int
                                   [&](int j, int i) { return sX[j * LD + i]; });
 #pragma unroll
         for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * (l >> 4) + q) * DV + c0 + (l & 15)] = acc[q];
+    }
+}
+
+// The factor kernel of the ungated and scalar-decay forms with bf16 inputs.  q,
+// k and v are exact in bf16, so they are staged as bf16 (half the LDS of fp32
+// copies, v over q once Mq is formed: two workgroups fit on a CU and each covers
+// the other's loads) and the products that take them need no split: Abar = K K^T
+// and Mq = Q K^T are single bf16 products, and W = T diag(beta e^G) K, U = T
+// diag(beta) V take the per-row factors into T's columns, split T and use K and
+// V as loaded.  G is summed in row order, as bwd_prep_kernel does.
+template <int VAR, int DK, int DV>
+__global__ __launch_bounds__(kGT, 2) void bwd_prep_bf16_kernel(BwdArgs p, float* ws, int N) {
+    static_assert(VAR <= 1, "one decay value per row");
+    typedef BwdWsS<DK, DV> L;
+    typedef BF16 E;
+    constexpr int LB = DK + 8;                    // bf16 q, k rows
+    constexpr int LV = DV + 8;                    // bf16 v rows
+    constexpr int LQV = LB > LV ? LB : LV;
+    constexpr int LF = kBC + 4;                   // fp32 C x C rows
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kBC * LB];
+    __shared__ __attribute__((aligned(16))) uint16_t sQV[kBC * LQV];   // q, then v
+    __shared__ __attribute__((aligned(16))) float sA[kBC * LF];
+    __shared__ __attribute__((aligned(16))) float sT[kBC * LF];
+    __shared__ float sBeta[kBC + 1];              // (+ a spare slot, never read)
+    __shared__ float sG[kBC];                     // raw gates, then G
+    __shared__ float sF[kBC];                     // beta_j e^{G_j}
+    __shared__ float sZ[3 * 16 * 20];             // scratch of the blocked inverse
+    const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, cl = l & 15;
+    const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
+    const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
+    float* R = ws + static_cast<int64_t>(u) * L::size;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // beta and the raw gate of each row (rows past the end: 0)
+    const float bt = load_elem<E>(p.beta, tok_index(p, b, t0 + min(tid % kBC, Cn - 1), h));
+    float gr = 0.f;
+    if constexpr (VAR == 1) gr = load_elem<E>(p.g, tok_index(p, b, t0 + min(tid % kBC, Cn - 1), h));
+    // q, k and v rows, 16 bytes a piece (rows past the end zeroed)
+    constexpr int PK = DK / 8, PV = DV / 8;
+    static_assert(kBC * PK % kGT == 0 && kBC * PV % kGT == 0, "piece split");
+    uint4 pq[kBC * PK / kGT], pk[kBC * PK / kGT], pv[kBC * PV / kGT];
+#pragma unroll
+    for (int j = 0; j < kBC * PK / kGT; ++j) {
+        const int e = tid + kGT * j, r = e / PK, c = 8 * (e % PK);
+        const int64_t qi = qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c;
+        pq[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qi);
+        pk[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + qi);
+    }
+#pragma unroll
+    for (int j = 0; j < kBC * PV / kGT; ++j) {
+        const int e = tid + kGT * j, r = e / PV, c = 8 * (e % PV);
+        pv[j] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) +
+                                                tok_index(p, b, t0 + min(r, Cn - 1), h) * DV + c);
+    }
+    auto sel = [](bool ok, uint4 x) { return ok ? x : make_uint4(0, 0, 0, 0); };
+    sBeta[min(tid, kBC)] = tid < Cn ? bt : 0.f;
+    if (tid < kBC) sG[tid] = tid < Cn ? gr : 0.f;
+#pragma unroll
+    for (int j = 0; j < kBC * PK / kGT; ++j) {
+        const int e = tid + kGT * j, r = e / PK, c = 8 * (e % PK);
+        *reinterpret_cast<uint4*>(sQV + r * LQV + c) = sel(r < Cn, pq[j]);
+        *reinterpret_cast<uint4*>(sK + r * LB + c) = sel(r < Cn, pk[j]);
+    }
+    __syncthreads();
+    // G_r = sum_{j <= r} g_j in row order, lane r of wave 0
+    float G = 0.f;
+    if (w == 0) {
+#pragma unroll 8
+        for (int j = 0; j < kBC; ++j) G += j <= l ? sG[j] : 0.f;
+    }
+    __syncthreads();
+    if (w == 0) {
+        sG[l] = G;
+        sF[l] = sBeta[l] * __expf(G);
+        R[L::oG + l] = G;
+    }
+    __syncthreads();
+    if (tid < DK) R[L::oGam + tid] = __expf(sG[kBC - 1]);
+    // Abar (strictly lower) and Mq (lower, diagonal included): K K^T and Q K^T,
+    // then e^{G_r - G_j}
+    for (int t = w; t < 16; t += kGW) {
+        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+        const uint16_t* krow = sK + (j0 + cl) * LB;
+        const f32x4 ab = Ops<BF16>::template nat<DK>(z4, sK + (r0 + cl) * LB, krow, g);
+        const f32x4 mq = Ops<BF16>::template nat<DK>(z4, sQV + (r0 + cl) * LQV, krow, g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * g + q, j = j0 + cl;
+            const float ex = (VAR == 1 && j <= r) ? __expf(sG[r] - sG[j]) : 1.f;
+            const float a_ = j < r ? ab[q] * ex : 0.f;
+            sA[r * LF + j] = a_;
+            R[L::oAb + r * kBC + j] = a_;
+            R[L::oMq + r * kBC + j] = j <= r ? mq[q] * ex : 0.f;
+        }
+    }
+    __syncthreads();
+    // v over q (Mq is formed)
+#pragma unroll
+    for (int j = 0; j < kBC * PV / kGT; ++j) {
+        const int e = tid + kGT * j, r = e / PV, c = 8 * (e % PV);
+        *reinterpret_cast<uint4*>(sQV + r * LQV + c) = sel(r < Cn, pv[j]);
+    }
+    // T = (I + diag(beta) Abar)^-1
+    unit_lower_inverse_blocked<true>(sA, LF, sBeta, sT, LF, sZ);
+    for (int e = tid; e < kBC * kBC; e += kGT) R[L::oT + e] = sT[(e / kBC) * LF + e % kBC];
+    __syncthreads();
+    // W = (T diag(beta e^G)) K and U = (T diag(beta)) V: A = T with its column
+    // factors, split; B as loaded (exact), read by the LDS transpose load.  Lane
+    // (g, c) holds k = k0 + 4 g + e and k0 + 16 + 4 g + e for both operands.
+    auto tfrag = [&](int r0, int k0, bool withG, bf16x8& ah, bf16x8& al) {
+        const float* trow = sT + (r0 + cl) * LF + k0 + 4 * g;
+        const float4 a0 = *reinterpret_cast<const float4*>(trow), a1 = *reinterpret_cast<const float4*>(trow + 16);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = k0 + 4 * g + (e < 4 ? e : 12 + e);
+            bf16_t hh, ll;
+            split_bf16(av[e] * (withG ? sF[j] : sBeta[j]), hh, ll);
+            ah[e] = hh;
+            al[e] = ll;
+        }
+    };
+    const bf16x8 zb = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = w; t < (kBC / 16) * (DK / 16); t += kGW) {
+        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        f32x4 acc = z4;
+#pragma unroll
+        for (int k0 = 0; k0 < kBC; k0 += 32) {
+            bf16x8 ah, al;
+            tfrag(r0, k0, true, ah, al);
+            const bf16x8 bh = cat8(tr_load_b16(sK, LB, k0, c0, g, cl), tr_load_b16(sK, LB, k0 + 16, c0, g, cl));
+            acc = mfma_split8<false, true>(ah, al, bh, zb, acc);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oW + (r0 + 4 * g + q) * DK + c0 + cl] = acc[q];
+    }
+    for (int t = w; t < (kBC / 16) * (DV / 16); t += kGW) {
+        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+        f32x4 acc = z4;
+#pragma unroll
+        for (int k0 = 0; k0 < kBC; k0 += 32) {
+            bf16x8 ah, al;
+            tfrag(r0, k0, false, ah, al);
+            const bf16x8 bh = cat8(tr_load_b16(sQV, LQV, k0, c0, g, cl), tr_load_b16(sQV, LQV, k0 + 16, c0, g, cl));
+            acc = mfma_split8<false, true>(ah, al, bh, zb, acc);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R[L::oU + (r0 + 4 * g + q) * DV + c0 + cl] = acc[q];
     }
 }
 
@@ -2554,7 +2702,10 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t s) {
     float* ws = static_cast<float*>(a.ws);   // one record per unit (bwd_workspace_bytes)
     const dim3 blk(kCT);
     const unsigned chains = chain_grid(a, DV);
-    hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
+    if constexpr (VAR <= 1 && kSplitMM<E>)
+        hipLaunchKernelGGL((bwd_prep_bf16_kernel<VAR, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
+    else
+        hipLaunchKernelGGL((bwd_prep_kernel<VAR, E, DK, DV>), dim3(static_cast<unsigned>(units)), dim3(kGT), 0, s, a, ws, N);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
         if constexpr (kSplitMM<E>)
