@@ -1469,6 +1469,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __shared__ float sBeta[kBC + 1];  // (+ a spare slot, never read)
     __shared__ float sCol[2 * DK];    // column terms of the last row of dG
     __shared__ float4 sPart[kGT];     // per-thread partial sums of four columns
+    __shared__ float sGrow[kBC];      // G per row (row-gate record, bf16 inputs)
+    // ungated and scalar-decay forms with bf16 inputs: G per row in sGrow, and
+    // the four sums of dG as products on split copies of dMq and dAbar
+    constexpr bool kRS = L::kRowGate && kSplitMM<E>;
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
@@ -1793,12 +1797,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         const float4 qv = load4<E>(p.q, qi), kv = load4<E>(p.k, qi);
         put(R0 + r * LD + c, ok ? qv : z4v);
         put(R1 + r * LD + c, ok ? kv : z4v);
-        if constexpr (L::kRowGate) {
+        if constexpr (kRS) {
+        } else if constexpr (L::kRowGate) {
             const float gr = R[L::oG + r];
             put(R2 + r * LD + c, make_float4(gr, gr, gr, gr));
         } else {
             put(R2 + r * LD + c, get(R + L::oG + 4 * e));
         }
+    }
+    if constexpr (kRS) {
+        if (tid < kBC) sGrow[tid] = R[L::oG + tid];
     }
     __syncthreads();
     // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
@@ -1820,10 +1828,11 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     };
     auto finish = [&](int r, int c, float a1, float a2, float a3, float a4, float dQh, float dX_,
                       float dKb) {
-        const float Gr = R2[r * LD + c];
+        const float Gr = kRS ? sGrow[r] : R2[r * LD + c];
+        const float GC = kRS ? sGrow[kBC - 1] : R2[(kBC - 1) * LD + c];
         const float qr = R0[r * LD + c], kr = R1[r * LD + c];
         const float eg = (VAR == 0) ? 1.f : __expf(Gr);
-        const float ebar = (VAR == 0) ? 1.f : __expf(R2[(kBC - 1) * LD + c] - Gr);
+        const float ebar = (VAR == 0) ? 1.f : __expf(GC - Gr);
         const int e = r * DK + c;
         const float dKh = sBeta[r] * dX_;
         if (r < Cn) {
@@ -1910,6 +1919,57 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
+        }
+    } else if constexpr (kRS) {
+        // the decay factor is one number per (r, j): fold it into dMq and dAbar,
+        // split them into R2 (free for the row-gate record), and take the four
+        // sums as products with q and k as loaded (exact in bf16)
+        constexpr int LM = kBC + 4;
+        static_assert(4 * kBC * LM * 2 <= RS * 4, "split C x C copies fit a staging region");
+        uint16_t* M1h = reinterpret_cast<uint16_t*>(R2);
+        uint16_t* M1l = M1h + kBC * LM;
+        uint16_t* M2h = M1l + kBC * LM;
+        uint16_t* M2l = M2h + kBC * LM;
+        for (int e = tid; e < kBC * kBC; e += kGT) {
+            const int r = e / kBC, j = e % kBC;
+            const float ex = (VAR == 1 && j <= r) ? __expf(sGrow[r] - sGrow[j]) : 1.f;
+            put_split1(M1h, M1l, r * LM + j, sM1[r * CP + j] * ex);
+            put_split1(M2h, M2l, r * LM + j, sM2[r * CP + j] * ex);
+        }
+        __syncthreads();
+        const bf16x8 zb = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int t = w; t < TCD; t += kGW) {
+            const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const Pre pr = preload(r0, c0);
+            f32x4 a1 = z4, a2 = z4, a3 = z4, a4 = z4;
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32) {
+                // k and q down the rows j = k0 + 4 g + e and k0 + 16 + 4 g + e, column c0 + c
+                bf16x8 kb, qb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = k0 + 4 * (l >> 4) + (e < 4 ? e : 12 + e);
+                    kb[e] = static_cast<bf16_t>(R1[j * LD + c0 + (l & 15)]);
+                    qb[e] = static_cast<bf16_t>(R0[j * LD + c0 + (l & 15)]);
+                }
+                const Frag m1r = frag_row(M1h, M1l, LM, r0 + (l & 15), k0, l >> 4);
+                const Frag m1t = frag_tr(M1h, M1l, LM, k0, r0, l >> 4, l & 15);
+                const Frag m2r = frag_row(M2h, M2l, LM, r0 + (l & 15), k0, l >> 4);
+                const Frag m2t = frag_tr(M2h, M2l, LM, k0, r0, l >> 4, l & 15);
+                a1 = mfma_split8<false, true>(m1r.h, m1r.l, kb, zb, a1);
+                a2 = mfma_split8<false, true>(m1t.h, m1t.l, qb, zb, a2);
+                a3 = mfma_split8<false, true>(m2r.h, m2r.l, kb, zb, a3);
+                a4 = mfma_split8<false, true>(m2t.h, m2t.l, kb, zb, a4);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float x = finish(ti(r0, q), tj(c0), a1[q], a2[q], a3[q], a4[q], pr.dQh[q], pr.dX[q], pr.dKb[q]);
+                if constexpr (VAR == 1) {
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m);
+                    if ((l & 15) == 0) sRow[(c0 / 16) * kBC + ti(r0, q)] = x;
+                }
+            }
         }
     } else {
         // the decay factor is one number per (r, j): fold it into dMq and dAbar and
