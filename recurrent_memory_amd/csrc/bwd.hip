@@ -1704,48 +1704,129 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     }
     __syncthreads();
     // dA = -T^T dT T^T (strictly lower); T -> R1[0 .. C*CP), tmp -> R1[C*CP ..)
-    float* sT = R1;
     float* sTmp = R1 + kBC * CP;
-    DR_TILE_FOR(e, kBC * kBC / 4, kGT) put(sT + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::oT + 4 * e));
-    __syncthreads();
-    for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
-        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
-                                  [&](int m, int j) { return sT[j * CP + m]; });
+    if constexpr (kSplitMM<E>) {
+        // bf16 inputs: T staged split (bf16 hi and lo, rows of C + 4) where the
+        // fp32 T would be, and read as 8-byte fragments (k = k0 + 4 g + e and
+        // k0 + 16 + 4 g + e); the other operand of each product split as read
+        constexpr int LT2 = kBC + 4;
+        static_assert(2 * kBC * LT2 * 2 <= kBC * CP * 4, "split T fits where T was");
+        uint16_t* Th = reinterpret_cast<uint16_t*>(R1);
+        uint16_t* Tl = Th + kBC * LT2;
+        DR_TILE_FOR(e, kBC * kBC / 4, kGT) put_split4(Th, Tl, (4 * e / kBC) * LT2 + 4 * e % kBC, get(R + L::oT + 4 * e));
+        __syncthreads();
+        const int g = l >> 4, cl = l & 15;
+        auto split8 = [](const float (&v)[8]) {
+            Frag f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
-    }
-    __syncthreads();
-    for (int t = w; t < TCC; t += kGW) {            // dA = -T^T tmp, masked
-        const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
-                                  [&](int m, int j) { return sTmp[m * CP + j]; });
+            for (int e = 0; e < 8; ++e) {
+                bf16_t hh, ll;
+                split_bf16(v[e], hh, ll);
+                f.h[e] = hh;
+                f.l[e] = ll;
+            }
+            return f;
+        };
+        auto arow = [&](const float* X, int ld, int row, int k0) {   // X[row][k]
+            const float4 a0 = get(X + row * ld + k0 + 4 * g), a1 = get(X + row * ld + k0 + 16 + 4 * g);
+            const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            return split8(v);
+        };
+        auto bcol = [&](const float* X, int ld, int k0, int col) {   // X[k][col]
+            float v[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = ti(r0, q), j = tj(j0);
-            sM2[r * CP + j] = j < r ? -acc[q] : 0.f;
+            for (int e = 0; e < 8; ++e) v[e] = X[(k0 + 4 * g + (e < 4 ? e : 12 + e)) * ld + col];
+            return split8(v);
+        };
+        for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            f32x4 acc = z4;
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32)
+                acc = mma3(arow(sM2, CP, r0 + cl, k0), frag_row(Th, Tl, LT2, j0 + cl, k0, g), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
         }
-    }
-    for (int t = w; t < TCD; t += kGW) {            // dX = T^T dW (dKhat = beta dX)
-        const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
-                                  [&](int m, int c) { return R0[m * LD + c]; });
+        __syncthreads();
+        for (int t = w; t < TCC; t += kGW) {            // dA = -T^T tmp, masked
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            f32x4 acc = z4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
-    }
-    __syncthreads();
-    for (int t = w; t < TCV; t += kGW) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
-        const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
-                                  [&](int m, int i) { return R2[m * LD + i]; });
+            for (int k0 = 0; k0 < kBC; k0 += 32)
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), bcol(sTmp, CP, k0, j0 + cl), acc);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = ti(r0, q), i = tj(c0);
-            R0[r * LD + i] = acc[q];
-            if (r < Cn) store_elem<E>(p.gv, tix(r) * DV + i, sBeta[r] * acc[q]);
+            for (int q = 0; q < 4; ++q) {
+                const int r = ti(r0, q), j = tj(j0);
+                sM2[r * CP + j] = j < r ? -acc[q] : 0.f;
+            }
         }
+        for (int t = w; t < TCD; t += kGW) {            // dX = T^T dW (dKhat = beta dX)
+            const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            f32x4 acc = z4;
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32)
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), bcol(R0, LD, k0, c0 + cl), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
+        }
+        __syncthreads();
+        for (int t = w; t < TCV; t += kGW) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
+            const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+            f32x4 acc = z4;
+#pragma unroll
+            for (int k0 = 0; k0 < kBC; k0 += 32)
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), bcol(R2, LD, k0, c0 + cl), acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = ti(r0, q), i = tj(c0);
+                R0[r * LD + i] = acc[q];
+                if (r < Cn) store_elem<E>(p.gv, tix(r) * DV + i, sBeta[r] * acc[q]);
+            }
+        }
+        __syncthreads();
+    } else {
+        float* sT = R1;
+        DR_TILE_FOR(e, kBC * kBC / 4, kGT) put(sT + (4 * e / kBC) * CP + 4 * e % kBC, get(R + L::oT + 4 * e));
+        __syncthreads();
+        for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sM2[r * CP + m]; },
+                                      [&](int m, int j) { return sT[j * CP + m]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sTmp[ti(r0, q) * CP + tj(j0)] = acc[q];
+        }
+        __syncthreads();
+        for (int t = w; t < TCC; t += kGW) {            // dA = -T^T tmp, masked
+            const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
+            const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                      [&](int m, int j) { return sTmp[m * CP + j]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = ti(r0, q), j = tj(j0);
+                sM2[r * CP + j] = j < r ? -acc[q] : 0.f;
+            }
+        }
+        for (int t = w; t < TCD; t += kGW) {            // dX = T^T dW (dKhat = beta dX)
+            const int r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+            const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                      [&](int m, int c) { return R0[m * LD + c]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
+        }
+        __syncthreads();
+        for (int t = w; t < TCV; t += kGW) {            // dY = T^T dVt -> dv = beta dY; dY -> R0
+            const int r0 = 16 * (t / (DV / 16)), c0 = 16 * (t % (DV / 16));
+            const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, c0, 0, kBC, [&](int r, int m) { return sT[m * CP + r]; },
+                                      [&](int m, int i) { return R2[m * LD + i]; });
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = ti(r0, q), i = tj(c0);
+                R0[r * LD + i] = acc[q];
+                if (r < Cn) store_elem<E>(p.gv, tix(r) * DV + i, sBeta[r] * acc[q]);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if constexpr (VAR != 4) {   // dbeta: kRT threads per row, fixed-order sums
         const int r = tid / kRT, qt = tid % kRT;
         float db = 0.f;
