@@ -1663,10 +1663,43 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     }
     __syncthreads();
     if (tid < DK) sCol[DK + tid] = col_total(tid);
+    // bf16 inputs: operands staged split (bf16 hi and lo planes) or split as read,
+    // lane (g, c) holding k = k0 + 4 g + e and k0 + 16 + 4 g + e in slot e
+    const int g = l >> 4, cl = l & 15;
+    auto split8 = [](const float (&v)[8]) {
+        Frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16_t hh, ll;
+            split_bf16(v[e], hh, ll);
+            f.h[e] = hh;
+            f.l[e] = ll;
+        }
+        return f;
+    };
+    auto arow = [&](const float* X, int ld, int row, int k0) {   // X[row][k]
+        const float4 a0 = get(X + row * ld + k0 + 4 * g), a1 = get(X + row * ld + k0 + 16 + 4 * g);
+        const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        return split8(v);
+    };
+    auto bcol = [&](const float* X, int ld, int k0, int col) {   // X[k][col]
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = X[(k0 + 4 * g + (e < 4 ? e : 12 + e)) * ld + col];
+        return split8(v);
+    };
+    constexpr int LS = (DK > DV ? DK : DV) + 8;   // rows of a region staged split
+    static_assert(2 * kBC * LS * 2 <= RS * 4, "a split region fits a staging region");
+    uint16_t* R0h = reinterpret_cast<uint16_t*>(R0);
+    uint16_t* R0l = R0h + kBC * LS;
+    uint16_t* R1h = reinterpret_cast<uint16_t*>(R1);
+    uint16_t* R1l = R1h + kBC * LS;
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
     DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // dW -> R0, X -> R1
         const int r = 4 * e / DK, c = 4 * e % DK;
-        put(R0 + r * LD + c, get(R + L::odW + 4 * e));
+        const float4 dw = get(R + L::odW + 4 * e);
+        if constexpr (kSplitMM<E>) put_split4(R0h, R0l, r * LS + c, dw);
+        else put(R0 + r * LD + c, dw);
         float4 kh;
         if constexpr (L::kRowGate) {   // Khat = k e^{G_r}, zero past the end
             const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);
@@ -1676,29 +1709,46 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             kh = get(R + L::oKh + 4 * e);
         }
         const float br = sBeta[r];
-        put(R1 + r * LD + c, make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w));
+        const float4 x = make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w);
+        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LS + c, x);
+        else put(R1 + r * LD + c, x);
     }
     __syncthreads();
     f32x4 adt[TCC / kGW];
 #pragma unroll
     for (int m = 0; m < TCC / kGW; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        adt[m] = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
-                         [&](int c, int j) { return R1[j * LD + c]; });
+        if constexpr (kSplitMM<E>) {
+            adt[m] = z4;
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                adt[m] = mma3(frag_row(R0h, R0l, LS, r0 + cl, k0, g), frag_row(R1h, R1l, LS, j0 + cl, k0, g), adt[m]);
+        } else {
+            adt[m] = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
+                             [&](int c, int j) { return R1[j * LD + c]; });
+        }
     }
     __syncthreads();
     DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // Y -> R1
         const int r = 4 * e / DV, i = 4 * e % DV;
         const float4 vv = load4<E>(p.v, tix(min(r, Cn - 1)) * DV + i);
         const float br = sBeta[r];
-        put(R1 + r * LD + i, r < Cn ? make_float4(br * vv.x, br * vv.y, br * vv.z, br * vv.w) : z4v);
+        const float4 y = r < Cn ? make_float4(br * vv.x, br * vv.y, br * vv.z, br * vv.w) : z4v;
+        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LS + i, y);
+        else put(R1 + r * LD + i, y);
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < TCC / kGW; ++m) {
         const int t = w + kGW * m, r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        adt[m] = mm_tile<kSplitMM<E>>(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
-                         [&](int i, int j) { return R1[j * LD + i]; });
+        if constexpr (kSplitMM<E>) {
+#pragma unroll
+            for (int k0 = 0; k0 < DV; k0 += 32)
+                adt[m] = mma3(arow(R2, LD, r0 + cl, k0), frag_row(R1h, R1l, LS, j0 + cl, k0, g), adt[m]);
+        } else {
+            adt[m] = mm_tile<kSplitMM<E>>(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
+                             [&](int i, int j) { return R1[j * LD + i]; });
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) sM2[ti(r0, q) * CP + tj(j0)] = adt[m][q];
     }
@@ -1715,29 +1765,6 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         uint16_t* Tl = Th + kBC * LT2;
         DR_TILE_FOR(e, kBC * kBC / 4, kGT) put_split4(Th, Tl, (4 * e / kBC) * LT2 + 4 * e % kBC, get(R + L::oT + 4 * e));
         __syncthreads();
-        const int g = l >> 4, cl = l & 15;
-        auto split8 = [](const float (&v)[8]) {
-            Frag f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16_t hh, ll;
-                split_bf16(v[e], hh, ll);
-                f.h[e] = hh;
-                f.l[e] = ll;
-            }
-            return f;
-        };
-        auto arow = [&](const float* X, int ld, int row, int k0) {   // X[row][k]
-            const float4 a0 = get(X + row * ld + k0 + 4 * g), a1 = get(X + row * ld + k0 + 16 + 4 * g);
-            const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            return split8(v);
-        };
-        auto bcol = [&](const float* X, int ld, int k0, int col) {   // X[k][col]
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = X[(k0 + 4 * g + (e < 4 ? e : 12 + e)) * ld + col];
-            return split8(v);
-        };
         for (int t = w; t < TCC; t += kGW) {            // tmp = dT T^T
             const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
             f32x4 acc = z4;
@@ -1765,7 +1792,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             f32x4 acc = z4;
 #pragma unroll
             for (int k0 = 0; k0 < kBC; k0 += 32)
-                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), bcol(R0, LD, k0, c0 + cl), acc);
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), frag_tr(R0h, R0l, LS, k0, c0, g, cl), acc);
 #pragma unroll
             for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
         }
