@@ -1476,6 +1476,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     float* R0 = sR;
     float* R1 = sR + RS;
     float* R2 = sR + 2 * RS;
+    // bf16 inputs: a region may hold a matrix split into bf16 hi and lo planes
+    // (rows of LR), read as 8-byte fragments
+    constexpr int LR = (DK > DV ? DK : DV) + 8;
+    static_assert(2 * kBC * LR * 2 <= RS * 4, "a split region fits a staging region");
+    uint16_t* R0h = reinterpret_cast<uint16_t*>(R0);
+    uint16_t* R0l = R0h + kBC * LR;
+    uint16_t* R1h = reinterpret_cast<uint16_t*>(R1);
+    uint16_t* R1l = R1h + kBC * LR;
+    uint16_t* R2h = reinterpret_cast<uint16_t*>(R2);
+    uint16_t* R2l = R2h + kBC * LR;
     const int u = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int bh = u / N, n = u % N, b = bh / p.H, h = bh % p.H;
     const int t0 = n * kBC, Cn = min(kBC, p.T - t0);
@@ -1507,9 +1517,15 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // dO -> R0, Vt -> R1, dVt -> R2 (four columns per thread)
         const int r = 4 * e / DV, i = 4 * e % DV;
         const float4 d = load4<E>(p.dO, tix(min(r, Cn - 1)) * DV + i);
-        put(R0 + r * LD + i, r < Cn ? d : z4v);
-        put(R1 + r * LD + i, get(R + L::oVt + 4 * e));
-        put(R2 + r * LD + i, get(R + L::odVt + 4 * e));
+        if constexpr (kSplitMM<E>) {   // split planes (dO: exact, its lo plane zero)
+            put_split4(R0h, R0l, r * LR + i, r < Cn ? d : z4v);
+            put_split4(R1h, R1l, r * LR + i, get(R + L::oVt + 4 * e));
+            put_split4(R2h, R2l, r * LR + i, get(R + L::odVt + 4 * e));
+        } else {
+            put(R0 + r * LD + i, r < Cn ? d : z4v);
+            put(R1 + r * LD + i, get(R + L::oVt + 4 * e));
+            put(R2 + r * LD + i, get(R + L::odVt + 4 * e));
+        }
     }
     // column sums: thread (part, four columns); the parts combined in a fixed order
     constexpr int CG = DK / 4, NPART = kGT / CG;
@@ -1536,8 +1552,18 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
-        const f32x4 acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, exact([&](int r, int i) { return R0[r * LD + i]; }),
-                                  [&](int i, int j) { return R1[j * LD + i]; });
+        f32x4 acc = z4;
+        if constexpr (kSplitMM<E>) {
+#pragma unroll
+            for (int k0 = 0; k0 < DV; k0 += 32) {
+                const Frag ao = frag_row(R0h, R0l, LR, r0 + (l & 15), k0, l >> 4);
+                const Frag av = frag_row(R1h, R1l, LR, j0 + (l & 15), k0, l >> 4);
+                acc = mfma_split8<true, false>(ao.h, ao.l, av.h, av.l, acc);   // dO exact
+            }
+        } else {
+            acc = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DV, exact([&](int r, int i) { return R0[r * LD + i]; }),
+                                      [&](int i, int j) { return R1[j * LD + i]; });
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = ti(r0, q), j = tj(j0);
@@ -1579,37 +1605,19 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                 else if (pass == 0) fetch_rows(L::odS, 0);
                 if constexpr (kSplitMM<E>) {
                     static_assert(QR == 32, "one k step per row block");
-                    // A fragment: row r0 + c of X, k = i0 + 4 g + e and i0 + 16 + 4 g + e
-                    auto afrag = [&](const float* X, int r0, bool exact_, float sgn) {
-                        const float* xr = X + (r0 + (l & 15)) * LD + i0 + 4 * (l >> 4);
-                        const float4 a0 = get(xr), a1 = get(xr + 16);
-                        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                        Frag f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            bf16_t hh, ll;
-                            if (exact_) {
-                                hh = static_cast<bf16_t>(av[e]);
-                                ll = static_cast<bf16_t>(0.f);
-                            } else {
-                                split_bf16(sgn * av[e], hh, ll);
-                            }
-                            f.h[e] = hh;
-                            f.l[e] = ll;
-                        }
-                        return f;
-                    };
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
                         const Frag bs = frag_tr(sSh, sSl, LS, 0, c0, l >> 4, l & 15);
+                        // A: rows r0 + c of dO, dVt (pass 0) or Vt (pass 1), split planes;
+                        // dW accumulates +dVt S and is negated when written
                         if (pass == 0) {
-                            const Frag ao = afrag(R0, r0, true, 1.f);    // dO as loaded: exact in bf16
+                            const Frag ao = frag_row(R0h, R0l, LR, r0 + (l & 15), i0, l >> 4);   // dO exact
                             aq[m] = mfma_split8<true, false>(ao.h, ao.l, bs.h, bs.l, aq[m]);
-                            const Frag av = afrag(R2, r0, false, -1.f);
+                            const Frag av = frag_row(R2h, R2l, LR, r0 + (l & 15), i0, l >> 4);
                             aw[m] = mfma_split8(av.h, av.l, bs.h, bs.l, aw[m]);
                         } else {
-                            const Frag av = afrag(R1, r0, false, 1.f);
+                            const Frag av = frag_row(R1h, R1l, LR, r0 + (l & 15), i0, l >> 4);
                             aq[m] = mfma_split8(av.h, av.l, bs.h, bs.l, aq[m]);
                         }
                     }
@@ -1635,7 +1643,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                     const int r = ti(r0, q), c = tj(c0);
                     if (pass == 0) {
                         R[L::odQh + r * DK + c] = aq[m][q];
-                        R[L::odW + r * DK + c] = aw[m][q];
+                        R[L::odW + r * DK + c] = kSplitMM<E> ? -aw[m][q] : aw[m][q];
                     } else {
                         R[L::odKb + r * DK + c] = aq[m][q];
                     }
@@ -1688,17 +1696,11 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         for (int e = 0; e < 8; ++e) v[e] = X[(k0 + 4 * g + (e < 4 ? e : 12 + e)) * ld + col];
         return split8(v);
     };
-    constexpr int LS = (DK > DV ? DK : DV) + 8;   // rows of a region staged split
-    static_assert(2 * kBC * LS * 2 <= RS * 4, "a split region fits a staging region");
-    uint16_t* R0h = reinterpret_cast<uint16_t*>(R0);
-    uint16_t* R0l = R0h + kBC * LS;
-    uint16_t* R1h = reinterpret_cast<uint16_t*>(R1);
-    uint16_t* R1l = R1h + kBC * LS;
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
     DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // dW -> R0, X -> R1
         const int r = 4 * e / DK, c = 4 * e % DK;
         const float4 dw = get(R + L::odW + 4 * e);
-        if constexpr (kSplitMM<E>) put_split4(R0h, R0l, r * LS + c, dw);
+        if constexpr (kSplitMM<E>) put_split4(R0h, R0l, r * LR + c, dw);
         else put(R0 + r * LD + c, dw);
         float4 kh;
         if constexpr (L::kRowGate) {   // Khat = k e^{G_r}, zero past the end
@@ -1710,7 +1712,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
         const float br = sBeta[r];
         const float4 x = make_float4(br * kh.x, br * kh.y, br * kh.z, br * kh.w);
-        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LS + c, x);
+        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LR + c, x);
         else put(R1 + r * LD + c, x);
     }
     __syncthreads();
@@ -1722,7 +1724,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             adt[m] = z4;
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32)
-                adt[m] = mma3(frag_row(R0h, R0l, LS, r0 + cl, k0, g), frag_row(R1h, R1l, LS, j0 + cl, k0, g), adt[m]);
+                adt[m] = mma3(frag_row(R0h, R0l, LR, r0 + cl, k0, g), frag_row(R1h, R1l, LR, j0 + cl, k0, g), adt[m]);
         } else {
             adt[m] = mm_tile<kSplitMM<E>>(z4, r0, j0, 0, DK, [&](int r, int c) { return R0[r * LD + c]; },
                              [&](int c, int j) { return R1[j * LD + c]; });
@@ -1734,7 +1736,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         const float4 vv = load4<E>(p.v, tix(min(r, Cn - 1)) * DV + i);
         const float br = sBeta[r];
         const float4 y = r < Cn ? make_float4(br * vv.x, br * vv.y, br * vv.z, br * vv.w) : z4v;
-        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LS + i, y);
+        if constexpr (kSplitMM<E>) put_split4(R1h, R1l, r * LR + i, y);
         else put(R1 + r * LD + i, y);
     }
     __syncthreads();
@@ -1744,7 +1746,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         if constexpr (kSplitMM<E>) {
 #pragma unroll
             for (int k0 = 0; k0 < DV; k0 += 32)
-                adt[m] = mma3(arow(R2, LD, r0 + cl, k0), frag_row(R1h, R1l, LS, j0 + cl, k0, g), adt[m]);
+                adt[m] = mma3(frag_row(R2h, R2l, LR, r0 + cl, k0, g), frag_row(R1h, R1l, LR, j0 + cl, k0, g), adt[m]);
         } else {
             adt[m] = mm_tile<kSplitMM<E>>(adt[m], r0, j0, 0, DV, [&](int r, int i) { return R2[r * LD + i]; },
                              [&](int i, int j) { return R1[j * LD + i]; });
@@ -1792,7 +1794,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             f32x4 acc = z4;
 #pragma unroll
             for (int k0 = 0; k0 < kBC; k0 += 32)
-                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), frag_tr(R0h, R0l, LS, k0, c0, g, cl), acc);
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), frag_tr(R0h, R0l, LR, k0, c0, g, cl), acc);
 #pragma unroll
             for (int q = 0; q < 4; ++q) R[L::odX + ti(r0, q) * DK + tj(c0)] = acc[q];
         }
@@ -1802,7 +1804,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             f32x4 acc = z4;
 #pragma unroll
             for (int k0 = 0; k0 < kBC; k0 += 32)
-                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), bcol(R2, LD, k0, c0 + cl), acc);
+                acc = mma3(frag_tr(Th, Tl, LT2, k0, r0, g, cl), frag_tr(R2h, R2l, LR, k0, c0, g, cl), acc);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = ti(r0, q), i = tj(c0);
