@@ -243,7 +243,10 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  * Grouped query/key heads (H_k < H): q, k, dq and dk are [B, T, H_k, d_k]; dq and
  * dk are summed over each group of value heads, through two fp32 buffers of
  * [B, T, H, d_k] at the end of the workspace.  Outputs must not overlap any input
- * or one another.  Arithmetic is fp32 throughout.
+ * or one another.  Intermediates are fp32; with fp32 inputs the products run in
+ * fp32, with DR_BF16 inputs each fp32 operand of a product is split into two
+ * bf16 values (hi + lo) and the product taken as hi*hi + hi*lo + lo*hi with fp32
+ * accumulation (about 2^-17 relative error per product term).
  *
  *   workspace, workspace_bytes
  *          at least delta_bwd_workspace_bytes(desc) bytes: B * H * ceil(T / 64)
