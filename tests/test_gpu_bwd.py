@@ -3,7 +3,8 @@
 Every gradient of DeltaNet, GDN, KDA and GDN-2 in fp32 and bf16, at every head width,
 for sequence lengths 1, 63, 64, 65 and 200 (ragged last chunk), with a random
 initial state and a gradient arriving at the final state; plus a case with no
-final-state gradient and dS0 not requested, and a larger sampled case.
+final-state gradient and dS0 not requested, and larger cases (T = 1024, 330 heads,
+the timed GDN backward's full size) with every head checked.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ from oracle_pool import bwd_all_heads
 from gpu_util import LOG_DECAY_FLOOR, TOL, announce, dev, floor_gates, host, slice_rel_err
 from oracle import delta_bwd as oracle_bwd
 from recurrent_memory_amd import ops
-from recurrent_memory_amd.inputs import Workload, make_forward_inputs
+from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_forward_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +120,20 @@ def test_bwd_long_all_heads(variant):
     gr = _run(variant, "bf16", w, x, dO, dST)
     ref = bwd_all_heads(variant, {**x, "dO": dO, "dS_T": dST}, w.B, w.H)
     _check(variant, "bf16", gr, ref)
+
+
+def test_bwd_headline_all_heads():
+    """GDN, bf16, B=4, H=16, T=4096, d=128 with no initial state and no final-state
+    gradient, as the backward is timed: every gradient of all 64 heads against the
+    oracle."""
+    w = WORKLOADS["gdn_bf16_b4_h16_t4096_d128"]
+    announce("bwd_headline", w.name)
+    x = make_forward_inputs(w)
+    assert x["S0"] is None
+    dO, _ = _upstream(w, 17)
+    gr = _run("gdn", "bf16", w, x, dO, None)
+    ref = bwd_all_heads("gdn", {**x, "dO": dO, "dS_T": None}, w.B, w.H)
+    _check("gdn", "bf16", gr, ref)
 
 
 def test_bwd_deterministic():
