@@ -17,7 +17,7 @@ from oracle import delta_decode as oracle_decode
 from oracle import delta_fwd as oracle_fwd
 from oracle import efla_step_size
 from recurrent_memory_amd import ops
-from recurrent_memory_amd.inputs import Workload, make_decode_inputs, make_forward_inputs
+from recurrent_memory_amd.inputs import WORKLOADS, Workload, make_decode_inputs, make_forward_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,18 @@ def test_efla_step_sizes(dtype, d, Hk, key_norm):
     assert np.array_equal(host(beta), c)
     c1 = host(ops.efla_beta("gdn", k[:, 7].contiguous(), dev(x["beta"][:, 7], dtype)))
     assert np.array_equal(c1, c[:, 7])
+
+
+def test_efla_step_sizes_full_size():
+    """The timed EFLA workload (bf16, B=4, H=16, T=4096, d=128): every step size
+    against the oracle's."""
+    w = WORKLOADS["gdn_bf16_b4_h16_t4096_d128"]
+    announce("efla_full", w.name)
+    x = make_forward_inputs(w)
+    c = host(ops.efla_beta("gdn", dev(x["k"], "bf16"), dev(x["beta"], "bf16")))
+    ref = efla_step_size(x["k"], x["beta"])
+    assert c.shape == ref.shape
+    assert (np.abs(c - ref) / np.abs(ref)).max() <= 2.0 ** -8
 
 
 def test_efla_zero_keys_keep_beta():
