@@ -1547,9 +1547,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         }
         return acc;
     };
-    col_sums(L::oS, L::odS, DV);   // sum_i S dS' per column
-    __syncthreads();
-    if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
+    __syncthreads();   // dO, Vt and dVt staged
     for (int t = w; t < TCC; t += kGW) {            // dMq = Tril0(dO Vt^T)
         const int r0 = 16 * (t / 4), j0 = 16 * (t % 4);
         f32x4 acc = z4;
@@ -1570,6 +1568,10 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             sM1[r * CP + j] = j <= r ? acc[q] : 0.f;
         }
     }
+    // sum_i S dS' per column, from the staged row blocks: a thread's elements of
+    // a block sit in the same four columns in every block, and it keeps those of
+    // S until the matching block of dS' arrives
+    float4 sds = z4v;
     {   // dQhat = dO S, dW = -dVt S, then dKbar = Vt dS', with S and dS' staged by rows
         constexpr int MT = TCD / kGW;   // tiles per wave
         f32x4 aq[MT], aw[MT];
@@ -1579,12 +1581,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         // block's loads are in flight while the current block's products run
         constexpr int NPF = QR * DK / 4 / kGT;
         float4 pf[NPF];
+        float4 keepS[DV / QR][NPF];
+        static_assert(kGT % (DK / 4) == 0, "the same columns in every block");
         auto fetch_rows = [&](int64_t src, int i0) {
 #pragma unroll
             for (int j = 0; j < NPF; ++j) pf[j] = get(R + src + i0 * DK + 4 * (tid + kGT * j));
         };
         fetch_rows(L::oS, 0);
+#pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
             for (int i0 = 0; i0 < DV; i0 += QR) {
                 __syncthreads();
                 // bf16 inputs: the rows are staged split (bf16 hi and lo, rows of
@@ -1599,6 +1605,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                     const int e = 4 * (tid + kGT * j);
                     if constexpr (kSplitMM<E>) put_split4(sSh, sSl, (e / DK) * LS + e % DK, pf[j]);
                     else put(sM2 + (e / DK) * (DK + 4) + e % DK, pf[j]);
+                    if (pass == 0) keepS[i0 / QR][j] = pf[j];
+                    else sds = fma4(keepS[i0 / QR][j], pf[j], sds);
                 }
                 __syncthreads();
                 if (i0 + QR < DV) fetch_rows(pass == 0 ? L::oS : L::odS, i0 + QR);
@@ -1652,6 +1660,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             }
         }
     }
+    sPart[tid] = sds;   // part tid / (DK / 4), columns 4 (tid % (DK / 4)) + [0, 4)
+    __syncthreads();
+    if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
     __syncthreads();
     if constexpr (L::kRowGate) {   // sum_r dKbar Kbar per column, Kbar = k e^{G_C - G_r} (zero past the end)
         const float GC = R[L::oG + kBC - 1];
