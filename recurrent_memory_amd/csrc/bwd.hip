@@ -1469,7 +1469,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __shared__ float sBeta[kBC + 1];  // (+ a spare slot, never read)
     __shared__ float sCol[2 * DK];    // column terms of the last row of dG
     __shared__ float4 sPart[kGT];     // per-thread partial sums of four columns
-    __shared__ float sGrow[kBC];      // G per row (row-gate record, bf16 inputs)
+    __shared__ float sGrow[kBC];      // G per row (row-gate record)
+    __shared__ float sRed[kGW * 16];  // per-wave column sums of dKbar Kbar (row-gate record)
     // ungated and scalar-decay forms with bf16 inputs: G per row in sGrow, and
     // the four sums of dG as products on split copies of dMq and dAbar
     constexpr bool kRS = L::kRowGate && kSplitMM<E>;
@@ -1513,6 +1514,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     {
         const float bt = VAR == 4 ? 1.f : load_elem<E>(p.beta, tix(min(tid % kBC, Cn - 1)));
         sBeta[min(tid, kBC)] = tid < Cn ? bt : 0.f;
+    }
+    if constexpr (L::kRowGate) {
+        if (tid < kBC) sGrow[tid] = R[L::oG + tid];
     }
     DR_TILE_FOR(e, kBC * DV / 4, kGT) {   // dO -> R0, Vt -> R1, dVt -> R2 (four columns per thread)
         const int r = 4 * e / DV, i = 4 * e % DV;
@@ -1572,6 +1576,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     // a block sit in the same four columns in every block, and it keeps those of
     // S until the matching block of dS' arrives
     float4 sds = z4v;
+    float kbs = 0.f;   // this lane's part of sum_r dKbar Kbar in its column (row-gate record)
     {   // dQhat = dO S, dW = -dVt S, then dKbar = Vt dS', with S and dS' staged by rows
         constexpr int MT = TCD / kGW;   // tiles per wave
         f32x4 aq[MT], aw[MT];
@@ -1588,6 +1593,21 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             for (int j = 0; j < NPF; ++j) pf[j] = get(R + src + i0 * DK + 4 * (tid + kGT * j));
         };
         fetch_rows(L::oS, 0);
+        // row-gate record: k at this lane's dKbar elements (rows past the end from
+        // the last row), for the per-column sum of dKbar Kbar, Kbar = k e^{G_C - G_r};
+        // loaded here so that the passes cover the loads.  A wave's tiles all sit in
+        // the 16 columns 16 (w mod DK / 16) + [0, 16).
+        float kraw[L::kRowGate ? MT : 1][4];
+        if constexpr (L::kRowGate) {
+            static_assert(kGW % (DK / 16) == 0, "a wave's tiles share their columns");
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    kraw[m][q] = load_elem<E>(p.k, qk_index(p, b, t0 + min(ti(r0, q), Cn - 1), h) * DK + tj(c0));
+            }
+        }
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -1654,34 +1674,34 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                         R[L::odW + r * DK + c] = kSplitMM<E> ? -aw[m][q] : aw[m][q];
                     } else {
                         R[L::odKb + r * DK + c] = aq[m][q];
+                        if constexpr (L::kRowGate)
+                            kbs = fmaf(aq[m][q], r < Cn ? kraw[m][q] * __expf(sGrow[kBC - 1] - sGrow[r]) : 0.f, kbs);
                     }
                 }
                 aq[m] = z4;
             }
         }
     }
+    if constexpr (L::kRowGate) {   // over the four lanes of a column, then the waves that share it
+        kbs += __shfl_xor(kbs, 16, 64);
+        kbs += __shfl_xor(kbs, 32, 64);
+        if (l < 16) sRed[w * 16 + l] = kbs;
+    }
     sPart[tid] = sds;   // part tid / (DK / 4), columns 4 (tid % (DK / 4)) + [0, 4)
     __syncthreads();
     if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
-    __syncthreads();
-    if constexpr (L::kRowGate) {   // sum_r dKbar Kbar per column, Kbar = k e^{G_C - G_r} (zero past the end)
-        const float GC = R[L::oG + kBC - 1];
-        const int c = 4 * (tid % CG), part = tid / CG, rp = kBC / NPART;
-        float4 acc = z4v;
-#pragma unroll
-        for (int k = 0; k < rp; ++k) {
-            const int i = part * rp + k;
-            const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + min(i, Cn - 1), h) * DK + c);
-            const float f = __expf(GC - R[L::oG + i]);
-            acc = fma4(get(R + L::odKb + i * DK + c),
-                       i < Cn ? make_float4(kv.x * f, kv.y * f, kv.z * f, kv.w * f) : z4v, acc);
+    if constexpr (L::kRowGate) {
+        if (tid < DK) {
+            float a = 0.f;
+            for (int v = tid / 16; v < kGW; v += DK / 16) a += sRed[v * 16 + tid % 16];
+            sCol[DK + tid] = a;
         }
-        sPart[tid] = acc;
     } else {
+        __syncthreads();
         col_sums(L::odKb, L::oKb, kBC);   // sum_r dKbar Kbar per column
+        __syncthreads();
+        if (tid < DK) sCol[DK + tid] = col_total(tid);
     }
-    __syncthreads();
-    if (tid < DK) sCol[DK + tid] = col_total(tid);
     // bf16 inputs: operands staged split (bf16 hi and lo planes) or split as read,
     // lane (g, c) holding k = k0 + 4 g + e and k0 + 16 + 4 g + e in slot e
     const int g = l >> 4, cl = l & 15;
@@ -1925,9 +1945,6 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         } else {
             put(R2 + r * LD + c, get(R + L::oG + 4 * e));
         }
-    }
-    if constexpr (kRS) {
-        if (tid < kBC) sGrow[tid] = R[L::oG + tid];
     }
     __syncthreads();
     // a1 = sum_{j<=r} dMq[r,j] k_j E,  a2 = sum_{j>=r} dMq[j,r] q_j E,
