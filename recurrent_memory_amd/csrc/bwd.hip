@@ -298,10 +298,10 @@ __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int l
 }
 
 // Workspace record of one (batch, head, chunk), in floats.  The gradient
-// kernel, the record's last reader, keeps four [C][DK] intermediates (dW, dX,
-// dQhat, dKbar) in it; they occupy the fields it never reads (W, U) or has read
-// before writing them (Vt, dVt), so the record grows only where 4 DK exceeds
-// DK + 3 DV.
+// kernel, the record's last reader, keeps three [C][DK] intermediates (dQhat,
+// dX, dKbar) in it; they occupy the fields it never reads (W, U) or has read
+// before writing them (Vt, dVt), so the record grows only where 3 DK exceeds
+// DK + 3 DV.  (dW goes from its accumulators to LDS.)
 template <int DK, int DV>
 struct BwdWs {
     static constexpr bool kRowGate = false;
@@ -322,8 +322,7 @@ struct BwdWs {
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
     // the gradient kernel's intermediates, over W, U, Vt, dVt
     static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
-    static constexpr int64_t odW = odQh + C * DK;   // dW           [C][DK]
-    static constexpr int64_t odX = odW + C * DK;    // dX           [C][DK]
+    static constexpr int64_t odX = odQh + C * DK;   // dX           [C][DK]
     static constexpr int64_t odKb = odX + C * DK;   // dKbar        [C][DK]
     static constexpr int64_t size = (odVt + C * DV > odKb + C * DK) ? odVt + C * DV : odKb + C * DK;
     static constexpr int64_t oEb = oKb;             // (the split-gate chains' Ebar; unused here)
@@ -351,8 +350,7 @@ struct BwdWsS {
     static constexpr int64_t oVt = oU + C * DV;     // Vt           [C][DV]
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
     static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
-    static constexpr int64_t odW = odQh + C * DK;   // dW           [C][DK]
-    static constexpr int64_t odX = odW + C * DK;    // dX           [C][DK]
+    static constexpr int64_t odX = odQh + C * DK;   // dX           [C][DK]
     static constexpr int64_t odKb = odX + C * DK;   // dKbar        [C][DK]
     static constexpr int64_t size = (odVt + C * DV > odKb + C * DK) ? odVt + C * DV : odKb + C * DK;
 };
@@ -1613,6 +1611,18 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
 #pragma unroll
             for (int i0 = 0; i0 < DV; i0 += QR) {
                 __syncthreads();
+                if (pass == 1 && i0 == 0) {   // dW over dO, which pass 1 does not read
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = ti(r0, q), c = tj(c0);
+                            if constexpr (kSplitMM<E>) put_split1(R0h, R0l, r * LR + c, -aw[m][q]);
+                            else R0[r * LD + c] = aw[m][q];
+                        }
+                    }
+                }
                 // bf16 inputs: the rows are staged split (bf16 hi and lo, rows of
                 // DK + 8) and read by the LDS transpose load; the A rows are read
                 // 16 bytes at a time and split in registers
@@ -1671,7 +1681,6 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                     const int r = ti(r0, q), c = tj(c0);
                     if (pass == 0) {
                         R[L::odQh + r * DK + c] = aq[m][q];
-                        R[L::odW + r * DK + c] = kSplitMM<E> ? -aw[m][q] : aw[m][q];
                     } else {
                         R[L::odKb + r * DK + c] = aq[m][q];
                         if constexpr (L::kRowGate)
@@ -1728,11 +1737,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
         return split8(v);
     };
     // dT = dW X^T + dVt Y^T with X = beta Khat, Y = beta v
-    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // dW -> R0, X -> R1
+    DR_TILE_FOR(e, kBC * DK / 4, kGT) {   // X -> R1 (dW is in R0)
         const int r = 4 * e / DK, c = 4 * e % DK;
-        const float4 dw = get(R + L::odW + 4 * e);
-        if constexpr (kSplitMM<E>) put_split4(R0h, R0l, r * LR + c, dw);
-        else put(R0 + r * LD + c, dw);
         float4 kh;
         if constexpr (L::kRowGate) {   // Khat = k e^{G_r}, zero past the end
             const float4 kv = load4<E>(p.k, qk_index(p, b, t0 + min(r, Cn - 1), h) * DK + c);

@@ -245,7 +245,8 @@ def test_workspace_size_queries():
     assert ws_bytes("bwd", desc(variant=3, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 30425 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 1445 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=2, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 20825 * 1024 // 100))
-    assert ws_bytes("bwd", desc(variant=1, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 24075 * 1024 // 100))
+    assert ws_bytes("bwd", desc(variant=1, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 20875 * 1024 // 100))
+    assert ws_bytes("bwd", desc(variant=2, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 3365 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=128)) == (DR_OK, up(2 * 3 * n64 * 2245 * 1024 // 10))
     grouped = ws_bytes("bwd", desc(variant=1, H=4, H_k=2))[1]
     assert grouped == up(2 * 4 * n64 * 30475 * 1024 // 100) + 2 * up(2 * 100 * 4 * 128 * 4)
