@@ -252,8 +252,8 @@ dr_status delta_efla_beta(const dr_desc* desc, const void* k, const void* beta, 
  *          at least delta_bwd_workspace_bytes(desc) bytes: B * H * ceil(T / 64)
  *          records, rounded up to 256 bytes, plus the two grouped-head buffers
  *          when H_k < H.  A record is, for d_k/d_v = 128/128 (128/64, 64/128,
- *          64/64): DR_DELTANET and DR_GDN 304.75 KiB (208.75, 224.5, 144.5);
- *          DR_KDA and DR_FG2 432.5 KiB (336.5, 288.25, 208.25); DR_GDN2
+ *          64/64): DR_DELTANET and DR_GDN 272.75 KiB (208.75, 192.5, 128.5);
+ *          DR_KDA and DR_FG2 400.5 KiB (336.5, 256.25, 192.25); DR_GDN2
  *          560.5 KiB (464.5, 368.25, 304.25)
  */
 dr_status delta_bwd_workspace_bytes(const dr_desc* desc, size_t* bytes);

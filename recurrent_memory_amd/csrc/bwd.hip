@@ -297,11 +297,13 @@ __device__ __forceinline__ void unit_lower_inverse_blocked(const float* A, int l
     __syncthreads();
 }
 
-// Workspace record of one (batch, head, chunk), in floats.  The gradient
-// kernel, the record's last reader, keeps three [C][DK] intermediates (dQhat,
-// dX, dKbar) in it; they occupy the fields it never reads (W, U) or has read
-// before writing them (Vt, dVt), so the record grows only where 3 DK exceeds
-// DK + 3 DV.  (dW goes from its accumulators to LDS.)
+// Workspace record of one (batch, head, chunk), in floats.  The forward chain
+// writes Vt over U (each lane reads its U elements before it writes the same Vt
+// elements; nothing else reads U).  The gradient kernel, the record's last
+// reader, keeps three [C][DK] intermediates (dQhat, dX, dKbar) in it; they
+// occupy the field it never reads (W) and those it has read before writing them
+// (Vt, dVt), so the record grows only where 3 DK exceeds DK + 2 DV.  (dW goes
+// from its accumulators to LDS.)
 template <int DK, int DV>
 struct BwdWs {
     static constexpr bool kRowGate = false;
@@ -317,10 +319,10 @@ struct BwdWs {
     static constexpr int64_t oS = oGam + DK;        // S entering   [DV][DK]
     static constexpr int64_t odS = oS + DV * DK;    // dS leaving   [DV][DK]
     static constexpr int64_t oW = odS + DV * DK;    // W            [C][DK]
-    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
-    static constexpr int64_t oVt = oU + C * DV;     // Vt           [C][DV]
+    static constexpr int64_t oU = oW + C * DK;      // U, then Vt   [C][DV]
+    static constexpr int64_t oVt = oU;              // Vt           [C][DV]
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
-    // the gradient kernel's intermediates, over W, U, Vt, dVt
+    // the gradient kernel's intermediates, over W, Vt, dVt
     static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
     static constexpr int64_t odX = odQh + C * DK;   // dX           [C][DK]
     static constexpr int64_t odKb = odX + C * DK;   // dKbar        [C][DK]
@@ -333,7 +335,7 @@ struct BwdWs {
 // (Qhat = q e^G, Khat = k e^G, Kbar = k e^{G_C - G}) are rebuilt from the inputs
 // where they are read, with the same factors: less workspace, and that much less
 // written by the factor kernel and read by the others.  The gradient kernel's
-// intermediates overlay W, U, Vt and dVt as in BwdWs.
+// intermediates overlay W, Vt and dVt as in BwdWs.
 template <int DK, int DV>
 struct BwdWsS {
     static constexpr bool kRowGate = true;
@@ -346,8 +348,8 @@ struct BwdWsS {
     static constexpr int64_t oS = oGam + DK;        // S entering   [DV][DK]
     static constexpr int64_t odS = oS + DV * DK;    // dS leaving   [DV][DK]
     static constexpr int64_t oW = odS + DV * DK;    // W            [C][DK]
-    static constexpr int64_t oU = oW + C * DK;      // U            [C][DV]
-    static constexpr int64_t oVt = oU + C * DV;     // Vt           [C][DV]
+    static constexpr int64_t oU = oW + C * DK;      // U, then Vt   [C][DV]
+    static constexpr int64_t oVt = oU;              // Vt           [C][DV]
     static constexpr int64_t odVt = oVt + C * DV;   // dVt          [C][DV]
     static constexpr int64_t odQh = oW;             // dQhat, then dG [C][DK]
     static constexpr int64_t odX = odQh + C * DK;   // dX           [C][DK]

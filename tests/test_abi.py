@@ -220,8 +220,8 @@ def test_workspace_size_queries():
     """Sizes follow the header's statement: none for the scalar-decay forward and
     for fp32 channel-wise forms; one 38 KiB (split gates: 50 KiB) block per 32
     tokens of a head for the bf16 channel-wise forward; one record per 64 tokens
-    of a head for the backward (d = 128: 304.75 KiB for the ungated and scalar-decay
-    forms, 432.5 KiB for KDA and FG^2-GDN, 560.5 KiB for the split gates), plus two
+    of a head for the backward (d = 128: 272.75 KiB for the ungated and scalar-decay
+    forms, 400.5 KiB for KDA and FG^2-GDN, 560.5 KiB for the split gates), plus two
     fp32 [B,T,H,d_k] buffers with grouped heads; the DeltaTTT-pre intermediates."""
     up = lambda n: (n + 255) // 256 * 256
     assert ws_bytes("fwd", None)[0] == DR_E_NULLPTR
@@ -236,20 +236,20 @@ def test_workspace_size_queries():
     assert ws_bytes("fwd", desc(variant=2, d_k=64)) == (DR_OK, up(2 * 3 * nc * 21 * 1024))
     assert ws_bytes("fwd", desc(variant=3, d_k=64)) == (DR_OK, up(2 * 3 * nc * 29 * 1024))
     n64 = (100 + 63) // 64
-    assert ws_bytes("bwd", desc(variant=1)) == (DR_OK, up(2 * 3 * n64 * 30475 * 1024 // 100))
-    assert ws_bytes("bwd", desc(variant=0)) == (DR_OK, up(2 * 3 * n64 * 30475 * 1024 // 100))
-    assert ws_bytes("bwd", desc(variant=2)) == (DR_OK, up(2 * 3 * n64 * 4325 * 1024 // 10))
-    assert ws_bytes("bwd", desc(variant=4)) == (DR_OK, up(2 * 3 * n64 * 4325 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=1)) == (DR_OK, up(2 * 3 * n64 * 27275 * 1024 // 100))
+    assert ws_bytes("bwd", desc(variant=0)) == (DR_OK, up(2 * 3 * n64 * 27275 * 1024 // 100))
+    assert ws_bytes("bwd", desc(variant=2)) == (DR_OK, up(2 * 3 * n64 * 4005 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=4)) == (DR_OK, up(2 * 3 * n64 * 4005 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=3)) == (DR_OK, up(2 * 3 * n64 * 5605 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=3, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 4645 * 1024 // 10))
     assert ws_bytes("bwd", desc(variant=3, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 30425 * 1024 // 100))
-    assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 1445 * 1024 // 10))
-    assert ws_bytes("bwd", desc(variant=2, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 20825 * 1024 // 100))
+    assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 1285 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=2, d_k=64, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 19225 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=1, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 20875 * 1024 // 100))
     assert ws_bytes("bwd", desc(variant=2, d_k=128, d_v=64)) == (DR_OK, up(2 * 3 * n64 * 3365 * 1024 // 10))
-    assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=128)) == (DR_OK, up(2 * 3 * n64 * 2245 * 1024 // 10))
+    assert ws_bytes("bwd", desc(variant=1, d_k=64, d_v=128)) == (DR_OK, up(2 * 3 * n64 * 1925 * 1024 // 10))
     grouped = ws_bytes("bwd", desc(variant=1, H=4, H_k=2))[1]
-    assert grouped == up(2 * 4 * n64 * 30475 * 1024 // 100) + 2 * up(2 * 100 * 4 * 128 * 4)
+    assert grouped == up(2 * 4 * n64 * 27275 * 1024 // 100) + 2 * up(2 * 100 * 4 * 128 * 4)
     tok = 2 * 100 * 3
     f32_pieces = up(tok * 128 * 4) + 4 * up(tok * 128 * 4) + up(2 * 3 * 128 * 4)
     assert ws_bytes("ttt_pre", desc(variant=1, dtype=0)) == (DR_OK, f32_pieces)
