@@ -416,7 +416,9 @@ def main():
                        "kernel_avg_us": t_b * 1e6, "tokens_per_s": B * T / t_b,
                        "hbm_GBs": nb / t_b / 1e9, "hbm_frac": nb / t_b / 1e9 / HBM_PEAK_GBS,
                        "tflops": nf / t_b / 1e12, "algorithmic_bytes_per_launch": nb,
-                       "algorithmic_flops_per_launch": nf})
+                       "algorithmic_flops_per_launch": nf,
+                       "workspace_bytes": ops.workspace_bytes(
+                           "bwd", ops.DrDesc(B, T, H, dk, dv, 64, ops.VARIANTS["gdn"], ops.DTYPES[bf], H))})
         # DeltaTTT-pre (two memory layers) on the headline shape
         from recurrent_memory_amd.inputs import make_ttt_inputs
         xt = make_ttt_inputs(w)
