@@ -1470,7 +1470,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     __shared__ float sCol[2 * DK];    // column terms of the last row of dG
     __shared__ float4 sPart[kGT];     // per-thread partial sums of four columns
     __shared__ float sGrow[kBC];      // G per row (row-gate record)
-    __shared__ float sRed[kGW * 16];  // per-wave column sums of dKbar Kbar (row-gate record)
+    __shared__ float sRed[kGW * 16];  // per-wave column sums of dKbar Kbar
     // ungated and scalar-decay forms with bf16 inputs: G per row in sGrow, and
     // the four sums of dG as products on split copies of dMq and dAbar
     constexpr bool kRS = L::kRowGate && kSplitMM<E>;
@@ -1533,16 +1533,6 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     }
     // column sums: thread (part, four columns); the parts combined in a fixed order
     constexpr int CG = DK / 4, NPART = kGT / CG;
-    auto col_sums = [&](int64_t oa, int64_t ob, int rows) {   // sum_r a[r, c] b[r, c] -> sPart
-        const int c = 4 * (tid % CG), part = tid / CG, rp = rows / NPART;
-        float4 acc = z4v;
-#pragma unroll
-        for (int k = 0; k < rp; ++k) {
-            const int i = part * rp + k;
-            acc = fma4(get(R + oa + i * DK + c), get(R + ob + i * DK + c), acc);
-        }
-        sPart[tid] = acc;
-    };
     auto col_total = [&](int c) {
         float acc = 0.f;
         for (int part = 0; part < NPART; ++part) {
@@ -1576,7 +1566,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
     // a block sit in the same four columns in every block, and it keeps those of
     // S until the matching block of dS' arrives
     float4 sds = z4v;
-    float kbs = 0.f;   // this lane's part of sum_r dKbar Kbar in its column (row-gate record)
+    float kbs = 0.f;   // this lane's part of sum_r dKbar Kbar in its column
     {   // dQhat = dO S, dW = -dVt S, then dKbar = Vt dS', with S and dS' staged by rows
         constexpr int MT = TCD / kGW;   // tiles per wave
         f32x4 aq[MT], aw[MT];
@@ -1593,19 +1583,22 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
             for (int j = 0; j < NPF; ++j) pf[j] = get(R + src + i0 * DK + 4 * (tid + kGT * j));
         };
         fetch_rows(L::oS, 0);
-        // row-gate record: k at this lane's dKbar elements (rows past the end from
-        // the last row), for the per-column sum of dKbar Kbar, Kbar = k e^{G_C - G_r};
-        // loaded here so that the passes cover the loads.  A wave's tiles all sit in
-        // the 16 columns 16 (w mod DK / 16) + [0, 16).
-        float kraw[L::kRowGate ? MT : 1][4];
-        if constexpr (L::kRowGate) {
-            static_assert(kGW % (DK / 16) == 0, "a wave's tiles share their columns");
+        // Kbar at this lane's dKbar elements, for the per-column sum of dKbar Kbar:
+        // row-gate record, k (rows past the end from the last row; Kbar = k e^{G_C - G_r}
+        // is formed where it is used); otherwise Kbar from the record.  Loaded here
+        // so that the passes cover the loads.  A wave's tiles all sit in the 16
+        // columns 16 (w mod DK / 16) + [0, 16).
+        float kraw[MT][4];
+        static_assert(kGW % (DK / 16) == 0, "a wave's tiles share their columns");
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
+        for (int m = 0; m < MT; ++m) {
+            const int t = w + kGW * m, r0 = 16 * (t / (DK / 16)), c0 = 16 * (t % (DK / 16));
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (L::kRowGate)
                     kraw[m][q] = load_elem<E>(p.k, qk_index(p, b, t0 + min(ti(r0, q), Cn - 1), h) * DK + tj(c0));
+                else
+                    kraw[m][q] = R[L::oKb + ti(r0, q) * DK + tj(c0)];
             }
         }
 #pragma unroll
@@ -1687,31 +1680,25 @@ __global__ __launch_bounds__(kGT) void bwd_grads_kernel(BwdArgs p, float* ws, in
                         R[L::odKb + r * DK + c] = aq[m][q];
                         if constexpr (L::kRowGate)
                             kbs = fmaf(aq[m][q], r < Cn ? kraw[m][q] * __expf(sGrow[kBC - 1] - sGrow[r]) : 0.f, kbs);
+                        else
+                            kbs = fmaf(aq[m][q], kraw[m][q], kbs);
                     }
                 }
                 aq[m] = z4;
             }
         }
     }
-    if constexpr (L::kRowGate) {   // over the four lanes of a column, then the waves that share it
-        kbs += __shfl_xor(kbs, 16, 64);
-        kbs += __shfl_xor(kbs, 32, 64);
-        if (l < 16) sRed[w * 16 + l] = kbs;
-    }
+    // sum_r dKbar Kbar: over the four lanes of a column, then the waves that share it
+    kbs += __shfl_xor(kbs, 16, 64);
+    kbs += __shfl_xor(kbs, 32, 64);
+    if (l < 16) sRed[w * 16 + l] = kbs;
     sPart[tid] = sds;   // part tid / (DK / 4), columns 4 (tid % (DK / 4)) + [0, 4)
     __syncthreads();
-    if (tid < DK) sCol[tid] = R[L::oGam + tid] * col_total(tid);
-    if constexpr (L::kRowGate) {
-        if (tid < DK) {
-            float a = 0.f;
-            for (int v = tid / 16; v < kGW; v += DK / 16) a += sRed[v * 16 + tid % 16];
-            sCol[DK + tid] = a;
-        }
-    } else {
-        __syncthreads();
-        col_sums(L::odKb, L::oKb, kBC);   // sum_r dKbar Kbar per column
-        __syncthreads();
-        if (tid < DK) sCol[DK + tid] = col_total(tid);
+    if (tid < DK) {
+        sCol[tid] = R[L::oGam + tid] * col_total(tid);
+        float a = 0.f;
+        for (int v = tid / 16; v < kGW; v += DK / 16) a += sRed[v * 16 + tid % 16];
+        sCol[DK + tid] = a;
     }
     // bf16 inputs: operands staged split (bf16 hi and lo planes) or split as read,
     // lane (g, c) holding k = k0 + 4 g + e and k0 + 16 + 4 g + e in slot e
